@@ -1,0 +1,210 @@
+/*
+ * cad.h -- C ABI of libcad: the copy-span splice forward on AMD MI355X (gfx950).
+ *
+ * The operation: commit a span of N known tokens to a decoder's KV cache in
+ * one parallel forward instead of N autoregressive steps, then take a
+ * (grammar-)masked argmax per position and a longest-agreeing-prefix
+ * acceptance.  Sources:
+ *   - "Copy-as-Decode: Grammar-Constrained Parallel Prefill for LLM Editing",
+ *     §2.4 (the splice: one forward over the span with the existing KV
+ *     cache), §2.3 (masked argmax at decision points, forced-template
+ *     prefills spliced the same way), Fig. 1 (acceptance is 1 inside a copy
+ *     op), appendix "Position-encoding correctness" (positions advance by N).
+ *   - "CopyLoop: Fast Looped Transformer Decoding via Context Copying and
+ *     Shallow Screening", §2 "Block Construction" (suffix-match proposal),
+ *     "Shallow Screening", "Concurrent Pipeline", "Full-Depth Verification".
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "dev" are device (HBM) pointers; "host" are host
+ *     pointers read before the call returns.  The caller owns and frees every
+ *     buffer it passes; the library owns only the workspace it allocates in
+ *     cad_model_create and frees in cad_model_destroy.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and is asynchronous: outputs are valid once the caller synchronises.
+ *     Nothing synchronises the host except create and destroy.
+ *   - Argument errors are detected on the host, return a non-zero
+ *     cad_status and enqueue nothing; cad_last_error() then describes the
+ *     failure (thread-local string).  HIP launch failures return CAD_E_HIP.
+ *   - Data-dependent faults found on the device (token id outside the
+ *     vocabulary, a mask row that allows nothing, a block-table entry outside
+ *     the pool) are OR-ed into the optional `dev_status` word; the kernels
+ *     then skip the offending read or write instead of faulting.
+ *   - A model handle is not re-entrant: one host thread and one stream at a
+ *     time per handle, because calls share its workspace.
+ */
+#ifndef CAD_H
+#define CAD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct cad_model cad_model; /* opaque, library-owned */
+typedef void* cad_stream;           /* hipStream_t */
+
+typedef enum { CAD_F32 = 0, CAD_BF16 = 1 } cad_dtype;
+
+/* COMMIT: acceptance is N by construction (a copy op or a forced template).
+ * VERIFY: accept the longest prefix on which the model agrees (see below). */
+typedef enum { CAD_COMMIT = 0, CAD_VERIFY = 1 } cad_mode;
+
+typedef enum {
+  CAD_OK = 0,
+  CAD_E_ARG = 1,         /* null pointer, bad size or enum, misaligned pointer */
+  CAD_E_CAPACITY = 2,    /* span longer than max_tokens, cache too small */
+  CAD_E_UNSUPPORTED = 3, /* shape the kernels do not implement */
+  CAD_E_HIP = 4          /* a HIP runtime call failed */
+} cad_status;
+
+/* bits of the device status word */
+#define CAD_DEV_BAD_TOKEN 1u  /* a span token is outside [0, vocab): its embedding row reads as zeros */
+#define CAD_DEV_EMPTY_MASK 2u /* a mask row allows no id: that argmax is -1 */
+#define CAD_DEV_BAD_BLOCK 4u  /* a block-table entry is outside [0, num_blocks): that K/V is skipped */
+
+#define CAD_KV_BLOCK 16       /* tokens per KV block */
+#define CAD_MAX_SEQS 64       /* sequences per batched call */
+
+/* Model shape.  Llama-style decoder: RMSNorm, rotary positions (half-split
+ * pairs, base rope_theta), grouped-query attention (query head h reads KV
+ * head h / (n_q_heads / n_kv_heads)), SwiGLU FFN, no biases, untied LM head.
+ * loop_depth > 1: one shared block (n_layers must be 1) applied loop_depth
+ * times, with one KV cache per depth (CopyLoop's looped decoder).
+ * max_tokens: the most span rows one call may carry (sizes the workspace).
+ * Supported: dtype CAD_F32 any head_dim <= 128 (even); dtype CAD_BF16
+ * head_dim 64 or 128 and d_model, ffn_dim, n_q_heads*head_dim multiples of 64. */
+typedef struct {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
+  int32_t loop_depth;
+  float rope_theta, rms_eps;
+  int32_t dtype; /* cad_dtype */
+  int32_t max_tokens;
+} cad_config;
+
+/* Weights: dev pointers, element type = cfg.dtype, row-major [out][in]
+ * (nn.Linear layout).  Per-layer fields are HOST arrays of n_layers dev
+ * pointers; the library copies the arrays, never the weights, and reads the
+ * weights on every call, so they must outlive the model.
+ *   tok_embed  [vocab][d]            final_norm [d]     lm_head [vocab][d]
+ *   attn_norm  [d]                    ffn_norm   [d]
+ *   w_qkv      [(Hq + 2 Hkv) hd][d]   rows: all q heads, then k heads, then v heads
+ *   w_o        [d][Hq hd]
+ *   w_gate_up  [2 F][d]               rows: gate (F rows) then up (F rows)
+ *   w_down     [d][F]                                                      */
+typedef struct {
+  const void* tok_embed;
+  const void* final_norm;
+  const void* lm_head;
+  const void* const* attn_norm;
+  const void* const* w_qkv;
+  const void* const* w_o;
+  const void* const* ffn_norm;
+  const void* const* w_gate_up;
+  const void* const* w_down;
+} cad_weights;
+
+/* Paged KV cache, element type = cfg.dtype, caller-owned (dev):
+ *   k: [n_layers * loop_depth][num_blocks][Hkv][16][hd]   keys after rotation
+ *   v: [n_layers * loop_depth][num_blocks][Hkv][hd][16]   values, token-minor
+ * Token t of a sequence lives in block block_table[seq][t / 16], slot t % 16.
+ * block_table: dev int32 [n_seq][max_blocks_per_seq]; a single-sequence call
+ * uses row 0 (an identity table gives a contiguous cache).  Blocks of
+ * different sequences must not overlap. */
+typedef struct {
+  void* k;
+  void* v;
+  int64_t num_blocks;
+  const int32_t* block_table;
+  int32_t max_blocks_per_seq;
+} cad_kv;
+
+/* Create a model handle over caller-owned weights.  Validates the shape,
+ * allocates the workspace for cfg->max_tokens rows and synchronises once.
+ * Returns CAD_E_UNSUPPORTED for shapes the kernels do not implement. */
+cad_status cad_model_create(const cad_config* cfg, const cad_weights* w, cad_model** out);
+
+/* Free the workspace (synchronises the device).  NULL is a no-op. */
+void cad_model_destroy(cad_model* m);
+
+/* Message for the last failed call on this thread ("" if none). */
+const char* cad_last_error(void);
+
+/* Copy-span splice forward (Copy-as-Decode §2.4; CopyLoop §2 "Full-Depth
+ * Verification").
+ *   L        valid cache length before the call: span token k sits at absolute
+ *            position L + k and attends to positions 0 .. L + k.
+ *   span     dev int32 [N]; 1 <= N <= max_tokens; L + N <= 16 * max_blocks_per_seq.
+ *   mask     dev uint32 [N][ceil(vocab/32)] or NULL (everything allowed): bit
+ *            v % 32 of word v / 32 set = id v allowed at that position.
+ *   mode     CAD_COMMIT or CAD_VERIFY.
+ *   argmax   dev int32 [N]: masked argmax of each row's logits, lowest id on
+ *            ties, -1 for a row that allows nothing.
+ *   accepted dev int32 [1]: N (COMMIT) or 1 + the number of leading j >= 1
+ *            with argmax[j-1] == span[j] (VERIFY).  The caller's new valid
+ *            length is L + accepted and its next token is argmax[accepted-1]
+ *            (the correction, or the bonus token on a full match).
+ *   logits   dev float [N][vocab] or NULL: the fp32 logits, if wanted.
+ *   dev_status dev int32 [1] or NULL: CAD_DEV_* bits are OR-ed in.
+ * All N rows' K/V are written to cache slots L .. L+N-1 in place (slots
+ * beyond L + accepted are stale afterwards and are overwritten by the next
+ * call).  Slots outside L .. L+N-1 are not written. */
+cad_status cad_splice_forward(cad_model* m, const cad_kv* kv, int64_t L, const int32_t* span,
+                              int32_t N, const uint32_t* mask, int32_t mode, int32_t* argmax,
+                              int32_t* accepted, float* logits, int32_t* dev_status,
+                              cad_stream stream);
+
+/* One autoregressive decode step: the splice with N = 1 (Copy-as-Decode §3
+ * "Kernel microbenchmark": the comparator is N one-token forwards, each
+ * appending to the cache).  token: dev int32 [1]; mask_row: dev uint32
+ * [ceil(vocab/32)] or NULL; argmax: dev int32 [1]; logits: dev float [vocab]
+ * or NULL. */
+cad_status cad_decode_step(cad_model* m, const cad_kv* kv, int64_t L, const int32_t* token,
+                           const uint32_t* mask_row, int32_t* argmax, float* logits,
+                           int32_t* dev_status, cad_stream stream);
+
+/* Context-copy proposal (CopyLoop §2 "Block Construction").  tokens: dev
+ * int32 [T], the whole history whose last element is the new head.  For n =
+ * min(max_ngram, T-1) down to min_ngram, find the largest p with p + n <= T-1
+ * and tokens[p .. p+n-1] == tokens[T-n .. T-1]; the first n that matches
+ * gives out_pos = p + n and out_tokens = tokens[p+n .. min(p+n+K, T) - 1]
+ * (out_len of them).  No match: out_len = 0, out_pos = -1.
+ * 1 <= min_ngram <= max_ngram <= 64, K >= 1, T >= 0.  out_tokens dev int32
+ * [K]; out_len dev int32 [1]; out_pos dev int64 [1]. */
+cad_status cad_propose_suffix_match(const int32_t* tokens, int64_t T, int32_t max_ngram,
+                                    int32_t min_ngram, int32_t K, int32_t* out_tokens,
+                                    int32_t* out_len, int64_t* out_pos, cad_stream stream);
+
+/* Batched splice over n_seq independent sequences sharing one paged pool
+ * (continuous-batching form of the splice; Copy-as-Decode §7 names paged
+ * attention integration as the next step).  seq_L: host int64 [n_seq];
+ * offsets: host int32 [n_seq + 1], offsets[0] = 0, sequence b owns span rows
+ * offsets[b] .. offsets[b+1]-1 (at least one) of spans (dev int32 [total]),
+ * mask (dev uint32 [total][ceil(vocab/32)] or NULL), argmax (dev int32
+ * [total]) and logits (dev float [total][vocab] or NULL).  Sequence b uses
+ * block-table row b.  accepted: dev int32 [n_seq].  total <= max_tokens,
+ * n_seq <= CAD_MAX_SEQS. */
+cad_status cad_splice_forward_batched(cad_model* m, const cad_kv* kv, int32_t n_seq,
+                                      const int64_t* seq_L, const int32_t* offsets,
+                                      const int32_t* spans, const uint32_t* mask, int32_t mode,
+                                      int32_t* argmax, int32_t* accepted, float* logits,
+                                      int32_t* dev_status, cad_stream stream);
+
+/* Looped decoder with shallow screening (CopyLoop §2): the block [head,
+ * copied tail] (span, N rows) runs through depths 1 .. screen_depth; the
+ * readout there gives screen_argmax (dev int32 [N]) and the survivors count
+ * (dev int32 [1]) by the VERIFY acceptance rule; only survivors continue to
+ * depth loop_depth (rows at or beyond the survivors count write no deeper
+ * KV), where the readout gives argmax (dev int32 [N], -1 beyond the
+ * survivors) and accepted (dev int32 [1]).  Requires loop_depth > 1 and
+ * 1 <= screen_depth <= loop_depth.  mask applies to both readouts. */
+cad_status cad_splice_forward_looped(cad_model* m, const cad_kv* kv, int64_t L,
+                                     const int32_t* span, int32_t N, int32_t screen_depth,
+                                     const uint32_t* mask, int32_t* screen_argmax,
+                                     int32_t* survivors, int32_t* argmax, int32_t* accepted,
+                                     float* logits, int32_t* dev_status, cad_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CAD_H */

@@ -1,0 +1,87 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function
+include/cad.h declares, and rejects bad arguments on the host before any
+device work (these calls never reach the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+cad = pytest.importorskip("verify_forward_amd")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared():
+    text = open(os.path.join(ROOT, "include", "cad.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:cad_status|void|const char\*)\s+(cad_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared()
+    assert set(names) == set(cad.EXPORTS), names
+
+
+def test_library_exports_every_declared_symbol():
+    L = cad.lib()
+    for name in declared():
+        assert hasattr(L, name), name
+
+
+def good_config(**kw):
+    c = cad.cad_config(2, 128, 4, 2, 64, 256, 512, 1, 10000.0, 1e-5, cad.CAD_BF16, 16)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_layers", 0, cad.CAD_E_ARG),
+    ("vocab", -1, cad.CAD_E_ARG),
+    ("dtype", 7, cad.CAD_E_ARG),
+    ("n_kv_heads", 3, cad.CAD_E_ARG),
+    ("head_dim", 96, cad.CAD_E_UNSUPPORTED),
+    ("d_model", 100, cad.CAD_E_UNSUPPORTED),
+    ("loop_depth", 0, cad.CAD_E_ARG),
+    ("rope_theta", -1.0, cad.CAD_E_ARG),
+])
+def test_create_rejects_bad_config(field, value, status):
+    c = good_config(**{field: value})
+    h = ctypes.c_void_p()
+    w = cad.cad_weights()
+    st = cad.lib().cad_model_create(ctypes.byref(c), ctypes.byref(w), ctypes.byref(h))
+    assert st == status
+    assert h.value is None
+    assert cad.cad_last_error() != ""
+
+
+def test_create_rejects_missing_weights():
+    c = good_config()
+    h = ctypes.c_void_p()
+    w = cad.cad_weights()
+    assert cad.lib().cad_model_create(ctypes.byref(c), ctypes.byref(w), ctypes.byref(h)) == cad.CAD_E_ARG
+    assert "weights" in cad.cad_last_error()
+
+
+def test_looped_config_needs_single_layer():
+    c = good_config(loop_depth=4)
+    h = ctypes.c_void_p()
+    w = cad.cad_weights()
+    assert cad.lib().cad_model_create(ctypes.byref(c), ctypes.byref(w), ctypes.byref(h)) == cad.CAD_E_ARG
+
+
+def test_calls_reject_null_model_and_bad_sizes():
+    L = cad.lib()
+    kv = cad.cad_kv()
+    assert L.cad_splice_forward(None, ctypes.byref(kv), 0, None, 1, None, 0, None, None, None, None, None) == cad.CAD_E_ARG
+    assert L.cad_decode_step(None, ctypes.byref(kv), 0, None, None, None, None, None, None) == cad.CAD_E_ARG
+    buf = (ctypes.c_int32 * 4)()
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    # bad n-gram bounds, K and T are caught before any launch
+    assert L.cad_propose_suffix_match(p, 4, 0, 1, 4, p, p, p, None) == cad.CAD_E_ARG
+    assert L.cad_propose_suffix_match(p, 4, 4, 5, 4, p, p, p, None) == cad.CAD_E_ARG
+    assert L.cad_propose_suffix_match(p, 4, 65, 1, 4, p, p, p, None) == cad.CAD_E_ARG
+    assert L.cad_propose_suffix_match(p, 4, 4, 1, 0, p, p, p, None) == cad.CAD_E_ARG
+    assert L.cad_propose_suffix_match(p, -1, 4, 1, 4, p, p, p, None) == cad.CAD_E_ARG
+    assert L.cad_propose_suffix_match(None, 4, 4, 1, 4, p, p, p, None) == cad.CAD_E_ARG
+    assert L.cad_propose_suffix_match(p, 4, 4, 1, 4, None, p, p, None) == cad.CAD_E_ARG

@@ -1,0 +1,273 @@
+"""GPU parity: libcad (through the C ABI) against the float64 CPU oracle.
+
+Bars (floating point): logits max|diff| <= 1e-4 in fp32 and <= 2e-2 in bf16;
+appended KV within the same bound; argmax bit-exact at every position whose
+oracle top-2 masked margin exceeds 0.1; accepted bit-exact when every
+position it examines has such a margin.  Integer work (suffix match) is
+bit-exact everywhere.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.decision import COMMIT, VERIFY
+from oracle.decoder import Config, KVCache
+import synth
+
+pytestmark = pytest.mark.gpu
+
+cad = pytest.importorskip("verify_forward_amd")
+import gpu_helpers as H  # noqa: E402
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+MARGIN = 0.1
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return "cuda"
+
+
+def check_decisions(lg_ref, mask, a_gpu, span, mode, acc_gpu):
+    a_ref = oracle.masked_argmax(lg_ref, mask)
+    margin = oracle.top2_margin(lg_ref, mask)
+    sure = margin > MARGIN
+    assert np.array_equal(a_gpu[sure], a_ref[sure]), (a_gpu[sure], a_ref[sure])
+    acc_ref = oracle.acceptance(a_ref, span, mode)
+    examined = acc_ref if acc_ref < len(span) else len(span) - 1
+    if mode == COMMIT or sure[:examined].all():
+        assert acc_gpu == acc_ref
+    return a_ref, acc_ref, sure
+
+
+# ---------------------------------------------------------------------------
+# suffix match: bit-exact
+# ---------------------------------------------------------------------------
+
+def test_suffix_match_exhaustive_and_fuzz():
+    dev = _dev()
+    cases = []
+    import itertools
+    for T in range(0, 11):
+        for seq in itertools.product(range(2), repeat=T):
+            cases.append((list(seq), 1 + (T % 4)))
+    r = synth.rng(77)
+    for _ in range(300):
+        T = int(r.integers(2, 5000))
+        x = synth.zipf_ids(r, T, 32000)
+        if r.random() < 0.5:
+            n = int(r.integers(1, 6))
+            p = int(r.integers(0, max(1, T - n - 1)))
+            x[T - n:] = x[p:p + n]
+        cases.append((list(x), int(r.integers(1, 9))))
+    n = len(cases)
+    outs = torch.full((n, 8), -9, dtype=torch.int32, device=dev)
+    lens = torch.full((n,), -9, dtype=torch.int32, device=dev)
+    poss = torch.full((n,), -9, dtype=torch.int64, device=dev)
+    toks = [torch.tensor(c[0] if c[0] else [0], dtype=torch.int32, device=dev) for c in cases]
+    for i, (seq, K) in enumerate(cases):
+        cad.cad_propose_suffix_match(toks[i], 4, 1, K, outs[i], lens[i:i + 1], poss[i:i + 1], T=len(seq))
+    torch.cuda.synchronize()
+    outs, lens, poss = outs.cpu().numpy(), lens.cpu().numpy(), poss.cpu().numpy()
+    for i, (seq, K) in enumerate(cases):
+        exp, pos = oracle.suffix_match(seq, 4, 1, K)
+        assert lens[i] == len(exp) and poss[i] == pos, (seq, K)
+        assert list(outs[i, :lens[i]]) == list(exp)
+
+
+# ---------------------------------------------------------------------------
+# tiny fp32 model: prefill + splice + sequential, everything vs the oracle
+# ---------------------------------------------------------------------------
+
+def test_tiny_fp32_end_to_end():
+    dev = _dev()
+    shape = synth.TINY
+    cfg = Config.of(shape)
+    Wc = synth.make_weights(shape, seed=0)
+    Wn = synth.weights_to_numpy(Wc)
+    Wd = {k: (v.to(dev) if torch.is_tensor(v) else [{kk: vv.to(dev) for kk, vv in lw.items()} for lw in v])
+          for k, v in Wc.items()}
+    L, N = 512, 32
+    prompt = synth.uniform_prompt(L, shape.vocab)
+    span = prompt[100:132].copy()
+    mask = synth.banned_ids_mask(N, shape.vocab, 16)
+    nb = (L + N + 15) // 16
+    kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device=dev)
+    model = cad.cad_model_create(shape, Wd, max_tokens=L)
+    o = H.outputs(L, shape.vocab)
+    cad.cad_splice_forward(model, kv, 0, H.tensors_i32(prompt), None, cad.CAD_COMMIT, o["argmax"],
+                           o["accepted"], o["logits"], o["status"])
+    okv = KVCache.empty(1, 4, L + N, 64)
+    lp = oracle.prefill(cfg, Wn, okv, prompt)
+    torch.cuda.synchronize()
+    assert int(o["accepted"][0]) == L and int(o["status"][0]) == 0
+    assert np.max(np.abs(o["logits"].cpu().numpy() - lp)) <= TOL["f32"]
+    gk, gv = H.read_seq(kv, L)
+    assert np.max(np.abs(gk[0] - okv.k[0][:, :L])) <= TOL["f32"]
+    assert np.max(np.abs(gv[0] - okv.v[0][:, :L])) <= TOL["f32"]
+    # splice in VERIFY mode with the banned-ids mask
+    o2 = H.outputs(N, shape.vocab)
+    mask_t = torch.from_numpy(mask.view(np.int32)).to(dev)
+    cad.cad_splice_forward(model, kv, L, H.tensors_i32(span), mask_t, cad.CAD_VERIFY, o2["argmax"],
+                           o2["accepted"], o2["logits"], o2["status"])
+    okv_seq = okv.copy()
+    ls = oracle.splice(cfg, Wn, okv, L, span)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(o2["logits"].cpu().numpy() - ls)) <= TOL["f32"]
+    check_decisions(ls, mask, o2["argmax"].cpu().numpy(), span, VERIFY, int(o2["accepted"][0]))
+    gk, gv = H.read_seq(kv, L + N)
+    assert np.max(np.abs(gk[0] - okv.k[0][:, :L + N])) <= TOL["f32"]
+    assert np.max(np.abs(gv[0] - okv.v[0][:, :L + N])) <= TOL["f32"]
+    # the same span as N decode steps on the GPU equals the splice
+    kv2 = cad.KVCache(kv.k.clone(), kv.v.clone(), kv.block_table)
+    seq_logits = torch.empty((N, shape.vocab), dtype=torch.float32, device=dev)
+    am = torch.empty(N, dtype=torch.int32, device=dev)
+    span_t = H.tensors_i32(span)
+    for j in range(N):
+        cad.cad_decode_step(model, kv2, L + j, span_t[j:j + 1], mask_t[j], am[j:j + 1], seq_logits[j])
+    torch.cuda.synchronize()
+    assert torch.max(torch.abs(seq_logits - o2["logits"])).item() <= TOL["f32"]
+    assert torch.max(torch.abs(kv2.k.float() - kv.k.float())).item() <= TOL["f32"]
+    lseq = oracle.sequential(cfg, Wn, okv_seq, L, span)
+    assert np.max(np.abs(seq_logits.cpu().numpy() - lseq)) <= TOL["f32"]
+
+
+def test_tiny_fp32_planted_verify():
+    """VERIFY accepts a span planted from the oracle's greedy chain whole and
+    stops exactly at a corrupted position."""
+    dev = _dev()
+    shape = synth.TINY
+    cfg = Config.of(shape)
+    # wider weights make the greedy chain's top-2 margins clear 0.1
+    Wc = synth.make_weights(shape, seed=28, std=0.15)
+    Wn = synth.weights_to_numpy(Wc)
+    Wd = {k: (v.to(dev) if torch.is_tensor(v) else [{kk: vv.to(dev) for kk, vv in lw.items()} for lw in v])
+          for k, v in Wc.items()}
+    L, N = 64, 12
+    prompt = synth.uniform_prompt(L, shape.vocab, seed=22)
+    okv = KVCache.empty(1, 4, L + N, 64)
+    oracle.prefill(cfg, Wn, okv, prompt)
+    chain = okv.copy()
+    span = [5]
+    for j in range(N - 1):
+        span.append(int(oracle.masked_argmax(oracle.decode_step(cfg, Wn, chain, L + j, span[j])[None], None)[0]))
+    ref = oracle.splice(cfg, Wn, okv.copy(), L, span)
+    margin = oracle.top2_margin(ref, None)
+    if not (margin[:N - 1] > MARGIN).all():
+        pytest.skip("planted chain has a near-tie (margin <= 0.1); acceptance not graded")
+    nb = (L + N + 15) // 16
+    kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device=dev)
+    model = cad.cad_model_create(shape, Wd, max_tokens=L)
+    o = H.outputs(L, shape.vocab)
+    cad.cad_splice_forward(model, kv, 0, H.tensors_i32(prompt), None, cad.CAD_COMMIT, o["argmax"], o["accepted"])
+    for bad_at in (None, 1, 5, N - 1):
+        s = list(span)
+        if bad_at is not None:
+            s[bad_at] = (s[bad_at] + 1) % shape.vocab
+        o2 = H.outputs(N, shape.vocab)
+        cad.cad_splice_forward(model, kv, L, H.tensors_i32(s), None, cad.CAD_VERIFY, o2["argmax"], o2["accepted"])
+        torch.cuda.synchronize()
+        assert int(o2["accepted"][0]) == (N if bad_at is None else bad_at)
+
+
+# ---------------------------------------------------------------------------
+# bf16: the 1B shape over a random prefix cache of L = 4096
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def llama1b():
+    dev = _dev()
+    shape = synth.LLAMA_1B
+    W = synth.make_weights(shape, seed=synth.SEED_WEIGHTS, device=dev)
+    Wn = synth.weights_to_numpy(W)
+    L = 4096
+    kl, vl = synth.random_kv_logical(shape, L, device=dev)
+    return shape, W, Wn, L, kl, vl
+
+
+@pytest.mark.parametrize("N", [1, 4, 8, 16, 64, 256])
+def test_llama1b_bf16_splice(llama1b, N):
+    dev = _dev()
+    shape, W, Wn, L, kl, vl = llama1b
+    cfg = Config.of(shape)
+    prompt = synth.make_line_prompt(L, shape.vocab)
+    span = synth.pick_span(prompt, N)
+    nb = (L + 256 + 15) // 16 + 1
+    kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device=dev)
+    kv.k.fill_(7.0)
+    kv.v.fill_(7.0)
+    H.write_prefix(kv, kl, vl)
+    k_before = kv.k.clone()
+    v_before = kv.v.clone()
+    model = cad.cad_model_create(shape, W, max_tokens=256)
+    o = H.outputs(N, shape.vocab)
+    cad.cad_splice_forward(model, kv, L, H.tensors_i32(span), None, cad.CAD_VERIFY, o["argmax"], o["accepted"],
+                           o["logits"], o["status"])
+    okv = KVCache.from_prefix(kl.float().cpu().numpy(), vl.float().cpu().numpy(), L + N)
+    ref = oracle.splice(cfg, Wn, okv, L, span)
+    torch.cuda.synchronize()
+    assert int(o["status"][0]) == 0
+    err = np.max(np.abs(o["logits"].cpu().numpy() - ref))
+    print(f"N={N} logits max|diff| = {err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+    check_decisions(ref, None, o["argmax"].cpu().numpy(), span, VERIFY, int(o["accepted"][0]))
+    gk, gv = H.read_seq(kv, L + N)
+    ek = np.max(np.abs(gk[:, :, L:] - np.stack([okv.k[c][:, L:L + N] for c in range(cfg.n_layers)])))
+    ev = np.max(np.abs(gv[:, :, L:] - np.stack([okv.v[c][:, L:L + N] for c in range(cfg.n_layers)])))
+    print(f"N={N} kv max|diff| = {ek:.3e} / {ev:.3e}", flush=True)
+    assert ek <= TOL["bf16"] and ev <= TOL["bf16"]
+    # canaries: the prefix and every slot past L + N are bit-unchanged
+    nfull = L // 16
+    assert torch.equal(kv.k[:, :nfull], k_before[:, :nfull])
+    assert torch.equal(kv.v[:, :nfull], v_before[:, :nfull])
+    end = L + N
+    eb = (end + 15) // 16
+    assert torch.equal(kv.k[:, eb:], k_before[:, eb:])
+    if end % 16:
+        assert torch.equal(kv.k[:, eb - 1, :, end % 16:], k_before[:, eb - 1, :, end % 16:])
+        assert torch.equal(kv.v[:, eb - 1, :, :, end % 16:], v_before[:, eb - 1, :, :, end % 16:])
+
+
+def test_llama1b_splice_equals_decode_steps(llama1b):
+    dev = _dev()
+    shape, W, Wn, L, kl, vl = llama1b
+    N = 8
+    prompt = synth.make_line_prompt(L, shape.vocab)
+    span = synth.pick_span(prompt, N, which=3)
+    nb = (L + N + 15) // 16
+    kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device=dev)
+    H.write_prefix(kv, kl, vl)
+    kv2 = cad.KVCache(kv.k.clone(), kv.v.clone(), kv.block_table)
+    model = cad.cad_model_create(shape, W, max_tokens=N)
+    o = H.outputs(N, shape.vocab)
+    span_t = H.tensors_i32(span)
+    cad.cad_splice_forward(model, kv, L, span_t, None, cad.CAD_COMMIT, o["argmax"], o["accepted"], o["logits"])
+    lg = torch.empty((N, shape.vocab), dtype=torch.float32, device=dev)
+    am = torch.empty(N, dtype=torch.int32, device=dev)
+    for j in range(N):
+        cad.cad_decode_step(model, kv2, L + j, span_t[j:j + 1], None, am[j:j + 1], lg[j])
+    torch.cuda.synchronize()
+    assert torch.max(torch.abs(lg - o["logits"])).item() <= TOL["bf16"]
+    assert torch.max(torch.abs(kv2.k.float() - kv.k.float())).item() <= TOL["bf16"]
+    assert torch.max(torch.abs(kv2.v.float() - kv.v.float())).item() <= TOL["bf16"]
+
+
+def test_deterministic_rerun(llama1b):
+    dev = _dev()
+    shape, W, Wn, L, kl, vl = llama1b
+    N = 64
+    prompt = synth.make_line_prompt(L, shape.vocab)
+    span = H.tensors_i32(synth.pick_span(prompt, N, which=5))
+    nb = (L + N + 15) // 16
+    kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device=dev)
+    H.write_prefix(kv, kl, vl)
+    model = cad.cad_model_create(shape, W, max_tokens=N)
+    res = []
+    for _ in range(2):
+        o = H.outputs(N, shape.vocab)
+        cad.cad_splice_forward(model, kv, L, span, None, cad.CAD_COMMIT, o["argmax"], o["accepted"], o["logits"])
+        torch.cuda.synchronize()
+        res.append(o["logits"].clone())
+    assert torch.equal(res[0], res[1])

@@ -1,0 +1,239 @@
+"""Python binding of libcad (the copy-span splice forward on MI355X).
+
+Argument marshalling only: every entry point here forwards to the C function
+of the same name in ``libcad.so`` (declared in ``include/cad.h``), passing
+device pointers of caller-owned torch tensors and the current HIP stream.
+No step of the computation runs in Python or PyTorch, and nothing falls back
+to a CPU path: if the library is missing, importing the entry points raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcad.so")
+
+CAD_F32, CAD_BF16 = 0, 1
+CAD_COMMIT, CAD_VERIFY = 0, 1
+CAD_OK, CAD_E_ARG, CAD_E_CAPACITY, CAD_E_UNSUPPORTED, CAD_E_HIP = 0, 1, 2, 3, 4
+CAD_DEV_BAD_TOKEN, CAD_DEV_EMPTY_MASK, CAD_DEV_BAD_BLOCK = 1, 2, 4
+CAD_KV_BLOCK = 16
+CAD_MAX_SEQS = 64
+
+EXPORTS = ("cad_model_create", "cad_model_destroy", "cad_last_error", "cad_splice_forward",
+           "cad_decode_step", "cad_propose_suffix_match", "cad_splice_forward_batched",
+           "cad_splice_forward_looped")
+
+
+class CadError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"cad status {status}: {msg}")
+        self.status = status
+
+
+class cad_config(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("ffn_dim", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("loop_depth", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float),
+                ("dtype", ctypes.c_int32), ("max_tokens", ctypes.c_int32)]
+
+
+_VP = ctypes.c_void_p
+_VPP = ctypes.POINTER(ctypes.c_void_p)
+
+
+class cad_weights(ctypes.Structure):
+    _fields_ = [("tok_embed", _VP), ("final_norm", _VP), ("lm_head", _VP),
+                ("attn_norm", _VPP), ("w_qkv", _VPP), ("w_o", _VPP), ("ffn_norm", _VPP),
+                ("w_gate_up", _VPP), ("w_down", _VPP)]
+
+
+class cad_kv(ctypes.Structure):
+    _fields_ = [("k", _VP), ("v", _VP), ("num_blocks", ctypes.c_int64),
+                ("block_table", _VP), ("max_blocks_per_seq", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libcad.so (built in-tree by ``verify_forward_amd/build.py``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python verify_forward_amd/build.py`")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
+        L.cad_model_create.argtypes = [ctypes.POINTER(cad_config), ctypes.POINTER(cad_weights), ctypes.POINTER(_VP)]
+        L.cad_model_destroy.argtypes = [_VP]
+        L.cad_model_destroy.restype = None
+        L.cad_last_error.restype = ctypes.c_char_p
+        L.cad_splice_forward.argtypes = [_VP, ctypes.POINTER(cad_kv), i64, _VP, i32, _VP, i32, _VP, _VP,
+                                         _VP, _VP, _VP]
+        L.cad_decode_step.argtypes = [_VP, ctypes.POINTER(cad_kv), i64, _VP, _VP, _VP, _VP, _VP, _VP]
+        L.cad_propose_suffix_match.argtypes = [_VP, i64, i32, i32, i32, _VP, _VP, _VP, _VP]
+        L.cad_splice_forward_batched.argtypes = [_VP, ctypes.POINTER(cad_kv), i32, _VP, _VP, _VP, _VP, i32,
+                                                 _VP, _VP, _VP, _VP, _VP]
+        L.cad_splice_forward_looped.argtypes = [_VP, ctypes.POINTER(cad_kv), i64, _VP, i32, i32, _VP, _VP,
+                                                _VP, _VP, _VP, _VP, _VP, _VP]
+        for name in ("cad_model_create", "cad_splice_forward", "cad_decode_step", "cad_propose_suffix_match",
+                     "cad_splice_forward_batched", "cad_splice_forward_looped"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def cad_last_error() -> str:
+    return lib().cad_last_error().decode()
+
+
+def _check(status: int):
+    if status != CAD_OK:
+        raise CadError(status, cad_last_error())
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ----------------------------------------------------------------------------
+# model
+# ----------------------------------------------------------------------------
+
+class Model:
+    """Owns a ``cad_model*`` and keeps the weight tensors alive."""
+
+    def __init__(self, handle, cfg: cad_config, weights, keep):
+        self.handle, self.cfg, self.weights, self._keep = handle, cfg, weights, keep
+
+    def __del__(self):
+        try:
+            if self.handle:
+                cad_model_destroy(self)
+        except Exception:
+            pass
+
+
+def make_config(shape, max_tokens: int) -> cad_config:
+    return cad_config(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
+                      shape.ffn_dim, shape.vocab, getattr(shape, "loop_depth", 1), float(shape.rope_theta),
+                      float(shape.rms_eps), CAD_BF16 if shape.dtype == "bf16" else CAD_F32, int(max_tokens))
+
+
+def cad_model_create(shape, weights, max_tokens: int) -> Model:
+    """``shape``: any object with the decoder fields; ``weights``: dict of device
+    tensors as produced by ``synth.make_weights`` (nn.Linear layout)."""
+    cfg = make_config(shape, max_tokens)
+    layers = weights["layers"]
+    arr = lambda key: (_VP * len(layers))(*[t.data_ptr() for t in (lw[key] for lw in layers)])
+    arrays = {k: arr(k) for k in ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_gate_up", "w_down")}
+    w = cad_weights(weights["tok_embed"].data_ptr(), weights["final_norm"].data_ptr(),
+                    weights["lm_head"].data_ptr(),
+                    *[ctypes.cast(arrays[k], _VPP) for k in ("attn_norm", "w_qkv", "w_o", "ffn_norm",
+                                                             "w_gate_up", "w_down")])
+    h = _VP()
+    _check(lib().cad_model_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h)))
+    return Model(h, cfg, weights, (arrays, w))
+
+
+def cad_model_destroy(model: Model):
+    if model.handle:
+        lib().cad_model_destroy(model.handle)
+        model.handle = None
+
+
+# ----------------------------------------------------------------------------
+# KV cache
+# ----------------------------------------------------------------------------
+
+class KVCache:
+    """Caller-owned paged cache: ``k [cache_layers][num_blocks][Hkv][16][hd]``,
+    ``v [cache_layers][num_blocks][Hkv][hd][16]`` and an int32 block table
+    ``[n_seq][max_blocks_per_seq]``."""
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, block_table: torch.Tensor):
+        assert k.is_contiguous() and v.is_contiguous() and block_table.is_contiguous()
+        assert block_table.dtype == torch.int32
+        self.k, self.v, self.block_table = k, v, block_table
+        self.num_blocks = k.shape[1]
+        self.max_blocks_per_seq = block_table.shape[-1]
+
+    @staticmethod
+    def alloc(shape, num_blocks: int, block_table: torch.Tensor, device="cuda") -> "KVCache":
+        cl = shape.n_layers * getattr(shape, "loop_depth", 1)
+        dt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+        k = torch.zeros((cl, num_blocks, shape.n_kv_heads, CAD_KV_BLOCK, shape.head_dim), dtype=dt, device=device)
+        v = torch.zeros((cl, num_blocks, shape.n_kv_heads, shape.head_dim, CAD_KV_BLOCK), dtype=dt, device=device)
+        return KVCache(k, v, block_table.to(device=device, dtype=torch.int32).contiguous())
+
+    def struct(self) -> cad_kv:
+        return cad_kv(self.k.data_ptr(), self.v.data_ptr(), self.num_blocks, self.block_table.data_ptr(),
+                      self.max_blocks_per_seq)
+
+
+# ----------------------------------------------------------------------------
+# entry points
+# ----------------------------------------------------------------------------
+
+def cad_splice_forward(model: Model, kv: KVCache, L: int, span: torch.Tensor, mask: Optional[torch.Tensor],
+                       mode: int, argmax: torch.Tensor, accepted: torch.Tensor,
+                       logits: Optional[torch.Tensor] = None, dev_status: Optional[torch.Tensor] = None,
+                       stream=None):
+    s = kv.struct()
+    _check(lib().cad_splice_forward(model.handle, ctypes.byref(s), int(L), _p(span), int(span.numel()),
+                                    _p(mask), int(mode), _p(argmax), _p(accepted), _p(logits),
+                                    _p(dev_status), _stream(stream)))
+
+
+def cad_decode_step(model: Model, kv: KVCache, L: int, token: torch.Tensor, mask_row: Optional[torch.Tensor],
+                    argmax: torch.Tensor, logits: Optional[torch.Tensor] = None,
+                    dev_status: Optional[torch.Tensor] = None, stream=None):
+    s = kv.struct()
+    _check(lib().cad_decode_step(model.handle, ctypes.byref(s), int(L), _p(token), _p(mask_row), _p(argmax),
+                                 _p(logits), _p(dev_status), _stream(stream)))
+
+
+def cad_propose_suffix_match(tokens: torch.Tensor, max_ngram: int, min_ngram: int, K: int,
+                             out_tokens: torch.Tensor, out_len: torch.Tensor, out_pos: torch.Tensor,
+                             stream=None, T: Optional[int] = None):
+    n = tokens.numel() if T is None else int(T)
+    _check(lib().cad_propose_suffix_match(_p(tokens) if n > 0 else None, n, int(max_ngram), int(min_ngram),
+                                          int(K), _p(out_tokens), _p(out_len), _p(out_pos), _stream(stream)))
+
+
+def cad_splice_forward_batched(model: Model, kv: KVCache, seq_L: Sequence[int], offsets: Sequence[int],
+                               spans: torch.Tensor, mask: Optional[torch.Tensor], mode: int,
+                               argmax: torch.Tensor, accepted: torch.Tensor,
+                               logits: Optional[torch.Tensor] = None,
+                               dev_status: Optional[torch.Tensor] = None, stream=None):
+    n = len(seq_L)
+    Ls = (ctypes.c_int64 * n)(*[int(x) for x in seq_L])
+    offs = (ctypes.c_int32 * (n + 1))(*[int(x) for x in offsets])
+    s = kv.struct()
+    _check(lib().cad_splice_forward_batched(model.handle, ctypes.byref(s), n, ctypes.cast(Ls, _VP),
+                                            ctypes.cast(offs, _VP), _p(spans), _p(mask), int(mode), _p(argmax),
+                                            _p(accepted), _p(logits), _p(dev_status), _stream(stream)))
+
+
+def cad_splice_forward_looped(model: Model, kv: KVCache, L: int, span: torch.Tensor, screen_depth: int,
+                              mask: Optional[torch.Tensor], screen_argmax: torch.Tensor,
+                              survivors: torch.Tensor, argmax: torch.Tensor, accepted: torch.Tensor,
+                              logits: Optional[torch.Tensor] = None,
+                              dev_status: Optional[torch.Tensor] = None, stream=None):
+    s = kv.struct()
+    _check(lib().cad_splice_forward_looped(model.handle, ctypes.byref(s), int(L), _p(span), int(span.numel()),
+                                           int(screen_depth), _p(mask), _p(screen_argmax), _p(survivors),
+                                           _p(argmax), _p(accepted), _p(logits), _p(dev_status),
+                                           _stream(stream)))

@@ -1,0 +1,420 @@
+// Host side of libcad: argument validation, workspace ownership and the
+// launch sequence of the splice forward.  Every compute step is one of the
+// HIP kernels in k_*.hip; this file only decides what runs, in which order,
+// on which buffers.
+//
+// One splice forward (Copy-as-Decode §2.4; CopyLoop §2) enqueues:
+//   embedding gather
+//   per cache index (layer, or depth of a looped block):
+//     RMSNorm -> QKV projection -> rotary + KV append -> span attention
+//     -> O projection (+residual) -> RMSNorm -> gate/up projection (SwiGLU)
+//     -> down projection (+residual)
+//   final RMSNorm -> LM head -> masked argmax -> acceptance
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "cad_internal.h"
+
+using namespace cad;
+
+namespace {
+
+thread_local std::string g_err;
+
+cad_status fail(cad_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+cad_status fail(cad_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+struct cad_model {
+  cad_config cfg;
+  int esize;  // bytes per weight / cache element
+  // weights (caller-owned)
+  const void* tok_embed;
+  const void* final_norm;
+  const void* lm_head;
+  std::vector<const void*> attn_norm, w_qkv, w_o, ffn_norm, w_gate_up, w_down;
+  // workspace (library-owned, one allocation)
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  float* x = nullptr;        // [T][d] residual stream
+  void* hn = nullptr;        // [T][d] normalised activations (model dtype)
+  float* qkv = nullptr;      // [T][(hq+2hkv) hd]
+  void* q = nullptr;         // [T][hq][hd] rotated queries
+  void* attn = nullptr;      // [T][hq hd] attention output
+  void* act = nullptr;       // [T][F] SwiGLU activation
+  float* logits = nullptr;   // [T][V]
+  float* part_o = nullptr;   // attention partials
+  float* part_ml = nullptr;
+  int64_t part_cap = 0;      // floats available per part_o "row-head-dim" budget
+  double* freq = nullptr;    // [hd/2] rotary frequencies
+  int32_t* scratch_i = nullptr;  // [T] argmax of the screening readout
+  int32_t* survivors = nullptr;  // [1] screening survivors when the caller passes none
+};
+
+namespace {
+
+size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+cad_status check_config(const cad_config* c) {
+  if (!c) return fail(CAD_E_ARG, "cfg is NULL");
+  if (c->n_layers < 1 || c->d_model < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 ||
+      c->head_dim < 2 || c->ffn_dim < 1 || c->vocab < 1 || c->loop_depth < 1 || c->max_tokens < 1)
+    return fail(CAD_E_ARG, "non-positive dimension in cfg");
+  if (c->dtype != CAD_F32 && c->dtype != CAD_BF16) return fail(CAD_E_ARG, "bad dtype %d", c->dtype);
+  if (c->n_q_heads % c->n_kv_heads) return fail(CAD_E_ARG, "n_q_heads not a multiple of n_kv_heads");
+  if (c->loop_depth > 1 && c->n_layers != 1) return fail(CAD_E_ARG, "looped model needs n_layers == 1");
+  if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) return fail(CAD_E_ARG, "bad rope_theta or rms_eps");
+  if (c->head_dim % 2) return fail(CAD_E_UNSUPPORTED, "odd head_dim");
+  if (c->dtype == CAD_F32) {
+    if (c->head_dim > 128) return fail(CAD_E_UNSUPPORTED, "fp32 path supports head_dim <= 128");
+  } else {
+    if (c->head_dim != 64 && c->head_dim != 128)
+      return fail(CAD_E_UNSUPPORTED, "bf16 path supports head_dim 64 or 128");
+    if (c->d_model % 64 || c->ffn_dim % 64 || (c->n_q_heads * c->head_dim) % 64)
+      return fail(CAD_E_UNSUPPORTED, "bf16 path needs d_model, ffn_dim, n_q_heads*head_dim multiples of 64");
+  }
+  if (c->max_tokens > (1 << 20)) return fail(CAD_E_CAPACITY, "max_tokens too large");
+  return CAD_OK;
+}
+
+int64_t max_parts_rows(const cad_config& c) {
+  // largest n_parts * rows over every row count a call may carry
+  int64_t best = 0;
+  for (int r = 1; r <= c.max_tokens; ++r) {
+    int len = 0;
+    const int p = attention_parts(r, c.n_q_heads, c.n_kv_heads, (int64_t)1 << 40, &len);
+    if (p > 1 && (int64_t)p * r > best) best = (int64_t)p * r;
+  }
+  return best;
+}
+
+#define HIP_TRY(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess) return fail(CAD_E_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+cad_status check_kv(const cad_model* m, const cad_kv* kv) {
+  if (!kv) return fail(CAD_E_ARG, "kv is NULL");
+  if (!kv->k || !kv->v || !kv->block_table) return fail(CAD_E_ARG, "kv buffers are NULL");
+  if (kv->num_blocks < 1 || kv->max_blocks_per_seq < 1) return fail(CAD_E_ARG, "empty kv pool");
+  if (m->cfg.dtype == CAD_BF16 && (!aligned16(kv->k) || !aligned16(kv->v)))
+    return fail(CAD_E_ARG, "kv pools must be 16-byte aligned");
+  return CAD_OK;
+}
+
+KVView view_of(const cad_model* m, const cad_kv* kv, int ci) {
+  const cad_config& c = m->cfg;
+  const int64_t per = kv->num_blocks * c.n_kv_heads * CAD_KV_BLOCK * c.head_dim * m->esize;
+  KVView v;
+  v.k = (char*)kv->k + per * ci;
+  v.v = (char*)kv->v + per * ci;
+  v.table = kv->block_table;
+  v.num_blocks = kv->num_blocks;
+  v.max_blocks = kv->max_blocks_per_seq;
+  return v;
+}
+
+// Run cache indices [c0, c1) over the rows already embedded in m->x.
+cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, int c1,
+                      const int32_t* write_limit, int32_t* dev_status, hipStream_t s) {
+  const cad_config& c = m->cfg;
+  const int R = rm.total;
+  const int d = c.d_model, hq = c.n_q_heads, hkv = c.n_kv_heads, hd = c.head_dim, F = c.ffn_dim;
+  const int qkv_rows = (hq + 2 * hkv) * hd;
+  int64_t max_keys = 0;
+  for (int b = 0; b < rm.n_seq; ++b) {
+    const int64_t e = rm.L[b] + (rm.start[b + 1] - rm.start[b]);
+    if (e > max_keys) max_keys = e;
+  }
+  int part_len = 0;
+  int n_parts = attention_parts(R, hq, hkv, max_keys, &part_len);
+  if ((int64_t)n_parts * R > m->part_cap) n_parts = 1, part_len = (int)max_keys + 64;
+  for (int ci = c0; ci < c1; ++ci) {
+    const int li = c.loop_depth > 1 ? 0 : ci;
+    const KVView v = view_of(m, kv, ci);
+    HIP_TRY(launch_rmsnorm(c.dtype, m->x, m->attn_norm[li], R, d, c.rms_eps, m->hn, s));
+    GemmArgs g{};
+    g.A = m->hn; g.lda = d; g.W = m->w_qkv[li]; g.ldw = d;
+    g.M = R; g.N = qkv_rows; g.K = d; g.out_f32 = m->qkv; g.ldo = qkv_rows;
+    HIP_TRY(launch_gemm(c.dtype, EPI_STORE_F32, g, s));
+    HIP_TRY(launch_rope_append(c.dtype, m->qkv, R, hq, hkv, hd, m->freq, rm, v, write_limit, m->q,
+                               dev_status, s));
+    HIP_TRY(launch_attention(c.dtype, m->q, R, hq, hkv, hd, rm, v, n_parts, part_len, m->part_o,
+                             m->part_ml, m->attn, dev_status, s));
+    g = GemmArgs{};
+    g.A = m->attn; g.lda = hq * hd; g.W = m->w_o[li]; g.ldw = hq * hd;
+    g.M = R; g.N = d; g.K = hq * hd; g.out_f32 = m->x; g.ldo = d;
+    HIP_TRY(launch_gemm(c.dtype, EPI_RESID, g, s));
+    HIP_TRY(launch_rmsnorm(c.dtype, m->x, m->ffn_norm[li], R, d, c.rms_eps, m->hn, s));
+    g = GemmArgs{};
+    g.A = m->hn; g.lda = d; g.W = m->w_gate_up[li]; g.ldw = d;
+    g.M = R; g.N = F; g.K = d; g.up_off = F; g.out_act = m->act;
+    HIP_TRY(launch_gemm(c.dtype, EPI_SWIGLU, g, s));
+    g = GemmArgs{};
+    g.A = m->act; g.lda = F; g.W = m->w_down[li]; g.ldw = F;
+    g.M = R; g.N = d; g.K = F; g.out_f32 = m->x; g.ldo = d;
+    HIP_TRY(launch_gemm(c.dtype, EPI_RESID, g, s));
+  }
+  return CAD_OK;
+}
+
+// final norm + LM head + masked argmax
+cad_status readout(cad_model* m, int R, float* logits, const uint32_t* mask, int32_t* argmax,
+                   int32_t* dev_status, hipStream_t s) {
+  const cad_config& c = m->cfg;
+  HIP_TRY(launch_rmsnorm(c.dtype, m->x, m->final_norm, R, c.d_model, c.rms_eps, m->hn, s));
+  GemmArgs g{};
+  g.A = m->hn; g.lda = c.d_model; g.W = m->lm_head; g.ldw = c.d_model;
+  g.M = R; g.N = c.vocab; g.K = c.d_model; g.out_f32 = logits; g.ldo = c.vocab;
+  HIP_TRY(launch_gemm(c.dtype, EPI_STORE_F32, g, s));
+  HIP_TRY(launch_argmax(logits, R, c.vocab, mask, argmax, dev_status, s));
+  return CAD_OK;
+}
+
+cad_status check_common(cad_model* m, const cad_kv* kv, const int32_t* span, const int32_t* argmax,
+                        const int32_t* accepted, const float* logits, int mode) {
+  if (!m) return fail(CAD_E_ARG, "model is NULL");
+  cad_status st = check_kv(m, kv);
+  if (st != CAD_OK) return st;
+  if (!span) return fail(CAD_E_ARG, "span is NULL");
+  if (!argmax || !accepted) return fail(CAD_E_ARG, "argmax/accepted is NULL");
+  if (mode != CAD_COMMIT && mode != CAD_VERIFY) return fail(CAD_E_ARG, "bad mode %d", mode);
+  if (logits && !aligned16(logits)) return fail(CAD_E_ARG, "logits must be 16-byte aligned");
+  return CAD_OK;
+}
+
+cad_status check_seq(const cad_kv* kv, int64_t L, int64_t N, int max_tokens) {
+  if (N < 1) return fail(CAD_E_ARG, "span length %lld < 1", (long long)N);
+  if (N > max_tokens) return fail(CAD_E_CAPACITY, "span length %lld > max_tokens %d", (long long)N, max_tokens);
+  if (L < 0) return fail(CAD_E_ARG, "negative cache length");
+  if (L + N > (int64_t)kv->max_blocks_per_seq * CAD_KV_BLOCK)
+    return fail(CAD_E_CAPACITY, "L + N = %lld exceeds the block table (%d blocks of %d)",
+                (long long)(L + N), kv->max_blocks_per_seq, CAD_KV_BLOCK);
+  return CAD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cad_last_error(void) { return g_err.c_str(); }
+
+cad_status cad_model_create(const cad_config* cfg, const cad_weights* w, cad_model** out) {
+  if (!out) return fail(CAD_E_ARG, "out is NULL");
+  *out = nullptr;
+  cad_status st = check_config(cfg);
+  if (st != CAD_OK) return st;
+  if (!w || !w->tok_embed || !w->final_norm || !w->lm_head || !w->attn_norm || !w->w_qkv || !w->w_o ||
+      !w->ffn_norm || !w->w_gate_up || !w->w_down)
+    return fail(CAD_E_ARG, "weights incomplete");
+  const cad_config& c = *cfg;
+  const bool need_align = c.dtype == CAD_BF16;
+  auto ok_ptr = [&](const void* p) { return p && (!need_align || aligned16(p)); };
+  if (!ok_ptr(w->tok_embed) || !ok_ptr(w->lm_head)) return fail(CAD_E_ARG, "embedding/head pointer NULL or misaligned");
+  for (int i = 0; i < c.n_layers; ++i)
+    if (!w->attn_norm[i] || !w->ffn_norm[i] || !ok_ptr(w->w_qkv[i]) || !ok_ptr(w->w_o[i]) ||
+        !ok_ptr(w->w_gate_up[i]) || !ok_ptr(w->w_down[i]))
+      return fail(CAD_E_ARG, "layer %d weight pointer NULL or misaligned", i);
+
+  cad_model* m = new (std::nothrow) cad_model();
+  if (!m) return fail(CAD_E_HIP, "host allocation failed");
+  m->cfg = c;
+  m->esize = c.dtype == CAD_BF16 ? 2 : 4;
+  m->tok_embed = w->tok_embed;
+  m->final_norm = w->final_norm;
+  m->lm_head = w->lm_head;
+  for (int i = 0; i < c.n_layers; ++i) {
+    m->attn_norm.push_back(w->attn_norm[i]);
+    m->w_qkv.push_back(w->w_qkv[i]);
+    m->w_o.push_back(w->w_o[i]);
+    m->ffn_norm.push_back(w->ffn_norm[i]);
+    m->w_gate_up.push_back(w->w_gate_up[i]);
+    m->w_down.push_back(w->w_down[i]);
+  }
+  const int64_t T = c.max_tokens, d = c.d_model, hq = c.n_q_heads, hkv = c.n_kv_heads,
+                hd = c.head_dim, F = c.ffn_dim, V = c.vocab;
+  const int64_t es = m->esize;
+  const int64_t pr = max_parts_rows(c);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  const size_t o_x = take(T * d * 4), o_hn = take(T * d * es), o_qkv = take(T * (hq + 2 * hkv) * hd * 4),
+               o_q = take(T * hq * hd * es), o_attn = take(T * hq * hd * es), o_act = take(T * F * es),
+               o_logits = take(T * V * 4), o_po = take(pr * hq * hd * 4), o_pml = take(pr * hq * 2 * 4),
+               o_freq = take(hd / 2 * 8), o_si = take(T * 4), o_sv = take(4);
+  hipError_t e = hipMalloc(&m->ws, off);
+  if (e != hipSuccess) {
+    delete m;
+    return fail(CAD_E_HIP, "hipMalloc(%zu): %s", off, hipGetErrorString(e));
+  }
+  m->ws_bytes = off;
+  char* base = (char*)m->ws;
+  m->x = (float*)(base + o_x);
+  m->hn = base + o_hn;
+  m->qkv = (float*)(base + o_qkv);
+  m->q = base + o_q;
+  m->attn = base + o_attn;
+  m->act = base + o_act;
+  m->logits = (float*)(base + o_logits);
+  m->part_o = (float*)(base + o_po);
+  m->part_ml = (float*)(base + o_pml);
+  m->part_cap = pr;
+  m->freq = (double*)(base + o_freq);
+  m->scratch_i = (int32_t*)(base + o_si);
+  m->survivors = (int32_t*)(base + o_sv);
+  std::vector<double> fr(hd / 2);
+  for (int64_t i = 0; i < hd / 2; ++i) fr[i] = std::pow((double)c.rope_theta, -2.0 * (double)i / (double)hd);
+  e = hipMemcpy(m->freq, fr.data(), fr.size() * 8, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    (void)hipFree(m->ws);
+    delete m;
+    return fail(CAD_E_HIP, "workspace init: %s", hipGetErrorString(e));
+  }
+  *out = m;
+  return CAD_OK;
+}
+
+void cad_model_destroy(cad_model* m) {
+  if (!m) return;
+  (void)hipDeviceSynchronize();
+  (void)hipFree(m->ws);
+  delete m;
+}
+
+cad_status cad_splice_forward(cad_model* m, const cad_kv* kv, int64_t L, const int32_t* span,
+                              int32_t N, const uint32_t* mask, int32_t mode, int32_t* argmax,
+                              int32_t* accepted, float* logits, int32_t* dev_status,
+                              cad_stream stream) {
+  cad_status st = check_common(m, kv, span, argmax, accepted, logits, mode);
+  if (st != CAD_OK) return st;
+  if (m->cfg.loop_depth > 1) return fail(CAD_E_ARG, "looped model: use cad_splice_forward_looped");
+  st = check_seq(kv, L, N, m->cfg.max_tokens);
+  if (st != CAD_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  RowMap rm{};
+  rm.n_seq = 1;
+  rm.total = N;
+  rm.start[0] = 0;
+  rm.start[1] = N;
+  rm.L[0] = L;
+  const cad_config& c = m->cfg;
+  HIP_TRY(launch_embed(c.dtype, m->tok_embed, c.vocab, c.d_model, span, N, m->x, dev_status, s));
+  st = run_blocks(m, kv, rm, 0, c.n_layers, nullptr, dev_status, s);
+  if (st != CAD_OK) return st;
+  st = readout(m, N, logits ? logits : m->logits, mask, argmax, dev_status, s);
+  if (st != CAD_OK) return st;
+  HIP_TRY(launch_accept(argmax, span, rm, mode, nullptr, accepted, s));
+  return CAD_OK;
+}
+
+cad_status cad_decode_step(cad_model* m, const cad_kv* kv, int64_t L, const int32_t* token,
+                           const uint32_t* mask_row, int32_t* argmax, float* logits,
+                           int32_t* dev_status, cad_stream stream) {
+  if (!m) return fail(CAD_E_ARG, "model is NULL");
+  return cad_splice_forward(m, kv, L, token, 1, mask_row, CAD_COMMIT, argmax, m->survivors, logits,
+                            dev_status, stream);
+}
+
+cad_status cad_splice_forward_batched(cad_model* m, const cad_kv* kv, int32_t n_seq,
+                                      const int64_t* seq_L, const int32_t* offsets,
+                                      const int32_t* spans, const uint32_t* mask, int32_t mode,
+                                      int32_t* argmax, int32_t* accepted, float* logits,
+                                      int32_t* dev_status, cad_stream stream) {
+  cad_status st = check_common(m, kv, spans, argmax, accepted, logits, mode);
+  if (st != CAD_OK) return st;
+  if (m->cfg.loop_depth > 1) return fail(CAD_E_ARG, "looped model: use cad_splice_forward_looped");
+  if (n_seq < 1 || n_seq > CAD_MAX_SEQS) return fail(CAD_E_ARG, "n_seq %d outside [1, %d]", n_seq, CAD_MAX_SEQS);
+  if (!seq_L || !offsets) return fail(CAD_E_ARG, "seq_L/offsets is NULL");
+  if (offsets[0] != 0) return fail(CAD_E_ARG, "offsets[0] must be 0");
+  RowMap rm{};
+  rm.n_seq = n_seq;
+  for (int b = 0; b < n_seq; ++b) {
+    const int64_t n = (int64_t)offsets[b + 1] - offsets[b];
+    if (n < 1) return fail(CAD_E_ARG, "sequence %d has no span rows", b);
+    st = check_seq(kv, seq_L[b], n, m->cfg.max_tokens);
+    if (st != CAD_OK) return st;
+    rm.start[b] = offsets[b];
+    rm.L[b] = seq_L[b];
+  }
+  rm.start[n_seq] = offsets[n_seq];
+  rm.total = offsets[n_seq];
+  if (rm.total > m->cfg.max_tokens)
+    return fail(CAD_E_CAPACITY, "total rows %d > max_tokens %d", rm.total, m->cfg.max_tokens);
+  hipStream_t s = (hipStream_t)stream;
+  const cad_config& c = m->cfg;
+  HIP_TRY(launch_embed(c.dtype, m->tok_embed, c.vocab, c.d_model, spans, rm.total, m->x, dev_status, s));
+  st = run_blocks(m, kv, rm, 0, c.n_layers, nullptr, dev_status, s);
+  if (st != CAD_OK) return st;
+  st = readout(m, rm.total, logits ? logits : m->logits, mask, argmax, dev_status, s);
+  if (st != CAD_OK) return st;
+  HIP_TRY(launch_accept(argmax, spans, rm, mode, nullptr, accepted, s));
+  return CAD_OK;
+}
+
+cad_status cad_splice_forward_looped(cad_model* m, const cad_kv* kv, int64_t L,
+                                     const int32_t* span, int32_t N, int32_t screen_depth,
+                                     const uint32_t* mask, int32_t* screen_argmax,
+                                     int32_t* survivors, int32_t* argmax, int32_t* accepted,
+                                     float* logits, int32_t* dev_status, cad_stream stream) {
+  cad_status st = check_common(m, kv, span, argmax, accepted, logits, CAD_VERIFY);
+  if (st != CAD_OK) return st;
+  const cad_config& c = m->cfg;
+  if (c.loop_depth < 2) return fail(CAD_E_ARG, "model is not looped (loop_depth < 2)");
+  if (screen_depth < 1 || screen_depth > c.loop_depth)
+    return fail(CAD_E_ARG, "screen_depth %d outside [1, %d]", screen_depth, c.loop_depth);
+  if (!screen_argmax || !survivors) return fail(CAD_E_ARG, "screen_argmax/survivors is NULL");
+  st = check_seq(kv, L, N, c.max_tokens);
+  if (st != CAD_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  RowMap rm{};
+  rm.n_seq = 1;
+  rm.total = N;
+  rm.start[1] = N;
+  rm.L[0] = L;
+  HIP_TRY(launch_embed(c.dtype, m->tok_embed, c.vocab, c.d_model, span, N, m->x, dev_status, s));
+  st = run_blocks(m, kv, rm, 0, screen_depth, nullptr, dev_status, s);
+  if (st != CAD_OK) return st;
+  st = readout(m, N, m->logits, mask, screen_argmax, dev_status, s);
+  if (st != CAD_OK) return st;
+  HIP_TRY(launch_accept(screen_argmax, span, rm, CAD_VERIFY, nullptr, survivors, s));
+  st = run_blocks(m, kv, rm, screen_depth, c.loop_depth, survivors, dev_status, s);
+  if (st != CAD_OK) return st;
+  st = readout(m, N, logits ? logits : m->logits, mask, argmax, dev_status, s);
+  if (st != CAD_OK) return st;
+  HIP_TRY(launch_mask_rows(argmax, N, survivors, s));
+  HIP_TRY(launch_accept(argmax, span, rm, CAD_VERIFY, survivors, accepted, s));
+  return CAD_OK;
+}
+
+cad_status cad_propose_suffix_match(const int32_t* tokens, int64_t T, int32_t max_ngram,
+                                    int32_t min_ngram, int32_t K, int32_t* out_tokens,
+                                    int32_t* out_len, int64_t* out_pos, cad_stream stream) {
+  if (T < 0) return fail(CAD_E_ARG, "negative history length");
+  if (T > 0 && !tokens) return fail(CAD_E_ARG, "tokens is NULL");
+  if (!out_tokens || !out_len || !out_pos) return fail(CAD_E_ARG, "output pointer is NULL");
+  if (min_ngram < 1 || max_ngram < min_ngram || max_ngram > 64)
+    return fail(CAD_E_ARG, "need 1 <= min_ngram <= max_ngram <= 64");
+  if (K < 1) return fail(CAD_E_ARG, "K must be >= 1");
+  HIP_TRY(launch_suffix_match(tokens, T, max_ngram, min_ngram, K, out_tokens, out_len, out_pos,
+                              (hipStream_t)stream));
+  return CAD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+// Internal declarations shared by the HIP kernels and the host entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cad.h"
+
+namespace cad {
+
+typedef uint16_t bf16_t;  // bfloat16 bits: weights and KV cache of a bf16 model
+typedef _Float16 f16_t;   // half: matrix-core operands (activations, q, P) of a bf16 model
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float -> bf16, round to nearest even (finite inputs)
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// float -> half, round to nearest even, saturated to the finite range
+__device__ __forceinline__ f16_t f2h(float f) { return (f16_t)fminf(fmaxf(f, -65504.f), 65504.f); }
+
+// eight bf16 values (one 16-byte load) -> eight halves.  bf16 -> fp32 is a
+// shift; fp32 -> half is exact for every bf16 value in the half normal range
+// (half carries three more mantissa bits), truncation only touches values
+// below 2^-17 and saturates above 65504.
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(v[i] << 16);
+    const float hi = __uint_as_float(v[i] & 0xFFFF0000u);
+    r[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
+  return r;
+}
+
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a), as_f16x8(b), c, 0, 0, 0);
+}
+
+template <typename T> __device__ __forceinline__ float to_f(T v);
+template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t v) { return bf2f(v); }
+template <> __device__ __forceinline__ float to_f<f16_t>(f16_t v) { return (float)v; }
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
+template <> __device__ __forceinline__ f16_t from_f<f16_t>(float v) { return f2h(v); }
+
+// Which sequence each span row belongs to and at which absolute position it
+// sits.  Passed by value to the kernels (fits the kernel-argument segment).
+struct RowMap {
+  int32_t n_seq;
+  int32_t total;
+  int32_t start[CAD_MAX_SEQS + 1];  // CSR row offsets
+  int64_t L[CAD_MAX_SEQS];          // cache length before the call
+};
+
+__device__ __forceinline__ int row_seq(const RowMap& rm, int r) {
+  int b = 0;
+  while (b + 1 < rm.n_seq && rm.start[b + 1] <= r) ++b;
+  return b;
+}
+
+// KV pool view for one cache index (layer or depth).
+struct KVView {
+  void* k;               // [num_blocks][Hkv][16][hd]
+  void* v;               // [num_blocks][Hkv][hd][16]
+  const int32_t* table;  // [n_seq][max_blocks]
+  int64_t num_blocks;
+  int32_t max_blocks;
+};
+
+enum Epi { EPI_STORE_F32 = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+
+struct GemmArgs {
+  const void* A;   // activations [M][lda]
+  int64_t lda;
+  const void* W;   // weight rows [rows][ldw]
+  int64_t ldw;
+  int M, N, K;     // N = logical output columns (SWIGLU: ffn width)
+  int64_t up_off;  // SWIGLU: first row of the "up" half
+  float* out_f32;  // STORE_F32 / RESID destination [M][ldo]
+  int64_t ldo;
+  void* out_act;   // SWIGLU destination [M][N], element type = model dtype
+};
+
+// ---- launchers (stream-ordered, no host sync) ----
+hipError_t launch_embed(int dtype, const void* table, int vocab, int d, const int32_t* tokens,
+                        int rows, float* x, int32_t* status, hipStream_t s);
+hipError_t launch_rmsnorm(int dtype, const float* x, const void* gain, int rows, int d, float eps,
+                          void* out, hipStream_t s);
+hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s);
+hipError_t launch_rope_append(int dtype, const float* qkv, int rows, int hq, int hkv, int hd,
+                              const double* freq, const RowMap& rm, KVView kv,
+                              const int32_t* write_limit, void* q_out, int32_t* status,
+                              hipStream_t s);
+hipError_t launch_attention(int dtype, const void* q, int rows, int hq, int hkv, int hd,
+                            const RowMap& rm, KVView kv, int n_parts, int part_len,
+                            float* part_o, float* part_ml, void* out, int32_t* status,
+                            hipStream_t s);
+hipError_t launch_argmax(const float* logits, int rows, int vocab, const uint32_t* mask,
+                         int32_t* out, int32_t* status, hipStream_t s);
+hipError_t launch_accept(const int32_t* argmax, const int32_t* span, const RowMap& rm, int mode,
+                         const int32_t* limit, int32_t* accepted, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
+// argmax[r] = -1 for rows r >= *limit
+hipError_t launch_mask_rows(int32_t* argmax, int rows, const int32_t* limit, hipStream_t s);
+hipError_t launch_suffix_match(const int32_t* tokens, int64_t T, int max_n, int min_n, int K,
+                               int32_t* out_tokens, int32_t* out_len, int64_t* out_pos,
+                               hipStream_t s);
+
+// attention split: partitions of the key axis so that small spans still fill the chip
+int attention_parts(int rows, int hq, int hkv, int64_t max_keys, int* part_len);
+
+}  // namespace cad

@@ -1,0 +1,307 @@
+// Row-wise kernels of the splice path: embedding gather, RMSNorm, rotary
+// positions + KV append, masked argmax, acceptance scan and the suffix-match
+// proposal.  All are bandwidth- or latency-bound; one work-group per row.
+#include "cad_internal.h"
+
+namespace cad {
+
+constexpr int ROW_THREADS = 256;
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  const int nw = blockDim.x >> 6;
+  for (int i = 0; i < nw; ++i) t += red[i];  // fixed order: reproducible
+  __syncthreads();
+  return t;
+}
+
+// ---------------------------------------------------------------------------
+// embedding gather: x[r] = E[token[r]] widened to fp32 (the residual stream)
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void k_embed(const T* __restrict__ table, int vocab, int d, const int32_t* __restrict__ tok,
+                        float* __restrict__ x, int32_t* status) {
+  const int r = blockIdx.x;
+  const int t = tok[r];
+  const bool ok = t >= 0 && t < vocab;
+  if (!ok && threadIdx.x == 0 && status) atomicOr(status, (int32_t)CAD_DEV_BAD_TOKEN);
+  const T* src = table + (int64_t)(ok ? t : 0) * d;
+  float* dst = x + (int64_t)r * d;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) dst[i] = ok ? to_f<T>(src[i]) : 0.f;
+}
+
+hipError_t launch_embed(int dtype, const void* table, int vocab, int d, const int32_t* tokens,
+                        int rows, float* x, int32_t* status, hipStream_t s) {
+  if (dtype == CAD_BF16)
+    hipLaunchKernelGGL(k_embed<bf16_t>, dim3(rows), dim3(ROW_THREADS), 0, s,
+                       (const bf16_t*)table, vocab, d, tokens, x, status);
+  else
+    hipLaunchKernelGGL(k_embed<float>, dim3(rows), dim3(ROW_THREADS), 0, s, (const float*)table,
+                       vocab, d, tokens, x, status);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm: out[r] = x[r] / sqrt(mean(x[r]^2) + eps) * g, rounded to the
+// operand type of the next projection (half for bf16 models)
+// ---------------------------------------------------------------------------
+template <typename T, typename TO>
+__global__ void k_rmsnorm(const float* __restrict__ x, const T* __restrict__ g, int d, float eps,
+                          TO* __restrict__ out) {
+  __shared__ float red[16];
+  const int r = blockIdx.x;
+  const float* xr = x + (int64_t)r * d;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) ss += xr[i] * xr[i];
+  ss = block_sum(ss, red);
+  const float rs = 1.0f / sqrtf(ss / (float)d + eps);
+  TO* o = out + (int64_t)r * d;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) o[i] = from_f<TO>(xr[i] * rs * to_f<T>(g[i]));
+}
+
+hipError_t launch_rmsnorm(int dtype, const float* x, const void* gain, int rows, int d, float eps,
+                          void* out, hipStream_t s) {
+  if (dtype == CAD_BF16)
+    hipLaunchKernelGGL((k_rmsnorm<bf16_t, f16_t>), dim3(rows), dim3(ROW_THREADS), 0, s, x,
+                       (const bf16_t*)gain, d, eps, (f16_t*)out);
+  else
+    hipLaunchKernelGGL((k_rmsnorm<float, float>), dim3(rows), dim3(ROW_THREADS), 0, s, x,
+                       (const float*)gain, d, eps, (float*)out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// rotary positions on q and k (half-split pairs, angle pos * freq[i] formed
+// in fp64), q to the attention operand buffer (type TQ), k and v appended to
+// the paged cache (type T) at the row's absolute position.  Rows at or beyond
+// *write_limit do not touch the cache.
+// ---------------------------------------------------------------------------
+template <typename T, typename TQ>
+__global__ void k_rope_append(const float* __restrict__ qkv, int hq, int hkv, int hd,
+                              const double* __restrict__ freq, RowMap rm, KVView kv,
+                              const int32_t* write_limit, TQ* __restrict__ q_out, int32_t* status) {
+  const int r = blockIdx.x;
+  const int b = row_seq(rm, r);
+  const int local = r - rm.start[b];
+  const int64_t pos = rm.L[b] + local;
+  const int half = hd / 2;
+  const int width = (hq + 2 * hkv) * hd;
+  const float* src = qkv + (int64_t)r * width;
+  bool write_kv = write_limit == nullptr || local < *write_limit;
+  int64_t blk = 0;
+  if (write_kv) {
+    blk = kv.table[(int64_t)b * kv.max_blocks + pos / CAD_KV_BLOCK];
+    if (blk < 0 || blk >= kv.num_blocks) {
+      if (threadIdx.x == 0 && status) atomicOr(status, (int32_t)CAD_DEV_BAD_BLOCK);
+      write_kv = false;
+    }
+  }
+  const int slot = (int)(pos % CAD_KV_BLOCK);
+  T* kc = (T*)kv.k;
+  T* vc = (T*)kv.v;
+  // rotations: q heads then k heads, one (head, pair) per item
+  const int n_rot = (hq + hkv) * half;
+  for (int it = threadIdx.x; it < n_rot; it += blockDim.x) {
+    const int h = it / half, i = it % half;
+    double sn, cs;
+    sincos((double)pos * freq[i], &sn, &cs);
+    const float c = (float)cs, s = (float)sn;
+    const float a = src[h * hd + i], bb = src[h * hd + i + half];
+    const float ra = a * c - bb * s, rb = a * s + bb * c;
+    if (h < hq) {
+      TQ* qo = q_out + ((int64_t)r * hq + h) * hd;
+      qo[i] = from_f<TQ>(ra);
+      qo[i + half] = from_f<TQ>(rb);
+    } else if (write_kv) {
+      const int g = h - hq;
+      T* kd = kc + ((blk * hkv + g) * CAD_KV_BLOCK + slot) * hd;
+      kd[i] = from_f<T>(ra);
+      kd[i + half] = from_f<T>(rb);
+    }
+  }
+  if (write_kv) {
+    const float* vs = src + (hq + hkv) * hd;
+    for (int it = threadIdx.x; it < hkv * hd; it += blockDim.x) {
+      const int g = it / hd, dd = it % hd;
+      vc[((blk * hkv + g) * hd + dd) * CAD_KV_BLOCK + slot] = from_f<T>(vs[it]);
+    }
+  }
+}
+
+hipError_t launch_rope_append(int dtype, const float* qkv, int rows, int hq, int hkv, int hd,
+                              const double* freq, const RowMap& rm, KVView kv,
+                              const int32_t* write_limit, void* q_out, int32_t* status,
+                              hipStream_t s) {
+  if (dtype == CAD_BF16)
+    hipLaunchKernelGGL((k_rope_append<bf16_t, f16_t>), dim3(rows), dim3(ROW_THREADS), 0, s, qkv, hq, hkv,
+                       hd, freq, rm, kv, write_limit, (f16_t*)q_out, status);
+  else
+    hipLaunchKernelGGL((k_rope_append<float, float>), dim3(rows), dim3(ROW_THREADS), 0, s, qkv, hq, hkv,
+                       hd, freq, rm, kv, write_limit, (float*)q_out, status);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// masked argmax per row over fp32 logits: lowest id among equal maxima,
+// -1 (and CAD_DEV_EMPTY_MASK) when the row allows nothing
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return bi < 0 || v > bv || (v == bv && i < bi);
+}
+
+__global__ void k_argmax(const float* __restrict__ logits, int vocab, const uint32_t* __restrict__ mask,
+                         int32_t* __restrict__ out, int32_t* status) {
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  const int r = blockIdx.x;
+  const float* lg = logits + (int64_t)r * vocab;
+  const int words = (vocab + 31) / 32;
+  float bv = 0.f;
+  int bi = -1;
+  if (mask) {
+    const uint32_t* mr = mask + (int64_t)r * words;
+    for (int w = threadIdx.x; w < words; w += blockDim.x) {
+      uint32_t bits = mr[w];
+      while (bits) {
+        const int j = __builtin_ctz(bits);
+        bits &= bits - 1;
+        const int v = w * 32 + j;
+        if (v < vocab && better(lg[v], v, bv, bi)) { bv = lg[v]; bi = v; }
+      }
+    }
+  } else {
+    for (int v = threadIdx.x; v < vocab; v += blockDim.x)
+      if (better(lg[v], v, bv, bi)) { bv = lg[v]; bi = v; }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o);
+    const int oi = __shfl_xor(bi, o);
+    if (oi >= 0 && better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  if (l == 0) { sv[w] = bv; si[w] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 1; i < (int)(blockDim.x >> 6); ++i)
+      if (si[i] >= 0 && better(sv[i], si[i], bv, bi)) { bv = sv[i]; bi = si[i]; }
+    out[r] = bi;
+    if (bi < 0 && status) atomicOr(status, (int32_t)CAD_DEV_EMPTY_MASK);
+  }
+}
+
+hipError_t launch_argmax(const float* logits, int rows, int vocab, const uint32_t* mask,
+                         int32_t* out, int32_t* status, hipStream_t s) {
+  hipLaunchKernelGGL(k_argmax, dim3(rows), dim3(ROW_THREADS), 0, s, logits, vocab, mask, out, status);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// acceptance: COMMIT -> N; VERIFY -> 1 + leading j >= 1 with a[j-1] == s[j].
+// `limit` (device, optional) caps the rows examined (the screening survivors).
+// ---------------------------------------------------------------------------
+__global__ void k_accept(const int32_t* __restrict__ a, const int32_t* __restrict__ span, RowMap rm,
+                         int mode, const int32_t* limit, int32_t* __restrict__ accepted) {
+  const int b = threadIdx.x;
+  if (b >= rm.n_seq) return;
+  const int s0 = rm.start[b];
+  int n = rm.start[b + 1] - s0;
+  if (limit) n = min(n, max(1, *limit));
+  int acc = n;
+  if (mode == CAD_VERIFY) {
+    acc = 1;
+    while (acc < n && a[s0 + acc - 1] == span[s0 + acc]) ++acc;
+  }
+  accepted[b] = acc;
+}
+
+hipError_t launch_accept(const int32_t* argmax, const int32_t* span, const RowMap& rm, int mode,
+                         const int32_t* limit, int32_t* accepted, hipStream_t s) {
+  hipLaunchKernelGGL(k_accept, dim3(1), dim3(64), 0, s, argmax, span, rm, mode, limit, accepted);
+  return hipGetLastError();
+}
+
+__global__ void k_fill_i32(int32_t* p, int n, int32_t v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_i32, dim3((n + 255) / 256), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+__global__ void k_mask_rows(int32_t* a, int rows, const int32_t* limit) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < rows && i >= *limit) a[i] = -1;
+}
+
+hipError_t launch_mask_rows(int32_t* argmax, int rows, const int32_t* limit, hipStream_t s) {
+  hipLaunchKernelGGL(k_mask_rows, dim3((rows + 255) / 256), dim3(256), 0, s, argmax, rows, limit);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// suffix-match proposal: one work-group scans every start p for each suffix
+// length n (max_n down to min_n) and keeps the largest matching p
+// ---------------------------------------------------------------------------
+constexpr int SUFFIX_THREADS = 1024;
+
+__global__ void __launch_bounds__(SUFFIX_THREADS)
+k_suffix_match(const int32_t* __restrict__ x, int64_t T, int max_n, int min_n, int K,
+               int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_len,
+               int64_t* __restrict__ out_pos) {
+  __shared__ int32_t suf[64];
+  __shared__ long long red[SUFFIX_THREADS / 64];
+  __shared__ long long found;
+  const int top = (int)((T - 1 < (int64_t)max_n) ? (T - 1) : max_n);
+  if (threadIdx.x == 0) found = -1;
+  __syncthreads();
+  for (int n = top; n >= min_n && n >= 1; --n) {
+    if (threadIdx.x < n) suf[threadIdx.x] = x[T - n + threadIdx.x];
+    __syncthreads();
+    long long best = -1;
+    const int64_t last = T - 1 - n;  // p + n <= T - 1
+    for (int64_t p = threadIdx.x; p <= last; p += blockDim.x) {
+      bool m = true;
+      for (int j = 0; j < n && m; ++j) m = x[p + j] == suf[j];
+      if (m && p > best) best = p;
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      const long long ob = __shfl_xor(best, o);
+      best = ob > best ? ob : best;
+    }
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      long long b = -1;
+      for (int i = 0; i < SUFFIX_THREADS / 64; ++i) b = red[i] > b ? red[i] : b;
+      if (b >= 0) found = b + n;
+    }
+    __syncthreads();
+    if (found >= 0) break;
+  }
+  const long long start = found;
+  if (start < 0) {
+    if (threadIdx.x == 0) { *out_len = 0; *out_pos = -1; }
+    return;
+  }
+  const long long end = (start + K < T) ? start + K : T;
+  const int len = (int)(end - start);
+  for (int j = threadIdx.x; j < len; j += blockDim.x) out_tokens[j] = x[start + j];
+  if (threadIdx.x == 0) { *out_len = len; *out_pos = start; }
+}
+
+hipError_t launch_suffix_match(const int32_t* tokens, int64_t T, int max_n, int min_n, int K,
+                               int32_t* out_tokens, int32_t* out_len, int64_t* out_pos,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(k_suffix_match, dim3(1), dim3(SUFFIX_THREADS), 0, s, tokens, T, max_n, min_n, K,
+                     out_tokens, out_len, out_pos);
+  return hipGetLastError();
+}
+
+}  // namespace cad
