@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Throughput of the copy-span splice forward on one MI355X.
+
+Workload (one "step" = one call of ``cad_splice_forward``, the whole hot path:
+embedding, 32 decoder layers with KV append and causal span attention, LM
+head, masked argmax and acceptance): a Llama-style 7B shape (32 layers,
+d_model 4096, 32 query / 8 KV heads of 128, SwiGLU FFN 14336, vocab 32000),
+random-init bf16 weights, a KV cache of L = 16384 tokens, one copy span of
+N = 512 tokens taken from a duplicated line of a synthetic repeated-line
+prompt, a per-position vocabulary bitmask allowing 60% of the ids, COMMIT
+mode (Copy-as-Decode §2.4: acceptance is 1 inside a copy op).  Inputs are
+resident in HBM before the timed region; the step is idempotent (it rewrites
+the same cache slots), so repeating it measures steady-state throughput.
+
+Prints one JSON line.  ``value`` is spliced tokens/s (N / seconds per step).
+``roofline`` reports the kernel family that takes the most time in the timed
+region (HIP events around its launches, on its stream), its algorithmic work
+per launch and the MI355X peak it is bound by.  ``cpu_baseline`` times the
+float64 CPU oracle on a bounded sample of the same workload.  ``sweep``
+reports the other span lengths of the same shape.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16/bf16 matrix cores, TFLOP/s
+RIDGE = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+METRIC = "spliced tokens/sec (copy-span forward, 7B shape) + % of HBM/MFMA roofline"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# algorithmic work
+# ----------------------------------------------------------------------------
+
+def p_lin(s):
+    return s.n_layers * (s.d_model * s.qkv_rows + s.n_q_heads * s.head_dim * s.d_model
+                         + 3 * s.d_model * s.ffn_dim) + s.d_model * s.vocab
+
+
+def forward_work(s, N, L, w=2):
+    """Bytes the forward must move and FLOPs it must do (no logits write)."""
+    words = (s.vocab + 31) // 32
+    byts = (w * p_lin(s) + w * s.d_model * (2 * s.n_layers + 1) + w * s.d_model * N
+            + s.n_layers * 2 * s.n_kv_heads * s.head_dim * w * (L + N) + 4 * N * words + 8 * N)
+    flops = 2 * p_lin(s) * N + 4 * s.n_q_heads * s.head_dim * s.n_layers * (N * L + N * (N + 1) // 2)
+    return byts, flops
+
+
+def family_work(s, fam, N, L):
+    """(bytes, flops) of ONE launch of a kernel family: weights read once,
+    half activations in, outputs out; attention reads K and V of L + N keys."""
+    d, F, V, hq, hkv, hd = s.d_model, s.ffn_dim, s.vocab, s.n_q_heads, s.n_kv_heads, s.head_dim
+    if fam == "gemm_qkv":
+        return 2 * s.qkv_rows * d + 2 * N * d + 4 * N * s.qkv_rows, 2 * N * s.qkv_rows * d
+    if fam == "gemm_o":
+        return 2 * d * hq * hd + 2 * N * hq * hd + 8 * N * d, 2 * N * d * hq * hd
+    if fam == "gemm_gate_up":
+        return 2 * 2 * F * d + 2 * N * d + 2 * N * F, 2 * N * 2 * F * d
+    if fam == "gemm_down":
+        return 2 * d * F + 2 * N * F + 8 * N * d, 2 * N * d * F
+    if fam == "gemm_lm_head":
+        return 2 * V * d + 2 * N * d + 4 * N * V, 2 * N * V * d
+    if fam == "attention":
+        byts = 2 * hkv * hd * 2 * (L + N) + 2 * 2 * N * hq * hd
+        return byts, 4 * hq * hd * (N * L + N * (N + 1) // 2)
+    return None
+
+
+# ----------------------------------------------------------------------------
+# GPU workload
+# ----------------------------------------------------------------------------
+
+class Workload:
+    def __init__(self, shape, L, max_tokens, device="cuda"):
+        import torch
+        import synth
+        import verify_forward_amd as cad
+        self.torch, self.synth, self.cad = torch, synth, cad
+        self.shape, self.L = shape, L
+        t0 = time.time()
+        self.W = synth.make_weights(shape, device=device)
+        nb = (L + max_tokens + 15) // 16
+        self.kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device=device)
+        g = torch.Generator(device=device)
+        g.manual_seed(synth.SEED_KV)
+        std = synth.kv_std(shape)
+        for t in (self.kv.k, self.kv.v):
+            t.copy_(torch.randn(t.shape, generator=g, device=device, dtype=torch.float32).mul_(std))
+        self.model = cad.cad_model_create(shape, self.W, max_tokens=max_tokens)
+        self.prompt = synth.make_line_prompt(L, shape.vocab)
+        torch.cuda.synchronize()
+        log(f"[bench] weights + cache ready in {time.time() - t0:.1f}s")
+
+    def inputs(self, N, allowed_frac=0.6):
+        torch, synth = self.torch, self.synth
+        span = synth.pick_span(self.prompt, N)
+        n_allowed = int(round(allowed_frac * self.shape.vocab))
+        mask = synth.allowed_fraction_mask(N, self.shape.vocab, n_allowed)
+        dev = "cuda"
+        return dict(span=torch.from_numpy(span.astype("int32")).to(dev),
+                    mask=torch.from_numpy(mask.view("int32")).to(dev),
+                    argmax=torch.empty(N, dtype=torch.int32, device=dev),
+                    accepted=torch.empty(1, dtype=torch.int32, device=dev),
+                    status=torch.zeros(1, dtype=torch.int32, device=dev))
+
+    def step(self, io):
+        self.cad.cad_splice_forward(self.model, self.kv, self.L, io["span"], io["mask"], self.cad.CAD_COMMIT,
+                                    io["argmax"], io["accepted"], None, io["status"])
+
+    def time_steps(self, io, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step(io)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step(io)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the float64 oracle on a bounded sample
+# ----------------------------------------------------------------------------
+
+def cpu_baseline(shape, L, N):
+    """Oracle splice of all N rows through 1 and then 2 of the decoder layers
+    (plus the LM head and argmax each time); the full-depth time is
+    extrapolated as t1 + (n_layers - 1) * (t2 - t1)."""
+    import numpy as np
+    import torch
+    import oracle
+    import synth
+    from oracle.decoder import Config, KVCache
+    cores = len(os.sched_getaffinity(0))
+    times = {}
+    for nl in (1, 2):
+        sub = shape.replace(n_layers=nl)
+        W = synth.weights_to_numpy(synth.make_weights(shape, device="cuda", layers=range(nl)))
+        kl, vl = synth.random_kv_logical(sub, L, device="cuda")
+        kl, vl = kl.float().cpu().numpy(), vl.float().cpu().numpy()
+        prompt = synth.make_line_prompt(L, shape.vocab)
+        span = synth.pick_span(prompt, N)
+        mask = synth.allowed_fraction_mask(N, shape.vocab, int(round(0.6 * shape.vocab)))
+        kv = KVCache.from_prefix(kl, vl, L + N)
+        t0 = time.perf_counter()
+        lg = oracle.splice(Config.of(sub), W, kv, L, span)
+        a = oracle.masked_argmax(lg, mask)
+        oracle.acceptance(a, span, 0)
+        times[nl] = time.perf_counter() - t0
+        log(f"[bench] oracle sample: {nl} layer(s), {N} rows: {times[nl]:.1f}s")
+        del W, kv, lg
+        torch.cuda.empty_cache()
+    per_layer = max(times[2] - times[1], 1e-9)
+    full = times[1] + (shape.n_layers - 1) * per_layer
+    try:
+        blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"]["name"]
+    except Exception:
+        blas = "unknown"
+    return {"value": N / full, "unit": "spliced tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"float64 NumPy oracle ({blas}), all {N} span rows through 1 and 2 of the "
+                       f"{shape.n_layers} layers + LM head + masked argmax at L={L}; full depth "
+                       f"extrapolated as t1 + {shape.n_layers - 1}*(t2 - t1) = {full:.1f}s"),
+            "sample_seconds": round(times[1] + times[2], 2)}
+
+
+# ----------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--span", type=int, default=512)
+    ap.add_argument("--L", type=int, default=16384)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the splice forward of one "
+                                   "sequence is measured on a single MI355X; multi-GPU runs are not part "
+                                   "of this build", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import synth
+    import verify_forward_amd as cad
+    shape = synth.LLAMA_7B
+    N, L = args.span, args.L
+    wl = Workload(shape, L, max_tokens=max(N, 512))
+    io = wl.inputs(N)
+
+    # timed region, with HIP events bracketing every launch by kernel family
+    for _ in range(args.warmup):
+        wl.step(io)
+    torch.cuda.synchronize()
+    cad.cad_profile_enable(wl.model, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        wl.step(io)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    cad.cad_profile_enable(wl.model, False)
+    status = int(io["status"][0])
+    prof = {f: cad.cad_profile_read(wl.model, f) for f in cad.PROFILE_FAMILIES}
+    ms_step = dt / args.steps * 1e3
+    value = N * args.steps / dt
+    byts, flops = forward_work(shape, N, L)
+    fam = max((f for f in prof if family_work(shape, f, N, L)), key=lambda f: prof[f][1])
+    n_launch, fam_ms = prof[fam]
+    per_launch_s = fam_ms / n_launch / 1e3
+    fb, ff = family_work(shape, fam, N, L)
+    if ff / fb > RIDGE:
+        roof = {"bound": "mfma", "achieved": round(ff / per_launch_s / 1e12, 2), "peak": MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(fb / per_launch_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = fam
+    roof["avg_launch_us"] = round(per_launch_s * 1e6, 2)
+    roof["launches"] = n_launch
+    roof["work_per_launch"] = {"bytes": fb, "flops": ff}
+    kernels = {f: {"launches": n, "ms_per_step": round(ms / args.steps, 4)} for f, (n, ms) in prof.items() if n}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "spliced tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "storage_dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "copy-span splice forward, Llama-style 7B shape (32 layers, d_model 4096, "
+                               "32 q / 8 kv heads x 128, SwiGLU 14336, vocab 32000), random-init weights",
+                   "L": L, "N": N, "batch": 1, "mask_allowed_frac": 0.6, "mode": "commit"},
+        "forward": {"bytes": byts, "flops": flops,
+                    "hbm_frac": round(byts / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                    "mfma_frac": round(flops / (ms_step * 1e-3) / (MFMA_PEAK_TFLOPS * 1e12), 4),
+                    "roof_ms": round(max(byts / (HBM_PEAK_GBS * 1e9), flops / (MFMA_PEAK_TFLOPS * 1e12)) * 1e3, 4)},
+        "roofline": roof,
+        "kernels": kernels,
+        "device_status": status,
+    }
+    out["forward"]["binding_roof_frac"] = round(out["forward"]["roof_ms"] / ms_step, 4)
+
+    if not args.no_sweep:
+        sweep = []
+        for n in (1, 4, 8, 16, 128):
+            if n == N:
+                continue
+            io_n = wl.inputs(n)
+            steps = 10
+            t = wl.time_steps(io_n, steps, 2)
+            ms = t / steps * 1e3
+            b, f = forward_work(shape, n, L)
+            sweep.append({"N": n, "ms": round(ms, 4), "tok_s": round(n / (ms * 1e-3), 1),
+                          "hbm_frac": round(b / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                          "mfma_frac": round(f / (ms * 1e-3) / (MFMA_PEAK_TFLOPS * 1e12), 4)})
+            log(f"[bench] sweep N={n}: {ms:.3f} ms")
+        out["sweep"] = sweep
+
+    if not args.no_cpu_baseline:
+        del wl
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(shape, L, N)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

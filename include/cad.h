@@ -204,6 +204,19 @@ cad_status cad_splice_forward_looped(cad_model* m, const cad_kv* kv, int64_t L,
                                      int32_t* survivors, int32_t* argmax, int32_t* accepted,
                                      float* logits, int32_t* dev_status, cad_stream stream);
 
+/* ---- instrumentation (measurement only, not part of the method) ----
+ * When enabled on a model, every kernel launch the model enqueues is
+ * bracketed by a pair of hipEvents recorded on the launch's stream, grouped
+ * by kernel family: "embed", "rmsnorm", "gemm_qkv", "rope_append",
+ * "attention" (partial kernel and merge), "gemm_o", "gemm_gate_up",
+ * "gemm_down", "gemm_lm_head", "argmax", "accept", "mask_rows".
+ * cad_profile_enable(m, 1) starts a fresh collection (0 stops it; records
+ * are kept until the next enable).  cad_profile_read waits for the recorded
+ * events of `family` and returns how many launches were recorded and their
+ * summed duration in milliseconds.  Unknown family: CAD_E_ARG. */
+cad_status cad_profile_enable(cad_model* m, int32_t enable);
+cad_status cad_profile_read(cad_model* m, const char* family, int64_t* launches, double* total_ms);
+
 #ifdef __cplusplus
 }
 #endif

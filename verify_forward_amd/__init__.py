@@ -26,7 +26,10 @@ CAD_MAX_SEQS = 64
 
 EXPORTS = ("cad_model_create", "cad_model_destroy", "cad_last_error", "cad_splice_forward",
            "cad_decode_step", "cad_propose_suffix_match", "cad_splice_forward_batched",
-           "cad_splice_forward_looped")
+           "cad_splice_forward_looped", "cad_profile_enable", "cad_profile_read")
+
+PROFILE_FAMILIES = ("embed", "rmsnorm", "gemm_qkv", "rope_append", "attention", "gemm_o", "gemm_gate_up",
+                    "gemm_down", "gemm_lm_head", "argmax", "accept", "mask_rows")
 
 
 class CadError(RuntimeError):
@@ -82,8 +85,11 @@ def lib() -> ctypes.CDLL:
                                                  _VP, _VP, _VP, _VP, _VP]
         L.cad_splice_forward_looped.argtypes = [_VP, ctypes.POINTER(cad_kv), i64, _VP, i32, i32, _VP, _VP,
                                                 _VP, _VP, _VP, _VP, _VP, _VP]
+        L.cad_profile_enable.argtypes = [_VP, i32]
+        L.cad_profile_read.argtypes = [_VP, ctypes.c_char_p, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)]
         for name in ("cad_model_create", "cad_splice_forward", "cad_decode_step", "cad_propose_suffix_match",
-                     "cad_splice_forward_batched", "cad_splice_forward_looped"):
+                     "cad_splice_forward_batched", "cad_splice_forward_looped", "cad_profile_enable",
+                     "cad_profile_read"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -237,3 +243,15 @@ def cad_splice_forward_looped(model: Model, kv: KVCache, L: int, span: torch.Ten
                                            int(screen_depth), _p(mask), _p(screen_argmax), _p(survivors),
                                            _p(argmax), _p(accepted), _p(logits), _p(dev_status),
                                            _stream(stream)))
+
+
+def cad_profile_enable(model: Model, enable: bool = True):
+    _check(lib().cad_profile_enable(model.handle, 1 if enable else 0))
+
+
+def cad_profile_read(model: Model, family: str):
+    """Return ``(launches, total_ms)`` recorded for a kernel family."""
+    n = ctypes.c_int64()
+    ms = ctypes.c_double()
+    _check(lib().cad_profile_read(model.handle, family.encode(), ctypes.byref(n), ctypes.byref(ms)))
+    return int(n.value), float(ms.value)

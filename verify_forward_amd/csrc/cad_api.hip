@@ -39,10 +39,34 @@ cad_status fail(cad_status s, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+#define HIP_TRY(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess) return fail(CAD_E_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
 }  // namespace
+
+enum ProfFamily {
+  PF_EMBED, PF_NORM, PF_QKV, PF_ROPE, PF_ATTN, PF_O, PF_GATEUP, PF_DOWN, PF_HEAD, PF_ARGMAX,
+  PF_ACCEPT, PF_MASKROWS, PF_COUNT
+};
+static const char* const kProfNames[PF_COUNT] = {
+    "embed", "rmsnorm", "gemm_qkv", "rope_append", "attention", "gemm_o", "gemm_gate_up",
+    "gemm_down", "gemm_lm_head", "argmax", "accept", "mask_rows"};
+
+struct ProfRec {
+  int family;
+  hipEvent_t a, b;
+};
 
 struct cad_model {
   cad_config cfg;
+  // instrumentation
+  bool prof_on = false;
+  std::vector<ProfRec> prof;
+  std::vector<hipEvent_t> prof_pool;
+  size_t prof_used = 0;
   int esize;  // bytes per weight / cache element
   // weights (caller-owned)
   const void* tok_embed;
@@ -70,6 +94,31 @@ struct cad_model {
 namespace {
 
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+hipEvent_t prof_event(cad_model* m) {
+  if (m->prof_used == m->prof_pool.size()) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    m->prof_pool.push_back(e);
+  }
+  return m->prof_pool[m->prof_used++];
+}
+
+// Launch `fn` (returning hipError_t), bracketed by events when profiling.
+template <typename Fn>
+hipError_t prof_launch(cad_model* m, int family, hipStream_t s, Fn fn) {
+  if (!m->prof_on) return fn();
+  ProfRec r{family, prof_event(m), prof_event(m)};
+  if (r.a && r.b) (void)hipEventRecord(r.a, s);
+  hipError_t e = fn();
+  if (r.a && r.b) {
+    (void)hipEventRecord(r.b, s);
+    m->prof.push_back(r);
+  }
+  return e;
+}
+
+#define LAUNCH(fam, expr) HIP_TRY(prof_launch(m, fam, s, [&]() { return (expr); }))
 
 cad_status check_config(const cad_config* c) {
   if (!c) return fail(CAD_E_ARG, "cfg is NULL");
@@ -103,12 +152,6 @@ int64_t max_parts_rows(const cad_config& c) {
   }
   return best;
 }
-
-#define HIP_TRY(expr)                                                                   \
-  do {                                                                                  \
-    hipError_t e_ = (expr);                                                             \
-    if (e_ != hipSuccess) return fail(CAD_E_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
-  } while (0)
 
 cad_status check_kv(const cad_model* m, const cad_kv* kv) {
   if (!kv) return fail(CAD_E_ARG, "kv is NULL");
@@ -149,28 +192,28 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
   for (int ci = c0; ci < c1; ++ci) {
     const int li = c.loop_depth > 1 ? 0 : ci;
     const KVView v = view_of(m, kv, ci);
-    HIP_TRY(launch_rmsnorm(c.dtype, m->x, m->attn_norm[li], R, d, c.rms_eps, m->hn, s));
+    LAUNCH(PF_NORM, launch_rmsnorm(c.dtype, m->x, m->attn_norm[li], R, d, c.rms_eps, m->hn, s));
     GemmArgs g{};
     g.A = m->hn; g.lda = d; g.W = m->w_qkv[li]; g.ldw = d;
     g.M = R; g.N = qkv_rows; g.K = d; g.out_f32 = m->qkv; g.ldo = qkv_rows;
-    HIP_TRY(launch_gemm(c.dtype, EPI_STORE_F32, g, s));
-    HIP_TRY(launch_rope_append(c.dtype, m->qkv, R, hq, hkv, hd, m->freq, rm, v, write_limit, m->q,
+    LAUNCH(PF_QKV, launch_gemm(c.dtype, EPI_STORE_F32, g, s));
+    LAUNCH(PF_ROPE, launch_rope_append(c.dtype, m->qkv, R, hq, hkv, hd, m->freq, rm, v, write_limit, m->q,
                                dev_status, s));
-    HIP_TRY(launch_attention(c.dtype, m->q, R, hq, hkv, hd, rm, v, n_parts, part_len, m->part_o,
+    LAUNCH(PF_ATTN, launch_attention(c.dtype, m->q, R, hq, hkv, hd, rm, v, n_parts, part_len, m->part_o,
                              m->part_ml, m->attn, dev_status, s));
     g = GemmArgs{};
     g.A = m->attn; g.lda = hq * hd; g.W = m->w_o[li]; g.ldw = hq * hd;
     g.M = R; g.N = d; g.K = hq * hd; g.out_f32 = m->x; g.ldo = d;
-    HIP_TRY(launch_gemm(c.dtype, EPI_RESID, g, s));
-    HIP_TRY(launch_rmsnorm(c.dtype, m->x, m->ffn_norm[li], R, d, c.rms_eps, m->hn, s));
+    LAUNCH(PF_O, launch_gemm(c.dtype, EPI_RESID, g, s));
+    LAUNCH(PF_NORM, launch_rmsnorm(c.dtype, m->x, m->ffn_norm[li], R, d, c.rms_eps, m->hn, s));
     g = GemmArgs{};
     g.A = m->hn; g.lda = d; g.W = m->w_gate_up[li]; g.ldw = d;
     g.M = R; g.N = F; g.K = d; g.up_off = F; g.out_act = m->act;
-    HIP_TRY(launch_gemm(c.dtype, EPI_SWIGLU, g, s));
+    LAUNCH(PF_GATEUP, launch_gemm(c.dtype, EPI_SWIGLU, g, s));
     g = GemmArgs{};
     g.A = m->act; g.lda = F; g.W = m->w_down[li]; g.ldw = F;
     g.M = R; g.N = d; g.K = F; g.out_f32 = m->x; g.ldo = d;
-    HIP_TRY(launch_gemm(c.dtype, EPI_RESID, g, s));
+    LAUNCH(PF_DOWN, launch_gemm(c.dtype, EPI_RESID, g, s));
   }
   return CAD_OK;
 }
@@ -179,12 +222,12 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
 cad_status readout(cad_model* m, int R, float* logits, const uint32_t* mask, int32_t* argmax,
                    int32_t* dev_status, hipStream_t s) {
   const cad_config& c = m->cfg;
-  HIP_TRY(launch_rmsnorm(c.dtype, m->x, m->final_norm, R, c.d_model, c.rms_eps, m->hn, s));
+  LAUNCH(PF_NORM, launch_rmsnorm(c.dtype, m->x, m->final_norm, R, c.d_model, c.rms_eps, m->hn, s));
   GemmArgs g{};
   g.A = m->hn; g.lda = c.d_model; g.W = m->lm_head; g.ldw = c.d_model;
   g.M = R; g.N = c.vocab; g.K = c.d_model; g.out_f32 = logits; g.ldo = c.vocab;
-  HIP_TRY(launch_gemm(c.dtype, EPI_STORE_F32, g, s));
-  HIP_TRY(launch_argmax(logits, R, c.vocab, mask, argmax, dev_status, s));
+  LAUNCH(PF_HEAD, launch_gemm(c.dtype, EPI_STORE_F32, g, s));
+  LAUNCH(PF_ARGMAX, launch_argmax(logits, R, c.vocab, mask, argmax, dev_status, s));
   return CAD_OK;
 }
 
@@ -294,6 +337,7 @@ cad_status cad_model_create(const cad_config* cfg, const cad_weights* w, cad_mod
 void cad_model_destroy(cad_model* m) {
   if (!m) return;
   (void)hipDeviceSynchronize();
+  for (hipEvent_t e : m->prof_pool) (void)hipEventDestroy(e);
   (void)hipFree(m->ws);
   delete m;
 }
@@ -315,12 +359,12 @@ cad_status cad_splice_forward(cad_model* m, const cad_kv* kv, int64_t L, const i
   rm.start[1] = N;
   rm.L[0] = L;
   const cad_config& c = m->cfg;
-  HIP_TRY(launch_embed(c.dtype, m->tok_embed, c.vocab, c.d_model, span, N, m->x, dev_status, s));
+  LAUNCH(PF_EMBED, launch_embed(c.dtype, m->tok_embed, c.vocab, c.d_model, span, N, m->x, dev_status, s));
   st = run_blocks(m, kv, rm, 0, c.n_layers, nullptr, dev_status, s);
   if (st != CAD_OK) return st;
   st = readout(m, N, logits ? logits : m->logits, mask, argmax, dev_status, s);
   if (st != CAD_OK) return st;
-  HIP_TRY(launch_accept(argmax, span, rm, mode, nullptr, accepted, s));
+  LAUNCH(PF_ACCEPT, launch_accept(argmax, span, rm, mode, nullptr, accepted, s));
   return CAD_OK;
 }
 
@@ -359,12 +403,12 @@ cad_status cad_splice_forward_batched(cad_model* m, const cad_kv* kv, int32_t n_
     return fail(CAD_E_CAPACITY, "total rows %d > max_tokens %d", rm.total, m->cfg.max_tokens);
   hipStream_t s = (hipStream_t)stream;
   const cad_config& c = m->cfg;
-  HIP_TRY(launch_embed(c.dtype, m->tok_embed, c.vocab, c.d_model, spans, rm.total, m->x, dev_status, s));
+  LAUNCH(PF_EMBED, launch_embed(c.dtype, m->tok_embed, c.vocab, c.d_model, spans, rm.total, m->x, dev_status, s));
   st = run_blocks(m, kv, rm, 0, c.n_layers, nullptr, dev_status, s);
   if (st != CAD_OK) return st;
   st = readout(m, rm.total, logits ? logits : m->logits, mask, argmax, dev_status, s);
   if (st != CAD_OK) return st;
-  HIP_TRY(launch_accept(argmax, spans, rm, mode, nullptr, accepted, s));
+  LAUNCH(PF_ACCEPT, launch_accept(argmax, spans, rm, mode, nullptr, accepted, s));
   return CAD_OK;
 }
 
@@ -388,18 +432,50 @@ cad_status cad_splice_forward_looped(cad_model* m, const cad_kv* kv, int64_t L,
   rm.total = N;
   rm.start[1] = N;
   rm.L[0] = L;
-  HIP_TRY(launch_embed(c.dtype, m->tok_embed, c.vocab, c.d_model, span, N, m->x, dev_status, s));
+  LAUNCH(PF_EMBED, launch_embed(c.dtype, m->tok_embed, c.vocab, c.d_model, span, N, m->x, dev_status, s));
   st = run_blocks(m, kv, rm, 0, screen_depth, nullptr, dev_status, s);
   if (st != CAD_OK) return st;
   st = readout(m, N, m->logits, mask, screen_argmax, dev_status, s);
   if (st != CAD_OK) return st;
-  HIP_TRY(launch_accept(screen_argmax, span, rm, CAD_VERIFY, nullptr, survivors, s));
+  LAUNCH(PF_ACCEPT, launch_accept(screen_argmax, span, rm, CAD_VERIFY, nullptr, survivors, s));
   st = run_blocks(m, kv, rm, screen_depth, c.loop_depth, survivors, dev_status, s);
   if (st != CAD_OK) return st;
   st = readout(m, N, logits ? logits : m->logits, mask, argmax, dev_status, s);
   if (st != CAD_OK) return st;
-  HIP_TRY(launch_mask_rows(argmax, N, survivors, s));
-  HIP_TRY(launch_accept(argmax, span, rm, CAD_VERIFY, survivors, accepted, s));
+  LAUNCH(PF_MASKROWS, launch_mask_rows(argmax, N, survivors, s));
+  LAUNCH(PF_ACCEPT, launch_accept(argmax, span, rm, CAD_VERIFY, survivors, accepted, s));
+  return CAD_OK;
+}
+
+cad_status cad_profile_enable(cad_model* m, int32_t enable) {
+  if (!m) return fail(CAD_E_ARG, "model is NULL");
+  if (enable) {
+    HIP_TRY(hipDeviceSynchronize());
+    m->prof.clear();
+    m->prof_used = 0;
+  }
+  m->prof_on = enable != 0;
+  return CAD_OK;
+}
+
+cad_status cad_profile_read(cad_model* m, const char* family, int64_t* launches, double* total_ms) {
+  if (!m || !family || !launches || !total_ms) return fail(CAD_E_ARG, "NULL argument");
+  int f = -1;
+  for (int i = 0; i < PF_COUNT; ++i)
+    if (!strcmp(family, kProfNames[i])) f = i;
+  if (f < 0) return fail(CAD_E_ARG, "unknown kernel family '%s'", family);
+  int64_t n = 0;
+  double ms = 0.0;
+  for (const ProfRec& r : m->prof) {
+    if (r.family != f) continue;
+    HIP_TRY(hipEventSynchronize(r.b));
+    float t = 0.f;
+    HIP_TRY(hipEventElapsedTime(&t, r.a, r.b));
+    ++n;
+    ms += t;
+  }
+  *launches = n;
+  *total_ms = ms;
   return CAD_OK;
 }
 
