@@ -6,14 +6,19 @@
 //
 // bf16 models (matrix cores, half operands: q arrives as half, K and V are
 // widened from the bf16 cache to half while staged in LDS, P is rounded to
-// half).  One work-group = one KV head x 64 query rows
-// (query row = span row * G + head-in-group, so the G query heads that share
-// a KV head share every K/V tile) x one partition of the key axis.  Keys are
-// processed 32 at a time: the K tile [32][hd] and the V tile, stored
-// token-minor in the cache ([hd][16] per block), are staged in LDS and used
-// by all four waves.  Each wave owns 16 query rows and computes
+// half).  One work-group = one KV head x 128 query rows (query row = span row
+// * G + head-in-group, so the G query heads that share a KV head share every
+// K/V tile) x one partition of the key axis.  Keys are processed 64 at a
+// time through a double-buffered LDS stage: the K tile [64][hd] and the V
+// tile, stored token-minor in the cache ([hd][16] per block) and kept
+// transposed in LDS, are loaded once per work-group and read by all four
+// waves; the global loads of tile t+1 are in flight while tile t is on the
+// matrix cores.  Each wave owns 32 query rows (two 16-column blocks) and
+// computes
 //   S^T = K Q^T      (v_mfma_f32_16x16x32_f16; lane -> one query column)
-//   O^T += V^T P^T   (P^T's k index is permuted to the keys the lane holds)
+//   O^T += V^T P^T   (the key order inside each 32-key group of the LDS V
+//                     tile is permuted so that the eight keys a lane feeds as
+//                     P^T are exactly the eight it holds in S^T)
 // so the online-softmax state of a query lives in the four lanes that hold
 // its column and never needs a transpose.  Partitions write unnormalised
 // partial outputs plus (max, sum) and are merged by a log-sum-exp kernel;
@@ -30,7 +35,7 @@ struct AttnArgs {
   int rows, hq, hkv, G;
   RowMap rm;
   KVView kv;
-  int32_t tstart[CAD_MAX_SEQS + 1];  // 64-row query tiles per sequence (CSR)
+  int32_t tstart[CAD_MAX_SEQS + 1];  // FA_QT-row query tiles per sequence (CSR)
   int n_parts, part_len;
   float* part_o;   // [n_parts][rows * hq][hd]
   float* part_ml;  // [n_parts][rows * hq][2]
@@ -39,179 +44,294 @@ struct AttnArgs {
   float scale_log2;  // log2(e) / sqrt(hd)
 };
 
-constexpr int AT_KEYS = 32;
-constexpr int AT_PAD = 8;
+constexpr int FA_KT = 64;                  // keys per tile
+constexpr int FA_QPW = 32;                 // query rows per wave
+constexpr int FA_WAVES = 8;
+constexpr int FA_QT = FA_QPW * FA_WAVES;   // query rows per work-group
+constexpr int FA_NT = 64 * FA_WAVES;       // threads per work-group
+
+// Work-group -> (query tile, KV head, key partition).  The query tiles that
+// read the same KV head and key range are placed on one XCD (work-group ids
+// are dealt to the eight XCDs round-robin) so that their shared K/V tiles
+// are fetched from HBM once and then hit that XCD's L2.
+__device__ __forceinline__ void attn_tile_of(int& x, int& y, int& z) {
+  const int X = gridDim.x, Y = gridDim.y, Z = gridDim.z;
+  const int id = blockIdx.x + X * (blockIdx.y + Y * blockIdx.z);
+  if ((Y * Z) % 8 != 0) {
+    x = blockIdx.x; y = blockIdx.y; z = blockIdx.z;
+    return;
+  }
+  const int xcd = id & 7, slot = id >> 3;
+  const int gi = xcd + 8 * (slot / X);
+  x = slot % X;
+  y = gi % Y;
+  z = gi / Y;
+}
+
+// Online softmax keeps a per-query running maximum in exp2 units and moves
+// it only when a tile raises some query's maximum by more than this margin,
+// so the O rescale is skipped on most tiles; until then the unnormalised
+// weights stay below 2^FA_LAZY, far inside half's range.
+constexpr float FA_LAZY = 8.0f;
 
 template <int HD>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(FA_NT)
 k_attn_bf16(AttnArgs p) {
-  constexpr int KLD = HD + AT_PAD;       // sK row stride (halves)
-  constexpr int VLD = AT_KEYS + AT_PAD;  // sVt row stride (halves)
-  constexpr int DS = HD / 32;            // k steps of the QK^T product
-  constexpr int DB = HD / 16;            // 16-wide output blocks
-  __shared__ __attribute__((aligned(16))) f16_t sK[AT_KEYS * KLD];
-  __shared__ __attribute__((aligned(16))) f16_t sVt[HD * VLD];
+  constexpr int KLD = HD + 8;          // sK row stride (halves): 16 B pad keeps 16-row reads conflict-free
+  constexpr int VLD = FA_KT + 8;       // sV row stride (halves)
+  constexpr int DS = HD / 32;          // k steps of S^T = K Q^T
+  constexpr int DB = HD / 16;          // 16-row d blocks of O^T
+  constexpr int TBLK = FA_KT / CAD_KV_BLOCK;   // cache blocks per tile
+  constexpr int TPB = FA_NT / TBLK;            // staging threads per cache block
+  constexpr int KCH = CAD_KV_BLOCK * HD / 8 / TPB;  // 16-byte K chunks per thread and tile
+  constexpr int VCH = HD * CAD_KV_BLOCK / 8 / TPB;  // 16-byte V chunks per thread and tile
+  static_assert(KCH >= 1 && KCH * TPB * 8 == CAD_KV_BLOCK * HD && VCH * TPB * 8 == HD * CAD_KV_BLOCK,
+                "tile split");
+  static_assert(TPB % 64 == 0, "a wave stages from one cache block");
+  __shared__ __attribute__((aligned(16))) f16_t sK[2][FA_KT * KLD];
+  __shared__ __attribute__((aligned(16))) f16_t sV[2][HD * VLD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, i16 = lane & 15;
-  const int kvh = blockIdx.y, part = blockIdx.z;
-  // which sequence / tile
+  int bx, kvh, part;
+  attn_tile_of(bx, kvh, part);
   int b = 0;
-  while (b + 1 < p.rm.n_seq && p.tstart[b + 1] <= (int)blockIdx.x) ++b;
-  const int tile = blockIdx.x - p.tstart[b];
+  while (b + 1 < p.rm.n_seq && p.tstart[b + 1] <= bx) ++b;
+  const int tile = bx - p.tstart[b];
   const int n_rows = p.rm.start[b + 1] - p.rm.start[b];
   const int R = n_rows * p.G;
   const int64_t L = p.rm.L[b];
-  // this lane's query column
-  const int qr = tile * 64 + wave * 16 + i16;
-  const bool q_ok = qr < R;
-  const int k_local = q_ok ? qr / p.G : 0;
-  const int head = kvh * p.G + (q_ok ? qr % p.G : 0);
-  const int grow = p.rm.start[b] + k_local;
-  const int64_t q_last_key = L + k_local;  // inclusive causal limit
-  // work-group key range
-  const int last_row = min((tile * 64 + 63) / p.G, n_rows - 1);
-  const int64_t wg_keys_end = L + last_row + 1;
+  const int q_first = tile * FA_QT;
+  const int q_wave = q_first + wave * FA_QPW;
+  const bool wave_active = q_wave < R;
+  // keys of this work-group: [k_begin, k_end); k_begin is a multiple of FA_KT
+  const int q_last = min(q_first + FA_QT, R) - 1;
   const int64_t k_begin = (int64_t)part * p.part_len;
-  const int64_t k_end = min((int64_t)(part + 1) * p.part_len, wg_keys_end);
+  const int64_t k_end = min(k_begin + p.part_len, L + q_last / p.G + 1);
+  // causal limit shared by every query of the wave (its first query's)
+  const int64_t wave_min_last = L + q_wave / p.G;
 
-  // Q fragments (operand B of S^T = K Q^T): Q[query][ds*32 + 8*g4 .. +7]
-  u32x4 qf[DS];
-  const f16_t* qsrc = (const f16_t*)p.q + ((int64_t)grow * p.hq + head) * HD;
+  // this lane's two query columns
+  bool q_ok[2];
+  int64_t q_last_key[2], qrow[2];
+  u32x4 qf[2][DS];
 #pragma unroll
-  for (int ds = 0; ds < DS; ++ds) {
-    qf[ds] = q_ok ? *(const u32x4*)(qsrc + ds * 32 + g4 * 8) : u32x4{0u, 0u, 0u, 0u};
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qi = q_wave + qb * 16 + i16;
+    q_ok[qb] = qi < R;
+    const int k_local = q_ok[qb] ? qi / p.G : 0;
+    const int head = kvh * p.G + (q_ok[qb] ? qi % p.G : 0);
+    q_last_key[qb] = L + k_local;
+    qrow[qb] = (int64_t)(p.rm.start[b] + k_local) * p.hq + head;  // index of (row, head)
+    const f16_t* qsrc = (const f16_t*)p.q + qrow[qb] * HD;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds)
+      qf[qb][ds] = q_ok[qb] ? *(const u32x4*)(qsrc + ds * 32 + g4 * 8) : u32x4{0u, 0u, 0u, 0u};
   }
-  f32x4 o[DB];
+  f32x4 o[DB][2];
 #pragma unroll
-  for (int d = 0; d < DB; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int d = 0; d < DB; ++d) o[d][0] = o[d][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // finite start: exp2 of (masked score - m_run) is 0, never NaN
+  float m_run[2] = {-1e30f, -1e30f}, l_run[2] = {0.f, 0.f};
 
-  const bf16_t* kbase = (const bf16_t*)p.kv.k;
-  const bf16_t* vbase = (const bf16_t*)p.kv.v;
   const int32_t* table = p.kv.table + (int64_t)b * p.kv.max_blocks;
-
-  for (int64_t kt = k_begin; kt < k_end; kt += AT_KEYS) {
-    // ---- stage K [32][HD] and V^T [HD][32] in LDS ----
-    constexpr int KCH = AT_KEYS * HD / 8;  // 16-byte chunks of the K tile
-    for (int c = tid; c < KCH; c += 256) {
-      const int key = c / (HD / 8), c8 = c % (HD / 8);
-      const int64_t kk = kt + key;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (kk < k_end) {
-        const int64_t blk = table[kk / CAD_KV_BLOCK];
-        if (blk >= 0 && blk < p.kv.num_blocks)
-          v = bf16x8_to_f16x8(
-              *(const u32x4*)(kbase + ((blk * p.hkv + kvh) * CAD_KV_BLOCK + kk % CAD_KV_BLOCK) * HD + c8 * 8));
-        else if (p.status)
-          atomicOr(p.status, (int32_t)CAD_DEV_BAD_BLOCK);
-      }
-      *(u32x4*)(&sK[key * KLD + c8 * 8]) = v;
+  const int n_tiles = k_begin < k_end ? (int)((k_end - k_begin + FA_KT - 1) / FA_KT) : 0;
+  // Staging: the threads of wave w copy cache block jb = w / (TPB / 64) of
+  // each tile, so the block id is uniform over the wave (a scalar load).
+  const int jb = __builtin_amdgcn_readfirstlane(tid / TPB);
+  const int ct = tid % TPB;
+  const int64_t kv_blk_stride = (int64_t)p.hkv * CAD_KV_BLOCK * HD;  // elements per cache block
+  const bf16_t* kbase = (const bf16_t*)p.kv.k + (int64_t)kvh * CAD_KV_BLOCK * HD;
+  const bf16_t* vbase = (const bf16_t*)p.kv.v + (int64_t)kvh * CAD_KV_BLOCK * HD;
+  // cache block of tile t for this wave, or -1 when the tile's part of the
+  // key range does not reach it (then nothing is read)
+  auto block_of = [&](int t) -> int64_t {
+    const int64_t first_key = k_begin + (int64_t)t * FA_KT + jb * CAD_KV_BLOCK;
+    if (t >= n_tiles || first_key >= k_end) return -1;
+    return table[first_key / CAD_KV_BLOCK];
+  };
+  u32x4 rk[KCH], rv[VCH];
+  auto gload = [&](int64_t kt, int64_t bb) {
+    const int64_t k0 = kt + jb * CAD_KV_BLOCK;  // first key of this wave's block
+    const bool ok = bb >= 0 && bb < p.kv.num_blocks;
+    if (bb >= 0 && !ok && p.status && ct == 0) atomicOr(p.status, (int32_t)CAD_DEV_BAD_BLOCK);
+    const int nvalid = ok ? (int)min<int64_t>(k_end - k0, CAD_KV_BLOCK) : 0;  // keys of the block in range
+    const bf16_t* kb = kbase + (ok ? bb : 0) * kv_blk_stride;
+    const bf16_t* vb = vbase + (ok ? bb : 0) * kv_blk_stride;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = ct + TPB * i;  // [16 keys][HD / 8 chunks]
+      const int key = c / (HD / 8);
+      rk[i] = key < nvalid ? *(const u32x4*)(kb + c * 8) : u32x4{0u, 0u, 0u, 0u};
     }
-    constexpr int VCH = 2 * HD * 2;  // 2 blocks x HD rows x 2 chunks of 8 tokens
-    for (int c = tid; c < VCH; c += 256) {
-      const int half = c & 1, d = (c >> 1) % HD, kb = (c >> 1) / HD;
-      const int64_t k0 = kt + kb * 16 + half * 8;  // first token of the chunk
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (k0 < k_end) {
-        const int64_t blk = table[k0 / CAD_KV_BLOCK];
-        if (blk >= 0 && blk < p.kv.num_blocks) {
-          v = bf16x8_to_f16x8(*(const u32x4*)(vbase + ((blk * p.hkv + kvh) * HD + d) * CAD_KV_BLOCK + half * 8));
-          // zero tokens of the chunk that lie past the range end
-          const int64_t valid = k_end - k0;
-          if (valid < 8) {
-            uint16_t* e = (uint16_t*)&v;
-            for (int j = (int)valid; j < 8; ++j) e[j] = 0;
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int c = ct + TPB * i;  // [HD rows][2 chunks of 8 tokens]
+      const int hf = c & 1;
+      u32x4 v = *(const u32x4*)(vb + c * 8);
+      // zero the tokens past the key range (stale slots may hold anything)
+      const int nv = nvalid - 8 * hf;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t keep = (2 * w + 1 < nv) ? 0xFFFFFFFFu : (2 * w < nv ? 0x0000FFFFu : 0u);
+        v[w] &= keep;
+      }
+      rv[i] = v;
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = ct + TPB * i;
+      const int key = jb * CAD_KV_BLOCK + c / (HD / 8), c8 = c % (HD / 8);
+      *(u32x4*)(&sK[buf][key * KLD + c8 * 8]) = bf16x8_to_f16x8(rk[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int c = ct + TPB * i;
+      const int d = c >> 1, hf = c & 1;
+      // tile keys 16 jb + 8 hf + e (e < 8).  Inside its 32-key group (32 ks
+      // + 16 (jb & 1) + 8 hf + e) key 16 h + 4 j + r sits at column 8 j + 4 h
+      // + r: the eight columns 8 j .. 8 j + 7 then hold keys 4 j .. 4 j + 3
+      // and 16 + 4 j .. 16 + 4 j + 3, the keys lane group j holds in S^T.
+      const u32x4 h = bf16x8_to_f16x8(rv[i]);
+      const int col = (jb >> 1) * 32 + 16 * hf + 4 * (jb & 1);
+      f16_t* row = &sV[buf][d * VLD + col];
+      *(u32x2*)(row) = u32x2{h[0], h[1]};      // e = 0..3 -> j = 2 hf
+      *(u32x2*)(row + 8) = u32x2{h[2], h[3]};  // e = 4..7 -> j = 2 hf + 1
+    }
+  };
+
+  // Tile t + 1 is loaded into registers while tile t is on the matrix cores
+  // and written to the other LDS buffer at the end of the iteration (that
+  // buffer was last read before the barrier that closed tile t - 1).  Block
+  // ids run one more tile ahead.
+  int64_t blk = block_of(0);
+  if (n_tiles > 0) {
+    gload(k_begin, blk);
+    sstore(0);
+  }
+  blk = block_of(1);
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    const int64_t kt = k_begin + (int64_t)t * FA_KT;
+    const bool more = t + 1 < n_tiles;
+    if (more) gload(kt + FA_KT, blk);
+    const int64_t blk_next = block_of(t + 2);
+    if (wave_active) {
+      // ---- S^T = K Q^T for four 16-key blocks x two 16-query blocks ----
+      f32x4 s[4][2];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) s[kb][0] = s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const u32x4 kf = *(const u32x4*)(&sK[buf][(kb * 16 + i16) * KLD + ds * 32 + g4 * 8]);
+          s[kb][0] = mfma16(kf, qf[0][ds], s[kb][0]);
+          s[kb][1] = mfma16(kf, qf[1][ds], s[kb][1]);
+        }
+      // lane holds S[query (qb, i16)][key kt + 16 kb + 4 g4 + r]
+      const int end_rel = (int)min<int64_t>(k_end - kt, FA_KT);
+      const bool need_mask = kt + FA_KT - 1 > wave_min_last || end_rel < FA_KT;
+      float mx[2];
+      bool grow = false;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        if (need_mask) {
+          const int lim = (int)max<int64_t>(min<int64_t>(q_last_key[qb] - kt + 1, end_rel), 0);
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (kb * 16 + g4 * 4 + r >= lim) s[kb][qb][r] = -INFINITY;
+        }
+        float m = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          m = fmaxf(fmaxf(m, fmaxf(s[kb][qb][0], s[kb][qb][1])), fmaxf(s[kb][qb][2], s[kb][qb][3]));
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        mx[qb] = m * p.scale_log2;
+        grow |= mx[qb] > m_run[qb] + FA_LAZY;
+      }
+      if (__ballot(grow)) {  // some query's maximum moved: rescale (wave-uniform branch)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const float m_new = fmaxf(m_run[qb], mx[qb]);
+          const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+          m_run[qb] = m_new;
+          l_run[qb] *= alpha;
+#pragma unroll
+          for (int d = 0; d < DB; ++d) o[d][qb] *= alpha;
+        }
+      }
+      u32x4 pf[2][2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float nm = -m_run[qb];
+        float psum = 0.f;
+        uint32_t pk[8];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          float e[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][r], p.scale_log2, nm));
+            psum += e[r];
           }
+          pk[kb * 2 + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(e[0], e[1]));
+          pk[kb * 2 + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(e[2], e[3]));
         }
+        l_run[qb] += psum;
+        // k step ks covers key blocks 2 ks and 2 ks + 1
+        pf[qb][0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+        pf[qb][1] = u32x4{pk[4], pk[5], pk[6], pk[7]};
       }
-      *(u32x4*)(&sVt[d * VLD + kb * 16 + half * 8]) = v;
-    }
-    __syncthreads();
-
-    // ---- S^T for the two 16-key blocks ----
-    f32x4 s[2];
+      // ---- O^T += V^T P^T ----
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      s[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        const u32x4 kf = *(const u32x4*)(&sK[(i * 16 + i16) * KLD + ds * 32 + g4 * 8]);
-        s[i] = mfma16(kf, qf[ds], s[i]);
-      }
-    }
-    // lane holds S[query i16][key kt + 16 i + 4 g4 + r]
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t key = kt + i * 16 + g4 * 4 + r;
-        const bool ok = q_ok && key < k_end && key <= q_last_key;
-        const float v = ok ? s[i][r] * p.scale_log2 : -INFINITY;
-        s[i][r] = v;
-        tmax = fmaxf(tmax, v);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    float alpha = 1.f;
-    u32x2 pk[2];
-    if (m_new == -INFINITY) {
-      pk[0] = u32x2{0u, 0u};
-      pk[1] = u32x2{0u, 0u};
-    } else {
-      alpha = exp2f(m_run - m_new);
-      float psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        float e[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          e[r] = exp2f(s[i][r] - m_new);
-          psum += e[r];
+        for (int d = 0; d < DB; ++d) {
+          const u32x4 vf = *(const u32x4*)(&sV[buf][(d * 16 + i16) * VLD + ks * 32 + g4 * 8]);
+          o[d][0] = mfma16(vf, pf[0][ks], o[d][0]);
+          o[d][1] = mfma16(vf, pf[1][ks], o[d][1]);
         }
-        pk[i] = u32x2{__builtin_bit_cast(uint32_t, f16x2{(f16_t)e[0], (f16_t)e[1]}),
-                      __builtin_bit_cast(uint32_t, f16x2{(f16_t)e[2], (f16_t)e[3]})};
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
     }
-    const u32x4 pf = {pk[0][0], pk[0][1], pk[1][0], pk[1][1]};
-    // ---- O^T += V^T P^T ----
-#pragma unroll
-    for (int d = 0; d < DB; ++d) {
-      const f16_t* vr = &sVt[(d * 16 + i16) * VLD];
-      const u32x2 v0 = *(const u32x2*)(vr + g4 * 4);
-      const u32x2 v1 = *(const u32x2*)(vr + 16 + g4 * 4);
-      const u32x4 vf = {v0[0], v0[1], v1[0], v1[1]};
-      o[d] *= alpha;
-      o[d] = mfma16(vf, pf, o[d]);
-    }
+    if (more) sstore(buf ^ 1);
+    blk = blk_next;
     __syncthreads();
   }
-  // combine the four lanes of each query column
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  if (!q_ok) return;
-  // lane holds O^T[d = 16 db + 4 g4 + r][query i16]
-  if (p.n_parts == 1) {
-    f16_t* out = (f16_t*)p.out + ((int64_t)grow * p.hq + head) * HD;
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  if (!wave_active) return;
 #pragma unroll
-    for (int d = 0; d < DB; ++d) {
-      const int dd = d * 16 + g4 * 4;
-      const uint32_t lo = __builtin_bit_cast(uint32_t, f16x2{f2h(o[d][0] * inv), f2h(o[d][1] * inv)});
-      const uint32_t hi = __builtin_bit_cast(uint32_t, f16x2{f2h(o[d][2] * inv), f2h(o[d][3] * inv)});
-      *(u32x2*)(out + dd) = u32x2{lo, hi};
-    }
-  } else {
-    const int64_t qi = (int64_t)part * p.rows * p.hq + (int64_t)grow * p.hq + head;
-    float* po = p.part_o + qi * HD;
+  for (int qb = 0; qb < 2; ++qb) {
+    // combine the four lanes of each query column
+    float l = l_run[qb];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (!q_ok[qb]) continue;
+    // lane holds O^T[d = 16 db + 4 g4 + r][query]
+    if (p.n_parts == 1) {
+      f16_t* out = (f16_t*)p.out + qrow[qb] * HD;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-    for (int d = 0; d < DB; ++d) *(f32x4*)(po + d * 16 + g4 * 4) = o[d];
-    if (g4 == 0) {
-      p.part_ml[qi * 2 + 0] = m_run;
-      p.part_ml[qi * 2 + 1] = l_run;
+      for (int d = 0; d < DB; ++d) {
+        const int dd = d * 16 + g4 * 4;
+        const uint32_t lo = __builtin_bit_cast(uint32_t, f16x2{f2h(o[d][qb][0] * inv), f2h(o[d][qb][1] * inv)});
+        const uint32_t hi = __builtin_bit_cast(uint32_t, f16x2{f2h(o[d][qb][2] * inv), f2h(o[d][qb][3] * inv)});
+        *(u32x2*)(out + dd) = u32x2{lo, hi};
+      }
+    } else {
+      // partial: unnormalised O, and (m, l) with m in exp2 units; a query
+      // that saw no key in this partition has l = 0 and is skipped by the merge
+      const int64_t qi = (int64_t)part * p.rows * p.hq + qrow[qb];
+      float* po = p.part_o + qi * HD;
+#pragma unroll
+      for (int d = 0; d < DB; ++d) *(f32x4*)(po + d * 16 + g4 * 4) = o[d][qb];
+      if (g4 == 0) {
+        p.part_ml[qi * 2 + 0] = m_run[qb];
+        p.part_ml[qi * 2 + 1] = l;
+      }
     }
   }
 }
@@ -293,16 +413,18 @@ k_attn_f32(AttnArgs p, int hd) {
 }
 
 int attention_parts(int rows, int hq, int hkv, int64_t max_keys, int* part_len) {
+  // about one work-group per compute unit (256 CUs), key partitions of at
+  // least 256 keys
   const int G = hq / hkv;
-  const int tiles = (rows * G + 63) / 64;
+  const int tiles = (rows * G + FA_QT - 1) / FA_QT;
   const int base = hkv * tiles;
-  int parts = (512 + base - 1) / base;
+  int parts = (256 + base - 1) / base;
   const int64_t min_len = 256;
   const int64_t cap = (max_keys + min_len - 1) / min_len;
   if (parts > cap) parts = (int)cap;
   if (parts < 1) parts = 1;
   int64_t len = (max_keys + parts - 1) / parts;
-  len = (len + AT_KEYS - 1) / AT_KEYS * AT_KEYS;
+  len = (len + FA_KT - 1) / FA_KT * FA_KT;
   *part_len = (int)len;
   return (int)((max_keys + len - 1) / len);
 }
@@ -334,14 +456,14 @@ hipError_t launch_attention(int dtype, const void* q, int rows, int hq, int hkv,
   a.tstart[0] = 0;
   for (int b = 0; b < rm.n_seq; ++b) {
     const int R = (rm.start[b + 1] - rm.start[b]) * a.G;
-    nt += (R + 63) / 64;
+    nt += (R + FA_QT - 1) / FA_QT;
     a.tstart[b + 1] = nt;
   }
   dim3 grid(nt, hkv, n_parts);
   if (hd == 64)
-    hipLaunchKernelGGL(k_attn_bf16<64>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_attn_bf16<64>, grid, dim3(FA_NT), 0, s, a);
   else
-    hipLaunchKernelGGL(k_attn_bf16<128>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_attn_bf16<128>, grid, dim3(FA_NT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_parts == 1) return e;
   const int64_t nq = (int64_t)rows * hq;
