@@ -89,6 +89,8 @@ struct cad_model {
   double* freq = nullptr;    // [hd/2] rotary frequencies
   int32_t* scratch_i = nullptr;  // [T] argmax of the screening readout
   int32_t* survivors = nullptr;  // [1] screening survivors when the caller passes none
+  float* split_ws = nullptr;     // split-K partial tiles of the tiled GEMM (bf16 models)
+  int32_t* split_cnt = nullptr;  // per-tile arrival counters, zero between launches
 };
 
 namespace {
@@ -196,6 +198,7 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
     GemmArgs g{};
     g.A = m->hn; g.lda = d; g.W = m->w_qkv[li]; g.ldw = d;
     g.M = R; g.N = qkv_rows; g.K = d; g.out_f32 = m->qkv; g.ldo = qkv_rows;
+    g.split_ws = m->split_ws; g.split_cnt = m->split_cnt;
     LAUNCH(PF_QKV, launch_gemm(c.dtype, EPI_STORE_F32, g, s));
     LAUNCH(PF_ROPE, launch_rope_append(c.dtype, m->qkv, R, hq, hkv, hd, m->freq, rm, v, write_limit, m->q,
                                dev_status, s));
@@ -204,6 +207,7 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
     g = GemmArgs{};
     g.A = m->attn; g.lda = hq * hd; g.W = m->w_o[li]; g.ldw = hq * hd;
     g.M = R; g.N = d; g.K = hq * hd; g.out_f32 = m->x; g.ldo = d;
+    g.split_ws = m->split_ws; g.split_cnt = m->split_cnt;
     LAUNCH(PF_O, launch_gemm(c.dtype, EPI_RESID, g, s));
     LAUNCH(PF_NORM, launch_rmsnorm(c.dtype, m->x, m->ffn_norm[li], R, d, c.rms_eps, m->hn, s));
     g = GemmArgs{};
@@ -213,6 +217,7 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
     g = GemmArgs{};
     g.A = m->act; g.lda = F; g.W = m->w_down[li]; g.ldw = F;
     g.M = R; g.N = d; g.K = F; g.out_f32 = m->x; g.ldo = d;
+    g.split_ws = m->split_ws; g.split_cnt = m->split_cnt;
     LAUNCH(PF_DOWN, launch_gemm(c.dtype, EPI_RESID, g, s));
   }
   return CAD_OK;
@@ -226,6 +231,7 @@ cad_status readout(cad_model* m, int R, float* logits, const uint32_t* mask, int
   GemmArgs g{};
   g.A = m->hn; g.lda = c.d_model; g.W = m->lm_head; g.ldw = c.d_model;
   g.M = R; g.N = c.vocab; g.K = c.d_model; g.out_f32 = logits; g.ldo = c.vocab;
+  g.split_ws = m->split_ws; g.split_cnt = m->split_cnt;
   LAUNCH(PF_HEAD, launch_gemm(c.dtype, EPI_STORE_F32, g, s));
   LAUNCH(PF_ARGMAX, launch_argmax(logits, R, c.vocab, mask, argmax, dev_status, s));
   return CAD_OK;
@@ -301,6 +307,9 @@ cad_status cad_model_create(const cad_config* cfg, const cad_weights* w, cad_mod
                o_q = take(T * hq * hd * es), o_attn = take(T * hq * hd * es), o_act = take(T * F * es),
                o_logits = take(T * V * 4), o_po = take(pr * hq * hd * 4), o_pml = take(pr * hq * 2 * 4),
                o_freq = take(hd / 2 * 8), o_si = take(T * 4), o_sv = take(4);
+  const bool split = c.dtype == CAD_BF16;
+  const size_t o_sws = take(split ? (size_t)GEMM_SPLIT_SLOTS * GEMM_TILE_FLOATS * 4 : 0),
+               o_scnt = take(split ? (size_t)GEMM_SPLIT_SLOTS * 4 : 0);
   hipError_t e = hipMalloc(&m->ws, off);
   if (e != hipSuccess) {
     delete m;
@@ -321,9 +330,14 @@ cad_status cad_model_create(const cad_config* cfg, const cad_weights* w, cad_mod
   m->freq = (double*)(base + o_freq);
   m->scratch_i = (int32_t*)(base + o_si);
   m->survivors = (int32_t*)(base + o_sv);
+  if (split) {
+    m->split_ws = (float*)(base + o_sws);
+    m->split_cnt = (int32_t*)(base + o_scnt);
+  }
   std::vector<double> fr(hd / 2);
   for (int64_t i = 0; i < hd / 2; ++i) fr[i] = std::pow((double)c.rope_theta, -2.0 * (double)i / (double)hd);
   e = hipMemcpy(m->freq, fr.data(), fr.size() * 8, hipMemcpyHostToDevice);
+  if (e == hipSuccess && m->split_cnt) e = hipMemset(m->split_cnt, 0, (size_t)GEMM_SPLIT_SLOTS * 4);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     (void)hipFree(m->ws);

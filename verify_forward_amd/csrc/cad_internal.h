@@ -94,7 +94,16 @@ struct GemmArgs {
   float* out_f32;  // STORE_F32 / RESID destination [M][ldo]
   int64_t ldo;
   void* out_act;   // SWIGLU destination [M][N], element type = model dtype
+  // split-K scratch (library workspace): partial tiles and per-tile arrival
+  // counters, which start at zero and are left at zero by every launch
+  float* split_ws;
+  int32_t* split_cnt;
 };
+
+// split-K limits of the tiled GEMM: at most GEMM_SPLIT_SLOTS (tile, split)
+// work-groups carry a partial tile of GEMM_TILE_FLOATS floats
+constexpr int GEMM_SPLIT_SLOTS = 512;
+constexpr int GEMM_TILE_FLOATS = 128 * 128;
 
 // ---- launchers (stream-ordered, no host sync) ----
 hipError_t launch_embed(int dtype, const void* table, int vocab, int d, const int32_t* tokens,

@@ -17,7 +17,13 @@
 //     reduced through LDS in a fixed order.  Every lane loads 32 contiguous
 //     bytes of a weight row per 64-wide k step straight into registers.
 //   * tiled (M > 16): 128x128 output tile per 256-thread work-group, K in
-//     steps of 64 staged through double-buffered LDS.
+//     steps of 64 staged through double-buffered LDS.  When the output has
+//     too few tiles to occupy the 256 compute units, K is split over up to
+//     eight work-groups per tile; each writes its fp32 partial tile to the
+//     workspace and the last to arrive (per-tile counter) sums the partials
+//     in split order and runs the epilogue, so results do not depend on
+//     scheduling.  The global loads run two k steps ahead of the matrix
+//     cores (two register stages in front of the LDS double buffer).
 // fp32 (the small reference-shape path) uses a plain LDS-tiled VALU kernel.
 #include "cad_internal.h"
 
@@ -135,24 +141,36 @@ k_gemm_skinny(GemmArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int TB = 128, TK = 64, TPAD = 8, TLD = TK + TPAD;
 
+// Work-group -> (weight tile tn, activation tile tm, k split), weight tile
+// fastest: the work-groups resident at one time share a few activation
+// tiles, and each XCD (work-groups are dealt to the eight XCDs round-robin)
+// sees every eighth weight tile for all of them.
+__device__ __forceinline__ void gemm_tile_of(int n_tn, int n_tm, int& tn, int& tm, int& sp) {
+  const int id = blockIdx.x;
+  tn = id % n_tn;
+  tm = (id / n_tn) % n_tm;
+  sp = id / (n_tn * n_tm);
+}
+
 template <int EPI>
-__global__ void __launch_bounds__(256)
-k_gemm_tiled(GemmArgs a) {
+__global__ void __launch_bounds__(256, 2)
+k_gemm_tiled(GemmArgs a, int n_tn, int n_tm, int splits) {
   __shared__ __attribute__((aligned(16))) f16_t sw[2][TB * TLD];
   __shared__ __attribute__((aligned(16))) f16_t sa[2][TB * TLD];
+  __shared__ int s_last;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, i16 = lane & 15;
   const int wn = (wave & 1) * 64;   // wave's offset in the weight-row dim of the tile
   const int wm = (wave >> 1) * 64;  // wave's offset in the activation-row dim
-  const int tn = blockIdx.x, tm = blockIdx.y;
+  int tn, tm, sp;
+  gemm_tile_of(n_tn, n_tm, tn, tm, sp);
   const f16_t* A = (const f16_t*)a.A;
   const bf16_t* W = (const bf16_t*)a.W;
 
   // global -> LDS assignment: 4 chunks of 8 bf16 per thread per operand
   const bf16_t* wsrc[4];
   const f16_t* asrc[4];
-  bool aok[4];
   int soff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -170,20 +188,23 @@ k_gemm_tiled(GemmArgs a) {
       wr = min(tn * TB + row, a.N - 1);
     }
     wsrc[i] = W + wr * a.ldw + col;
-    const int ar = tm * TB + row;
-    aok[i] = ar < a.M;
-    asrc[i] = A + (int64_t)(aok[i] ? ar : 0) * a.lda + col;
+    // activation rows past M read row M - 1: their outputs are never stored
+    asrc[i] = A + (int64_t)min(tm * TB + row, a.M - 1) * a.lda + col;
   }
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  u32x4 rw[4], ra[4];
-  auto gload = [&](int k0) {
+  // two register stages: the global loads of k step j are issued two steps
+  // before step j is computed and are written to LDS at the end of step j - 1.
+  // Every load is unconditional (indices are clamped instead) so that the
+  // waits for one stage never cover the other stage's loads.
+  u32x4 rw0[4], ra0[4], rw1[4], ra1[4];
+  auto gload = [&](u32x4 (&rw)[4], u32x4 (&ra)[4], int kt) {
+    const int k0 = kt * TK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       rw[i] = *(const u32x4*)(wsrc[i] + k0);
-      ra[i] = aok[i] ? *(const u32x4*)(asrc[i] + k0) : zero;
+      ra[i] = *(const u32x4*)(asrc[i] + k0);
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](const u32x4 (&rw)[4], const u32x4 (&ra)[4], int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       *(u32x4*)(&sw[buf][soff[i]]) = bf16x8_to_f16x8(rw[i]);
@@ -195,14 +216,7 @@ k_gemm_tiled(GemmArgs a) {
   for (int x = 0; x < 4; ++x)
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nk = a.K / TK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * TK);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < TK / 32; ++ks) {
       u32x4 fw[4], fa[4];
@@ -218,10 +232,56 @@ k_gemm_tiled(GemmArgs a) {
         for (int y = 0; y < 4; ++y)
           acc[x][y] = mfma16(fw[x], fa[y], acc[x][y]);
     }
-    if (kt + 1 < nk) {
-      sstore(buf ^ 1);
-    }
+  };
+
+  const int nk = a.K / TK;
+  const int kt0 = (int)((int64_t)nk * sp / splits), kt1 = (int)((int64_t)nk * (sp + 1) / splits);
+  gload(rw0, ra0, kt0);
+  sstore(rw0, ra0, 0);
+  gload(rw1, ra1, min(kt0 + 1, kt1 - 1));
+  __syncthreads();
+  for (int kt = kt0; kt < kt1; kt += 2) {
+    // even step: LDS buffer 0 holds step kt, stage 1 step kt + 1 (past the
+    // end: a repeat of the last step, staged into a buffer nobody reads)
+    gload(rw0, ra0, min(kt + 2, kt1 - 1));
+    compute(0);
+    sstore(rw1, ra1, 1);
     __syncthreads();
+    if (kt + 1 >= kt1) break;
+    // odd step: LDS buffer 1 holds step kt + 1, stage 0 step kt + 2
+    gload(rw1, ra1, min(kt + 3, kt1 - 1));
+    compute(1);
+    sstore(rw0, ra0, 0);
+    __syncthreads();
+  }
+  if (splits > 1) {
+    // publish this split's partial tile; the last arrival sums all of them
+    const int tile = tm * n_tn + tn;
+    f32x4* mine = (f32x4*)(a.split_ws + ((int64_t)tile * splits + sp) * GEMM_TILE_FLOATS);
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) mine[(x * 4 + y) * 256 + tid] = acc[x][y];
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(&a.split_cnt[tile], 1) == splits - 1;
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    // sum in split order (this work-group's own partial is read back too)
+    const f32x4* all = (const f32x4*)(a.split_ws + (int64_t)tile * splits * GEMM_TILE_FLOATS) + tid;
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) acc[x][y] = all[(x * 4 + y) * 256];
+    for (int q = 1; q < splits; ++q) {
+      const f32x4* pq = all + (int64_t)q * (GEMM_TILE_FLOATS / 4);
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] += pq[(x * 4 + y) * 256];
+    }
+    if (tid == 0) a.split_cnt[tile] = 0;
   }
   // epilogue: acc[x][y] lane -> weight rows wn + 16x + 4g + r, activation row wm + 16y + i16
 #pragma unroll
@@ -310,8 +370,14 @@ static hipError_t launch_epi(int dtype, const GemmArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_gemm_skinny<EPI>, dim3((a.N + 15) / 16), dim3(64 * SK_WAVES), 0, s, a);
   } else {
     const int cols_per_tile = (EPI == EPI_SWIGLU) ? TB / 2 : TB;
-    dim3 grid((a.N + cols_per_tile - 1) / cols_per_tile, (a.M + TB - 1) / TB);
-    hipLaunchKernelGGL(k_gemm_tiled<EPI>, grid, dim3(256), 0, s, a);
+    const int n_tn = (a.N + cols_per_tile - 1) / cols_per_tile, n_tm = (a.M + TB - 1) / TB;
+    const int tiles = n_tn * n_tm, nk = a.K / TK;
+    // split K while the tiles alone leave compute units idle (two
+    // work-groups fit per CU), keeping at least 32 k steps per split
+    int splits = 1;
+    if (EPI != EPI_SWIGLU && a.split_ws && a.split_cnt)
+      while (splits < 8 && tiles * splits * 2 <= GEMM_SPLIT_SLOTS && nk / (splits * 2) >= 32) splits *= 2;
+    hipLaunchKernelGGL(k_gemm_tiled<EPI>, dim3(tiles * splits), dim3(256), 0, s, a, n_tn, n_tm, splits);
   }
   return hipGetLastError();
 }
