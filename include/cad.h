@@ -205,16 +205,20 @@ cad_status cad_splice_forward_looped(cad_model* m, const cad_kv* kv, int64_t L,
                                      float* logits, int32_t* dev_status, cad_stream stream);
 
 /* ---- instrumentation (measurement only, not part of the method) ----
- * When enabled on a model, every kernel launch the model enqueues is
- * bracketed by a pair of hipEvents recorded on the launch's stream, grouped
- * by kernel family: "embed", "rmsnorm", "gemm_qkv", "rope_append",
- * "attention" (partial kernel and merge), "gemm_o", "gemm_gate_up",
- * "gemm_down", "gemm_lm_head", "argmax", "accept", "mask_rows".
- * cad_profile_enable(m, 1) starts a fresh collection (0 stops it; records
- * are kept until the next enable).  cad_profile_read waits for the recorded
- * events of `family` and returns how many launches were recorded and their
- * summed duration in milliseconds.  Unknown family: CAD_E_ARG. */
-cad_status cad_profile_enable(cad_model* m, int32_t enable);
+ * Kernel families, in bit order: 0 "embed", 1 "rmsnorm", 2 "gemm_qkv",
+ * 3 "rope_append", 4 "attention" (the partial-attention kernel), 5
+ * "attn_merge" (the log-sum-exp merge of key partitions), 6 "gemm_o", 7
+ * "gemm_gate_up", 8 "gemm_down", 9 "gemm_lm_head", 10 "argmax", 11 "accept",
+ * 12 "mask_rows".  Each family is one kernel (one named kernel per path).
+ * cad_profile_enable(m, family_mask) starts a fresh collection in which
+ * every launch of a family whose bit is set is bracketed by a pair of
+ * hipEvents recorded on the launch's stream (synchronises the device once);
+ * family_mask 0 stops recording (records are kept until the next start; -1
+ * records every family).  cad_profile_read waits for the recorded events of
+ * `family` and returns how many launches were recorded and their summed
+ * duration in milliseconds.  Unknown family: CAD_E_ARG. */
+#define CAD_PROFILE_ALL (-1)
+cad_status cad_profile_enable(cad_model* m, int32_t family_mask);
 cad_status cad_profile_read(cad_model* m, const char* family, int64_t* launches, double* total_ms);
 
 #ifdef __cplusplus

@@ -54,3 +54,26 @@ def outputs(N: int, vocab: int, n_seq: int = 1, device="cuda"):
                 accepted=torch.full((n_seq,), -7, dtype=torch.int32, device=device),
                 logits=torch.empty((N, vocab), dtype=torch.float32, device=device),
                 status=torch.zeros(1, dtype=torch.int32, device=device))
+
+
+def bf16_ulp(x):
+    """Spacing of bfloat16 numbers at |x| (8 significant bits)."""
+    a = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
+def kv_close(gpu, ref, tol):
+    """Cache entries are stored in bfloat16: a GPU value matches an exact
+    reference value within ``tol`` plus half a bfloat16 spacing at the
+    reference (the rounding that storing any value in the cache applies)."""
+    gpu, ref = np.asarray(gpu, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    excess = np.abs(gpu - ref) - (tol + 0.5 * bf16_ulp(ref))
+    return float(np.max(excess)) <= 0.0, float(np.max(np.abs(gpu - ref)))
+
+
+def kv_close_stored(a, b, tol):
+    """Two bfloat16 caches agree within ``tol`` or one bfloat16 spacing (a
+    value close to a rounding boundary may land on either neighbour)."""
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    lim = np.maximum(tol, bf16_ulp(np.maximum(np.abs(a), np.abs(b))))
+    return bool(np.all(np.abs(a - b) <= lim)), float(np.max(np.abs(a - b)))

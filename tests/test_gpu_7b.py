@@ -1,0 +1,124 @@
+"""GPU parity at the full Llama-style 7B shape, in the launch configuration
+the benchmark times (32 layers, d_model 4096, 32 query / 8 KV heads of 128,
+SwiGLU 14336, vocab 32000, bf16 weights; KV cache of L = 16384 tokens; a copy
+span of N = 512 tokens from a duplicated line of the repeated-line prompt;
+a per-position mask allowing 60% of the vocabulary; COMMIT mode), plus an
+N = 16 splice (the weight-streaming path) over the same cache.
+
+The float64 oracle computes every row of both splices, layer by layer, with
+each layer's weights widened to float64 once (about a minute of CPU).
+
+Bars: logits within 2e-2; appended K/V within 2e-2 plus half a bfloat16
+spacing (the cache stores bfloat16); masked argmax bit-exact where the
+oracle's top-2 margin exceeds 0.1; acceptance N in COMMIT mode.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.decoder import Config, KVCache, splice_layer, final_logits
+import synth
+
+pytestmark = pytest.mark.gpu
+
+cad = pytest.importorskip("verify_forward_amd")
+import gpu_helpers as H  # noqa: E402
+
+TOL = 2e-2
+MARGIN = 0.1
+BLK = cad.CAD_KV_BLOCK
+
+
+def _rows(kv, first, n):
+    """GPU K/V of tokens first..first+n-1 (identity block table, block-aligned
+    start), as float64 [layers][Hkv][n][hd]."""
+    assert first % BLK == 0 and n % BLK == 0
+    b0, nb = first // BLK, n // BLK
+    k = kv.k[:, b0:b0 + nb].permute(0, 2, 1, 3, 4).reshape(kv.k.shape[0], kv.k.shape[2], n, -1)
+    v = kv.v[:, b0:b0 + nb].permute(0, 2, 1, 4, 3).reshape(kv.v.shape[0], kv.v.shape[2], n, -1)
+    return k.to(torch.float64).cpu().numpy(), v.to(torch.float64).cpu().numpy()
+
+
+def _check_decisions(ref, mask, a_gpu):
+    a_ref = oracle.masked_argmax(ref, mask)
+    sure = oracle.top2_margin(ref, mask) > MARGIN
+    assert np.array_equal(a_gpu[sure], a_ref[sure]), (a_gpu[sure], a_ref[sure])
+    return int(sure.sum())
+
+
+def test_llama7b_bench_configuration():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dev = "cuda"
+    shape = synth.LLAMA_7B
+    cfg = Config.of(shape)
+    L, N, NS = 16384, 512, 16
+    W = synth.make_weights(shape, device=dev)
+    k_log, v_log = synth.random_kv_logical(shape, L, device=dev)
+    prompt = synth.make_line_prompt(L, shape.vocab)
+    span = synth.pick_span(prompt, N)
+    span16 = synth.pick_span(prompt, NS, which=1)
+    n_allowed = int(round(0.6 * shape.vocab))
+    mask = synth.allowed_fraction_mask(N, shape.vocab, n_allowed)
+    mask16 = synth.allowed_fraction_mask(NS, shape.vocab, n_allowed, which=1)
+    model = cad.cad_model_create(shape, W, max_tokens=N)
+
+    # ---- GPU: the benchmarked splice, and an N = 16 splice on a fresh copy
+    nb = (L + N) // BLK
+    kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device=dev)
+    H.write_prefix(kv, k_log, v_log)
+    o = H.outputs(N, shape.vocab)
+    cad.cad_splice_forward(model, kv, L, H.tensors_i32(span), torch.from_numpy(mask.view(np.int32)).to(dev),
+                           cad.CAD_COMMIT, o["argmax"], o["accepted"], o["logits"], o["status"])
+    nb16 = (L + NS) // BLK
+    kv16 = cad.KVCache.alloc(shape, nb16, synth.identity_block_table(nb16), device=dev)
+    H.write_prefix(kv16, k_log, v_log)
+    o16 = H.outputs(NS, shape.vocab)
+    cad.cad_splice_forward(model, kv16, L, H.tensors_i32(span16), torch.from_numpy(mask16.view(np.int32)).to(dev),
+                           cad.CAD_COMMIT, o16["argmax"], o16["accepted"], o16["logits"], o16["status"])
+    torch.cuda.synchronize()
+    assert int(o["status"][0]) == 0 and int(o16["status"][0]) == 0
+    assert int(o["accepted"][0]) == N and int(o16["accepted"][0]) == NS
+    gk, gv = _rows(kv, L, N)          # appended K/V of all 512 rows
+    gk16, gv16 = _rows(kv16, L, NS)
+    lg = o["logits"].cpu().numpy()
+    lg16 = o16["logits"].cpu().numpy()
+
+    # ---- oracle, layer by layer: pass A (all N rows), pass C (N = 16)
+    emb = W["tok_embed"]
+    xa = emb[torch.as_tensor(span, device=dev).long()].double().cpu().numpy()
+    xc = emb[torch.as_tensor(span16, device=dev).long()].double().cpu().numpy()
+    ka, va, kc, vc = [], [], [], []
+    hd, hkv = shape.head_dim, shape.n_kv_heads
+    for ci in range(shape.n_layers):
+        lw = {k: t.double().cpu().numpy() for k, t in W["layers"][ci].items()}
+        kp = k_log[ci].double().cpu().numpy()
+        vp = v_log[ci].double().cpu().numpy()
+        zn, z16 = np.zeros((hkv, N, hd)), np.zeros((hkv, NS, hd))
+        cache_a = KVCache([np.concatenate([kp, zn], axis=1)], [np.concatenate([vp, zn], axis=1)])
+        xa = splice_layer(cfg, lw, cache_a, 0, xa, L)
+        ka.append(cache_a.k[0][:, L:]); va.append(cache_a.v[0][:, L:])
+        cache_c = KVCache([np.concatenate([kp, z16], axis=1)], [np.concatenate([vp, z16], axis=1)])
+        xc = splice_layer(cfg, lw, cache_c, 0, xc, L)
+        kc.append(cache_c.k[0][:, L:]); vc.append(cache_c.v[0][:, L:])
+        del lw, kp, vp, cache_a, cache_c
+    top = {"final_norm": W["final_norm"].double().cpu().numpy(), "lm_head": W["lm_head"].double().cpu().numpy()}
+    ref_a, ref_c = final_logits(cfg, top, xa), final_logits(cfg, top, xc)
+
+    errs = {"N=512": np.max(np.abs(lg - ref_a)), "N=16": np.max(np.abs(lg16 - ref_c))}
+    kv_checks = {"kv N=512": [(gk, np.stack(ka)), (gv, np.stack(va))],
+                 "kv N=16": [(gk16, np.stack(kc)), (gv16, np.stack(vc))]}
+    kv_ok = {}
+    for k, pairs in kv_checks.items():
+        res = [H.kv_close(g, r, TOL) for g, r in pairs]
+        kv_ok[k] = all(ok for ok, _ in res)
+        errs[k] = max(e for _, e in res)
+    print("7B max|diff|: " + ", ".join(f"{k} {v:.3e}" for k, v in errs.items()), flush=True)
+    for k in ("N=512", "N=16"):
+        assert errs[k] <= TOL, (k, errs[k])
+    for k, ok in kv_ok.items():
+        assert ok, (k, errs[k])
+    graded = _check_decisions(ref_a, mask, o["argmax"].cpu().numpy())
+    graded += _check_decisions(ref_c, mask16, o16["argmax"].cpu().numpy())
+    print(f"7B argmax bit-exact on {graded}/{N + NS} graded rows", flush=True)

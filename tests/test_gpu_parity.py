@@ -214,10 +214,10 @@ def test_llama1b_bf16_splice(llama1b, N):
     assert err <= TOL["bf16"]
     check_decisions(ref, None, o["argmax"].cpu().numpy(), span, VERIFY, int(o["accepted"][0]))
     gk, gv = H.read_seq(kv, L + N)
-    ek = np.max(np.abs(gk[:, :, L:] - np.stack([okv.k[c][:, L:L + N] for c in range(cfg.n_layers)])))
-    ev = np.max(np.abs(gv[:, :, L:] - np.stack([okv.v[c][:, L:L + N] for c in range(cfg.n_layers)])))
+    okk, ek = H.kv_close(gk[:, :, L:], np.stack([okv.k[c][:, L:L + N] for c in range(cfg.n_layers)]), TOL["bf16"])
+    okv_, ev = H.kv_close(gv[:, :, L:], np.stack([okv.v[c][:, L:L + N] for c in range(cfg.n_layers)]), TOL["bf16"])
     print(f"N={N} kv max|diff| = {ek:.3e} / {ev:.3e}", flush=True)
-    assert ek <= TOL["bf16"] and ev <= TOL["bf16"]
+    assert okk and okv_
     # canaries: the prefix and every slot past L + N are bit-unchanged
     nfull = L // 16
     assert torch.equal(kv.k[:, :nfull], k_before[:, :nfull])
@@ -250,8 +250,11 @@ def test_llama1b_splice_equals_decode_steps(llama1b):
         cad.cad_decode_step(model, kv2, L + j, span_t[j:j + 1], None, am[j:j + 1], lg[j])
     torch.cuda.synchronize()
     assert torch.max(torch.abs(lg - o["logits"])).item() <= TOL["bf16"]
-    assert torch.max(torch.abs(kv2.k.float() - kv.k.float())).item() <= TOL["bf16"]
-    assert torch.max(torch.abs(kv2.v.float() - kv.v.float())).item() <= TOL["bf16"]
+    # both caches hold bfloat16: the splice reads its own keys at half
+    # precision, the steps read earlier steps' keys back from the cache
+    ok_k, _ = H.kv_close_stored(kv2.k.float().cpu().numpy(), kv.k.float().cpu().numpy(), TOL["bf16"])
+    ok_v, _ = H.kv_close_stored(kv2.v.float().cpu().numpy(), kv.v.float().cpu().numpy(), TOL["bf16"])
+    assert ok_k and ok_v
 
 
 def test_deterministic_rerun(llama1b):

@@ -1,0 +1,247 @@
+"""GPU parity of the two splice variants against the float64 oracle.
+
+* Batched paged splice (continuous-batching form; Copy-as-Decode §7 names
+  paged attention and batching as the integration path): independent
+  sequences with their own cache lengths share one paged pool through a
+  shuffled block table; each sequence commits a one-token generation step or
+  a copy span of whole lines.  The oracle is the per-sequence splice.
+* Looped decoder with shallow screening (CopyLoop §2 "Block Construction",
+  "Shallow Screening", "Full-Depth Verification"): a block [head, copied
+  tail] proposed by the suffix matcher runs to the screening depth, the
+  agreeing prefix survives to full depth and is verified there.  A second
+  case plants the full-depth greedy chain with screening at full depth, so
+  every position must be accepted.
+
+Bars as in the other parity tests: logits within 2e-2 and K/V within 2e-2
+plus half a bfloat16 spacing (bf16 models),
+argmax and acceptance bit-exact where every position they depend on has an
+oracle top-2 margin above 0.1; the suffix-match proposal is always exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.decision import VERIFY, COMMIT
+from oracle.decoder import Config, KVCache
+import synth
+
+pytestmark = pytest.mark.gpu
+
+cad = pytest.importorskip("verify_forward_amd")
+import gpu_helpers as H  # noqa: E402
+
+TOL = 2e-2
+MARGIN = 0.1
+BLK = cad.CAD_KV_BLOCK
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return "cuda"
+
+
+def _f64_weights(W):
+    conv = lambda t: t.double().cpu().numpy()
+    return {"tok_embed": conv(W["tok_embed"]), "final_norm": conv(W["final_norm"]), "lm_head": conv(W["lm_head"]),
+            "layers": [{k: conv(v) for k, v in lw.items()} for lw in W["layers"]]}
+
+
+def _acceptance_graded(ref, mask, span, mode):
+    """Oracle acceptance and whether every position it examined is graded."""
+    a = oracle.masked_argmax(ref, mask)
+    acc = oracle.acceptance(a, span, mode)
+    sure = oracle.top2_margin(ref, mask) > MARGIN
+    examined = acc if acc < len(span) else len(span) - 1
+    return acc, a, sure, mode == COMMIT or bool(sure[:examined].all())
+
+
+# ---------------------------------------------------------------------------
+# batched paged splice, 1B shape
+# ---------------------------------------------------------------------------
+
+def test_batched_paged_splice_1b():
+    dev = _dev()
+    shape = synth.LLAMA_1B
+    cfg = Config.of(shape)
+    W = synth.make_weights(shape, device=dev)
+    W64 = _f64_weights(W)
+    r = synth.rng(31, 4)
+    n_seq = 6
+    Ls = [int(x) for x in r.integers(40, 1400, size=n_seq)]
+    Ls[0] = 1023                       # ends one slot before a block boundary
+    prompts = [synth.make_line_prompt(1600, shape.vocab, seed=100 + b, line_len_range=(8, 16)) for b in range(n_seq)]
+    spans = []
+    for b in range(n_seq):
+        if b % 3 == 2:                 # a one-token generation step
+            spans.append(np.array([int(r.integers(0, shape.vocab))], dtype=np.int32))
+        else:                          # a copy of whole duplicated lines
+            st = int(prompts[b].dup_starts[int(r.integers(0, len(prompts[b].dup_starts)))])
+            idx = int(np.searchsorted(prompts[b].line_starts, st))
+            end = int(prompts[b].line_starts[min(idx + 1 + b % 3, len(prompts[b].line_starts) - 1)])
+            spans.append(prompts[b].tokens[st:max(end, st + 2)][:48].copy())
+    offsets = np.concatenate([[0], np.cumsum([len(s) for s in spans])]).astype(np.int32)
+    total = int(offsets[-1])
+    mask = synth.banned_ids_mask(total, shape.vocab, 500, seed=9)
+    # paged pool: every sequence takes its blocks from one shuffled permutation
+    need = [(Ls[b] + len(spans[b]) + BLK - 1) // BLK for b in range(n_seq)]
+    max_blocks = max(need)
+    pool = int(sum(need)) + 7
+    perm = synth.shuffled_block_table(pool, pool, seed=5).numpy()
+    table = np.full((n_seq, max_blocks), -1, dtype=np.int32)
+    used = 0
+    for b in range(n_seq):
+        table[b, :need[b]] = perm[used:used + need[b]]
+        used += need[b]
+    kv = cad.KVCache.alloc(shape, pool, torch.from_numpy(table), device=dev)
+    kv.k.fill_(3.0)
+    kv.v.fill_(3.0)
+    pre = []
+    for b in range(n_seq):
+        kl, vl = synth.random_kv_logical(shape, Ls[b], seed=200 + b, device=dev)
+        H.write_prefix(kv, kl, vl, seq=b)
+        pre.append((kl, vl))
+    k_before = kv.k.clone()
+    model = cad.cad_model_create(shape, W, max_tokens=total)
+    o = H.outputs(total, shape.vocab, n_seq=n_seq)
+    cad.cad_splice_forward_batched(model, kv, Ls, offsets, H.tensors_i32(np.concatenate(spans)),
+                                   torch.from_numpy(mask.view(np.int32)).to(dev), cad.CAD_VERIFY,
+                                   o["argmax"], o["accepted"], o["logits"], o["status"])
+    torch.cuda.synchronize()
+    assert int(o["status"][0]) == 0
+    lg = o["logits"].cpu().numpy()
+    am = o["argmax"].cpu().numpy()
+    acc = o["accepted"].cpu().numpy()
+    for b in range(n_seq):
+        s0, s1 = int(offsets[b]), int(offsets[b + 1])
+        kl, vl = pre[b]
+        okv = KVCache.from_prefix(kl.double().cpu().numpy(), vl.double().cpu().numpy(), Ls[b] + len(spans[b]))
+        ref = oracle.splice(cfg, W64, okv, Ls[b], spans[b])
+        err = np.max(np.abs(lg[s0:s1] - ref))
+        print(f"seq {b}: L={Ls[b]} N={len(spans[b])} logits max|diff| {err:.3e}", flush=True)
+        assert err <= TOL
+        acc_ref, a_ref, sure, graded = _acceptance_graded(ref, mask[s0:s1], spans[b], VERIFY)
+        assert np.array_equal(am[s0:s1][sure], a_ref[sure])
+        if graded:
+            assert acc[b] == acc_ref
+        gk, gv = H.read_seq(kv, Ls[b] + len(spans[b]), seq=b)
+        ok_k, _ = H.kv_close(gk[:, :, Ls[b]:], np.stack([okv.k[c][:, Ls[b]:] for c in range(cfg.n_layers)]), TOL)
+        ok_v, _ = H.kv_close(gv[:, :, Ls[b]:], np.stack([okv.v[c][:, Ls[b]:] for c in range(cfg.n_layers)]), TOL)
+        assert ok_k and ok_v
+    # blocks no sequence owns are untouched
+    free = perm[used:]
+    assert torch.equal(kv.k[:, torch.as_tensor(free, device=dev).long()],
+                       k_before[:, torch.as_tensor(free, device=dev).long()])
+
+
+# ---------------------------------------------------------------------------
+# looped shared block with shallow screening
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def looped():
+    dev = _dev()
+    shape = synth.LOOPED
+    W = synth.make_weights(shape, device=dev)
+    W64 = _f64_weights(W)
+    L = 4096
+    kl, vl = synth.random_kv_logical(shape, L, device=dev)
+    prompt = synth.make_line_prompt(L, shape.vocab)
+    model = cad.cad_model_create(shape, W, max_tokens=16)
+    return shape, W, W64, L, kl, vl, prompt, model
+
+
+def _looped_cache(shape, L, kl, vl, N, dev):
+    nb = (L + N + BLK - 1) // BLK
+    kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device=dev)
+    H.write_prefix(kv, kl, vl)
+    return kv
+
+
+def test_looped_screening_natural(looped):
+    dev = _dev()
+    shape, W, W64, L, kl, vl, prompt, model = looped
+    cfg = Config.of(shape)
+    D, ds, K = shape.loop_depth, 2, 8
+    # history = prompt + a head equal to the first token of a duplicated line,
+    # so the suffix matcher finds an earlier occurrence to copy from
+    head = int(prompt.tokens[int(prompt.dup_starts[3])])
+    hist = np.concatenate([prompt.tokens, [head]]).astype(np.int32)
+    out_t = torch.full((K,), -9, dtype=torch.int32, device=dev)
+    out_n = torch.full((1,), -9, dtype=torch.int32, device=dev)
+    out_p = torch.full((1,), -9, dtype=torch.int64, device=dev)
+    cad.cad_propose_suffix_match(H.tensors_i32(hist), 4, 1, K, out_t, out_n, out_p)
+    torch.cuda.synchronize()
+    prop, pos = oracle.suffix_match(hist, 4, 1, K)
+    n = int(out_n[0])
+    assert n == len(prop) and int(out_p[0]) == pos and list(out_t[:n].cpu().numpy()) == list(prop)
+    span = np.concatenate([[head], prop]).astype(np.int32)
+    N = len(span)
+    kv = _looped_cache(shape, L, kl, vl, N, dev)
+    sa = torch.full((N,), -9, dtype=torch.int32, device=dev)
+    sv = torch.full((1,), -9, dtype=torch.int32, device=dev)
+    o = H.outputs(N, shape.vocab)
+    cad.cad_splice_forward_looped(model, kv, L, H.tensors_i32(span), ds, None, sa, sv, o["argmax"], o["accepted"],
+                                  o["logits"], o["status"])
+    okv = KVCache.from_prefix(kl.double().cpu().numpy(), vl.double().cpu().numpy(), L + N)
+    res = oracle.looped_splice(cfg, W64, okv, L, span, ds)
+    torch.cuda.synchronize()
+    assert int(o["status"][0]) == 0
+    s_ref = res["screen_logits"]
+    sure = oracle.top2_margin(s_ref, None) > MARGIN
+    sa_gpu = sa.cpu().numpy()
+    assert np.array_equal(sa_gpu[sure], res["screen_argmax"][sure])
+    m = res["survivors"]
+    examined = m if m < N else N - 1
+    if sure[:examined].all():
+        assert int(sv[0]) == m
+        lg = o["logits"].cpu().numpy()[:m]
+        err = np.max(np.abs(lg - res["logits"]))
+        print(f"looped natural: N={N} survivors {m} full-depth logits max|diff| {err:.3e}", flush=True)
+        assert err <= TOL
+        acc_ref, a_ref, sure_f, graded = _acceptance_graded(res["logits"], None, list(span[:m]), VERIFY)
+        a_gpu = o["argmax"].cpu().numpy()
+        assert np.array_equal(a_gpu[:m][sure_f], a_ref[sure_f])
+        assert (a_gpu[m:] == -1).all()
+        if graded:
+            assert int(o["accepted"][0]) == acc_ref
+
+
+def test_looped_planted_full_depth_chain(looped):
+    """Screening at full depth and a span planted from the oracle's own
+    full-depth greedy chain: all N positions are accepted, and corrupting
+    position j stops acceptance exactly there."""
+    dev = _dev()
+    shape, W, W64, L, kl, vl, prompt, model = looped
+    cfg = Config.of(shape)
+    D, N = shape.loop_depth, 9
+    base = KVCache.from_prefix(kl.double().cpu().numpy(), vl.double().cpu().numpy(), L + N)
+    span = None
+    for head in (17, 4242, 31000, 2024, 777):
+        chain = base.copy()
+        s = [head]
+        lgs = []
+        for j in range(N):
+            lg = oracle.decode_step(cfg, W64, chain, L + j, s[j])[None]
+            lgs.append(lg[0])
+            if j + 1 < N:
+                s.append(int(oracle.masked_argmax(lg, None)[0]))
+        if (oracle.top2_margin(np.stack(lgs), None)[:N - 1] > MARGIN).all():
+            span = s
+            break
+    if span is None:
+        pytest.skip("no planted chain with all top-2 margins above 0.1 among the candidate heads")
+    for bad_at in (None, 3):
+        sp = list(span)
+        if bad_at is not None:
+            sp[bad_at] = (sp[bad_at] + 1) % shape.vocab
+        kv = _looped_cache(shape, L, kl, vl, N, dev)
+        sa = torch.full((N,), -9, dtype=torch.int32, device=dev)
+        sv = torch.full((1,), -9, dtype=torch.int32, device=dev)
+        o = H.outputs(N, shape.vocab)
+        cad.cad_splice_forward_looped(model, kv, L, H.tensors_i32(sp), D, None, sa, sv, o["argmax"],
+                                      o["accepted"], o["logits"], o["status"])
+        torch.cuda.synchronize()
+        want = N if bad_at is None else bad_at
+        assert int(sv[0]) == want and int(o["accepted"][0]) == want

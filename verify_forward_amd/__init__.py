@@ -28,8 +28,9 @@ EXPORTS = ("cad_model_create", "cad_model_destroy", "cad_last_error", "cad_splic
            "cad_decode_step", "cad_propose_suffix_match", "cad_splice_forward_batched",
            "cad_splice_forward_looped", "cad_profile_enable", "cad_profile_read")
 
-PROFILE_FAMILIES = ("embed", "rmsnorm", "gemm_qkv", "rope_append", "attention", "gemm_o", "gemm_gate_up",
-                    "gemm_down", "gemm_lm_head", "argmax", "accept", "mask_rows")
+PROFILE_FAMILIES = ("embed", "rmsnorm", "gemm_qkv", "rope_append", "attention", "attn_merge", "gemm_o",
+                    "gemm_gate_up", "gemm_down", "gemm_lm_head", "argmax", "accept", "mask_rows")
+CAD_PROFILE_ALL = -1
 
 
 class CadError(RuntimeError):
@@ -245,8 +246,18 @@ def cad_splice_forward_looped(model: Model, kv: KVCache, L: int, span: torch.Ten
                                            _stream(stream)))
 
 
-def cad_profile_enable(model: Model, enable: bool = True):
-    _check(lib().cad_profile_enable(model.handle, 1 if enable else 0))
+def cad_profile_enable(model: Model, families=CAD_PROFILE_ALL):
+    """Record launch events for ``families``: an iterable of family names,
+    ``CAD_PROFILE_ALL`` (every family) or a false value (stop recording)."""
+    if families is True or families == CAD_PROFILE_ALL:
+        mask = CAD_PROFILE_ALL
+    elif not families:
+        mask = 0
+    else:
+        mask = 0
+        for f in families:
+            mask |= 1 << PROFILE_FAMILIES.index(f)
+    _check(lib().cad_profile_enable(model.handle, mask))
 
 
 def cad_profile_read(model: Model, family: str):

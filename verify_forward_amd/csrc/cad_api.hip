@@ -48,12 +48,12 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 }  // namespace
 
 enum ProfFamily {
-  PF_EMBED, PF_NORM, PF_QKV, PF_ROPE, PF_ATTN, PF_O, PF_GATEUP, PF_DOWN, PF_HEAD, PF_ARGMAX,
-  PF_ACCEPT, PF_MASKROWS, PF_COUNT
+  PF_EMBED, PF_NORM, PF_QKV, PF_ROPE, PF_ATTN, PF_MERGE, PF_O, PF_GATEUP, PF_DOWN, PF_HEAD,
+  PF_ARGMAX, PF_ACCEPT, PF_MASKROWS, PF_COUNT
 };
 static const char* const kProfNames[PF_COUNT] = {
-    "embed", "rmsnorm", "gemm_qkv", "rope_append", "attention", "gemm_o", "gemm_gate_up",
-    "gemm_down", "gemm_lm_head", "argmax", "accept", "mask_rows"};
+    "embed", "rmsnorm", "gemm_qkv", "rope_append", "attention", "attn_merge", "gemm_o",
+    "gemm_gate_up", "gemm_down", "gemm_lm_head", "argmax", "accept", "mask_rows"};
 
 struct ProfRec {
   int family;
@@ -63,7 +63,7 @@ struct ProfRec {
 struct cad_model {
   cad_config cfg;
   // instrumentation
-  bool prof_on = false;
+  uint32_t prof_mask = 0;  // families whose launches are bracketed by events
   std::vector<ProfRec> prof;
   std::vector<hipEvent_t> prof_pool;
   size_t prof_used = 0;
@@ -77,7 +77,9 @@ struct cad_model {
   void* ws = nullptr;
   size_t ws_bytes = 0;
   float* x = nullptr;        // [T][d] residual stream
-  void* hn = nullptr;        // [T][d] normalised activations (model dtype)
+  // activations feeding a projection: fp32 [T][n] (fp32 models) or two half
+  // planes [T][n] each, hi then lo (bf16 models), in the same bytes
+  void* hn = nullptr;        // [T][d] normalised activations
   float* qkv = nullptr;      // [T][(hq+2hkv) hd]
   void* q = nullptr;         // [T][hq][hd] rotated queries
   void* attn = nullptr;      // [T][hq hd] attention output
@@ -89,6 +91,9 @@ struct cad_model {
   double* freq = nullptr;    // [hd/2] rotary frequencies
   int32_t* scratch_i = nullptr;  // [T] argmax of the screening readout
   int32_t* survivors = nullptr;  // [1] screening survivors when the caller passes none
+  f16_t* span_k = nullptr;       // this call's span K/V at half precision (bf16 models)
+  f16_t* span_v = nullptr;
+  int32_t span_cap = 0;          // rows of the span workspace
   float* split_ws = nullptr;     // split-K partial tiles of the tiled GEMM (bf16 models)
   int32_t* split_cnt = nullptr;  // per-tile arrival counters, zero between launches
 };
@@ -109,7 +114,7 @@ hipEvent_t prof_event(cad_model* m) {
 // Launch `fn` (returning hipError_t), bracketed by events when profiling.
 template <typename Fn>
 hipError_t prof_launch(cad_model* m, int family, hipStream_t s, Fn fn) {
-  if (!m->prof_on) return fn();
+  if (!(m->prof_mask >> family & 1u)) return fn();
   ProfRec r{family, prof_event(m), prof_event(m)};
   if (r.a && r.b) (void)hipEventRecord(r.a, s);
   hipError_t e = fn();
@@ -149,8 +154,8 @@ int64_t max_parts_rows(const cad_config& c) {
   int64_t best = 0;
   for (int r = 1; r <= c.max_tokens; ++r) {
     int len = 0;
-    const int p = attention_parts(r, c.n_q_heads, c.n_kv_heads, (int64_t)1 << 40, &len);
-    if (p > 1 && (int64_t)p * r > best) best = (int64_t)p * r;
+    const int p = attention_parts(r, c.n_q_heads, c.n_kv_heads, (int64_t)1 << 40, &len) + 1;
+    if ((int64_t)p * r > best) best = (int64_t)p * r;
   }
   return best;
 }
@@ -173,7 +178,15 @@ KVView view_of(const cad_model* m, const cad_kv* kv, int ci) {
   v.table = kv->block_table;
   v.num_blocks = kv->num_blocks;
   v.max_blocks = kv->max_blocks_per_seq;
+  v.span_k = m->span_k;
+  v.span_v = m->span_v;
+  v.span_cap = m->span_cap;
   return v;
+}
+
+// lo plane of an activation buffer (bf16 models): after the T x n hi plane
+void* lo_plane(const cad_model* m, void* buf, int64_t n) {
+  return m->cfg.dtype == CAD_BF16 ? (void*)((f16_t*)buf + (int64_t)m->cfg.max_tokens * n) : nullptr;
 }
 
 // Run cache indices [c0, c1) over the rows already embedded in m->x.
@@ -183,42 +196,48 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
   const int R = rm.total;
   const int d = c.d_model, hq = c.n_q_heads, hkv = c.n_kv_heads, hd = c.head_dim, F = c.ffn_dim;
   const int qkv_rows = (hq + 2 * hkv) * hd;
-  int64_t max_keys = 0;
-  for (int b = 0; b < rm.n_seq; ++b) {
-    const int64_t e = rm.L[b] + (rm.start[b + 1] - rm.start[b]);
-    if (e > max_keys) max_keys = e;
-  }
+  int64_t max_L = 0;
+  for (int b = 0; b < rm.n_seq; ++b) max_L = rm.L[b] > max_L ? rm.L[b] : max_L;
   int part_len = 0;
-  int n_parts = attention_parts(R, hq, hkv, max_keys, &part_len);
-  if ((int64_t)n_parts * R > m->part_cap) n_parts = 1, part_len = (int)max_keys + 64;
+  const int n_parts = attention_parts(R, hq, hkv, max_L, &part_len) + 1;  // + the span partition
+  if ((int64_t)n_parts * R > m->part_cap)
+    return fail(CAD_E_CAPACITY, "attention partitions %d x %d rows exceed the workspace", n_parts, R);
+  if (c.dtype == CAD_BF16 && rm.pstart[rm.n_seq] > m->span_cap)
+    return fail(CAD_E_CAPACITY, "span workspace too small for %d padded rows", rm.pstart[rm.n_seq]);
   for (int ci = c0; ci < c1; ++ci) {
     const int li = c.loop_depth > 1 ? 0 : ci;
     const KVView v = view_of(m, kv, ci);
-    LAUNCH(PF_NORM, launch_rmsnorm(c.dtype, m->x, m->attn_norm[li], R, d, c.rms_eps, m->hn, s));
+    LAUNCH(PF_NORM, launch_rmsnorm(c.dtype, m->x, m->attn_norm[li], R, d, c.rms_eps, m->hn,
+                                   lo_plane(m, m->hn, d), s));
     GemmArgs g{};
-    g.A = m->hn; g.lda = d; g.W = m->w_qkv[li]; g.ldw = d;
+    g.A = m->hn; g.A_lo = lo_plane(m, m->hn, d); g.lda = d; g.W = m->w_qkv[li]; g.ldw = d;
     g.M = R; g.N = qkv_rows; g.K = d; g.out_f32 = m->qkv; g.ldo = qkv_rows;
     g.split_ws = m->split_ws; g.split_cnt = m->split_cnt;
-    LAUNCH(PF_QKV, launch_gemm(c.dtype, EPI_STORE_F32, g, s));
+    LAUNCH(PF_QKV, launch_gemm(c.dtype, GEMM_QKV, g, s));
     LAUNCH(PF_ROPE, launch_rope_append(c.dtype, m->qkv, R, hq, hkv, hd, m->freq, rm, v, write_limit, m->q,
                                dev_status, s));
     LAUNCH(PF_ATTN, launch_attention(c.dtype, m->q, R, hq, hkv, hd, rm, v, n_parts, part_len, m->part_o,
-                             m->part_ml, m->attn, dev_status, s));
+                                     m->part_ml, m->attn, lo_plane(m, m->attn, (int64_t)hq * hd), dev_status, s));
+    if (c.dtype == CAD_BF16 && n_parts > 1)
+      LAUNCH(PF_MERGE, launch_attention_merge(m->part_o, m->part_ml, n_parts, R, hq, hd, m->attn,
+                                              lo_plane(m, m->attn, (int64_t)hq * hd), s));
     g = GemmArgs{};
-    g.A = m->attn; g.lda = hq * hd; g.W = m->w_o[li]; g.ldw = hq * hd;
+    g.A = m->attn; g.A_lo = lo_plane(m, m->attn, (int64_t)hq * hd); g.lda = hq * hd;
+    g.W = m->w_o[li]; g.ldw = hq * hd;
     g.M = R; g.N = d; g.K = hq * hd; g.out_f32 = m->x; g.ldo = d;
     g.split_ws = m->split_ws; g.split_cnt = m->split_cnt;
-    LAUNCH(PF_O, launch_gemm(c.dtype, EPI_RESID, g, s));
-    LAUNCH(PF_NORM, launch_rmsnorm(c.dtype, m->x, m->ffn_norm[li], R, d, c.rms_eps, m->hn, s));
+    LAUNCH(PF_O, launch_gemm(c.dtype, GEMM_O, g, s));
+    LAUNCH(PF_NORM, launch_rmsnorm(c.dtype, m->x, m->ffn_norm[li], R, d, c.rms_eps, m->hn,
+                                   lo_plane(m, m->hn, d), s));
     g = GemmArgs{};
-    g.A = m->hn; g.lda = d; g.W = m->w_gate_up[li]; g.ldw = d;
-    g.M = R; g.N = F; g.K = d; g.up_off = F; g.out_act = m->act;
-    LAUNCH(PF_GATEUP, launch_gemm(c.dtype, EPI_SWIGLU, g, s));
+    g.A = m->hn; g.A_lo = lo_plane(m, m->hn, d); g.lda = d; g.W = m->w_gate_up[li]; g.ldw = d;
+    g.M = R; g.N = F; g.K = d; g.up_off = F; g.out_act = m->act; g.out_act_lo = lo_plane(m, m->act, F);
+    LAUNCH(PF_GATEUP, launch_gemm(c.dtype, GEMM_GATE_UP, g, s));
     g = GemmArgs{};
-    g.A = m->act; g.lda = F; g.W = m->w_down[li]; g.ldw = F;
+    g.A = m->act; g.A_lo = lo_plane(m, m->act, F); g.lda = F; g.W = m->w_down[li]; g.ldw = F;
     g.M = R; g.N = d; g.K = F; g.out_f32 = m->x; g.ldo = d;
     g.split_ws = m->split_ws; g.split_cnt = m->split_cnt;
-    LAUNCH(PF_DOWN, launch_gemm(c.dtype, EPI_RESID, g, s));
+    LAUNCH(PF_DOWN, launch_gemm(c.dtype, GEMM_DOWN, g, s));
   }
   return CAD_OK;
 }
@@ -227,12 +246,13 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
 cad_status readout(cad_model* m, int R, float* logits, const uint32_t* mask, int32_t* argmax,
                    int32_t* dev_status, hipStream_t s) {
   const cad_config& c = m->cfg;
-  LAUNCH(PF_NORM, launch_rmsnorm(c.dtype, m->x, m->final_norm, R, c.d_model, c.rms_eps, m->hn, s));
+  LAUNCH(PF_NORM, launch_rmsnorm(c.dtype, m->x, m->final_norm, R, c.d_model, c.rms_eps, m->hn,
+                                 lo_plane(m, m->hn, c.d_model), s));
   GemmArgs g{};
-  g.A = m->hn; g.lda = c.d_model; g.W = m->lm_head; g.ldw = c.d_model;
+  g.A = m->hn; g.A_lo = lo_plane(m, m->hn, c.d_model); g.lda = c.d_model; g.W = m->lm_head; g.ldw = c.d_model;
   g.M = R; g.N = c.vocab; g.K = c.d_model; g.out_f32 = logits; g.ldo = c.vocab;
   g.split_ws = m->split_ws; g.split_cnt = m->split_cnt;
-  LAUNCH(PF_HEAD, launch_gemm(c.dtype, EPI_STORE_F32, g, s));
+  LAUNCH(PF_HEAD, launch_gemm(c.dtype, GEMM_LM_HEAD, g, s));
   LAUNCH(PF_ARGMAX, launch_argmax(logits, R, c.vocab, mask, argmax, dev_status, s));
   return CAD_OK;
 }
@@ -303,12 +323,14 @@ cad_status cad_model_create(const cad_config* cfg, const cad_weights* w, cad_mod
   const int64_t pr = max_parts_rows(c);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
-  const size_t o_x = take(T * d * 4), o_hn = take(T * d * es), o_qkv = take(T * (hq + 2 * hkv) * hd * 4),
-               o_q = take(T * hq * hd * es), o_attn = take(T * hq * hd * es), o_act = take(T * F * es),
+  const size_t o_x = take(T * d * 4), o_hn = take(T * d * 4), o_qkv = take(T * (hq + 2 * hkv) * hd * 4),
+               o_q = take(T * hq * hd * es), o_attn = take(T * hq * hd * 4), o_act = take(T * F * 4),
                o_logits = take(T * V * 4), o_po = take(pr * hq * hd * 4), o_pml = take(pr * hq * 2 * 4),
                o_freq = take(hd / 2 * 8), o_si = take(T * 4), o_sv = take(4);
   const bool split = c.dtype == CAD_BF16;
-  const size_t o_sws = take(split ? (size_t)GEMM_SPLIT_SLOTS * GEMM_TILE_FLOATS * 4 : 0),
+  const int64_t span_cap = split ? (T + 64 * CAD_MAX_SEQS + 63) / 64 * 64 : 0;
+  const size_t o_spk = take((size_t)span_cap * hkv * hd * 2), o_spv = take((size_t)span_cap * hkv * hd * 2);
+  const size_t o_sws = take(split ? (size_t)GEMM_SPLIT_FLOATS * 4 : 0),
                o_scnt = take(split ? (size_t)GEMM_SPLIT_SLOTS * 4 : 0);
   hipError_t e = hipMalloc(&m->ws, off);
   if (e != hipSuccess) {
@@ -331,6 +353,9 @@ cad_status cad_model_create(const cad_config* cfg, const cad_weights* w, cad_mod
   m->scratch_i = (int32_t*)(base + o_si);
   m->survivors = (int32_t*)(base + o_sv);
   if (split) {
+    m->span_k = (f16_t*)(base + o_spk);
+    m->span_v = (f16_t*)(base + o_spv);
+    m->span_cap = (int32_t)span_cap;
     m->split_ws = (float*)(base + o_sws);
     m->split_cnt = (int32_t*)(base + o_scnt);
   }
@@ -372,6 +397,7 @@ cad_status cad_splice_forward(cad_model* m, const cad_kv* kv, int64_t L, const i
   rm.start[0] = 0;
   rm.start[1] = N;
   rm.L[0] = L;
+  rowmap_pad(rm);
   const cad_config& c = m->cfg;
   LAUNCH(PF_EMBED, launch_embed(c.dtype, m->tok_embed, c.vocab, c.d_model, span, N, m->x, dev_status, s));
   st = run_blocks(m, kv, rm, 0, c.n_layers, nullptr, dev_status, s);
@@ -413,6 +439,7 @@ cad_status cad_splice_forward_batched(cad_model* m, const cad_kv* kv, int32_t n_
   }
   rm.start[n_seq] = offsets[n_seq];
   rm.total = offsets[n_seq];
+  rowmap_pad(rm);
   if (rm.total > m->cfg.max_tokens)
     return fail(CAD_E_CAPACITY, "total rows %d > max_tokens %d", rm.total, m->cfg.max_tokens);
   hipStream_t s = (hipStream_t)stream;
@@ -446,6 +473,7 @@ cad_status cad_splice_forward_looped(cad_model* m, const cad_kv* kv, int64_t L,
   rm.total = N;
   rm.start[1] = N;
   rm.L[0] = L;
+  rowmap_pad(rm);
   LAUNCH(PF_EMBED, launch_embed(c.dtype, m->tok_embed, c.vocab, c.d_model, span, N, m->x, dev_status, s));
   st = run_blocks(m, kv, rm, 0, screen_depth, nullptr, dev_status, s);
   if (st != CAD_OK) return st;
@@ -461,14 +489,14 @@ cad_status cad_splice_forward_looped(cad_model* m, const cad_kv* kv, int64_t L,
   return CAD_OK;
 }
 
-cad_status cad_profile_enable(cad_model* m, int32_t enable) {
+cad_status cad_profile_enable(cad_model* m, int32_t family_mask) {
   if (!m) return fail(CAD_E_ARG, "model is NULL");
-  if (enable) {
+  if (family_mask) {
     HIP_TRY(hipDeviceSynchronize());
     m->prof.clear();
     m->prof_used = 0;
   }
-  m->prof_on = enable != 0;
+  m->prof_mask = (uint32_t)family_mask & ((1u << PF_COUNT) - 1u);
   return CAD_OK;
 }
 

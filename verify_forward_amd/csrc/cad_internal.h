@@ -28,6 +28,14 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
 // float -> half, round to nearest even, saturated to the finite range
 __device__ __forceinline__ f16_t f2h(float f) { return (f16_t)fminf(fmaxf(f, -65504.f), 65504.f); }
 
+// float -> (hi, lo) halves: hi = half(x), lo = half(x - hi), both round to
+// nearest; hi + lo equals x to about 2^-22 relative (operands of the
+// two-product matrix-core path)
+__device__ __forceinline__ void split_f16(float x, f16_t& hi, f16_t& lo) {
+  hi = f2h(x);
+  lo = f2h(x - (float)hi);
+}
+
 // eight bf16 values (one 16-byte load) -> eight halves.  bf16 -> fp32 is a
 // shift; fp32 -> half is exact for every bf16 value in the half normal range
 // (half carries three more mantissa bits), truncation only touches values
@@ -63,9 +71,16 @@ template <> __device__ __forceinline__ f16_t from_f<f16_t>(float v) { return f2h
 struct RowMap {
   int32_t n_seq;
   int32_t total;
-  int32_t start[CAD_MAX_SEQS + 1];  // CSR row offsets
-  int64_t L[CAD_MAX_SEQS];          // cache length before the call
+  int32_t start[CAD_MAX_SEQS + 1];   // CSR row offsets
+  int32_t pstart[CAD_MAX_SEQS + 1];  // row offsets in the span K/V workspace (each sequence padded to 64 rows)
+  int64_t L[CAD_MAX_SEQS];           // cache length before the call
 };
+
+// fill pstart from start
+inline void rowmap_pad(RowMap& rm) {
+  rm.pstart[0] = 0;
+  for (int b = 0; b < rm.n_seq; ++b) rm.pstart[b + 1] = rm.pstart[b] + (rm.start[b + 1] - rm.start[b] + 63) / 64 * 64;
+}
 
 __device__ __forceinline__ int row_seq(const RowMap& rm, int r) {
   int b = 0;
@@ -80,12 +95,24 @@ struct KVView {
   const int32_t* table;  // [n_seq][max_blocks]
   int64_t num_blocks;
   int32_t max_blocks;
+  // bf16 models: this call's span K (after rotation) and V at half precision,
+  // read by attention for keys >= L instead of their bf16 cache copies.
+  // span_k [span_cap][Hkv][hd]; span_v [Hkv][hd][span_cap]; rows at RowMap.pstart
+  f16_t* span_k;
+  f16_t* span_v;
+  int32_t span_cap;
 };
 
 enum Epi { EPI_STORE_F32 = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+// projection roles; each fixes its epilogue (qkv, lm_head: store; o, down:
+// residual add; gate_up: SwiGLU) and names its kernels
+enum GemmRole { GEMM_QKV = 0, GEMM_O = 1, GEMM_GATE_UP = 2, GEMM_DOWN = 3, GEMM_LM_HEAD = 4 };
 
 struct GemmArgs {
-  const void* A;   // activations [M][lda]
+  // activations [M][lda]: fp32 for fp32 models; for bf16 models two half
+  // planes, A = hi part, A_lo = the half-rounded remainder (hi + lo ~ fp32)
+  const void* A;
+  const void* A_lo;
   int64_t lda;
   const void* W;   // weight rows [rows][ldw]
   int64_t ldw;
@@ -93,32 +120,39 @@ struct GemmArgs {
   int64_t up_off;  // SWIGLU: first row of the "up" half
   float* out_f32;  // STORE_F32 / RESID destination [M][ldo]
   int64_t ldo;
-  void* out_act;   // SWIGLU destination [M][N], element type = model dtype
+  void* out_act;     // SWIGLU destination [M][N]: fp32 (fp32 models) or the hi plane (bf16 models)
+  void* out_act_lo;  // bf16 models: lo plane of the SWIGLU destination
   // split-K scratch (library workspace): partial tiles and per-tile arrival
   // counters, which start at zero and are left at zero by every launch
   float* split_ws;
   int32_t* split_cnt;
 };
 
-// split-K limits of the tiled GEMM: at most GEMM_SPLIT_SLOTS (tile, split)
-// work-groups carry a partial tile of GEMM_TILE_FLOATS floats
+// split-K limits of the tiled GEMMs: at most GEMM_SPLIT_SLOTS output tiles
+// (arrival counters) and GEMM_SPLIT_FLOATS floats of partial tiles (64 MB)
 constexpr int GEMM_SPLIT_SLOTS = 512;
+constexpr int64_t GEMM_SPLIT_FLOATS = (int64_t)16 << 20;
 constexpr int GEMM_TILE_FLOATS = 128 * 128;
 
 // ---- launchers (stream-ordered, no host sync) ----
 hipError_t launch_embed(int dtype, const void* table, int vocab, int d, const int32_t* tokens,
                         int rows, float* x, int32_t* status, hipStream_t s);
+// out: fp32 [rows][d] (fp32 models) or half planes out (hi) / out_lo (bf16 models)
 hipError_t launch_rmsnorm(int dtype, const float* x, const void* gain, int rows, int d, float eps,
-                          void* out, hipStream_t s);
-hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s);
+                          void* out, void* out_lo, hipStream_t s);
+hipError_t launch_gemm(int dtype, int role, const GemmArgs& a, hipStream_t s);
 hipError_t launch_rope_append(int dtype, const float* qkv, int rows, int hq, int hkv, int hd,
                               const double* freq, const RowMap& rm, KVView kv,
                               const int32_t* write_limit, void* q_out, int32_t* status,
                               hipStream_t s);
+// n_parts = cache partitions (keys < L, part_len each) + one span partition
 hipError_t launch_attention(int dtype, const void* q, int rows, int hq, int hkv, int hd,
                             const RowMap& rm, KVView kv, int n_parts, int part_len,
-                            float* part_o, float* part_ml, void* out, int32_t* status,
+                            float* part_o, float* part_ml, void* out, void* out_lo, int32_t* status,
                             hipStream_t s);
+// log-sum-exp merge of the key partitions (bf16 models, n_parts > 1), into half planes
+hipError_t launch_attention_merge(const float* part_o, const float* part_ml, int n_parts, int rows,
+                                  int hq, int hd, void* out, void* out_lo, hipStream_t s);
 hipError_t launch_argmax(const float* logits, int rows, int vocab, const uint32_t* mask,
                          int32_t* out, int32_t* status, hipStream_t s);
 hipError_t launch_accept(const int32_t* argmax, const int32_t* span, const RowMap& rm, int mode,
@@ -130,7 +164,8 @@ hipError_t launch_suffix_match(const int32_t* tokens, int64_t T, int max_n, int 
                                int32_t* out_tokens, int32_t* out_len, int64_t* out_pos,
                                hipStream_t s);
 
-// attention split: partitions of the key axis so that small spans still fill the chip
-int attention_parts(int rows, int hq, int hkv, int64_t max_keys, int* part_len);
+// attention split: partitions of the cached keys (0 .. max L) so that small
+// spans still fill the chip; the span's own keys form one more partition
+int attention_parts(int rows, int hq, int hkv, int64_t max_cache_keys, int* part_len);
 
 }  // namespace cad

@@ -39,7 +39,8 @@ struct AttnArgs {
   int n_parts, part_len;
   float* part_o;   // [n_parts][rows * hq][hd]
   float* part_ml;  // [n_parts][rows * hq][2]
-  void* out;       // [rows][hq * hd]
+  void* out;       // [rows][hq * hd]: fp32 (fp32 models) or the half hi plane (bf16 models)
+  void* out_lo;    // bf16 models: the half lo plane
   int32_t* status;
   float scale_log2;  // log2(e) / sqrt(hd)
 };
@@ -103,10 +104,15 @@ k_attn_bf16(AttnArgs p) {
   const int q_first = tile * FA_QT;
   const int q_wave = q_first + wave * FA_QPW;
   const bool wave_active = q_wave < R;
-  // keys of this work-group: [k_begin, k_end); k_begin is a multiple of FA_KT
+  // keys of this work-group: [k_begin, k_end).  Partitions 0 .. n_parts - 2
+  // cover the cached keys 0 .. L - 1 (part_len each, a multiple of FA_KT) and
+  // read the paged bf16 cache; the last partition covers this call's own
+  // keys L .. and reads them from the half-precision span workspace.
   const int q_last = min(q_first + FA_QT, R) - 1;
-  const int64_t k_begin = (int64_t)part * p.part_len;
-  const int64_t k_end = min(k_begin + p.part_len, L + q_last / p.G + 1);
+  const int64_t causal_end = L + q_last / p.G + 1;
+  const bool span_part = part == p.n_parts - 1;
+  const int64_t k_begin = span_part ? L : (int64_t)part * p.part_len;
+  const int64_t k_end = span_part ? causal_end : min(k_begin + p.part_len, L);
   // causal limit shared by every query of the wave (its first query's)
   const int64_t wave_min_last = L + q_wave / p.G;
 
@@ -143,31 +149,45 @@ k_attn_bf16(AttnArgs p) {
   const bf16_t* kbase = (const bf16_t*)p.kv.k + (int64_t)kvh * CAD_KV_BLOCK * HD;
   const bf16_t* vbase = (const bf16_t*)p.kv.v + (int64_t)kvh * CAD_KV_BLOCK * HD;
   // cache block of tile t for this wave, or -1 when the tile's part of the
-  // key range does not reach it (then nothing is read)
+  // key range does not reach it (then nothing is read); unused by the span part
   auto block_of = [&](int t) -> int64_t {
     const int64_t first_key = k_begin + (int64_t)t * FA_KT + jb * CAD_KV_BLOCK;
-    if (t >= n_tiles || first_key >= k_end) return -1;
+    if (span_part || t >= n_tiles || first_key >= k_end) return -1;
     return table[first_key / CAD_KV_BLOCK];
   };
+  // span workspace rows of this sequence: row pstart + (key - L)
+  const int64_t span_row0 = p.rm.pstart[b];
+  const f16_t* span_k = p.kv.span_k;
+  const f16_t* span_v = p.kv.span_v;
   u32x4 rk[KCH], rv[VCH];
+  // Every load below reads valid memory (a clamped block, or the sequence's
+  // 64-row padded workspace region) and is unconditional; out-of-range keys
+  // are zeroed afterwards, so the waits for tile t + 1 never cover extra work.
   auto gload = [&](int64_t kt, int64_t bb) {
     const int64_t k0 = kt + jb * CAD_KV_BLOCK;  // first key of this wave's block
-    const bool ok = bb >= 0 && bb < p.kv.num_blocks;
-    if (bb >= 0 && !ok && p.status && ct == 0) atomicOr(p.status, (int32_t)CAD_DEV_BAD_BLOCK);
-    const int nvalid = ok ? (int)min<int64_t>(k_end - k0, CAD_KV_BLOCK) : 0;  // keys of the block in range
-    const bf16_t* kb = kbase + (ok ? bb : 0) * kv_blk_stride;
-    const bf16_t* vb = vbase + (ok ? bb : 0) * kv_blk_stride;
+    const bool ok = span_part || (bb >= 0 && bb < p.kv.num_blocks);
+    if (!span_part && bb >= 0 && !ok && p.status && ct == 0) atomicOr(p.status, (int32_t)CAD_DEV_BAD_BLOCK);
+    const int nvalid = ok ? (int)max<int64_t>(min<int64_t>(k_end - k0, CAD_KV_BLOCK), 0) : 0;
+    const bf16_t* kb = kbase + (ok && !span_part ? bb : 0) * kv_blk_stride;
+    const bf16_t* vb = vbase + (ok && !span_part ? bb : 0) * kv_blk_stride;
+    const int64_t srow = span_row0 + (k0 - L);  // span workspace row of key k0
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int c = ct + TPB * i;  // [16 keys][HD / 8 chunks]
-      const int key = c / (HD / 8);
-      rk[i] = key < nvalid ? *(const u32x4*)(kb + c * 8) : u32x4{0u, 0u, 0u, 0u};
+      const int key = c / (HD / 8), c8 = c % (HD / 8);
+      const u32x4* src = span_part ? (const u32x4*)(span_k + ((srow + key) * p.hkv + kvh) * HD + c8 * 8)
+                                   : (const u32x4*)(kb + c * 8);
+      const u32x4 v = *src;
+      rk[i] = key < nvalid ? v : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < VCH; ++i) {
       const int c = ct + TPB * i;  // [HD rows][2 chunks of 8 tokens]
-      const int hf = c & 1;
-      u32x4 v = *(const u32x4*)(vb + c * 8);
+      const int d = c >> 1, hf = c & 1;
+      const u32x4* src = span_part
+                             ? (const u32x4*)(span_v + ((int64_t)kvh * HD + d) * p.kv.span_cap + srow + 8 * hf)
+                             : (const u32x4*)(vb + c * 8);
+      u32x4 v = *src;
       // zero the tokens past the key range (stale slots may hold anything)
       const int nv = nvalid - 8 * hf;
 #pragma unroll
@@ -183,7 +203,7 @@ k_attn_bf16(AttnArgs p) {
     for (int i = 0; i < KCH; ++i) {
       const int c = ct + TPB * i;
       const int key = jb * CAD_KV_BLOCK + c / (HD / 8), c8 = c % (HD / 8);
-      *(u32x4*)(&sK[buf][key * KLD + c8 * 8]) = bf16x8_to_f16x8(rk[i]);
+      *(u32x4*)(&sK[buf][key * KLD + c8 * 8]) = span_part ? rk[i] : bf16x8_to_f16x8(rk[i]);
     }
 #pragma unroll
     for (int i = 0; i < VCH; ++i) {
@@ -193,7 +213,7 @@ k_attn_bf16(AttnArgs p) {
       // + 16 (jb & 1) + 8 hf + e) key 16 h + 4 j + r sits at column 8 j + 4 h
       // + r: the eight columns 8 j .. 8 j + 7 then hold keys 4 j .. 4 j + 3
       // and 16 + 4 j .. 16 + 4 j + 3, the keys lane group j holds in S^T.
-      const u32x4 h = bf16x8_to_f16x8(rv[i]);
+      const u32x4 h = span_part ? rv[i] : bf16x8_to_f16x8(rv[i]);
       const int col = (jb >> 1) * 32 + 16 * hf + 4 * (jb & 1);
       f16_t* row = &sV[buf][d * VLD + col];
       *(u32x2*)(row) = u32x2{h[0], h[1]};      // e = 0..3 -> j = 2 hf
@@ -280,8 +300,9 @@ k_attn_bf16(AttnArgs p) {
             e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][r], p.scale_log2, nm));
             psum += e[r];
           }
-          pk[kb * 2 + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(e[0], e[1]));
-          pk[kb * 2 + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(e[2], e[3]));
+          // round to nearest (unbiased), weights are in [0, 2^FA_LAZY]
+          pk[kb * 2 + 0] = __builtin_bit_cast(uint32_t, f16x2{(f16_t)e[0], (f16_t)e[1]});
+          pk[kb * 2 + 1] = __builtin_bit_cast(uint32_t, f16x2{(f16_t)e[2], (f16_t)e[3]});
         }
         l_run[qb] += psum;
         // k step ks covers key blocks 2 ks and 2 ks + 1
@@ -313,13 +334,18 @@ k_attn_bf16(AttnArgs p) {
     // lane holds O^T[d = 16 db + 4 g4 + r][query]
     if (p.n_parts == 1) {
       f16_t* out = (f16_t*)p.out + qrow[qb] * HD;
+      f16_t* out_lo = (f16_t*)p.out_lo + qrow[qb] * HD;
       const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
       for (int d = 0; d < DB; ++d) {
+        f16_t hi[4], lo[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) split_f16(o[d][qb][r] * inv, hi[r], lo[r]);
         const int dd = d * 16 + g4 * 4;
-        const uint32_t lo = __builtin_bit_cast(uint32_t, f16x2{f2h(o[d][qb][0] * inv), f2h(o[d][qb][1] * inv)});
-        const uint32_t hi = __builtin_bit_cast(uint32_t, f16x2{f2h(o[d][qb][2] * inv), f2h(o[d][qb][3] * inv)});
-        *(u32x2*)(out + dd) = u32x2{lo, hi};
+        *(u32x2*)(out + dd) = u32x2{__builtin_bit_cast(uint32_t, f16x2{hi[0], hi[1]}),
+                                    __builtin_bit_cast(uint32_t, f16x2{hi[2], hi[3]})};
+        *(u32x2*)(out_lo + dd) = u32x2{__builtin_bit_cast(uint32_t, f16x2{lo[0], lo[1]}),
+                                       __builtin_bit_cast(uint32_t, f16x2{lo[2], lo[3]})};
       }
     } else {
       // partial: unnormalised O, and (m, l) with m in exp2 units; a query
@@ -336,10 +362,11 @@ k_attn_bf16(AttnArgs p) {
   }
 }
 
-// log-sum-exp merge of the partitions (base-2 exponent, as produced above)
-template <typename T>
+// log-sum-exp merge of the partitions (base-2 exponent, as produced above),
+// written as half hi / lo planes
 __global__ void k_attn_merge(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                             int n_parts, int64_t nq, int hd, T* __restrict__ out) {
+                             int n_parts, int64_t nq, int hd, f16_t* __restrict__ out,
+                             f16_t* __restrict__ out_lo) {
   const int64_t qi = blockIdx.x;
   float m = -INFINITY;
   for (int pp = 0; pp < n_parts; ++pp) {
@@ -355,7 +382,7 @@ __global__ void k_attn_merge(const float* __restrict__ part_o, const float* __re
       num += w * part_o[((int64_t)pp * nq + qi) * hd + d];
       den += w * l;
     }
-    out[qi * hd + d] = from_f<T>(den > 0.f ? num / den : 0.f);
+    split_f16(den > 0.f ? num / den : 0.f, out[qi * hd + d], out_lo[qi * hd + d]);
   }
 }
 
@@ -412,26 +439,30 @@ k_attn_f32(AttnArgs p, int hd) {
   }
 }
 
-int attention_parts(int rows, int hq, int hkv, int64_t max_keys, int* part_len) {
-  // about one work-group per compute unit (256 CUs), key partitions of at
-  // least 256 keys
+int attention_parts(int rows, int hq, int hkv, int64_t max_cache_keys, int* part_len) {
+  // partitions of the cached keys: about one work-group per compute unit
+  // (256 CUs) together with the query tiles, at least 256 keys each
   const int G = hq / hkv;
   const int tiles = (rows * G + FA_QT - 1) / FA_QT;
   const int base = hkv * tiles;
+  if (max_cache_keys <= 0) {
+    *part_len = FA_KT;
+    return 0;
+  }
   int parts = (256 + base - 1) / base;
   const int64_t min_len = 256;
-  const int64_t cap = (max_keys + min_len - 1) / min_len;
+  const int64_t cap = (max_cache_keys + min_len - 1) / min_len;
   if (parts > cap) parts = (int)cap;
   if (parts < 1) parts = 1;
-  int64_t len = (max_keys + parts - 1) / parts;
+  int64_t len = (max_cache_keys + parts - 1) / parts;
   len = (len + FA_KT - 1) / FA_KT * FA_KT;
   *part_len = (int)len;
-  return (int)((max_keys + len - 1) / len);
+  return (int)((max_cache_keys + len - 1) / len);
 }
 
 hipError_t launch_attention(int dtype, const void* q, int rows, int hq, int hkv, int hd,
                             const RowMap& rm, KVView kv, int n_parts, int part_len,
-                            float* part_o, float* part_ml, void* out, int32_t* status,
+                            float* part_o, float* part_ml, void* out, void* out_lo, int32_t* status,
                             hipStream_t s) {
   AttnArgs a;
   a.q = q;
@@ -446,6 +477,7 @@ hipError_t launch_attention(int dtype, const void* q, int rows, int hq, int hkv,
   a.part_o = part_o;
   a.part_ml = part_ml;
   a.out = out;
+  a.out_lo = out_lo;
   a.status = status;
   a.scale_log2 = 1.4426950408889634f / sqrtf((float)hd);
   if (dtype == CAD_F32) {
@@ -464,11 +496,14 @@ hipError_t launch_attention(int dtype, const void* q, int rows, int hq, int hkv,
     hipLaunchKernelGGL(k_attn_bf16<64>, grid, dim3(FA_NT), 0, s, a);
   else
     hipLaunchKernelGGL(k_attn_bf16<128>, grid, dim3(FA_NT), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || n_parts == 1) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_merge(const float* part_o, const float* part_ml, int n_parts, int rows,
+                                  int hq, int hd, void* out, void* out_lo, hipStream_t s) {
   const int64_t nq = (int64_t)rows * hq;
-  hipLaunchKernelGGL(k_attn_merge<f16_t>, dim3((unsigned)nq), dim3(hd), 0, s, part_o, part_ml,
-                     n_parts, nq, hd, (f16_t*)out);
+  hipLaunchKernelGGL(k_attn_merge, dim3((unsigned)nq), dim3(hd), 0, s, part_o, part_ml, n_parts, nq, hd,
+                     (f16_t*)out, (f16_t*)out_lo);
   return hipGetLastError();
 }
 

@@ -3,27 +3,31 @@
 // with the consumer fused into the epilogue:
 //   EPI_STORE_F32  C -> fp32 buffer (QKV projection, LM head)
 //   EPI_RESID      x += C into the fp32 residual stream (O and down projections)
-//   EPI_SWIGLU     silu(C_gate) * C_up -> activation (gate/up projection)
+//   EPI_SWIGLU     silu(C_gate) * C_up -> fp32 activation (gate/up projection)
 //
 // bf16 models use the gfx950 matrix cores in half precision
-// (v_mfma_f32_16x16x32_f16): weights stay bf16 in HBM and are widened to half
-// in registers (exact in half's normal range), activations arrive as half,
-// so the only rounding left at a projection input is half's 11-bit mantissa
-// instead of bf16's 8.  The MFMA is issued with the weight tile as its first
-// operand and the activations as the second, so each lane ends up holding four consecutive output columns of one
-// row (C^T layout: lane l, register r -> column 4*(l/16)+r, row l%16).
+// (v_mfma_f32_16x16x32_f16).  Weights stay bf16 in HBM and are widened to
+// half (exact in half's normal range).  Activations arrive as two half
+// planes written by their producer: the "hi" part and the half-rounded
+// remainder "lo"; each weight fragment meets both (two matrix-core
+// products), so the activation operand carries ~22 significant bits and the
+// only rounding left is the fp32 accumulation.  The MFMA takes the weight tile as its first operand and
+// the activations as the second, so each lane ends up holding four
+// consecutive output columns of one row (lane l, register r -> column
+// 4*(l/16)+r, row l%16).
 //   * skinny (M <= 16): weight-streaming.  A work-group owns 16 output
 //     columns (32 weight rows for SWIGLU); its four waves split K and are
 //     reduced through LDS in a fixed order.  Every lane loads 32 contiguous
 //     bytes of a weight row per 64-wide k step straight into registers.
 //   * tiled (M > 16): 128x128 output tile per 256-thread work-group, K in
-//     steps of 64 staged through double-buffered LDS.  When the output has
-//     too few tiles to occupy the 256 compute units, K is split over up to
-//     eight work-groups per tile; each writes its fp32 partial tile to the
-//     workspace and the last to arrive (per-tile counter) sums the partials
-//     in split order and runs the epilogue, so results do not depend on
-//     scheduling.  The global loads run two k steps ahead of the matrix
-//     cores (two register stages in front of the LDS double buffer).
+//     steps of 32 staged through double-buffered LDS (weights, activation hi,
+//     activation lo planes).  When the output has too few tiles to occupy the 256
+//     compute units, K is split over up to eight work-groups per tile; each
+//     writes its fp32 partial tile to the workspace and the last to arrive
+//     (per-tile counter) sums the partials in split order and runs the
+//     epilogue, so results do not depend on scheduling.  The global loads run
+//     two k steps ahead of the matrix cores (two register stages in front of
+//     the LDS double buffer).
 // fp32 (the small reference-shape path) uses a plain LDS-tiled VALU kernel.
 #include "cad_internal.h"
 
@@ -31,9 +35,12 @@ namespace cad {
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
+
+
 // Apply the epilogue to four consecutive output columns n .. n+3 of row m.
-// For SWIGLU `c` holds the gate values and `cu` the matching up values.
-template <int EPI, typename TA>
+// For SWIGLU `c` holds the gate values and `cu` the matching up values; the
+// activation is written as fp32 or (SPLIT, bf16 models) as half hi / lo planes.
+template <int EPI, bool SPLIT>
 __device__ __forceinline__ void epi4(const GemmArgs& a, int m, int n, f32x4 c, f32x4 cu) {
   if (m >= a.M) return;
   if (EPI == EPI_STORE_F32 || EPI == EPI_RESID) {
@@ -50,10 +57,15 @@ __device__ __forceinline__ void epi4(const GemmArgs& a, int m, int n, f32x4 c, f
       for (int r = 0; r < 4; ++r)
         if (n + r < a.N) o[r] = (EPI == EPI_RESID) ? o[r] + c[r] : c[r];
     }
-  } else {
-    TA* o = (TA*)a.out_act + (int64_t)m * a.N + n;
+  } else if (SPLIT) {
+    f16_t* o = (f16_t*)a.out_act + (int64_t)m * a.N + n;
+    f16_t* ol = (f16_t*)a.out_act_lo + (int64_t)m * a.N + n;
     for (int r = 0; r < 4; ++r)
-      if (n + r < a.N) o[r] = from_f<TA>(silu_mul(c[r], cu[r]));
+      if (n + r < a.N) split_f16(silu_mul(c[r], cu[r]), o[r], ol[r]);
+  } else {
+    float* o = (float*)a.out_act + (int64_t)m * a.N + n;
+    for (int r = 0; r < 4; ++r)
+      if (n + r < a.N) o[r] = silu_mul(c[r], cu[r]);
   }
 }
 
@@ -63,32 +75,40 @@ __device__ __forceinline__ void epi4(const GemmArgs& a, int m, int n, f32x4 c, f
 constexpr int SK_WAVES = 4;
 
 template <int EPI>
-__global__ void __launch_bounds__(64 * SK_WAVES)
-k_gemm_skinny(GemmArgs a) {
+__device__ __forceinline__ void gemm_skinny_body(const GemmArgs& a) {
   constexpr int NB = (EPI == EPI_SWIGLU) ? 2 : 1;  // 16-row weight blocks per work-group
   __shared__ f32x4 part[SK_WAVES][NB][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, i16 = lane & 15;
   const int n0 = blockIdx.x * 16;
-  const f16_t* A = (const f16_t*)a.A;
   const bf16_t* W = (const bf16_t*)a.W;
   // this lane's weight rows (clamped: columns past N are computed and dropped)
   const int ncol = min(n0 + i16, a.N - 1);
   const bf16_t* wrow[NB];
   wrow[0] = W + (int64_t)ncol * a.ldw;
   if (NB == 2) wrow[NB - 1] = W + (a.up_off + ncol) * a.ldw;
-  const bool arow_ok = i16 < a.M;
-  const f16_t* arow = A + (int64_t)(arow_ok ? i16 : 0) * a.lda;
+  // activation rows past M read row M - 1 and are dropped by the epilogue
+  const int64_t aoff = (int64_t)min(i16, a.M - 1) * a.lda;
+  const f16_t* arow_hi = (const f16_t*)a.A + aoff;
+  const f16_t* arow_lo = (const f16_t*)a.A_lo + aoff;
   // k split across waves in units of 64
   const int kp_total = a.K / 64;
   const int kp0 = (kp_total * wave) / SK_WAVES, kp1 = (kp_total * (wave + 1)) / SK_WAVES;
   f32x4 acc[NB];
   for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+  // 16 activations at k .. k + 15: (hi, lo) operands of the two products
+  auto act16 = [&](int k, u32x4 (&hi)[2], u32x4 (&lo)[2]) {
+    const u32x4* qh = (const u32x4*)(arow_hi + k);
+    const u32x4* ql = (const u32x4*)(arow_lo + k);
+    hi[0] = qh[0];
+    hi[1] = qh[1];
+    lo[0] = ql[0];
+    lo[1] = ql[1];
+  };
   constexpr int U = 4;
   int kp = kp0;
   for (; kp + U <= kp1; kp += U) {
-    u32x4 wv[NB][U][2], av[U][2];
+    u32x4 wv[NB][U][2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = (kp + u) * 64 + g * 16;
@@ -98,27 +118,34 @@ k_gemm_skinny(GemmArgs a) {
         wv[b][u][0] = __builtin_nontemporal_load(p);
         wv[b][u][1] = __builtin_nontemporal_load(p + 1);
       }
-      const u32x4* q = (const u32x4*)(arow + k);
-      av[u][0] = arow_ok ? q[0] : zero;
-      av[u][1] = arow_ok ? q[1] : zero;
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      u32x4 ah[2], al[2];
+      act16((kp + u) * 64 + g * 16, ah, al);
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        acc[b] = mfma16(bf16x8_to_f16x8(wv[b][u][0]), av[u][0], acc[b]);
-        acc[b] = mfma16(bf16x8_to_f16x8(wv[b][u][1]), av[u][1], acc[b]);
-      }
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 w = bf16x8_to_f16x8(wv[b][u][h]);
+          acc[b] = mfma16(w, ah[h], acc[b]);
+          acc[b] = mfma16(w, al[h], acc[b]);
+        }
+    }
   }
   for (; kp < kp1; ++kp) {
     const int k = kp * 64 + g * 16;
-    u32x4 a0 = zero, a1 = zero;
-    if (arow_ok) { a0 = ((const u32x4*)(arow + k))[0]; a1 = ((const u32x4*)(arow + k))[1]; }
+    u32x4 ah[2], al[2];
+    act16(k, ah, al);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const u32x4* p = (const u32x4*)(wrow[b] + k);
-      acc[b] = mfma16(bf16x8_to_f16x8(p[0]), a0, acc[b]);
-      acc[b] = mfma16(bf16x8_to_f16x8(p[1]), a1, acc[b]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4 w = bf16x8_to_f16x8(p[h]);
+        acc[b] = mfma16(w, ah[h], acc[b]);
+        acc[b] = mfma16(w, al[h], acc[b]);
+      }
     }
   }
 #pragma unroll
@@ -132,14 +159,14 @@ k_gemm_skinny(GemmArgs a) {
       for (int w = 1; w < SK_WAVES; ++w) s[b] += part[w][b][lane];
     }
     // lane holds C^T rows n0 + 4g + r (output columns) of activation row i16
-    epi4<EPI, f16_t>(a, i16, n0 + 4 * g, s[0], s[NB - 1]);
+    epi4<EPI, true>(a, i16, n0 + 4 * g, s[0], s[NB - 1]);
   }
 }
 
 // ---------------------------------------------------------------------------
 // bf16 tiled: 128 (weight rows) x 128 (activation rows) per work-group
 // ---------------------------------------------------------------------------
-constexpr int TB = 128, TK = 64, TPAD = 8, TLD = TK + TPAD;
+constexpr int TB = 128, TK = 32, TLD = TK + 8;  // 80-byte rows: 16-row fragment reads hit distinct banks
 
 // Work-group -> (weight tile tn, activation tile tm, k split), weight tile
 // fastest: the work-groups resident at one time share a few activation
@@ -153,10 +180,10 @@ __device__ __forceinline__ void gemm_tile_of(int n_tn, int n_tm, int& tn, int& t
 }
 
 template <int EPI>
-__global__ void __launch_bounds__(256, 2)
-k_gemm_tiled(GemmArgs a, int n_tn, int n_tm, int splits) {
+__device__ __forceinline__ void gemm_tiled_body(const GemmArgs& a, int n_tn, int n_tm, int splits) {
   __shared__ __attribute__((aligned(16))) f16_t sw[2][TB * TLD];
-  __shared__ __attribute__((aligned(16))) f16_t sa[2][TB * TLD];
+  __shared__ __attribute__((aligned(16))) f16_t sah[2][TB * TLD];
+  __shared__ __attribute__((aligned(16))) f16_t sal[2][TB * TLD];
   __shared__ int s_last;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -165,18 +192,17 @@ k_gemm_tiled(GemmArgs a, int n_tn, int n_tm, int splits) {
   const int wm = (wave >> 1) * 64;  // wave's offset in the activation-row dim
   int tn, tm, sp;
   gemm_tile_of(n_tn, n_tm, tn, tm, sp);
-  const f16_t* A = (const f16_t*)a.A;
   const bf16_t* W = (const bf16_t*)a.W;
 
-  // global -> LDS assignment: 4 chunks of 8 bf16 per thread per operand
-  const bf16_t* wsrc[4];
-  const f16_t* asrc[4];
-  int soff[4];
+  // global -> LDS assignment per 32-wide k step: weights 2 chunks of 8 bf16
+  // per thread (4 threads per row), activations likewise per plane
+  const bf16_t* wsrc[2];
+  int wsoff[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 2; ++i) {
     const int c = tid + 256 * i;
-    const int row = c >> 3, col = (c & 7) * 8;
-    soff[i] = row * TLD + col;
+    const int row = c >> 2, col = (c & 3) * 8;
+    wsoff[i] = row * TLD + col;
     int64_t wr;
     if (EPI == EPI_SWIGLU) {
       // 16-row interleave: even blocks gate, odd blocks up, same output columns
@@ -188,27 +214,41 @@ k_gemm_tiled(GemmArgs a, int n_tn, int n_tm, int splits) {
       wr = min(tn * TB + row, a.N - 1);
     }
     wsrc[i] = W + wr * a.ldw + col;
-    // activation rows past M read row M - 1: their outputs are never stored
-    asrc[i] = A + (int64_t)min(tm * TB + row, a.M - 1) * a.lda + col;
+  }
+  // activations: 2 chunks of 8 halves per plane per thread (4 threads per row);
+  // rows past M read row M - 1: their outputs are never stored
+  const f16_t* ahsrc[2];
+  const f16_t* alsrc[2];
+  int asoff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + 256 * i;
+    const int row = c >> 2, col = (c & 3) * 8;
+    asoff[i] = row * TLD + col;
+    const int64_t off = (int64_t)min(tm * TB + row, a.M - 1) * a.lda + col;
+    ahsrc[i] = (const f16_t*)a.A + off;
+    alsrc[i] = (const f16_t*)a.A_lo + off;
   }
   // two register stages: the global loads of k step j are issued two steps
   // before step j is computed and are written to LDS at the end of step j - 1.
   // Every load is unconditional (indices are clamped instead) so that the
   // waits for one stage never cover the other stage's loads.
-  u32x4 rw0[4], ra0[4], rw1[4], ra1[4];
-  auto gload = [&](u32x4 (&rw)[4], u32x4 (&ra)[4], int kt) {
+  u32x4 rw0[2], rh0[2], rl0[2], rw1[2], rh1[2], rl1[2];
+  auto gload = [&](u32x4 (&rw)[2], u32x4 (&rh)[2], u32x4 (&rl)[2], int kt) {
     const int k0 = kt * TK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       rw[i] = *(const u32x4*)(wsrc[i] + k0);
-      ra[i] = *(const u32x4*)(asrc[i] + k0);
+      rh[i] = *(const u32x4*)(ahsrc[i] + k0);
+      rl[i] = *(const u32x4*)(alsrc[i] + k0);
     }
   };
-  auto sstore = [&](const u32x4 (&rw)[4], const u32x4 (&ra)[4], int buf) {
+  auto sstore = [&](const u32x4 (&rw)[2], const u32x4 (&rh)[2], const u32x4 (&rl)[2], int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *(u32x4*)(&sw[buf][soff[i]]) = bf16x8_to_f16x8(rw[i]);
-      *(u32x4*)(&sa[buf][soff[i]]) = ra[i];
+    for (int i = 0; i < 2; ++i) {
+      *(u32x4*)(&sw[buf][wsoff[i]]) = bf16x8_to_f16x8(rw[i]);
+      *(u32x4*)(&sah[buf][asoff[i]]) = rh[i];
+      *(u32x4*)(&sal[buf][asoff[i]]) = rl[i];
     }
   };
   f32x4 acc[4][4];
@@ -217,41 +257,41 @@ k_gemm_tiled(GemmArgs a, int n_tn, int n_tm, int splits) {
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int buf) {
+    u32x4 fw[4], fh[4], fl[4];
 #pragma unroll
-    for (int ks = 0; ks < TK / 32; ++ks) {
-      u32x4 fw[4], fa[4];
+    for (int x = 0; x < 4; ++x) fw[x] = *(const u32x4*)(&sw[buf][(wn + x * 16 + i16) * TLD + g * 8]);
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
-        fw[x] = *(const u32x4*)(&sw[buf][(wn + x * 16 + i16) * TLD + ks * 32 + g * 8]);
-#pragma unroll
-      for (int y = 0; y < 4; ++y)
-        fa[y] = *(const u32x4*)(&sa[buf][(wm + y * 16 + i16) * TLD + ks * 32 + g * 8]);
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y)
-          acc[x][y] = mfma16(fw[x], fa[y], acc[x][y]);
+    for (int y = 0; y < 4; ++y) {
+      fh[y] = *(const u32x4*)(&sah[buf][(wm + y * 16 + i16) * TLD + g * 8]);
+      fl[y] = *(const u32x4*)(&sal[buf][(wm + y * 16 + i16) * TLD + g * 8]);
     }
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        acc[x][y] = mfma16(fw[x], fh[y], acc[x][y]);
+        acc[x][y] = mfma16(fw[x], fl[y], acc[x][y]);
+      }
   };
 
   const int nk = a.K / TK;
   const int kt0 = (int)((int64_t)nk * sp / splits), kt1 = (int)((int64_t)nk * (sp + 1) / splits);
-  gload(rw0, ra0, kt0);
-  sstore(rw0, ra0, 0);
-  gload(rw1, ra1, min(kt0 + 1, kt1 - 1));
+  gload(rw0, rh0, rl0, kt0);
+  sstore(rw0, rh0, rl0, 0);
+  gload(rw1, rh1, rl1, min(kt0 + 1, kt1 - 1));
   __syncthreads();
   for (int kt = kt0; kt < kt1; kt += 2) {
     // even step: LDS buffer 0 holds step kt, stage 1 step kt + 1 (past the
     // end: a repeat of the last step, staged into a buffer nobody reads)
-    gload(rw0, ra0, min(kt + 2, kt1 - 1));
+    gload(rw0, rh0, rl0, min(kt + 2, kt1 - 1));
     compute(0);
-    sstore(rw1, ra1, 1);
+    sstore(rw1, rh1, rl1, 1);
     __syncthreads();
     if (kt + 1 >= kt1) break;
     // odd step: LDS buffer 1 holds step kt + 1, stage 0 step kt + 2
-    gload(rw1, ra1, min(kt + 3, kt1 - 1));
+    gload(rw1, rh1, rl1, min(kt + 3, kt1 - 1));
     compute(1);
-    sstore(rw0, ra0, 0);
+    sstore(rw0, rh0, rl0, 0);
     __syncthreads();
   }
   if (splits > 1) {
@@ -292,13 +332,13 @@ k_gemm_tiled(GemmArgs a, int n_tn, int n_tm, int splits) {
       for (int x = 0; x < 4; x += 2) {
         const int blk = (wn >> 4) + x;  // even block: gate; blk + 1: up
         const int n = tn * (TB / 2) + (blk >> 1) * 16 + 4 * g;
-        epi4<EPI, f16_t>(a, m, n, acc[x][y], acc[x + 1][y]);
+        epi4<EPI, true>(a, m, n, acc[x][y], acc[x + 1][y]);
       }
     } else {
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int n = tn * TB + wn + x * 16 + 4 * g;
-        epi4<EPI, f16_t>(a, m, n, acc[x][y], acc[x][y]);
+        epi4<EPI, true>(a, m, n, acc[x][y], acc[x][y]);
       }
     }
   }
@@ -308,8 +348,7 @@ k_gemm_tiled(GemmArgs a, int n_tn, int n_tm, int splits) {
 // fp32 VALU path: 64x64 tile, 256 threads, 4x4 outputs each
 // ---------------------------------------------------------------------------
 template <int EPI>
-__global__ void __launch_bounds__(256)
-k_gemm_f32(GemmArgs a) {
+__device__ __forceinline__ void gemm_f32_body(const GemmArgs& a) {
   __shared__ float sa[16][64 + 1];
   __shared__ float sw[16][64 + 1];
   const int tid = threadIdx.x;
@@ -357,36 +396,65 @@ k_gemm_f32(GemmArgs a) {
     const int m = m0 + ty * 4 + i;
     f32x4 c = {acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
     f32x4 cu = {accu[i][0], accu[i][1], accu[i][2], accu[i][3]};
-    epi4<EPI, float>(a, m, n0 + tx * 4, c, cu);
+    epi4<EPI, false>(a, m, n0 + tx * 4, c, cu);
   }
 }
 
+// One named kernel per projection and path, so that profiles attribute time
+// to the projection (qkv, o, gate_up, down, lm_head) rather than to a shared
+// template instance.
+#define CAD_GEMM_KERNELS(NAME, EPI)                                                        \
+  __global__ void __launch_bounds__(256, 2)                                                \
+      k_gemm_##NAME(GemmArgs a, int n_tn, int n_tm, int splits) {                          \
+    gemm_tiled_body<EPI>(a, n_tn, n_tm, splits);                                           \
+  }                                                                                        \
+  __global__ void __launch_bounds__(64 * SK_WAVES) k_gemv_##NAME(GemmArgs a) {             \
+    gemm_skinny_body<EPI>(a);                                                              \
+  }                                                                                        \
+  __global__ void __launch_bounds__(256) k_gemm_f32_##NAME(GemmArgs a) { gemm_f32_body<EPI>(a); }
+
+CAD_GEMM_KERNELS(qkv, EPI_STORE_F32)
+CAD_GEMM_KERNELS(o, EPI_RESID)
+CAD_GEMM_KERNELS(gate_up, EPI_SWIGLU)
+CAD_GEMM_KERNELS(down, EPI_RESID)
+CAD_GEMM_KERNELS(lm_head, EPI_STORE_F32)
+#undef CAD_GEMM_KERNELS
+
+typedef void (*TiledFn)(GemmArgs, int, int, int);
+typedef void (*PlainFn)(GemmArgs);
+
 template <int EPI>
-static hipError_t launch_epi(int dtype, const GemmArgs& a, hipStream_t s) {
+static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled, PlainFn skinny, PlainFn f32,
+                             hipStream_t s) {
   if (dtype == CAD_F32) {
     dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
-    hipLaunchKernelGGL(k_gemm_f32<EPI>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(f32, grid, dim3(256), 0, s, a);
   } else if (a.M <= 16) {
-    hipLaunchKernelGGL(k_gemm_skinny<EPI>, dim3((a.N + 15) / 16), dim3(64 * SK_WAVES), 0, s, a);
+    hipLaunchKernelGGL(skinny, dim3((a.N + 15) / 16), dim3(64 * SK_WAVES), 0, s, a);
   } else {
     const int cols_per_tile = (EPI == EPI_SWIGLU) ? TB / 2 : TB;
     const int n_tn = (a.N + cols_per_tile - 1) / cols_per_tile, n_tm = (a.M + TB - 1) / TB;
     const int tiles = n_tn * n_tm, nk = a.K / TK;
     // split K while the tiles alone leave compute units idle (two
-    // work-groups fit per CU), keeping at least 32 k steps per split
+    // work-groups fit per CU), keeping at least 64 k steps of 32 per split
     int splits = 1;
     if (EPI != EPI_SWIGLU && a.split_ws && a.split_cnt)
-      while (splits < 8 && tiles * splits * 2 <= GEMM_SPLIT_SLOTS && nk / (splits * 2) >= 32) splits *= 2;
-    hipLaunchKernelGGL(k_gemm_tiled<EPI>, dim3(tiles * splits), dim3(256), 0, s, a, n_tn, n_tm, splits);
+      while (splits < 8 && tiles * splits * 2 <= GEMM_SPLIT_SLOTS && nk / (splits * 2) >= 64 &&
+             (int64_t)tiles * splits * 2 * GEMM_TILE_FLOATS <= GEMM_SPLIT_FLOATS)
+        splits *= 2;
+    hipLaunchKernelGGL(tiled, dim3(tiles * splits), dim3(256), 0, s, a, n_tn, n_tm, splits);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
-  switch (epi) {
-    case EPI_STORE_F32: return launch_epi<EPI_STORE_F32>(dtype, a, s);
-    case EPI_RESID: return launch_epi<EPI_RESID>(dtype, a, s);
-    default: return launch_epi<EPI_SWIGLU>(dtype, a, s);
+hipError_t launch_gemm(int dtype, int role, const GemmArgs& a, hipStream_t s) {
+  switch (role) {
+    case GEMM_QKV: return launch_epi<EPI_STORE_F32>(dtype, a, k_gemm_qkv, k_gemv_qkv, k_gemm_f32_qkv, s);
+    case GEMM_O: return launch_epi<EPI_RESID>(dtype, a, k_gemm_o, k_gemv_o, k_gemm_f32_o, s);
+    case GEMM_GATE_UP:
+      return launch_epi<EPI_SWIGLU>(dtype, a, k_gemm_gate_up, k_gemv_gate_up, k_gemm_f32_gate_up, s);
+    case GEMM_DOWN: return launch_epi<EPI_RESID>(dtype, a, k_gemm_down, k_gemv_down, k_gemm_f32_down, s);
+    default: return launch_epi<EPI_STORE_F32>(dtype, a, k_gemm_lm_head, k_gemv_lm_head, k_gemm_f32_lm_head, s);
   }
 }
 

@@ -46,12 +46,13 @@ hipError_t launch_embed(int dtype, const void* table, int vocab, int d, const in
 }
 
 // ---------------------------------------------------------------------------
-// RMSNorm: out[r] = x[r] / sqrt(mean(x[r]^2) + eps) * g, rounded to the
-// operand type of the next projection (half for bf16 models)
+// RMSNorm: out[r] = x[r] / sqrt(mean(x[r]^2) + eps) * g: fp32 for fp32
+// models, split into half hi / lo planes (the next projection's operands)
+// for bf16 models
 // ---------------------------------------------------------------------------
-template <typename T, typename TO>
+template <typename T, bool SPLIT>
 __global__ void k_rmsnorm(const float* __restrict__ x, const T* __restrict__ g, int d, float eps,
-                          TO* __restrict__ out) {
+                          void* __restrict__ out, void* __restrict__ out_lo) {
   __shared__ float red[16];
   const int r = blockIdx.x;
   const float* xr = x + (int64_t)r * d;
@@ -59,18 +60,27 @@ __global__ void k_rmsnorm(const float* __restrict__ x, const T* __restrict__ g, 
   for (int i = threadIdx.x; i < d; i += blockDim.x) ss += xr[i] * xr[i];
   ss = block_sum(ss, red);
   const float rs = 1.0f / sqrtf(ss / (float)d + eps);
-  TO* o = out + (int64_t)r * d;
-  for (int i = threadIdx.x; i < d; i += blockDim.x) o[i] = from_f<TO>(xr[i] * rs * to_f<T>(g[i]));
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    const float v = xr[i] * rs * to_f<T>(g[i]);
+    if (SPLIT) {
+      f16_t hi, lo;
+      split_f16(v, hi, lo);
+      ((f16_t*)out)[(int64_t)r * d + i] = hi;
+      ((f16_t*)out_lo)[(int64_t)r * d + i] = lo;
+    } else {
+      ((float*)out)[(int64_t)r * d + i] = v;
+    }
+  }
 }
 
 hipError_t launch_rmsnorm(int dtype, const float* x, const void* gain, int rows, int d, float eps,
-                          void* out, hipStream_t s) {
+                          void* out, void* out_lo, hipStream_t s) {
   if (dtype == CAD_BF16)
-    hipLaunchKernelGGL((k_rmsnorm<bf16_t, f16_t>), dim3(rows), dim3(ROW_THREADS), 0, s, x,
-                       (const bf16_t*)gain, d, eps, (f16_t*)out);
+    hipLaunchKernelGGL((k_rmsnorm<bf16_t, true>), dim3(rows), dim3(ROW_THREADS), 0, s, x,
+                       (const bf16_t*)gain, d, eps, out, out_lo);
   else
-    hipLaunchKernelGGL((k_rmsnorm<float, float>), dim3(rows), dim3(ROW_THREADS), 0, s, x,
-                       (const float*)gain, d, eps, (float*)out);
+    hipLaunchKernelGGL((k_rmsnorm<float, false>), dim3(rows), dim3(ROW_THREADS), 0, s, x,
+                       (const float*)gain, d, eps, out, out_lo);
   return hipGetLastError();
 }
 
@@ -78,7 +88,9 @@ hipError_t launch_rmsnorm(int dtype, const float* x, const void* gain, int rows,
 // rotary positions on q and k (half-split pairs, angle pos * freq[i] formed
 // in fp64), q to the attention operand buffer (type TQ), k and v appended to
 // the paged cache (type T) at the row's absolute position.  Rows at or beyond
-// *write_limit do not touch the cache.
+// *write_limit do not touch the cache.  bf16 models also keep every row's k
+// and v at half precision in the span workspace (kv.span_k / kv.span_v),
+// which attention reads for this call's own keys.
 // ---------------------------------------------------------------------------
 template <typename T, typename TQ>
 __global__ void k_rope_append(const float* __restrict__ qkv, int hq, int hkv, int hd,
@@ -103,6 +115,8 @@ __global__ void k_rope_append(const float* __restrict__ qkv, int hq, int hkv, in
   const int slot = (int)(pos % CAD_KV_BLOCK);
   T* kc = (T*)kv.k;
   T* vc = (T*)kv.v;
+  const int64_t wrow = rm.pstart[b] + local;  // span workspace row
+  f16_t* sk = kv.span_k ? kv.span_k + wrow * hkv * hd : nullptr;
   // rotations: q heads then k heads, one (head, pair) per item
   const int n_rot = (hq + hkv) * half;
   for (int it = threadIdx.x; it < n_rot; it += blockDim.x) {
@@ -116,19 +130,24 @@ __global__ void k_rope_append(const float* __restrict__ qkv, int hq, int hkv, in
       TQ* qo = q_out + ((int64_t)r * hq + h) * hd;
       qo[i] = from_f<TQ>(ra);
       qo[i + half] = from_f<TQ>(rb);
-    } else if (write_kv) {
+    } else {
       const int g = h - hq;
-      T* kd = kc + ((blk * hkv + g) * CAD_KV_BLOCK + slot) * hd;
-      kd[i] = from_f<T>(ra);
-      kd[i + half] = from_f<T>(rb);
+      if (write_kv) {
+        T* kd = kc + ((blk * hkv + g) * CAD_KV_BLOCK + slot) * hd;
+        kd[i] = from_f<T>(ra);
+        kd[i + half] = from_f<T>(rb);
+      }
+      if (sk) {
+        sk[g * hd + i] = f2h(ra);
+        sk[g * hd + i + half] = f2h(rb);
+      }
     }
   }
-  if (write_kv) {
-    const float* vs = src + (hq + hkv) * hd;
-    for (int it = threadIdx.x; it < hkv * hd; it += blockDim.x) {
-      const int g = it / hd, dd = it % hd;
-      vc[((blk * hkv + g) * hd + dd) * CAD_KV_BLOCK + slot] = from_f<T>(vs[it]);
-    }
+  const float* vs = src + (hq + hkv) * hd;
+  for (int it = threadIdx.x; it < hkv * hd; it += blockDim.x) {
+    const int g = it / hd, dd = it % hd;
+    if (write_kv) vc[((blk * hkv + g) * hd + dd) * CAD_KV_BLOCK + slot] = from_f<T>(vs[it]);
+    if (kv.span_v) kv.span_v[((int64_t)g * hd + dd) * kv.span_cap + wrow] = f2h(vs[it]);
   }
 }
 
