@@ -77,7 +77,7 @@ struct cad_model {
   void* ws = nullptr;
   size_t ws_bytes = 0;
   float* x = nullptr;        // [T][d] residual stream
-  // activations feeding a projection: fp32 [T][n] (fp32 models) or two half
+  // activations feeding a projection: fp32 [T][n] (fp32 models) or two bf16
   // planes [T][n] each, hi then lo (bf16 models), in the same bytes
   void* hn = nullptr;        // [T][d] normalised activations
   float* qkv = nullptr;      // [T][(hq+2hkv) hd]
@@ -95,7 +95,6 @@ struct cad_model {
   f16_t* span_v = nullptr;
   int32_t span_cap = 0;          // rows of the span workspace
   float* split_ws = nullptr;     // split-K partial tiles of the tiled GEMM (bf16 models)
-  int32_t* split_cnt = nullptr;  // per-tile arrival counters, zero between launches
 };
 
 namespace {
@@ -186,7 +185,7 @@ KVView view_of(const cad_model* m, const cad_kv* kv, int ci) {
 
 // lo plane of an activation buffer (bf16 models): after the T x n hi plane
 void* lo_plane(const cad_model* m, void* buf, int64_t n) {
-  return m->cfg.dtype == CAD_BF16 ? (void*)((f16_t*)buf + (int64_t)m->cfg.max_tokens * n) : nullptr;
+  return m->cfg.dtype == CAD_BF16 ? (void*)((bf16_t*)buf + (int64_t)m->cfg.max_tokens * n) : nullptr;
 }
 
 // Run cache indices [c0, c1) over the rows already embedded in m->x.
@@ -212,7 +211,7 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
     GemmArgs g{};
     g.A = m->hn; g.A_lo = lo_plane(m, m->hn, d); g.lda = d; g.W = m->w_qkv[li]; g.ldw = d;
     g.M = R; g.N = qkv_rows; g.K = d; g.out_f32 = m->qkv; g.ldo = qkv_rows;
-    g.split_ws = m->split_ws; g.split_cnt = m->split_cnt;
+    g.split_ws = m->split_ws;
     LAUNCH(PF_QKV, launch_gemm(c.dtype, GEMM_QKV, g, s));
     LAUNCH(PF_ROPE, launch_rope_append(c.dtype, m->qkv, R, hq, hkv, hd, m->freq, rm, v, write_limit, m->q,
                                dev_status, s));
@@ -225,7 +224,7 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
     g.A = m->attn; g.A_lo = lo_plane(m, m->attn, (int64_t)hq * hd); g.lda = hq * hd;
     g.W = m->w_o[li]; g.ldw = hq * hd;
     g.M = R; g.N = d; g.K = hq * hd; g.out_f32 = m->x; g.ldo = d;
-    g.split_ws = m->split_ws; g.split_cnt = m->split_cnt;
+    g.split_ws = m->split_ws;
     LAUNCH(PF_O, launch_gemm(c.dtype, GEMM_O, g, s));
     LAUNCH(PF_NORM, launch_rmsnorm(c.dtype, m->x, m->ffn_norm[li], R, d, c.rms_eps, m->hn,
                                    lo_plane(m, m->hn, d), s));
@@ -236,7 +235,7 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
     g = GemmArgs{};
     g.A = m->act; g.A_lo = lo_plane(m, m->act, F); g.lda = F; g.W = m->w_down[li]; g.ldw = F;
     g.M = R; g.N = d; g.K = F; g.out_f32 = m->x; g.ldo = d;
-    g.split_ws = m->split_ws; g.split_cnt = m->split_cnt;
+    g.split_ws = m->split_ws;
     LAUNCH(PF_DOWN, launch_gemm(c.dtype, GEMM_DOWN, g, s));
   }
   return CAD_OK;
@@ -251,7 +250,7 @@ cad_status readout(cad_model* m, int R, float* logits, const uint32_t* mask, int
   GemmArgs g{};
   g.A = m->hn; g.A_lo = lo_plane(m, m->hn, c.d_model); g.lda = c.d_model; g.W = m->lm_head; g.ldw = c.d_model;
   g.M = R; g.N = c.vocab; g.K = c.d_model; g.out_f32 = logits; g.ldo = c.vocab;
-  g.split_ws = m->split_ws; g.split_cnt = m->split_cnt;
+  g.split_ws = m->split_ws;
   LAUNCH(PF_HEAD, launch_gemm(c.dtype, GEMM_LM_HEAD, g, s));
   LAUNCH(PF_ARGMAX, launch_argmax(logits, R, c.vocab, mask, argmax, dev_status, s));
   return CAD_OK;
@@ -330,8 +329,7 @@ cad_status cad_model_create(const cad_config* cfg, const cad_weights* w, cad_mod
   const bool split = c.dtype == CAD_BF16;
   const int64_t span_cap = split ? (T + 64 * CAD_MAX_SEQS + 63) / 64 * 64 : 0;
   const size_t o_spk = take((size_t)span_cap * hkv * hd * 2), o_spv = take((size_t)span_cap * hkv * hd * 2);
-  const size_t o_sws = take(split ? (size_t)GEMM_SPLIT_FLOATS * 4 : 0),
-               o_scnt = take(split ? (size_t)GEMM_SPLIT_SLOTS * 4 : 0);
+  const size_t o_sws = take(split ? (size_t)GEMM_SPLIT_FLOATS * 4 : 0);
   hipError_t e = hipMalloc(&m->ws, off);
   if (e != hipSuccess) {
     delete m;
@@ -357,12 +355,10 @@ cad_status cad_model_create(const cad_config* cfg, const cad_weights* w, cad_mod
     m->span_v = (f16_t*)(base + o_spv);
     m->span_cap = (int32_t)span_cap;
     m->split_ws = (float*)(base + o_sws);
-    m->split_cnt = (int32_t*)(base + o_scnt);
   }
   std::vector<double> fr(hd / 2);
   for (int64_t i = 0; i < hd / 2; ++i) fr[i] = std::pow((double)c.rope_theta, -2.0 * (double)i / (double)hd);
   e = hipMemcpy(m->freq, fr.data(), fr.size() * 8, hipMemcpyHostToDevice);
-  if (e == hipSuccess && m->split_cnt) e = hipMemset(m->split_cnt, 0, (size_t)GEMM_SPLIT_SLOTS * 4);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     (void)hipFree(m->ws);

@@ -28,12 +28,14 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
 // float -> half, round to nearest even, saturated to the finite range
 __device__ __forceinline__ f16_t f2h(float f) { return (f16_t)fminf(fmaxf(f, -65504.f), 65504.f); }
 
-// float -> (hi, lo) halves: hi = half(x), lo = half(x - hi), both round to
-// nearest; hi + lo equals x to about 2^-22 relative (operands of the
-// two-product matrix-core path)
-__device__ __forceinline__ void split_f16(float x, f16_t& hi, f16_t& lo) {
-  hi = f2h(x);
-  lo = f2h(x - (float)hi);
+// float -> (hi, lo) bf16 pair: hi = bf16(x), lo = bf16(x - hi), both round
+// to nearest even; x - hi is exact in fp32, so hi + lo equals x to about
+// 2^-17 relative.  This is how a bf16 model hands activations to a
+// projection: two planes, each multiplied with the bf16 weights on the
+// matrix cores (two products, fp32 accumulate).
+__device__ __forceinline__ void split_bf16(float x, bf16_t& hi, bf16_t& lo) {
+  hi = f2bf(x);
+  lo = f2bf(x - bf2f(hi));
 }
 
 // eight bf16 values (one 16-byte load) -> eight halves.  bf16 -> fp32 is a
@@ -55,6 +57,13 @@ __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a), as_f16x8(b), c, 0, 0, 0);
+}
+
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+// v_mfma_f32_16x16x32_bf16: same fragment layout as the half variant
+__device__ __forceinline__ f32x4 mfma16_bf(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, a), __builtin_bit_cast(bf16x8v, b), c,
+                                                 0, 0, 0);
 }
 
 template <typename T> __device__ __forceinline__ float to_f(T v);
@@ -109,8 +118,8 @@ enum Epi { EPI_STORE_F32 = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
 enum GemmRole { GEMM_QKV = 0, GEMM_O = 1, GEMM_GATE_UP = 2, GEMM_DOWN = 3, GEMM_LM_HEAD = 4 };
 
 struct GemmArgs {
-  // activations [M][lda]: fp32 for fp32 models; for bf16 models two half
-  // planes, A = hi part, A_lo = the half-rounded remainder (hi + lo ~ fp32)
+  // activations [M][lda]: fp32 for fp32 models; for bf16 models two bf16
+  // planes, A = hi part, A_lo = the bf16-rounded remainder (hi + lo ~ fp32)
   const void* A;
   const void* A_lo;
   int64_t lda;
@@ -122,22 +131,17 @@ struct GemmArgs {
   int64_t ldo;
   void* out_act;     // SWIGLU destination [M][N]: fp32 (fp32 models) or the hi plane (bf16 models)
   void* out_act_lo;  // bf16 models: lo plane of the SWIGLU destination
-  // split-K scratch (library workspace): partial tiles and per-tile arrival
-  // counters, which start at zero and are left at zero by every launch
+  // split-K scratch (library workspace): fp32 partial sums [split][M][cols]
   float* split_ws;
-  int32_t* split_cnt;
 };
 
-// split-K limits of the tiled GEMMs: at most GEMM_SPLIT_SLOTS output tiles
-// (arrival counters) and GEMM_SPLIT_FLOATS floats of partial tiles (64 MB)
-constexpr int GEMM_SPLIT_SLOTS = 512;
-constexpr int64_t GEMM_SPLIT_FLOATS = (int64_t)16 << 20;
-constexpr int GEMM_TILE_FLOATS = 128 * 128;
+// split-K workspace of the tiled GEMMs: GEMM_SPLIT_FLOATS floats (128 MB)
+constexpr int64_t GEMM_SPLIT_FLOATS = (int64_t)32 << 20;
 
 // ---- launchers (stream-ordered, no host sync) ----
 hipError_t launch_embed(int dtype, const void* table, int vocab, int d, const int32_t* tokens,
                         int rows, float* x, int32_t* status, hipStream_t s);
-// out: fp32 [rows][d] (fp32 models) or half planes out (hi) / out_lo (bf16 models)
+// out: fp32 [rows][d] (fp32 models) or bf16 planes out (hi) / out_lo (bf16 models)
 hipError_t launch_rmsnorm(int dtype, const float* x, const void* gain, int rows, int d, float eps,
                           void* out, void* out_lo, hipStream_t s);
 hipError_t launch_gemm(int dtype, int role, const GemmArgs& a, hipStream_t s);
@@ -150,7 +154,7 @@ hipError_t launch_attention(int dtype, const void* q, int rows, int hq, int hkv,
                             const RowMap& rm, KVView kv, int n_parts, int part_len,
                             float* part_o, float* part_ml, void* out, void* out_lo, int32_t* status,
                             hipStream_t s);
-// log-sum-exp merge of the key partitions (bf16 models, n_parts > 1), into half planes
+// log-sum-exp merge of the key partitions (bf16 models, n_parts > 1), into bf16 planes
 hipError_t launch_attention_merge(const float* part_o, const float* part_ml, int n_parts, int rows,
                                   int hq, int hd, void* out, void* out_lo, hipStream_t s);
 hipError_t launch_argmax(const float* logits, int rows, int vocab, const uint32_t* mask,

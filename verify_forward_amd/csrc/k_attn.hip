@@ -39,8 +39,8 @@ struct AttnArgs {
   int n_parts, part_len;
   float* part_o;   // [n_parts][rows * hq][hd]
   float* part_ml;  // [n_parts][rows * hq][2]
-  void* out;       // [rows][hq * hd]: fp32 (fp32 models) or the half hi plane (bf16 models)
-  void* out_lo;    // bf16 models: the half lo plane
+  void* out;       // [rows][hq * hd]: fp32 (fp32 models) or the bf16 hi plane (bf16 models)
+  void* out_lo;    // bf16 models: the bf16 lo plane
   int32_t* status;
   float scale_log2;  // log2(e) / sqrt(hd)
 };
@@ -333,19 +333,17 @@ k_attn_bf16(AttnArgs p) {
     if (!q_ok[qb]) continue;
     // lane holds O^T[d = 16 db + 4 g4 + r][query]
     if (p.n_parts == 1) {
-      f16_t* out = (f16_t*)p.out + qrow[qb] * HD;
-      f16_t* out_lo = (f16_t*)p.out_lo + qrow[qb] * HD;
+      bf16_t* out = (bf16_t*)p.out + qrow[qb] * HD;
+      bf16_t* out_lo = (bf16_t*)p.out_lo + qrow[qb] * HD;
       const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
       for (int d = 0; d < DB; ++d) {
-        f16_t hi[4], lo[4];
+        bf16_t hi[4], lo[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) split_f16(o[d][qb][r] * inv, hi[r], lo[r]);
+        for (int r = 0; r < 4; ++r) split_bf16(o[d][qb][r] * inv, hi[r], lo[r]);
         const int dd = d * 16 + g4 * 4;
-        *(u32x2*)(out + dd) = u32x2{__builtin_bit_cast(uint32_t, f16x2{hi[0], hi[1]}),
-                                    __builtin_bit_cast(uint32_t, f16x2{hi[2], hi[3]})};
-        *(u32x2*)(out_lo + dd) = u32x2{__builtin_bit_cast(uint32_t, f16x2{lo[0], lo[1]}),
-                                       __builtin_bit_cast(uint32_t, f16x2{lo[2], lo[3]})};
+        *(u32x2*)(out + dd) = u32x2{hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16)};
+        *(u32x2*)(out_lo + dd) = u32x2{lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16)};
       }
     } else {
       // partial: unnormalised O, and (m, l) with m in exp2 units; a query
@@ -363,10 +361,10 @@ k_attn_bf16(AttnArgs p) {
 }
 
 // log-sum-exp merge of the partitions (base-2 exponent, as produced above),
-// written as half hi / lo planes
+// written as bf16 hi / lo planes
 __global__ void k_attn_merge(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                             int n_parts, int64_t nq, int hd, f16_t* __restrict__ out,
-                             f16_t* __restrict__ out_lo) {
+                             int n_parts, int64_t nq, int hd, bf16_t* __restrict__ out,
+                             bf16_t* __restrict__ out_lo) {
   const int64_t qi = blockIdx.x;
   float m = -INFINITY;
   for (int pp = 0; pp < n_parts; ++pp) {
@@ -382,7 +380,7 @@ __global__ void k_attn_merge(const float* __restrict__ part_o, const float* __re
       num += w * part_o[((int64_t)pp * nq + qi) * hd + d];
       den += w * l;
     }
-    split_f16(den > 0.f ? num / den : 0.f, out[qi * hd + d], out_lo[qi * hd + d]);
+    split_bf16(den > 0.f ? num / den : 0.f, out[qi * hd + d], out_lo[qi * hd + d]);
   }
 }
 
@@ -503,7 +501,7 @@ hipError_t launch_attention_merge(const float* part_o, const float* part_ml, int
                                   int hq, int hd, void* out, void* out_lo, hipStream_t s) {
   const int64_t nq = (int64_t)rows * hq;
   hipLaunchKernelGGL(k_attn_merge, dim3((unsigned)nq), dim3(hd), 0, s, part_o, part_ml, n_parts, nq, hd,
-                     (f16_t*)out, (f16_t*)out_lo);
+                     (bf16_t*)out, (bf16_t*)out_lo);
   return hipGetLastError();
 }
 

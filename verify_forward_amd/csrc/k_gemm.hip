@@ -3,31 +3,35 @@
 // with the consumer fused into the epilogue:
 //   EPI_STORE_F32  C -> fp32 buffer (QKV projection, LM head)
 //   EPI_RESID      x += C into the fp32 residual stream (O and down projections)
-//   EPI_SWIGLU     silu(C_gate) * C_up -> fp32 activation (gate/up projection)
+//   EPI_SWIGLU     silu(C_gate) * C_up -> activation planes (gate/up projection)
 //
-// bf16 models use the gfx950 matrix cores in half precision
-// (v_mfma_f32_16x16x32_f16).  Weights stay bf16 in HBM and are widened to
-// half (exact in half's normal range).  Activations arrive as two half
-// planes written by their producer: the "hi" part and the half-rounded
-// remainder "lo"; each weight fragment meets both (two matrix-core
-// products), so the activation operand carries ~22 significant bits and the
-// only rounding left is the fp32 accumulation.  The MFMA takes the weight tile as its first operand and
-// the activations as the second, so each lane ends up holding four
-// consecutive output columns of one row (lane l, register r -> column
-// 4*(l/16)+r, row l%16).
+// bf16 models use the gfx950 matrix cores in bf16
+// (v_mfma_f32_16x16x32_bf16).  Weights go from HBM to the matrix cores
+// untouched.  Activations arrive as two bf16 planes written by their
+// producer, hi = bf16(x) and lo = bf16(x - hi); each weight fragment meets
+// both (two products), so the activation operand carries ~17 significant
+// bits and the only other rounding is the fp32 accumulation.  The MFMA
+// takes the weight fragment as its first operand and the activations as the
+// second, so each lane ends up holding four consecutive output columns of
+// one row (lane l, register r -> column 4*(l/16)+r, row l%16).
 //   * skinny (M <= 16): weight-streaming.  A work-group owns 16 output
 //     columns (32 weight rows for SWIGLU); its four waves split K and are
-//     reduced through LDS in a fixed order.  Every lane loads 32 contiguous
-//     bytes of a weight row per 64-wide k step straight into registers.
-//   * tiled (M > 16): 128x128 output tile per 256-thread work-group, K in
-//     steps of 32 staged through double-buffered LDS (weights, activation hi,
-//     activation lo planes).  When the output has too few tiles to occupy the 256
-//     compute units, K is split over up to eight work-groups per tile; each
-//     writes its fp32 partial tile to the workspace and the last to arrive
-//     (per-tile counter) sums the partials in split order and runs the
-//     epilogue, so results do not depend on scheduling.  The global loads run
-//     two k steps ahead of the matrix cores (two register stages in front of
-//     the LDS double buffer).
+//     reduced through LDS in a fixed order.
+//   * tiled (M > 16): a work-group of eight (or four) waves owns 256 weight
+//     rows and 256 (or 128) activation rows; each wave computes all 256
+//     weight rows against its own 32 activation rows.  The weight tile is the
+//     only operand that goes through LDS (three buffers, k steps of 32,
+//     loaded three steps ahead into registers); each wave loads its
+//     activation fragments (both planes) straight into registers two steps
+//     ahead.  LDS traffic per
+//     multiply-add is then set by the weights alone, which keeps the LDS
+//     port (128 B/clk/CU) below the matrix-core rate.  When the output has
+//     too few tiles to occupy the 256 compute units, K is split over several
+//     work-groups per tile; each writes its fp32 partial sums to the
+//     workspace and a second kernel adds them in split order and runs the
+//     epilogue, so results do not depend on scheduling.  (Handing partials
+//     between work-groups inside one kernel would need a device-scope
+//     release per work-group, which on this chip writes back the whole L2.)
 // fp32 (the small reference-shape path) uses a plain LDS-tiled VALU kernel.
 #include "cad_internal.h"
 
@@ -35,11 +39,9 @@ namespace cad {
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
-
-
 // Apply the epilogue to four consecutive output columns n .. n+3 of row m.
 // For SWIGLU `c` holds the gate values and `cu` the matching up values; the
-// activation is written as fp32 or (SPLIT, bf16 models) as half hi / lo planes.
+// activation is written as fp32 or (SPLIT, bf16 models) as bf16 hi / lo planes.
 template <int EPI, bool SPLIT>
 __device__ __forceinline__ void epi4(const GemmArgs& a, int m, int n, f32x4 c, f32x4 cu) {
   if (m >= a.M) return;
@@ -58,10 +60,17 @@ __device__ __forceinline__ void epi4(const GemmArgs& a, int m, int n, f32x4 c, f
         if (n + r < a.N) o[r] = (EPI == EPI_RESID) ? o[r] + c[r] : c[r];
     }
   } else if (SPLIT) {
-    f16_t* o = (f16_t*)a.out_act + (int64_t)m * a.N + n;
-    f16_t* ol = (f16_t*)a.out_act_lo + (int64_t)m * a.N + n;
-    for (int r = 0; r < 4; ++r)
-      if (n + r < a.N) split_f16(silu_mul(c[r], cu[r]), o[r], ol[r]);
+    bf16_t* o = (bf16_t*)a.out_act + (int64_t)m * a.N + n;
+    bf16_t* ol = (bf16_t*)a.out_act_lo + (int64_t)m * a.N + n;
+    if (n + 3 < a.N && ((a.N & 3) == 0)) {
+      bf16_t h[4], l[4];
+      for (int r = 0; r < 4; ++r) split_bf16(silu_mul(c[r], cu[r]), h[r], l[r]);
+      *(u32x2*)o = u32x2{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16)};
+      *(u32x2*)ol = u32x2{l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16)};
+    } else {
+      for (int r = 0; r < 4; ++r)
+        if (n + r < a.N) split_bf16(silu_mul(c[r], cu[r]), o[r], ol[r]);
+    }
   } else {
     float* o = (float*)a.out_act + (int64_t)m * a.N + n;
     for (int r = 0; r < 4; ++r)
@@ -89,8 +98,8 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& a) {
   if (NB == 2) wrow[NB - 1] = W + (a.up_off + ncol) * a.ldw;
   // activation rows past M read row M - 1 and are dropped by the epilogue
   const int64_t aoff = (int64_t)min(i16, a.M - 1) * a.lda;
-  const f16_t* arow_hi = (const f16_t*)a.A + aoff;
-  const f16_t* arow_lo = (const f16_t*)a.A_lo + aoff;
+  const bf16_t* arow_hi = (const bf16_t*)a.A + aoff;
+  const bf16_t* arow_lo = (const bf16_t*)a.A_lo + aoff;
   // k split across waves in units of 64
   const int kp_total = a.K / 64;
   const int kp0 = (kp_total * wave) / SK_WAVES, kp1 = (kp_total * (wave + 1)) / SK_WAVES;
@@ -127,9 +136,8 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& a) {
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const u32x4 w = bf16x8_to_f16x8(wv[b][u][h]);
-          acc[b] = mfma16(w, ah[h], acc[b]);
-          acc[b] = mfma16(w, al[h], acc[b]);
+          acc[b] = mfma16_bf(wv[b][u][h], ah[h], acc[b]);
+          acc[b] = mfma16_bf(wv[b][u][h], al[h], acc[b]);
         }
     }
   }
@@ -142,9 +150,9 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& a) {
       const u32x4* p = (const u32x4*)(wrow[b] + k);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const u32x4 w = bf16x8_to_f16x8(p[h]);
-        acc[b] = mfma16(w, ah[h], acc[b]);
-        acc[b] = mfma16(w, al[h], acc[b]);
+        const u32x4 w = p[h];
+        acc[b] = mfma16_bf(w, ah[h], acc[b]);
+        acc[b] = mfma16_bf(w, al[h], acc[b]);
       }
     }
   }
@@ -164,14 +172,15 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 tiled: 128 (weight rows) x 128 (activation rows) per work-group
+// bf16 tiled
 // ---------------------------------------------------------------------------
-constexpr int TB = 128, TK = 32, TLD = TK + 8;  // 80-byte rows: 16-row fragment reads hit distinct banks
+constexpr int TK = 32;         // k per pipeline step (one MFMA k-slice)
+constexpr int WLD = TK + 8;    // LDS row stride of a weight stage (80 bytes: 16-row fragment reads hit distinct banks)
 
 // Work-group -> (weight tile tn, activation tile tm, k split), weight tile
-// fastest: the work-groups resident at one time share a few activation
-// tiles, and each XCD (work-groups are dealt to the eight XCDs round-robin)
-// sees every eighth weight tile for all of them.
+// fastest: work-groups that share a weight tile are n_tn apart, which puts
+// them on the same XCD (work-groups are dealt to the eight XCDs round-robin)
+// whenever n_tn is a multiple of eight.
 __device__ __forceinline__ void gemm_tile_of(int n_tn, int n_tm, int& tn, int& tm, int& sp) {
   const int id = blockIdx.x;
   tn = id % n_tn;
@@ -179,169 +188,173 @@ __device__ __forceinline__ void gemm_tile_of(int n_tn, int n_tm, int& tn, int& t
   sp = id / (n_tn * n_tm);
 }
 
-template <int EPI>
+template <int EPI, int TN, int NW, int MB>
 __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& a, int n_tn, int n_tm, int splits) {
-  __shared__ __attribute__((aligned(16))) f16_t sw[2][TB * TLD];
-  __shared__ __attribute__((aligned(16))) f16_t sah[2][TB * TLD];
-  __shared__ __attribute__((aligned(16))) f16_t sal[2][TB * TLD];
-  __shared__ int s_last;
+  constexpr int NT = 64 * NW;       // threads
+  constexpr int TM = 16 * MB * NW;  // activation rows per tile (MB 16-row blocks per wave)
+  constexpr int NB = TN / 16;       // 16-row weight blocks (every wave covers all of them)
+  constexpr int WCH = TN * 4 / NT;  // 16-byte weight chunks per thread per k step
+  static_assert(WCH >= 1 && TN * 4 % NT == 0, "weight staging must cover the tile exactly");
+  __shared__ __attribute__((aligned(16))) bf16_t sw[3][TN * WLD];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, i16 = lane & 15;
-  const int wn = (wave & 1) * 64;   // wave's offset in the weight-row dim of the tile
-  const int wm = (wave >> 1) * 64;  // wave's offset in the activation-row dim
   int tn, tm, sp;
   gemm_tile_of(n_tn, n_tm, tn, tm, sp);
   const bf16_t* W = (const bf16_t*)a.W;
 
-  // global -> LDS assignment per 32-wide k step: weights 2 chunks of 8 bf16
-  // per thread (4 threads per row), activations likewise per plane
-  const bf16_t* wsrc[2];
-  int wsoff[2];
+  // weight staging: chunk c = tid + NT*i is 16 bytes (8 k) of tile row c/4
+  const bf16_t* wsrc[WCH];
+  int wsoff[WCH];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + 256 * i;
+  for (int i = 0; i < WCH; ++i) {
+    const int c = tid + NT * i;
     const int row = c >> 2, col = (c & 3) * 8;
-    wsoff[i] = row * TLD + col;
+    wsoff[i] = row * WLD + col;
     int64_t wr;
     if (EPI == EPI_SWIGLU) {
       // 16-row interleave: even blocks gate, odd blocks up, same output columns
       const int blk = row >> 4, pr = blk >> 1;
-      int j = tn * (TB / 2) + pr * 16 + (row & 15);
-      j = min(j, a.N - 1);
+      const int j = min(tn * (TN / 2) + pr * 16 + (row & 15), a.N - 1);
       wr = (blk & 1) ? a.up_off + j : j;
     } else {
-      wr = min(tn * TB + row, a.N - 1);
+      wr = min(tn * TN + row, a.N - 1);
     }
     wsrc[i] = W + wr * a.ldw + col;
   }
-  // activations: 2 chunks of 8 halves per plane per thread (4 threads per row);
-  // rows past M read row M - 1: their outputs are never stored
-  const f16_t* ahsrc[2];
-  const f16_t* alsrc[2];
-  int asoff[2];
+  // this wave's activation rows wrow0 + 16*mb + i16 (rows past M read row
+  // M - 1; their outputs are never stored), k offset 8*g within a step
+  const int wrow0 = tm * TM + 16 * MB * wave;
+  const bool live = wrow0 < a.M;  // wave-uniform: a wave past M only stages weights
+  const bf16_t* ahp[MB];
+  const bf16_t* alp[MB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + 256 * i;
-    const int row = c >> 2, col = (c & 3) * 8;
-    asoff[i] = row * TLD + col;
-    const int64_t off = (int64_t)min(tm * TB + row, a.M - 1) * a.lda + col;
-    ahsrc[i] = (const f16_t*)a.A + off;
-    alsrc[i] = (const f16_t*)a.A_lo + off;
+  for (int mb = 0; mb < MB; ++mb) {
+    const int64_t off = (int64_t)min(wrow0 + 16 * mb + i16, a.M - 1) * a.lda + 8 * g;
+    ahp[mb] = (const bf16_t*)a.A + off;
+    alp[mb] = (const bf16_t*)a.A_lo + off;
   }
-  // two register stages: the global loads of k step j are issued two steps
-  // before step j is computed and are written to LDS at the end of step j - 1.
-  // Every load is unconditional (indices are clamped instead) so that the
-  // waits for one stage never cover the other stage's loads.
-  u32x4 rw0[2], rh0[2], rl0[2], rw1[2], rh1[2], rl1[2];
-  auto gload = [&](u32x4 (&rw)[2], u32x4 (&rh)[2], u32x4 (&rl)[2], int kt) {
-    const int k0 = kt * TK;
+
+  f32x4 acc[NB][MB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      rw[i] = *(const u32x4*)(wsrc[i] + k0);
-      rh[i] = *(const u32x4*)(ahsrc[i] + k0);
-      rl[i] = *(const u32x4*)(alsrc[i] + k0);
+  for (int x = 0; x < NB; ++x)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[x][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Every global load is unconditional (indices are clamped instead), so the
+  // waits for one stage never cover another stage's loads.
+  auto wload = [&](u32x4 (&r)[WCH], int kt) {
+#pragma unroll
+    for (int i = 0; i < WCH; ++i) r[i] = *(const u32x4*)(wsrc[i] + kt * TK);
+  };
+  auto aload = [&](u32x4 (&r)[MB][2], int kt) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      r[mb][0] = *(const u32x4*)(ahp[mb] + kt * TK);
+      r[mb][1] = *(const u32x4*)(alp[mb] + kt * TK);
     }
   };
-  auto sstore = [&](const u32x4 (&rw)[2], const u32x4 (&rh)[2], const u32x4 (&rl)[2], int buf) {
+  auto wstore = [&](const u32x4 (&r)[WCH], int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *(u32x4*)(&sw[buf][wsoff[i]]) = bf16x8_to_f16x8(rw[i]);
-      *(u32x4*)(&sah[buf][asoff[i]]) = rh[i];
-      *(u32x4*)(&sal[buf][asoff[i]]) = rl[i];
-    }
+    for (int i = 0; i < WCH; ++i) *(u32x4*)(&sw[buf][wsoff[i]]) = r[i];
   };
-  f32x4 acc[4][4];
+  auto compute = [&](int buf, const u32x4 (&ra)[MB][2]) {
+    if (!live) {
+      // consume the activation registers anyway: otherwise their loads are
+      // still in flight on this path when the next loads reuse the registers,
+      // and the compiler guards every later load with a wait for all of them
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
-#pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int buf) {
-    u32x4 fw[4], fh[4], fl[4];
-#pragma unroll
-    for (int x = 0; x < 4; ++x) fw[x] = *(const u32x4*)(&sw[buf][(wn + x * 16 + i16) * TLD + g * 8]);
-#pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      fh[y] = *(const u32x4*)(&sah[buf][(wm + y * 16 + i16) * TLD + g * 8]);
-      fl[y] = *(const u32x4*)(&sal[buf][(wm + y * 16 + i16) * TLD + g * 8]);
+      for (int mb = 0; mb < MB; ++mb) asm volatile("" ::"v"(ra[mb][0]), "v"(ra[mb][1]));
+      return;
     }
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < NB; ++x) {
+      const u32x4 w = *(const u32x4*)(&sw[buf][(x * 16 + i16) * WLD + g * 8]);
 #pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        acc[x][y] = mfma16(fw[x], fh[y], acc[x][y]);
-        acc[x][y] = mfma16(fw[x], fl[y], acc[x][y]);
+      for (int mb = 0; mb < MB; ++mb) {
+        acc[x][mb] = mfma16_bf(w, ra[mb][0], acc[x][mb]);
+        acc[x][mb] = mfma16_bf(w, ra[mb][1], acc[x][mb]);
       }
+    }
   };
 
   const int nk = a.K / TK;
   const int kt0 = (int)((int64_t)nk * sp / splits), kt1 = (int)((int64_t)nk * (sp + 1) / splits);
-  gload(rw0, rh0, rl0, kt0);
-  sstore(rw0, rh0, rl0, 0);
-  gload(rw1, rh1, rl1, min(kt0 + 1, kt1 - 1));
+  auto cl = [&](int kt) { return min(kt, kt1 - 1); };  // past the end: load the last step again (never used)
+  // Pipeline over three LDS buffers and three register buffers per operand:
+  // the weights of step j are loaded at the start of step j - 3 into rw[j%3]
+  // and written to LDS buffer j%3 at the end of step j - 2; the activations
+  // of step j are loaded at the start of step j - 2 into ra[j%3].  The
+  // prologue issues its loads in the order the loop does, so the loop is
+  // entered with the same loads in flight as it is re-entered.
+  u32x4 rw0[WCH], rw1[WCH], rw2[WCH], ra0[MB][2], ra1[MB][2], ra2[MB][2];
+  wload(rw0, kt0);
+  wload(rw1, cl(kt0 + 1));
+  aload(ra0, kt0);
+  wload(rw2, cl(kt0 + 2));
+  aload(ra1, cl(kt0 + 1));
+  wstore(rw0, 0);
+  wstore(rw1, 1);
   __syncthreads();
-  for (int kt = kt0; kt < kt1; kt += 2) {
-    // even step: LDS buffer 0 holds step kt, stage 1 step kt + 1 (past the
-    // end: a repeat of the last step, staged into a buffer nobody reads)
-    gload(rw0, rh0, rl0, min(kt + 2, kt1 - 1));
-    compute(0);
-    sstore(rw1, rh1, rl1, 1);
-    __syncthreads();
-    if (kt + 1 >= kt1) break;
-    // odd step: LDS buffer 1 holds step kt + 1, stage 0 step kt + 2
-    gload(rw1, rh1, rl1, min(kt + 3, kt1 - 1));
-    compute(1);
-    sstore(rw0, rh0, rl0, 0);
-    __syncthreads();
+#define CAD_GEMM_STEP(KT, U, RW_NEW, RA_NEW, RA_CUR, RW_OUT)   \
+  wload(RW_NEW, cl((KT) + 3));                                  \
+  aload(RA_NEW, cl((KT) + 2));                                  \
+  __builtin_amdgcn_sched_barrier(0);                            \
+  compute(U, RA_CUR);                                           \
+  __builtin_amdgcn_sched_barrier(0);                            \
+  wstore(RW_OUT, ((U) + 2) % 3);                                \
+  __syncthreads();
+  // three steps per iteration, no exit in between (every path back to the
+  // loop head has the same loads in flight); up to two more steps after it
+  int kt = kt0;
+  for (; kt + 2 < kt1; kt += 3) {
+    CAD_GEMM_STEP(kt, 0, rw0, ra2, ra0, rw2)
+    CAD_GEMM_STEP(kt + 1, 1, rw1, ra0, ra1, rw0)
+    CAD_GEMM_STEP(kt + 2, 2, rw2, ra1, ra2, rw1)
   }
+  if (kt < kt1) {
+    CAD_GEMM_STEP(kt, 0, rw0, ra2, ra0, rw2)
+  }
+  if (kt + 1 < kt1) {
+    CAD_GEMM_STEP(kt + 1, 1, rw1, ra0, ra1, rw0)
+  }
+#undef CAD_GEMM_STEP
+  // epilogue: acc[x][mb] lane -> weight rows 16x + 4g + r, activation row wrow0 + 16mb + i16
+  auto emit = [&](int x, int mb, f32x4 c, f32x4 cu) {
+    const int m = wrow0 + 16 * mb + i16;
+    if (EPI == EPI_SWIGLU)
+      epi4<EPI, true>(a, m, tn * (TN / 2) + (x >> 1) * 16 + 4 * g, c, cu);  // block x: gate, x + 1: up
+    else
+      epi4<EPI, true>(a, m, tn * TN + x * 16 + 4 * g, c, c);
+  };
+  constexpr int XS = (EPI == EPI_SWIGLU) ? 2 : 1;
+  if (!live) return;
   if (splits > 1) {
-    // publish this split's partial tile; the last arrival sums all of them
-    const int tile = tm * n_tn + tn;
-    f32x4* mine = (f32x4*)(a.split_ws + ((int64_t)tile * splits + sp) * GEMM_TILE_FLOATS);
+    // partial sums of this k split -> workspace [split][M][ncols] (fp32; for
+    // SWIGLU gate columns 0..N-1 and up columns N..2N-1); a separate kernel
+    // adds the splits in order and runs the epilogue
+    const int ncols = (EPI == EPI_SWIGLU) ? 2 * a.N : a.N;
+    float* ws = a.split_ws + (int64_t)sp * a.M * ncols;
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = wrow0 + 16 * mb + i16;
+      if (m >= a.M) continue;
 #pragma unroll
-      for (int y = 0; y < 4; ++y) mine[(x * 4 + y) * 256 + tid] = acc[x][y];
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&a.split_cnt[tile], 1) == splits - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    // sum in split order (this work-group's own partial is read back too)
-    const f32x4* all = (const f32x4*)(a.split_ws + (int64_t)tile * splits * GEMM_TILE_FLOATS) + tid;
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int y = 0; y < 4; ++y) acc[x][y] = all[(x * 4 + y) * 256];
-    for (int q = 1; q < splits; ++q) {
-      const f32x4* pq = all + (int64_t)q * (GEMM_TILE_FLOATS / 4);
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] += pq[(x * 4 + y) * 256];
-    }
-    if (tid == 0) a.split_cnt[tile] = 0;
-  }
-  // epilogue: acc[x][y] lane -> weight rows wn + 16x + 4g + r, activation row wm + 16y + i16
-#pragma unroll
-  for (int y = 0; y < 4; ++y) {
-    const int m = tm * TB + wm + y * 16 + i16;
-    if (EPI == EPI_SWIGLU) {
-#pragma unroll
-      for (int x = 0; x < 4; x += 2) {
-        const int blk = (wn >> 4) + x;  // even block: gate; blk + 1: up
-        const int n = tn * (TB / 2) + (blk >> 1) * 16 + 4 * g;
-        epi4<EPI, true>(a, m, n, acc[x][y], acc[x + 1][y]);
-      }
-    } else {
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int n = tn * TB + wn + x * 16 + 4 * g;
-        epi4<EPI, true>(a, m, n, acc[x][y], acc[x][y]);
+      for (int x = 0; x < NB; ++x) {
+        // output column of this fragment (N is a multiple of 64 on this
+        // path, so a group of four never straddles it)
+        const int j = (EPI == EPI_SWIGLU) ? tn * (TN / 2) + (x >> 1) * 16 + 4 * g : tn * TN + x * 16 + 4 * g;
+        if (j >= a.N) continue;
+        const int n = (EPI == EPI_SWIGLU && (x & 1)) ? a.N + j : j;
+        *(f32x4*)(ws + (int64_t)m * ncols + n) = acc[x][mb];
       }
     }
+    return;
   }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int x = 0; x < NB; x += XS) emit(x, mb, acc[x][mb], acc[x + XS - 1][mb]);
 }
 
 // ---------------------------------------------------------------------------
@@ -403,10 +416,38 @@ __device__ __forceinline__ void gemm_f32_body(const GemmArgs& a) {
 // One named kernel per projection and path, so that profiles attribute time
 // to the projection (qkv, o, gate_up, down, lm_head) rather than to a shared
 // template instance.
+// Sum of the k-split partials in split order, then the epilogue; one
+// thread per four consecutive output columns of one row.
+template <int EPI>
+__device__ __forceinline__ void gemm_reduce_body(const GemmArgs& a, int splits) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // group of four columns
+  const int groups = a.N / 4;
+  if (q >= (int64_t)a.M * groups) return;
+  const int m = (int)(q / groups), n = (int)(q % groups) * 4;
+  const int ncols = (EPI == EPI_SWIGLU) ? 2 * a.N : a.N;
+  const int64_t plane = (int64_t)a.M * ncols;
+  const float* p = a.split_ws + (int64_t)m * ncols + n;
+  f32x4 c = *(const f32x4*)p, cu = c;
+  if (EPI == EPI_SWIGLU) cu = *(const f32x4*)(p + a.N);
+  for (int s = 1; s < splits; ++s) {
+    c += *(const f32x4*)(p + s * plane);
+    if (EPI == EPI_SWIGLU) cu += *(const f32x4*)(p + s * plane + a.N);
+  }
+  epi4<EPI, true>(a, m, n, c, cu);
+}
+
+// Tiled shapes: eight waves (two per SIMD) of 256 weight rows x 256
+// activation rows, and four waves of 256 x 128 for spans of at most 128 rows.
+constexpr int TILE_N = 256;
 #define CAD_GEMM_KERNELS(NAME, EPI)                                                        \
-  __global__ void __launch_bounds__(256, 2)                                                \
-      k_gemm_##NAME(GemmArgs a, int n_tn, int n_tm, int splits) {                          \
-    gemm_tiled_body<EPI>(a, n_tn, n_tm, splits);                                           \
+  __global__ void __launch_bounds__(512) k_gemm_##NAME(GemmArgs a, int n_tn, int n_tm, int splits) { \
+    gemm_tiled_body<EPI, TILE_N, 8, 2>(a, n_tn, n_tm, splits);                             \
+  }                                                                                        \
+  __global__ void __launch_bounds__(256) k_gemm4_##NAME(GemmArgs a, int n_tn, int n_tm, int splits) { \
+    gemm_tiled_body<EPI, TILE_N, 4, 2>(a, n_tn, n_tm, splits);                             \
+  }                                                                                        \
+  __global__ void __launch_bounds__(256) k_gemm_reduce_##NAME(GemmArgs a, int splits) {    \
+    gemm_reduce_body<EPI>(a, splits);                                                      \
   }                                                                                        \
   __global__ void __launch_bounds__(64 * SK_WAVES) k_gemv_##NAME(GemmArgs a) {             \
     gemm_skinny_body<EPI>(a);                                                              \
@@ -421,40 +462,51 @@ CAD_GEMM_KERNELS(lm_head, EPI_STORE_F32)
 #undef CAD_GEMM_KERNELS
 
 typedef void (*TiledFn)(GemmArgs, int, int, int);
+typedef void (*ReduceFn)(GemmArgs, int);
 typedef void (*PlainFn)(GemmArgs);
 
 template <int EPI>
-static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled, PlainFn skinny, PlainFn f32,
-                             hipStream_t s) {
+static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled8, TiledFn tiled4, ReduceFn reduce,
+                             PlainFn skinny, PlainFn f32, hipStream_t s) {
   if (dtype == CAD_F32) {
     dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
     hipLaunchKernelGGL(f32, grid, dim3(256), 0, s, a);
   } else if (a.M <= 16) {
     hipLaunchKernelGGL(skinny, dim3((a.N + 15) / 16), dim3(64 * SK_WAVES), 0, s, a);
   } else {
-    const int cols_per_tile = (EPI == EPI_SWIGLU) ? TB / 2 : TB;
-    const int n_tn = (a.N + cols_per_tile - 1) / cols_per_tile, n_tm = (a.M + TB - 1) / TB;
+    const bool small = a.M <= 128;
+    const int tm_rows = small ? 128 : 256;
+    const int cols_per_tile = (EPI == EPI_SWIGLU) ? TILE_N / 2 : TILE_N;
+    const int n_tn = (a.N + cols_per_tile - 1) / cols_per_tile, n_tm = (a.M + tm_rows - 1) / tm_rows;
     const int tiles = n_tn * n_tm, nk = a.K / TK;
-    // split K while the tiles alone leave compute units idle (two
-    // work-groups fit per CU), keeping at least 64 k steps of 32 per split
+    // one work-group per CU at a time: split K while the split tiles still
+    // fit the 256 compute units at once, keeping at least 16 k steps of 32
+    // per split and the partials within the workspace
+    const int64_t split_floats = (int64_t)a.M * a.N * (EPI == EPI_SWIGLU ? 2 : 1);
     int splits = 1;
-    if (EPI != EPI_SWIGLU && a.split_ws && a.split_cnt)
-      while (splits < 8 && tiles * splits * 2 <= GEMM_SPLIT_SLOTS && nk / (splits * 2) >= 64 &&
-             (int64_t)tiles * splits * 2 * GEMM_TILE_FLOATS <= GEMM_SPLIT_FLOATS)
-        splits *= 2;
-    hipLaunchKernelGGL(tiled, dim3(tiles * splits), dim3(256), 0, s, a, n_tn, n_tm, splits);
+    if (a.split_ws && a.N % 64 == 0)
+      while (tiles * (splits + 1) <= 256 && nk / (splits + 1) >= 16 && split_floats * (splits + 1) <= GEMM_SPLIT_FLOATS)
+        ++splits;
+    hipLaunchKernelGGL(small ? tiled4 : tiled8, dim3(tiles * splits), dim3(small ? 256 : 512), 0, s, a, n_tn, n_tm,
+                       splits);
+    if (splits > 1) {
+      const int64_t groups = (int64_t)a.M * (a.N / 4);
+      hipLaunchKernelGGL(reduce, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, a, splits);
+    }
   }
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(int dtype, int role, const GemmArgs& a, hipStream_t s) {
   switch (role) {
-    case GEMM_QKV: return launch_epi<EPI_STORE_F32>(dtype, a, k_gemm_qkv, k_gemv_qkv, k_gemm_f32_qkv, s);
-    case GEMM_O: return launch_epi<EPI_RESID>(dtype, a, k_gemm_o, k_gemv_o, k_gemm_f32_o, s);
-    case GEMM_GATE_UP:
-      return launch_epi<EPI_SWIGLU>(dtype, a, k_gemm_gate_up, k_gemv_gate_up, k_gemm_f32_gate_up, s);
-    case GEMM_DOWN: return launch_epi<EPI_RESID>(dtype, a, k_gemm_down, k_gemv_down, k_gemm_f32_down, s);
-    default: return launch_epi<EPI_STORE_F32>(dtype, a, k_gemm_lm_head, k_gemv_lm_head, k_gemm_f32_lm_head, s);
+#define CAD_LAUNCH(EPI, NAME) \
+  launch_epi<EPI>(dtype, a, k_gemm_##NAME, k_gemm4_##NAME, k_gemm_reduce_##NAME, k_gemv_##NAME, k_gemm_f32_##NAME, s)
+    case GEMM_QKV: return CAD_LAUNCH(EPI_STORE_F32, qkv);
+    case GEMM_O: return CAD_LAUNCH(EPI_RESID, o);
+    case GEMM_GATE_UP: return CAD_LAUNCH(EPI_SWIGLU, gate_up);
+    case GEMM_DOWN: return CAD_LAUNCH(EPI_RESID, down);
+    default: return CAD_LAUNCH(EPI_STORE_F32, lm_head);
+#undef CAD_LAUNCH
   }
 }
 

@@ -47,7 +47,7 @@ hipError_t launch_embed(int dtype, const void* table, int vocab, int d, const in
 
 // ---------------------------------------------------------------------------
 // RMSNorm: out[r] = x[r] / sqrt(mean(x[r]^2) + eps) * g: fp32 for fp32
-// models, split into half hi / lo planes (the next projection's operands)
+// models, split into bf16 hi / lo planes (the next projection's operands)
 // for bf16 models
 // ---------------------------------------------------------------------------
 template <typename T, bool SPLIT>
@@ -63,10 +63,10 @@ __global__ void k_rmsnorm(const float* __restrict__ x, const T* __restrict__ g, 
   for (int i = threadIdx.x; i < d; i += blockDim.x) {
     const float v = xr[i] * rs * to_f<T>(g[i]);
     if (SPLIT) {
-      f16_t hi, lo;
-      split_f16(v, hi, lo);
-      ((f16_t*)out)[(int64_t)r * d + i] = hi;
-      ((f16_t*)out_lo)[(int64_t)r * d + i] = lo;
+      bf16_t hi, lo;
+      split_bf16(v, hi, lo);
+      ((bf16_t*)out)[(int64_t)r * d + i] = hi;
+      ((bf16_t*)out_lo)[(int64_t)r * d + i] = lo;
     } else {
       ((float*)out)[(int64_t)r * d + i] = v;
     }
