@@ -72,8 +72,9 @@ typedef enum {
  * loop_depth > 1: one shared block (n_layers must be 1) applied loop_depth
  * times, with one KV cache per depth (CopyLoop's looped decoder).
  * max_tokens: the most span rows one call may carry (sizes the workspace).
- * Supported: dtype CAD_F32 any head_dim <= 128 (even); dtype CAD_BF16
- * head_dim 64 or 128 and d_model, ffn_dim, n_q_heads*head_dim multiples of 64. */
+ * Supported: d_model a multiple of 4, at most 8192; dtype CAD_F32 any
+ * head_dim <= 128 (even); dtype CAD_BF16 head_dim 64 or 128 and d_model,
+ * ffn_dim, n_q_heads*head_dim multiples of 64. */
 typedef struct {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
   int32_t loop_depth;

@@ -94,7 +94,8 @@ struct cad_model {
   f16_t* span_k = nullptr;       // this call's span K/V at half precision (bf16 models)
   f16_t* span_v = nullptr;
   int32_t span_cap = 0;          // rows of the span workspace
-  float* split_ws = nullptr;     // split-K partial tiles of the tiled GEMM (bf16 models)
+  float* split_ws = nullptr;     // split-K partial sums of the projections (bf16 models)
+  int x_parts = 0;               // partial planes in split_ws still to be added to x
 };
 
 namespace {
@@ -136,6 +137,7 @@ cad_status check_config(const cad_config* c) {
   if (c->loop_depth > 1 && c->n_layers != 1) return fail(CAD_E_ARG, "looped model needs n_layers == 1");
   if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) return fail(CAD_E_ARG, "bad rope_theta or rms_eps");
   if (c->head_dim % 2) return fail(CAD_E_UNSUPPORTED, "odd head_dim");
+  if (c->d_model % 4 || c->d_model > 8192) return fail(CAD_E_UNSUPPORTED, "d_model must be a multiple of 4, at most 8192");
   if (c->dtype == CAD_F32) {
     if (c->head_dim > 128) return fail(CAD_E_UNSUPPORTED, "fp32 path supports head_dim <= 128");
   } else {
@@ -206,15 +208,17 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
   for (int ci = c0; ci < c1; ++ci) {
     const int li = c.loop_depth > 1 ? 0 : ci;
     const KVView v = view_of(m, kv, ci);
-    LAUNCH(PF_NORM, launch_rmsnorm(c.dtype, m->x, m->attn_norm[li], R, d, c.rms_eps, m->hn,
-                                   lo_plane(m, m->hn, d), s));
+    LAUNCH(PF_NORM, launch_rmsnorm(c.dtype, m->x, m->split_ws, m->x_parts, m->attn_norm[li], R, d, c.rms_eps,
+                                   m->hn, lo_plane(m, m->hn, d), s));
+    m->x_parts = 0;
     GemmArgs g{};
     g.A = m->hn; g.A_lo = lo_plane(m, m->hn, d); g.lda = d; g.W = m->w_qkv[li]; g.ldw = d;
     g.M = R; g.N = qkv_rows; g.K = d; g.out_f32 = m->qkv; g.ldo = qkv_rows;
     g.split_ws = m->split_ws;
-    LAUNCH(PF_QKV, launch_gemm(c.dtype, GEMM_QKV, g, s));
-    LAUNCH(PF_ROPE, launch_rope_append(c.dtype, m->qkv, R, hq, hkv, hd, m->freq, rm, v, write_limit, m->q,
-                               dev_status, s));
+    int qkv_parts = 0;
+    LAUNCH(PF_QKV, launch_gemm(c.dtype, GEMM_QKV, g, s, &qkv_parts));
+    LAUNCH(PF_ROPE, launch_rope_append(c.dtype, m->qkv, m->split_ws, qkv_parts, R, hq, hkv, hd, m->freq, rm, v,
+                                       write_limit, m->q, dev_status, s));
     LAUNCH(PF_ATTN, launch_attention(c.dtype, m->q, R, hq, hkv, hd, rm, v, n_parts, part_len, m->part_o,
                                      m->part_ml, m->attn, lo_plane(m, m->attn, (int64_t)hq * hd), dev_status, s));
     if (c.dtype == CAD_BF16 && n_parts > 1)
@@ -225,9 +229,10 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
     g.W = m->w_o[li]; g.ldw = hq * hd;
     g.M = R; g.N = d; g.K = hq * hd; g.out_f32 = m->x; g.ldo = d;
     g.split_ws = m->split_ws;
-    LAUNCH(PF_O, launch_gemm(c.dtype, GEMM_O, g, s));
-    LAUNCH(PF_NORM, launch_rmsnorm(c.dtype, m->x, m->ffn_norm[li], R, d, c.rms_eps, m->hn,
+    LAUNCH(PF_O, launch_gemm(c.dtype, GEMM_O, g, s, &m->x_parts));
+    LAUNCH(PF_NORM, launch_rmsnorm(c.dtype, m->x, m->split_ws, m->x_parts, m->ffn_norm[li], R, d, c.rms_eps, m->hn,
                                    lo_plane(m, m->hn, d), s));
+    m->x_parts = 0;
     g = GemmArgs{};
     g.A = m->hn; g.A_lo = lo_plane(m, m->hn, d); g.lda = d; g.W = m->w_gate_up[li]; g.ldw = d;
     g.M = R; g.N = F; g.K = d; g.up_off = F; g.out_act = m->act; g.out_act_lo = lo_plane(m, m->act, F);
@@ -236,7 +241,7 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
     g.A = m->act; g.A_lo = lo_plane(m, m->act, F); g.lda = F; g.W = m->w_down[li]; g.ldw = F;
     g.M = R; g.N = d; g.K = F; g.out_f32 = m->x; g.ldo = d;
     g.split_ws = m->split_ws;
-    LAUNCH(PF_DOWN, launch_gemm(c.dtype, GEMM_DOWN, g, s));
+    LAUNCH(PF_DOWN, launch_gemm(c.dtype, GEMM_DOWN, g, s, &m->x_parts));
   }
   return CAD_OK;
 }
@@ -245,8 +250,9 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
 cad_status readout(cad_model* m, int R, float* logits, const uint32_t* mask, int32_t* argmax,
                    int32_t* dev_status, hipStream_t s) {
   const cad_config& c = m->cfg;
-  LAUNCH(PF_NORM, launch_rmsnorm(c.dtype, m->x, m->final_norm, R, c.d_model, c.rms_eps, m->hn,
-                                 lo_plane(m, m->hn, c.d_model), s));
+  LAUNCH(PF_NORM, launch_rmsnorm(c.dtype, m->x, m->split_ws, m->x_parts, m->final_norm, R, c.d_model, c.rms_eps,
+                                 m->hn, lo_plane(m, m->hn, c.d_model), s));
+  m->x_parts = 0;
   GemmArgs g{};
   g.A = m->hn; g.A_lo = lo_plane(m, m->hn, c.d_model); g.lda = c.d_model; g.W = m->lm_head; g.ldw = c.d_model;
   g.M = R; g.N = c.vocab; g.K = c.d_model; g.out_f32 = logits; g.ldo = c.vocab;
@@ -395,6 +401,7 @@ cad_status cad_splice_forward(cad_model* m, const cad_kv* kv, int64_t L, const i
   rm.L[0] = L;
   rowmap_pad(rm);
   const cad_config& c = m->cfg;
+  m->x_parts = 0;
   LAUNCH(PF_EMBED, launch_embed(c.dtype, m->tok_embed, c.vocab, c.d_model, span, N, m->x, dev_status, s));
   st = run_blocks(m, kv, rm, 0, c.n_layers, nullptr, dev_status, s);
   if (st != CAD_OK) return st;
@@ -440,6 +447,7 @@ cad_status cad_splice_forward_batched(cad_model* m, const cad_kv* kv, int32_t n_
     return fail(CAD_E_CAPACITY, "total rows %d > max_tokens %d", rm.total, m->cfg.max_tokens);
   hipStream_t s = (hipStream_t)stream;
   const cad_config& c = m->cfg;
+  m->x_parts = 0;
   LAUNCH(PF_EMBED, launch_embed(c.dtype, m->tok_embed, c.vocab, c.d_model, spans, rm.total, m->x, dev_status, s));
   st = run_blocks(m, kv, rm, 0, c.n_layers, nullptr, dev_status, s);
   if (st != CAD_OK) return st;
@@ -470,6 +478,7 @@ cad_status cad_splice_forward_looped(cad_model* m, const cad_kv* kv, int64_t L,
   rm.start[1] = N;
   rm.L[0] = L;
   rowmap_pad(rm);
+  m->x_parts = 0;
   LAUNCH(PF_EMBED, launch_embed(c.dtype, m->tok_embed, c.vocab, c.d_model, span, N, m->x, dev_status, s));
   st = run_blocks(m, kv, rm, 0, screen_depth, nullptr, dev_status, s);
   if (st != CAD_OK) return st;

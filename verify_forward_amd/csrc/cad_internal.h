@@ -142,13 +142,17 @@ constexpr int64_t GEMM_SPLIT_FLOATS = (int64_t)32 << 20;
 hipError_t launch_embed(int dtype, const void* table, int vocab, int d, const int32_t* tokens,
                         int rows, float* x, int32_t* status, hipStream_t s);
 // out: fp32 [rows][d] (fp32 models) or bf16 planes out (hi) / out_lo (bf16 models)
-hipError_t launch_rmsnorm(int dtype, const float* x, const void* gain, int rows, int d, float eps,
-                          void* out, void* out_lo, hipStream_t s);
-hipError_t launch_gemm(int dtype, int role, const GemmArgs& a, hipStream_t s);
-hipError_t launch_rope_append(int dtype, const float* qkv, int rows, int hq, int hkv, int hd,
-                              const double* freq, const RowMap& rm, KVView kv,
-                              const int32_t* write_limit, void* q_out, int32_t* status,
-                              hipStream_t s);
+// x += the n_part pending k-split partial planes x_part [n_part][rows][d]
+// (added in order, x written back), then the norm
+hipError_t launch_rmsnorm(int dtype, float* x, const float* x_part, int n_part, const void* gain, int rows, int d,
+                          float eps, void* out, void* out_lo, hipStream_t s);
+// partials: see launch_epi; nullptr makes every launch apply its epilogue
+hipError_t launch_gemm(int dtype, int role, const GemmArgs& a, hipStream_t s, int* partials = nullptr);
+// qkv: [rows][width] fp32, or (n_part > 0) the sum of the partial planes
+// qkv_part [n_part][rows][width]
+hipError_t launch_rope_append(int dtype, const float* qkv, const float* qkv_part, int n_part, int rows, int hq,
+                              int hkv, int hd, const double* freq, const RowMap& rm, KVView kv,
+                              const int32_t* write_limit, void* q_out, int32_t* status, hipStream_t s);
 // n_parts = cache partitions (keys < L, part_len each) + one span partition
 hipError_t launch_attention(int dtype, const void* q, int rows, int hq, int hkv, int hd,
                             const RowMap& rm, KVView kv, int n_parts, int part_len,

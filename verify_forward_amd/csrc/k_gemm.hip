@@ -14,9 +14,10 @@
 // takes the weight fragment as its first operand and the activations as the
 // second, so each lane ends up holding four consecutive output columns of
 // one row (lane l, register r -> column 4*(l/16)+r, row l%16).
-//   * skinny (M <= 16): weight-streaming.  A work-group owns 16 output
-//     columns (32 weight rows for SWIGLU); its four waves split K and are
-//     reduced through LDS in a fixed order.
+//   * skinny (M <= 16): weight-streaming.  A work-group owns 64 weight
+//     rows and a K range; the activation chunk is shared through LDS and
+//     each wave streams 16 weight rows into registers (sixteen lanes per
+//     row) and transposes them to MFMA fragments through LDS.
 //   * tiled (M > 16): a work-group of eight (or four) waves owns 256 weight
 //     rows and 256 (or 128) activation rows; each wave computes all 256
 //     weight rows against its own 32 activation rows.  The weight tile is the
@@ -79,95 +80,148 @@ __device__ __forceinline__ void epi4(const GemmArgs& a, int m, int n, f32x4 c, f
 }
 
 // ---------------------------------------------------------------------------
-// bf16 skinny: M <= 16
+// bf16 skinny: M <= 16, weight streaming
 // ---------------------------------------------------------------------------
-constexpr int SK_WAVES = 4;
+// A work-group of four waves owns 64 weight rows (four 16-row blocks, one
+// per wave; for SWIGLU a block is 8 gate rows + the 8 matching up rows) and
+// a range of K in chunks of 512.  The activations of a chunk (at most 16
+// rows, both planes) are staged once in LDS and shared by the four waves.
+// Each wave streams its 16 weight rows (1 KB per row and chunk) into
+// registers one chunk ahead, sixteen lanes per row per load (256 contiguous
+// bytes: HBM streams at ~5 TB/s this way against ~4 TB/s with four lanes
+// per row), and turns them into MFMA fragments through a small LDS
+// transpose, half a chunk at a time.  With K split over S work-groups the
+// partial sums go to the workspace and the consumer adds them.
+constexpr int SK_KC = 512;             // k per chunk
+constexpr int SK_ALD = SK_KC + 8;      // LDS row stride of the activation chunk (1040 B: conflict-free)
+constexpr int SK_WLD = SK_KC / 2 + 8;  // LDS row stride of a half-chunk weight transpose (528 B: conflict-free)
+constexpr int SK_AIT = 16 * 2 * (SK_KC / 8) / 256;  // 16-byte activation pieces per thread and chunk
 
 template <int EPI>
-__device__ __forceinline__ void gemm_skinny_body(const GemmArgs& a) {
-  constexpr int NB = (EPI == EPI_SWIGLU) ? 2 : 1;  // 16-row weight blocks per work-group
-  __shared__ f32x4 part[SK_WAVES][NB][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ void gemm_skinny_body(const GemmArgs& a, int n_rg, int splits) {
+  __shared__ __attribute__((aligned(16))) bf16_t sa[2][16 * SK_ALD];     // [plane][row][k]
+  __shared__ __attribute__((aligned(16))) bf16_t swt[4][16 * SK_WLD];    // per-wave weight transpose
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, i16 = lane & 15;
-  const int n0 = blockIdx.x * 16;
+  const int rg = blockIdx.x % n_rg, sp = blockIdx.x / n_rg;
+  const int blk = rg * 4 + wave;  // this wave's 16-row weight block
   const bf16_t* W = (const bf16_t*)a.W;
-  // this lane's weight rows (clamped: columns past N are computed and dropped)
-  const int ncol = min(n0 + i16, a.N - 1);
-  const bf16_t* wrow[NB];
-  wrow[0] = W + (int64_t)ncol * a.ldw;
-  if (NB == 2) wrow[NB - 1] = W + (a.up_off + ncol) * a.ldw;
-  // activation rows past M read row M - 1 and are dropped by the epilogue
-  const int64_t aoff = (int64_t)min(i16, a.M - 1) * a.lda;
-  const bf16_t* arow_hi = (const bf16_t*)a.A + aoff;
-  const bf16_t* arow_lo = (const bf16_t*)a.A_lo + aoff;
-  // k split across waves in units of 64
-  const int kp_total = a.K / 64;
-  const int kp0 = (kp_total * wave) / SK_WAVES, kp1 = (kp_total * (wave + 1)) / SK_WAVES;
-  f32x4 acc[NB];
-  for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // 16 activations at k .. k + 15: (hi, lo) operands of the two products
-  auto act16 = [&](int k, u32x4 (&hi)[2], u32x4 (&lo)[2]) {
-    const u32x4* qh = (const u32x4*)(arow_hi + k);
-    const u32x4* ql = (const u32x4*)(arow_lo + k);
-    hi[0] = qh[0];
-    hi[1] = qh[1];
-    lo[0] = ql[0];
-    lo[1] = ql[1];
+  // weight row of block row i (clamped: columns past N are computed and dropped)
+  auto wrow_of = [&](int i) -> int64_t {
+    if (EPI == EPI_SWIGLU) {
+      const int col = min(blk * 8 + (i & 7), a.N - 1);
+      return (i < 8) ? col : a.up_off + col;
+    }
+    return min(blk * 16 + i, a.N - 1);
   };
-  constexpr int U = 4;
-  int kp = kp0;
-  for (; kp + U <= kp1; kp += U) {
-    u32x4 wv[NB][U][2];
+  // load j (0..15) of a chunk: block row 4 (j % 4) + lane / 16, k offset
+  // 128 (j / 4) + 8 (lane % 16) within the chunk
+  const bf16_t* wp[4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = (kp + u) * 64 + g * 16;
+  for (int q = 0; q < 4; ++q) wp[q] = W + wrow_of(4 * q + g) * a.ldw + 8 * i16;
+  const int nch = (a.K + SK_KC - 1) / SK_KC;
+  const int c0 = (int)((int64_t)nch * sp / splits), c1 = (int)((int64_t)nch * (sp + 1) / splits);
+  // activation staging: piece q = tid + 256*j is 16 bytes: plane q / 1024,
+  // row (q / 64) % 16, k offset 8 * (q % 64) within the chunk.  Rows >= M and
+  // k past K are written as zeros (their products vanish).
+  const bf16_t* ap[SK_AIT];
+  int aoff[SK_AIT], akk[SK_AIT];
+  bool aok[SK_AIT];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const u32x4* p = (const u32x4*)(wrow[b] + k);
-        wv[b][u][0] = __builtin_nontemporal_load(p);
-        wv[b][u][1] = __builtin_nontemporal_load(p + 1);
+  for (int j = 0; j < SK_AIT; ++j) {
+    const int q = tid + 256 * j;
+    const int plane = q >> 10, row = (q >> 6) & 15, kk = 8 * (q & 63);
+    aoff[j] = plane * (16 * SK_ALD) + row * SK_ALD + kk;
+    akk[j] = kk;
+    aok[j] = row < a.M;
+    ap[j] = (const bf16_t*)(plane ? a.A_lo : a.A) + (int64_t)min(row, a.M - 1) * a.lda + kk;
+  }
+  auto aload = [&](u32x4 (&r)[SK_AIT], int c) {
+#pragma unroll
+    for (int j = 0; j < SK_AIT; ++j) r[j] = *(const u32x4*)(ap[j] + min(c * SK_KC, a.K - 8 - akk[j]));
+  };
+  // unconditional stores (a branch here makes the compiler wait for every
+  // load in flight, the next chunk's weights included)
+  auto astore = [&](const u32x4 (&r)[SK_AIT], int c) {
+#pragma unroll
+    for (int j = 0; j < SK_AIT; ++j) {
+      const bool keep = aok[j] && c * SK_KC + akk[j] < a.K;
+      *(u32x4*)(&sa[0][0] + aoff[j]) = keep ? r[j] : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  // weights past K are clamped inside the row; the activations there are zero
+  auto wload = [&](u32x4 (&r)[16], int c) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      r[j] = __builtin_nontemporal_load((const u32x4*)(wp[j & 3] + min(c * SK_KC + 128 * (j >> 2), a.K - 8 - 8 * i16)));
+  };
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  bf16_t* tw = &swt[wave][0];
+  auto compute = [&](const u32x4 (&w)[16]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // half h: loads 8h .. 8h+7 hold k 256 h .. 256 h + 255 of the chunk
+#pragma unroll
+      for (int j = 8 * h; j < 8 * h + 8; ++j)
+        *(u32x4*)(tw + (4 * (j & 3) + g) * SK_WLD + 128 * ((j >> 2) & 1) + 8 * i16) = w[j];
+      const bf16_t* tr = tw + i16 * SK_WLD + 8 * g;
+      const bf16_t* sh = &sa[0][0] + i16 * SK_ALD + 256 * h + 8 * g;
+      const bf16_t* sl = &sa[1][0] + i16 * SK_ALD + 256 * h + 8 * g;
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) {
+        const u32x4 wf = *(const u32x4*)(tr + 32 * s2);
+        acc = mfma16_bf(wf, *(const u32x4*)(sh + 32 * s2), acc);
+        acc = mfma16_bf(wf, *(const u32x4*)(sl + 32 * s2), acc);
       }
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      u32x4 ah[2], al[2];
-      act16((kp + u) * 64 + g * 16, ah, al);
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          acc[b] = mfma16_bf(wv[b][u][h], ah[h], acc[b]);
-          acc[b] = mfma16_bf(wv[b][u][h], al[h], acc[b]);
-        }
-    }
-  }
-  for (; kp < kp1; ++kp) {
-    const int k = kp * 64 + g * 16;
-    u32x4 ah[2], al[2];
-    act16(k, ah, al);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const u32x4* p = (const u32x4*)(wrow[b] + k);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const u32x4 w = p[h];
-        acc[b] = mfma16_bf(w, ah[h], acc[b]);
-        acc[b] = mfma16_bf(w, al[h], acc[b]);
-      }
-    }
-  }
-#pragma unroll
-  for (int b = 0; b < NB; ++b) part[wave][b][lane] = acc[b];
+  };
+  // Pipeline: the activations of chunk j are loaded two steps ahead and
+  // written to LDS between two barriers at the end of step j - 1; the
+  // weights of chunk j are loaded at the start of step j - 1.  Activations
+  // are issued before weights, so waiting for them never waits for the
+  // weights.  Work-groups start their chunk sweep at different chunks
+  // (rotated by the row group), spreading the memory channels in use.
+  const int ncs = c1 - c0, rot = rg % ncs;
+  auto ch = [&](int i) { i = min(i, ncs - 1); return c0 + (i + rot) % ncs; };  // i-th chunk visited
+  u32x4 w0[16], w1[16], ra0[SK_AIT], ra1[SK_AIT];
+  aload(ra0, ch(0));
+  astore(ra0, ch(0));
+  aload(ra1, ch(1));
+  wload(w0, ch(0));
   __syncthreads();
-  if (wave == 0) {
-    f32x4 s[NB];
+  int i = 0;
+  for (; i + 1 < ncs; i += 2) {
+    aload(ra0, ch(i + 2));
+    wload(w1, ch(i + 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(w0);
+    __syncthreads();
+    astore(ra1, ch(i + 1));
+    __syncthreads();
+    aload(ra1, ch(i + 3));
+    wload(w0, ch(i + 2));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(w1);
+    __syncthreads();
+    astore(ra0, ch(i + 2));
+    __syncthreads();
+  }
+  if (i < ncs) compute(w0);
+  // lane: activation row m = i16, weight rows 4g + r of the block
+  const int m = i16;
+  if (EPI == EPI_SWIGLU) {
+    // lanes g = 0, 1 hold gate rows 4g + r, lanes g + 2 the matching up rows
+    f32x4 cu;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      s[b] = part[0][b][lane];
-      for (int w = 1; w < SK_WAVES; ++w) s[b] += part[w][b][lane];
+    for (int r = 0; r < 4; ++r) cu[r] = __shfl_xor(acc[r], 32);
+    if (g < 2) epi4<EPI, true>(a, m, blk * 8 + 4 * g, acc, cu);
+  } else {
+    const int n = blk * 16 + 4 * g;
+    if (splits == 1) {
+      epi4<EPI, true>(a, m, n, acc, acc);
+    } else if (m < a.M && n < a.N) {
+      *(f32x4*)(a.split_ws + ((int64_t)sp * a.M + m) * a.N + n) = acc;
     }
-    // lane holds C^T rows n0 + 4g + r (output columns) of activation row i16
-    epi4<EPI, true>(a, i16, n0 + 4 * g, s[0], s[NB - 1]);
   }
 }
 
@@ -449,8 +503,8 @@ constexpr int TILE_N = 256;
   __global__ void __launch_bounds__(256) k_gemm_reduce_##NAME(GemmArgs a, int splits) {    \
     gemm_reduce_body<EPI>(a, splits);                                                      \
   }                                                                                        \
-  __global__ void __launch_bounds__(64 * SK_WAVES) k_gemv_##NAME(GemmArgs a) {             \
-    gemm_skinny_body<EPI>(a);                                                              \
+  __global__ void __launch_bounds__(256) k_gemv_##NAME(GemmArgs a, int n_rg, int splits) { \
+    gemm_skinny_body<EPI>(a, n_rg, splits);                                                \
   }                                                                                        \
   __global__ void __launch_bounds__(256) k_gemm_f32_##NAME(GemmArgs a) { gemm_f32_body<EPI>(a); }
 
@@ -463,16 +517,33 @@ CAD_GEMM_KERNELS(lm_head, EPI_STORE_F32)
 
 typedef void (*TiledFn)(GemmArgs, int, int, int);
 typedef void (*ReduceFn)(GemmArgs, int);
+typedef void (*SkinnyFn)(GemmArgs, int, int);
 typedef void (*PlainFn)(GemmArgs);
 
+// partials != nullptr (store / residual epilogues only): a k-split result
+// may be left as *partials fp32 planes [split][M][N] in a.split_ws for the
+// consumer to add (in split order); *partials = 0 when the epilogue ran.
 template <int EPI>
 static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled8, TiledFn tiled4, ReduceFn reduce,
-                             PlainFn skinny, PlainFn f32, hipStream_t s) {
+                             SkinnyFn skinny, PlainFn f32, int* partials, hipStream_t s) {
+  if (partials) *partials = 0;
+  const bool leave = partials != nullptr && EPI != EPI_SWIGLU && a.split_ws != nullptr && a.N % 4 == 0;
   if (dtype == CAD_F32) {
     dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
     hipLaunchKernelGGL(f32, grid, dim3(256), 0, s, a);
   } else if (a.M <= 16) {
-    hipLaunchKernelGGL(skinny, dim3((a.N + 15) / 16), dim3(64 * SK_WAVES), 0, s, a);
+    const int nblk = (EPI == EPI_SWIGLU) ? (a.N + 7) / 8 : (a.N + 15) / 16;
+    const int n_rg = (nblk + 3) / 4;
+    const int nch = (a.K + SK_KC - 1) / SK_KC;
+    // about two work-groups per compute unit: split K (whole chunks) when
+    // the row groups alone are fewer
+    int splits = 1;
+    if (leave)
+      while (n_rg * (splits + 1) <= 512 && splits + 1 <= nch &&
+             (int64_t)(splits + 1) * a.M * a.N <= GEMM_SPLIT_FLOATS)
+        ++splits;
+    hipLaunchKernelGGL(skinny, dim3(n_rg * splits), dim3(256), 0, s, a, n_rg, splits);
+    if (splits > 1) *partials = splits;
   } else {
     const bool small = a.M <= 128;
     const int tm_rows = small ? 128 : 256;
@@ -490,17 +561,22 @@ static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled8, Tiled
     hipLaunchKernelGGL(small ? tiled4 : tiled8, dim3(tiles * splits), dim3(small ? 256 : 512), 0, s, a, n_tn, n_tm,
                        splits);
     if (splits > 1) {
-      const int64_t groups = (int64_t)a.M * (a.N / 4);
-      hipLaunchKernelGGL(reduce, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, a, splits);
+      if (leave) {
+        *partials = splits;
+      } else {
+        const int64_t groups = (int64_t)a.M * (a.N / 4);
+        hipLaunchKernelGGL(reduce, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, a, splits);
+      }
     }
   }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(int dtype, int role, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm(int dtype, int role, const GemmArgs& a, hipStream_t s, int* partials) {
   switch (role) {
 #define CAD_LAUNCH(EPI, NAME) \
-  launch_epi<EPI>(dtype, a, k_gemm_##NAME, k_gemm4_##NAME, k_gemm_reduce_##NAME, k_gemv_##NAME, k_gemm_f32_##NAME, s)
+  launch_epi<EPI>(dtype, a, k_gemm_##NAME, k_gemm4_##NAME, k_gemm_reduce_##NAME, k_gemv_##NAME, k_gemm_f32_##NAME, \
+                  partials, s)
     case GEMM_QKV: return CAD_LAUNCH(EPI_STORE_F32, qkv);
     case GEMM_O: return CAD_LAUNCH(EPI_RESID, o);
     case GEMM_GATE_UP: return CAD_LAUNCH(EPI_SWIGLU, gate_up);

@@ -50,38 +50,83 @@ hipError_t launch_embed(int dtype, const void* table, int vocab, int d, const in
 // models, split into bf16 hi / lo planes (the next projection's operands)
 // for bf16 models
 // ---------------------------------------------------------------------------
-template <typename T, bool SPLIT>
-__global__ void k_rmsnorm(const float* __restrict__ x, const T* __restrict__ g, int d, float eps,
-                          void* __restrict__ out, void* __restrict__ out_lo) {
-  __shared__ float red[16];
+template <typename T, bool SPLIT, int V4>
+__global__ void __launch_bounds__(ROW_THREADS) k_rmsnorm(float* __restrict__ x, const float* __restrict__ x_part,
+                                                         int n_part, int rows, const T* __restrict__ g, int d,
+                                                         float eps, void* __restrict__ out,
+                                                         void* __restrict__ out_lo) {
+  // each thread keeps up to V4 groups of four elements in registers: one
+  // pass over x, all loads issued before the reduction.  Pending k-split
+  // partial sums of the projection that last wrote x ([n_part][rows][d]) are
+  // added first, in split order, and x is written back.
+  __shared__ float red[ROW_THREADS / 64];
   const int r = blockIdx.x;
-  const float* xr = x + (int64_t)r * d;
+  float* xr = x + (int64_t)r * d;
+  const int n4 = d / 4;
+  f32x4 v[V4];
   float ss = 0.f;
-  for (int i = threadIdx.x; i < d; i += blockDim.x) ss += xr[i] * xr[i];
+#pragma unroll
+  for (int j = 0; j < V4; ++j) {
+    const int i4 = threadIdx.x + j * ROW_THREADS;
+    v[j] = i4 < n4 ? *(const f32x4*)(xr + 4 * i4) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  if (n_part > 0) {
+    for (int sp = 0; sp < n_part; ++sp) {
+      const float* pr = x_part + ((int64_t)sp * rows + r) * d;
+#pragma unroll
+      for (int j = 0; j < V4; ++j) {
+        const int i4 = threadIdx.x + j * ROW_THREADS;
+        if (i4 < n4) v[j] += *(const f32x4*)(pr + 4 * i4);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < V4; ++j) {
+      const int i4 = threadIdx.x + j * ROW_THREADS;
+      if (i4 < n4) *(f32x4*)(xr + 4 * i4) = v[j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < V4; ++j) ss += v[j][0] * v[j][0] + v[j][1] * v[j][1] + v[j][2] * v[j][2] + v[j][3] * v[j][3];
   ss = block_sum(ss, red);
   const float rs = 1.0f / sqrtf(ss / (float)d + eps);
-  for (int i = threadIdx.x; i < d; i += blockDim.x) {
-    const float v = xr[i] * rs * to_f<T>(g[i]);
+#pragma unroll
+  for (int j = 0; j < V4; ++j) {
+    const int i4 = threadIdx.x + j * ROW_THREADS;
+    if (i4 >= n4) continue;
+    const int i = 4 * i4;
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = v[j][e] * rs * to_f<T>(g[i + e]);
     if (SPLIT) {
-      bf16_t hi, lo;
-      split_bf16(v, hi, lo);
-      ((bf16_t*)out)[(int64_t)r * d + i] = hi;
-      ((bf16_t*)out_lo)[(int64_t)r * d + i] = lo;
+      bf16_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) split_bf16(y[e], hi[e], lo[e]);
+      *(u32x2*)((bf16_t*)out + (int64_t)r * d + i) = u32x2{hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16)};
+      *(u32x2*)((bf16_t*)out_lo + (int64_t)r * d + i) =
+          u32x2{lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16)};
     } else {
-      ((float*)out)[(int64_t)r * d + i] = v;
+      *(f32x4*)((float*)out + (int64_t)r * d + i) = f32x4{y[0], y[1], y[2], y[3]};
     }
   }
 }
 
-hipError_t launch_rmsnorm(int dtype, const float* x, const void* gain, int rows, int d, float eps,
-                          void* out, void* out_lo, hipStream_t s) {
-  if (dtype == CAD_BF16)
-    hipLaunchKernelGGL((k_rmsnorm<bf16_t, true>), dim3(rows), dim3(ROW_THREADS), 0, s, x,
-                       (const bf16_t*)gain, d, eps, out, out_lo);
-  else
-    hipLaunchKernelGGL((k_rmsnorm<float, false>), dim3(rows), dim3(ROW_THREADS), 0, s, x,
-                       (const float*)gain, d, eps, out, out_lo);
-  return hipGetLastError();
+hipError_t launch_rmsnorm(int dtype, float* x, const float* x_part, int n_part, const void* gain, int rows, int d,
+                          float eps, void* out, void* out_lo, hipStream_t s) {
+  const int v4 = (d / 4 + ROW_THREADS - 1) / ROW_THREADS;
+  if (d % 4 != 0 || v4 > 8 || (n_part > 0 && !x_part)) return hipErrorInvalidValue;
+#define CAD_RMS(V)                                                                                         \
+  if (v4 <= V) {                                                                                           \
+    if (dtype == CAD_BF16)                                                                                 \
+      hipLaunchKernelGGL((k_rmsnorm<bf16_t, true, V>), dim3(rows), dim3(ROW_THREADS), 0, s, x, x_part,     \
+                         n_part, rows, (const bf16_t*)gain, d, eps, out, out_lo);                          \
+    else                                                                                                   \
+      hipLaunchKernelGGL((k_rmsnorm<float, false, V>), dim3(rows), dim3(ROW_THREADS), 0, s, x, x_part,     \
+                         n_part, rows, (const float*)gain, d, eps, out, out_lo);                           \
+    return hipGetLastError();                                                                              \
+  }
+  CAD_RMS(1) CAD_RMS(2) CAD_RMS(4) CAD_RMS(8)
+#undef CAD_RMS
+  return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------------------
@@ -92,8 +137,11 @@ hipError_t launch_rmsnorm(int dtype, const float* x, const void* gain, int rows,
 // and v at half precision in the span workspace (kv.span_k / kv.span_v),
 // which attention reads for this call's own keys.
 // ---------------------------------------------------------------------------
+constexpr int ROPE_MAX_HALF = 128;  // head_dim up to 256
+
 template <typename T, typename TQ>
-__global__ void k_rope_append(const float* __restrict__ qkv, int hq, int hkv, int hd,
+__global__ void k_rope_append(const float* __restrict__ qkv, const float* __restrict__ qkv_part, int n_part,
+                              int rows, int hq, int hkv, int hd,
                               const double* __restrict__ freq, RowMap rm, KVView kv,
                               const int32_t* write_limit, TQ* __restrict__ q_out, int32_t* status) {
   const int r = blockIdx.x;
@@ -103,6 +151,14 @@ __global__ void k_rope_append(const float* __restrict__ qkv, int hq, int hkv, in
   const int half = hd / 2;
   const int width = (hq + 2 * hkv) * hd;
   const float* src = qkv + (int64_t)r * width;
+  // projection output element i of this row: the stored value, or the sum
+  // of the k-split partials [n_part][rows][width] in split order
+  auto ld = [&](int i) {
+    if (n_part == 0) return src[i];
+    float v = qkv_part[(int64_t)r * width + i];
+    for (int sp = 1; sp < n_part; ++sp) v += qkv_part[((int64_t)sp * rows + r) * width + i];
+    return v;
+  };
   bool write_kv = write_limit == nullptr || local < *write_limit;
   int64_t blk = 0;
   if (write_kv) {
@@ -117,14 +173,20 @@ __global__ void k_rope_append(const float* __restrict__ qkv, int hq, int hkv, in
   T* vc = (T*)kv.v;
   const int64_t wrow = rm.pstart[b] + local;  // span workspace row
   f16_t* sk = kv.span_k ? kv.span_k + wrow * hkv * hd : nullptr;
+  // the row's rotation, one (cos, sin) per pair, in LDS
+  __shared__ float2 rot[ROPE_MAX_HALF];
+  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+    double sn, cs;
+    sincos((double)pos * freq[i], &sn, &cs);
+    rot[i] = float2{(float)cs, (float)sn};
+  }
+  __syncthreads();
   // rotations: q heads then k heads, one (head, pair) per item
   const int n_rot = (hq + hkv) * half;
   for (int it = threadIdx.x; it < n_rot; it += blockDim.x) {
     const int h = it / half, i = it % half;
-    double sn, cs;
-    sincos((double)pos * freq[i], &sn, &cs);
-    const float c = (float)cs, s = (float)sn;
-    const float a = src[h * hd + i], bb = src[h * hd + i + half];
+    const float c = rot[i].x, s = rot[i].y;
+    const float a = ld(h * hd + i), bb = ld(h * hd + i + half);
     const float ra = a * c - bb * s, rb = a * s + bb * c;
     if (h < hq) {
       TQ* qo = q_out + ((int64_t)r * hq + h) * hd;
@@ -143,24 +205,24 @@ __global__ void k_rope_append(const float* __restrict__ qkv, int hq, int hkv, in
       }
     }
   }
-  const float* vs = src + (hq + hkv) * hd;
   for (int it = threadIdx.x; it < hkv * hd; it += blockDim.x) {
     const int g = it / hd, dd = it % hd;
-    if (write_kv) vc[((blk * hkv + g) * hd + dd) * CAD_KV_BLOCK + slot] = from_f<T>(vs[it]);
-    if (kv.span_v) kv.span_v[((int64_t)g * hd + dd) * kv.span_cap + wrow] = f2h(vs[it]);
+    const float vv = ld((hq + hkv) * hd + it);
+    if (write_kv) vc[((blk * hkv + g) * hd + dd) * CAD_KV_BLOCK + slot] = from_f<T>(vv);
+    if (kv.span_v) kv.span_v[((int64_t)g * hd + dd) * kv.span_cap + wrow] = f2h(vv);
   }
 }
 
-hipError_t launch_rope_append(int dtype, const float* qkv, int rows, int hq, int hkv, int hd,
-                              const double* freq, const RowMap& rm, KVView kv,
-                              const int32_t* write_limit, void* q_out, int32_t* status,
-                              hipStream_t s) {
+hipError_t launch_rope_append(int dtype, const float* qkv, const float* qkv_part, int n_part, int rows, int hq,
+                              int hkv, int hd, const double* freq, const RowMap& rm, KVView kv,
+                              const int32_t* write_limit, void* q_out, int32_t* status, hipStream_t s) {
+  if (hd / 2 > ROPE_MAX_HALF || (n_part > 0 && !qkv_part)) return hipErrorInvalidValue;
   if (dtype == CAD_BF16)
-    hipLaunchKernelGGL((k_rope_append<bf16_t, f16_t>), dim3(rows), dim3(ROW_THREADS), 0, s, qkv, hq, hkv,
-                       hd, freq, rm, kv, write_limit, (f16_t*)q_out, status);
+    hipLaunchKernelGGL((k_rope_append<bf16_t, f16_t>), dim3(rows), dim3(ROW_THREADS), 0, s, qkv, qkv_part, n_part,
+                       rows, hq, hkv, hd, freq, rm, kv, write_limit, (f16_t*)q_out, status);
   else
-    hipLaunchKernelGGL((k_rope_append<float, float>), dim3(rows), dim3(ROW_THREADS), 0, s, qkv, hq, hkv,
-                       hd, freq, rm, kv, write_limit, (float*)q_out, status);
+    hipLaunchKernelGGL((k_rope_append<float, float>), dim3(rows), dim3(ROW_THREADS), 0, s, qkv, qkv_part, n_part,
+                       rows, hq, hkv, hd, freq, rm, kv, write_limit, (float*)q_out, status);
   return hipGetLastError();
 }
 
