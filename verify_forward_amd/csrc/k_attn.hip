@@ -6,12 +6,13 @@
 //
 // bf16 models (matrix cores, half operands: q arrives as half, K and V are
 // widened from the bf16 cache to half while staged in LDS, P is rounded to
-// half).  One work-group = one KV head x 128 query rows (query row = span row
-// * G + head-in-group, so the G query heads that share a KV head share every
-// K/V tile) x one partition of the key axis.  Keys are processed 64 at a
+// half).  One work-group = one KV head x 256 query rows (128 for calls with
+// at most 128 query rows; query row = span row * G + head-in-group, so the G
+// query heads that share a KV head share every K/V tile) x one partition of
+// the key axis.  Keys are processed 64 at a
 // time through a double-buffered LDS stage: the K tile [64][hd] and the V
 // tile, stored token-minor in the cache ([hd][16] per block) and kept
-// transposed in LDS, are loaded once per work-group and read by all four
+// transposed in LDS, are loaded once per work-group and read by all its
 // waves; the global loads of tile t+1 are in flight while tile t is on the
 // matrix cores.  Each wave owns 32 query rows (two 16-column blocks) and
 // computes
@@ -35,7 +36,7 @@ struct AttnArgs {
   int rows, hq, hkv, G;
   RowMap rm;
   KVView kv;
-  int32_t tstart[CAD_MAX_SEQS + 1];  // FA_QT-row query tiles per sequence (CSR)
+  int32_t tstart[CAD_MAX_SEQS + 1];  // query tiles per sequence (CSR)
   int n_parts, part_len;
   float* part_o;   // [n_parts][rows * hq][hd]
   float* part_ml;  // [n_parts][rows * hq][2]
@@ -47,9 +48,10 @@ struct AttnArgs {
 
 constexpr int FA_KT = 64;                  // keys per tile
 constexpr int FA_QPW = 32;                 // query rows per wave
-constexpr int FA_WAVES = 8;
-constexpr int FA_QT = FA_QPW * FA_WAVES;   // query rows per work-group
-constexpr int FA_NT = 64 * FA_WAVES;       // threads per work-group
+// Work-group shape: eight waves (256 query rows) for long spans, four waves
+// (128 query rows, twice the work-groups over the key axis) when a call has
+// at most 128 query rows, where the cache stream has to be spread wider.
+inline int attn_waves(int query_rows) { return query_rows <= 128 ? 4 : 8; }
 
 // Work-group -> (query tile, KV head, key partition).  The query tiles that
 // read the same KV head and key range are placed on one XCD (work-group ids
@@ -75,9 +77,11 @@ __device__ __forceinline__ void attn_tile_of(int& x, int& y, int& z) {
 // weights stay below 2^FA_LAZY, far inside half's range.
 constexpr float FA_LAZY = 8.0f;
 
-template <int HD>
-__global__ void __launch_bounds__(FA_NT)
+template <int HD, int NW>
+__global__ void __launch_bounds__(64 * NW, 8 / NW)
 k_attn_bf16(AttnArgs p) {
+  constexpr int FA_NT = 64 * NW;            // threads per work-group
+  constexpr int FA_QT = FA_QPW * NW;        // query rows per work-group
   constexpr int KLD = HD + 8;          // sK row stride (halves): 16 B pad keeps 16-row reads conflict-free
   constexpr int VLD = FA_KT + 8;       // sV row stride (halves)
   constexpr int DS = HD / 32;          // k steps of S^T = K Q^T
@@ -462,15 +466,18 @@ k_attn_f32(AttnArgs p, int hd) {
 
 int attention_parts(int rows, int hq, int hkv, int64_t max_cache_keys, int* part_len) {
   // partitions of the cached keys: about one work-group per compute unit
-  // (256 CUs) together with the query tiles, at least 256 keys each
+  // (256 CUs; two for the four-wave shape) together with the query tiles,
+  // at least 256 keys each
   const int G = hq / hkv;
-  const int tiles = (rows * G + FA_QT - 1) / FA_QT;
+  const int nw = attn_waves(rows * G), qt = FA_QPW * nw;
+  const int tiles = (rows * G + qt - 1) / qt;
   const int base = hkv * tiles;
   if (max_cache_keys <= 0) {
     *part_len = FA_KT;
     return 0;
   }
-  int parts = (256 + base - 1) / base;
+  const int target = nw == 4 ? 512 : 256;
+  int parts = (target + base - 1) / base;
   const int64_t min_len = 256;
   const int64_t cap = (max_cache_keys + min_len - 1) / min_len;
   if (parts > cap) parts = (int)cap;
@@ -505,18 +512,23 @@ hipError_t launch_attention(int dtype, const void* q, int rows, int hq, int hkv,
     hipLaunchKernelGGL(k_attn_f32, dim3(rows, hq), dim3(64), 0, s, a, hd);
     return hipGetLastError();
   }
+  const int nw = attn_waves(rows * a.G), qt = FA_QPW * nw;
   int nt = 0;
   a.tstart[0] = 0;
   for (int b = 0; b < rm.n_seq; ++b) {
     const int R = (rm.start[b + 1] - rm.start[b]) * a.G;
-    nt += (R + FA_QT - 1) / FA_QT;
+    nt += (R + qt - 1) / qt;
     a.tstart[b + 1] = nt;
   }
   dim3 grid(nt, hkv, n_parts);
-  if (hd == 64)
-    hipLaunchKernelGGL(k_attn_bf16<64>, grid, dim3(FA_NT), 0, s, a);
+  if (hd == 64 && nw == 4)
+    hipLaunchKernelGGL((k_attn_bf16<64, 4>), grid, dim3(256), 0, s, a);
+  else if (hd == 64)
+    hipLaunchKernelGGL((k_attn_bf16<64, 8>), grid, dim3(512), 0, s, a);
+  else if (nw == 4)
+    hipLaunchKernelGGL((k_attn_bf16<128, 4>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(k_attn_bf16<128>, grid, dim3(FA_NT), 0, s, a);
+    hipLaunchKernelGGL((k_attn_bf16<128, 8>), grid, dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -150,15 +150,29 @@ __global__ void k_rope_append(const float* __restrict__ qkv, const float* __rest
   const int64_t pos = rm.L[b] + local;
   const int half = hd / 2;
   const int width = (hq + 2 * hkv) * hd;
-  const float* src = qkv + (int64_t)r * width;
-  // projection output element i of this row: the stored value, or the sum
-  // of the k-split partials [n_part][rows][width] in split order
-  auto ld = [&](int i) {
-    if (n_part == 0) return src[i];
-    float v = qkv_part[(int64_t)r * width + i];
-    for (int sp = 1; sp < n_part; ++sp) v += qkv_part[((int64_t)sp * rows + r) * width + i];
-    return v;
-  };
+  // the row's projection output, staged in LDS: the stored values, or the
+  // sum of the k-split partials [n_part][rows][width] in split order
+  extern __shared__ float srow[];
+  {
+    const float* src = qkv + (int64_t)r * width;
+    const int n4 = width / 4;
+    for (int i4 = threadIdx.x; i4 < n4; i4 += blockDim.x) {
+      f32x4 v;
+      if (n_part == 0) {
+        v = *(const f32x4*)(src + 4 * i4);
+      } else {
+        v = *(const f32x4*)(qkv_part + (int64_t)r * width + 4 * i4);
+        for (int sp = 1; sp < n_part; ++sp) v += *(const f32x4*)(qkv_part + ((int64_t)sp * rows + r) * width + 4 * i4);
+      }
+      *(f32x4*)(srow + 4 * i4) = v;
+    }
+    for (int i = 4 * n4 + threadIdx.x; i < width; i += blockDim.x) {
+      float v = n_part == 0 ? src[i] : qkv_part[(int64_t)r * width + i];
+      for (int sp = 1; sp < n_part; ++sp) v += qkv_part[((int64_t)sp * rows + r) * width + i];
+      srow[i] = v;
+    }
+  }
+  auto ld = [&](int i) { return srow[i]; };
   bool write_kv = write_limit == nullptr || local < *write_limit;
   int64_t blk = 0;
   if (write_kv) {
@@ -216,12 +230,13 @@ __global__ void k_rope_append(const float* __restrict__ qkv, const float* __rest
 hipError_t launch_rope_append(int dtype, const float* qkv, const float* qkv_part, int n_part, int rows, int hq,
                               int hkv, int hd, const double* freq, const RowMap& rm, KVView kv,
                               const int32_t* write_limit, void* q_out, int32_t* status, hipStream_t s) {
-  if (hd / 2 > ROPE_MAX_HALF || (n_part > 0 && !qkv_part)) return hipErrorInvalidValue;
+  const size_t lds = (size_t)(hq + 2 * hkv) * hd * sizeof(float);
+  if (hd / 2 > ROPE_MAX_HALF || (n_part > 0 && !qkv_part) || lds > 65536) return hipErrorInvalidValue;
   if (dtype == CAD_BF16)
-    hipLaunchKernelGGL((k_rope_append<bf16_t, f16_t>), dim3(rows), dim3(ROW_THREADS), 0, s, qkv, qkv_part, n_part,
+    hipLaunchKernelGGL((k_rope_append<bf16_t, f16_t>), dim3(rows), dim3(ROW_THREADS), lds, s, qkv, qkv_part, n_part,
                        rows, hq, hkv, hd, freq, rm, kv, write_limit, (f16_t*)q_out, status);
   else
-    hipLaunchKernelGGL((k_rope_append<float, float>), dim3(rows), dim3(ROW_THREADS), 0, s, qkv, qkv_part, n_part,
+    hipLaunchKernelGGL((k_rope_append<float, float>), dim3(rows), dim3(ROW_THREADS), lds, s, qkv, qkv_part, n_part,
                        rows, hq, hkv, hd, freq, rm, kv, write_limit, (float*)q_out, status);
   return hipGetLastError();
 }
