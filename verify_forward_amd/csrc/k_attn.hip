@@ -367,47 +367,59 @@ k_attn_bf16(AttnArgs p) {
 // log-sum-exp merge of the partitions (base-2 exponent, as produced above),
 // written as bf16 hi / lo planes.  One work-group per (row, head): the
 // partition weights 2^(m_p - m) (0 for a partition that saw no key) are
-// formed once in LDS, then every thread sums its output dimension over the
-// partitions in order.
+// formed once in LDS; with many partitions four thread groups each sum one
+// quarter of them (eight loads in flight per thread) for the output
+// dimension they own, and the quarters are added in order.
 constexpr int MERGE_MAX_PARTS = 512;
-__global__ void __launch_bounds__(128) k_attn_merge(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                                                    int n_parts, int64_t nq, int hd, bf16_t* __restrict__ out,
-                                                    bf16_t* __restrict__ out_lo) {
-  __shared__ float sw[MERGE_MAX_PARTS];
-  __shared__ float red[2];
+constexpr int MERGE_GROUPS = 4;
+__global__ void __launch_bounds__(128 * MERGE_GROUPS) k_attn_merge(const float* __restrict__ part_o,
+                                                                   const float* __restrict__ part_ml, int n_parts,
+                                                                   int64_t nq, int hd, bf16_t* __restrict__ out,
+                                                                   bf16_t* __restrict__ out_lo) {
+  __shared__ float sw[MERGE_MAX_PARTS], sl[MERGE_MAX_PARTS];
+  __shared__ float red[MERGE_GROUPS * 2];
+  __shared__ float snum[MERGE_GROUPS][128];
   const int64_t qi = blockIdx.x;
-  const int t = threadIdx.x;
-  // maximum over partitions with a positive sum (fixed-order tree within the block)
+  const int t = threadIdx.x, nt = blockDim.x;
+  // maximum over partitions with a positive sum
   float mloc = -INFINITY;
-  for (int pp = t; pp < n_parts; pp += blockDim.x) {
+  for (int pp = t; pp < n_parts; pp += nt) {
     const float2 ml = *(const float2*)(part_ml + ((int64_t)pp * nq + qi) * 2);
     sw[pp] = ml.y > 0.f ? ml.x : -INFINITY;
+    sl[pp] = ml.y;
     mloc = fmaxf(mloc, sw[pp]);
   }
   for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
   if ((t & 63) == 0) red[t >> 6] = mloc;
   __syncthreads();
-  const float m = fmaxf(red[0], blockDim.x > 64 ? red[1] : -INFINITY);
-  for (int pp = t; pp < n_parts; pp += blockDim.x) sw[pp] = sw[pp] == -INFINITY ? 0.f : exp2f(sw[pp] - m);
+  float m = red[0];
+  for (int w = 1; w < nt / 64; ++w) m = fmaxf(m, red[w]);
+  for (int pp = t; pp < n_parts; pp += nt) sw[pp] = sw[pp] == -INFINITY ? 0.f : exp2f(sw[pp] - m);
   __syncthreads();
   // denominator: sum of w_p * l_p in partition order (every thread the same)
   float den = 0.f;
-  for (int pp = 0; pp < n_parts; ++pp) den += sw[pp] * part_ml[((int64_t)pp * nq + qi) * 2 + 1];
-  for (int d = t; d < hd; d += blockDim.x) {
+  for (int pp = 0; pp < n_parts; ++pp) den += sw[pp] * sl[pp];
+  const int ng = nt / 128, grp = t / 128, d = t % 128;
+  const int q0 = n_parts * grp / ng, q1 = n_parts * (grp + 1) / ng;
+  float num = 0.f;
+  if (d < hd) {
     const float* po = part_o + qi * hd + d;
     const int64_t stride = nq * hd;
-    float num = 0.f;
-    int pp = 0;
-    for (; pp + 4 <= n_parts; pp += 4) {
-      const float o0 = po[(pp + 0) * stride], o1 = po[(pp + 1) * stride];
-      const float o2 = po[(pp + 2) * stride], o3 = po[(pp + 3) * stride];
-      num += sw[pp] * o0;
-      num += sw[pp + 1] * o1;
-      num += sw[pp + 2] * o2;
-      num += sw[pp + 3] * o3;
+    for (int pp = q0; pp < q1; pp += 8) {
+      float ov[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) ov[u] = po[(int64_t)min(pp + u, q1 - 1) * stride];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (pp + u < q1) num += sw[pp + u] * ov[u];
     }
-    for (; pp < n_parts; ++pp) num += sw[pp] * po[pp * stride];
-    split_bf16(den > 0.f ? num / den : 0.f, out[qi * hd + d], out_lo[qi * hd + d]);
+    snum[grp][d] = num;
+  }
+  __syncthreads();
+  if (grp == 0 && d < hd) {
+    float tot = snum[0][d];
+    for (int g2 = 1; g2 < ng; ++g2) tot += snum[g2][d];
+    split_bf16(den > 0.f ? tot / den : 0.f, out[qi * hd + d], out_lo[qi * hd + d]);
   }
 }
 
@@ -536,7 +548,8 @@ hipError_t launch_attention_merge(const float* part_o, const float* part_ml, int
                                   int hq, int hd, void* out, void* out_lo, hipStream_t s) {
   const int64_t nq = (int64_t)rows * hq;
   if (n_parts > MERGE_MAX_PARTS || hd > 128) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_attn_merge, dim3((unsigned)nq), dim3(128), 0, s, part_o, part_ml, n_parts, nq, hd,
+  const int groups = n_parts >= 16 ? MERGE_GROUPS : 1;
+  hipLaunchKernelGGL(k_attn_merge, dim3((unsigned)nq), dim3(128 * groups), 0, s, part_o, part_ml, n_parts, nq, hd,
                      (bf16_t*)out, (bf16_t*)out_lo);
   return hipGetLastError();
 }

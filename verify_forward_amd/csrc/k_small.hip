@@ -71,13 +71,24 @@ __global__ void __launch_bounds__(ROW_THREADS) k_rmsnorm(float* __restrict__ x, 
     v[j] = i4 < n4 ? *(const f32x4*)(xr + 4 * i4) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   if (n_part > 0) {
-    for (int sp = 0; sp < n_part; ++sp) {
-      const float* pr = x_part + ((int64_t)sp * rows + r) * d;
+    // four partial planes per batch, all their loads in flight together
+    // (indices clamped; a clamped plane is multiplied by zero)
+    for (int sp = 0; sp < n_part; sp += 4) {
+      f32x4 t[4][V4];
 #pragma unroll
-      for (int j = 0; j < V4; ++j) {
-        const int i4 = threadIdx.x + j * ROW_THREADS;
-        if (i4 < n4) v[j] += *(const f32x4*)(pr + 4 * i4);
+      for (int u = 0; u < 4; ++u) {
+        const float* pr = x_part + ((int64_t)min(sp + u, n_part - 1) * rows + r) * d;
+#pragma unroll
+        for (int j = 0; j < V4; ++j) {
+          const int i4 = min(threadIdx.x + j * ROW_THREADS, n4 - 1);
+          t[u][j] = *(const f32x4*)(pr + 4 * i4);
+        }
       }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (sp + u < n_part)
+#pragma unroll
+          for (int j = 0; j < V4; ++j) v[j] += t[u][j];
     }
 #pragma unroll
     for (int j = 0; j < V4; ++j) {
@@ -161,8 +172,18 @@ __global__ void k_rope_append(const float* __restrict__ qkv, const float* __rest
       if (n_part == 0) {
         v = *(const f32x4*)(src + 4 * i4);
       } else {
-        v = *(const f32x4*)(qkv_part + (int64_t)r * width + 4 * i4);
-        for (int sp = 1; sp < n_part; ++sp) v += *(const f32x4*)(qkv_part + ((int64_t)sp * rows + r) * width + 4 * i4);
+        // eight partial planes per batch, loads in flight together (indices
+        // clamped, the clamped repeats are not added)
+        v = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < n_part; sp += 8) {
+          f32x4 t[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            t[u] = *(const f32x4*)(qkv_part + ((int64_t)min(sp + u, n_part - 1) * rows + r) * width + 4 * i4);
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (sp + u < n_part) v = (sp + u == 0) ? t[u] : v + t[u];
+        }
       }
       *(f32x4*)(srow + 4 * i4) = v;
     }
