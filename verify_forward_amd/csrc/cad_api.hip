@@ -155,7 +155,7 @@ int64_t max_parts_rows(const cad_config& c) {
   int64_t best = 0;
   for (int r = 1; r <= c.max_tokens; ++r) {
     int len = 0;
-    const int p = attention_parts(r, c.n_q_heads, c.n_kv_heads, (int64_t)1 << 40, &len) + 1;
+    const int p = attention_parts(r, c.n_q_heads, c.n_kv_heads, c.head_dim, (int64_t)1 << 40, &len) + 1;
     if ((int64_t)p * r > best) best = (int64_t)p * r;
   }
   return best;
@@ -190,6 +190,12 @@ void* lo_plane(const cad_model* m, void* buf, int64_t n) {
   return m->cfg.dtype == CAD_BF16 ? (void*)((bf16_t*)buf + (int64_t)m->cfg.max_tokens * n) : nullptr;
 }
 
+// half remainder plane of q (bf16 models): after the T x hq x hd hi plane
+void* q_lo_plane(const cad_model* m) {
+  const cad_config& c = m->cfg;
+  return c.dtype == CAD_BF16 ? (void*)((f16_t*)m->q + (int64_t)c.max_tokens * c.n_q_heads * c.head_dim) : nullptr;
+}
+
 // Run cache indices [c0, c1) over the rows already embedded in m->x.
 cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, int c1,
                       const int32_t* write_limit, int32_t* dev_status, hipStream_t s) {
@@ -200,7 +206,7 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
   int64_t max_L = 0;
   for (int b = 0; b < rm.n_seq; ++b) max_L = rm.L[b] > max_L ? rm.L[b] : max_L;
   int part_len = 0;
-  const int n_parts = attention_parts(R, hq, hkv, max_L, &part_len) + 1;  // + the span partition
+  const int n_parts = attention_parts(R, hq, hkv, hd, max_L, &part_len) + 1;  // + the span partition
   if ((int64_t)n_parts * R > m->part_cap)
     return fail(CAD_E_CAPACITY, "attention partitions %d x %d rows exceed the workspace", n_parts, R);
   if (c.dtype == CAD_BF16 && rm.pstart[rm.n_seq] > m->span_cap)
@@ -218,8 +224,8 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
     int qkv_parts = 0;
     LAUNCH(PF_QKV, launch_gemm(c.dtype, GEMM_QKV, g, s, &qkv_parts));
     LAUNCH(PF_ROPE, launch_rope_append(c.dtype, m->qkv, m->split_ws, qkv_parts, R, hq, hkv, hd, m->freq, rm, v,
-                                       write_limit, m->q, dev_status, s));
-    LAUNCH(PF_ATTN, launch_attention(c.dtype, m->q, R, hq, hkv, hd, rm, v, n_parts, part_len, m->part_o,
+                                       write_limit, m->q, q_lo_plane(m), dev_status, s));
+    LAUNCH(PF_ATTN, launch_attention(c.dtype, m->q, q_lo_plane(m), R, hq, hkv, hd, rm, v, n_parts, part_len, m->part_o,
                                      m->part_ml, m->attn, lo_plane(m, m->attn, (int64_t)hq * hd), dev_status, s));
     if (c.dtype == CAD_BF16 && n_parts > 1)
       LAUNCH(PF_MERGE, launch_attention_merge(m->part_o, m->part_ml, n_parts, R, hq, hd, m->attn,
@@ -329,7 +335,7 @@ cad_status cad_model_create(const cad_config* cfg, const cad_weights* w, cad_mod
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
   const size_t o_x = take(T * d * 4), o_hn = take(T * d * 4), o_qkv = take(T * (hq + 2 * hkv) * hd * 4),
-               o_q = take(T * hq * hd * es), o_attn = take(T * hq * hd * 4), o_act = take(T * F * 4),
+               o_q = take(T * hq * hd * es * (c.dtype == CAD_BF16 ? 2 : 1)), o_attn = take(T * hq * hd * 4), o_act = take(T * F * 4),
                o_logits = take(T * V * 4), o_po = take(pr * hq * hd * 4), o_pml = take(pr * hq * 2 * 4),
                o_freq = take(hd / 2 * 8), o_si = take(T * 4), o_sv = take(4);
   const bool split = c.dtype == CAD_BF16;

@@ -152,9 +152,11 @@ hipError_t launch_gemm(int dtype, int role, const GemmArgs& a, hipStream_t s, in
 // qkv_part [n_part][rows][width]
 hipError_t launch_rope_append(int dtype, const float* qkv, const float* qkv_part, int n_part, int rows, int hq,
                               int hkv, int hd, const double* freq, const RowMap& rm, KVView kv,
-                              const int32_t* write_limit, void* q_out, int32_t* status, hipStream_t s);
+                              const int32_t* write_limit, void* q_out, void* q_lo, int32_t* status,
+                              hipStream_t s);
 // n_parts = cache partitions (keys < L, part_len each) + one span partition
-hipError_t launch_attention(int dtype, const void* q, int rows, int hq, int hkv, int hd,
+// q_lo: bf16 models, the half remainder plane of q (nullptr for fp32)
+hipError_t launch_attention(int dtype, const void* q, const void* q_lo, int rows, int hq, int hkv, int hd,
                             const RowMap& rm, KVView kv, int n_parts, int part_len,
                             float* part_o, float* part_ml, void* out, void* out_lo, int32_t* status,
                             hipStream_t s);
@@ -174,6 +176,6 @@ hipError_t launch_suffix_match(const int32_t* tokens, int64_t T, int max_n, int 
 
 // attention split: partitions of the cached keys (0 .. max L) so that small
 // spans still fill the chip; the span's own keys form one more partition
-int attention_parts(int rows, int hq, int hkv, int64_t max_cache_keys, int* part_len);
+int attention_parts(int rows, int hq, int hkv, int hd, int64_t max_cache_keys, int* part_len);
 
 }  // namespace cad

@@ -32,7 +32,8 @@
 namespace cad {
 
 struct AttnArgs {
-  const void* q;   // [rows][hq][hd]
+  const void* q;     // [rows][hq][hd]: fp32 (fp32 models) or the half hi plane
+  const void* q_lo;  // bf16 models: the half remainder plane
   int rows, hq, hkv, G;
   RowMap rm;
   KVView kv;
@@ -47,11 +48,13 @@ struct AttnArgs {
 };
 
 constexpr int FA_KT = 64;                  // keys per tile
-constexpr int FA_QPW = 32;                 // query rows per wave
-// Work-group shape: eight waves (256 query rows) for long spans, four waves
-// (128 query rows, twice the work-groups over the key axis) when a call has
-// at most 128 query rows, where the cache stream has to be spread wider.
-inline int attn_waves(int query_rows) { return query_rows <= 128 ? 4 : 8; }
+// Work-group shapes: eight waves of 32 query rows (two waves per SIMD) for
+// long spans; four waves of 16 rows (several work-groups per CU, twice the
+// work-groups over the key axis to spread the cache stream wider) when a
+// call has at most 64 query rows.  (One wave per SIMD with 48 or 64 rows
+// each, which reads each K/V fragment from LDS once for more queries,
+// measured 2.6x slower: nothing hides LDS and softmax latency then.)
+inline int attn_qt(int query_rows, int hd) { return query_rows <= 64 ? 64 : 256; }
 
 // Work-group -> (query tile, KV head, key partition).  The query tiles that
 // read the same KV head and key range are placed on one XCD (work-group ids
@@ -77,11 +80,12 @@ __device__ __forceinline__ void attn_tile_of(int& x, int& y, int& z) {
 // weights stay below 2^FA_LAZY, far inside half's range.
 constexpr float FA_LAZY = 8.0f;
 
-template <int HD, int NW>
+template <int HD, int NW, int QB>
 __global__ void __launch_bounds__(64 * NW, 8 / NW)
 k_attn_bf16(AttnArgs p) {
   constexpr int FA_NT = 64 * NW;            // threads per work-group
-  constexpr int FA_QT = FA_QPW * NW;        // query rows per work-group
+  constexpr int QPW = 16 * QB;              // query rows per wave (QB 16-column blocks)
+  constexpr int FA_QT = QPW * NW;           // query rows per work-group
   constexpr int KLD = HD + 8;          // sK row stride (halves): 16 B pad keeps 16-row reads conflict-free
   constexpr int VLD = FA_KT + 8;       // sV row stride (halves)
   constexpr int DS = HD / 32;          // k steps of S^T = K Q^T
@@ -106,7 +110,7 @@ k_attn_bf16(AttnArgs p) {
   const int R = n_rows * p.G;
   const int64_t L = p.rm.L[b];
   const int q_first = tile * FA_QT;
-  const int q_wave = q_first + wave * FA_QPW;
+  const int q_wave = q_first + wave * QPW;
   const bool wave_active = q_wave < R;
   // keys of this work-group: [k_begin, k_end).  Partitions 0 .. n_parts - 2
   // cover the cached keys 0 .. L - 1 (part_len each, a multiple of FA_KT) and
@@ -120,12 +124,19 @@ k_attn_bf16(AttnArgs p) {
   // causal limit shared by every query of the wave (its first query's)
   const int64_t wave_min_last = L + q_wave / p.G;
 
-  // this lane's two query columns
-  bool q_ok[2];
-  int64_t q_last_key[2], qrow[2];
-  u32x4 qf[2][DS];
+  // this lane's query columns.  q arrives as two half planes (hi, and the
+  // half-rounded remainder lo); S^T takes two products per K fragment, so q
+  // enters the scores with ~22 significant bits.  The hi fragments stay in
+  // registers; the lo fragments too with one query block per wave, and in
+  // LDS (read only by this wave) with two.
+  constexpr bool QLO_LDS = QB >= 2;
+  constexpr int QLD = HD + 8;  // sQlo row stride (halves): conflict-free 16-row reads
+  __shared__ __attribute__((aligned(16))) f16_t sQlo[QLO_LDS ? NW * QPW * QLD : 8];
+  bool q_ok[QB];
+  int64_t q_last_key[QB], qrow[QB];
+  u32x4 qf[QB][DS], qfl[QLO_LDS ? 1 : QB][DS];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const int qi = q_wave + qb * 16 + i16;
     q_ok[qb] = qi < R;
     const int k_local = q_ok[qb] ? qi / p.G : 0;
@@ -133,15 +144,27 @@ k_attn_bf16(AttnArgs p) {
     q_last_key[qb] = L + k_local;
     qrow[qb] = (int64_t)(p.rm.start[b] + k_local) * p.hq + head;  // index of (row, head)
     const f16_t* qsrc = (const f16_t*)p.q + qrow[qb] * HD;
+    const f16_t* qlsrc = (const f16_t*)p.q_lo + qrow[qb] * HD;
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds)
-      qf[qb][ds] = q_ok[qb] ? *(const u32x4*)(qsrc + ds * 32 + g4 * 8) : u32x4{0u, 0u, 0u, 0u};
+    for (int ds = 0; ds < DS; ++ds) {
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      qf[qb][ds] = q_ok[qb] ? *(const u32x4*)(qsrc + ds * 32 + g4 * 8) : zero;
+      const u32x4 vl = q_ok[qb] ? *(const u32x4*)(qlsrc + ds * 32 + g4 * 8) : zero;
+      if (QLO_LDS)
+        *(u32x4*)(&sQlo[(wave * QPW + qb * 16 + i16) * QLD + ds * 32 + g4 * 8]) = vl;
+      else
+        qfl[QLO_LDS ? 0 : qb][ds] = vl;
+    }
   }
-  f32x4 o[DB][2];
+  f32x4 o[DB][QB];
 #pragma unroll
-  for (int d = 0; d < DB; ++d) o[d][0] = o[d][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) o[d][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   // finite start: exp2 of (masked score - m_run) is 0, never NaN
-  float m_run[2] = {-1e30f, -1e30f}, l_run[2] = {0.f, 0.f};
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) m_run[qb] = -1e30f, l_run[qb] = 0.f;
 
   const int32_t* table = p.kv.table + (int64_t)b * p.kv.max_blocks;
   const int n_tiles = k_begin < k_end ? (int)((k_end - k_begin + FA_KT - 1) / FA_KT) : 0;
@@ -244,24 +267,35 @@ k_attn_bf16(AttnArgs p) {
     const int64_t blk_next = block_of(t + 2);
     if (wave_active) {
       // ---- S^T = K Q^T for four 16-key blocks x two 16-query blocks ----
-      f32x4 s[4][2];
+      f32x4 s[4][QB];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) s[kb][0] = s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds)
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        u32x4 ql[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          ql[qb] = QLO_LDS ? *(const u32x4*)(&sQlo[(wave * QPW + qb * 16 + i16) * QLD + ds * 32 + g4 * 8])
+                           : qfl[QLO_LDS ? 0 : qb][ds];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           const u32x4 kf = *(const u32x4*)(&sK[buf][(kb * 16 + i16) * KLD + ds * 32 + g4 * 8]);
-          s[kb][0] = mfma16(kf, qf[0][ds], s[kb][0]);
-          s[kb][1] = mfma16(kf, qf[1][ds], s[kb][1]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            s[kb][qb] = mfma16(kf, qf[qb][ds], s[kb][qb]);
+            s[kb][qb] = mfma16(kf, ql[qb], s[kb][qb]);
+          }
         }
+      }
       // lane holds S[query (qb, i16)][key kt + 16 kb + 4 g4 + r]
       const int end_rel = (int)min<int64_t>(k_end - kt, FA_KT);
       const bool need_mask = kt + FA_KT - 1 > wave_min_last || end_rel < FA_KT;
-      float mx[2];
+      float mx[QB];
       bool grow = false;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < QB; ++qb) {
         if (need_mask) {
           const int lim = (int)max<int64_t>(min<int64_t>(q_last_key[qb] - kt + 1, end_rel), 0);
 #pragma unroll
@@ -281,7 +315,7 @@ k_attn_bf16(AttnArgs p) {
       }
       if (__ballot(grow)) {  // some query's maximum moved: rescale (wave-uniform branch)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
           const float m_new = fmaxf(m_run[qb], mx[qb]);
           const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
           m_run[qb] = m_new;
@@ -290,9 +324,9 @@ k_attn_bf16(AttnArgs p) {
           for (int d = 0; d < DB; ++d) o[d][qb] *= alpha;
         }
       }
-      u32x4 pf[2][2];
+      u32x4 pf[QB][2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < QB; ++qb) {
         const float nm = -m_run[qb];
         float psum = 0.f;
         uint32_t pk[8];
@@ -319,8 +353,8 @@ k_attn_bf16(AttnArgs p) {
 #pragma unroll
         for (int d = 0; d < DB; ++d) {
           const u32x4 vf = *(const u32x4*)(&sV[buf][(d * 16 + i16) * VLD + ks * 32 + g4 * 8]);
-          o[d][0] = mfma16(vf, pf[0][ks], o[d][0]);
-          o[d][1] = mfma16(vf, pf[1][ks], o[d][1]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) o[d][qb] = mfma16(vf, pf[qb][ks], o[d][qb]);
         }
     }
     if (more) sstore(buf ^ 1);
@@ -329,7 +363,7 @@ k_attn_bf16(AttnArgs p) {
   }
   if (!wave_active) return;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     // combine the four lanes of each query column
     float l = l_run[qb];
     l += __shfl_xor(l, 16);
@@ -476,19 +510,19 @@ k_attn_f32(AttnArgs p, int hd) {
   }
 }
 
-int attention_parts(int rows, int hq, int hkv, int64_t max_cache_keys, int* part_len) {
+int attention_parts(int rows, int hq, int hkv, int hd, int64_t max_cache_keys, int* part_len) {
   // partitions of the cached keys: about one work-group per compute unit
   // (256 CUs; two for the four-wave shape) together with the query tiles,
   // at least 256 keys each
   const int G = hq / hkv;
-  const int nw = attn_waves(rows * G), qt = FA_QPW * nw;
+  const int qt = attn_qt(rows * G, hd);
   const int tiles = (rows * G + qt - 1) / qt;
   const int base = hkv * tiles;
   if (max_cache_keys <= 0) {
     *part_len = FA_KT;
     return 0;
   }
-  const int target = nw == 4 ? 512 : 256;
+  const int target = qt == 64 ? 512 : 256;
   int parts = (target + base - 1) / base;
   const int64_t min_len = 256;
   const int64_t cap = (max_cache_keys + min_len - 1) / min_len;
@@ -500,12 +534,13 @@ int attention_parts(int rows, int hq, int hkv, int64_t max_cache_keys, int* part
   return (int)((max_cache_keys + len - 1) / len);
 }
 
-hipError_t launch_attention(int dtype, const void* q, int rows, int hq, int hkv, int hd,
+hipError_t launch_attention(int dtype, const void* q, const void* q_lo, int rows, int hq, int hkv, int hd,
                             const RowMap& rm, KVView kv, int n_parts, int part_len,
                             float* part_o, float* part_ml, void* out, void* out_lo, int32_t* status,
                             hipStream_t s) {
   AttnArgs a;
   a.q = q;
+  a.q_lo = q_lo;
   a.rows = rows;
   a.hq = hq;
   a.hkv = hkv;
@@ -524,7 +559,7 @@ hipError_t launch_attention(int dtype, const void* q, int rows, int hq, int hkv,
     hipLaunchKernelGGL(k_attn_f32, dim3(rows, hq), dim3(64), 0, s, a, hd);
     return hipGetLastError();
   }
-  const int nw = attn_waves(rows * a.G), qt = FA_QPW * nw;
+  const int qt = attn_qt(rows * a.G, hd);
   int nt = 0;
   a.tstart[0] = 0;
   for (int b = 0; b < rm.n_seq; ++b) {
@@ -533,14 +568,14 @@ hipError_t launch_attention(int dtype, const void* q, int rows, int hq, int hkv,
     a.tstart[b + 1] = nt;
   }
   dim3 grid(nt, hkv, n_parts);
-  if (hd == 64 && nw == 4)
-    hipLaunchKernelGGL((k_attn_bf16<64, 4>), grid, dim3(256), 0, s, a);
+  if (hd == 64 && qt == 64)
+    hipLaunchKernelGGL((k_attn_bf16<64, 4, 1>), grid, dim3(256), 0, s, a);
   else if (hd == 64)
-    hipLaunchKernelGGL((k_attn_bf16<64, 8>), grid, dim3(512), 0, s, a);
-  else if (nw == 4)
-    hipLaunchKernelGGL((k_attn_bf16<128, 4>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_attn_bf16<64, 8, 2>), grid, dim3(512), 0, s, a);
+  else if (qt == 64)
+    hipLaunchKernelGGL((k_attn_bf16<128, 4, 1>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((k_attn_bf16<128, 8>), grid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL((k_attn_bf16<128, 8, 2>), grid, dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -154,7 +154,8 @@ template <typename T, typename TQ>
 __global__ void k_rope_append(const float* __restrict__ qkv, const float* __restrict__ qkv_part, int n_part,
                               int rows, int hq, int hkv, int hd,
                               const double* __restrict__ freq, RowMap rm, KVView kv,
-                              const int32_t* write_limit, TQ* __restrict__ q_out, int32_t* status) {
+                              const int32_t* write_limit, TQ* __restrict__ q_out, TQ* __restrict__ q_lo,
+                              int32_t* status) {
   const int r = blockIdx.x;
   const int b = row_seq(rm, r);
   const int local = r - rm.start[b];
@@ -227,6 +228,11 @@ __global__ void k_rope_append(const float* __restrict__ qkv, const float* __rest
       TQ* qo = q_out + ((int64_t)r * hq + h) * hd;
       qo[i] = from_f<TQ>(ra);
       qo[i + half] = from_f<TQ>(rb);
+      if (q_lo) {  // half-precision remainder plane: q = hi + lo to ~2^-22
+        TQ* ql = q_lo + ((int64_t)r * hq + h) * hd;
+        ql[i] = from_f<TQ>(ra - to_f<TQ>(qo[i]));
+        ql[i + half] = from_f<TQ>(rb - to_f<TQ>(qo[i + half]));
+      }
     } else {
       const int g = h - hq;
       if (write_kv) {
@@ -250,15 +256,16 @@ __global__ void k_rope_append(const float* __restrict__ qkv, const float* __rest
 
 hipError_t launch_rope_append(int dtype, const float* qkv, const float* qkv_part, int n_part, int rows, int hq,
                               int hkv, int hd, const double* freq, const RowMap& rm, KVView kv,
-                              const int32_t* write_limit, void* q_out, int32_t* status, hipStream_t s) {
+                              const int32_t* write_limit, void* q_out, void* q_lo, int32_t* status,
+                              hipStream_t s) {
   const size_t lds = (size_t)(hq + 2 * hkv) * hd * sizeof(float);
   if (hd / 2 > ROPE_MAX_HALF || (n_part > 0 && !qkv_part) || lds > 65536) return hipErrorInvalidValue;
   if (dtype == CAD_BF16)
     hipLaunchKernelGGL((k_rope_append<bf16_t, f16_t>), dim3(rows), dim3(ROW_THREADS), lds, s, qkv, qkv_part, n_part,
-                       rows, hq, hkv, hd, freq, rm, kv, write_limit, (f16_t*)q_out, status);
+                       rows, hq, hkv, hd, freq, rm, kv, write_limit, (f16_t*)q_out, (f16_t*)q_lo, status);
   else
     hipLaunchKernelGGL((k_rope_append<float, float>), dim3(rows), dim3(ROW_THREADS), lds, s, qkv, qkv_part, n_part,
-                       rows, hq, hkv, hd, freq, rm, kv, write_limit, (float*)q_out, status);
+                       rows, hq, hkv, hd, freq, rm, kv, write_limit, (float*)q_out, (float*)nullptr, status);
   return hipGetLastError();
 }
 
