@@ -194,7 +194,8 @@ k_attn_bf16(AttnArgs p) {
     const int64_t k0 = kt + jb * CAD_KV_BLOCK;  // first key of this wave's block
     const bool ok = span_part || (bb >= 0 && bb < p.kv.num_blocks);
     if (!span_part && bb >= 0 && !ok && p.status && ct == 0) atomicOr(p.status, (int32_t)CAD_DEV_BAD_BLOCK);
-    const int nvalid = ok ? (int)max<int64_t>(min<int64_t>(k_end - k0, CAD_KV_BLOCK), 0) : 0;
+    const int64_t rem = k_end - k0;  // keys left in the range from k0 (clamped in 32-bit below)
+    const int nvalid = !ok ? 0 : rem >= CAD_KV_BLOCK ? CAD_KV_BLOCK : rem > 0 ? (int)rem : 0;
     const bf16_t* kb = kbase + (ok && !span_part ? bb : 0) * kv_blk_stride;
     const bf16_t* vb = vbase + (ok && !span_part ? bb : 0) * kv_blk_stride;
     const int64_t srow = span_row0 + (k0 - L);  // span workspace row of key k0
