@@ -175,38 +175,53 @@ k_attn_bf16(AttnArgs p) {
   const int64_t kv_blk_stride = (int64_t)p.hkv * CAD_KV_BLOCK * HD;  // elements per cache block
   const bf16_t* kbase = (const bf16_t*)p.kv.k + (int64_t)kvh * CAD_KV_BLOCK * HD;
   const bf16_t* vbase = (const bf16_t*)p.kv.v + (int64_t)kvh * CAD_KV_BLOCK * HD;
-  // cache block of tile t for this wave, or -1 when the tile's part of the
-  // key range does not reach it (then nothing is read); unused by the span part
-  auto block_of = [&](int t) -> int64_t {
+  // cache block of tile t for this wave (lane 0 of the result), or -1 when
+  // the tile's part of the key range does not reach it (then nothing is
+  // read); unused by the span part.  Lanes 32..63 read the next block's id
+  // (clamped to the range): the value is then not wave-uniform, stays in a
+  // vector register, and the wait for it falls where lane 0 is read a tile
+  // later instead of right after the load.
+  // The load is unconditional (index clamped into the range, entry 0 for the
+  // span part or an empty range) so that no path overwrites its register
+  // while it is in flight; block_used says whether the tile reads the block.
+  const int blast = k_end > k_begin ? (int)((k_end - 1) / CAD_KV_BLOCK) : 0;
+  auto block_used = [&](int t) -> bool {
     const int64_t first_key = k_begin + (int64_t)t * FA_KT + jb * CAD_KV_BLOCK;
-    if (span_part || t >= n_tiles || first_key >= k_end) return -1;
-    return table[first_key / CAD_KV_BLOCK];
+    return !span_part && t < n_tiles && first_key < k_end;
+  };
+  auto block_of = [&](int t) -> int32_t {
+    const int64_t first_key = k_begin + (int64_t)t * FA_KT + jb * CAD_KV_BLOCK;
+    const int bi = span_part ? 0 : min((int)(first_key / CAD_KV_BLOCK), blast);
+    return table[min(bi + (lane >> 5), blast)];
   };
   // span workspace rows of this sequence: row pstart + (key - L)
   const int64_t span_row0 = p.rm.pstart[b];
   const f16_t* span_k = p.kv.span_k;
   const f16_t* span_v = p.kv.span_v;
   u32x4 rk[KCH], rv[VCH];
+  int nvalid_pend = 0;  // valid keys of this wave's cache block in the staged tile
   // Every load below reads valid memory (a clamped block, or the sequence's
   // 64-row padded workspace region) and is unconditional; out-of-range keys
   // are zeroed afterwards, so the waits for tile t + 1 never cover extra work.
-  auto gload = [&](int64_t kt, int64_t bb) {
+  auto gload = [&](int64_t kt, int32_t blkv, bool used) {
+    const int64_t bb = used ? __builtin_amdgcn_readlane(blkv, 0) : -1;
     const int64_t k0 = kt + jb * CAD_KV_BLOCK;  // first key of this wave's block
     const bool ok = span_part || (bb >= 0 && bb < p.kv.num_blocks);
     if (!span_part && bb >= 0 && !ok && p.status && ct == 0) atomicOr(p.status, (int32_t)CAD_DEV_BAD_BLOCK);
     const int64_t rem = k_end - k0;  // keys left in the range from k0 (clamped in 32-bit below)
-    const int nvalid = !ok ? 0 : rem >= CAD_KV_BLOCK ? CAD_KV_BLOCK : rem > 0 ? (int)rem : 0;
+    nvalid_pend = !ok ? 0 : rem >= CAD_KV_BLOCK ? CAD_KV_BLOCK : rem > 0 ? (int)rem : 0;
     const bf16_t* kb = kbase + (ok && !span_part ? bb : 0) * kv_blk_stride;
     const bf16_t* vb = vbase + (ok && !span_part ? bb : 0) * kv_blk_stride;
     const int64_t srow = span_row0 + (k0 - L);  // span workspace row of key k0
+    // raw loads only: the registers are not touched again until sstore, so
+    // the wait for them lands at the end of the tile, not right here
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int c = ct + TPB * i;  // [16 keys][HD / 8 chunks]
       const int key = c / (HD / 8), c8 = c % (HD / 8);
       const u32x4* src = span_part ? (const u32x4*)(span_k + ((srow + key) * p.hkv + kvh) * HD + c8 * 8)
                                    : (const u32x4*)(kb + c * 8);
-      const u32x4 v = *src;
-      rk[i] = key < nvalid ? v : u32x4{0u, 0u, 0u, 0u};
+      rk[i] = *src;
     }
 #pragma unroll
     for (int i = 0; i < VCH; ++i) {
@@ -215,23 +230,18 @@ k_attn_bf16(AttnArgs p) {
       const u32x4* src = span_part
                              ? (const u32x4*)(span_v + ((int64_t)kvh * HD + d) * p.kv.span_cap + srow + 8 * hf)
                              : (const u32x4*)(vb + c * 8);
-      u32x4 v = *src;
-      // zero the tokens past the key range (stale slots may hold anything)
-      const int nv = nvalid - 8 * hf;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t keep = (2 * w + 1 < nv) ? 0xFFFFFFFFu : (2 * w < nv ? 0x0000FFFFu : 0u);
-        v[w] &= keep;
-      }
-      rv[i] = v;
+      rv[i] = *src;
     }
   };
   auto sstore = [&](int buf) {
+    // keys past the range are zeroed here (stale slots may hold anything)
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int c = ct + TPB * i;
-      const int key = jb * CAD_KV_BLOCK + c / (HD / 8), c8 = c % (HD / 8);
-      *(u32x4*)(&sK[buf][key * KLD + c8 * 8]) = span_part ? rk[i] : bf16x8_to_f16x8(rk[i]);
+      const int kin = c / (HD / 8), c8 = c % (HD / 8);
+      const int key = jb * CAD_KV_BLOCK + kin;
+      const u32x4 v = kin < nvalid_pend ? rk[i] : u32x4{0u, 0u, 0u, 0u};
+      *(u32x4*)(&sK[buf][key * KLD + c8 * 8]) = span_part ? v : bf16x8_to_f16x8(v);
     }
 #pragma unroll
     for (int i = 0; i < VCH; ++i) {
@@ -241,7 +251,14 @@ k_attn_bf16(AttnArgs p) {
       // + 16 (jb & 1) + 8 hf + e) key 16 h + 4 j + r sits at column 8 j + 4 h
       // + r: the eight columns 8 j .. 8 j + 7 then hold keys 4 j .. 4 j + 3
       // and 16 + 4 j .. 16 + 4 j + 3, the keys lane group j holds in S^T.
-      const u32x4 h = span_part ? rv[i] : bf16x8_to_f16x8(rv[i]);
+      u32x4 v = rv[i];
+      const int nv = nvalid_pend - 8 * hf;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t keep = (2 * w + 1 < nv) ? 0xFFFFFFFFu : (2 * w < nv ? 0x0000FFFFu : 0u);
+        v[w] &= keep;
+      }
+      const u32x4 h = span_part ? v : bf16x8_to_f16x8(v);
       const int col = (jb >> 1) * 32 + 16 * hf + 4 * (jb & 1);
       f16_t* row = &sV[buf][d * VLD + col];
       *(u32x2*)(row) = u32x2{h[0], h[1]};      // e = 0..3 -> j = 2 hf
@@ -253,9 +270,9 @@ k_attn_bf16(AttnArgs p) {
   // and written to the other LDS buffer at the end of the iteration (that
   // buffer was last read before the barrier that closed tile t - 1).  Block
   // ids run one more tile ahead.
-  int64_t blk = block_of(0);
+  int32_t blk = block_of(0);
   if (n_tiles > 0) {
-    gload(k_begin, blk);
+    gload(k_begin, blk, block_used(0));
     sstore(0);
   }
   blk = block_of(1);
@@ -264,8 +281,8 @@ k_attn_bf16(AttnArgs p) {
     const int buf = t & 1;
     const int64_t kt = k_begin + (int64_t)t * FA_KT;
     const bool more = t + 1 < n_tiles;
-    if (more) gload(kt + FA_KT, blk);
-    const int64_t blk_next = block_of(t + 2);
+    if (more) gload(kt + FA_KT, blk, block_used(t + 1));
+    const int32_t blk_next = block_of(t + 2);
     if (wave_active) {
       // ---- S^T = K Q^T for four 16-key blocks x two 16-query blocks ----
       f32x4 s[4][QB];

@@ -71,12 +71,13 @@ __global__ void __launch_bounds__(ROW_THREADS) k_rmsnorm(float* __restrict__ x, 
     v[j] = i4 < n4 ? *(const f32x4*)(xr + 4 * i4) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   if (n_part > 0) {
-    // four partial planes per batch, all their loads in flight together
-    // (indices clamped; a clamped plane is multiplied by zero)
-    for (int sp = 0; sp < n_part; sp += 4) {
-      f32x4 t[4][V4];
+    // PB partial planes per batch, all their loads in flight together
+    // (indices clamped; the clamped repeats are not added)
+    constexpr int PB = V4 <= 2 ? 8 : 16 / V4;
+    for (int sp = 0; sp < n_part; sp += PB) {
+      f32x4 t[PB][V4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < PB; ++u) {
         const float* pr = x_part + ((int64_t)min(sp + u, n_part - 1) * rows + r) * d;
 #pragma unroll
         for (int j = 0; j < V4; ++j) {
@@ -85,7 +86,7 @@ __global__ void __launch_bounds__(ROW_THREADS) k_rmsnorm(float* __restrict__ x, 
         }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < PB; ++u)
         if (sp + u < n_part)
 #pragma unroll
           for (int j = 0; j < V4; ++j) v[j] += t[u][j];
@@ -142,7 +143,7 @@ hipError_t launch_rmsnorm(int dtype, float* x, const float* x_part, int n_part, 
 
 // ---------------------------------------------------------------------------
 // rotary positions on q and k (half-split pairs, angle pos * freq[i] formed
-// in fp64), q to the attention operand buffer (type TQ), k and v appended to
+// and reduced in fp64), q to the attention operand buffer (type TQ), k and v appended to
 // the paged cache (type T) at the row's absolute position.  Rows at or beyond
 // *write_limit do not touch the cache.  bf16 models also keep every row's k
 // and v at half precision in the span workspace (kv.span_k / kv.span_v),
@@ -212,9 +213,16 @@ __global__ void k_rope_append(const float* __restrict__ qkv, const float* __rest
   // the row's rotation, one (cos, sin) per pair, in LDS
   __shared__ float2 rot[ROPE_MAX_HALF];
   for (int i = threadIdx.x; i < half; i += blockDim.x) {
-    double sn, cs;
-    sincos((double)pos * freq[i], &sn, &cs);
-    rot[i] = float2{(float)cs, (float)sn};
+    // angle pos * freq[i] in fp64, reduced by a multiple of 2 pi (2 pi split
+    // into a double and its remainder, Cody-Waite) to |r| <= pi, whose sine
+    // and cosine single precision takes on its fast path
+    const double ang = (double)pos * freq[i];
+    const double k = rint(ang * 0.15915494309189535);           // 1 / (2 pi)
+    double r = fma(-k, 6.283185307179586, ang);                  // 2 pi, high part
+    r = fma(-k, 2.4492935982947064e-16, r);                      // 2 pi - high part
+    float sn, cs;
+    sincosf((float)r, &sn, &cs);
+    rot[i] = float2{cs, sn};
   }
   __syncthreads();
   // rotations: q heads then k heads, one (head, pair) per item
