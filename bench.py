@@ -130,6 +130,193 @@ class Workload:
         return time.perf_counter() - t0
 
 
+
+# ----------------------------------------------------------------------------
+# the other workloads of the same hot path (reported beside the headline)
+# ----------------------------------------------------------------------------
+
+def copy_bandwidth():
+    """Achievable HBM reference: a 1 GiB device-to-device copy, GB/s moved (read + write)."""
+    import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 5
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(2 * (1 << 30) / dt / 1e9, 1)
+
+
+def serve_bench(wl, steps=5, draws=3):
+    """Batched editing serve at the 7B shape: 32 sequences with cache lengths
+    U[1024, 8192] in one paged pool of 16-token blocks (shuffled), each step
+    one cad_splice_forward_batched call in which every sequence splices a copy
+    of Geometric(1/4) duplicated lines (probability 0.106, cap 512 tokens) or
+    takes a one-token generation step.  Reports spliced tokens/s over
+    ``draws`` different steps."""
+    import numpy as np
+    import torch
+    import synth
+    cad = wl.cad
+    shape, n_seq = wl.shape, 32
+    r = synth.rng(synth.SEED_SERVE, 77)
+    prompts = [synth.make_line_prompt(8192, shape.vocab, seed=1000 + b, line_len_range=(8, 16)) for b in range(n_seq)]
+    plan = []
+    for _ in range(draws):
+        st = synth.serve_step(n_seq, prompts, r)
+        while sum(len(x) for x in st.spans) > 2048:
+            st = synth.serve_step(n_seq, prompts, r)
+        plan.append(st)
+    max_L = 8192 + 512
+    need = (max_L + 15) // 16
+    pool = need * n_seq
+    table = synth.shuffled_block_table(pool, pool, seed=77).reshape(n_seq, need)
+    kv = cad.KVCache.alloc(shape, pool, table, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(synth.SEED_KV + 1)
+    std = synth.kv_std(shape)
+    for t in (kv.k, kv.v):
+        for i in range(t.shape[0]):
+            t[i].copy_(torch.randn(t[i].shape, generator=g, device="cuda", dtype=torch.float32).mul_(std))
+    model = cad.cad_model_create(shape, wl.W, max_tokens=2048)
+    tot_tok, tot_s, rows = 0, 0.0, []
+    for st in plan:
+        offs = np.concatenate([[0], np.cumsum([len(x) for x in st.spans])]).astype(np.int32)
+        total = int(offs[-1])
+        spans = torch.from_numpy(np.concatenate(st.spans).astype(np.int32)).cuda()
+        am = torch.empty(total, dtype=torch.int32, device="cuda")
+        acc = torch.empty(n_seq, dtype=torch.int32, device="cuda")
+        stat = torch.zeros(1, dtype=torch.int32, device="cuda")
+        call = lambda: cad.cad_splice_forward_batched(model, kv, st.L, offs, spans, None, cad.CAD_COMMIT, am, acc,
+                                                       None, stat)
+        for _ in range(2):
+            call()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / steps
+        tot_tok += total
+        tot_s += dt
+        rows.append({"rows": total, "copies": int(st.is_copy.sum()), "mean_L": int(st.L.mean()),
+                     "ms": round(dt * 1e3, 3)})
+        if int(stat[0]) != 0:
+            log(f"[bench] serve: device status {int(stat[0])}")
+    cad.cad_model_destroy(model)
+    del kv
+    torch.cuda.empty_cache()
+    return {"workload": "batched editing serve, 7B shape, 32 sequences, L_b ~ U[1024, 8192], paged 16-token "
+                        "blocks, per-sequence copy (p=0.106, Geometric(1/4) lines, cap 512) or 1-token gen, COMMIT",
+            "value": round(tot_tok / tot_s, 1), "unit": "spliced tokens/s", "steps": rows}
+
+
+def looped_bench(reps=10):
+    """Looped shared block (d 2048, 16 x 128 MHA, FFN 5632, depth 8): a head
+    plus up to K = 8 tokens copied after the longest prompt-suffix match
+    (proposal on the device) at L = 4096, screened at depth 2 and verified at
+    depth 8 (natural random-init case), and the worst case with every
+    position taken to depth 8 (screen depth 8).  Reports blocks/s and tokens
+    processed per second (positions x depths / 8)."""
+    import numpy as np
+    import torch
+    import synth
+    import verify_forward_amd as cad
+    shape, L, K = synth.LOOPED, 4096, 8
+    W = synth.make_weights(shape, device="cuda")
+    prompt = synth.make_line_prompt(L, shape.vocab)
+    nb = (L + 16 + 15) // 16
+    kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(synth.SEED_KV + 2)
+    for t in (kv.k, kv.v):
+        t.copy_(torch.randn(t.shape, generator=g, device="cuda", dtype=torch.float32).mul_(synth.kv_std(shape)))
+    model = cad.cad_model_create(shape, W, max_tokens=16)
+    head = int(prompt.tokens[int(prompt.dup_starts[3])])
+    hist = torch.from_numpy(np.concatenate([prompt.tokens, [head]]).astype(np.int32)).cuda()
+    out_t = torch.zeros(K, dtype=torch.int32, device="cuda")
+    out_n = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out_p = torch.zeros(1, dtype=torch.int64, device="cuda")
+    cad.cad_propose_suffix_match(hist, 4, 1, K, out_t, out_n, out_p)
+    torch.cuda.synchronize()
+    n = int(out_n[0])
+    span = torch.cat([torch.tensor([head], dtype=torch.int32, device="cuda"), out_t[:n]])
+    N = span.numel()
+    res = {}
+    for name, ds in (("screen_depth_2", 2), ("all_positions_depth_8", shape.loop_depth)):
+        sa = torch.empty(N, dtype=torch.int32, device="cuda")
+        sv = torch.empty(1, dtype=torch.int32, device="cuda")
+        am = torch.empty(N, dtype=torch.int32, device="cuda")
+        acc = torch.empty(1, dtype=torch.int32, device="cuda")
+
+        def call():
+            cad.cad_propose_suffix_match(hist, 4, 1, K, out_t, out_n, out_p)
+            cad.cad_splice_forward_looped(model, kv, L, span, ds, None, sa, sv, am, acc)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            call()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / reps
+        surv = int(sv[0])
+        work = N * ds + surv * (shape.loop_depth - ds)
+        res[name] = {"N": N, "survivors": surv, "ms_per_block": round(dt * 1e3, 4),
+                     "blocks_per_s": round(1 / dt, 1),
+                     "tokens_processed_per_s": round(work / shape.loop_depth / dt, 1)}
+    cad.cad_model_destroy(model)
+    del kv, W
+    torch.cuda.empty_cache()
+    return {"workload": "looped shared block (d 2048, 16 x 128 heads, FFN 5632, vocab 32000, depth 8), "
+                        "L=4096, head + suffix-match proposal (K=8)", **res}
+
+
+def s_of_n(wl, Ns=(8, 64, 512), L=1024):
+    """The pages' s(N) = T(N one-token decode steps) / T(one splice of N) at the
+    7B shape and L = 1024 (Copy-as-Decode §3, Table 1's comparison)."""
+    import torch
+    import synth
+    cad = wl.cad
+    shape = wl.shape
+    nb = (L + 512 + 15) // 16
+    kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device="cuda")
+    kv.k.copy_(wl.kv.k[:, :nb])
+    kv.v.copy_(wl.kv.v[:, :nb])
+    prompt = synth.make_line_prompt(L, shape.vocab)
+    out = []
+    for N in Ns:
+        span = torch.from_numpy(synth.pick_span(prompt, N).astype("int32")).cuda()
+        am = torch.empty(N, dtype=torch.int32, device="cuda")
+        acc = torch.empty(1, dtype=torch.int32, device="cuda")
+        one = torch.empty(1, dtype=torch.int32, device="cuda")
+        splice = lambda: cad.cad_splice_forward(wl.model, kv, L, span, None, cad.CAD_COMMIT, am, acc)
+
+        def decode_chain():
+            for i in range(N):
+                cad.cad_decode_step(wl.model, kv, L + i, span[i:i + 1], None, one)
+        res = {}
+        for name, fn, reps in (("splice", splice, 5), ("decode", decode_chain, 1)):
+            fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                fn()
+            torch.cuda.synchronize()
+            res[name] = (time.perf_counter() - t0) / reps
+        out.append({"N": N, "splice_ms": round(res["splice"] * 1e3, 3), "decode_steps_ms": round(res["decode"] * 1e3, 3),
+                    "s": round(res["decode"] / res["splice"], 2)})
+        log(f"[bench] s(N={N}) at L={L}: {out[-1]['s']}")
+    del kv
+    torch.cuda.empty_cache()
+    return out
+
 # ----------------------------------------------------------------------------
 # CPU baseline: the float64 oracle on a bounded sample
 # ----------------------------------------------------------------------------
@@ -212,6 +399,8 @@ def main():
     ap.add_argument("--L", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the serve, looped, s(N) and copy-bandwidth reports")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain device copy of 1 GiB first (a known-size reference for HBM counters)")
     args = ap.parse_args()
@@ -315,9 +504,20 @@ def main():
             log(f"[bench] sweep N={n}: {ms:.3f} ms")
         out["sweep"] = sweep
 
-    if not args.no_cpu_baseline:
+    if not args.no_extras:
+        out["s_of_N_L1024"] = s_of_n(wl)
+        out["serve"] = serve_bench(wl)
+        log(f"[bench] serve: {out['serve']['value']} tok/s")
+        out["achievable_copy_GBs"] = copy_bandwidth()
+
+    if not args.no_cpu_baseline or not args.no_extras:
         del wl
         torch.cuda.empty_cache()
+    if not args.no_extras:
+        out["looped"] = looped_bench()
+        log("[bench] looped done")
+
+    if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, L, N)
     else:
         out["cpu_baseline"] = None
