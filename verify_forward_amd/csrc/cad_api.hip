@@ -155,7 +155,10 @@ int64_t max_parts_rows(const cad_config& c) {
   int64_t best = 0;
   for (int r = 1; r <= c.max_tokens; ++r) {
     int len = 0;
-    const int p = attention_parts(r, c.n_q_heads, c.n_kv_heads, c.head_dim, (int64_t)1 << 40, &len) + 1;
+    // both tile shapes: one sequence, and r one-row sequences
+    const int p1 = attention_parts(r, 1, c.n_q_heads, c.n_kv_heads, (int64_t)1 << 40, &len) + 1;
+    const int p2 = attention_parts(r, r, c.n_q_heads, c.n_kv_heads, (int64_t)1 << 40, &len) + 1;
+    const int p = p1 > p2 ? p1 : p2;
     if ((int64_t)p * r > best) best = (int64_t)p * r;
   }
   return best;
@@ -206,7 +209,7 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
   int64_t max_L = 0;
   for (int b = 0; b < rm.n_seq; ++b) max_L = rm.L[b] > max_L ? rm.L[b] : max_L;
   int part_len = 0;
-  const int n_parts = attention_parts(R, hq, hkv, hd, max_L, &part_len) + 1;  // + the span partition
+  const int n_parts = attention_parts(R, rm.n_seq, hq, hkv, max_L, &part_len) + 1;  // + the span partition
   if ((int64_t)n_parts * R > m->part_cap)
     return fail(CAD_E_CAPACITY, "attention partitions %d x %d rows exceed the workspace", n_parts, R);
   if (c.dtype == CAD_BF16 && rm.pstart[rm.n_seq] > m->span_cap)
@@ -242,6 +245,7 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
     g = GemmArgs{};
     g.A = m->hn; g.A_lo = lo_plane(m, m->hn, d); g.lda = d; g.W = m->w_gate_up[li]; g.ldw = d;
     g.M = R; g.N = F; g.K = d; g.up_off = F; g.out_act = m->act; g.out_act_lo = lo_plane(m, m->act, F);
+    g.split_ws = m->split_ws;
     LAUNCH(PF_GATEUP, launch_gemm(c.dtype, GEMM_GATE_UP, g, s));
     g = GemmArgs{};
     g.A = m->act; g.A_lo = lo_plane(m, m->act, F); g.lda = F; g.W = m->w_down[li]; g.ldw = F;

@@ -176,6 +176,6 @@ hipError_t launch_suffix_match(const int32_t* tokens, int64_t T, int max_n, int 
 
 // attention split: partitions of the cached keys (0 .. max L) so that small
 // spans still fill the chip; the span's own keys form one more partition
-int attention_parts(int rows, int hq, int hkv, int hd, int64_t max_cache_keys, int* part_len);
+int attention_parts(int rows, int n_seq, int hq, int hkv, int64_t max_cache_keys, int* part_len);
 
 }  // namespace cad

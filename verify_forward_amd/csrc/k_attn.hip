@@ -50,11 +50,12 @@ struct AttnArgs {
 constexpr int FA_KT = 64;                  // keys per tile
 // Work-group shapes: eight waves of 32 query rows (two waves per SIMD) for
 // long spans; four waves of 16 rows (several work-groups per CU, twice the
-// work-groups over the key axis to spread the cache stream wider) when a
-// call has at most 64 query rows.  (One wave per SIMD with 48 or 64 rows
+// work-groups over the key axis to spread the cache stream wider) when the
+// call's sequences average at most 64 query rows (short spans, and batched
+// serving, where most sequences take a one-token step).  (One wave per SIMD with 48 or 64 rows
 // each, which reads each K/V fragment from LDS once for more queries,
 // measured 2.6x slower: nothing hides LDS and softmax latency then.)
-inline int attn_qt(int query_rows, int hd) { return query_rows <= 64 ? 64 : 256; }
+inline int attn_qt(int query_rows, int n_seq) { return query_rows <= 64 * n_seq ? 64 : 256; }
 
 // Work-group -> (query tile, KV head, key partition).  The query tiles that
 // read the same KV head and key range are placed on one XCD (work-group ids
@@ -528,12 +529,12 @@ k_attn_f32(AttnArgs p, int hd) {
   }
 }
 
-int attention_parts(int rows, int hq, int hkv, int hd, int64_t max_cache_keys, int* part_len) {
+int attention_parts(int rows, int n_seq, int hq, int hkv, int64_t max_cache_keys, int* part_len) {
   // partitions of the cached keys: about one work-group per compute unit
   // (256 CUs; two for the four-wave shape) together with the query tiles,
   // at least 256 keys each
   const int G = hq / hkv;
-  const int qt = attn_qt(rows * G, hd);
+  const int qt = attn_qt(rows * G, n_seq);
   const int tiles = (rows * G + qt - 1) / qt;
   const int base = hkv * tiles;
   if (max_cache_keys <= 0) {
@@ -577,7 +578,7 @@ hipError_t launch_attention(int dtype, const void* q, const void* q_lo, int rows
     hipLaunchKernelGGL(k_attn_f32, dim3(rows, hq), dim3(64), 0, s, a, hd);
     return hipGetLastError();
   }
-  const int qt = attn_qt(rows * a.G, hd);
+  const int qt = attn_qt(rows * a.G, rm.n_seq);
   int nt = 0;
   a.tstart[0] = 0;
   for (int b = 0; b < rm.n_seq; ++b) {
