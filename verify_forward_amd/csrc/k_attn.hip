@@ -45,6 +45,7 @@ struct AttnArgs {
   void* out_lo;    // bf16 models: the bf16 lo plane
   int32_t* status;
   float scale_log2;  // log2(e) / sqrt(hd)
+  float pos_inf;     // +inf
 };
 
 constexpr int FA_KT = 64;                  // keys per tile
@@ -80,6 +81,23 @@ __device__ __forceinline__ void attn_tile_of(int& x, int& y, int& z) {
 // so the O rescale is skipped on most tiles; until then the unnormalised
 // weights stay below 2^FA_LAZY, far inside half's range.
 constexpr float FA_LAZY = 8.0f;
+
+// max(a, b) as the median of (a, b, +inf): one instruction, where fmaxf first
+// quiets each operand that comes straight from the matrix cores or a lane
+// swap (no NaN can reach the scores: masked keys are -inf, every product is
+// finite).  `inf` arrives as a kernel argument so that the compiler does not
+// turn the median back into fmaxf.
+__device__ __forceinline__ float max_raw(float a, float b, float inf) { return __builtin_amdgcn_fmed3f(a, b, inf); }
+
+// max over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four row groups of a
+// wave that hold one query column), by the two half-swapping lane
+// permutations instead of LDS-routed shuffles
+__device__ __forceinline__ float max_col4(float m, float inf) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  m = max_raw(__uint_as_float(a[0]), __uint_as_float(a[1]), inf);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return max_raw(__uint_as_float(b[0]), __uint_as_float(b[1]), inf);
+}
 
 template <int HD, int NW, int QB>
 __global__ void __launch_bounds__(64 * NW, 8 / NW)
@@ -134,7 +152,8 @@ k_attn_bf16(AttnArgs p) {
   constexpr int QLD = HD + 8;  // sQlo row stride (halves): conflict-free 16-row reads
   __shared__ __attribute__((aligned(16))) f16_t sQlo[QLO_LDS ? NW * QPW * QLD : 8];
   bool q_ok[QB];
-  int64_t q_last_key[QB], qrow[QB];
+  int q_last_rel[QB];  // this lane's last visible key, relative to k_begin
+  int64_t qrow[QB];
   u32x4 qf[QB][DS], qfl[QLO_LDS ? 1 : QB][DS];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -142,7 +161,7 @@ k_attn_bf16(AttnArgs p) {
     q_ok[qb] = qi < R;
     const int k_local = q_ok[qb] ? qi / p.G : 0;
     const int head = kvh * p.G + (q_ok[qb] ? qi % p.G : 0);
-    q_last_key[qb] = L + k_local;
+    q_last_rel[qb] = (int)(L + k_local - k_begin);
     qrow[qb] = (int64_t)(p.rm.start[b] + k_local) * p.hq + head;  // index of (row, head)
     const f16_t* qsrc = (const f16_t*)p.q + qrow[qb] * HD;
     const f16_t* qlsrc = (const f16_t*)p.q_lo + qrow[qb] * HD;
@@ -235,14 +254,31 @@ k_attn_bf16(AttnArgs p) {
     }
   };
   auto sstore = [&](int buf) {
-    // keys past the range are zeroed here (stale slots may hold anything)
+    // keys past the range are zeroed here (stale slots may hold anything);
+    // nvalid_pend is wave-uniform and below a full block only at the ends
+    // of the key range
+    if (nvalid_pend < CAD_KV_BLOCK) {
+#pragma unroll
+      for (int i = 0; i < KCH; ++i) {
+        const int kin = (ct + TPB * i) / (HD / 8);
+        if (kin >= nvalid_pend) rk[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int i = 0; i < VCH; ++i) {
+        const int nv = nvalid_pend - 8 * ((ct + TPB * i) & 1);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t keep = (2 * w + 1 < nv) ? 0xFFFFFFFFu : (2 * w < nv ? 0x0000FFFFu : 0u);
+          rv[i][w] &= keep;
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int c = ct + TPB * i;
       const int kin = c / (HD / 8), c8 = c % (HD / 8);
       const int key = jb * CAD_KV_BLOCK + kin;
-      const u32x4 v = kin < nvalid_pend ? rk[i] : u32x4{0u, 0u, 0u, 0u};
-      *(u32x4*)(&sK[buf][key * KLD + c8 * 8]) = span_part ? v : bf16x8_to_f16x8(v);
+      *(u32x4*)(&sK[buf][key * KLD + c8 * 8]) = span_part ? rk[i] : bf16x8_to_f16x8(rk[i]);
     }
 #pragma unroll
     for (int i = 0; i < VCH; ++i) {
@@ -252,14 +288,7 @@ k_attn_bf16(AttnArgs p) {
       // + 16 (jb & 1) + 8 hf + e) key 16 h + 4 j + r sits at column 8 j + 4 h
       // + r: the eight columns 8 j .. 8 j + 7 then hold keys 4 j .. 4 j + 3
       // and 16 + 4 j .. 16 + 4 j + 3, the keys lane group j holds in S^T.
-      u32x4 v = rv[i];
-      const int nv = nvalid_pend - 8 * hf;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t keep = (2 * w + 1 < nv) ? 0xFFFFFFFFu : (2 * w < nv ? 0x0000FFFFu : 0u);
-        v[w] &= keep;
-      }
-      const u32x4 h = span_part ? v : bf16x8_to_f16x8(v);
+      const u32x4 h = span_part ? rv[i] : bf16x8_to_f16x8(rv[i]);
       const int col = (jb >> 1) * 32 + 16 * hf + 4 * (jb & 1);
       f16_t* row = &sV[buf][d * VLD + col];
       *(u32x2*)(row) = u32x2{h[0], h[1]};      // e = 0..3 -> j = 2 hf
@@ -316,19 +345,18 @@ k_attn_bf16(AttnArgs p) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         if (need_mask) {
-          const int lim = (int)max<int64_t>(min<int64_t>(q_last_key[qb] - kt + 1, end_rel), 0);
+          const int lim = max(min(q_last_rel[qb] - t * FA_KT + 1, end_rel), 0);
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
               if (kb * 16 + g4 * 4 + r >= lim) s[kb][qb][r] = -INFINITY;
         }
-        float m = -INFINITY;
+        float mk[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
-          m = fmaxf(fmaxf(m, fmaxf(s[kb][qb][0], s[kb][qb][1])), fmaxf(s[kb][qb][2], s[kb][qb][3]));
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
+          mk[kb] = fmaxf(max_raw(s[kb][qb][0], s[kb][qb][1], p.pos_inf), max_raw(s[kb][qb][2], s[kb][qb][3], p.pos_inf));
+        const float m = max_col4(fmaxf(fmaxf(mk[0], mk[1]), fmaxf(mk[2], mk[3])), p.pos_inf);
         mx[qb] = m * p.scale_log2;
         grow |= mx[qb] > m_run[qb] + FA_LAZY;
       }
@@ -347,19 +375,24 @@ k_attn_bf16(AttnArgs p) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const float nm = -m_run[qb];
+        // the row sum takes the weights as rounded for the matrix cores
+        // (pairs summed by a half dot product with (1, 1) into fp32), so the
+        // numerator and the denominator see the same P
         float psum = 0.f;
+        const f16x2 ones = {(f16_t)1.0f, (f16_t)1.0f};
         uint32_t pk[8];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           float e[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][r], p.scale_log2, nm));
-            psum += e[r];
-          }
+          for (int r = 0; r < 4; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][r], p.scale_log2, nm));
           // round to nearest (unbiased), weights are in [0, 2^FA_LAZY]
-          pk[kb * 2 + 0] = __builtin_bit_cast(uint32_t, f16x2{(f16_t)e[0], (f16_t)e[1]});
-          pk[kb * 2 + 1] = __builtin_bit_cast(uint32_t, f16x2{(f16_t)e[2], (f16_t)e[3]});
+          const f16x2 e01 = {(f16_t)e[0], (f16_t)e[1]};
+          const f16x2 e23 = {(f16_t)e[2], (f16_t)e[3]};
+          psum = __builtin_amdgcn_fdot2(e01, ones, psum, false);
+          psum = __builtin_amdgcn_fdot2(e23, ones, psum, false);
+          pk[kb * 2 + 0] = __builtin_bit_cast(uint32_t, e01);
+          pk[kb * 2 + 1] = __builtin_bit_cast(uint32_t, e23);
         }
         l_run[qb] += psum;
         // k step ks covers key blocks 2 ks and 2 ks + 1
@@ -574,6 +607,7 @@ hipError_t launch_attention(int dtype, const void* q, const void* q_lo, int rows
   a.out_lo = out_lo;
   a.status = status;
   a.scale_log2 = 1.4426950408889634f / sqrtf((float)hd);
+  a.pos_inf = INFINITY;
   if (dtype == CAD_F32) {
     hipLaunchKernelGGL(k_attn_f32, dim3(rows, hq), dim3(64), 0, s, a, hd);
     return hipGetLastError();
