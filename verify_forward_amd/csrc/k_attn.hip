@@ -467,6 +467,16 @@ __global__ void __launch_bounds__(128 * MERGE_GROUPS) k_attn_merge(const float* 
   __shared__ float snum[MERGE_GROUPS][128];
   const int64_t qi = blockIdx.x;
   const int t = threadIdx.x, nt = blockDim.x;
+  const int ng = nt / 128, grp = t / 128, d = t % 128;
+  const int q0 = n_parts * grp / ng, q1 = n_parts * (grp + 1) / ng;
+  // the first MP partial outputs of this thread's range are loaded before
+  // anything else (they do not depend on the weights)
+  constexpr int MP = 16;
+  const float* po = part_o + qi * hd + min(d, hd - 1);
+  const int64_t stride = nq * hd;
+  float ov0[MP];
+#pragma unroll
+  for (int u = 0; u < MP; ++u) ov0[u] = po[(int64_t)max(min(q0 + u, q1 - 1), 0) * stride];
   // maximum over partitions with a positive sum
   float mloc = -INFINITY;
   for (int pp = t; pp < n_parts; pp += nt) {
@@ -485,13 +495,12 @@ __global__ void __launch_bounds__(128 * MERGE_GROUPS) k_attn_merge(const float* 
   // denominator: sum of w_p * l_p in partition order (every thread the same)
   float den = 0.f;
   for (int pp = 0; pp < n_parts; ++pp) den += sw[pp] * sl[pp];
-  const int ng = nt / 128, grp = t / 128, d = t % 128;
-  const int q0 = n_parts * grp / ng, q1 = n_parts * (grp + 1) / ng;
   float num = 0.f;
   if (d < hd) {
-    const float* po = part_o + qi * hd + d;
-    const int64_t stride = nq * hd;
-    for (int pp = q0; pp < q1; pp += 8) {
+#pragma unroll
+    for (int u = 0; u < MP; ++u)
+      if (q0 + u < q1) num += sw[q0 + u] * ov0[u];
+    for (int pp = q0 + MP; pp < q1; pp += 8) {
       float ov[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) ov[u] = po[(int64_t)min(pp + u, q1 - 1) * stride];

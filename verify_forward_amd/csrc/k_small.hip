@@ -63,12 +63,17 @@ __global__ void __launch_bounds__(ROW_THREADS) k_rmsnorm(float* __restrict__ x, 
   const int r = blockIdx.x;
   float* xr = x + (int64_t)r * d;
   const int n4 = d / 4;
-  f32x4 v[V4];
+  f32x4 v[V4], gv[V4];
   float ss = 0.f;
+  // x and the gain are both loaded up front (the gain does not wait for
+  // the reduction)
 #pragma unroll
   for (int j = 0; j < V4; ++j) {
     const int i4 = threadIdx.x + j * ROW_THREADS;
     v[j] = i4 < n4 ? *(const f32x4*)(xr + 4 * i4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const int c4 = min(i4, n4 - 1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) gv[j][e] = to_f<T>(g[4 * c4 + e]);
   }
   if (n_part > 0) {
     // PB partial planes per batch, all their loads in flight together
@@ -108,7 +113,7 @@ __global__ void __launch_bounds__(ROW_THREADS) k_rmsnorm(float* __restrict__ x, 
     const int i = 4 * i4;
     float y[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) y[e] = v[j][e] * rs * to_f<T>(g[i + e]);
+    for (int e = 0; e < 4; ++e) y[e] = v[j][e] * rs * gv[j][e];
     if (SPLIT) {
       bf16_t hi[4], lo[4];
 #pragma unroll
@@ -150,9 +155,10 @@ hipError_t launch_rmsnorm(int dtype, float* x, const float* x_part, int n_part, 
 // which attention reads for this call's own keys.
 // ---------------------------------------------------------------------------
 constexpr int ROPE_MAX_HALF = 128;  // head_dim up to 256
+constexpr int ROPE_THREADS = 512;
 
 template <typename T, typename TQ>
-__global__ void k_rope_append(const float* __restrict__ qkv, const float* __restrict__ qkv_part, int n_part,
+__global__ void __launch_bounds__(ROPE_THREADS) k_rope_append(const float* __restrict__ qkv, const float* __restrict__ qkv_part, int n_part,
                               int rows, int hq, int hkv, int hd,
                               const double* __restrict__ freq, RowMap rm, KVView kv,
                               const int32_t* write_limit, TQ* __restrict__ q_out, TQ* __restrict__ q_lo,
@@ -163,47 +169,54 @@ __global__ void k_rope_append(const float* __restrict__ qkv, const float* __rest
   const int64_t pos = rm.L[b] + local;
   const int half = hd / 2;
   const int width = (hq + 2 * hkv) * hd;
+  // independent loads first: this row's cache block and its rotation
+  // frequency (one pair per thread)
+  bool write_kv = write_limit == nullptr || local < *write_limit;
+  const int64_t blk = write_kv ? kv.table[(int64_t)b * kv.max_blocks + pos / CAD_KV_BLOCK] : 0;
+  const double fr = (int)threadIdx.x < half ? freq[threadIdx.x] : 0.0;
   // the row's projection output, staged in LDS: the stored values, or the
   // sum of the k-split partials [n_part][rows][width] in split order
   extern __shared__ float srow[];
   {
-    const float* src = qkv + (int64_t)r * width;
+    // RV 16-byte pieces per thread in flight at once (indices clamped; the
+    // clamped repeats are not stored); partial planes added in split order
+    const float* src = n_part == 0 ? qkv + (int64_t)r * width : qkv_part + (int64_t)r * width;
+    const int64_t plane = (int64_t)rows * width;
     const int n4 = width / 4;
-    for (int i4 = threadIdx.x; i4 < n4; i4 += blockDim.x) {
-      f32x4 v;
-      if (n_part == 0) {
-        v = *(const f32x4*)(src + 4 * i4);
-      } else {
-        // eight partial planes per batch, loads in flight together (indices
-        // clamped, the clamped repeats are not added)
-        v = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int sp = 0; sp < n_part; sp += 8) {
-          f32x4 t[8];
+    constexpr int RV = 4;
+    for (int base = 0; base < n4; base += RV * ROPE_THREADS) {
+      f32x4 v[RV];
 #pragma unroll
-          for (int u = 0; u < 8; ++u)
-            t[u] = *(const f32x4*)(qkv_part + ((int64_t)min(sp + u, n_part - 1) * rows + r) * width + 4 * i4);
-#pragma unroll
-          for (int u = 0; u < 8; ++u)
-            if (sp + u < n_part) v = (sp + u == 0) ? t[u] : v + t[u];
-        }
+      for (int u = 0; u < RV; ++u) {
+        const int i4 = min(base + (int)threadIdx.x + u * ROPE_THREADS, n4 - 1);
+        v[u] = *(const f32x4*)(src + 4 * i4);
       }
-      *(f32x4*)(srow + 4 * i4) = v;
+      for (int sp = 1; sp < n_part; ++sp) {
+        f32x4 t[RV];
+#pragma unroll
+        for (int u = 0; u < RV; ++u) {
+          const int i4 = min(base + (int)threadIdx.x + u * ROPE_THREADS, n4 - 1);
+          t[u] = *(const f32x4*)(src + sp * plane + 4 * i4);
+        }
+#pragma unroll
+        for (int u = 0; u < RV; ++u) v[u] += t[u];
+      }
+#pragma unroll
+      for (int u = 0; u < RV; ++u) {
+        const int i4 = base + (int)threadIdx.x + u * ROPE_THREADS;
+        if (i4 < n4) *(f32x4*)(srow + 4 * i4) = v[u];
+      }
     }
     for (int i = 4 * n4 + threadIdx.x; i < width; i += blockDim.x) {
-      float v = n_part == 0 ? src[i] : qkv_part[(int64_t)r * width + i];
-      for (int sp = 1; sp < n_part; ++sp) v += qkv_part[((int64_t)sp * rows + r) * width + i];
+      float v = src[i];
+      for (int sp = 1; sp < n_part; ++sp) v += src[sp * plane + i];
       srow[i] = v;
     }
   }
   auto ld = [&](int i) { return srow[i]; };
-  bool write_kv = write_limit == nullptr || local < *write_limit;
-  int64_t blk = 0;
-  if (write_kv) {
-    blk = kv.table[(int64_t)b * kv.max_blocks + pos / CAD_KV_BLOCK];
-    if (blk < 0 || blk >= kv.num_blocks) {
-      if (threadIdx.x == 0 && status) atomicOr(status, (int32_t)CAD_DEV_BAD_BLOCK);
-      write_kv = false;
-    }
+  if (write_kv && (blk < 0 || blk >= kv.num_blocks)) {
+    if (threadIdx.x == 0 && status) atomicOr(status, (int32_t)CAD_DEV_BAD_BLOCK);
+    write_kv = false;
   }
   const int slot = (int)(pos % CAD_KV_BLOCK);
   T* kc = (T*)kv.k;
@@ -212,11 +225,12 @@ __global__ void k_rope_append(const float* __restrict__ qkv, const float* __rest
   f16_t* sk = kv.span_k ? kv.span_k + wrow * hkv * hd : nullptr;
   // the row's rotation, one (cos, sin) per pair, in LDS
   __shared__ float2 rot[ROPE_MAX_HALF];
-  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+  if ((int)threadIdx.x < half) {
+    const int i = threadIdx.x;
     // angle pos * freq[i] in fp64, reduced by a multiple of 2 pi (2 pi split
     // into a double and its remainder, Cody-Waite) to |r| <= pi, whose sine
     // and cosine single precision takes on its fast path
-    const double ang = (double)pos * freq[i];
+    const double ang = (double)pos * fr;
     const double k = rint(ang * 0.15915494309189535);           // 1 / (2 pi)
     double r = fma(-k, 6.283185307179586, ang);                  // 2 pi, high part
     r = fma(-k, 2.4492935982947064e-16, r);                      // 2 pi - high part
@@ -267,12 +281,13 @@ hipError_t launch_rope_append(int dtype, const float* qkv, const float* qkv_part
                               const int32_t* write_limit, void* q_out, void* q_lo, int32_t* status,
                               hipStream_t s) {
   const size_t lds = (size_t)(hq + 2 * hkv) * hd * sizeof(float);
-  if (hd / 2 > ROPE_MAX_HALF || (n_part > 0 && !qkv_part) || lds > 65536) return hipErrorInvalidValue;
+  if (hd / 2 > ROPE_MAX_HALF || hd / 2 > ROPE_THREADS || (n_part > 0 && !qkv_part) || lds > 65536)
+    return hipErrorInvalidValue;
   if (dtype == CAD_BF16)
-    hipLaunchKernelGGL((k_rope_append<bf16_t, f16_t>), dim3(rows), dim3(ROW_THREADS), lds, s, qkv, qkv_part, n_part,
+    hipLaunchKernelGGL((k_rope_append<bf16_t, f16_t>), dim3(rows), dim3(ROPE_THREADS), lds, s, qkv, qkv_part, n_part,
                        rows, hq, hkv, hd, freq, rm, kv, write_limit, (f16_t*)q_out, (f16_t*)q_lo, status);
   else
-    hipLaunchKernelGGL((k_rope_append<float, float>), dim3(rows), dim3(ROW_THREADS), lds, s, qkv, qkv_part, n_part,
+    hipLaunchKernelGGL((k_rope_append<float, float>), dim3(rows), dim3(ROPE_THREADS), lds, s, qkv, qkv_part, n_part,
                        rows, hq, hkv, hd, freq, rm, kv, write_limit, (float*)q_out, (float*)nullptr, status);
   return hipGetLastError();
 }
@@ -285,37 +300,50 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return bi < 0 || v > bv || (v == bv && i < bi);
 }
 
-__global__ void k_argmax(const float* __restrict__ logits, int vocab, const uint32_t* __restrict__ mask,
-                         int32_t* __restrict__ out, int32_t* status) {
-  __shared__ float sv[16];
-  __shared__ int si[16];
+constexpr int ARGMAX_THREADS = 1024;
+
+// One work-group per row; each thread takes whole 32-token mask words: the
+// word and its 32 logits (eight 16-byte loads, all in flight together) are
+// read unconditionally (indices clamped to the row) and the allowed ids are
+// compared in registers, in increasing id order.
+__global__ void __launch_bounds__(ARGMAX_THREADS) k_argmax(const float* __restrict__ logits, int vocab,
+                                                           const uint32_t* __restrict__ mask,
+                                                           int32_t* __restrict__ out, int32_t* status) {
+  __shared__ float sv[ARGMAX_THREADS / 64];
+  __shared__ int si[ARGMAX_THREADS / 64];
   const int r = blockIdx.x;
   const float* lg = logits + (int64_t)r * vocab;
   const int words = (vocab + 31) / 32;
+  const bool vec = (vocab & 3) == 0;  // rows 16-byte aligned: vector loads
   float bv = 0.f;
   int bi = -1;
-  if (mask) {
-    const uint32_t* mr = mask + (int64_t)r * words;
-    for (int w = threadIdx.x; w < words; w += blockDim.x) {
-      uint32_t bits = mr[w];
-      while (bits) {
-        const int j = __builtin_ctz(bits);
-        bits &= bits - 1;
-        const int v = w * 32 + j;
-        if (v < vocab && better(lg[v], v, bv, bi)) { bv = lg[v]; bi = v; }
+  for (int w = threadIdx.x; w < words; w += blockDim.x) {
+    const uint32_t bits = mask ? mask[(int64_t)r * words + w] : 0xFFFFFFFFu;
+    float x[32];
+    if (vec) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int v4 = min(w * 8 + j, vocab / 4 - 1);
+        const f32x4 t = *(const f32x4*)(lg + 4 * v4);
+        x[4 * j] = t[0], x[4 * j + 1] = t[1], x[4 * j + 2] = t[2], x[4 * j + 3] = t[3];
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) x[j] = lg[min(w * 32 + j, vocab - 1)];
     }
-  } else {
-    for (int v = threadIdx.x; v < vocab; v += blockDim.x)
-      if (better(lg[v], v, bv, bi)) { bv = lg[v]; bi = v; }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const int v = w * 32 + j;
+      if (((bits >> j) & 1u) && v < vocab && better(x[j], v, bv, bi)) { bv = x[j]; bi = v; }
+    }
   }
   for (int o = 32; o > 0; o >>= 1) {
     const float ov = __shfl_xor(bv, o);
     const int oi = __shfl_xor(bi, o);
     if (oi >= 0 && better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
   }
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  if (l == 0) { sv[w] = bv; si[w] = bi; }
+  const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
+  if (l == 0) { sv[wv] = bv; si[wv] = bi; }
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int i = 1; i < (int)(blockDim.x >> 6); ++i)
@@ -327,7 +355,8 @@ __global__ void k_argmax(const float* __restrict__ logits, int vocab, const uint
 
 hipError_t launch_argmax(const float* logits, int rows, int vocab, const uint32_t* mask,
                          int32_t* out, int32_t* status, hipStream_t s) {
-  hipLaunchKernelGGL(k_argmax, dim3(rows), dim3(ROW_THREADS), 0, s, logits, vocab, mask, out, status);
+  if (vocab <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_argmax, dim3(rows), dim3(ARGMAX_THREADS), 0, s, logits, vocab, mask, out, status);
   return hipGetLastError();
 }
 
