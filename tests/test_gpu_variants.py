@@ -211,27 +211,29 @@ def test_looped_screening_natural(looped):
 def test_looped_planted_full_depth_chain(looped):
     """Screening at full depth and a span planted from the oracle's own
     full-depth greedy chain: all N positions are accepted, and corrupting
-    position j stops acceptance exactly there."""
+    position j stops acceptance exactly there.  Each position's mask allows
+    the greedy id and only ids at least 0.5 below it, so every examined
+    position has a masked top-2 margin of at least 0.5 (random-init logits
+    rarely give eight clear margins in a row without one)."""
     dev = _dev()
     shape, W, W64, L, kl, vl, prompt, model = looped
     cfg = Config.of(shape)
     D, N = shape.loop_depth, 9
-    base = KVCache.from_prefix(kl.double().cpu().numpy(), vl.double().cpu().numpy(), L + N)
-    span = None
-    for head in (17, 4242, 31000, 2024, 777):
-        chain = base.copy()
-        s = [head]
-        lgs = []
-        for j in range(N):
-            lg = oracle.decode_step(cfg, W64, chain, L + j, s[j])[None]
-            lgs.append(lg[0])
-            if j + 1 < N:
-                s.append(int(oracle.masked_argmax(lg, None)[0]))
-        if (oracle.top2_margin(np.stack(lgs), None)[:N - 1] > MARGIN).all():
-            span = s
-            break
-    if span is None:
-        pytest.skip("no planted chain with all top-2 margins above 0.1 among the candidate heads")
+    chain = KVCache.from_prefix(kl.double().cpu().numpy(), vl.double().cpu().numpy(), L + N)
+    span = [17]
+    lgs = []
+    for j in range(N):
+        lg = oracle.decode_step(cfg, W64, chain, L + j, span[j])[None]
+        lgs.append(lg[0])
+        if j + 1 < N:
+            span.append(int(oracle.masked_argmax(lg, None)[0]))
+    lgs = np.stack(lgs)
+    allowed = lgs < lgs.max(axis=1, keepdims=True) - 0.5
+    allowed[np.arange(N), lgs.argmax(axis=1)] = True
+    mask = np.packbits(allowed, axis=1, bitorder="little").view("<u4")
+    assert (oracle.masked_argmax(lgs, mask)[:N - 1] == np.asarray(span[1:])).all()
+    assert (oracle.top2_margin(lgs, mask) >= 0.5).all()
+    mask_dev = torch.from_numpy(mask.view(np.int32).copy()).to(dev)
     for bad_at in (None, 3):
         sp = list(span)
         if bad_at is not None:
@@ -240,8 +242,12 @@ def test_looped_planted_full_depth_chain(looped):
         sa = torch.full((N,), -9, dtype=torch.int32, device=dev)
         sv = torch.full((1,), -9, dtype=torch.int32, device=dev)
         o = H.outputs(N, shape.vocab)
-        cad.cad_splice_forward_looped(model, kv, L, H.tensors_i32(sp), D, None, sa, sv, o["argmax"],
+        cad.cad_splice_forward_looped(model, kv, L, H.tensors_i32(sp), D, mask_dev, sa, sv, o["argmax"],
                                       o["accepted"], o["logits"], o["status"])
         torch.cuda.synchronize()
         want = N if bad_at is None else bad_at
+        assert int(o["status"][0]) == 0
+        print(f"looped planted: corrupt at {bad_at}: survivors {int(sv[0])} accepted {int(o['accepted'][0])}",
+              flush=True)
         assert int(sv[0]) == want and int(o["accepted"][0]) == want
+        assert (o["argmax"].cpu().numpy()[:want - 1] == np.asarray(span[1:want])).all()
