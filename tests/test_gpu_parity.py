@@ -134,6 +134,58 @@ def test_tiny_fp32_end_to_end():
     assert np.max(np.abs(seq_logits.cpu().numpy() - lseq)) <= TOL["f32"]
 
 
+def test_masked_argmax_edge_rows_fp32():
+    """Masked argmax on the device for a vocabulary that is neither a multiple
+    of 32 nor of 4 (1001 ids: a partial last mask word, scalar logit loads):
+    an empty row gives -1 and the empty-mask status bit, a single allowed id
+    (the last one, or a low one) is returned as is, set bits past the
+    vocabulary are ignored, and random rows match the oracle where the masked
+    top-2 margin clears the fp32 bar by far."""
+    dev = _dev()
+    shape = synth.Shape("tiny-v1001", 1, 256, 4, 4, 64, 1024, 1001, dtype="f32")
+    cfg = Config.of(shape)
+    Wc = synth.make_weights(shape, seed=0)
+    Wn = synth.weights_to_numpy(Wc)
+    Wd = {k: (v.to(dev) if torch.is_tensor(v) else [{kk: vv.to(dev) for kk, vv in lw.items()} for lw in v])
+          for k, v in Wc.items()}
+    L, N, V = 64, 8, shape.vocab
+    words = (V + 31) // 32
+    prompt = synth.uniform_prompt(L, V)
+    span = prompt[10:10 + N].copy()
+    allowed = np.random.default_rng(5).random((N, words * 32)) < 0.5
+    allowed[0] = False                      # empty row
+    allowed[1] = False
+    allowed[1, V - 1] = True                # only the last id
+    allowed[2] = False
+    allowed[2, 7] = True                    # only a low id
+    allowed[3] = False
+    allowed[3, 992:] = True                 # the last word, bits past V set too
+    mask = np.packbits(allowed, axis=1, bitorder="little").view("<u4").copy()
+    nb = (L + N + 15) // 16
+    kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device=dev)
+    model = cad.cad_model_create(shape, Wd, max_tokens=L)
+    o = H.outputs(L, V)
+    cad.cad_splice_forward(model, kv, 0, H.tensors_i32(prompt), None, cad.CAD_COMMIT, o["argmax"],
+                           o["accepted"], o["logits"], o["status"])
+    o2 = H.outputs(N, V)
+    cad.cad_splice_forward(model, kv, L, H.tensors_i32(span), torch.from_numpy(mask.view(np.int32)).to(dev),
+                           cad.CAD_COMMIT, o2["argmax"], o2["accepted"], o2["logits"], o2["status"])
+    okv = KVCache.empty(1, 4, L + N, 64)
+    oracle.prefill(cfg, Wn, okv, prompt)
+    ls = oracle.splice(cfg, Wn, okv, L, span)
+    torch.cuda.synchronize()
+    assert int(o["status"][0]) == 0
+    assert np.max(np.abs(o2["logits"].cpu().numpy() - ls)) <= TOL["f32"]
+    a = o2["argmax"].cpu().numpy()
+    assert a[0] == -1 and a[1] == V - 1 and a[2] == 7
+    assert int(o2["status"][0]) == 2 and int(o2["accepted"][0]) == N
+    a_ref = oracle.masked_argmax(ls, mask)
+    sure = oracle.top2_margin(ls, mask) > 1e-3
+    assert a_ref[0] == -1 and a_ref[1] == V - 1 and a_ref[2] == 7
+    assert np.array_equal(a[3:][sure[3:]], a_ref[3:][sure[3:]])
+    assert sure[3:].sum() >= 4
+
+
 def test_tiny_fp32_planted_verify():
     """VERIFY accepts a span planted from the oracle's greedy chain whole and
     stops exactly at a corrupted position."""
