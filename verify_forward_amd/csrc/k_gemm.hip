@@ -247,8 +247,8 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& a, int n_tn, int
   constexpr int NT = 64 * NW;       // threads
   constexpr int TM = 16 * MB * NW;  // activation rows per tile (MB 16-row blocks per wave)
   constexpr int NB = TN / 16;       // 16-row weight blocks (every wave covers all of them)
-  constexpr int WCH = TN * 4 / NT;  // 16-byte weight chunks per thread per k step
-  static_assert(WCH >= 1 && TN * 4 % NT == 0, "weight staging must cover the tile exactly");
+  constexpr int WCH = (TN * 4 + NT - 1) / NT;  // 16-byte weight chunks per thread per k step
+  static_assert(TN % 32 == 0, "whole gate/up block pairs");
   __shared__ __attribute__((aligned(16))) bf16_t sw[3][TN * WLD];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -262,7 +262,10 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& a, int n_tn, int
   int wsoff[WCH];
 #pragma unroll
   for (int i = 0; i < WCH; ++i) {
-    const int c = tid + NT * i;
+    // when the tile's chunks do not divide evenly, the threads past the last
+    // chunk load and store the last one again (same data, same place), so
+    // every load and store stays unconditional
+    const int c = min(tid + NT * i, TN * 4 - 1);
     const int row = c >> 2, col = (c & 3) * 8;
     wsoff[i] = row * WLD + col;
     int64_t wr;
@@ -492,10 +495,14 @@ __device__ __forceinline__ void gemm_reduce_body(const GemmArgs& a, int splits) 
 
 // Tiled shapes: eight waves (two per SIMD) of 256 weight rows x 256
 // activation rows, and four waves of 256 x 128 for spans of at most 128 rows.
+// The eight-wave gate/up kernel takes 224 weight rows (112 gate + 112 up
+// columns): 14336 columns then make 128 tiles per 256 activation rows, so
+// two row tiles fill the 256 CUs exactly (256-row tiles left 32 idle).
 constexpr int TILE_N = 256;
+constexpr int tile_n8(int epi) { return epi == EPI_SWIGLU ? 224 : TILE_N; }
 #define CAD_GEMM_KERNELS(NAME, EPI)                                                        \
   __global__ void __launch_bounds__(512) k_gemm_##NAME(GemmArgs a, int n_tn, int n_tm, int splits) { \
-    gemm_tiled_body<EPI, TILE_N, 8, 2>(a, n_tn, n_tm, splits);                             \
+    gemm_tiled_body<EPI, tile_n8(EPI), 8, 2>(a, n_tn, n_tm, splits);                       \
   }                                                                                        \
   __global__ void __launch_bounds__(256) k_gemm4_##NAME(GemmArgs a, int n_tn, int n_tm, int splits) { \
     gemm_tiled_body<EPI, TILE_N, 4, 2>(a, n_tn, n_tm, splits);                             \
@@ -547,7 +554,8 @@ static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled8, Tiled
   } else {
     const bool small = a.M <= 128;
     const int tm_rows = small ? 128 : 256;
-    const int cols_per_tile = (EPI == EPI_SWIGLU) ? TILE_N / 2 : TILE_N;
+    const int tn = small ? TILE_N : tile_n8(EPI);
+    const int cols_per_tile = (EPI == EPI_SWIGLU) ? tn / 2 : tn;
     const int n_tn = (a.N + cols_per_tile - 1) / cols_per_tile, n_tm = (a.M + tm_rows - 1) / tm_rows;
     const int tiles = n_tn * n_tm, nk = a.K / TK;
     // one work-group per CU at a time: split K while the split tiles still
