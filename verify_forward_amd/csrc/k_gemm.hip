@@ -497,12 +497,14 @@ __device__ __forceinline__ void gemm_reduce_body(const GemmArgs& a, int splits) 
 // activation rows, and four waves of 256 x 128 for spans of at most 128 rows.
 // The eight-wave gate/up kernel takes 224 weight rows (112 gate + 112 up
 // columns): 14336 columns then make 128 tiles per 256 activation rows, so
-// two row tiles fill the 256 CUs exactly (256-row tiles left 32 idle).
+// two row tiles fill the 256 CUs exactly (256-row tiles left 32 idle); the
+// QKV kernel takes 192 (6144 rows: 32 tiles, four k splits of two row tiles
+// fill the CUs, where 256-row tiles with five splits left 16 idle).
 constexpr int TILE_N = 256;
-constexpr int tile_n8(int epi) { return epi == EPI_SWIGLU ? 224 : TILE_N; }
-#define CAD_GEMM_KERNELS(NAME, EPI)                                                        \
+constexpr int TN8_GATE_UP = 224, TN8_QKV = 192;
+#define CAD_GEMM_KERNELS(NAME, EPI, TN8)                                                   \
   __global__ void __launch_bounds__(512) k_gemm_##NAME(GemmArgs a, int n_tn, int n_tm, int splits) { \
-    gemm_tiled_body<EPI, tile_n8(EPI), 8, 2>(a, n_tn, n_tm, splits);                       \
+    gemm_tiled_body<EPI, TN8, 8, 2>(a, n_tn, n_tm, splits);                                \
   }                                                                                        \
   __global__ void __launch_bounds__(256) k_gemm4_##NAME(GemmArgs a, int n_tn, int n_tm, int splits) { \
     gemm_tiled_body<EPI, TILE_N, 4, 2>(a, n_tn, n_tm, splits);                             \
@@ -515,11 +517,11 @@ constexpr int tile_n8(int epi) { return epi == EPI_SWIGLU ? 224 : TILE_N; }
   }                                                                                        \
   __global__ void __launch_bounds__(256) k_gemm_f32_##NAME(GemmArgs a) { gemm_f32_body<EPI>(a); }
 
-CAD_GEMM_KERNELS(qkv, EPI_STORE_F32)
-CAD_GEMM_KERNELS(o, EPI_RESID)
-CAD_GEMM_KERNELS(gate_up, EPI_SWIGLU)
-CAD_GEMM_KERNELS(down, EPI_RESID)
-CAD_GEMM_KERNELS(lm_head, EPI_STORE_F32)
+CAD_GEMM_KERNELS(qkv, EPI_STORE_F32, TN8_QKV)
+CAD_GEMM_KERNELS(o, EPI_RESID, TILE_N)
+CAD_GEMM_KERNELS(gate_up, EPI_SWIGLU, TN8_GATE_UP)
+CAD_GEMM_KERNELS(down, EPI_RESID, TILE_N)
+CAD_GEMM_KERNELS(lm_head, EPI_STORE_F32, TILE_N)
 #undef CAD_GEMM_KERNELS
 
 typedef void (*TiledFn)(GemmArgs, int, int, int);
@@ -531,7 +533,7 @@ typedef void (*PlainFn)(GemmArgs);
 // may be left as *partials fp32 planes [split][M][N] in a.split_ws for the
 // consumer to add (in split order); *partials = 0 when the epilogue ran.
 template <int EPI>
-static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled8, TiledFn tiled4, ReduceFn reduce,
+static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled8, int tn8, TiledFn tiled4, ReduceFn reduce,
                              SkinnyFn skinny, PlainFn f32, int* partials, hipStream_t s) {
   if (partials) *partials = 0;
   const bool leave = partials != nullptr && EPI != EPI_SWIGLU && a.split_ws != nullptr && a.N % 4 == 0;
@@ -554,7 +556,7 @@ static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled8, Tiled
   } else {
     const bool small = a.M <= 128;
     const int tm_rows = small ? 128 : 256;
-    const int tn = small ? TILE_N : tile_n8(EPI);
+    const int tn = small ? TILE_N : tn8;
     const int cols_per_tile = (EPI == EPI_SWIGLU) ? tn / 2 : tn;
     const int n_tn = (a.N + cols_per_tile - 1) / cols_per_tile, n_tm = (a.M + tm_rows - 1) / tm_rows;
     const int tiles = n_tn * n_tm, nk = a.K / TK;
@@ -582,14 +584,14 @@ static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled8, Tiled
 
 hipError_t launch_gemm(int dtype, int role, const GemmArgs& a, hipStream_t s, int* partials) {
   switch (role) {
-#define CAD_LAUNCH(EPI, NAME) \
-  launch_epi<EPI>(dtype, a, k_gemm_##NAME, k_gemm4_##NAME, k_gemm_reduce_##NAME, k_gemv_##NAME, k_gemm_f32_##NAME, \
-                  partials, s)
-    case GEMM_QKV: return CAD_LAUNCH(EPI_STORE_F32, qkv);
-    case GEMM_O: return CAD_LAUNCH(EPI_RESID, o);
-    case GEMM_GATE_UP: return CAD_LAUNCH(EPI_SWIGLU, gate_up);
-    case GEMM_DOWN: return CAD_LAUNCH(EPI_RESID, down);
-    default: return CAD_LAUNCH(EPI_STORE_F32, lm_head);
+#define CAD_LAUNCH(EPI, NAME, TN8) \
+  launch_epi<EPI>(dtype, a, k_gemm_##NAME, TN8, k_gemm4_##NAME, k_gemm_reduce_##NAME, k_gemv_##NAME, \
+                  k_gemm_f32_##NAME, partials, s)
+    case GEMM_QKV: return CAD_LAUNCH(EPI_STORE_F32, qkv, TN8_QKV);
+    case GEMM_O: return CAD_LAUNCH(EPI_RESID, o, TILE_N);
+    case GEMM_GATE_UP: return CAD_LAUNCH(EPI_SWIGLU, gate_up, TN8_GATE_UP);
+    case GEMM_DOWN: return CAD_LAUNCH(EPI_RESID, down, TILE_N);
+    default: return CAD_LAUNCH(EPI_STORE_F32, lm_head, TILE_N);
 #undef CAD_LAUNCH
   }
 }
