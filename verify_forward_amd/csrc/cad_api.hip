@@ -154,10 +154,9 @@ int64_t max_parts_rows(const cad_config& c) {
   // largest n_parts * rows over every row count a call may carry
   int64_t best = 0;
   for (int r = 1; r <= c.max_tokens; ++r) {
-    int len = 0;
     // both tile shapes: one sequence, and r one-row sequences
-    const int p1 = attention_parts(r, 1, c.n_q_heads, c.n_kv_heads, (int64_t)1 << 40, &len) + 1;
-    const int p2 = attention_parts(r, r, c.n_q_heads, c.n_kv_heads, (int64_t)1 << 40, &len) + 1;
+    const int p1 = attention_parts(r, 1, c.n_q_heads, c.n_kv_heads, (int64_t)1 << 40);
+    const int p2 = attention_parts(r, r, c.n_q_heads, c.n_kv_heads, (int64_t)1 << 40);
     const int p = p1 > p2 ? p1 : p2;
     if ((int64_t)p * r > best) best = (int64_t)p * r;
   }
@@ -208,8 +207,8 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
   const int qkv_rows = (hq + 2 * hkv) * hd;
   int64_t max_L = 0;
   for (int b = 0; b < rm.n_seq; ++b) max_L = rm.L[b] > max_L ? rm.L[b] : max_L;
-  int part_len = 0;
-  const int n_parts = attention_parts(R, rm.n_seq, hq, hkv, max_L, &part_len) + 1;  // + the span partition
+  // partitions of each query tile's key axis (cached keys, then the span's own)
+  const int n_parts = attention_parts(R, rm.n_seq, hq, hkv, max_L);
   if ((int64_t)n_parts * R > m->part_cap)
     return fail(CAD_E_CAPACITY, "attention partitions %d x %d rows exceed the workspace", n_parts, R);
   if (c.dtype == CAD_BF16 && rm.pstart[rm.n_seq] > m->span_cap)
@@ -228,7 +227,7 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
     LAUNCH(PF_QKV, launch_gemm(c.dtype, GEMM_QKV, g, s, &qkv_parts));
     LAUNCH(PF_ROPE, launch_rope_append(c.dtype, m->qkv, m->split_ws, qkv_parts, R, hq, hkv, hd, m->freq, rm, v,
                                        write_limit, m->q, q_lo_plane(m), dev_status, s));
-    LAUNCH(PF_ATTN, launch_attention(c.dtype, m->q, q_lo_plane(m), R, hq, hkv, hd, rm, v, n_parts, part_len, m->part_o,
+    LAUNCH(PF_ATTN, launch_attention(c.dtype, m->q, q_lo_plane(m), R, hq, hkv, hd, rm, v, n_parts, m->part_o,
                                      m->part_ml, m->attn, lo_plane(m, m->attn, (int64_t)hq * hd), dev_status, s));
     if (c.dtype == CAD_BF16 && n_parts > 1)
       LAUNCH(PF_MERGE, launch_attention_merge(m->part_o, m->part_ml, n_parts, R, hq, hd, m->attn,

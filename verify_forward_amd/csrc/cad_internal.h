@@ -157,7 +157,7 @@ hipError_t launch_rope_append(int dtype, const float* qkv, const float* qkv_part
 // n_parts = cache partitions (keys < L, part_len each) + one span partition
 // q_lo: bf16 models, the half remainder plane of q (nullptr for fp32)
 hipError_t launch_attention(int dtype, const void* q, const void* q_lo, int rows, int hq, int hkv, int hd,
-                            const RowMap& rm, KVView kv, int n_parts, int part_len,
+                            const RowMap& rm, KVView kv, int n_parts,
                             float* part_o, float* part_ml, void* out, void* out_lo, int32_t* status,
                             hipStream_t s);
 // log-sum-exp merge of the key partitions (bf16 models, n_parts > 1), into bf16 planes
@@ -176,6 +176,6 @@ hipError_t launch_suffix_match(const int32_t* tokens, int64_t T, int max_n, int 
 
 // attention split: partitions of the cached keys (0 .. max L) so that small
 // spans still fill the chip; the span's own keys form one more partition
-int attention_parts(int rows, int n_seq, int hq, int hkv, int64_t max_cache_keys, int* part_len);
+int attention_parts(int rows, int n_seq, int hq, int hkv, int64_t max_cache_keys);
 
 }  // namespace cad

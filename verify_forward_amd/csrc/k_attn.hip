@@ -38,7 +38,7 @@ struct AttnArgs {
   RowMap rm;
   KVView kv;
   int32_t tstart[CAD_MAX_SEQS + 1];  // query tiles per sequence (CSR)
-  int n_parts, part_len;
+  int n_parts;
   float* part_o;   // [n_parts][rows * hq][hd]
   float* part_ml;  // [n_parts][rows * hq][2]
   void* out;       // [rows][hq * hd]: fp32 (fp32 models) or the bf16 hi plane (bf16 models)
@@ -131,15 +131,27 @@ k_attn_bf16(AttnArgs p) {
   const int q_first = tile * FA_QT;
   const int q_wave = q_first + wave * QPW;
   const bool wave_active = q_wave < R;
-  // keys of this work-group: [k_begin, k_end).  Partitions 0 .. n_parts - 2
-  // cover the cached keys 0 .. L - 1 (part_len each, a multiple of FA_KT) and
-  // read the paged bf16 cache; the last partition covers this call's own
-  // keys L .. and reads them from the half-precision span workspace.
+  // Keys of this work-group.  The key axis of a query tile is the cached
+  // keys 0 .. L - 1 (paged bf16 cache, TA tiles of 64 keys, the last one
+  // possibly short) followed by this call's own keys L .. causal_end - 1
+  // (half-precision span workspace, TB tiles).  The n_parts partitions take
+  // equal runs of these TA + TB tiles (to one tile); a partition's cached
+  // tiles are its segment A and its span tiles its segment B, each read from
+  // its own source.
   const int q_last = min(q_first + FA_QT, R) - 1;
   const int64_t causal_end = L + q_last / p.G + 1;
-  const bool span_part = part == p.n_parts - 1;
-  const int64_t k_begin = span_part ? L : (int64_t)part * p.part_len;
-  const int64_t k_end = span_part ? causal_end : min(k_begin + p.part_len, L);
+  const int64_t TA = (L + FA_KT - 1) / FA_KT, TB = (causal_end - L + FA_KT - 1) / FA_KT;
+  const int64_t t0 = (TA + TB) * part / p.n_parts, t1 = (TA + TB) * (part + 1) / p.n_parts;
+  const int64_t a_begin = min(t0, TA) * FA_KT;
+  const int64_t a_end = min(min(t1, TA) * FA_KT, L);
+  const int64_t b_begin = L + max(t0 - TA, (int64_t)0) * FA_KT;
+  const int64_t b_end = min(L + max(t1 - TA, (int64_t)0) * FA_KT, causal_end);
+  const int nA = (int)(min(t1, TA) - min(t0, TA));
+  const int n_tiles = (int)(t1 - t0);
+  auto tile_start = [&](int t) -> int64_t {
+    return t < nA ? a_begin + (int64_t)t * FA_KT : b_begin + (int64_t)(t - nA) * FA_KT;
+  };
+  auto tile_end = [&](int t) -> int64_t { return t < nA ? a_end : b_end; };
   // causal limit shared by every query of the wave (its first query's)
   const int64_t wave_min_last = L + q_wave / p.G;
 
@@ -152,7 +164,7 @@ k_attn_bf16(AttnArgs p) {
   constexpr int QLD = HD + 8;  // sQlo row stride (halves): conflict-free 16-row reads
   __shared__ __attribute__((aligned(16))) f16_t sQlo[QLO_LDS ? NW * QPW * QLD : 8];
   bool q_ok[QB];
-  int q_last_rel[QB];  // this lane's last visible key, relative to k_begin
+  int64_t q_last_key[QB];  // this lane's last visible key
   int64_t qrow[QB];
   u32x4 qf[QB][DS], qfl[QLO_LDS ? 1 : QB][DS];
 #pragma unroll
@@ -161,7 +173,7 @@ k_attn_bf16(AttnArgs p) {
     q_ok[qb] = qi < R;
     const int k_local = q_ok[qb] ? qi / p.G : 0;
     const int head = kvh * p.G + (q_ok[qb] ? qi % p.G : 0);
-    q_last_rel[qb] = (int)(L + k_local - k_begin);
+    q_last_key[qb] = L + k_local;
     qrow[qb] = (int64_t)(p.rm.start[b] + k_local) * p.hq + head;  // index of (row, head)
     const f16_t* qsrc = (const f16_t*)p.q + qrow[qb] * HD;
     const f16_t* qlsrc = (const f16_t*)p.q_lo + qrow[qb] * HD;
@@ -187,7 +199,6 @@ k_attn_bf16(AttnArgs p) {
   for (int qb = 0; qb < QB; ++qb) m_run[qb] = -1e30f, l_run[qb] = 0.f;
 
   const int32_t* table = p.kv.table + (int64_t)b * p.kv.max_blocks;
-  const int n_tiles = k_begin < k_end ? (int)((k_end - k_begin + FA_KT - 1) / FA_KT) : 0;
   // Staging: the threads of wave w copy cache block jb = w / (TPB / 64) of
   // each tile, so the block id is uniform over the wave (a scalar load).
   const int jb = __builtin_amdgcn_readfirstlane(tid / TPB);
@@ -204,14 +215,13 @@ k_attn_bf16(AttnArgs p) {
   // The load is unconditional (index clamped into the range, entry 0 for the
   // span part or an empty range) so that no path overwrites its register
   // while it is in flight; block_used says whether the tile reads the block.
-  const int blast = k_end > k_begin ? (int)((k_end - 1) / CAD_KV_BLOCK) : 0;
+  const int blast = a_end > a_begin ? (int)((a_end - 1) / CAD_KV_BLOCK) : 0;
   auto block_used = [&](int t) -> bool {
-    const int64_t first_key = k_begin + (int64_t)t * FA_KT + jb * CAD_KV_BLOCK;
-    return !span_part && t < n_tiles && first_key < k_end;
+    return t < nA && a_begin + (int64_t)t * FA_KT + jb * CAD_KV_BLOCK < a_end;
   };
   auto block_of = [&](int t) -> int32_t {
-    const int64_t first_key = k_begin + (int64_t)t * FA_KT + jb * CAD_KV_BLOCK;
-    const int bi = span_part ? 0 : min((int)(first_key / CAD_KV_BLOCK), blast);
+    const int64_t first_key = a_begin + (int64_t)t * FA_KT + jb * CAD_KV_BLOCK;
+    const int bi = t < nA ? min((int)(first_key / CAD_KV_BLOCK), blast) : 0;
     return table[min(bi + (lane >> 5), blast)];
   };
   // span workspace rows of this sequence: row pstart + (key - L)
@@ -220,15 +230,18 @@ k_attn_bf16(AttnArgs p) {
   const f16_t* span_v = p.kv.span_v;
   u32x4 rk[KCH], rv[VCH];
   int nvalid_pend = 0;  // valid keys of this wave's cache block in the staged tile
+  bool span_pend = false;  // the staged tile comes from the span workspace
   // Every load below reads valid memory (a clamped block, or the sequence's
   // 64-row padded workspace region) and is unconditional; out-of-range keys
   // are zeroed afterwards, so the waits for tile t + 1 never cover extra work.
-  auto gload = [&](int64_t kt, int32_t blkv, bool used) {
+  auto gload = [&](int t, int32_t blkv, bool used) {
+    const bool span_part = t >= nA;  // wave-uniform
     const int64_t bb = used ? __builtin_amdgcn_readlane(blkv, 0) : -1;
-    const int64_t k0 = kt + jb * CAD_KV_BLOCK;  // first key of this wave's block
+    const int64_t k0 = tile_start(t) + jb * CAD_KV_BLOCK;  // first key of this wave's block
     const bool ok = span_part || (bb >= 0 && bb < p.kv.num_blocks);
     if (!span_part && bb >= 0 && !ok && p.status && ct == 0) atomicOr(p.status, (int32_t)CAD_DEV_BAD_BLOCK);
-    const int64_t rem = k_end - k0;  // keys left in the range from k0 (clamped in 32-bit below)
+    span_pend = span_part;
+    const int64_t rem = tile_end(t) - k0;  // keys left in the segment from k0 (clamped in 32-bit below)
     nvalid_pend = !ok ? 0 : rem >= CAD_KV_BLOCK ? CAD_KV_BLOCK : rem > 0 ? (int)rem : 0;
     const bf16_t* kb = kbase + (ok && !span_part ? bb : 0) * kv_blk_stride;
     const bf16_t* vb = vbase + (ok && !span_part ? bb : 0) * kv_blk_stride;
@@ -278,7 +291,7 @@ k_attn_bf16(AttnArgs p) {
       const int c = ct + TPB * i;
       const int kin = c / (HD / 8), c8 = c % (HD / 8);
       const int key = jb * CAD_KV_BLOCK + kin;
-      *(u32x4*)(&sK[buf][key * KLD + c8 * 8]) = span_part ? rk[i] : bf16x8_to_f16x8(rk[i]);
+      *(u32x4*)(&sK[buf][key * KLD + c8 * 8]) = span_pend ? rk[i] : bf16x8_to_f16x8(rk[i]);
     }
 #pragma unroll
     for (int i = 0; i < VCH; ++i) {
@@ -288,7 +301,7 @@ k_attn_bf16(AttnArgs p) {
       // + 16 (jb & 1) + 8 hf + e) key 16 h + 4 j + r sits at column 8 j + 4 h
       // + r: the eight columns 8 j .. 8 j + 7 then hold keys 4 j .. 4 j + 3
       // and 16 + 4 j .. 16 + 4 j + 3, the keys lane group j holds in S^T.
-      const u32x4 h = span_part ? rv[i] : bf16x8_to_f16x8(rv[i]);
+      const u32x4 h = span_pend ? rv[i] : bf16x8_to_f16x8(rv[i]);
       const int col = (jb >> 1) * 32 + 16 * hf + 4 * (jb & 1);
       f16_t* row = &sV[buf][d * VLD + col];
       *(u32x2*)(row) = u32x2{h[0], h[1]};      // e = 0..3 -> j = 2 hf
@@ -302,16 +315,16 @@ k_attn_bf16(AttnArgs p) {
   // ids run one more tile ahead.
   int32_t blk = block_of(0);
   if (n_tiles > 0) {
-    gload(k_begin, blk, block_used(0));
+    gload(0, blk, block_used(0));
     sstore(0);
   }
   blk = block_of(1);
   __syncthreads();
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
-    const int64_t kt = k_begin + (int64_t)t * FA_KT;
+    const int64_t kt = tile_start(t);
     const bool more = t + 1 < n_tiles;
-    if (more) gload(kt + FA_KT, blk, block_used(t + 1));
+    if (more) gload(t + 1, blk, block_used(t + 1));
     const int32_t blk_next = block_of(t + 2);
     if (wave_active) {
       // ---- S^T = K Q^T for four 16-key blocks x two 16-query blocks ----
@@ -338,14 +351,14 @@ k_attn_bf16(AttnArgs p) {
         }
       }
       // lane holds S[query (qb, i16)][key kt + 16 kb + 4 g4 + r]
-      const int end_rel = (int)min<int64_t>(k_end - kt, FA_KT);
+      const int end_rel = (int)min<int64_t>(tile_end(t) - kt, FA_KT);
       const bool need_mask = kt + FA_KT - 1 > wave_min_last || end_rel < FA_KT;
       float mx[QB];
       bool grow = false;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         if (need_mask) {
-          const int lim = max(min(q_last_rel[qb] - t * FA_KT + 1, end_rel), 0);
+          const int lim = (int)max<int64_t>(min<int64_t>(q_last_key[qb] - kt + 1, end_rel), 0);
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -571,32 +584,24 @@ k_attn_f32(AttnArgs p, int hd) {
   }
 }
 
-int attention_parts(int rows, int n_seq, int hq, int hkv, int64_t max_cache_keys, int* part_len) {
-  // partitions of the cached keys: about one work-group per compute unit
-  // (256 CUs; two for the four-wave shape) together with the query tiles,
-  // at least 256 keys each
+int attention_parts(int rows, int n_seq, int hq, int hkv, int64_t max_cache_keys) {
+  // partitions of each query tile's key axis: about one work-group per
+  // compute unit (256 CUs; two for the four-wave shape) together with the
+  // query tiles, at least 256 cached keys each, at least one
   const int G = hq / hkv;
   const int qt = attn_qt(rows * G, n_seq);
   const int tiles = (rows * G + qt - 1) / qt;
   const int base = hkv * tiles;
-  if (max_cache_keys <= 0) {
-    *part_len = FA_KT;
-    return 0;
-  }
   const int target = qt == 64 ? 512 : 256;
   int parts = (target + base - 1) / base;
-  const int64_t min_len = 256;
-  const int64_t cap = (max_cache_keys + min_len - 1) / min_len;
+  const int64_t cap = max_cache_keys / 256;
   if (parts > cap) parts = (int)cap;
-  if (parts < 1) parts = 1;
-  int64_t len = (max_cache_keys + parts - 1) / parts;
-  len = (len + FA_KT - 1) / FA_KT * FA_KT;
-  *part_len = (int)len;
-  return (int)((max_cache_keys + len - 1) / len);
+  if (parts > MERGE_MAX_PARTS) parts = MERGE_MAX_PARTS;
+  return parts < 1 ? 1 : parts;
 }
 
 hipError_t launch_attention(int dtype, const void* q, const void* q_lo, int rows, int hq, int hkv, int hd,
-                            const RowMap& rm, KVView kv, int n_parts, int part_len,
+                            const RowMap& rm, KVView kv, int n_parts,
                             float* part_o, float* part_ml, void* out, void* out_lo, int32_t* status,
                             hipStream_t s) {
   AttnArgs a;
@@ -609,7 +614,6 @@ hipError_t launch_attention(int dtype, const void* q, const void* q_lo, int rows
   a.rm = rm;
   a.kv = kv;
   a.n_parts = n_parts;
-  a.part_len = part_len;
   a.part_o = part_o;
   a.part_ml = part_ml;
   a.out = out;
