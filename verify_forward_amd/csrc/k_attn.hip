@@ -531,6 +531,44 @@ __global__ void __launch_bounds__(128 * MERGE_GROUPS) k_attn_merge(const float* 
   }
 }
 
+// The same merge for at most NP <= MERGE_SMALL partitions (long spans): one
+// thread per output element of four (row, head) pairs per work-group; each
+// thread loads every partition's (max, sum) and its own partial values at
+// once (no LDS, no barrier), forms the weights 2^(m_p - m) and adds the
+// partitions in order.
+constexpr int MERGE_SMALL = 16;
+template <int NP>
+__global__ void __launch_bounds__(512) k_attn_merge_small(const float* __restrict__ part_o,
+                                                          const float* __restrict__ part_ml, int n_parts,
+                                                          int64_t nq, int hd, bf16_t* __restrict__ out,
+                                                          bf16_t* __restrict__ out_lo) {
+  const int64_t qi = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 7);
+  const int d = threadIdx.x & 127;
+  if (qi >= nq || d >= hd) return;
+  float2 ml[NP];
+  float ov[NP];
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp) {
+    const int q = min(pp, n_parts - 1);
+    ml[pp] = *(const float2*)(part_ml + ((int64_t)q * nq + qi) * 2);
+    ov[pp] = part_o[((int64_t)q * nq + qi) * hd + d];
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp)
+    if (pp < n_parts && ml[pp].y > 0.f) m = fmaxf(m, ml[pp].x);
+  float den = 0.f, num = 0.f;
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp) {
+    if (pp < n_parts && ml[pp].y > 0.f) {
+      const float w = exp2f(ml[pp].x - m);
+      den += w * ml[pp].y;
+      num += w * ov[pp];
+    }
+  }
+  split_bf16(den > 0.f ? num / den : 0.f, out[qi * hd + d], out_lo[qi * hd + d]);
+}
+
 // ---------------------------------------------------------------------------
 // fp32 path
 // ---------------------------------------------------------------------------
@@ -649,6 +687,19 @@ hipError_t launch_attention_merge(const float* part_o, const float* part_ml, int
                                   int hq, int hd, void* out, void* out_lo, hipStream_t s) {
   const int64_t nq = (int64_t)rows * hq;
   if (n_parts > MERGE_MAX_PARTS || hd > 128) return hipErrorInvalidValue;
+  if (n_parts <= MERGE_SMALL) {
+    const dim3 grid((unsigned)((nq + 3) / 4));
+    if (n_parts <= 4)
+      hipLaunchKernelGGL(k_attn_merge_small<4>, grid, dim3(512), 0, s, part_o, part_ml, n_parts, nq, hd,
+                         (bf16_t*)out, (bf16_t*)out_lo);
+    else if (n_parts <= 8)
+      hipLaunchKernelGGL(k_attn_merge_small<8>, grid, dim3(512), 0, s, part_o, part_ml, n_parts, nq, hd,
+                         (bf16_t*)out, (bf16_t*)out_lo);
+    else
+      hipLaunchKernelGGL(k_attn_merge_small<16>, grid, dim3(512), 0, s, part_o, part_ml, n_parts, nq, hd,
+                         (bf16_t*)out, (bf16_t*)out_lo);
+    return hipGetLastError();
+  }
   const int groups = n_parts >= 16 ? MERGE_GROUPS : 1;
   hipLaunchKernelGGL(k_attn_merge, dim3((unsigned)nq), dim3(128 * groups), 0, s, part_o, part_ml, n_parts, nq, hd,
                      (bf16_t*)out, (bf16_t*)out_lo);
