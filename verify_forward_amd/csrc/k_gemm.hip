@@ -231,15 +231,20 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& a, int n_rg, in
 constexpr int TK = 32;         // k per pipeline step (one MFMA k-slice)
 constexpr int WLD = TK + 8;    // LDS row stride of a weight stage (80 bytes: 16-row fragment reads hit distinct banks)
 
-// Work-group -> (weight tile tn, activation tile tm, k split), weight tile
-// fastest: work-groups that share a weight tile are n_tn apart, which puts
-// them on the same XCD (work-groups are dealt to the eight XCDs round-robin)
-// whenever n_tn is a multiple of eight.
-__device__ __forceinline__ void gemm_tile_of(int n_tn, int n_tm, int& tn, int& tm, int& sp) {
+// Work-group -> (weight tile tn, activation tile tm, k split).  Work-groups
+// are dealt to the eight XCDs round-robin (id % 8); when their count is a
+// multiple of eight, each XCD takes a contiguous block of the order (split
+// slowest, then weight tile, activation tile fastest), so the work-groups
+// that read one k range of the activations, and those that read one weight
+// tile, sit behind the same L2 (with eight splits of 32 tiles, one split
+// per XCD: each operand piece comes from HBM once).
+__device__ __forceinline__ void gemm_tile_of(int n_tn, int n_tm, int splits, int& tn, int& tm, int& sp) {
   const int id = blockIdx.x;
-  tn = id % n_tn;
-  tm = (id / n_tn) % n_tm;
-  sp = id / (n_tn * n_tm);
+  const int total = n_tn * n_tm * splits;
+  const int q = total % 8 == 0 ? (id % 8) * (total / 8) + id / 8 : id;
+  tm = q % n_tm;
+  tn = (q / n_tm) % n_tn;
+  sp = q / (n_tm * n_tn);
 }
 
 template <int EPI, int TN, int NW, int MB>
@@ -254,7 +259,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& a, int n_tn, int
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, i16 = lane & 15;
   int tn, tm, sp;
-  gemm_tile_of(n_tn, n_tm, tn, tm, sp);
+  gemm_tile_of(n_tn, n_tm, splits, tn, tm, sp);
   const bf16_t* W = (const bf16_t*)a.W;
 
   // weight staging: chunk c = tid + NT*i is 16 bytes (8 k) of tile row c/4
