@@ -232,16 +232,17 @@ constexpr int TK = 32;         // k per pipeline step (one MFMA k-slice)
 constexpr int WLD = TK + 8;    // LDS row stride of a weight stage (80 bytes: 16-row fragment reads hit distinct banks)
 
 // Work-group -> (weight tile tn, activation tile tm, k split).  Work-groups
-// are dealt to the eight XCDs round-robin (id % 8); when their count is a
-// multiple of eight, each XCD takes a contiguous block of the order (split
-// slowest, then weight tile, activation tile fastest), so the work-groups
-// that read one k range of the activations, and those that read one weight
-// tile, sit behind the same L2 (with eight splits of 32 tiles, one split
-// per XCD: each operand piece comes from HBM once).
+// are dealt to the eight XCDs round-robin (id % 8); each XCD takes a
+// contiguous block of the order (split slowest, then weight tile,
+// activation tile fastest; the first total % 8 blocks one longer), so the
+// work-groups that read one k range of the activations, and those that read
+// one weight tile, sit behind the same L2 (with eight splits of 32 tiles,
+// one split per XCD: each operand piece comes from HBM once).
 __device__ __forceinline__ void gemm_tile_of(int n_tn, int n_tm, int splits, int& tn, int& tm, int& sp) {
   const int id = blockIdx.x;
   const int total = n_tn * n_tm * splits;
-  const int q = total % 8 == 0 ? (id % 8) * (total / 8) + id / 8 : id;
+  const int x = id % 8;
+  const int q = x * (total / 8) + min(x, total % 8) + id / 8;
   tm = q % n_tm;
   tn = (q / n_tm) % n_tn;
   sp = q / (n_tm * n_tn);
