@@ -499,21 +499,22 @@ __device__ __forceinline__ void gemm_reduce_body(const GemmArgs& a, int splits) 
   epi4<EPI, true>(a, m, n, c, cu);
 }
 
-// Tiled shapes: eight waves (two per SIMD) of 256 weight rows x 256
-// activation rows, and four waves of 256 x 128 for spans of at most 128 rows.
-// The eight-wave gate/up kernel takes 224 weight rows (112 gate + 112 up
-// columns): 14336 columns then make 128 tiles per 256 activation rows, so
-// two row tiles fill the 256 CUs exactly (256-row tiles left 32 idle); the
-// QKV kernel takes 192 (6144 rows: 32 tiles, four k splits of two row tiles
-// fill the CUs, where 256-row tiles with five splits left 16 idle).
+// Tiled shapes: eight waves (two per SIMD) of 32 activation rows each (256
+// per tile), and for spans of 17-128 rows eight waves of 16 rows (128 per
+// tile; four waves of 32 rows left one wave per SIMD with nothing to hide
+// its latency).  Weight rows per tile: 256, except gate/up with 224 (112
+// gate + 112 up columns: 14336 columns make 128 tiles, so two row tiles
+// fill the 256 CUs exactly where 256-row tiles left 32 idle) and QKV with
+// 192 (6144 rows: 32 tiles; four k splits of two row tiles fill the CUs,
+// where 256-row tiles with five splits left 16 idle).
 constexpr int TILE_N = 256;
 constexpr int TN8_GATE_UP = 224, TN8_QKV = 192;
 #define CAD_GEMM_KERNELS(NAME, EPI, TN8)                                                   \
   __global__ void __launch_bounds__(512) k_gemm_##NAME(GemmArgs a, int n_tn, int n_tm, int splits) { \
     gemm_tiled_body<EPI, TN8, 8, 2>(a, n_tn, n_tm, splits);                                \
   }                                                                                        \
-  __global__ void __launch_bounds__(256) k_gemm4_##NAME(GemmArgs a, int n_tn, int n_tm, int splits) { \
-    gemm_tiled_body<EPI, TILE_N, 4, 2>(a, n_tn, n_tm, splits);                             \
+  __global__ void __launch_bounds__(512) k_gemm_s_##NAME(GemmArgs a, int n_tn, int n_tm, int splits) { \
+    gemm_tiled_body<EPI, TN8, 8, 1>(a, n_tn, n_tm, splits);                                \
   }                                                                                        \
   __global__ void __launch_bounds__(256) k_gemm_reduce_##NAME(GemmArgs a, int splits) {    \
     gemm_reduce_body<EPI>(a, splits);                                                      \
@@ -539,7 +540,7 @@ typedef void (*PlainFn)(GemmArgs);
 // may be left as *partials fp32 planes [split][M][N] in a.split_ws for the
 // consumer to add (in split order); *partials = 0 when the epilogue ran.
 template <int EPI>
-static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled8, int tn8, TiledFn tiled4, ReduceFn reduce,
+static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled8, int tn8, TiledFn tiled_s, ReduceFn reduce,
                              SkinnyFn skinny, PlainFn f32, int* partials, hipStream_t s) {
   if (partials) *partials = 0;
   const bool leave = partials != nullptr && EPI != EPI_SWIGLU && a.split_ws != nullptr && a.N % 4 == 0;
@@ -562,7 +563,7 @@ static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled8, int t
   } else {
     const bool small = a.M <= 128;
     const int tm_rows = small ? 128 : 256;
-    const int tn = small ? TILE_N : tn8;
+    const int tn = tn8;
     const int cols_per_tile = (EPI == EPI_SWIGLU) ? tn / 2 : tn;
     const int n_tn = (a.N + cols_per_tile - 1) / cols_per_tile, n_tm = (a.M + tm_rows - 1) / tm_rows;
     const int tiles = n_tn * n_tm, nk = a.K / TK;
@@ -574,7 +575,7 @@ static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled8, int t
     if (a.split_ws && a.N % 64 == 0)
       while (tiles * (splits + 1) <= 256 && nk / (splits + 1) >= 16 && split_floats * (splits + 1) <= GEMM_SPLIT_FLOATS)
         ++splits;
-    hipLaunchKernelGGL(small ? tiled4 : tiled8, dim3(tiles * splits), dim3(small ? 256 : 512), 0, s, a, n_tn, n_tm,
+    hipLaunchKernelGGL(small ? tiled_s : tiled8, dim3(tiles * splits), dim3(512), 0, s, a, n_tn, n_tm,
                        splits);
     if (splits > 1) {
       if (leave) {
@@ -591,7 +592,7 @@ static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled8, int t
 hipError_t launch_gemm(int dtype, int role, const GemmArgs& a, hipStream_t s, int* partials) {
   switch (role) {
 #define CAD_LAUNCH(EPI, NAME, TN8) \
-  launch_epi<EPI>(dtype, a, k_gemm_##NAME, TN8, k_gemm4_##NAME, k_gemm_reduce_##NAME, k_gemv_##NAME, \
+  launch_epi<EPI>(dtype, a, k_gemm_##NAME, TN8, k_gemm_s_##NAME, k_gemm_reduce_##NAME, k_gemv_##NAME, \
                   k_gemm_f32_##NAME, partials, s)
     case GEMM_QKV: return CAD_LAUNCH(EPI_STORE_F32, qkv, TN8_QKV);
     case GEMM_O: return CAD_LAUNCH(EPI_RESID, o, TILE_N);
