@@ -551,13 +551,18 @@ static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled8, int t
     const int nblk = (EPI == EPI_SWIGLU) ? (a.N + 7) / 8 : (a.N + 15) / 16;
     const int n_rg = (nblk + 3) / 4;
     const int nch = (a.K + SK_KC - 1) / SK_KC;
-    // about two work-groups per compute unit: split K (whole chunks) when
-    // the row groups alone are fewer
+    // when the consumer adds partial sums: one chunk per work-group (the
+    // most chunks the partial workspace holds, in whole-chunk splits) -- a
+    // work-group streaming a single chunk keeps the most loads in flight for
+    // its weights (measured: down at N = 1, 28 x 64 work-groups of one chunk
+    // ran at 5 TB/s, 8 x 64 of three or four chunks at 4.2)
     int splits = 1;
     if (leave)
-      while (n_rg * (splits + 1) <= 512 && splits + 1 <= nch &&
-             (int64_t)(splits + 1) * a.M * a.N <= GEMM_SPLIT_FLOATS)
-        ++splits;
+      for (int c = nch; c > 1; --c)
+        if (nch % c == 0 && (int64_t)c * a.M * a.N <= GEMM_SPLIT_FLOATS) {
+          splits = c;
+          break;
+        }
     hipLaunchKernelGGL(skinny, dim3(n_rg * splits), dim3(256), 0, s, a, n_rg, splits);
     if (splits > 1) *partials = splits;
   } else {

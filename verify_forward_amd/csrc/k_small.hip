@@ -50,16 +50,16 @@ hipError_t launch_embed(int dtype, const void* table, int vocab, int d, const in
 // models, split into bf16 hi / lo planes (the next projection's operands)
 // for bf16 models
 // ---------------------------------------------------------------------------
-template <typename T, bool SPLIT, int V4>
-__global__ void __launch_bounds__(ROW_THREADS) k_rmsnorm(float* __restrict__ x, const float* __restrict__ x_part,
-                                                         int n_part, int rows, const T* __restrict__ g, int d,
-                                                         float eps, void* __restrict__ out,
-                                                         void* __restrict__ out_lo) {
-  // each thread keeps up to V4 groups of four elements in registers: one
-  // pass over x, all loads issued before the reduction.  Pending k-split
-  // partial sums of the projection that last wrote x ([n_part][rows][d]) are
-  // added first, in split order, and x is written back.
-  __shared__ float red[ROW_THREADS / 64];
+template <typename T, bool SPLIT, int V4, int NT>
+__global__ void __launch_bounds__(NT) k_rmsnorm(float* __restrict__ x, const float* __restrict__ x_part,
+                                                int n_part, int rows, const T* __restrict__ g, int d,
+                                                float eps, void* __restrict__ out, void* __restrict__ out_lo) {
+  // each of the NT threads keeps up to V4 groups of four elements in
+  // registers: one pass over x, all loads issued before the reduction.
+  // Pending k-split partial sums of the projection that last wrote x
+  // ([n_part][rows][d], up to one plane per 512-wide k chunk) are added
+  // first, in split order, and x is written back.
+  __shared__ float red[NT / 64];
   const int r = blockIdx.x;
   float* xr = x + (int64_t)r * d;
   const int n4 = d / 4;
@@ -69,7 +69,7 @@ __global__ void __launch_bounds__(ROW_THREADS) k_rmsnorm(float* __restrict__ x, 
   // the reduction)
 #pragma unroll
   for (int j = 0; j < V4; ++j) {
-    const int i4 = threadIdx.x + j * ROW_THREADS;
+    const int i4 = threadIdx.x + j * NT;
     v[j] = i4 < n4 ? *(const f32x4*)(xr + 4 * i4) : f32x4{0.f, 0.f, 0.f, 0.f};
     const int c4 = min(i4, n4 - 1);
 #pragma unroll
@@ -78,7 +78,7 @@ __global__ void __launch_bounds__(ROW_THREADS) k_rmsnorm(float* __restrict__ x, 
   if (n_part > 0) {
     // PB partial planes per batch, all their loads in flight together
     // (indices clamped; the clamped repeats are not added)
-    constexpr int PB = V4 <= 2 ? 8 : 16 / V4;
+    constexpr int PB = NT >= 1024 ? 16 / V4 : (V4 <= 2 ? 8 : 16 / V4);
     for (int sp = 0; sp < n_part; sp += PB) {
       f32x4 t[PB][V4];
 #pragma unroll
@@ -86,7 +86,7 @@ __global__ void __launch_bounds__(ROW_THREADS) k_rmsnorm(float* __restrict__ x, 
         const float* pr = x_part + ((int64_t)min(sp + u, n_part - 1) * rows + r) * d;
 #pragma unroll
         for (int j = 0; j < V4; ++j) {
-          const int i4 = min(threadIdx.x + j * ROW_THREADS, n4 - 1);
+          const int i4 = min((int)threadIdx.x + j * NT, n4 - 1);
           t[u][j] = *(const f32x4*)(pr + 4 * i4);
         }
       }
@@ -98,7 +98,7 @@ __global__ void __launch_bounds__(ROW_THREADS) k_rmsnorm(float* __restrict__ x, 
     }
 #pragma unroll
     for (int j = 0; j < V4; ++j) {
-      const int i4 = threadIdx.x + j * ROW_THREADS;
+      const int i4 = threadIdx.x + j * NT;
       if (i4 < n4) *(f32x4*)(xr + 4 * i4) = v[j];
     }
   }
@@ -108,7 +108,7 @@ __global__ void __launch_bounds__(ROW_THREADS) k_rmsnorm(float* __restrict__ x, 
   const float rs = 1.0f / sqrtf(ss / (float)d + eps);
 #pragma unroll
   for (int j = 0; j < V4; ++j) {
-    const int i4 = threadIdx.x + j * ROW_THREADS;
+    const int i4 = threadIdx.x + j * NT;
     if (i4 >= n4) continue;
     const int i = 4 * i4;
     float y[4];
@@ -129,19 +129,24 @@ __global__ void __launch_bounds__(ROW_THREADS) k_rmsnorm(float* __restrict__ x, 
 
 hipError_t launch_rmsnorm(int dtype, float* x, const float* x_part, int n_part, const void* gain, int rows, int d,
                           float eps, void* out, void* out_lo, hipStream_t s) {
-  const int v4 = (d / 4 + ROW_THREADS - 1) / ROW_THREADS;
+  // few rows of 4096 and more (short spans, whose projections leave up to
+  // one partial plane per 512-wide k chunk): 1024 threads, one or two groups
+  // of four each, so that 16 / V4 planes are in flight at once; else 256
+  const int nt = (d >= 4096 && rows <= 64) ? 1024 : ROW_THREADS;
+  const int v4 = (d / 4 + nt - 1) / nt;
   if (d % 4 != 0 || v4 > 8 || (n_part > 0 && !x_part)) return hipErrorInvalidValue;
-#define CAD_RMS(V)                                                                                         \
-  if (v4 <= V) {                                                                                           \
+#define CAD_RMS(V, NT)                                                                                     \
+  if (v4 <= V && nt == NT) {                                                                               \
     if (dtype == CAD_BF16)                                                                                 \
-      hipLaunchKernelGGL((k_rmsnorm<bf16_t, true, V>), dim3(rows), dim3(ROW_THREADS), 0, s, x, x_part,     \
-                         n_part, rows, (const bf16_t*)gain, d, eps, out, out_lo);                          \
+      hipLaunchKernelGGL((k_rmsnorm<bf16_t, true, V, NT>), dim3(rows), dim3(NT), 0, s, x, x_part, n_part,  \
+                         rows, (const bf16_t*)gain, d, eps, out, out_lo);                                  \
     else                                                                                                   \
-      hipLaunchKernelGGL((k_rmsnorm<float, false, V>), dim3(rows), dim3(ROW_THREADS), 0, s, x, x_part,     \
-                         n_part, rows, (const float*)gain, d, eps, out, out_lo);                           \
+      hipLaunchKernelGGL((k_rmsnorm<float, false, V, NT>), dim3(rows), dim3(NT), 0, s, x, x_part, n_part,  \
+                         rows, (const float*)gain, d, eps, out, out_lo);                                   \
     return hipGetLastError();                                                                              \
   }
-  CAD_RMS(1) CAD_RMS(2) CAD_RMS(4) CAD_RMS(8)
+  CAD_RMS(1, 256) CAD_RMS(2, 256) CAD_RMS(4, 256) CAD_RMS(8, 256)
+  CAD_RMS(1, 1024) CAD_RMS(2, 1024) CAD_RMS(4, 1024) CAD_RMS(8, 1024)
 #undef CAD_RMS
   return hipErrorInvalidValue;
 }
