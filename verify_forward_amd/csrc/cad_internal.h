@@ -154,7 +154,8 @@ hipError_t launch_rope_append(int dtype, const float* qkv, const float* qkv_part
                               int hkv, int hd, const double* freq, const RowMap& rm, KVView kv,
                               const int32_t* write_limit, void* q_out, void* q_lo, int32_t* status,
                               hipStream_t s);
-// n_parts = cache partitions (keys < L, part_len each) + one span partition
+// n_parts = partitions of each query tile's key axis (its cached keys, then
+// the call's own keys), equal runs of 64-key tiles each
 // q_lo: bf16 models, the half remainder plane of q (nullptr for fp32)
 hipError_t launch_attention(int dtype, const void* q, const void* q_lo, int rows, int hq, int hkv, int hd,
                             const RowMap& rm, KVView kv, int n_parts,
@@ -174,8 +175,8 @@ hipError_t launch_suffix_match(const int32_t* tokens, int64_t T, int max_n, int 
                                int32_t* out_tokens, int32_t* out_len, int64_t* out_pos,
                                hipStream_t s);
 
-// attention split: partitions of the cached keys (0 .. max L) so that small
-// spans still fill the chip; the span's own keys form one more partition
+// attention split: partitions of each query tile's key axis (cached keys up
+// to max L, then the span's own) so that small spans still fill the chip
 int attention_parts(int rows, int n_seq, int hq, int hkv, int64_t max_cache_keys);
 
 }  // namespace cad

@@ -208,12 +208,12 @@ k_attn_bf16(AttnArgs p) {
   const bf16_t* vbase = (const bf16_t*)p.kv.v + (int64_t)kvh * CAD_KV_BLOCK * HD;
   // cache block of tile t for this wave (lane 0 of the result), or -1 when
   // the tile's part of the key range does not reach it (then nothing is
-  // read); unused by the span part.  Lanes 32..63 read the next block's id
+  // read); unused by span tiles.  Lanes 32..63 read the next block's id
   // (clamped to the range): the value is then not wave-uniform, stays in a
   // vector register, and the wait for it falls where lane 0 is read a tile
   // later instead of right after the load.
-  // The load is unconditional (index clamped into the range, entry 0 for the
-  // span part or an empty range) so that no path overwrites its register
+  // The load is unconditional (index clamped into the range, entry 0 for
+  // span tiles or an empty range) so that no path overwrites its register
   // while it is in flight; block_used says whether the tile reads the block.
   const int blast = a_end > a_begin ? (int)((a_end - 1) / CAD_KV_BLOCK) : 0;
   auto block_used = [&](int t) -> bool {
@@ -235,16 +235,16 @@ k_attn_bf16(AttnArgs p) {
   // 64-row padded workspace region) and is unconditional; out-of-range keys
   // are zeroed afterwards, so the waits for tile t + 1 never cover extra work.
   auto gload = [&](int t, int32_t blkv, bool used) {
-    const bool span_part = t >= nA;  // wave-uniform
+    const bool span_tile = t >= nA;  // wave-uniform
     const int64_t bb = used ? __builtin_amdgcn_readlane(blkv, 0) : -1;
     const int64_t k0 = tile_start(t) + jb * CAD_KV_BLOCK;  // first key of this wave's block
-    const bool ok = span_part || (bb >= 0 && bb < p.kv.num_blocks);
-    if (!span_part && bb >= 0 && !ok && p.status && ct == 0) atomicOr(p.status, (int32_t)CAD_DEV_BAD_BLOCK);
-    span_pend = span_part;
+    const bool ok = span_tile || (bb >= 0 && bb < p.kv.num_blocks);
+    if (!span_tile && bb >= 0 && !ok && p.status && ct == 0) atomicOr(p.status, (int32_t)CAD_DEV_BAD_BLOCK);
+    span_pend = span_tile;
     const int64_t rem = tile_end(t) - k0;  // keys left in the segment from k0 (clamped in 32-bit below)
     nvalid_pend = !ok ? 0 : rem >= CAD_KV_BLOCK ? CAD_KV_BLOCK : rem > 0 ? (int)rem : 0;
-    const bf16_t* kb = kbase + (ok && !span_part ? bb : 0) * kv_blk_stride;
-    const bf16_t* vb = vbase + (ok && !span_part ? bb : 0) * kv_blk_stride;
+    const bf16_t* kb = kbase + (ok && !span_tile ? bb : 0) * kv_blk_stride;
+    const bf16_t* vb = vbase + (ok && !span_tile ? bb : 0) * kv_blk_stride;
     const int64_t srow = span_row0 + (k0 - L);  // span workspace row of key k0
     // raw loads only: the registers are not touched again until sstore, so
     // the wait for them lands at the end of the tile, not right here
@@ -252,7 +252,7 @@ k_attn_bf16(AttnArgs p) {
     for (int i = 0; i < KCH; ++i) {
       const int c = ct + TPB * i;  // [16 keys][HD / 8 chunks]
       const int key = c / (HD / 8), c8 = c % (HD / 8);
-      const u32x4* src = span_part ? (const u32x4*)(span_k + ((srow + key) * p.hkv + kvh) * HD + c8 * 8)
+      const u32x4* src = span_tile ? (const u32x4*)(span_k + ((srow + key) * p.hkv + kvh) * HD + c8 * 8)
                                    : (const u32x4*)(kb + c * 8);
       rk[i] = *src;
     }
@@ -260,7 +260,7 @@ k_attn_bf16(AttnArgs p) {
     for (int i = 0; i < VCH; ++i) {
       const int c = ct + TPB * i;  // [HD rows][2 chunks of 8 tokens]
       const int d = c >> 1, hf = c & 1;
-      const u32x4* src = span_part
+      const u32x4* src = span_tile
                              ? (const u32x4*)(span_v + ((int64_t)kvh * HD + d) * p.kv.span_cap + srow + 8 * hf)
                              : (const u32x4*)(vb + c * 8);
       rv[i] = *src;
