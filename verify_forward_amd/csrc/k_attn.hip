@@ -105,8 +105,10 @@ k_attn_bf16(AttnArgs p) {
   constexpr int FA_NT = 64 * NW;            // threads per work-group
   constexpr int QPW = 16 * QB;              // query rows per wave (QB 16-column blocks)
   constexpr int FA_QT = QPW * NW;           // query rows per work-group
-  constexpr int KLD = HD + 8;          // sK row stride (halves): 16 B pad keeps 16-row reads conflict-free
-  constexpr int VLD = FA_KT + 8;       // sV row stride (halves)
+  // LDS row strides (halves) with 32 bytes of padding (measured 2 % faster
+  // than 16 bytes for the eight-wave shape)
+  constexpr int KLD = HD + 16;         // sK
+  constexpr int VLD = FA_KT + 16;      // sV
   constexpr int DS = HD / 32;          // k steps of S^T = K Q^T
   constexpr int DB = HD / 16;          // 16-row d blocks of O^T
   constexpr int TBLK = FA_KT / CAD_KV_BLOCK;   // cache blocks per tile
@@ -161,7 +163,7 @@ k_attn_bf16(AttnArgs p) {
   // registers; the lo fragments too with one query block per wave, and in
   // LDS (read only by this wave) with two.
   constexpr bool QLO_LDS = QB >= 2;
-  constexpr int QLD = HD + 8;  // sQlo row stride (halves): conflict-free 16-row reads
+  constexpr int QLD = HD + 16;  // sQlo row stride (halves)
   __shared__ __attribute__((aligned(16))) f16_t sQlo[QLO_LDS ? NW * QPW * QLD : 8];
   bool q_ok[QB];
   int64_t q_last_key[QB];  // this lane's last visible key
