@@ -95,6 +95,7 @@ struct cad_model {
   f16_t* span_v = nullptr;
   int32_t span_cap = 0;          // rows of the span workspace
   float* split_ws = nullptr;     // split-K partial sums of the projections (bf16 models)
+  float* norm_ss = nullptr;      // [16][d / 256] slice sums of squares (bf16 models, few rows)
   int x_parts = 0;               // partial planes in split_ws still to be added to x
 };
 
@@ -198,6 +199,38 @@ void* q_lo_plane(const cad_model* m) {
   return c.dtype == CAD_BF16 ? (void*)((f16_t*)m->q + (int64_t)c.max_tokens * c.n_q_heads * c.head_dim) : nullptr;
 }
 
+// RMSNorm (with gain `gain`) of the R rows of the residual stream, after
+// adding the pending k-split partials, as the activation operand of the
+// projection described by g.  A bf16 model with at most
+// NORM_IN_PROJ_MAX_ROWS rows leaves the normalisation to the
+// weight-streaming projection (launch_rms_slices writes the slice sums of
+// squares; g carries the residual and the gain): every work-group of the
+// projection then normalises the rows it stages, which beats the one-row-
+// per-work-group norm kernel for a few rows (N = 1: 2.2 us saved per norm,
+// the projections about even) but not at 16 (each of the 448 gate/up
+// work-groups repeats the work for 16 rows).  Otherwise the full kernel
+// writes the hi/lo planes.
+constexpr int NORM_IN_PROJ_MAX_ROWS = 8;
+hipError_t launch_norm(cad_model* m, const void* gain, int R, GemmArgs& g, hipStream_t s) {
+  const cad_config& c = m->cfg;
+  const int np = m->x_parts;
+  m->x_parts = 0;
+  g.lda = c.d_model;
+  if (c.dtype == CAD_BF16 && R <= NORM_IN_PROJ_MAX_ROWS && aligned16(gain)) {
+    g.A = m->x;
+    g.A_lo = nullptr;
+    g.norm_g = gain;
+    g.norm_ss = m->norm_ss;
+    g.norm_slices = rms_slices(c.d_model);
+    g.norm_eps = c.rms_eps;
+    return launch_rms_slices(m->x, m->split_ws, np, R, c.d_model, m->norm_ss, s);
+  }
+  g.A = m->hn;
+  g.A_lo = lo_plane(m, m->hn, c.d_model);
+  return launch_rmsnorm(c.dtype, m->x, m->split_ws, np, gain, R, c.d_model, c.rms_eps, m->hn,
+                        lo_plane(m, m->hn, c.d_model), s);
+}
+
 // Run cache indices [c0, c1) over the rows already embedded in m->x.
 cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, int c1,
                       const int32_t* write_limit, int32_t* dev_status, hipStream_t s) {
@@ -216,11 +249,9 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
   for (int ci = c0; ci < c1; ++ci) {
     const int li = c.loop_depth > 1 ? 0 : ci;
     const KVView v = view_of(m, kv, ci);
-    LAUNCH(PF_NORM, launch_rmsnorm(c.dtype, m->x, m->split_ws, m->x_parts, m->attn_norm[li], R, d, c.rms_eps,
-                                   m->hn, lo_plane(m, m->hn, d), s));
-    m->x_parts = 0;
     GemmArgs g{};
-    g.A = m->hn; g.A_lo = lo_plane(m, m->hn, d); g.lda = d; g.W = m->w_qkv[li]; g.ldw = d;
+    LAUNCH(PF_NORM, launch_norm(m, m->attn_norm[li], R, g, s));
+    g.W = m->w_qkv[li]; g.ldw = d;
     g.M = R; g.N = qkv_rows; g.K = d; g.out_f32 = m->qkv; g.ldo = qkv_rows;
     g.split_ws = m->split_ws;
     int qkv_parts = 0;
@@ -238,11 +269,9 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
     g.M = R; g.N = d; g.K = hq * hd; g.out_f32 = m->x; g.ldo = d;
     g.split_ws = m->split_ws;
     LAUNCH(PF_O, launch_gemm(c.dtype, GEMM_O, g, s, &m->x_parts));
-    LAUNCH(PF_NORM, launch_rmsnorm(c.dtype, m->x, m->split_ws, m->x_parts, m->ffn_norm[li], R, d, c.rms_eps, m->hn,
-                                   lo_plane(m, m->hn, d), s));
-    m->x_parts = 0;
     g = GemmArgs{};
-    g.A = m->hn; g.A_lo = lo_plane(m, m->hn, d); g.lda = d; g.W = m->w_gate_up[li]; g.ldw = d;
+    LAUNCH(PF_NORM, launch_norm(m, m->ffn_norm[li], R, g, s));
+    g.W = m->w_gate_up[li]; g.ldw = d;
     g.M = R; g.N = F; g.K = d; g.up_off = F; g.out_act = m->act; g.out_act_lo = lo_plane(m, m->act, F);
     g.split_ws = m->split_ws;
     LAUNCH(PF_GATEUP, launch_gemm(c.dtype, GEMM_GATE_UP, g, s));
@@ -259,11 +288,9 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
 cad_status readout(cad_model* m, int R, float* logits, const uint32_t* mask, int32_t* argmax,
                    int32_t* dev_status, hipStream_t s) {
   const cad_config& c = m->cfg;
-  LAUNCH(PF_NORM, launch_rmsnorm(c.dtype, m->x, m->split_ws, m->x_parts, m->final_norm, R, c.d_model, c.rms_eps,
-                                 m->hn, lo_plane(m, m->hn, c.d_model), s));
-  m->x_parts = 0;
   GemmArgs g{};
-  g.A = m->hn; g.A_lo = lo_plane(m, m->hn, c.d_model); g.lda = c.d_model; g.W = m->lm_head; g.ldw = c.d_model;
+  LAUNCH(PF_NORM, launch_norm(m, m->final_norm, R, g, s));
+  g.W = m->lm_head; g.ldw = c.d_model;
   g.M = R; g.N = c.vocab; g.K = c.d_model; g.out_f32 = logits; g.ldo = c.vocab;
   g.split_ws = m->split_ws;
   LAUNCH(PF_HEAD, launch_gemm(c.dtype, GEMM_LM_HEAD, g, s));
@@ -345,6 +372,7 @@ cad_status cad_model_create(const cad_config* cfg, const cad_weights* w, cad_mod
   const int64_t span_cap = split ? (T + 64 * CAD_MAX_SEQS + 63) / 64 * 64 : 0;
   const size_t o_spk = take((size_t)span_cap * hkv * hd * 2), o_spv = take((size_t)span_cap * hkv * hd * 2);
   const size_t o_sws = take(split ? (size_t)GEMM_SPLIT_FLOATS * 4 : 0);
+  const size_t o_nss = take(split ? (size_t)16 * rms_slices((int)d) * 4 : 0);
   hipError_t e = hipMalloc(&m->ws, off);
   if (e != hipSuccess) {
     delete m;
@@ -370,6 +398,7 @@ cad_status cad_model_create(const cad_config* cfg, const cad_weights* w, cad_mod
     m->span_v = (f16_t*)(base + o_spv);
     m->span_cap = (int32_t)span_cap;
     m->split_ws = (float*)(base + o_sws);
+    m->norm_ss = (float*)(base + o_nss);
   }
   std::vector<double> fr(hd / 2);
   for (int64_t i = 0; i < hd / 2; ++i) fr[i] = std::pow((double)c.rope_theta, -2.0 * (double)i / (double)hd);

@@ -133,6 +133,14 @@ struct GemmArgs {
   void* out_act_lo;  // bf16 models: lo plane of the SWIGLU destination
   // split-K scratch (library workspace): fp32 partial sums [split][M][cols]
   float* split_ws;
+  // bf16 models, at most 16 rows: when norm_ss is set, A is the fp32
+  // residual stream [M][lda] and the projection normalises it while staging
+  // (RMSNorm with gain norm_g [K], bf16, and the slice sums of squares
+  // norm_ss [M][norm_slices] written by launch_rms_slices) into hi/lo planes
+  const void* norm_g;
+  const float* norm_ss;
+  int norm_slices;
+  float norm_eps;
 };
 
 // split-K workspace of the tiled GEMMs: GEMM_SPLIT_FLOATS floats (128 MB)
@@ -146,6 +154,11 @@ hipError_t launch_embed(int dtype, const void* table, int vocab, int d, const in
 // (added in order, x written back), then the norm
 hipError_t launch_rmsnorm(int dtype, float* x, const float* x_part, int n_part, const void* gain, int rows, int d,
                           float eps, void* out, void* out_lo, hipStream_t s);
+// few rows: x += the n_part partial planes (x written back) and the sums of
+// squares of 256-element slices to ss [rows][rms_slices(d)]; the
+// weight-streaming projection that follows applies the norm (GemmArgs.norm_*)
+hipError_t launch_rms_slices(float* x, const float* x_part, int n_part, int rows, int d, float* ss, hipStream_t s);
+int rms_slices(int d);
 // partials: see launch_epi; nullptr makes every launch apply its epilogue
 hipError_t launch_gemm(int dtype, int role, const GemmArgs& a, hipStream_t s, int* partials = nullptr);
 // qkv: [rows][width] fp32, or (n_part > 0) the sum of the partial planes

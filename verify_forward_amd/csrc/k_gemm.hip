@@ -97,7 +97,15 @@ constexpr int SK_ALD = SK_KC + 8;      // LDS row stride of the activation chunk
 constexpr int SK_WLD = SK_KC / 2 + 8;  // LDS row stride of a half-chunk weight transpose (528 B: conflict-free)
 constexpr int SK_AIT = 16 * 2 * (SK_KC / 8) / 256;  // 16-byte activation pieces per thread and chunk
 
-template <int EPI>
+// Staged activation registers of one chunk: the two bf16 planes (eight
+// 16-byte pieces per thread), or (NORM) four rows of eight fp32 residual
+// values (bits) and the eight matching gains; the normalised hi / lo pieces
+// of row j then replace its fp32 values in place (x[2j], x[2j + 1]), so the
+// stage costs four registers more than the plain one.
+template <bool NORM> struct SkStage { u32x4 r[SK_AIT]; };
+template <> struct SkStage<true> { u32x4 x[8]; u32x4 g; };
+
+template <int EPI, bool NORM>
 __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& a, int n_rg, int splits) {
   __shared__ __attribute__((aligned(16))) bf16_t sa[2][16 * SK_ALD];     // [plane][row][k]
   __shared__ __attribute__((aligned(16))) bf16_t swt[4][16 * SK_WLD];    // per-wave weight transpose
@@ -123,7 +131,9 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& a, int n_rg, in
   const int c0 = (int)((int64_t)nch * sp / splits), c1 = (int)((int64_t)nch * (sp + 1) / splits);
   // activation staging: piece q = tid + 256*j is 16 bytes: plane q / 1024,
   // row (q / 64) % 16, k offset 8 * (q % 64) within the chunk.  Rows >= M and
-  // k past K are written as zeros (their products vanish).
+  // k past K are written as zeros (their products vanish).  With NORM the
+  // thread holds the same pieces as fp32 values of rows wave + 4j (j < 4) and
+  // writes both planes of each.
   const bf16_t* ap[SK_AIT];
   int aoff[SK_AIT], akk[SK_AIT];
   bool aok[SK_AIT];
@@ -136,17 +146,76 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& a, int n_rg, in
     aok[j] = row < a.M;
     ap[j] = (const bf16_t*)(plane ? a.A_lo : a.A) + (int64_t)min(row, a.M - 1) * a.lda + kk;
   }
-  auto aload = [&](u32x4 (&r)[SK_AIT], int c) {
+  // NORM: 1 / rms of this thread's rows (wave + 4j).  Lane l loads slice
+  // sums l % 16 and l % 16 + 16 (at most 32 slices) of row wave + 4 (l / 16),
+  // all in one round trip; a fixed butterfly over the 16 lanes of a row adds
+  // them, and lane 16 j hands row j's result to the whole wave.
+  float rsj[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (NORM) {
+    const int u = lane & 15;
+    const float* ssr = a.norm_ss + (int64_t)min(wave + 4 * (lane >> 4), a.M - 1) * a.norm_slices;
+    float t = (u < a.norm_slices ? ssr[u] : 0.f) + (u + 16 < a.norm_slices ? ssr[u + 16] : 0.f);
 #pragma unroll
-    for (int j = 0; j < SK_AIT; ++j) r[j] = *(const u32x4*)(ap[j] + min(c * SK_KC, a.K - 8 - akk[j]));
+    for (int o = 1; o < 16; o <<= 1) t += __shfl_xor(t, o);
+    const float rs = 1.0f / sqrtf(t / (float)a.K + a.norm_eps);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rsj[j] = __shfl(rs, 16 * j);
+  }
+  auto aload = [&](SkStage<NORM>& st, int c) {
+    if constexpr (NORM) {
+      const int kk = 8 * lane;
+      const int off = min(c * SK_KC, a.K - 8 - kk);
+      st.g = *(const u32x4*)((const bf16_t*)a.norm_g + off + kk);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float* xp = (const float*)a.A + (int64_t)min(wave + 4 * j, a.M - 1) * a.lda + off + kk;
+        st.x[2 * j] = *(const u32x4*)xp;
+        st.x[2 * j + 1] = *(const u32x4*)(xp + 4);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < SK_AIT; ++j) st.r[j] = *(const u32x4*)(ap[j] + min(c * SK_KC, a.K - 8 - akk[j]));
+    }
+  };
+  // NORM: normalise and split the staged fp32 rows, in registers, before the
+  // barrier that guards the LDS store: row j's hi piece replaces x[2j] and
+  // its lo piece x[2j + 1]; rows >= M (whole waves) skip the work
+  auto prep = [&](SkStage<NORM>& st) {
+    if constexpr (NORM) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (wave + 4 * j >= a.M) continue;
+        u32x4 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bf16_t h2[2], l2[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int i = 2 * e + t;
+            const float xv = __uint_as_float(st.x[2 * j + i / 4][i % 4]);
+            const float gv = __uint_as_float((i & 1) ? (st.g[i / 2] & 0xFFFF0000u) : (st.g[i / 2] << 16));
+            split_bf16(xv * rsj[j] * gv, h2[t], l2[t]);
+          }
+          hi[e] = h2[0] | ((uint32_t)h2[1] << 16);
+          lo[e] = l2[0] | ((uint32_t)l2[1] << 16);
+        }
+        st.x[2 * j] = hi;
+        st.x[2 * j + 1] = lo;
+      }
+    }
+  };
+  // piece j of the stage: plane j / 4, row wave + 4 (j % 4)
+  auto piece = [&](const SkStage<NORM>& st, int j) -> u32x4 {
+    if constexpr (NORM) return st.x[j < 4 ? 2 * j : 2 * (j - 4) + 1];
+    else return st.r[j];
   };
   // unconditional stores (a branch here makes the compiler wait for every
   // load in flight, the next chunk's weights included)
-  auto astore = [&](const u32x4 (&r)[SK_AIT], int c) {
+  auto astore = [&](const SkStage<NORM>& st, int c) {
 #pragma unroll
     for (int j = 0; j < SK_AIT; ++j) {
       const bool keep = aok[j] && c * SK_KC + akk[j] < a.K;
-      *(u32x4*)(&sa[0][0] + aoff[j]) = keep ? r[j] : u32x4{0u, 0u, 0u, 0u};
+      *(u32x4*)(&sa[0][0] + aoff[j]) = keep ? piece(st, j) : u32x4{0u, 0u, 0u, 0u};
     }
   };
   // weights past K are clamped inside the row; the activations there are zero
@@ -183,11 +252,15 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& a, int n_rg, in
   // (rotated by the row group), spreading the memory channels in use.
   const int ncs = c1 - c0, rot = rg % ncs;
   auto ch = [&](int i) { i = min(i, ncs - 1); return c0 + (i + rot) % ncs; };  // i-th chunk visited
-  u32x4 w0[16], w1[16], ra0[SK_AIT], ra1[SK_AIT];
+  u32x4 w0[16], w1[16];
+  SkStage<NORM> ra0, ra1;
+  // the first weights are requested before the first activations are
+  // waited for (loads complete in order, so that wait leaves them in flight)
   aload(ra0, ch(0));
-  astore(ra0, ch(0));
   aload(ra1, ch(1));
   wload(w0, ch(0));
+  prep(ra0);
+  astore(ra0, ch(0));
   __syncthreads();
   int i = 0;
   for (; i + 1 < ncs; i += 2) {
@@ -195,6 +268,7 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& a, int n_rg, in
     wload(w1, ch(i + 1));
     __builtin_amdgcn_sched_barrier(0);
     compute(w0);
+    prep(ra1);
     __syncthreads();
     astore(ra1, ch(i + 1));
     __syncthreads();
@@ -202,6 +276,7 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& a, int n_rg, in
     wload(w0, ch(i + 2));
     __builtin_amdgcn_sched_barrier(0);
     compute(w1);
+    prep(ra0);
     __syncthreads();
     astore(ra0, ch(i + 2));
     __syncthreads();
@@ -520,7 +595,10 @@ constexpr int TN8_GATE_UP = 224, TN8_QKV = 192;
     gemm_reduce_body<EPI>(a, splits);                                                      \
   }                                                                                        \
   __global__ void __launch_bounds__(256) k_gemv_##NAME(GemmArgs a, int n_rg, int splits) { \
-    gemm_skinny_body<EPI>(a, n_rg, splits);                                                \
+    gemm_skinny_body<EPI, false>(a, n_rg, splits);                                         \
+  }                                                                                        \
+  __global__ void __launch_bounds__(256) k_gemvn_##NAME(GemmArgs a, int n_rg, int splits) { \
+    gemm_skinny_body<EPI, true>(a, n_rg, splits);                                          \
   }                                                                                        \
   __global__ void __launch_bounds__(256) k_gemm_f32_##NAME(GemmArgs a) { gemm_f32_body<EPI>(a); }
 
@@ -541,8 +619,9 @@ typedef void (*PlainFn)(GemmArgs);
 // consumer to add (in split order); *partials = 0 when the epilogue ran.
 template <int EPI>
 static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled8, int tn8, TiledFn tiled_s, ReduceFn reduce,
-                             SkinnyFn skinny, PlainFn f32, int* partials, hipStream_t s) {
+                             SkinnyFn skinny, SkinnyFn skinny_norm, PlainFn f32, int* partials, hipStream_t s) {
   if (partials) *partials = 0;
+  if (a.norm_ss && (dtype != CAD_BF16 || a.M > 16 || a.norm_slices > 32)) return hipErrorInvalidValue;
   const bool leave = partials != nullptr && EPI != EPI_SWIGLU && a.split_ws != nullptr && a.N % 4 == 0;
   if (dtype == CAD_F32) {
     dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
@@ -563,7 +642,7 @@ static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled8, int t
           splits = c;
           break;
         }
-    hipLaunchKernelGGL(skinny, dim3(n_rg * splits), dim3(256), 0, s, a, n_rg, splits);
+    hipLaunchKernelGGL(a.norm_ss ? skinny_norm : skinny, dim3(n_rg * splits), dim3(256), 0, s, a, n_rg, splits);
     if (splits > 1) *partials = splits;
   } else {
     const bool small = a.M <= 128;
@@ -597,7 +676,7 @@ static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled8, int t
 hipError_t launch_gemm(int dtype, int role, const GemmArgs& a, hipStream_t s, int* partials) {
   switch (role) {
 #define CAD_LAUNCH(EPI, NAME, TN8) \
-  launch_epi<EPI>(dtype, a, k_gemm_##NAME, TN8, k_gemm_s_##NAME, k_gemm_reduce_##NAME, k_gemv_##NAME, \
+  launch_epi<EPI>(dtype, a, k_gemm_##NAME, TN8, k_gemm_s_##NAME, k_gemm_reduce_##NAME, k_gemv_##NAME, k_gemvn_##NAME, \
                   k_gemm_f32_##NAME, partials, s)
     case GEMM_QKV: return CAD_LAUNCH(EPI_STORE_F32, qkv, TN8_QKV);
     case GEMM_O: return CAD_LAUNCH(EPI_RESID, o, TILE_N);

@@ -152,12 +152,59 @@ hipError_t launch_rmsnorm(int dtype, float* x, const float* x_part, int n_part, 
 }
 
 // ---------------------------------------------------------------------------
+// RMSNorm for a few rows (the weight-streaming projections that follow
+// normalise while they stage their activations): x += the pending k-split
+// partial planes, one 256-element slice per work-group (so a single row is
+// spread over d / 256 compute units), and the slice's sum of squares to
+// ss[row][slice].  The consumer forms 1 / sqrt(sum(ss[row]) / d + eps) from
+// the slice sums in slice order.
+// ---------------------------------------------------------------------------
+constexpr int RMS_SLICE = 256;
+
+__global__ void __launch_bounds__(64) k_rms_slices(float* __restrict__ x, const float* __restrict__ x_part,
+                                                   int n_part, int rows, int d, float* __restrict__ ss) {
+  const int r = blockIdx.x, sl = blockIdx.y;
+  const int n4 = d / 4;
+  const int i4 = sl * (RMS_SLICE / 4) + threadIdx.x;
+  const int c4 = min(i4, n4 - 1);
+  float* xr = x + (int64_t)r * d;
+  f32x4 v = *(const f32x4*)(xr + 4 * c4);
+  // PB planes in flight at once (clamped repeats are not added)
+  constexpr int PB = 8;
+  for (int sp = 0; sp < n_part; sp += PB) {
+    f32x4 t[PB];
+#pragma unroll
+    for (int u = 0; u < PB; ++u) t[u] = *(const f32x4*)(x_part + ((int64_t)min(sp + u, n_part - 1) * rows + r) * d + 4 * c4);
+#pragma unroll
+    for (int u = 0; u < PB; ++u)
+      if (sp + u < n_part) v += t[u];
+  }
+  const bool ok = i4 < n4;
+  if (n_part > 0 && ok) *(f32x4*)(xr + 4 * i4) = v;
+  float q = ok ? v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3] : 0.f;
+  for (int o = 32; o > 0; o >>= 1) q += __shfl_xor(q, o);
+  if (threadIdx.x == 0) ss[(int64_t)r * gridDim.y + sl] = q;
+}
+
+int rms_slices(int d) { return (d + RMS_SLICE - 1) / RMS_SLICE; }
+
+hipError_t launch_rms_slices(float* x, const float* x_part, int n_part, int rows, int d, float* ss, hipStream_t s) {
+  if (d % 4 != 0 || rows < 1 || (n_part > 0 && !x_part)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_rms_slices, dim3(rows, rms_slices(d)), dim3(RMS_SLICE / 4), 0, s, x, x_part, n_part, rows, d, ss);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // rotary positions on q and k (half-split pairs, angle pos * freq[i] formed
 // and reduced in fp64), q to the attention operand buffer (type TQ), k and v appended to
 // the paged cache (type T) at the row's absolute position.  Rows at or beyond
 // *write_limit do not touch the cache.  bf16 models also keep every row's k
 // and v at half precision in the span workspace (kv.span_k / kv.span_v),
 // which attention reads for this call's own keys.
+// One work-group per row and group of heads: with gridDim.y == 1 the whole
+// row, with gridDim.y == hkv one KV group (its G query heads, its k head and
+// its v head), so that a few rows still spread their staging loads (the
+// k-split partials of the QKV projection) over many compute units.
 // ---------------------------------------------------------------------------
 constexpr int ROPE_MAX_HALF = 128;  // head_dim up to 256
 constexpr int ROPE_THREADS = 512;
@@ -174,35 +221,46 @@ __global__ void __launch_bounds__(ROPE_THREADS) k_rope_append(const float* __res
   const int64_t pos = rm.L[b] + local;
   const int half = hd / 2;
   const int width = (hq + 2 * hkv) * hd;
+  // this work-group's heads: query heads [qh0, qh0 + nq), kv heads [kh0, kh0 + nk)
+  const bool grouped = gridDim.y > 1;
+  const int nq = grouped ? hq / hkv : hq, nk = grouped ? 1 : hkv;
+  const int qh0 = grouped ? blockIdx.y * nq : 0, kh0 = grouped ? blockIdx.y : 0;
   // independent loads first: this row's cache block and its rotation
   // frequency (one pair per thread)
   bool write_kv = write_limit == nullptr || local < *write_limit;
   const int64_t blk = write_kv ? kv.table[(int64_t)b * kv.max_blocks + pos / CAD_KV_BLOCK] : 0;
   const double fr = (int)threadIdx.x < half ? freq[threadIdx.x] : 0.0;
-  // the row's projection output, staged in LDS: the stored values, or the
-  // sum of the k-split partials [n_part][rows][width] in split order
+  // the row's projection output for these heads, staged in LDS as
+  // [q heads][k heads][v heads] x hd: the stored values, or the sum of the
+  // k-split partials [n_part][rows][width] in split order
   extern __shared__ float srow[];
   {
-    // RV 16-byte pieces per thread in flight at once (indices clamped; the
-    // clamped repeats are not stored); partial planes added in split order
     const float* src = n_part == 0 ? qkv + (int64_t)r * width : qkv_part + (int64_t)r * width;
     const int64_t plane = (int64_t)rows * width;
-    const int n4 = width / 4;
+    const int nqc = nq * hd, nkc = nk * hd;  // staged columns of q, and of k (and of v)
+    const int staged = nqc + 2 * nkc;
+    // staged column j -> projection column (the three runs are contiguous)
+    auto src_col = [&](int j) {
+      return j < nqc ? qh0 * hd + j
+                     : (j < nqc + nkc ? (hq + kh0) * hd + (j - nqc) : (hq + hkv + kh0) * hd + (j - nqc - nkc));
+    };
+    // RV 16-byte pieces per thread in flight at once (indices clamped; the
+    // clamped repeats are not stored); partial planes added in split order.
+    // hd is a multiple of 4, so a 4-column piece never straddles two runs.
+    const int n4 = (hd % 4 == 0) ? staged / 4 : 0;
     constexpr int RV = 4;
     for (int base = 0; base < n4; base += RV * ROPE_THREADS) {
       f32x4 v[RV];
+      int col[RV];
 #pragma unroll
       for (int u = 0; u < RV; ++u) {
-        const int i4 = min(base + (int)threadIdx.x + u * ROPE_THREADS, n4 - 1);
-        v[u] = *(const f32x4*)(src + 4 * i4);
+        col[u] = src_col(4 * min(base + (int)threadIdx.x + u * ROPE_THREADS, n4 - 1));
+        v[u] = *(const f32x4*)(src + col[u]);
       }
       for (int sp = 1; sp < n_part; ++sp) {
         f32x4 t[RV];
 #pragma unroll
-        for (int u = 0; u < RV; ++u) {
-          const int i4 = min(base + (int)threadIdx.x + u * ROPE_THREADS, n4 - 1);
-          t[u] = *(const f32x4*)(src + sp * plane + 4 * i4);
-        }
+        for (int u = 0; u < RV; ++u) t[u] = *(const f32x4*)(src + sp * plane + col[u]);
 #pragma unroll
         for (int u = 0; u < RV; ++u) v[u] += t[u];
       }
@@ -212,10 +270,11 @@ __global__ void __launch_bounds__(ROPE_THREADS) k_rope_append(const float* __res
         if (i4 < n4) *(f32x4*)(srow + 4 * i4) = v[u];
       }
     }
-    for (int i = 4 * n4 + threadIdx.x; i < width; i += blockDim.x) {
-      float v = src[i];
-      for (int sp = 1; sp < n_part; ++sp) v += src[sp * plane + i];
-      srow[i] = v;
+    for (int j = 4 * n4 + threadIdx.x; j < staged; j += blockDim.x) {
+      const int c = src_col(j);
+      float v = src[c];
+      for (int sp = 1; sp < n_part; ++sp) v += src[sp * plane + c];
+      srow[j] = v;
     }
   }
   auto ld = [&](int i) { return srow[i]; };
@@ -244,14 +303,15 @@ __global__ void __launch_bounds__(ROPE_THREADS) k_rope_append(const float* __res
     rot[i] = float2{cs, sn};
   }
   __syncthreads();
-  // rotations: q heads then k heads, one (head, pair) per item
-  const int n_rot = (hq + hkv) * half;
+  // rotations: q heads then k heads (staged order), one (head, pair) per item
+  const int n_rot = (nq + nk) * half;
   for (int it = threadIdx.x; it < n_rot; it += blockDim.x) {
-    const int h = it / half, i = it % half;
+    const int hs = it / half, i = it % half;
     const float c = rot[i].x, s = rot[i].y;
-    const float a = ld(h * hd + i), bb = ld(h * hd + i + half);
+    const float a = ld(hs * hd + i), bb = ld(hs * hd + i + half);
     const float ra = a * c - bb * s, rb = a * s + bb * c;
-    if (h < hq) {
+    if (hs < nq) {
+      const int h = qh0 + hs;
       TQ* qo = q_out + ((int64_t)r * hq + h) * hd;
       qo[i] = from_f<TQ>(ra);
       qo[i + half] = from_f<TQ>(rb);
@@ -261,7 +321,7 @@ __global__ void __launch_bounds__(ROPE_THREADS) k_rope_append(const float* __res
         ql[i + half] = from_f<TQ>(rb - to_f<TQ>(qo[i + half]));
       }
     } else {
-      const int g = h - hq;
+      const int g = kh0 + hs - nq;
       if (write_kv) {
         T* kd = kc + ((blk * hkv + g) * CAD_KV_BLOCK + slot) * hd;
         kd[i] = from_f<T>(ra);
@@ -273,26 +333,32 @@ __global__ void __launch_bounds__(ROPE_THREADS) k_rope_append(const float* __res
       }
     }
   }
-  for (int it = threadIdx.x; it < hkv * hd; it += blockDim.x) {
-    const int g = it / hd, dd = it % hd;
-    const float vv = ld((hq + hkv) * hd + it);
+  for (int it = threadIdx.x; it < nk * hd; it += blockDim.x) {
+    const int g = kh0 + it / hd, dd = it % hd;
+    const float vv = ld((nq + nk) * hd + it);
     if (write_kv) vc[((blk * hkv + g) * hd + dd) * CAD_KV_BLOCK + slot] = from_f<T>(vv);
     if (kv.span_v) kv.span_v[((int64_t)g * hd + dd) * kv.span_cap + wrow] = f2h(vv);
   }
 }
 
+// rows at most this many: one work-group per (row, KV group)
+constexpr int ROPE_GROUPED_MAX_ROWS = 64;
+
 hipError_t launch_rope_append(int dtype, const float* qkv, const float* qkv_part, int n_part, int rows, int hq,
                               int hkv, int hd, const double* freq, const RowMap& rm, KVView kv,
                               const int32_t* write_limit, void* q_out, void* q_lo, int32_t* status,
                               hipStream_t s) {
-  const size_t lds = (size_t)(hq + 2 * hkv) * hd * sizeof(float);
+  const bool grouped = rows <= ROPE_GROUPED_MAX_ROWS && hkv > 1;
+  const int heads = grouped ? hq / hkv + 2 : hq + 2 * hkv;
+  const size_t lds = (size_t)heads * hd * sizeof(float);
   if (hd / 2 > ROPE_MAX_HALF || hd / 2 > ROPE_THREADS || (n_part > 0 && !qkv_part) || lds > 65536)
     return hipErrorInvalidValue;
+  const dim3 grid(rows, grouped ? hkv : 1);
   if (dtype == CAD_BF16)
-    hipLaunchKernelGGL((k_rope_append<bf16_t, f16_t>), dim3(rows), dim3(ROPE_THREADS), lds, s, qkv, qkv_part, n_part,
+    hipLaunchKernelGGL((k_rope_append<bf16_t, f16_t>), grid, dim3(ROPE_THREADS), lds, s, qkv, qkv_part, n_part,
                        rows, hq, hkv, hd, freq, rm, kv, write_limit, (f16_t*)q_out, (f16_t*)q_lo, status);
   else
-    hipLaunchKernelGGL((k_rope_append<float, float>), dim3(rows), dim3(ROPE_THREADS), lds, s, qkv, qkv_part, n_part,
+    hipLaunchKernelGGL((k_rope_append<float, float>), grid, dim3(ROPE_THREADS), lds, s, qkv, qkv_part, n_part,
                        rows, hq, hkv, hd, freq, rm, kv, write_limit, (float*)q_out, (float*)nullptr, status);
   return hipGetLastError();
 }
