@@ -156,8 +156,8 @@ int64_t max_parts_rows(const cad_config& c) {
   int64_t best = 0;
   for (int r = 1; r <= c.max_tokens; ++r) {
     // both tile shapes: one sequence, and r one-row sequences
-    const int p1 = attention_parts(r, 1, c.n_q_heads, c.n_kv_heads, (int64_t)1 << 40);
-    const int p2 = attention_parts(r, r, c.n_q_heads, c.n_kv_heads, (int64_t)1 << 40);
+    const int p1 = attention_parts(r, 1, c.n_q_heads, c.n_kv_heads, (int64_t)1 << 40, r);
+    const int p2 = attention_parts(r, r, c.n_q_heads, c.n_kv_heads, (int64_t)1 << 40, 1);
     const int p = p1 > p2 ? p1 : p2;
     if ((int64_t)p * r > best) best = (int64_t)p * r;
   }
@@ -239,9 +239,13 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
   const int d = c.d_model, hq = c.n_q_heads, hkv = c.n_kv_heads, hd = c.head_dim, F = c.ffn_dim;
   const int qkv_rows = (hq + 2 * hkv) * hd;
   int64_t max_L = 0;
-  for (int b = 0; b < rm.n_seq; ++b) max_L = rm.L[b] > max_L ? rm.L[b] : max_L;
+  int max_rows = 0;
+  for (int b = 0; b < rm.n_seq; ++b) {
+    max_L = rm.L[b] > max_L ? rm.L[b] : max_L;
+    max_rows = rm.start[b + 1] - rm.start[b] > max_rows ? rm.start[b + 1] - rm.start[b] : max_rows;
+  }
   // partitions of each query tile's key axis (cached keys, then the span's own)
-  const int n_parts = attention_parts(R, rm.n_seq, hq, hkv, max_L);
+  const int n_parts = attention_parts(R, rm.n_seq, hq, hkv, max_L, max_rows);
   if ((int64_t)n_parts * R > m->part_cap)
     return fail(CAD_E_CAPACITY, "attention partitions %d x %d rows exceed the workspace", n_parts, R);
   if (c.dtype == CAD_BF16 && rm.pstart[rm.n_seq] > m->span_cap)

@@ -190,6 +190,7 @@ hipError_t launch_suffix_match(const int32_t* tokens, int64_t T, int max_n, int 
 
 // attention split: partitions of each query tile's key axis (cached keys up
 // to max L, then the span's own) so that small spans still fill the chip
-int attention_parts(int rows, int n_seq, int hq, int hkv, int64_t max_cache_keys);
+// (max_seq_rows: the most span rows any sequence of the call has)
+int attention_parts(int rows, int n_seq, int hq, int hkv, int64_t max_cache_keys, int max_seq_rows);
 
 }  // namespace cad

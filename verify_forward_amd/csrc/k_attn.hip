@@ -465,6 +465,275 @@ k_attn_bf16(AttnArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Short spans: every sequence of the call has at most 16 query rows per KV
+// head (N <= 16 / G).  One work-group = one (sequence, KV head, key
+// partition); its four waves take the partition's 32-key tiles in turn, each
+// with its own online softmax over the same query columns (one 16-column
+// block), and K and V go from the paged cache (or the span workspace)
+// straight into matrix-core fragments: no LDS stage and no barrier until
+// the four waves combine their states at the end.  Every wave computes (the
+// LDS-staged kernel gives such a call one computing wave per work-group),
+// and each keeps one tile in flight while it works on the previous one.
+//   S^T = K (Q_hi + Q_lo)^T: lane (g, i) supplies key 16 kb + i, dims
+//     32 ds + 8 g .. + 7; it then holds keys 16 kb + 4 g + r of query i.
+//   O^T += V^T P^T: as its k index 8 g + e the V fragment takes key 4 g + e
+//     of the tile's first block (e < 4) and key 4 g + e - 4 of its second,
+//     exactly the keys lane (g, i) holds in S^T, so P^T is formed in place.
+// Cached K and V are widened from bf16 to half exactly; the span's own keys
+// come from the half-precision span workspace.  Partials use the layout of
+// the LDS-staged kernel, so the same merge follows.
+// ---------------------------------------------------------------------------
+constexpr int DEC_KT = 32;  // keys per tile: two cache blocks
+
+template <int HD>
+__global__ void __launch_bounds__(256, 2) k_attn_dec(AttnArgs p) {
+  constexpr int DS = HD / 32, DB = HD / 16;
+  // wave index made provably uniform, so that tile, block and base-pointer
+  // arithmetic stays scalar and each load needs one 32-bit lane offset
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4, i16 = lane & 15;
+  const int part = blockIdx.x % p.n_parts;
+  const int bh = blockIdx.x / p.n_parts;
+  const int kvh = bh % p.hkv, b = bh / p.hkv;
+  const int n_rows = p.rm.start[b + 1] - p.rm.start[b];
+  const int R = n_rows * p.G;  // <= 16 (checked by the launcher)
+  const int64_t L = p.rm.L[b];
+  // this lane's query column
+  const bool q_ok = i16 < R;
+  const int k_local = q_ok ? i16 / p.G : 0;
+  // key axis: TA cached tiles (keys 0 .. L - 1, the last possibly short) and
+  // one span tile (keys L .. L + n_rows - 1, n_rows <= 16); the partitions
+  // take equal runs of these tiles, the waves every fourth tile of a run
+  const int64_t TA = (L + DEC_KT - 1) / DEC_KT, TT = TA + 1;
+  const int64_t t0 = TT * part / p.n_parts, t1 = TT * (part + 1) / p.n_parts;
+  const int nw = t1 - t0 > wave ? (int)((t1 - t0 - wave + 3) / 4) : 0;
+  const int64_t nblk = (L + CAD_KV_BLOCK - 1) / CAD_KV_BLOCK;  // cached blocks of the sequence
+  const int32_t* table = p.kv.table + (int64_t)b * p.kv.max_blocks;
+  const int64_t kv_blk_stride = (int64_t)p.hkv * CAD_KV_BLOCK * HD;
+  const bf16_t* kbase = (const bf16_t*)p.kv.k + (int64_t)kvh * CAD_KV_BLOCK * HD;
+  const bf16_t* vbase = (const bf16_t*)p.kv.v + (int64_t)kvh * CAD_KV_BLOCK * HD;
+  const int64_t srow0 = p.rm.pstart[b];  // span workspace row of key L (64-row padded region)
+
+  f32x4 o[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -1e30f, l_run = 0.f;
+  constexpr int QLDS = HD + 8;
+  __shared__ __attribute__((aligned(16))) f16_t sq[2][16 * QLDS];
+
+  {
+    auto tile_of = [&](int i) -> int64_t { return t0 + wave + 4 * (int64_t)min(i, nw - 1); };
+    // block ids of tile i: lanes with bit 0 clear read its first block, the
+    // others its second (indices clamped to the sequence's cached blocks;
+    // the span tile reads entry 0 and ignores it)
+    auto ids_of = [&](int i) -> int32_t {
+      const int64_t t = tile_of(i);
+      const int64_t bi = t < TA ? min(2 * t + (lane & 1), nblk - 1) : 0;
+      return table[bi];
+    };
+    struct Buf {
+      u32x4 k[2][DS];
+      u32x4 v[DB];
+    };
+    // raw loads of tile i (unconditional: the source is chosen by address).
+    // Base pointers are wave-uniform; lane offsets (elements) are fixed per
+    // lane: K [16 keys][HD] per cache block, V [HD][16] per cache block,
+    // span K [row][hkv][HD], span V [hkv][HD][span_cap].
+    const uint32_t ko_c = (uint32_t)(i16 * HD + 8 * g4);
+    const uint32_t ko_s = (uint32_t)(i16 * p.hkv * HD + 8 * g4);
+    const uint32_t vo_c = (uint32_t)(i16 * CAD_KV_BLOCK + 4 * g4);
+    const uint32_t vo_s = (uint32_t)(i16 * p.kv.span_cap + 4 * g4);
+    const f16_t* sk_base = p.kv.span_k + (srow0 * p.hkv + kvh) * HD;
+    const f16_t* sv_base = p.kv.span_v + (int64_t)kvh * HD * p.kv.span_cap + srow0;
+    auto issue = [&](Buf& bf, int i, int32_t ids) {
+      const int64_t t = tile_of(i);
+      const bool span = t >= TA;  // wave-uniform
+      int64_t b0 = __builtin_amdgcn_readlane(ids, 0), b1 = __builtin_amdgcn_readlane(ids, 1);
+      const bool ok = span || (b0 >= 0 && b0 < p.kv.num_blocks && b1 >= 0 && b1 < p.kv.num_blocks);
+      if (!ok && p.status && lane == 0) atomicOr(p.status, (int32_t)CAD_DEV_BAD_BLOCK);
+      if (!ok || span) b0 = b1 = 0;
+      const uint32_t ko = span ? ko_s : ko_c;
+      const uint32_t vo = span ? vo_s : vo_c;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint16_t* kp = span ? (const uint16_t*)(sk_base + (int64_t)16 * kb * p.hkv * HD)
+                                  : (const uint16_t*)(kbase + (kb ? b1 : b0) * kv_blk_stride);
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) bf.k[kb][ds] = *(const u32x4*)(kp + ko + 32 * ds);
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const uint16_t* vp0 = span ? (const uint16_t*)(sv_base + (int64_t)16 * db * p.kv.span_cap)
+                                   : (const uint16_t*)(vbase + b0 * kv_blk_stride + 16 * db * CAD_KV_BLOCK);
+        const uint16_t* vp1 = span ? vp0 + 16 : (const uint16_t*)(vbase + b1 * kv_blk_stride + 16 * db * CAD_KV_BLOCK);
+        const u32x2 v0 = *(const u32x2*)(vp0 + vo);
+        const u32x2 v1 = *(const u32x2*)(vp1 + vo);
+        bf.v[db] = u32x4{v0[0], v0[1], v1[0], v1[1]};
+      }
+      return ok;
+    };
+    auto compute = [&](Buf& bf, int i, bool ok) {
+      const int64_t t = tile_of(i);
+      const bool span = t >= TA;
+      // keys of the tile a query may see: [0, lim) relative to the tile start
+      const int vlim = !ok ? 0 : span ? n_rows : (int)min<int64_t>(L - t * DEC_KT, DEC_KT);
+      const int lim = span ? min(vlim, k_local + 1) : vlim;
+      if (vlim < DEC_KT) {
+        // zero V of keys past the range (stale slots may hold anything; P is 0 there)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int k0 = (w < 2 ? 0 : 16) + 4 * g4 + 2 * (w & 1);  // keys of the two halves of word w
+            const uint32_t keep = (k0 + 1 < vlim) ? 0xFFFFFFFFu : (k0 < vlim ? 0x0000FFFFu : 0u);
+            bf.v[db][w] &= keep;
+          }
+      }
+      f32x4 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+          const u32x4 kf = span ? bf.k[kb][ds] : bf16x8_to_f16x8(bf.k[kb][ds]);
+          const u32x4 qh = *(const u32x4*)(&sq[0][i16 * QLDS + 32 * ds + 8 * g4]);
+          const u32x4 qlo = *(const u32x4*)(&sq[1][i16 * QLDS + 32 * ds + 8 * g4]);
+          s[kb] = mfma16(kf, qh, s[kb]);
+          s[kb] = mfma16(kf, qlo, s[kb]);
+        }
+      }
+      if (lim < DEC_KT) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (16 * kb + 4 * g4 + r >= lim) s[kb][r] = -INFINITY;
+      }
+      const float m4 = fmaxf(fmaxf(max_raw(s[0][0], s[0][1], p.pos_inf), max_raw(s[0][2], s[0][3], p.pos_inf)),
+                             fmaxf(max_raw(s[1][0], s[1][1], p.pos_inf), max_raw(s[1][2], s[1][3], p.pos_inf)));
+      const float mx = max_col4(m4, p.pos_inf) * p.scale_log2;
+      if (__ballot(mx > m_run + FA_LAZY)) {  // wave-uniform rescale
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < DB; ++d) o[d] *= alpha;
+      }
+      const float nm = -m_run;
+      const f16x2 ones = {(f16_t)1.0f, (f16_t)1.0f};
+      float psum = 0.f;
+      uint32_t pk[4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float e[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], p.scale_log2, nm));
+        const f16x2 e01 = {(f16_t)e[0], (f16_t)e[1]};
+        const f16x2 e23 = {(f16_t)e[2], (f16_t)e[3]};
+        psum = __builtin_amdgcn_fdot2(e01, ones, psum, false);
+        psum = __builtin_amdgcn_fdot2(e23, ones, psum, false);
+        pk[2 * kb] = __builtin_bit_cast(uint32_t, e01);
+        pk[2 * kb + 1] = __builtin_bit_cast(uint32_t, e23);
+      }
+      l_run += psum;
+      const u32x4 pf = {pk[0], pk[1], pk[2], pk[3]};
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x4 vf = span ? bf.v[db] : bf16x8_to_f16x8(bf.v[db]);
+        o[db] = mfma16(vf, pf, o[db]);
+      }
+    };
+    // tile i is computed while tile i + 1 is loaded; block ids run two
+    // tiles ahead.  Loads past the wave's last tile re-read that tile
+    // (clamped index: cache hits, never used).
+    Buf A, B;
+    int32_t idE = nw > 0 ? ids_of(0) : 0, idO = nw > 0 ? ids_of(1) : 0;
+    // the work-group's q columns (hi and lo planes), shared by the four waves
+    // through LDS: sq[plane][column][HD] (zero for columns past R); staged
+    // while the first block ids are in flight, and the first tile is
+    // requested before the barrier
+    for (int c = tid; c < 2 * 16 * (HD / 8); c += 256) {
+      const int pl = c / (16 * (HD / 8)), col = (c / (HD / 8)) % 16, c8 = c % (HD / 8);
+      const bool okc = col < R;
+      const int64_t row = (int64_t)(p.rm.start[b] + (okc ? col / p.G : 0)) * p.hq + kvh * p.G + (okc ? col % p.G : 0);
+      const f16_t* src = (const f16_t*)(pl ? p.q_lo : p.q) + row * HD + 8 * c8;
+      *(u32x4*)(&sq[pl][col * QLDS + 8 * c8]) = okc ? *(const u32x4*)src : u32x4{0u, 0u, 0u, 0u};
+    }
+    bool okA = nw > 0 ? issue(A, 0, idE) : false, okB = true;
+    if (nw > 0) idE = ids_of(2);
+    __syncthreads();
+    for (int i = 0; i < nw; i += 2) {
+      okB = issue(B, i + 1, idO);
+      idO = ids_of(i + 3);
+      compute(A, i, okA);
+      if (i + 1 >= nw) break;
+      okA = issue(A, i + 2, idE);
+      idE = ids_of(i + 4);
+      compute(B, i + 1, okB);
+    }
+  }
+  // combine the four waves: (m, l) per query column and O^T
+  __shared__ float sm[4][16], sl[4][16];
+  __shared__ float so[4][16][HD + 4];
+  float l = l_run;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (g4 == 0) {
+    sm[wave][i16] = m_run;
+    sl[wave][i16] = l;
+  }
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) so[wave][i16][16 * db + 4 * g4 + r] = o[db][r];
+  __syncthreads();
+  // thread -> (query column q, dims d0 .. d0 + HD / 16 - 1)
+  const int q = tid >> 4, d0 = (tid & 15) * (HD / 16);
+  float m = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    if (sl[w][q] > 0.f) m = fmaxf(m, sm[w][q]);
+  float wt[4], den = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    wt[w] = sl[w][q] > 0.f ? __builtin_amdgcn_exp2f(sm[w][q] - m) : 0.f;
+    den += wt[w] * sl[w][q];
+  }
+  if (q >= R) return;
+  const int kq = q / p.G;
+  const int64_t orow = (int64_t)(p.rm.start[b] + kq) * p.hq + kvh * p.G + q % p.G;
+  if (p.n_parts == 1) {
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    bf16_t* out = (bf16_t*)p.out + orow * HD;
+    bf16_t* out_lo = (bf16_t*)p.out_lo + orow * HD;
+#pragma unroll
+    for (int j = 0; j < HD / 16; ++j) {
+      const int d = d0 + j;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) v += wt[w] * so[w][q][d];
+      split_bf16(v * inv, out[d], out_lo[d]);
+    }
+  } else {
+    const int64_t qi = (int64_t)part * p.rows * p.hq + orow;
+    float* po = p.part_o + qi * HD;
+#pragma unroll
+    for (int j = 0; j < HD / 16; ++j) {
+      const int d = d0 + j;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) v += wt[w] * so[w][q][d];
+      po[d] = v;
+    }
+    if ((tid & 15) == 0) {
+      p.part_ml[qi * 2 + 0] = den > 0.f ? m : -1e30f;
+      p.part_ml[qi * 2 + 1] = den;
+    }
+  }
+}
+
 // log-sum-exp merge of the partitions (base-2 exponent, as produced above),
 // written as bf16 hi / lo planes.  One work-group per (row, head): the
 // partition weights 2^(m_p - m) (0 for a partition that saw no key) are
@@ -624,11 +893,24 @@ k_attn_f32(AttnArgs p, int hd) {
   }
 }
 
-int attention_parts(int rows, int n_seq, int hq, int hkv, int64_t max_cache_keys) {
+// the short-span kernel serves calls whose sequences all have at most 16
+// query rows per KV head
+inline bool attn_short(int max_seq_rows, int G) { return (int64_t)max_seq_rows * G <= 16; }
+constexpr int DEC_TARGET_WGS = 256;  // short-span kernel: about one work-group per CU (measured: 512 ran 2 us slower at N = 1)
+
+int attention_parts(int rows, int n_seq, int hq, int hkv, int64_t max_cache_keys, int max_seq_rows) {
   // partitions of each query tile's key axis: about one work-group per
-  // compute unit (256 CUs; two for the four-wave shape) together with the
-  // query tiles, at least 256 cached keys each, at least one
+  // compute unit (256 CUs; two for the four-wave shape)
+  // together with the query tiles, at least 256 cached keys each, at least one
   const int G = hq / hkv;
+  if (attn_short(max_seq_rows, G)) {
+    const int base = n_seq * hkv;
+    int parts = (DEC_TARGET_WGS + base - 1) / base;
+    const int64_t cap = max_cache_keys / 256;
+    if (parts > cap) parts = (int)cap;
+    if (parts > MERGE_MAX_PARTS) parts = MERGE_MAX_PARTS;
+    return parts < 1 ? 1 : parts;
+  }
   const int qt = attn_qt(rows * G, n_seq);
   const int tiles = (rows * G + qt - 1) / qt;
   const int base = hkv * tiles;
@@ -663,6 +945,17 @@ hipError_t launch_attention(int dtype, const void* q, const void* q_lo, int rows
   a.pos_inf = INFINITY;
   if (dtype == CAD_F32) {
     hipLaunchKernelGGL(k_attn_f32, dim3(rows, hq), dim3(64), 0, s, a, hd);
+    return hipGetLastError();
+  }
+  int max_seq_rows = 0;
+  for (int b = 0; b < rm.n_seq; ++b) max_seq_rows = max(max_seq_rows, rm.start[b + 1] - rm.start[b]);
+  if (attn_short(max_seq_rows, a.G)) {
+    const int64_t wgs = (int64_t)rm.n_seq * hkv * n_parts;
+    if (wgs > INT32_MAX || (hd != 64 && hd != 128)) return hipErrorInvalidValue;
+    if (hd == 64)
+      hipLaunchKernelGGL((k_attn_dec<64>), dim3((unsigned)wgs), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_attn_dec<128>), dim3((unsigned)wgs), dim3(256), 0, s, a);
     return hipGetLastError();
   }
   const int qt = attn_qt(rows * a.G, rm.n_seq);
