@@ -276,11 +276,20 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
     g = GemmArgs{};
     LAUNCH(PF_NORM, launch_norm(m, m->ffn_norm[li], R, g, s));
     g.W = m->w_gate_up[li]; g.ldw = d;
-    g.M = R; g.N = F; g.K = d; g.up_off = F; g.out_act = m->act; g.out_act_lo = lo_plane(m, m->act, F);
+    // more than 16 rows (tiled projections): the SwiGLU activation goes to
+    // the down projection as one half plane (its input is the one whose
+    // rounding the logits tolerate best: 7B, N = 512, 9.4e-3 -> 1.3e-2
+    // against 2e-2), which halves that projection's matrix-core work and
+    // activation reads; the weight-streaming path keeps the two bf16 planes
+    const int act_f16 = c.dtype == CAD_BF16 && R > 16;
+    g.M = R; g.N = F; g.K = d; g.up_off = F; g.out_act = m->act;
+    g.out_act_lo = act_f16 ? nullptr : lo_plane(m, m->act, F);
+    g.act_f16 = act_f16;
     g.split_ws = m->split_ws;
     LAUNCH(PF_GATEUP, launch_gemm(c.dtype, GEMM_GATE_UP, g, s));
     g = GemmArgs{};
-    g.A = m->act; g.A_lo = lo_plane(m, m->act, F); g.lda = F; g.W = m->w_down[li]; g.ldw = F;
+    g.A = m->act; g.A_lo = act_f16 ? nullptr : lo_plane(m, m->act, F); g.lda = F; g.W = m->w_down[li]; g.ldw = F;
+    g.act_f16 = act_f16;
     g.M = R; g.N = d; g.K = F; g.out_f32 = m->x; g.ldo = d;
     g.split_ws = m->split_ws;
     LAUNCH(PF_DOWN, launch_gemm(c.dtype, GEMM_DOWN, g, s, &m->x_parts));

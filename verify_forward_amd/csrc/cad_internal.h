@@ -141,6 +141,10 @@ struct GemmArgs {
   const float* norm_ss;
   int norm_slices;
   float norm_eps;
+  // bf16 models, more than 16 rows: the SWIGLU epilogue writes one half
+  // plane (out_act as f16, no lo plane), and the down projection reads it
+  // (A is then a single half plane and the weights are widened to half)
+  int act_f16;
 };
 
 // split-K workspace of the tiled GEMMs: GEMM_SPLIT_FLOATS floats (128 MB)

@@ -60,6 +60,17 @@ __device__ __forceinline__ void epi4(const GemmArgs& a, int m, int n, f32x4 c, f
       for (int r = 0; r < 4; ++r)
         if (n + r < a.N) o[r] = (EPI == EPI_RESID) ? o[r] + c[r] : c[r];
     }
+  } else if (SPLIT && a.act_f16) {
+    // one half plane (the down projection's operand on the tiled path)
+    f16_t* o = (f16_t*)a.out_act + (int64_t)m * a.N + n;
+    if (n + 3 < a.N && ((a.N & 3) == 0)) {
+      const f16x2 h01 = {f2h(silu_mul(c[0], cu[0])), f2h(silu_mul(c[1], cu[1]))};
+      const f16x2 h23 = {f2h(silu_mul(c[2], cu[2])), f2h(silu_mul(c[3], cu[3]))};
+      *(u32x2*)o = u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
+    } else {
+      for (int r = 0; r < 4; ++r)
+        if (n + r < a.N) o[r] = f2h(silu_mul(c[r], cu[r]));
+    }
   } else if (SPLIT) {
     bf16_t* o = (bf16_t*)a.out_act + (int64_t)m * a.N + n;
     bf16_t* ol = (bf16_t*)a.out_act_lo + (int64_t)m * a.N + n;
@@ -323,7 +334,11 @@ __device__ __forceinline__ void gemm_tile_of(int n_tn, int n_tm, int splits, int
   sp = q / (n_tm * n_tn);
 }
 
-template <int EPI, int TN, int NW, int MB>
+// F16A: the activations are one half plane (A) instead of two bf16 planes;
+// the weight tile is widened from bf16 to half (exact in half's normal
+// range) as it is written to LDS and each fragment pair takes one
+// v_mfma_f32_16x16x32_f16 product.
+template <int EPI, int TN, int NW, int MB, bool F16A = false>
 __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& a, int n_tn, int n_tm, int splits) {
   constexpr int NT = 64 * NW;       // threads
   constexpr int TM = 16 * MB * NW;  // activation rows per tile (MB 16-row blocks per wave)
@@ -370,7 +385,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& a, int n_tn, int
   for (int mb = 0; mb < MB; ++mb) {
     const int64_t off = (int64_t)min(wrow0 + 16 * mb + i16, a.M - 1) * a.lda + 8 * g;
     ahp[mb] = (const bf16_t*)a.A + off;
-    alp[mb] = (const bf16_t*)a.A_lo + off;
+    alp[mb] = F16A ? ahp[mb] : (const bf16_t*)a.A_lo + off;
   }
 
   f32x4 acc[NB][MB];
@@ -389,12 +404,12 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& a, int n_tn, int
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       r[mb][0] = *(const u32x4*)(ahp[mb] + kt * TK);
-      r[mb][1] = *(const u32x4*)(alp[mb] + kt * TK);
+      if (!F16A) r[mb][1] = *(const u32x4*)(alp[mb] + kt * TK);
     }
   };
   auto wstore = [&](const u32x4 (&r)[WCH], int buf) {
 #pragma unroll
-    for (int i = 0; i < WCH; ++i) *(u32x4*)(&sw[buf][wsoff[i]]) = r[i];
+    for (int i = 0; i < WCH; ++i) *(u32x4*)(&sw[buf][wsoff[i]]) = F16A ? bf16x8_to_f16x8(r[i]) : r[i];
   };
   auto compute = [&](int buf, const u32x4 (&ra)[MB][2]) {
     if (!live) {
@@ -402,7 +417,10 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& a, int n_tn, int
       // still in flight on this path when the next loads reuse the registers,
       // and the compiler guards every later load with a wait for all of them
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) asm volatile("" ::"v"(ra[mb][0]), "v"(ra[mb][1]));
+      for (int mb = 0; mb < MB; ++mb) {
+        if (F16A) asm volatile("" ::"v"(ra[mb][0]));
+        else asm volatile("" ::"v"(ra[mb][0]), "v"(ra[mb][1]));
+      }
       return;
     }
 #pragma unroll
@@ -410,8 +428,12 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& a, int n_tn, int
       const u32x4 w = *(const u32x4*)(&sw[buf][(x * 16 + i16) * WLD + g * 8]);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        acc[x][mb] = mfma16_bf(w, ra[mb][0], acc[x][mb]);
-        acc[x][mb] = mfma16_bf(w, ra[mb][1], acc[x][mb]);
+        if (F16A) {
+          acc[x][mb] = mfma16(w, ra[mb][0], acc[x][mb]);
+        } else {
+          acc[x][mb] = mfma16_bf(w, ra[mb][0], acc[x][mb]);
+          acc[x][mb] = mfma16_bf(w, ra[mb][1], acc[x][mb]);
+        }
       }
     }
   };
@@ -608,6 +630,13 @@ CAD_GEMM_KERNELS(gate_up, EPI_SWIGLU, TN8_GATE_UP)
 CAD_GEMM_KERNELS(down, EPI_RESID, TILE_N)
 CAD_GEMM_KERNELS(lm_head, EPI_STORE_F32, TILE_N)
 #undef CAD_GEMM_KERNELS
+// the down projection over a single half activation plane (act_f16)
+__global__ void __launch_bounds__(512) k_gemm_down_h(GemmArgs a, int n_tn, int n_tm, int splits) {
+  gemm_tiled_body<EPI_RESID, TILE_N, 8, 2, true>(a, n_tn, n_tm, splits);
+}
+__global__ void __launch_bounds__(512) k_gemm_s_down_h(GemmArgs a, int n_tn, int n_tm, int splits) {
+  gemm_tiled_body<EPI_RESID, TILE_N, 8, 1, true>(a, n_tn, n_tm, splits);
+}
 
 typedef void (*TiledFn)(GemmArgs, int, int, int);
 typedef void (*ReduceFn)(GemmArgs, int);
@@ -681,7 +710,13 @@ hipError_t launch_gemm(int dtype, int role, const GemmArgs& a, hipStream_t s, in
     case GEMM_QKV: return CAD_LAUNCH(EPI_STORE_F32, qkv, TN8_QKV);
     case GEMM_O: return CAD_LAUNCH(EPI_RESID, o, TILE_N);
     case GEMM_GATE_UP: return CAD_LAUNCH(EPI_SWIGLU, gate_up, TN8_GATE_UP);
-    case GEMM_DOWN: return CAD_LAUNCH(EPI_RESID, down, TILE_N);
+    case GEMM_DOWN:
+      if (a.act_f16) {
+        if (dtype != CAD_BF16 || a.M <= 16) return hipErrorInvalidValue;
+        return launch_epi<EPI_RESID>(dtype, a, k_gemm_down_h, TILE_N, k_gemm_s_down_h, k_gemm_reduce_down,
+                                     k_gemv_down, k_gemvn_down, k_gemm_f32_down, partials, s);
+      }
+      return CAD_LAUNCH(EPI_RESID, down, TILE_N);
     default: return CAD_LAUNCH(EPI_STORE_F32, lm_head, TILE_N);
 #undef CAD_LAUNCH
   }
