@@ -472,7 +472,9 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "storage_dtype": "bf16",
-        "operands": "projections: bf16 weights x bf16 hi/lo activation planes; attention: f16 (q hi/lo, K, V, P); fp32 accumulate",
+        "operands": ("projections: bf16 weights x bf16 hi/lo activation planes, except the down projection above "
+                     "16 rows (weights widened to f16 x one f16 activation plane); attention: f16 (q hi/lo, K, V, P); "
+                     "fp32 accumulate"),
         "data": "synthetic",
         "config": {"workload": f"copy-span splice forward, Llama-style 7B shape (32 layers, d_model 4096, "
                                f"32 q / 8 kv heads x 128, SwiGLU 14336, vocab 32000), random-init weights, "
