@@ -273,8 +273,12 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& a, int n_rg, in
   prep(ra0);
   astore(ra0, ch(0));
   __syncthreads();
+  // The loop runs while both of an iteration's weight loads are in range;
+  // the last two chunks (or the last one) are finished after it, so no
+  // weights are streamed past the last chunk (a clamped repeat would fetch
+  // them from HBM again: the loads are non-temporal).
   int i = 0;
-  for (; i + 1 < ncs; i += 2) {
+  for (; i + 2 < ncs; i += 2) {
     aload(ra0, ch(i + 2));
     wload(w1, ch(i + 1));
     __builtin_amdgcn_sched_barrier(0);
@@ -292,7 +296,19 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& a, int n_rg, in
     astore(ra0, ch(i + 2));
     __syncthreads();
   }
-  if (i < ncs) compute(w0);
+  if (i + 1 < ncs) {
+    // chunks i and i + 1 left: w0 holds chunk i, ra1 the activations of i + 1
+    wload(w1, ch(i + 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(w0);
+    prep(ra1);
+    __syncthreads();
+    astore(ra1, ch(i + 1));
+    __syncthreads();
+    compute(w1);
+  } else if (i < ncs) {
+    compute(w0);
+  }
   // lane: activation row m = i16, weight rows 4g + r of the block
   const int m = i16;
   if (EPI == EPI_SWIGLU) {
@@ -616,10 +632,10 @@ constexpr int TN8_GATE_UP = 224, TN8_QKV = 192;
   __global__ void __launch_bounds__(256) k_gemm_reduce_##NAME(GemmArgs a, int splits) {    \
     gemm_reduce_body<EPI>(a, splits);                                                      \
   }                                                                                        \
-  __global__ void __launch_bounds__(256) k_gemv_##NAME(GemmArgs a, int n_rg, int splits) { \
+  __global__ void __launch_bounds__(256, 2) k_gemv_##NAME(GemmArgs a, int n_rg, int splits) { \
     gemm_skinny_body<EPI, false>(a, n_rg, splits);                                         \
   }                                                                                        \
-  __global__ void __launch_bounds__(256) k_gemvn_##NAME(GemmArgs a, int n_rg, int splits) { \
+  __global__ void __launch_bounds__(256, 2) k_gemvn_##NAME(GemmArgs a, int n_rg, int splits) { \
     gemm_skinny_body<EPI, true>(a, n_rg, splits);                                          \
   }                                                                                        \
   __global__ void __launch_bounds__(256) k_gemm_f32_##NAME(GemmArgs a) { gemm_f32_body<EPI>(a); }
