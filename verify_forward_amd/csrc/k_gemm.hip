@@ -18,11 +18,12 @@
 //     rows and a K range; the activation chunk is shared through LDS and
 //     each wave streams 16 weight rows into registers (sixteen lanes per
 //     row) and transposes them to MFMA fragments through LDS.
-//   * tiled (M > 16): a work-group of eight (or four) waves owns 256 weight
-//     rows and 256 (or 128) activation rows; each wave computes all 256
-//     weight rows against its own 32 activation rows.  The weight tile is the
-//     only operand that goes through LDS (three buffers, k steps of 32,
-//     loaded three steps ahead into registers); each wave loads its
+//   * tiled (M > 16): a work-group of eight waves owns 256 weight rows and
+//     256 (or 128) activation rows; each wave computes all 256 weight rows
+//     against its own 32 (or 16) activation rows.  The weight tile is the
+//     only operand that goes through LDS (three buffers, k steps of 32, or
+//     64 for the 128-row tiles, loaded three steps ahead into registers);
+//     each wave loads its
 //     activation fragments (both planes) straight into registers two steps
 //     ahead.  LDS traffic per
 //     multiply-add is then set by the weights alone, which keeps the LDS
@@ -330,8 +331,7 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& a, int n_rg, in
 // ---------------------------------------------------------------------------
 // bf16 tiled
 // ---------------------------------------------------------------------------
-constexpr int TK = 32;         // k per pipeline step (one MFMA k-slice)
-constexpr int WLD = TK + 8;    // LDS row stride of a weight stage (80 bytes: 16-row fragment reads hit distinct banks)
+constexpr int TK = 32;         // one MFMA k-slice (the split heuristic counts k in these steps)
 
 // Work-group -> (weight tile tn, activation tile tm, k split).  Work-groups
 // are dealt to the eight XCDs round-robin (id % 8); each XCD takes a
@@ -354,14 +354,20 @@ __device__ __forceinline__ void gemm_tile_of(int n_tn, int n_tm, int splits, int
 // the weight tile is widened from bf16 to half (exact in half's normal
 // range) as it is written to LDS and each fragment pair takes one
 // v_mfma_f32_16x16x32_f16 product.
-template <int EPI, int TN, int NW, int MB, bool F16A = false>
+// TKK: k per pipeline step.  The 128-row tiles (17-128 rows, weight-bound)
+// take 64 (each weight row then arrives as whole 128-byte lines: N = 64 step
+// 7.68 -> 7.28 ms); the 256-row tiles keep 32 (registers).
+template <int EPI, int TN, int NW, int MB, bool F16A = false, int TKK = (MB == 1 ? 64 : 32)>
 __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& a, int n_tn, int n_tm, int splits) {
   constexpr int NT = 64 * NW;       // threads
   constexpr int TM = 16 * MB * NW;  // activation rows per tile (MB 16-row blocks per wave)
   constexpr int NB = TN / 16;       // 16-row weight blocks (every wave covers all of them)
-  constexpr int WCH = (TN * 4 + NT - 1) / NT;  // 16-byte weight chunks per thread per k step
+  constexpr int KH = TKK / 32;                  // 32-wide k halves per step
+  constexpr int CPR = TKK / 8;                  // 16-byte chunks per weight row and step
+  constexpr int WLDK = TKK + 8;                 // LDS row stride of a weight stage (80 or 144 bytes: the 16 rows of a fragment read hit distinct banks)
+  constexpr int WCH = (TN * CPR + NT - 1) / NT;  // 16-byte weight chunks per thread per k step
   static_assert(TN % 32 == 0, "whole gate/up block pairs");
-  __shared__ __attribute__((aligned(16))) bf16_t sw[3][TN * WLD];
+  __shared__ __attribute__((aligned(16))) bf16_t sw[3][TN * WLDK];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, i16 = lane & 15;
@@ -377,9 +383,9 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& a, int n_tn, int
     // when the tile's chunks do not divide evenly, the threads past the last
     // chunk load and store the last one again (same data, same place), so
     // every load and store stays unconditional
-    const int c = min(tid + NT * i, TN * 4 - 1);
-    const int row = c >> 2, col = (c & 3) * 8;
-    wsoff[i] = row * WLD + col;
+    const int c = min(tid + NT * i, TN * CPR - 1);
+    const int row = c / CPR, col = (c % CPR) * 8;
+    wsoff[i] = row * WLDK + col;
     int64_t wr;
     if (EPI == EPI_SWIGLU) {
       // 16-row interleave: even blocks gate, odd blocks up, same output columns
@@ -414,47 +420,53 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& a, int n_tn, int
   // waits for one stage never cover another stage's loads.
   auto wload = [&](u32x4 (&r)[WCH], int kt) {
 #pragma unroll
-    for (int i = 0; i < WCH; ++i) r[i] = *(const u32x4*)(wsrc[i] + kt * TK);
+    for (int i = 0; i < WCH; ++i) r[i] = *(const u32x4*)(wsrc[i] + kt * TKK);
   };
-  auto aload = [&](u32x4 (&r)[MB][2], int kt) {
+  auto aload = [&](u32x4 (&r)[MB][2 * KH], int kt) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      r[mb][0] = *(const u32x4*)(ahp[mb] + kt * TK);
-      if (!F16A) r[mb][1] = *(const u32x4*)(alp[mb] + kt * TK);
-    }
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int h = 0; h < KH; ++h) {
+        r[mb][2 * h] = *(const u32x4*)(ahp[mb] + kt * TKK + 32 * h);
+        if (!F16A) r[mb][2 * h + 1] = *(const u32x4*)(alp[mb] + kt * TKK + 32 * h);
+      }
   };
   auto wstore = [&](const u32x4 (&r)[WCH], int buf) {
 #pragma unroll
     for (int i = 0; i < WCH; ++i) *(u32x4*)(&sw[buf][wsoff[i]]) = F16A ? bf16x8_to_f16x8(r[i]) : r[i];
   };
-  auto compute = [&](int buf, const u32x4 (&ra)[MB][2]) {
+  auto compute = [&](int buf, const u32x4 (&ra)[MB][2 * KH]) {
     if (!live) {
       // consume the activation registers anyway: otherwise their loads are
       // still in flight on this path when the next loads reuse the registers,
       // and the compiler guards every later load with a wait for all of them
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        if (F16A) asm volatile("" ::"v"(ra[mb][0]));
-        else asm volatile("" ::"v"(ra[mb][0]), "v"(ra[mb][1]));
-      }
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int h = 0; h < KH; ++h) {
+          if (F16A) asm volatile("" ::"v"(ra[mb][2 * h]));
+          else asm volatile("" ::"v"(ra[mb][2 * h]), "v"(ra[mb][2 * h + 1]));
+        }
       return;
     }
 #pragma unroll
+    for (int h = 0; h < KH; ++h)
+#pragma unroll
     for (int x = 0; x < NB; ++x) {
-      const u32x4 w = *(const u32x4*)(&sw[buf][(x * 16 + i16) * WLD + g * 8]);
+      const u32x4 w = *(const u32x4*)(&sw[buf][(x * 16 + i16) * WLDK + 32 * h + g * 8]);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         if (F16A) {
-          acc[x][mb] = mfma16(w, ra[mb][0], acc[x][mb]);
+          acc[x][mb] = mfma16(w, ra[mb][2 * h], acc[x][mb]);
         } else {
-          acc[x][mb] = mfma16_bf(w, ra[mb][0], acc[x][mb]);
-          acc[x][mb] = mfma16_bf(w, ra[mb][1], acc[x][mb]);
+          acc[x][mb] = mfma16_bf(w, ra[mb][2 * h], acc[x][mb]);
+          acc[x][mb] = mfma16_bf(w, ra[mb][2 * h + 1], acc[x][mb]);
         }
       }
     }
   };
 
-  const int nk = a.K / TK;
+  const int nk = a.K / TKK;
   const int kt0 = (int)((int64_t)nk * sp / splits), kt1 = (int)((int64_t)nk * (sp + 1) / splits);
   auto cl = [&](int kt) { return min(kt, kt1 - 1); };  // past the end: load the last step again (never used)
   // Pipeline over three LDS buffers and three register buffers per operand:
@@ -463,7 +475,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& a, int n_tn, int
   // of step j are loaded at the start of step j - 2 into ra[j%3].  The
   // prologue issues its loads in the order the loop does, so the loop is
   // entered with the same loads in flight as it is re-entered.
-  u32x4 rw0[WCH], rw1[WCH], rw2[WCH], ra0[MB][2], ra1[MB][2], ra2[MB][2];
+  u32x4 rw0[WCH], rw1[WCH], rw2[WCH], ra0[MB][2 * KH], ra1[MB][2 * KH], ra2[MB][2 * KH];
   wload(rw0, kt0);
   wload(rw1, cl(kt0 + 1));
   aload(ra0, kt0);
