@@ -4,8 +4,9 @@ SwiGLU 14336, vocab 32000, bf16 weights; KV cache of L = 16384 tokens; a copy
 span of N = 512 tokens from a duplicated line of the repeated-line prompt;
 a per-position mask allowing 60% of the vocabulary; COMMIT mode), plus
 splices of N = 128 (the other span length of the 7B configuration, on the
-17-128-row projection kernels) and N = 16 (the weight-streaming path) over
-the same cache.
+17-128-row projection kernels), N = 16 (the weight-streaming path) and N = 4
+(the sliced RMSNorm folded into the projections, and attention with
+fragments loaded straight from the paged cache) over the same cache.
 
 The float64 oracle computes every row of both splices, layer by layer, with
 each layer's weights widened to float64 once (about a minute of CPU).
@@ -55,17 +56,19 @@ def test_llama7b_bench_configuration():
     dev = "cuda"
     shape = synth.LLAMA_7B
     cfg = Config.of(shape)
-    L, N, NM, NS = 16384, 512, 128, 16
+    L, N, NM, NS, NT = 16384, 512, 128, 16, 4
     W = synth.make_weights(shape, device=dev)
     k_log, v_log = synth.random_kv_logical(shape, L, device=dev)
     prompt = synth.make_line_prompt(L, shape.vocab)
     span = synth.pick_span(prompt, N)
     span16 = synth.pick_span(prompt, NS, which=1)
     span128 = synth.pick_span(prompt, NM, which=2)
+    span4 = synth.pick_span(prompt, NT, which=3)
     n_allowed = int(round(0.6 * shape.vocab))
     mask = synth.allowed_fraction_mask(N, shape.vocab, n_allowed)
     mask16 = synth.allowed_fraction_mask(NS, shape.vocab, n_allowed, which=1)
     mask128 = synth.allowed_fraction_mask(NM, shape.vocab, n_allowed, which=2)
+    mask4 = synth.allowed_fraction_mask(NT, shape.vocab, n_allowed, which=3)
     model = cad.cad_model_create(shape, W, max_tokens=N)
 
     # ---- GPU: the benchmarked splice, and an N = 16 splice on a fresh copy
@@ -88,8 +91,15 @@ def test_llama7b_bench_configuration():
     cad.cad_splice_forward(model, kv128, L, H.tensors_i32(span128),
                            torch.from_numpy(mask128.view(np.int32)).to(dev), cad.CAD_COMMIT, o128["argmax"],
                            o128["accepted"], o128["logits"], o128["status"])
+    nb4 = (L + NT + BLK - 1) // BLK
+    kv4 = cad.KVCache.alloc(shape, nb4, synth.identity_block_table(nb4), device=dev)
+    H.write_prefix(kv4, k_log, v_log)
+    o4 = H.outputs(NT, shape.vocab)
+    cad.cad_splice_forward(model, kv4, L, H.tensors_i32(span4), torch.from_numpy(mask4.view(np.int32)).to(dev),
+                           cad.CAD_COMMIT, o4["argmax"], o4["accepted"], o4["logits"], o4["status"])
     torch.cuda.synchronize()
     assert int(o["status"][0]) == 0 and int(o16["status"][0]) == 0 and int(o128["status"][0]) == 0
+    assert int(o4["status"][0]) == 0 and int(o4["accepted"][0]) == NT
     assert int(o["accepted"][0]) == N and int(o16["accepted"][0]) == NS and int(o128["accepted"][0]) == NM
     gk, gv = _rows(kv, L, N)          # appended K/V of all 512 rows
     gk16, gv16 = _rows(kv16, L, NS)
@@ -97,13 +107,18 @@ def test_llama7b_bench_configuration():
     lg = o["logits"].cpu().numpy()
     lg16 = o16["logits"].cpu().numpy()
     lg128 = o128["logits"].cpu().numpy()
+    lg4 = o4["logits"].cpu().numpy()
+    # the four appended rows sit in slots 0..3 of block L / 16 (identity table)
+    gk4 = kv4.k[:, L // BLK, :, :NT, :].to(torch.float64).cpu().numpy()
+    gv4 = kv4.v[:, L // BLK, :, :, :NT].transpose(2, 3).to(torch.float64).cpu().numpy()
 
     # ---- oracle, layer by layer: pass A (all N rows), pass B (N = 128), pass C (N = 16)
     emb = W["tok_embed"]
     xa = emb[torch.as_tensor(span, device=dev).long()].double().cpu().numpy()
     xc = emb[torch.as_tensor(span16, device=dev).long()].double().cpu().numpy()
     xb = emb[torch.as_tensor(span128, device=dev).long()].double().cpu().numpy()
-    ka, va, kc, vc, kb, vb = [], [], [], [], [], []
+    xd = emb[torch.as_tensor(span4, device=dev).long()].double().cpu().numpy()
+    ka, va, kc, vc, kb, vb, kd, vd = [], [], [], [], [], [], [], []
     hd, hkv = shape.head_dim, shape.n_kv_heads
     for ci in range(shape.n_layers):
         lw = {k: t.double().cpu().numpy() for k, t in W["layers"][ci].items()}
@@ -119,26 +134,33 @@ def test_llama7b_bench_configuration():
         cache_b = KVCache([np.concatenate([kp, z128], axis=1)], [np.concatenate([vp, z128], axis=1)])
         xb = splice_layer(cfg, lw, cache_b, 0, xb, L)
         kb.append(cache_b.k[0][:, L:]); vb.append(cache_b.v[0][:, L:])
-        del lw, kp, vp, cache_a, cache_b, cache_c
+        z4 = np.zeros((hkv, NT, hd))
+        cache_d = KVCache([np.concatenate([kp, z4], axis=1)], [np.concatenate([vp, z4], axis=1)])
+        xd = splice_layer(cfg, lw, cache_d, 0, xd, L)
+        kd.append(cache_d.k[0][:, L:]); vd.append(cache_d.v[0][:, L:])
+        del lw, kp, vp, cache_a, cache_b, cache_c, cache_d
     top = {"final_norm": W["final_norm"].double().cpu().numpy(), "lm_head": W["lm_head"].double().cpu().numpy()}
     ref_a, ref_b, ref_c = final_logits(cfg, top, xa), final_logits(cfg, top, xb), final_logits(cfg, top, xc)
+    ref_d = final_logits(cfg, top, xd)
 
     errs = {"N=512": np.max(np.abs(lg - ref_a)), "N=128": np.max(np.abs(lg128 - ref_b)),
-            "N=16": np.max(np.abs(lg16 - ref_c))}
+            "N=16": np.max(np.abs(lg16 - ref_c)), "N=4": np.max(np.abs(lg4 - ref_d))}
     kv_checks = {"kv N=512": [(gk, np.stack(ka)), (gv, np.stack(va))],
                  "kv N=128": [(gk128, np.stack(kb)), (gv128, np.stack(vb))],
-                 "kv N=16": [(gk16, np.stack(kc)), (gv16, np.stack(vc))]}
+                 "kv N=16": [(gk16, np.stack(kc)), (gv16, np.stack(vc))],
+                 "kv N=4": [(gk4, np.stack(kd)), (gv4, np.stack(vd))]}
     kv_ok = {}
     for k, pairs in kv_checks.items():
         res = [H.kv_close(g, r, TOL) for g, r in pairs]
         kv_ok[k] = all(ok for ok, _ in res)
         errs[k] = max(e for _, e in res)
     print("7B max|diff|: " + ", ".join(f"{k} {v:.3e}" for k, v in errs.items()), flush=True)
-    for k in ("N=512", "N=128", "N=16"):
+    for k in ("N=512", "N=128", "N=16", "N=4"):
         assert errs[k] <= TOL, (k, errs[k])
     for k, ok in kv_ok.items():
         assert ok, (k, errs[k])
     graded = _check_decisions(ref_a, mask, o["argmax"].cpu().numpy())
     graded += _check_decisions(ref_b, mask128, o128["argmax"].cpu().numpy())
     graded += _check_decisions(ref_c, mask16, o16["argmax"].cpu().numpy())
-    print(f"7B argmax bit-exact on {graded}/{N + NM + NS} graded rows", flush=True)
+    graded += _check_decisions(ref_d, mask4, o4["argmax"].cpu().numpy())
+    print(f"7B argmax bit-exact on {graded}/{N + NM + NS + NT} graded rows", flush=True)
