@@ -406,8 +406,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU: the splice forward of one "
-                                   "sequence is measured on a single MI355X; multi-GPU runs are not part "
-                                   "of this build", "n_gpus": args.gpus}))
+                                   "sequence is measured on a single MI355X; the library has no multi-GPU path",
+                          "n_gpus": args.gpus}))
         sys.exit(2)
 
     import torch
