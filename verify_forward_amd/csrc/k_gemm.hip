@@ -96,31 +96,46 @@ __device__ __forceinline__ void epi4(const GemmArgs& a, int m, int n, f32x4 c, f
 // ---------------------------------------------------------------------------
 // A work-group of four waves owns 64 weight rows (four 16-row blocks, one
 // per wave; for SWIGLU a block is 8 gate rows + the 8 matching up rows) and
-// a range of K in chunks of 512.  The activations of a chunk (at most 16
+// a range of K in chunks of SK_KC.  The activations of a chunk (at most 16
 // rows, both planes) are staged once in LDS and shared by the four waves.
-// Each wave streams its 16 weight rows (1 KB per row and chunk) into
+// Each wave streams its 16 weight rows (512 B per row and chunk) into
 // registers one chunk ahead, sixteen lanes per row per load (256 contiguous
 // bytes: HBM streams at ~5 TB/s this way against ~4 TB/s with four lanes
 // per row), and turns them into MFMA fragments through a small LDS
-// transpose, half a chunk at a time.  With K split over S work-groups the
-// partial sums go to the workspace and the consumer adds them.
-constexpr int SK_KC = 512;             // k per chunk
-constexpr int SK_ALD = SK_KC + 8;      // LDS row stride of the activation chunk (1040 B: conflict-free)
-constexpr int SK_WLD = SK_KC / 2 + 8;  // LDS row stride of a half-chunk weight transpose (528 B: conflict-free)
-constexpr int SK_AIT = 16 * 2 * (SK_KC / 8) / 256;  // 16-byte activation pieces per thread and chunk
+// transpose, 256 k at a time.  With K split over S work-groups the partial
+// sums go to the workspace and the consumer adds them.
+constexpr int SK_WLD = 256 + 8;  // LDS row stride of a half-chunk (256 k) weight transpose (528 B: conflict-free)
+// k per chunk.  256 rather than 512: the work-group then needs 150 VGPRs
+// and 50 KB of LDS instead of 246 and 66 KB, so three fit per CU instead of
+// two, and the weight streams ran faster in every projection (N = 1:
+// gate/up 49.6 -> 42.1 us, down 23.7 -> 19.7, QKV 13.9 -> 11.3; step 4.77
+// -> 4.31 ms).  The body is written for either width.
+constexpr int SK_KC = 256;
 
-// Staged activation registers of one chunk: the two bf16 planes (eight
-// 16-byte pieces per thread), or (NORM) four rows of eight fp32 residual
+// Chunk shapes for KC = 512 or 256 k per chunk.
+template <int KC> struct SkShape {
+  static constexpr int ALD = KC + 8;              // LDS row stride of the activation chunk (conflict-free)
+  static constexpr int PPR = KC / 8;              // 16-byte pieces per activation row and plane
+  static constexpr int AIT = 2 * 16 * PPR / 256;  // pieces per thread and chunk, both planes
+  static constexpr int NR = AIT / 2;              // activation rows per thread
+  static constexpr int RS = 256 / PPR;            // row step between a thread's rows
+  static constexpr int NWL = KC / 32;             // 16-byte weight loads per lane and chunk
+  static constexpr int NH = KC / 256;             // 256-wide halves per chunk
+};
+
+// Staged activation registers of one chunk: the two bf16 planes (AIT
+// 16-byte pieces per thread), or (NORM) NR rows of eight fp32 residual
 // values (bits) and the eight matching gains; the normalised hi / lo pieces
 // of row j then replace its fp32 values in place (x[2j], x[2j + 1]), so the
 // stage costs four registers more than the plain one.
-template <bool NORM> struct SkStage { u32x4 r[SK_AIT]; };
-template <> struct SkStage<true> { u32x4 x[8]; u32x4 g; };
+template <bool NORM, int KC> struct SkStage { u32x4 r[SkShape<KC>::AIT]; };
+template <int KC> struct SkStage<true, KC> { u32x4 x[2 * SkShape<KC>::NR]; u32x4 g; };
 
-template <int EPI, bool NORM>
+template <int EPI, bool NORM, int KC>
 __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& a, int n_rg, int splits) {
-  __shared__ __attribute__((aligned(16))) bf16_t sa[2][16 * SK_ALD];     // [plane][row][k]
-  __shared__ __attribute__((aligned(16))) bf16_t swt[4][16 * SK_WLD];    // per-wave weight transpose
+  using SH = SkShape<KC>;
+  __shared__ __attribute__((aligned(16))) bf16_t sa[2][16 * SH::ALD];     // [plane][row][k]
+  __shared__ __attribute__((aligned(16))) bf16_t swt[4][16 * SK_WLD];     // per-wave weight transpose
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, i16 = lane & 15;
   const int rg = blockIdx.x % n_rg, sp = blockIdx.x / n_rg;
@@ -134,69 +149,76 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& a, int n_rg, in
     }
     return min(blk * 16 + i, a.N - 1);
   };
-  // load j (0..15) of a chunk: block row 4 (j % 4) + lane / 16, k offset
-  // 128 (j / 4) + 8 (lane % 16) within the chunk
+  // load j (0 .. NWL - 1) of a chunk: block row 4 (j % 4) + lane / 16, k
+  // offset 128 (j / 4) + 8 (lane % 16) within the chunk
   const bf16_t* wp[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) wp[q] = W + wrow_of(4 * q + g) * a.ldw + 8 * i16;
-  const int nch = (a.K + SK_KC - 1) / SK_KC;
+  const int nch = (a.K + KC - 1) / KC;
   const int c0 = (int)((int64_t)nch * sp / splits), c1 = (int)((int64_t)nch * (sp + 1) / splits);
-  // activation staging: piece q = tid + 256*j is 16 bytes: plane q / 1024,
-  // row (q / 64) % 16, k offset 8 * (q % 64) within the chunk.  Rows >= M and
-  // k past K are written as zeros (their products vanish).  With NORM the
-  // thread holds the same pieces as fp32 values of rows wave + 4j (j < 4) and
-  // writes both planes of each.
-  const bf16_t* ap[SK_AIT];
-  int aoff[SK_AIT], akk[SK_AIT];
-  bool aok[SK_AIT];
+  // activation staging: piece q = tid + 256*j is 16 bytes: plane q / (16 PPR),
+  // row (q / PPR) % 16, k offset 8 * (q % PPR) within the chunk.  Rows >= M
+  // and k past K are written as zeros (their products vanish).  With NORM
+  // the thread holds the same pieces as fp32 values of rows r0 + RS j
+  // (r0 = tid / PPR, j < NR) and writes both planes of each.
+  const bf16_t* ap[SH::AIT];
+  int aoff[SH::AIT], akk[SH::AIT];
+  bool aok[SH::AIT];
 #pragma unroll
-  for (int j = 0; j < SK_AIT; ++j) {
+  for (int j = 0; j < SH::AIT; ++j) {
     const int q = tid + 256 * j;
-    const int plane = q >> 10, row = (q >> 6) & 15, kk = 8 * (q & 63);
-    aoff[j] = plane * (16 * SK_ALD) + row * SK_ALD + kk;
+    const int plane = q / (16 * SH::PPR), row = (q / SH::PPR) % 16, kk = 8 * (q % SH::PPR);
+    aoff[j] = plane * (16 * SH::ALD) + row * SH::ALD + kk;
     akk[j] = kk;
     aok[j] = row < a.M;
     ap[j] = (const bf16_t*)(plane ? a.A_lo : a.A) + (int64_t)min(row, a.M - 1) * a.lda + kk;
   }
-  // NORM: 1 / rms of this thread's rows (wave + 4j).  Lane l loads slice
-  // sums l % 16 and l % 16 + 16 (at most 32 slices) of row wave + 4 (l / 16),
-  // all in one round trip; a fixed butterfly over the 16 lanes of a row adds
-  // them, and lane 16 j hands row j's result to the whole wave.
-  float rsj[4] = {0.f, 0.f, 0.f, 0.f};
+  const int r0 = tid / SH::PPR, nkk = 8 * (tid % SH::PPR);  // NORM: first row and k offset
+  // NORM: 1 / rms of this thread's rows.  Four lanes per row (lane l: row
+  // l / 4) load every fourth slice sum (at most 32 slices), all in one round
+  // trip, add them in order and then over the four lanes by a fixed
+  // butterfly; each thread then fetches its rows' values from those lanes.
+  float rsj[SH::NR];
+#pragma unroll
+  for (int j = 0; j < SH::NR; ++j) rsj[j] = 0.f;
   if constexpr (NORM) {
-    const int u = lane & 15;
-    const float* ssr = a.norm_ss + (int64_t)min(wave + 4 * (lane >> 4), a.M - 1) * a.norm_slices;
-    float t = (u < a.norm_slices ? ssr[u] : 0.f) + (u + 16 < a.norm_slices ? ssr[u + 16] : 0.f);
+    const int sub = lane & 3;
+    const float* ssr = a.norm_ss + (int64_t)min(lane >> 2, a.M - 1) * a.norm_slices;
+    float v[8];
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) t += __shfl_xor(t, o);
-    const float rs = 1.0f / sqrtf(t / (float)a.K + a.norm_eps);
+    for (int t = 0; t < 8; ++t) v[t] = sub + 4 * t < a.norm_slices ? ssr[sub + 4 * t] : 0.f;
+    float tsum = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) rsj[j] = __shfl(rs, 16 * j);
+    for (int t = 0; t < 8; ++t) tsum += v[t];
+    tsum += __shfl_xor(tsum, 1);
+    tsum += __shfl_xor(tsum, 2);
+    const float rs = 1.0f / sqrtf(tsum / (float)a.K + a.norm_eps);
+#pragma unroll
+    for (int j = 0; j < SH::NR; ++j) rsj[j] = __shfl(rs, 4 * min(r0 + SH::RS * j, 15));
   }
-  auto aload = [&](SkStage<NORM>& st, int c) {
+  auto aload = [&](SkStage<NORM, KC>& st, int c) {
     if constexpr (NORM) {
-      const int kk = 8 * lane;
-      const int off = min(c * SK_KC, a.K - 8 - kk);
-      st.g = *(const u32x4*)((const bf16_t*)a.norm_g + off + kk);
+      const int off = min(c * KC, a.K - 8 - nkk);
+      st.g = *(const u32x4*)((const bf16_t*)a.norm_g + off + nkk);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float* xp = (const float*)a.A + (int64_t)min(wave + 4 * j, a.M - 1) * a.lda + off + kk;
+      for (int j = 0; j < SH::NR; ++j) {
+        const float* xp = (const float*)a.A + (int64_t)min(r0 + SH::RS * j, a.M - 1) * a.lda + off + nkk;
         st.x[2 * j] = *(const u32x4*)xp;
         st.x[2 * j + 1] = *(const u32x4*)(xp + 4);
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < SK_AIT; ++j) st.r[j] = *(const u32x4*)(ap[j] + min(c * SK_KC, a.K - 8 - akk[j]));
+      for (int j = 0; j < SH::AIT; ++j) st.r[j] = *(const u32x4*)(ap[j] + min(c * KC, a.K - 8 - akk[j]));
     }
   };
   // NORM: normalise and split the staged fp32 rows, in registers, before the
   // barrier that guards the LDS store: row j's hi piece replaces x[2j] and
-  // its lo piece x[2j + 1]; rows >= M (whole waves) skip the work
-  auto prep = [&](SkStage<NORM>& st) {
+  // its lo piece x[2j + 1]; rows >= M skip the work
+  auto prep = [&](SkStage<NORM, KC>& st) {
     if constexpr (NORM) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (wave + 4 * j >= a.M) continue;
+      for (int j = 0; j < SH::NR; ++j) {
+        if (r0 + SH::RS * j >= a.M) continue;
         u32x4 hi, lo;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -216,38 +238,38 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& a, int n_rg, in
       }
     }
   };
-  // piece j of the stage: plane j / 4, row wave + 4 (j % 4)
-  auto piece = [&](const SkStage<NORM>& st, int j) -> u32x4 {
-    if constexpr (NORM) return st.x[j < 4 ? 2 * j : 2 * (j - 4) + 1];
+  // piece j of the stage: plane j / NR, row r0 + RS (j % NR)
+  auto piece = [&](const SkStage<NORM, KC>& st, int j) -> u32x4 {
+    if constexpr (NORM) return st.x[j < SH::NR ? 2 * j : 2 * (j - SH::NR) + 1];
     else return st.r[j];
   };
   // unconditional stores (a branch here makes the compiler wait for every
   // load in flight, the next chunk's weights included)
-  auto astore = [&](const SkStage<NORM>& st, int c) {
+  auto astore = [&](const SkStage<NORM, KC>& st, int c) {
 #pragma unroll
-    for (int j = 0; j < SK_AIT; ++j) {
-      const bool keep = aok[j] && c * SK_KC + akk[j] < a.K;
+    for (int j = 0; j < SH::AIT; ++j) {
+      const bool keep = aok[j] && c * KC + akk[j] < a.K;
       *(u32x4*)(&sa[0][0] + aoff[j]) = keep ? piece(st, j) : u32x4{0u, 0u, 0u, 0u};
     }
   };
   // weights past K are clamped inside the row; the activations there are zero
-  auto wload = [&](u32x4 (&r)[16], int c) {
+  auto wload = [&](u32x4 (&r)[SH::NWL], int c) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      r[j] = __builtin_nontemporal_load((const u32x4*)(wp[j & 3] + min(c * SK_KC + 128 * (j >> 2), a.K - 8 - 8 * i16)));
+    for (int j = 0; j < SH::NWL; ++j)
+      r[j] = __builtin_nontemporal_load((const u32x4*)(wp[j & 3] + min(c * KC + 128 * (j >> 2), a.K - 8 - 8 * i16)));
   };
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   bf16_t* tw = &swt[wave][0];
-  auto compute = [&](const u32x4 (&w)[16]) {
+  auto compute = [&](const u32x4 (&w)[SH::NWL]) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < SH::NH; ++h) {
       // half h: loads 8h .. 8h+7 hold k 256 h .. 256 h + 255 of the chunk
 #pragma unroll
       for (int j = 8 * h; j < 8 * h + 8; ++j)
         *(u32x4*)(tw + (4 * (j & 3) + g) * SK_WLD + 128 * ((j >> 2) & 1) + 8 * i16) = w[j];
       const bf16_t* tr = tw + i16 * SK_WLD + 8 * g;
-      const bf16_t* sh = &sa[0][0] + i16 * SK_ALD + 256 * h + 8 * g;
-      const bf16_t* sl = &sa[1][0] + i16 * SK_ALD + 256 * h + 8 * g;
+      const bf16_t* sh = &sa[0][0] + i16 * SH::ALD + 256 * h + 8 * g;
+      const bf16_t* sl = &sa[1][0] + i16 * SH::ALD + 256 * h + 8 * g;
 #pragma unroll
       for (int s2 = 0; s2 < 8; ++s2) {
         const u32x4 wf = *(const u32x4*)(tr + 32 * s2);
@@ -264,8 +286,8 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& a, int n_rg, in
   // (rotated by the row group), spreading the memory channels in use.
   const int ncs = c1 - c0, rot = rg % ncs;
   auto ch = [&](int i) { i = min(i, ncs - 1); return c0 + (i + rot) % ncs; };  // i-th chunk visited
-  u32x4 w0[16], w1[16];
-  SkStage<NORM> ra0, ra1;
+  u32x4 w0[SH::NWL], w1[SH::NWL];
+  SkStage<NORM, KC> ra0, ra1;
   // the first weights are requested before the first activations are
   // waited for (loads complete in order, so that wait leaves them in flight)
   aload(ra0, ch(0));
@@ -645,10 +667,10 @@ constexpr int TN8_GATE_UP = 224, TN8_QKV = 192;
     gemm_reduce_body<EPI>(a, splits);                                                      \
   }                                                                                        \
   __global__ void __launch_bounds__(256, 2) k_gemv_##NAME(GemmArgs a, int n_rg, int splits) { \
-    gemm_skinny_body<EPI, false>(a, n_rg, splits);                                         \
+    gemm_skinny_body<EPI, false, SK_KC>(a, n_rg, splits);                                  \
   }                                                                                        \
   __global__ void __launch_bounds__(256, 2) k_gemvn_##NAME(GemmArgs a, int n_rg, int splits) { \
-    gemm_skinny_body<EPI, true>(a, n_rg, splits);                                          \
+    gemm_skinny_body<EPI, true, SK_KC>(a, n_rg, splits);                                   \
   }                                                                                        \
   __global__ void __launch_bounds__(256) k_gemm_f32_##NAME(GemmArgs a) { gemm_f32_body<EPI>(a); }
 
@@ -688,14 +710,18 @@ static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled8, int t
     const int nblk = (EPI == EPI_SWIGLU) ? (a.N + 7) / 8 : (a.N + 15) / 16;
     const int n_rg = (nblk + 3) / 4;
     const int nch = (a.K + SK_KC - 1) / SK_KC;
-    // when the consumer adds partial sums: one chunk per work-group (the
-    // most chunks the partial workspace holds, in whole-chunk splits) -- a
-    // work-group streaming a single chunk keeps the most loads in flight for
-    // its weights (measured: down at N = 1, 28 x 64 work-groups of one chunk
-    // ran at 5 TB/s, 8 x 64 of three or four chunks at 4.2)
+    // when the consumer adds partial sums: the most splits (whole chunks,
+    // within the partial workspace) -- work-groups that stream little each
+    // keep the most loads in flight for the weights (measured: down at N = 1,
+    // 28 x 64 work-groups of 512 k ran at 5 TB/s, 8 x 64 of 1536-2048 k at
+    // 4.2) -- but at most one split per 512 k: a split work-group then
+    // streams two 256-wide chunks, and the consumer adds no more partial
+    // planes than one per 512 k (one per 256 k made RoPE's staging 3 us
+    // slower)
     int splits = 1;
+    const int max_splits = (a.K + 511) / 512;
     if (leave)
-      for (int c = nch; c > 1; --c)
+      for (int c = min(nch, max_splits); c > 1; --c)
         if (nch % c == 0 && (int64_t)c * a.M * a.N <= GEMM_SPLIT_FLOATS) {
           splits = c;
           break;

@@ -57,7 +57,7 @@ __global__ void __launch_bounds__(NT) k_rmsnorm(float* __restrict__ x, const flo
   // each of the NT threads keeps up to V4 groups of four elements in
   // registers: one pass over x, all loads issued before the reduction.
   // Pending k-split partial sums of the projection that last wrote x
-  // ([n_part][rows][d], up to one plane per 512-wide k chunk) are added
+  // ([n_part][rows][d], up to one plane per 512 k of the projection) are added
   // first, in split order, and x is written back.
   __shared__ float red[NT / 64];
   const int r = blockIdx.x;
@@ -130,7 +130,7 @@ __global__ void __launch_bounds__(NT) k_rmsnorm(float* __restrict__ x, const flo
 hipError_t launch_rmsnorm(int dtype, float* x, const float* x_part, int n_part, const void* gain, int rows, int d,
                           float eps, void* out, void* out_lo, hipStream_t s) {
   // few rows of 4096 and more (short spans, whose projections leave up to
-  // one partial plane per 512-wide k chunk): 1024 threads, one or two groups
+  // one partial plane per 512 k): 1024 threads, one or two groups
   // of four each, so that 16 / V4 planes are in flight at once; else 256
   const int nt = (d >= 4096 && rows <= 64) ? 1024 : ROW_THREADS;
   const int v4 = (d / 4 + nt - 1) / nt;
