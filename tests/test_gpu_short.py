@@ -8,6 +8,10 @@ put them at ragged cache lengths (partial 32-key tiles and 16-slot
 blocks), on an empty cache, in batched calls of short sequences, with every
 stale cache slot holding NaN (a masked key must contribute nothing, not
 NaN * 0), and with a block id outside the pool (a status bit, no access).
+Batched calls that mix one-token steps with longer copies send every
+sequence through the LDS-staged attention instead, at 64-row query tiles
+(at most 64 query rows per sequence on average) and at 256-row tiles
+(more), with ragged last tiles in both.
 
 Bars: logits max|diff| <= 2e-2 (bf16 models); appended K/V within the same
 bound; argmax bit-exact where the oracle's masked top-2 margin exceeds 0.1.
@@ -168,6 +172,14 @@ def test_short_batched_sequences(model_w):
     _batched_case(shape, W, Wn, Ls=[0, 517, 1000, 33, 2041], Ns=[1, 4, 2, 3, 1], seed=61)
     print(f"shape={shape.name}: 7 rows over 4 sequences", flush=True)
     _batched_case(shape, W, Wn, Ls=[95, 0, 1600, 64], Ns=[1, 2, 1, 3], seed=62)
+
+
+def test_batched_mixed_steps_and_copies(model_w):
+    shape, W, Wn = model_w
+    print(f"shape={shape.name}: 66 rows over 5 sequences (64-row query tiles)", flush=True)
+    _batched_case(shape, W, Wn, Ls=[1200, 0, 900, 2047, 64], Ns=[1, 40, 1, 23, 1], seed=63)
+    print(f"shape={shape.name}: 161 rows over 3 sequences (256-row query tiles)", flush=True)
+    _batched_case(shape, W, Wn, Ls=[700, 1500, 31], Ns=[90, 1, 70], seed=64)
 
 
 def test_short_bad_block_sets_status(model_w):
