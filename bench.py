@@ -401,6 +401,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the serve, looped, s(N) and copy-bandwidth reports")
+    ap.add_argument("--only", choices=["serve", "looped"],
+                    help="run only the batched serve or the looped-block report (one JSON line; for kernel profiles)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain device copy of 1 GiB first (a known-size reference for HBM counters)")
     args = ap.parse_args()
@@ -422,7 +424,13 @@ def main():
         log("[bench] copy calibration: 1 GiB read + 1 GiB written")
     shape = synth.LLAMA_7B
     N, L = args.span, args.L
+    if args.only == "looped":
+        print(json.dumps({"looped": looped_bench()}), flush=True)
+        return
     wl = Workload(shape, L, max_tokens=max(N, 512))
+    if args.only == "serve":
+        print(json.dumps({"serve": serve_bench(wl)}), flush=True)
+        return
     io = wl.inputs(N)
 
     # untimed warmup; its last step records every kernel family to find the dominant one
