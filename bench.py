@@ -322,9 +322,10 @@ def s_of_n(wl, Ns=(8, 64, 512), L=1024):
 # ----------------------------------------------------------------------------
 
 def cpu_baseline(shape, L, N):
-    """Oracle splice of all N rows through 1 and then 2 of the decoder layers
-    (plus the LM head and argmax each time); the full-depth time is
-    extrapolated as t1 + (n_layers - 1) * (t2 - t1)."""
+    """Oracle splice of all N rows through 1 and then 6 of the decoder layers
+    (plus the LM head and argmax each time: about 10 s of CPU work at the 7B
+    shape); the full-depth time is extrapolated as t1 + (n_layers - 1) *
+    (t6 - t1) / 5."""
     import numpy as np
     import torch
     import oracle
@@ -332,7 +333,8 @@ def cpu_baseline(shape, L, N):
     from oracle.decoder import Config, KVCache
     cores = len(os.sched_getaffinity(0))
     times = {}
-    for nl in (1, 2):
+    lo, hi = 1, 6
+    for nl in (lo, hi):
         sub = shape.replace(n_layers=nl)
         W = synth.weights_to_numpy(synth.make_weights(shape, device="cuda", layers=range(nl)))
         kl, vl = synth.random_kv_logical(sub, L, device="cuda")
@@ -349,17 +351,17 @@ def cpu_baseline(shape, L, N):
         log(f"[bench] oracle sample: {nl} layer(s), {N} rows: {times[nl]:.1f}s")
         del W, kv, lg
         torch.cuda.empty_cache()
-    per_layer = max(times[2] - times[1], 1e-9)
-    full = times[1] + (shape.n_layers - 1) * per_layer
+    per_layer = max((times[hi] - times[lo]) / (hi - lo), 1e-9)
+    full = times[lo] + (shape.n_layers - lo) * per_layer
     try:
         blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"]["name"]
     except Exception:
         blas = "unknown"
     return {"value": N / full, "unit": "spliced tokens/s", "cores": cores, "kind": "oracle",
-            "sample": (f"float64 NumPy oracle ({blas}), all {N} span rows through 1 and 2 of the "
+            "sample": (f"float64 NumPy oracle ({blas}), all {N} span rows through {lo} and {hi} of the "
                        f"{shape.n_layers} layers + LM head + masked argmax at L={L}; full depth "
-                       f"extrapolated as t1 + {shape.n_layers - 1}*(t2 - t1) = {full:.1f}s"),
-            "sample_seconds": round(times[1] + times[2], 2)}
+                       f"extrapolated as t{lo} + {shape.n_layers - lo}*(t{hi} - t{lo})/{hi - lo} = {full:.1f}s"),
+            "sample_seconds": round(times[lo] + times[hi], 2)}
 
 
 # ----------------------------------------------------------------------------
