@@ -11,7 +11,9 @@ NaN * 0), and with a block id outside the pool (a status bit, no access).
 Batched calls that mix one-token steps with longer copies send every
 sequence through the LDS-staged attention instead, at 64-row query tiles
 (at most 64 query rows per sequence on average) and at 256-row tiles
-(more), with ragged last tiles in both.
+(more), with ragged last tiles in both.  Rejected calls (span over max_tokens or
+past the block table, negative length, unknown mode) must return their
+status without touching outputs or cache.
 
 Bars: logits max|diff| <= 2e-2 (bf16 models); appended K/V within the same
 bound; argmax bit-exact where the oracle's masked top-2 margin exceeds 0.1.
@@ -180,6 +182,53 @@ def test_batched_mixed_steps_and_copies(model_w):
     _batched_case(shape, W, Wn, Ls=[1200, 0, 900, 2047, 64], Ns=[1, 40, 1, 23, 1], seed=63)
     print(f"shape={shape.name}: 161 rows over 3 sequences (256-row query tiles)", flush=True)
     _batched_case(shape, W, Wn, Ls=[700, 1500, 31], Ns=[90, 1, 70], seed=64)
+
+
+def test_rejected_calls_enqueue_nothing(model_w):
+    """Argument and capacity errors come back as a status before anything is
+    enqueued (outputs and cache keep their bits); a call that fills the block
+    table exactly then runs and matches the oracle."""
+    dev = _dev()
+    shape, W, Wn = model_w
+    cfg = Config.of(shape)
+    nb, N = 7, 3
+    L = nb * BLK - N                  # L + N fills the seven blocks exactly
+    kl, vl = _prefix(shape, L, seed=19, dev=dev)
+    kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device=dev)
+    H.write_prefix(kv, kl, vl)
+    k_before, v_before = kv.k.clone(), kv.v.clone()
+    model = cad.cad_model_create(shape, W, max_tokens=8)
+    o9, o = H.outputs(9, shape.vocab), H.outputs(N, shape.vocab)
+    o9["logits"].fill_(123.0)
+    o["logits"].fill_(123.0)
+    span9 = H.tensors_i32(np.arange(1, 10))
+    span = H.tensors_i32([5, 6, 7])
+
+    def call(L_, sp, out, mode=cad.CAD_COMMIT):
+        cad.cad_splice_forward(model, kv, L_, sp, None, mode, out["argmax"], out["accepted"], out["logits"],
+                               out["status"])
+
+    cases = [(lambda: call(L, span9, o9), cad.CAD_E_CAPACITY),      # N > max_tokens
+             (lambda: call(L + 1, span, o), cad.CAD_E_CAPACITY),    # L + N past the block table
+             (lambda: call(-1, span, o), cad.CAD_E_ARG),            # negative cache length
+             (lambda: call(L, span, o, mode=7), cad.CAD_E_ARG)]     # unknown mode
+    for i, (fn, st) in enumerate(cases):
+        with pytest.raises(cad.CadError) as ei:
+            fn()
+        print(f"  case {i}: status {ei.value.status}: {ei.value}", flush=True)
+        assert ei.value.status == st
+    torch.cuda.synchronize()
+    for out in (o9, o):
+        assert bool((out["argmax"] == -7).all()) and bool((out["logits"] == 123.0).all())
+    assert torch.equal(_bits(kv.k), _bits(k_before)) and torch.equal(_bits(kv.v), _bits(v_before))
+    call(L, span, o)
+    okv = KVCache.from_prefix(kl.double().cpu().numpy(), vl.double().cpu().numpy(), L + N)
+    ref = oracle.splice(cfg, Wn, okv, L, np.array([5, 6, 7]))
+    torch.cuda.synchronize()
+    err = float(np.max(np.abs(o["logits"].cpu().numpy() - ref)))
+    print(f"  at the table's edge (L={L}, N={N}): logits max|diff| {err:.3e}", flush=True)
+    assert int(o["status"][0]) == 0 and int(o["accepted"][0]) == N
+    assert err <= TOL
 
 
 def test_short_bad_block_sets_status(model_w):
