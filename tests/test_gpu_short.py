@@ -13,7 +13,8 @@ sequence through the LDS-staged attention instead, at 64-row query tiles
 (at most 64 query rows per sequence on average) and at 256-row tiles
 (more), with ragged last tiles in both.  Rejected calls (span over max_tokens or
 past the block table, negative length, unknown mode) must return their
-status without touching outputs or cache.
+status without touching outputs or cache.  A batched call at the limit of
+64 sequences runs on both attention paths; one sequence more is refused.
 
 Bars: logits max|diff| <= 2e-2 (bf16 models); appended K/V within the same
 bound; argmax bit-exact where the oracle's masked top-2 margin exceeds 0.1.
@@ -182,6 +183,31 @@ def test_batched_mixed_steps_and_copies(model_w):
     _batched_case(shape, W, Wn, Ls=[1200, 0, 900, 2047, 64], Ns=[1, 40, 1, 23, 1], seed=63)
     print(f"shape={shape.name}: 161 rows over 3 sequences (256-row query tiles)", flush=True)
     _batched_case(shape, W, Wn, Ls=[700, 1500, 31], Ns=[90, 1, 70], seed=64)
+
+
+def test_batched_at_the_sequence_limit(model_w):
+    dev = _dev()
+    shape, W, Wn = model_w
+    n = cad.CAD_MAX_SEQS
+    r = synth.rng(65, n)
+    Ls = [int(x) for x in r.integers(0, 400, size=n)]
+    Ns = [int(x) for x in r.integers(1, 5, size=n)]
+    print(f"shape={shape.name}: {sum(Ns)} rows over {n} sequences (short-span kernels)", flush=True)
+    _batched_case(shape, W, Wn, Ls=Ls, Ns=Ns, seed=66)
+    Ns[17] = 20
+    print(f"shape={shape.name}: {sum(Ns)} rows over {n} sequences, one of 20 rows (LDS-staged)", flush=True)
+    _batched_case(shape, W, Wn, Ls=Ls, Ns=Ns, seed=67)
+    # one sequence more than the limit is refused before anything runs
+    kv = cad.KVCache.alloc(shape, 4, synth.identity_block_table(4), device=dev)
+    model = cad.cad_model_create(shape, W, max_tokens=n + 1)
+    o = H.outputs(n + 1, shape.vocab, n_seq=n + 1)
+    with pytest.raises(cad.CadError) as ei:
+        cad.cad_splice_forward_batched(model, kv, [0] * (n + 1), list(range(n + 2)),
+                                       H.tensors_i32(np.ones(n + 1)), None, cad.CAD_COMMIT, o["argmax"],
+                                       o["accepted"], o["logits"], o["status"])
+    assert ei.value.status == cad.CAD_E_ARG
+    torch.cuda.synchronize()
+    assert bool((o["argmax"] == -7).all())
 
 
 def test_rejected_calls_enqueue_nothing(model_w):
