@@ -134,6 +134,60 @@ def test_tiny_fp32_end_to_end():
     assert np.max(np.abs(seq_logits.cpu().numpy() - lseq)) <= TOL["f32"]
 
 
+def test_tiny_fp32_batched():
+    """The fp32 path (its own projection and attention kernels) in a batched
+    call: sequences of different cache lengths (empty, ragged, one slot
+    short of a block) and span lengths share a shuffled paged pool."""
+    dev = _dev()
+    shape = synth.TINY
+    cfg = Config.of(shape)
+    Wc = synth.make_weights(shape, seed=0)
+    Wn = synth.weights_to_numpy(Wc)
+    Wd = {k: (v.to(dev) if torch.is_tensor(v) else [{kk: vv.to(dev) for kk, vv in lw.items()} for lw in v])
+          for k, v in Wc.items()}
+    Ls, Ns = [0, 200, 511, 47], [5, 1, 32, 9]
+    n_seq = len(Ls)
+    r = synth.rng(71)
+    spans = [r.integers(0, shape.vocab, size=n).astype(np.int32) for n in Ns]
+    offsets = np.concatenate([[0], np.cumsum(Ns)]).astype(np.int32)
+    need = [(Ls[b] + Ns[b] + 15) // 16 for b in range(n_seq)]
+    pool = sum(need) + 3
+    perm = synth.shuffled_block_table(pool, pool, seed=72).numpy()
+    table = np.full((n_seq, max(need)), -1, dtype=np.int32)
+    used = 0
+    for b in range(n_seq):
+        table[b, :need[b]] = perm[used:used + need[b]]
+        used += need[b]
+    kv = cad.KVCache.alloc(shape, pool, torch.from_numpy(table), device=dev)
+    kv.k.fill_(float("nan"))
+    kv.v.fill_(float("nan"))
+    pre = []
+    for b in range(n_seq):
+        kl, vl = synth.random_kv_logical(shape, Ls[b], seed=80 + b, device=dev)
+        if Ls[b]:
+            H.write_prefix(kv, kl, vl, seq=b)
+        pre.append((kl, vl))
+    model = cad.cad_model_create(shape, Wd, max_tokens=int(offsets[-1]))
+    o = H.outputs(int(offsets[-1]), shape.vocab, n_seq=n_seq)
+    cad.cad_splice_forward_batched(model, kv, Ls, offsets, H.tensors_i32(np.concatenate(spans)), None,
+                                   cad.CAD_VERIFY, o["argmax"], o["accepted"], o["logits"], o["status"])
+    torch.cuda.synchronize()
+    assert int(o["status"][0]) == 0
+    lg = o["logits"].cpu().numpy()
+    for b in range(n_seq):
+        s0, s1 = int(offsets[b]), int(offsets[b + 1])
+        kl, vl = pre[b]
+        okv = KVCache.from_prefix(kl.double().cpu().numpy(), vl.double().cpu().numpy(), Ls[b] + Ns[b])
+        ref = oracle.splice(cfg, Wn, okv, Ls[b], spans[b])
+        err = float(np.max(np.abs(lg[s0:s1] - ref)))
+        print(f"  seq {b}: L={Ls[b]} N={Ns[b]} logits max|diff| {err:.3e}", flush=True)
+        assert err <= TOL["f32"]
+        check_decisions(ref, None, o["argmax"].cpu().numpy()[s0:s1], spans[b], VERIFY, int(o["accepted"][b]))
+        gk, gv = H.read_seq(kv, Ls[b] + Ns[b], seq=b)
+        assert np.max(np.abs(gk[0][:, Ls[b]:] - okv.k[0][:, Ls[b]:])) <= TOL["f32"]
+        assert np.max(np.abs(gv[0][:, Ls[b]:] - okv.v[0][:, Ls[b]:])) <= TOL["f32"]
+
+
 def test_masked_argmax_edge_rows_fp32():
     """Masked argmax on the device for a vocabulary that is neither a multiple
     of 32 nor of 4 (1001 ids: a partial last mask word, scalar logit loads):
