@@ -251,3 +251,54 @@ def test_looped_planted_full_depth_chain(looped):
               flush=True)
         assert int(sv[0]) == want and int(o["accepted"][0]) == want
         assert (o["argmax"].cpu().numpy()[:want - 1] == np.asarray(span[1:want])).all()
+
+
+def test_looped_fp32_tiny():
+    """The looped path on the fp32 kernels (tiny block applied 3 times, 1e-4
+    bar): screening at depth 1 against the oracle's screening argmax and
+    survivor count, full-depth logits of the survivors, and a chain planted
+    from the oracle's own depth-3 greedy decode, screened at full depth, that
+    must be accepted whole."""
+    dev = _dev()
+    shape = synth.TINY.replace(name="tiny-looped", loop_depth=3)
+    cfg = Config.of(shape)
+    Wc = synth.make_weights(shape, seed=0)
+    W64 = _f64_weights(Wc)
+    Wd = {k: (v.to(dev) if torch.is_tensor(v) else [{kk: vv.to(dev) for kk, vv in lw.items()} for lw in v])
+          for k, v in Wc.items()}
+    L, N = 300, 6
+    kl, vl = synth.random_kv_logical(shape, L, seed=90, device=dev)
+    model = cad.cad_model_create(shape, Wd, max_tokens=16)
+    # a chain planted from the full-depth greedy decode (the oracle's)
+    chain = KVCache.from_prefix(kl.double().cpu().numpy(), vl.double().cpu().numpy(), L + N)
+    span = [11]
+    for j in range(N - 1):
+        lg = oracle.decode_step(cfg, W64, chain, L + j, span[j])[None]
+        span.append(int(oracle.masked_argmax(lg, None)[0]))
+    span = np.asarray(span, dtype=np.int32)
+    for ds in (1, shape.loop_depth):
+        kv = _looped_cache(shape, L, kl, vl, N, dev)
+        sa = torch.full((N,), -9, dtype=torch.int32, device=dev)
+        sv = torch.full((1,), -9, dtype=torch.int32, device=dev)
+        o = H.outputs(N, shape.vocab)
+        cad.cad_splice_forward_looped(model, kv, L, H.tensors_i32(span), ds, None, sa, sv, o["argmax"],
+                                      o["accepted"], o["logits"], o["status"])
+        okv = KVCache.from_prefix(kl.double().cpu().numpy(), vl.double().cpu().numpy(), L + N)
+        res = oracle.looped_splice(cfg, W64, okv, L, span, ds)
+        torch.cuda.synchronize()
+        assert int(o["status"][0]) == 0
+        sure = oracle.top2_margin(res["screen_logits"], None) > 1e-3
+        assert np.array_equal(sa.cpu().numpy()[sure], res["screen_argmax"][sure])
+        m = res["survivors"]
+        examined = m if m < N else N - 1
+        print(f"looped fp32 tiny, screen depth {ds}: survivors {int(sv[0])} (oracle {m})", flush=True)
+        if sure[:examined].all():
+            assert int(sv[0]) == m
+            err = float(np.max(np.abs(o["logits"].cpu().numpy()[:m] - res["logits"])))
+            print(f"  full-depth logits max|diff| {err:.3e}", flush=True)
+            assert err <= 1e-4
+        if ds == shape.loop_depth:  # the planted chain survives and is accepted whole
+            assert m == N
+            if sure[:N - 1].all():
+                assert int(sv[0]) == N and int(o["accepted"][0]) == N
+
