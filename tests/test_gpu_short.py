@@ -274,3 +274,25 @@ def test_short_bad_block_sets_status(model_w):
                            o["logits"], o["status"])
     torch.cuda.synchronize()
     assert int(o["status"][0]) & cad.CAD_DEV_BAD_BLOCK
+
+
+def test_bad_token_sets_status(model_w):
+    """A token id outside the vocabulary sets a status bit; its row is
+    embedded as zeros (no table access out of range) and every output stays
+    finite."""
+    dev = _dev()
+    shape, W, Wn = model_w
+    L = 40
+    kl, vl = _prefix(shape, L, seed=7, dev=dev)
+    nb = (L + 3 + BLK - 1) // BLK
+    kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device=dev)
+    H.write_prefix(kv, kl, vl)
+    model = cad.cad_model_create(shape, W, max_tokens=16)
+    o = H.outputs(3, shape.vocab)
+    cad.cad_splice_forward(model, kv, L, H.tensors_i32([3, shape.vocab + 5, -2]), None, cad.CAD_COMMIT,
+                           o["argmax"], o["accepted"], o["logits"], o["status"])
+    torch.cuda.synchronize()
+    assert int(o["status"][0]) & cad.CAD_DEV_BAD_TOKEN
+    assert bool(torch.isfinite(o["logits"]).all())
+    assert int(o["accepted"][0]) == 3
+
