@@ -7,7 +7,8 @@ rows), and the rotary append on one work-group per KV group.  These cases
 put them at ragged cache lengths (partial 32-key tiles and 16-slot
 blocks), on an empty cache, in batched calls of short sequences, with every
 stale cache slot holding NaN (a masked key must contribute nothing, not
-NaN * 0), and with a block id outside the pool (a status bit, no access).
+NaN * 0), with a block id outside the pool and with token ids outside the
+vocabulary (status bits, no access out of range).
 Batched calls that mix one-token steps with longer copies send every
 sequence through the LDS-staged attention instead, at 64-row query tiles
 (at most 64 query rows per sequence on average) and at 256-row tiles
