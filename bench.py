@@ -12,15 +12,21 @@ mode (Copy-as-Decode §2.4: acceptance is 1 inside a copy op).  Inputs are
 resident in HBM before the timed region; the step is idempotent (it rewrites
 the same cache slots), so repeating it measures steady-state throughput.
 
-Prints one JSON line.  ``value`` is spliced tokens/s (N / seconds per step).
+Prints one JSON line.  ``value`` is spliced tokens/s (N / seconds per step)
+over exactly K steps with nothing recorded inside them.  ``per_call`` gives
+the median, p10 and p90 of K more calls, each bracketed by HIP events.
 ``roofline`` reports the kernel that takes the most time (found on one
 profiled warmup step), timed by HIP events around its launches on its
-stream inside the timed region, its algorithmic work per launch and the
-MI355X peak it is bound by; ``traffic`` is the HBM bytes per launch that
-rocprofv3 counters measured on the same kernels (committed summary under
-profiles/, ignored once the kernel sources change).  ``cpu_baseline`` times the
-float64 CPU oracle on a bounded sample of the same workload.  ``sweep``
-reports the other span lengths of the same shape.
+stream over K more steps, its algorithmic work per launch and the MI355X
+peak it is bound by; ``traffic`` is the HBM bytes per launch that rocprofv3
+counters measured on the same kernels (committed summary under profiles/,
+ignored once the kernel sources change).  ``cpu_baseline`` times the float64
+CPU oracle on a bounded sample of the same workload.  ``sweep`` reports the
+other span lengths of the same shape; the extras add the pages' s(N) sweep at
+L = 1024, the batched serve, the looped block, the 1B shape (flushed and
+unflushed) and achievable HBM and matrix-core references.  A device status
+other than 0 (a data fault in the timed calls) prints the line with an
+``error`` and exits with status 3.
 """
 import argparse
 import json
@@ -70,7 +76,8 @@ def family_work(s, fam, N, L):
     if fam == "gemm_down":
         return 2 * d * F + 2 * N * F + 8 * N * d, 2 * N * d * F
     if fam == "gemm_lm_head":
-        return 2 * V * d + 2 * N * d + 4 * N * V, 2 * N * V * d
+        # the masked argmax runs in the epilogue: the mask is read, no logits are written
+        return 2 * V * d + 2 * N * d + 4 * N * ((V + 31) // 32), 2 * N * V * d
     if fam == "attention":
         byts = 2 * hkv * hd * 2 * (L + N) + 2 * 2 * N * hq * hd
         return byts, 4 * hq * hd * (N * L + N * (N + 1) // 2)
@@ -118,16 +125,46 @@ class Workload:
         self.cad.cad_splice_forward(self.model, self.kv, self.L, io["span"], io["mask"], self.cad.CAD_COMMIT,
                                     io["argmax"], io["accepted"], None, io["status"])
 
-    def time_steps(self, io, steps, warmup):
-        torch = self.torch
-        for _ in range(warmup):
-            self.step(io)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            self.step(io)
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0
+
+def call_times_ms(fn, reps, warmup=2, flush=None):
+    """Per-call durations (ms) from HIP events recorded on the current stream
+    (the one the library launches on) around each call; ``flush`` (if given)
+    runs before each call, outside the events."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        if flush is not None:
+            flush()
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def pct(ts):
+    """median, p10 and p90 of a list of durations (ms)"""
+    import numpy as np
+    a = np.asarray(ts, dtype=np.float64)
+    return {"median_ms": round(float(np.median(a)), 4), "p10_ms": round(float(np.percentile(a, 10)), 4),
+            "p90_ms": round(float(np.percentile(a, 90)), 4)}
+
+
+class Flusher:
+    """Overwrites a 512 MB device buffer: evicts the 256 MB memory-side
+    (Infinity) cache between timed calls."""
+
+    def __init__(self):
+        import torch
+        self.buf = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+        self.v = 0.0
+
+    def __call__(self):
+        self.v += 1.0
+        self.buf.fill_(self.v)
 
 
 
@@ -195,18 +232,12 @@ def serve_bench(wl, steps=5, draws=3):
         stat = torch.zeros(1, dtype=torch.int32, device="cuda")
         call = lambda: cad.cad_splice_forward_batched(model, kv, st.L, offs, spans, None, cad.CAD_COMMIT, am, acc,
                                                        None, stat)
-        for _ in range(2):
-            call()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            call()
-        torch.cuda.synchronize()
-        dt = (time.perf_counter() - t0) / steps
+        ts = pct(call_times_ms(call, steps))
+        dt = ts["median_ms"] * 1e-3
         tot_tok += total
         tot_s += dt
         rows.append({"rows": total, "copies": int(st.is_copy.sum()), "mean_L": int(st.L.mean()),
-                     "ms": round(dt * 1e3, 3)})
+                     "ms": round(dt * 1e3, 3), **ts})
         if int(stat[0]) != 0:
             log(f"[bench] serve: device status {int(stat[0])}")
     cad.cad_model_destroy(model)
@@ -267,9 +298,12 @@ def looped_bench(reps=10):
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t0) / reps
         surv = int(sv[0])
-        work = N * ds + surv * (shape.loop_depth - ds)
+        # every row runs every depth (rows past the survivors write no
+        # deeper cache but are still computed), so the work done is N x D
+        # position-depths whatever the screening keeps
+        work = N * shape.loop_depth
         res[name] = {"N": N, "survivors": surv, "ms_per_block": round(dt * 1e3, 4),
-                     "blocks_per_s": round(1 / dt, 1),
+                     "blocks_per_s": round(1 / dt, 1), "position_depths_run": work,
                      "tokens_processed_per_s": round(work / shape.loop_depth / dt, 1)}
     cad.cad_model_destroy(model)
     del kv, W
@@ -278,9 +312,11 @@ def looped_bench(reps=10):
                         "L=4096, head + suffix-match proposal (K=8)", **res}
 
 
-def s_of_n(wl, Ns=(8, 64, 512), L=1024):
+def s_of_n(wl, Ns=(1, 2, 4, 8, 16, 32, 64, 128, 256, 512), L=1024):
     """The pages' s(N) = T(N one-token decode steps) / T(one splice of N) at the
-    7B shape and L = 1024 (Copy-as-Decode §3, Table 1's comparison)."""
+    7B shape and L = 1024 (Copy-as-Decode §3 "Kernel microbenchmark", Table 1's
+    comparison): the splice timed over 5 calls (median of HIP-event call
+    times), the chain of N decode steps once."""
     import torch
     import synth
     cad = wl.cad
@@ -301,21 +337,73 @@ def s_of_n(wl, Ns=(8, 64, 512), L=1024):
         def decode_chain():
             for i in range(N):
                 cad.cad_decode_step(wl.model, kv, L + i, span[i:i + 1], None, one)
-        res = {}
-        for name, fn, reps in (("splice", splice, 5), ("decode", decode_chain, 1)):
-            fn()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(reps):
-                fn()
-            torch.cuda.synchronize()
-            res[name] = (time.perf_counter() - t0) / reps
-        out.append({"N": N, "splice_ms": round(res["splice"] * 1e3, 3), "decode_steps_ms": round(res["decode"] * 1e3, 3),
-                    "s": round(res["decode"] / res["splice"], 2)})
+        t_splice = pct(call_times_ms(splice, 5, warmup=1))["median_ms"]
+        t_chain = call_times_ms(decode_chain, 1, warmup=1)[0]
+        out.append({"N": N, "splice_ms": t_splice, "decode_steps_ms": round(t_chain, 3),
+                    "s": round(t_chain / t_splice, 2)})
         log(f"[bench] s(N={N}) at L={L}: {out[-1]['s']}")
     del kv
     torch.cuda.empty_cache()
     return out
+
+
+def sweep_1b(reps=20, Ns=(1, 4, 8, 16, 64, 256), L=4096):
+    """The Llama-style 1B shape (16 layers, d 2048, 32 q / 8 kv heads of 64,
+    FFN 8192, vocab 32000), random-init bf16 weights, L = 4096 prompt of
+    repeated lines, spans of N tokens from duplicated lines, no mask, COMMIT:
+    per-call HIP-event times with a 512 MB buffer overwritten before each
+    call (flushed: weights and cache come from HBM, not the 256 MB
+    memory-side cache) and without (unflushed)."""
+    import torch
+    import synth
+    import verify_forward_amd as cad
+    shape = synth.LLAMA_1B
+    W = synth.make_weights(shape, device="cuda")
+    nb = (L + max(Ns) + 15) // 16
+    kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(synth.SEED_KV + 3)
+    for t in (kv.k, kv.v):
+        t.copy_(torch.randn(t.shape, generator=g, device="cuda", dtype=torch.float32).mul_(synth.kv_std(shape)))
+    model = cad.cad_model_create(shape, W, max_tokens=max(Ns))
+    prompt = synth.make_line_prompt(L, shape.vocab)
+    flush = Flusher()
+    rows = []
+    for N in Ns:
+        span = torch.from_numpy(synth.pick_span(prompt, N).astype("int32")).cuda()
+        am = torch.empty(N, dtype=torch.int32, device="cuda")
+        acc = torch.empty(1, dtype=torch.int32, device="cuda")
+        fn = lambda: cad.cad_splice_forward(model, kv, L, span, None, cad.CAD_COMMIT, am, acc)
+        b, f = forward_work(shape, N, L)
+        rec = {"N": N}
+        for name, fl in (("unflushed", None), ("flushed", flush)):
+            st = pct(call_times_ms(fn, reps, flush=fl))
+            ms = st["median_ms"]
+            rec[name] = {**st, "tok_s": round(N / (ms * 1e-3), 1),
+                         "hbm_frac": round(b / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                         "mfma_frac": round(f / (ms * 1e-3) / (MFMA_PEAK_TFLOPS * 1e12), 4)}
+        rows.append(rec)
+        log(f"[bench] 1B N={N}: {rec['unflushed']['median_ms']} ms unflushed, {rec['flushed']['median_ms']} ms flushed")
+    cad.cad_model_destroy(model)
+    del kv, W, flush
+    torch.cuda.empty_cache()
+    return {"workload": "Llama-style 1B shape (16 layers, d_model 2048, 32 q / 8 kv heads x 64, SwiGLU 8192, "
+                        "vocab 32000), random-init bf16, L=4096, span N from a duplicated line, COMMIT, no mask",
+            "L": L, "rows": rows}
+
+
+def matrix_core_reference():
+    """Achievable matrix-core rate on this GPU: torch's (hipBLASLt) bf16 GEMM
+    8192 x 8192 x 8192, TFLOP/s (a practical reference; the roofline peak
+    stays the published 2.5 PFLOP/s)."""
+    import torch
+    a = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
+    ts = call_times_ms(lambda: torch.matmul(a, b), 10, warmup=3)
+    ms = pct(ts)["median_ms"]
+    del a, b
+    torch.cuda.empty_cache()
+    return round(2 * 8192 ** 3 / (ms * 1e-3) / 1e12, 1)
 
 # ----------------------------------------------------------------------------
 # CPU baseline: the float64 oracle on a bounded sample
@@ -331,9 +419,12 @@ def cpu_baseline(shape, L, N):
     import oracle
     import synth
     from oracle.decoder import Config, KVCache
+    from threadpoolctl import threadpool_limits, threadpool_info
     cores = len(os.sched_getaffinity(0))
     times = {}
     lo, hi = 1, 6
+    limiter = threadpool_limits(limits=cores, user_api="blas")
+    blas_threads = sorted({i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"})
     for nl in (lo, hi):
         sub = shape.replace(n_layers=nl)
         W = synth.weights_to_numpy(synth.make_weights(shape, device="cuda", layers=range(nl)))
@@ -351,6 +442,7 @@ def cpu_baseline(shape, L, N):
         log(f"[bench] oracle sample: {nl} layer(s), {N} rows: {times[nl]:.1f}s")
         del W, kv, lg
         torch.cuda.empty_cache()
+    limiter.restore_original_limits()
     per_layer = max((times[hi] - times[lo]) / (hi - lo), 1e-9)
     full = times[lo] + (shape.n_layers - lo) * per_layer
     try:
@@ -358,7 +450,9 @@ def cpu_baseline(shape, L, N):
     except Exception:
         blas = "unknown"
     return {"value": N / full, "unit": "spliced tokens/s", "cores": cores, "kind": "oracle",
-            "sample": (f"float64 NumPy oracle ({blas}), all {N} span rows through {lo} and {hi} of the "
+            "blas_threads": blas_threads,
+            "sample": (f"float64 NumPy oracle ({blas}, BLAS threads pinned to {cores}), all {N} span rows "
+                       f"through {lo} and {hi} of the "
                        f"{shape.n_layers} layers + LM head + masked argmax at L={L}; full depth "
                        f"extrapolated as t{lo} + {shape.n_layers - lo}*(t{hi} - t{lo})/{hi - lo} = {full:.1f}s"),
             "sample_seconds": round(times[lo] + times[hi], 2)}
@@ -446,20 +540,26 @@ def main():
     kernels = {f: {"launches": n, "ms_per_step": round(ms, 4)} for f, (n, ms) in prof.items() if n}
     fam = max((f for f in prof if family_work(shape, f, N, L)), key=lambda f: prof[f][1])
 
-    # timed region: K steps; only the dominant kernel's launches are bracketed
-    # by HIP events (recorded on the stream the library launches on)
-    cad.cad_profile_enable(wl.model, [fam])
+    # headline: exactly K steps, nothing recorded inside
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         wl.step(io)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    ms_step = dt / args.steps * 1e3
+    value = N * args.steps / dt
+    # per-call spread: K more steps, each bracketed by a pair of HIP events
+    call = pct(call_times_ms(lambda: wl.step(io), args.steps, warmup=0))
+    # the dominant kernel: K more steps with its launches bracketed by HIP
+    # events on the stream the library launches on
+    cad.cad_profile_enable(wl.model, [fam])
+    for _ in range(args.steps):
+        wl.step(io)
+    torch.cuda.synchronize()
     cad.cad_profile_enable(wl.model, 0)
     status = int(io["status"][0])
     n_launch, fam_ms = cad.cad_profile_read(wl.model, fam)
-    ms_step = dt / args.steps * 1e3
-    value = N * args.steps / dt
     byts, flops = forward_work(shape, N, L)
     per_launch_s = fam_ms / n_launch / 1e3
     fb, ff = family_work(shape, fam, N, L)
@@ -490,6 +590,7 @@ def main():
                                f"32 q / 8 kv heads x 128, SwiGLU 14336, vocab 32000), random-init weights, "
                                f"KV cache L={L}, span N={N}",
                    "L": L, "N": N, "batch": 1, "mask_allowed_frac": 0.6, "mode": "commit"},
+        "per_call": call,
         "forward": {"bytes": byts, "flops": flops,
                     "hbm_frac": round(byts / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
                     "mfma_frac": round(flops / (ms_step * 1e-3) / (MFMA_PEAK_TFLOPS * 1e12), 4),
@@ -499,6 +600,11 @@ def main():
         "device_status": status,
     }
     out["forward"]["binding_roof_frac"] = round(out["forward"]["roof_ms"] / ms_step, 4)
+    if status != 0:
+        # a data fault (bad token, empty mask row, bad block) makes the numbers meaningless
+        out["error"] = f"device status {status}: the timed calls flagged a data fault"
+        print(json.dumps(out), flush=True)
+        sys.exit(3)
 
     if not args.no_sweep:
         sweep = []
@@ -506,11 +612,10 @@ def main():
             if n == N:
                 continue
             io_n = wl.inputs(n)
-            steps = 10
-            t = wl.time_steps(io_n, steps, 2)
-            ms = t / steps * 1e3
+            st = pct(call_times_ms(lambda: wl.step(io_n), 10))
+            ms = st["median_ms"]
             b, f = forward_work(shape, n, L)
-            sweep.append({"N": n, "ms": round(ms, 4), "tok_s": round(n / (ms * 1e-3), 1),
+            sweep.append({"N": n, **st, "ms": ms, "tok_s": round(n / (ms * 1e-3), 1),
                           "hbm_frac": round(b / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
                           "mfma_frac": round(f / (ms * 1e-3) / (MFMA_PEAK_TFLOPS * 1e12), 4)})
             log(f"[bench] sweep N={n}: {ms:.3f} ms")
@@ -521,6 +626,8 @@ def main():
         out["serve"] = serve_bench(wl)
         log(f"[bench] serve: {out['serve']['value']} tok/s")
         out["achievable_copy_GBs"] = copy_bandwidth()
+        out["achievable_matrix_core_TFLOPs"] = {"value": matrix_core_reference(),
+                                                "what": "torch (hipBLASLt) bf16 GEMM 8192^3, median of 10"}
 
     if not args.no_cpu_baseline or not args.no_extras:
         del wl
@@ -528,6 +635,7 @@ def main():
     if not args.no_extras:
         out["looped"] = looped_bench()
         log("[bench] looped done")
+        out["llama_1b"] = sweep_1b()
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, L, N)

@@ -72,9 +72,10 @@ typedef enum {
  * loop_depth > 1: one shared block (n_layers must be 1) applied loop_depth
  * times, with one KV cache per depth (CopyLoop's looped decoder).
  * max_tokens: the most span rows one call may carry (sizes the workspace).
- * Supported: d_model a multiple of 4, at most 8192; dtype CAD_F32 any
- * head_dim <= 128 (even); dtype CAD_BF16 head_dim 64 or 128 and d_model,
- * ffn_dim, n_q_heads*head_dim multiples of 64. */
+ * Supported: d_model a multiple of 4, at most 8192; (n_q_heads + 2
+ * n_kv_heads) * head_dim at most 16384; dtype CAD_F32 any head_dim <= 128
+ * (even); dtype CAD_BF16 head_dim 64 or 128 and d_model, ffn_dim,
+ * n_q_heads*head_dim multiples of 64.  Other shapes: CAD_E_UNSUPPORTED. */
 typedef struct {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
   int32_t loop_depth;
@@ -145,13 +146,15 @@ const char* cad_last_error(void);
  *            with argmax[j-1] == span[j] (VERIFY).  The caller's new valid
  *            length is L + accepted and its next token is argmax[accepted-1]
  *            (the correction, or the bonus token on a full match).
- *   logits   dev float [N][vocab] or NULL: the fp32 logits, if wanted.
+ *   logits   dev float [N][vocab] or NULL: the fp32 logits, if wanted (with
+ *            NULL no logits reach memory: the mask and the argmax are
+ *            applied in the LM head's epilogue).
  *   dev_status dev int32 [1] or NULL: CAD_DEV_* bits are OR-ed in.
  * All N rows' K/V are written to cache slots L .. L+N-1 in place (slots
  * beyond L + accepted are stale afterwards and are overwritten by the next
  * call).  Slots outside L .. L+N-1 are not written. */
 cad_status cad_splice_forward(cad_model* m, const cad_kv* kv, int64_t L, const int32_t* span,
-                              int32_t N, const uint32_t* mask, int32_t mode, int32_t* argmax,
+                              int32_t N, const uint32_t* mask, cad_mode mode, int32_t* argmax,
                               int32_t* accepted, float* logits, int32_t* dev_status,
                               cad_stream stream);
 
@@ -187,7 +190,7 @@ cad_status cad_propose_suffix_match(const int32_t* tokens, int64_t T, int32_t ma
  * n_seq <= CAD_MAX_SEQS. */
 cad_status cad_splice_forward_batched(cad_model* m, const cad_kv* kv, int32_t n_seq,
                                       const int64_t* seq_L, const int32_t* offsets,
-                                      const int32_t* spans, const uint32_t* mask, int32_t mode,
+                                      const int32_t* spans, const uint32_t* mask, cad_mode mode,
                                       int32_t* argmax, int32_t* accepted, float* logits,
                                       int32_t* dev_status, cad_stream stream);
 
@@ -208,9 +211,11 @@ cad_status cad_splice_forward_looped(cad_model* m, const cad_kv* kv, int64_t L,
 /* ---- instrumentation (measurement only, not part of the method) ----
  * Kernel families, in bit order: 0 "embed", 1 "rmsnorm", 2 "gemm_qkv",
  * 3 "rope_append", 4 "attention" (the partial-attention kernel), 5
- * "attn_merge" (the log-sum-exp merge of key partitions), 6 "gemm_o", 7
- * "gemm_gate_up", 8 "gemm_down", 9 "gemm_lm_head", 10 "argmax", 11 "accept",
- * 12 "mask_rows".  Each family is one kernel (one named kernel per path).
+ * "attn_merge" (the log-sum-exp merge of key partitions), 6 "gemm_o",
+ * 7 "gemm_gate_up", 8 "gemm_down", 9 "gemm_lm_head" (with the mask and the
+ * per-tile argmax in its epilogue), 10 "decide" (the argmax over the LM
+ * head's tiles and the acceptance scan).  Each family is one kernel (one
+ * named kernel per path; the LM head after a k split adds its reduce).
  * cad_profile_enable(m, family_mask) starts a fresh collection in which
  * every launch of a family whose bit is set is bracketed by a pair of
  * hipEvents recorded on the launch's stream (synchronises the device once);

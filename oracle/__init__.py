@@ -34,11 +34,11 @@ brute force for the suffix matcher and the masked argmax; planted acceptance.
 """
 from .decoder import (Config, KVCache, rms_norm, rope_rotate, decode_step,
                       splice, sequential, prefill, final_logits)
-from .decision import masked_argmax, acceptance, top2_margin, mask_allows
+from .decision import masked_argmax, acceptance, top2_margin
 from .suffix import suffix_match
 from .looped import looped_splice
 from .batched import batched_splice
 
 __all__ = ["Config", "KVCache", "rms_norm", "rope_rotate", "decode_step", "splice",
            "sequential", "prefill", "final_logits", "masked_argmax", "acceptance",
-           "top2_margin", "mask_allows", "suffix_match", "looped_splice", "batched_splice"]
+           "top2_margin", "suffix_match", "looped_splice", "batched_splice"]

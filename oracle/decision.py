@@ -22,12 +22,6 @@ import numpy as np
 COMMIT, VERIFY = 0, 1
 
 
-def mask_allows(mask_row: Optional[np.ndarray], v: int) -> bool:
-    if mask_row is None:
-        return True
-    return bool((int(mask_row[v // 32]) >> (v % 32)) & 1)
-
-
 def allowed_matrix(mask: Optional[np.ndarray], N: int, V: int) -> np.ndarray:
     """Unpack the bitmask into bool [N, V]."""
     if mask is None:
@@ -51,7 +45,13 @@ def masked_argmax(logits: np.ndarray, mask: Optional[np.ndarray]) -> np.ndarray:
 
 
 def top2_margin(logits: np.ndarray, mask: Optional[np.ndarray]) -> np.ndarray:
-    """Gap between the best and second-best allowed logit per row (inf if fewer than two)."""
+    """Gap between the best and the second-best *allowed* logit of each row:
+    0 when the maximum is tied between two allowed ids, inf when the row
+    allows fewer than two ids (its masked argmax then has no rival).
+
+    This decides which positions the parity tests grade bit-exactly: a
+    masked argmax is only well defined against rounding when its margin is
+    clear (the tolerance reading of the spec parity rule)."""
     N, V = logits.shape
     ok = allowed_matrix(mask, N, V)
     out = np.empty(N)

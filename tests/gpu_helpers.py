@@ -45,6 +45,20 @@ def read_seq(kv: cad.KVCache, n_tokens: int, seq: int = 0):
     return f(k), f(v)
 
 
+def read_span(kv: cad.KVCache, first: int, n: int, seq: int = 0):
+    """Logical ``[cache][Hkv][n][hd]`` float64 copies of tokens
+    ``first .. first + n - 1`` of a sequence (only the blocks that hold them
+    are read back)."""
+    table = kv.block_table.view(-1, kv.max_blocks_per_seq)[seq].long()
+    b0, b1 = first // BLK, (first + n - 1) // BLK + 1
+    blocks = table[b0:b1].to(kv.k.device)
+    k = kv.k[:, blocks].permute(0, 2, 1, 3, 4).reshape(kv.k.shape[0], kv.k.shape[2], (b1 - b0) * BLK, -1)
+    v = kv.v[:, blocks].permute(0, 2, 1, 4, 3).reshape(kv.v.shape[0], kv.v.shape[2], (b1 - b0) * BLK, -1)
+    o = first - b0 * BLK
+    f = lambda t: t[:, :, o:o + n].to(torch.float64).cpu().numpy()
+    return f(k), f(v)
+
+
 def tensors_i32(a, device="cuda"):
     return torch.as_tensor(np.asarray(a, dtype=np.int32), device=device)
 

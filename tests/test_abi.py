@@ -55,6 +55,18 @@ def test_create_rejects_bad_config(field, value, status):
     assert cad.cad_last_error() != ""
 
 
+def test_create_rejects_shape_beyond_the_rotary_stage():
+    """64 query and 64 KV heads of 128 (d_model 8192): the rotary kernel
+    could not stage a whole row of q, k and v heads, so create refuses the
+    shape up front instead of failing a later call mid-way."""
+    c = good_config(d_model=8192, n_q_heads=64, n_kv_heads=64, head_dim=128)
+    h = ctypes.c_void_p()
+    w = cad.cad_weights()
+    assert cad.lib().cad_model_create(ctypes.byref(c), ctypes.byref(w), ctypes.byref(h)) == cad.CAD_E_UNSUPPORTED
+    assert h.value is None
+    assert "16384" in cad.cad_last_error()
+
+
 def test_create_rejects_missing_weights():
     c = good_config()
     h = ctypes.c_void_p()

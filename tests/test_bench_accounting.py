@@ -70,6 +70,15 @@ def test_projection_family_flops_7b():
     assert bench.family_work(S, "gemm_lm_head", 512, 16384)[1] == 2 * 512 * 32000 * 4096
 
 
+def test_lm_head_bytes_carry_the_mask_and_no_logits():
+    """The LM head takes the masked argmax in its epilogue: per launch it
+    reads the 32000 x 4096 bf16 head, the 512 activation rows and 512 mask
+    rows of 1000 words, and writes no logits (262 MB of weights, 4 KB of
+    activations per row, 4000 bytes of mask per row)."""
+    b, _ = bench.family_work(S, "gemm_lm_head", 512, 16384)
+    assert b == 262_144_000 + 4_194_304 + 2_048_000
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)

@@ -11,6 +11,12 @@ fragments loaded straight from the paged cache) over the same cache.
 The float64 oracle computes every row of both splices, layer by layer, with
 each layer's weights widened to float64 once (about a minute of CPU).
 
+A second test runs the batched editing-serve configuration's launch shape
+at the 7B size: four sequences with cache lengths up to 8190 in one shuffled
+paged pool, one of them splicing a copy of about 48 tokens of whole
+duplicated lines and the others one-token steps, COMMIT mode, no mask (as
+the serve benchmark calls it), again against the oracle layer by layer.
+
 Bars: logits within 2e-2; appended K/V within 2e-2 plus half a bfloat16
 spacing (the cache stores bfloat16); masked argmax bit-exact where the
 oracle's top-2 margin exceeds 0.1; acceptance N in COMMIT mode.
@@ -164,3 +170,79 @@ def test_llama7b_bench_configuration():
     graded += _check_decisions(ref_c, mask16, o16["argmax"].cpu().numpy())
     graded += _check_decisions(ref_d, mask4, o4["argmax"].cpu().numpy())
     print(f"7B argmax bit-exact on {graded}/{N + NM + NS + NT} graded rows", flush=True)
+
+
+def test_llama7b_batched_serve_shape():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dev = "cuda"
+    shape = synth.LLAMA_7B
+    cfg = Config.of(shape)
+    W = synth.make_weights(shape, device=dev)
+    Ls = [8190, 3001, 4100, 1024]
+    n_seq = len(Ls)
+    r = synth.rng(41, 7)
+    prompt = synth.make_line_prompt(8192, shape.vocab, seed=1200, line_len_range=(8, 16))
+    st = int(prompt.dup_starts[5])
+    idx = int(np.searchsorted(prompt.line_starts, st))
+    end = int(prompt.line_starts[idx + 4])                # four whole lines (about 48 tokens)
+    spans = [prompt.tokens[st:end].astype(np.int32)]
+    spans += [np.array([int(r.integers(0, shape.vocab))], dtype=np.int32) for _ in range(n_seq - 1)]
+    offsets = np.concatenate([[0], np.cumsum([len(x) for x in spans])]).astype(np.int32)
+    total = int(offsets[-1])
+    need = [(Ls[b] + len(spans[b]) + BLK - 1) // BLK for b in range(n_seq)]
+    pool = int(sum(need)) + 3
+    perm = synth.shuffled_block_table(pool, pool, seed=8).numpy()
+    table = np.full((n_seq, max(need)), -1, dtype=np.int32)
+    used = 0
+    for b in range(n_seq):
+        table[b, :need[b]] = perm[used:used + need[b]]
+        used += need[b]
+    kv = cad.KVCache.alloc(shape, pool, torch.from_numpy(table), device=dev)
+    pre = []
+    for b in range(n_seq):
+        kl, vl = synth.random_kv_logical(shape, Ls[b], seed=300 + b, device=dev)
+        H.write_prefix(kv, kl, vl, seq=b)
+        pre.append((kl, vl))
+    model = cad.cad_model_create(shape, W, max_tokens=total)
+    o = H.outputs(total, shape.vocab, n_seq=n_seq)
+    cad.cad_splice_forward_batched(model, kv, Ls, offsets, H.tensors_i32(np.concatenate(spans)), None,
+                                   cad.CAD_COMMIT, o["argmax"], o["accepted"], o["logits"], o["status"])
+    torch.cuda.synchronize()
+    assert int(o["status"][0]) == 0
+    assert list(o["accepted"].cpu().numpy()) == [len(x) for x in spans]
+    lg = o["logits"].cpu().numpy()
+    am = o["argmax"].cpu().numpy()
+    gkv = [H.read_span(kv, Ls[b], len(spans[b]), seq=b) for b in range(n_seq)]
+
+    emb = W["tok_embed"]
+    xs = [emb[torch.as_tensor(sp, device=dev).long()].double().cpu().numpy() for sp in spans]
+    ks = [[] for _ in range(n_seq)]
+    vs = [[] for _ in range(n_seq)]
+    hd, hkv = shape.head_dim, shape.n_kv_heads
+    for ci in range(shape.n_layers):
+        lw = {k: t.double().cpu().numpy() for k, t in W["layers"][ci].items()}
+        for b in range(n_seq):
+            n = len(spans[b])
+            kp = pre[b][0][ci].double().cpu().numpy()
+            vp = pre[b][1][ci].double().cpu().numpy()
+            z = np.zeros((hkv, n, hd))
+            cache = KVCache([np.concatenate([kp, z], axis=1)], [np.concatenate([vp, z], axis=1)])
+            xs[b] = splice_layer(cfg, lw, cache, 0, xs[b], Ls[b])
+            ks[b].append(cache.k[0][:, Ls[b]:])
+            vs[b].append(cache.v[0][:, Ls[b]:])
+        del lw
+    top = {"final_norm": W["final_norm"].double().cpu().numpy(), "lm_head": W["lm_head"].double().cpu().numpy()}
+    graded = 0
+    for b in range(n_seq):
+        s0, s1 = int(offsets[b]), int(offsets[b + 1])
+        ref = final_logits(cfg, top, xs[b])
+        err = float(np.max(np.abs(lg[s0:s1] - ref)))
+        ok_k, ek = H.kv_close(gkv[b][0], np.stack(ks[b]), TOL)
+        ok_v, ev = H.kv_close(gkv[b][1], np.stack(vs[b]), TOL)
+        print(f"7B batched seq {b}: L={Ls[b]} N={s1 - s0} logits max|diff| {err:.3e}, K {ek:.3e}, V {ev:.3e}",
+              flush=True)
+        assert err <= TOL
+        assert ok_k and ok_v
+        graded += _check_decisions(ref, None, am[s0:s1])
+    print(f"7B batched argmax bit-exact on {graded}/{total} graded rows", flush=True)

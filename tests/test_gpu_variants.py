@@ -8,14 +8,19 @@
 * Looped decoder with shallow screening (CopyLoop §2 "Block Construction",
   "Shallow Screening", "Full-Depth Verification"): a block [head, copied
   tail] proposed by the suffix matcher runs to the screening depth, the
-  agreeing prefix survives to full depth and is verified there.  A second
-  case plants the full-depth greedy chain with screening at full depth, so
-  every position must be accepted.
+  agreeing prefix survives to full depth and is verified there.  Planted
+  cases take the tail from the oracle's own greedy chain at the screening
+  depth (every position survives to full depth) or at full depth with
+  screening there (every position is accepted, and a corrupted position
+  stops acceptance exactly there).  Each looped case is masked so that
+  every decision of both readouts has an oracle top-2 margin of at least
+  0.5 (1e-3 for fp32): every screening argmax, survivor count, full-depth
+  argmax and acceptance is compared, with no case left ungraded.
 
 Bars as in the other parity tests: logits within 2e-2 and K/V within 2e-2
-plus half a bfloat16 spacing (bf16 models),
-argmax and acceptance bit-exact where every position they depend on has an
-oracle top-2 margin above 0.1; the suffix-match proposal is always exact.
+plus half a bfloat16 spacing (bf16 models), 1e-4 for fp32; argmax and
+acceptance bit-exact where every position they depend on has an oracle
+top-2 margin above 0.1; the suffix-match proposal is always exact.
 """
 import numpy as np
 import pytest
@@ -159,13 +164,80 @@ def _looped_cache(shape, L, kl, vl, N, dev):
     return kv
 
 
+def _clear_margin_mask(screen_logits, full_logits, gap):
+    """A per-position mask under which every masked decision of both
+    readouts has a top-2 margin of at least ``gap``, built from the oracle's
+    unmasked logits.  Row k allows its screening argmax a_s; its full-depth
+    argmax a_f too when the two readouts separate them by ``gap`` each way
+    (rows past ``full_logits`` have no full-depth readout); and every id at
+    least ``gap`` below the allowed leaders in both readouts.  The screening
+    argmax is unchanged by the mask, so the survivors are too."""
+    N, V = screen_logits.shape
+    allowed = np.zeros((N, V), dtype=bool)
+    for k in range(N):
+        s = screen_logits[k]
+        a_s = int(np.argmax(s))
+        lead = [a_s]
+        ok = s <= s[a_s] - gap
+        if k < len(full_logits):
+            f = full_logits[k]
+            a_f = int(np.argmax(f))
+            if a_f != a_s and s[a_s] - s[a_f] >= gap and f[a_f] - f[a_s] >= gap:
+                lead.append(a_f)
+            ok &= f <= max(f[i] for i in lead) - gap
+        allowed[k] = ok
+        allowed[k, lead] = True
+    return synth.pack_mask(allowed)
+
+
+def _run_looped(model, shape, L, kl, vl, span, ds, mask, dev):
+    N = len(span)
+    kv = _looped_cache(shape, L, kl, vl, N, dev)
+    sa = torch.full((N,), -9, dtype=torch.int32, device=dev)
+    sv = torch.full((1,), -9, dtype=torch.int32, device=dev)
+    o = H.outputs(N, shape.vocab)
+    mask_dev = None if mask is None else torch.from_numpy(mask.view(np.int32).copy()).to(dev)
+    cad.cad_splice_forward_looped(model, kv, L, H.tensors_i32(span), ds, mask_dev, sa, sv, o["argmax"],
+                                  o["accepted"], o["logits"], o["status"])
+    torch.cuda.synchronize()
+    assert int(o["status"][0]) == 0
+    return (sa.cpu().numpy(), int(sv[0]), o["argmax"].cpu().numpy(), int(o["accepted"][0]),
+            o["logits"].cpu().numpy())
+
+
+def _looped_case(looped_args, span, ds, label, tol=TOL, gap=0.5):
+    """Oracle first (unmasked, to build a mask with clear margins), then the
+    GPU call with that mask, then every output compared."""
+    shape, W64, L, kl, vl, model, dev = looped_args
+    cfg = Config.of(shape)
+    N = len(span)
+    kl64, vl64 = kl.double().cpu().numpy(), vl.double().cpu().numpy()
+    res0 = oracle.looped_splice(cfg, W64, KVCache.from_prefix(kl64, vl64, L + N), L, span, ds)
+    mask = _clear_margin_mask(res0["screen_logits"], res0["logits"], gap)
+    res = oracle.looped_splice(cfg, W64, KVCache.from_prefix(kl64, vl64, L + N), L, span, ds, mask)
+    m = res["survivors"]
+    assert m == res0["survivors"]
+    assert (oracle.top2_margin(res["screen_logits"], mask) >= gap).all()
+    assert (oracle.top2_margin(res["logits"], mask[:m]) >= gap).all()
+    sa, surv, am, acc, lg = _run_looped(model, shape, L, kl, vl, span, ds, mask, dev)
+    err = float(np.max(np.abs(lg[:m] - res["logits"])))
+    print(f"{label}: N={N} screen depth {ds}: survivors {surv} (oracle {m}), accepted {acc} (oracle "
+          f"{res['accepted']}), full-depth logits of {m} rows max|diff| {err:.3e}", flush=True)
+    assert np.array_equal(sa, res["screen_argmax"])
+    assert surv == m
+    assert err <= tol
+    assert np.array_equal(am, res["argmax"])
+    assert acc == res["accepted"]
+    return res
+
+
 def test_looped_screening_natural(looped):
+    """The natural block: the suffix matcher's proposal after a head equal to
+    the first token of a duplicated line, screened at depth 2 and verified at
+    depth 8."""
     dev = _dev()
     shape, W, W64, L, kl, vl, prompt, model = looped
-    cfg = Config.of(shape)
-    D, ds, K = shape.loop_depth, 2, 8
-    # history = prompt + a head equal to the first token of a duplicated line,
-    # so the suffix matcher finds an earlier occurrence to copy from
+    K = 8
     head = int(prompt.tokens[int(prompt.dup_starts[3])])
     hist = np.concatenate([prompt.tokens, [head]]).astype(np.int32)
     out_t = torch.full((K,), -9, dtype=torch.int32, device=dev)
@@ -177,35 +249,30 @@ def test_looped_screening_natural(looped):
     n = int(out_n[0])
     assert n == len(prop) and int(out_p[0]) == pos and list(out_t[:n].cpu().numpy()) == list(prop)
     span = np.concatenate([[head], prop]).astype(np.int32)
-    N = len(span)
-    kv = _looped_cache(shape, L, kl, vl, N, dev)
-    sa = torch.full((N,), -9, dtype=torch.int32, device=dev)
-    sv = torch.full((1,), -9, dtype=torch.int32, device=dev)
-    o = H.outputs(N, shape.vocab)
-    cad.cad_splice_forward_looped(model, kv, L, H.tensors_i32(span), ds, None, sa, sv, o["argmax"], o["accepted"],
-                                  o["logits"], o["status"])
-    okv = KVCache.from_prefix(kl.double().cpu().numpy(), vl.double().cpu().numpy(), L + N)
-    res = oracle.looped_splice(cfg, W64, okv, L, span, ds)
-    torch.cuda.synchronize()
-    assert int(o["status"][0]) == 0
-    s_ref = res["screen_logits"]
-    sure = oracle.top2_margin(s_ref, None) > MARGIN
-    sa_gpu = sa.cpu().numpy()
-    assert np.array_equal(sa_gpu[sure], res["screen_argmax"][sure])
-    m = res["survivors"]
-    examined = m if m < N else N - 1
-    if sure[:examined].all():
-        assert int(sv[0]) == m
-        lg = o["logits"].cpu().numpy()[:m]
-        err = np.max(np.abs(lg - res["logits"]))
-        print(f"looped natural: N={N} survivors {m} full-depth logits max|diff| {err:.3e}", flush=True)
-        assert err <= TOL
-        acc_ref, a_ref, sure_f, graded = _acceptance_graded(res["logits"], None, list(span[:m]), VERIFY)
-        a_gpu = o["argmax"].cpu().numpy()
-        assert np.array_equal(a_gpu[:m][sure_f], a_ref[sure_f])
-        assert (a_gpu[m:] == -1).all()
-        if graded:
-            assert int(o["accepted"][0]) == acc_ref
+    _looped_case((shape, W64, L, kl, vl, model, dev), span, 2, "looped natural")
+
+
+def _shallow_chain(cfg, W64, kl, vl, L, head, n, depth):
+    """The oracle's own greedy chain at readout depth ``depth``: s[0] = head,
+    s[j] = argmax of the depth-``depth`` readout after s[j-1]."""
+    chain = KVCache.from_prefix(kl.double().cpu().numpy(), vl.double().cpu().numpy(), L + n)
+    span = [head]
+    for j in range(n - 1):
+        lg = oracle.decode_step(cfg, W64, chain, L + j, span[j], depth=depth)[None]
+        span.append(int(oracle.masked_argmax(lg, None)[0]))
+    return np.asarray(span, dtype=np.int32)
+
+
+def test_looped_screening_planted_shallow_chain(looped):
+    """A tail planted from the depth-2 greedy chain: screening at depth 2 keeps
+    all nine positions, so all nine go to depth 8 and their full-depth logits
+    and the verification there are compared with the oracle."""
+    dev = _dev()
+    shape, W, W64, L, kl, vl, prompt, model = looped
+    cfg = Config.of(shape)
+    span = _shallow_chain(cfg, W64, kl, vl, L, 23, 9, 2)
+    res = _looped_case((shape, W64, L, kl, vl, model, dev), span, 2, "looped planted depth-2 chain")
+    assert res["survivors"] == len(span)
 
 
 def test_looped_planted_full_depth_chain(looped):
@@ -213,52 +280,29 @@ def test_looped_planted_full_depth_chain(looped):
     full-depth greedy chain: all N positions are accepted, and corrupting
     position j stops acceptance exactly there.  Each position's mask allows
     the greedy id and only ids at least 0.5 below it, so every examined
-    position has a masked top-2 margin of at least 0.5 (random-init logits
-    rarely give eight clear margins in a row without one)."""
+    position has a masked top-2 margin of at least 0.5; the full-depth
+    logits of every survivor are compared."""
     dev = _dev()
     shape, W, W64, L, kl, vl, prompt, model = looped
     cfg = Config.of(shape)
     D, N = shape.loop_depth, 9
-    chain = KVCache.from_prefix(kl.double().cpu().numpy(), vl.double().cpu().numpy(), L + N)
-    span = [17]
-    lgs = []
-    for j in range(N):
-        lg = oracle.decode_step(cfg, W64, chain, L + j, span[j])[None]
-        lgs.append(lg[0])
-        if j + 1 < N:
-            span.append(int(oracle.masked_argmax(lg, None)[0]))
-    lgs = np.stack(lgs)
-    allowed = lgs < lgs.max(axis=1, keepdims=True) - 0.5
-    allowed[np.arange(N), lgs.argmax(axis=1)] = True
-    mask = np.packbits(allowed, axis=1, bitorder="little").view("<u4")
-    assert (oracle.masked_argmax(lgs, mask)[:N - 1] == np.asarray(span[1:])).all()
-    assert (oracle.top2_margin(lgs, mask) >= 0.5).all()
-    mask_dev = torch.from_numpy(mask.view(np.int32).copy()).to(dev)
+    span = list(_shallow_chain(cfg, W64, kl, vl, L, 17, N, D))
     for bad_at in (None, 3):
         sp = list(span)
         if bad_at is not None:
             sp[bad_at] = (sp[bad_at] + 1) % shape.vocab
-        kv = _looped_cache(shape, L, kl, vl, N, dev)
-        sa = torch.full((N,), -9, dtype=torch.int32, device=dev)
-        sv = torch.full((1,), -9, dtype=torch.int32, device=dev)
-        o = H.outputs(N, shape.vocab)
-        cad.cad_splice_forward_looped(model, kv, L, H.tensors_i32(sp), D, mask_dev, sa, sv, o["argmax"],
-                                      o["accepted"], o["logits"], o["status"])
-        torch.cuda.synchronize()
+        res = _looped_case((shape, W64, L, kl, vl, model, dev), np.asarray(sp, dtype=np.int32), D,
+                           f"looped planted full-depth chain, corrupt at {bad_at}")
         want = N if bad_at is None else bad_at
-        assert int(o["status"][0]) == 0
-        print(f"looped planted: corrupt at {bad_at}: survivors {int(sv[0])} accepted {int(o['accepted'][0])}",
-              flush=True)
-        assert int(sv[0]) == want and int(o["accepted"][0]) == want
-        assert (o["argmax"].cpu().numpy()[:want - 1] == np.asarray(span[1:want])).all()
+        assert res["survivors"] == want and res["accepted"] == want
 
 
 def test_looped_fp32_tiny():
     """The looped path on the fp32 kernels (tiny block applied 3 times, 1e-4
-    bar): screening at depth 1 against the oracle's screening argmax and
-    survivor count, full-depth logits of the survivors, and a chain planted
-    from the oracle's own depth-3 greedy decode, screened at full depth, that
-    must be accepted whole."""
+    bar, decisions graded at a 1e-3 margin): screening at depth 1 of a
+    natural block and of a tail planted from the depth-1 greedy chain, and a
+    chain planted from the depth-3 greedy decode screened at full depth,
+    which must be accepted whole."""
     dev = _dev()
     shape = synth.TINY.replace(name="tiny-looped", loop_depth=3)
     cfg = Config.of(shape)
@@ -269,36 +313,12 @@ def test_looped_fp32_tiny():
     L, N = 300, 6
     kl, vl = synth.random_kv_logical(shape, L, seed=90, device=dev)
     model = cad.cad_model_create(shape, Wd, max_tokens=16)
-    # a chain planted from the full-depth greedy decode (the oracle's)
-    chain = KVCache.from_prefix(kl.double().cpu().numpy(), vl.double().cpu().numpy(), L + N)
-    span = [11]
-    for j in range(N - 1):
-        lg = oracle.decode_step(cfg, W64, chain, L + j, span[j])[None]
-        span.append(int(oracle.masked_argmax(lg, None)[0]))
-    span = np.asarray(span, dtype=np.int32)
-    for ds in (1, shape.loop_depth):
-        kv = _looped_cache(shape, L, kl, vl, N, dev)
-        sa = torch.full((N,), -9, dtype=torch.int32, device=dev)
-        sv = torch.full((1,), -9, dtype=torch.int32, device=dev)
-        o = H.outputs(N, shape.vocab)
-        cad.cad_splice_forward_looped(model, kv, L, H.tensors_i32(span), ds, None, sa, sv, o["argmax"],
-                                      o["accepted"], o["logits"], o["status"])
-        okv = KVCache.from_prefix(kl.double().cpu().numpy(), vl.double().cpu().numpy(), L + N)
-        res = oracle.looped_splice(cfg, W64, okv, L, span, ds)
-        torch.cuda.synchronize()
-        assert int(o["status"][0]) == 0
-        sure = oracle.top2_margin(res["screen_logits"], None) > 1e-3
-        assert np.array_equal(sa.cpu().numpy()[sure], res["screen_argmax"][sure])
-        m = res["survivors"]
-        examined = m if m < N else N - 1
-        print(f"looped fp32 tiny, screen depth {ds}: survivors {int(sv[0])} (oracle {m})", flush=True)
-        if sure[:examined].all():
-            assert int(sv[0]) == m
-            err = float(np.max(np.abs(o["logits"].cpu().numpy()[:m] - res["logits"])))
-            print(f"  full-depth logits max|diff| {err:.3e}", flush=True)
-            assert err <= 1e-4
-        if ds == shape.loop_depth:  # the planted chain survives and is accepted whole
-            assert m == N
-            if sure[:N - 1].all():
-                assert int(sv[0]) == N and int(o["accepted"][0]) == N
-
+    args = (shape, W64, L, kl, vl, model, dev)
+    natural = np.asarray([11, 400, 7, 93, 1000, 5], dtype=np.int32)
+    _looped_case(args, natural, 1, "looped fp32 natural", tol=1e-4, gap=1e-3)
+    shallow = _shallow_chain(cfg, W64, kl, vl, L, 11, N, 1)
+    res = _looped_case(args, shallow, 1, "looped fp32 planted depth-1 chain", tol=1e-4, gap=1e-3)
+    assert res["survivors"] == N
+    full = _shallow_chain(cfg, W64, kl, vl, L, 11, N, shape.loop_depth)
+    res = _looped_case(args, full, shape.loop_depth, "looped fp32 planted full-depth chain", tol=1e-4, gap=1e-3)
+    assert res["survivors"] == N and res["accepted"] == N

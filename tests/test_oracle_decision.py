@@ -49,6 +49,54 @@ def test_masked_argmax_lowest_id_on_tie_and_empty_row():
     assert list(oracle.masked_argmax(logits, mask)) == [2, -1]
 
 
+def brute_margin(row, words):
+    """Top-2 gap by pairs: the best allowed value minus the best allowed
+    value at any *other* allowed id (a tie at the top gives 0); fewer than
+    two allowed ids give inf."""
+    ids = [v for v in range(len(row)) if words is None or (int(words[v // 32]) >> (v % 32)) & 1]
+    if len(ids) < 2:
+        return np.inf
+    top = ids[0]
+    for v in ids:
+        if row[v] > row[top]:
+            top = v
+    rival = None
+    for v in ids:
+        if v != top and (rival is None or row[v] > row[rival]):
+            rival = v
+    return row[top] - row[rival]
+
+
+def test_top2_margin_hand_worked_cases():
+    logits = np.array([[1.0, 5.0, 5.0, 2.0],      # tie at the top: 0
+                       [1.0, 5.0, 4.0, 2.0],      # 5 - 4
+                       [9.0, 5.0, 4.0, 2.0],      # masked below: the 9 is banned, 5 - 4
+                       [9.0, 5.0, 4.0, 2.0],      # one allowed id: no rival
+                       [9.0, 5.0, 4.0, 2.0],      # nothing allowed
+                       [-3.0, -1.0, -2.5, -7.0]])  # negative logits: -1 - (-2.5)
+    allowed = np.array([[True] * 4, [True] * 4, [False, True, True, True],
+                        [False, False, True, False], [False] * 4, [True] * 4])
+    got = oracle.top2_margin(logits, synth.pack_mask(allowed))
+    assert list(got) == [0.0, 1.0, 1.0, np.inf, np.inf, 1.5]
+    # unmasked: the banned 9 is back on top
+    assert oracle.top2_margin(logits[2:3], None)[0] == 4.0
+
+
+def test_top2_margin_brute_force():
+    r = np.random.default_rng(3)
+    for V in (1, 2, 31, 32, 33, 70):
+        for _ in range(40):
+            N = 3
+            logits = r.integers(-4, 5, size=(N, V)).astype(np.float64) + r.choice([0.0, 0.25], size=(N, V))
+            allowed = r.random((N, V)) < r.uniform(0.0, 1.0)
+            mask = synth.pack_mask(allowed)
+            got = oracle.top2_margin(logits, mask)
+            got_nm = oracle.top2_margin(logits, None)
+            for k in range(N):
+                assert got[k] == brute_margin(logits[k], mask[k])
+                assert got_nm[k] == brute_margin(logits[k], None)
+
+
 def test_pack_mask_bit_order():
     allowed = np.zeros((1, 70), dtype=bool)
     allowed[0, [0, 31, 32, 69]] = True

@@ -25,11 +25,11 @@ CAD_KV_BLOCK = 16
 CAD_MAX_SEQS = 64
 
 EXPORTS = ("cad_model_create", "cad_model_destroy", "cad_last_error", "cad_splice_forward",
-           "cad_decode_step", "cad_propose_suffix_match", "cad_splice_forward_batched",
-           "cad_splice_forward_looped", "cad_profile_enable", "cad_profile_read")
+           "cad_decode_step", "cad_propose_suffix_match",
+           "cad_splice_forward_batched", "cad_splice_forward_looped", "cad_profile_enable", "cad_profile_read")
 
 PROFILE_FAMILIES = ("embed", "rmsnorm", "gemm_qkv", "rope_append", "attention", "attn_merge", "gemm_o",
-                    "gemm_gate_up", "gemm_down", "gemm_lm_head", "argmax", "accept", "mask_rows")
+                    "gemm_gate_up", "gemm_down", "gemm_lm_head", "decide")
 CAD_PROFILE_ALL = -1
 
 
@@ -88,7 +88,8 @@ def lib() -> ctypes.CDLL:
                                                 _VP, _VP, _VP, _VP, _VP, _VP]
         L.cad_profile_enable.argtypes = [_VP, i32]
         L.cad_profile_read.argtypes = [_VP, ctypes.c_char_p, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)]
-        for name in ("cad_model_create", "cad_splice_forward", "cad_decode_step", "cad_propose_suffix_match",
+        for name in ("cad_model_create", "cad_splice_forward", "cad_decode_step",
+                     "cad_propose_suffix_match",
                      "cad_splice_forward_batched", "cad_splice_forward_looped", "cad_profile_enable",
                      "cad_profile_read"):
             getattr(L, name).restype = ctypes.c_int

@@ -9,7 +9,8 @@
 //     RMSNorm -> QKV projection -> rotary + KV append -> span attention
 //     -> O projection (+residual) -> RMSNorm -> gate/up projection (SwiGLU)
 //     -> down projection (+residual)
-//   final RMSNorm -> LM head -> masked argmax -> acceptance
+//   final RMSNorm -> LM head (masked-argmax candidates in its epilogue; fp32
+//   logits only when the caller asks) -> decision (argmax + acceptance)
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -49,15 +50,42 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 enum ProfFamily {
   PF_EMBED, PF_NORM, PF_QKV, PF_ROPE, PF_ATTN, PF_MERGE, PF_O, PF_GATEUP, PF_DOWN, PF_HEAD,
-  PF_ARGMAX, PF_ACCEPT, PF_MASKROWS, PF_COUNT
+  PF_DECIDE, PF_COUNT
 };
 static const char* const kProfNames[PF_COUNT] = {
     "embed", "rmsnorm", "gemm_qkv", "rope_append", "attention", "attn_merge", "gemm_o",
-    "gemm_gate_up", "gemm_down", "gemm_lm_head", "argmax", "accept", "mask_rows"};
+    "gemm_gate_up", "gemm_down", "gemm_lm_head", "decide"};
 
 struct ProfRec {
   int family;
   hipEvent_t a, b;
+};
+
+// Per-call device buffers of the splice path (activations, partial sums,
+// attention partials, candidates), carved from one block of device memory:
+// the model's workspace (allocated at create, sized for max_tokens rows and
+// CAD_MAX_SEQS sequences).
+struct Workspace {
+  int64_t rows = 0;          // row capacity T (plane stride of the two-plane buffers)
+  float* x = nullptr;        // [T][d] residual stream
+  // activations feeding a projection: fp32 [T][n] (fp32 models) or two bf16
+  // planes [T][n] each, hi then lo (bf16 models), in the same bytes
+  void* hn = nullptr;        // [T][d] normalised activations
+  float* qkv = nullptr;      // [T][(hq+2hkv) hd]
+  void* q = nullptr;         // [T][hq][hd] rotated queries
+  void* attn = nullptr;      // [T][hq hd] attention output
+  void* act = nullptr;       // [T][F] SwiGLU activation
+  uint32_t* cand = nullptr;  // [max_candidates(V)][T] masked-argmax candidates of the LM head
+  float* part_o = nullptr;   // attention partials
+  float* part_ml = nullptr;
+  int64_t part_cap = 0;      // rows x partitions the partials hold
+  int32_t* survivors = nullptr;  // [1] acceptance output when the caller passes none
+  f16_t* span_k = nullptr;       // this call's span K/V at half precision (bf16 models)
+  f16_t* span_v = nullptr;
+  int32_t span_cap = 0;          // rows of the span workspace
+  float* split_ws = nullptr;     // split-K partial sums of the projections (bf16 models)
+  int64_t split_cap = 0;         // floats in split_ws
+  float* norm_ss = nullptr;      // [16][d / 256] slice sums of squares (bf16 models, few rows)
 };
 
 struct cad_model {
@@ -73,30 +101,14 @@ struct cad_model {
   const void* final_norm;
   const void* lm_head;
   std::vector<const void*> attn_norm, w_qkv, w_o, ffn_norm, w_gate_up, w_down;
-  // workspace (library-owned, one allocation)
+  // device memory owned by the model (one allocation): the workspace and
+  // the rotary frequencies
   void* ws = nullptr;
   size_t ws_bytes = 0;
-  float* x = nullptr;        // [T][d] residual stream
-  // activations feeding a projection: fp32 [T][n] (fp32 models) or two bf16
-  // planes [T][n] each, hi then lo (bf16 models), in the same bytes
-  void* hn = nullptr;        // [T][d] normalised activations
-  float* qkv = nullptr;      // [T][(hq+2hkv) hd]
-  void* q = nullptr;         // [T][hq][hd] rotated queries
-  void* attn = nullptr;      // [T][hq hd] attention output
-  void* act = nullptr;       // [T][F] SwiGLU activation
-  float* logits = nullptr;   // [T][V]
-  float* part_o = nullptr;   // attention partials
-  float* part_ml = nullptr;
-  int64_t part_cap = 0;      // floats available per part_o "row-head-dim" budget
+  Workspace main;
+  Workspace* w = &main;      // the workspace the current call runs on
   double* freq = nullptr;    // [hd/2] rotary frequencies
-  int32_t* scratch_i = nullptr;  // [T] argmax of the screening readout
-  int32_t* survivors = nullptr;  // [1] screening survivors when the caller passes none
-  f16_t* span_k = nullptr;       // this call's span K/V at half precision (bf16 models)
-  f16_t* span_v = nullptr;
-  int32_t span_cap = 0;          // rows of the span workspace
-  float* split_ws = nullptr;     // split-K partial sums of the projections (bf16 models)
-  float* norm_ss = nullptr;      // [16][d / 256] slice sums of squares (bf16 models, few rows)
-  int x_parts = 0;               // partial planes in split_ws still to be added to x
+  int x_parts = 0;           // partial planes in split_ws still to be added to x
 };
 
 namespace {
@@ -147,14 +159,19 @@ cad_status check_config(const cad_config* c) {
     if (c->d_model % 64 || c->ffn_dim % 64 || (c->n_q_heads * c->head_dim) % 64)
       return fail(CAD_E_UNSUPPORTED, "bf16 path needs d_model, ffn_dim, n_q_heads*head_dim multiples of 64");
   }
+  // the rotary kernel stages one row's projection output (every q, k and v
+  // head, fp32) in LDS when it takes a whole row per work-group
+  if ((int64_t)(c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim * 4 > 65536)
+    return fail(CAD_E_UNSUPPORTED, "(n_q_heads + 2 n_kv_heads) * head_dim = %d exceeds 16384",
+                (c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim);
   if (c->max_tokens > (1 << 20)) return fail(CAD_E_CAPACITY, "max_tokens too large");
   return CAD_OK;
 }
 
-int64_t max_parts_rows(const cad_config& c) {
+int64_t max_parts_rows(const cad_config& c, int64_t T) {
   // largest n_parts * rows over every row count a call may carry
   int64_t best = 0;
-  for (int r = 1; r <= c.max_tokens; ++r) {
+  for (int r = 1; r <= T; ++r) {
     // both tile shapes: one sequence, and r one-row sequences
     const int p1 = attention_parts(r, 1, c.n_q_heads, c.n_kv_heads, (int64_t)1 << 40, r);
     const int p2 = attention_parts(r, r, c.n_q_heads, c.n_kv_heads, (int64_t)1 << 40, 1);
@@ -182,21 +199,67 @@ KVView view_of(const cad_model* m, const cad_kv* kv, int ci) {
   v.table = kv->block_table;
   v.num_blocks = kv->num_blocks;
   v.max_blocks = kv->max_blocks_per_seq;
-  v.span_k = m->span_k;
-  v.span_v = m->span_v;
-  v.span_cap = m->span_cap;
+  v.span_k = m->w->span_k;
+  v.span_v = m->w->span_v;
+  v.span_cap = m->w->span_cap;
   return v;
 }
 
 // lo plane of an activation buffer (bf16 models): after the T x n hi plane
 void* lo_plane(const cad_model* m, void* buf, int64_t n) {
-  return m->cfg.dtype == CAD_BF16 ? (void*)((bf16_t*)buf + (int64_t)m->cfg.max_tokens * n) : nullptr;
+  return m->cfg.dtype == CAD_BF16 ? (void*)((bf16_t*)buf + m->w->rows * n) : nullptr;
 }
 
 // half remainder plane of q (bf16 models): after the T x hq x hd hi plane
 void* q_lo_plane(const cad_model* m) {
   const cad_config& c = m->cfg;
-  return c.dtype == CAD_BF16 ? (void*)((f16_t*)m->q + (int64_t)c.max_tokens * c.n_q_heads * c.head_dim) : nullptr;
+  return c.dtype == CAD_BF16 ? (void*)((f16_t*)m->w->q + m->w->rows * c.n_q_heads * c.head_dim) : nullptr;
+}
+
+// Lay out a workspace for T rows of at most `seqs` sequences with
+// `split_floats` floats of split-K partial sums, from `base` (nullptr: only
+// size it).  Returns the bytes it takes.
+size_t layout_workspace(const cad_config& c, int64_t T, int64_t seqs, int64_t split_floats, char* base,
+                        Workspace* w) {
+  const int64_t d = c.d_model, hq = c.n_q_heads, hkv = c.n_kv_heads, hd = c.head_dim, F = c.ffn_dim, V = c.vocab;
+  const bool bf = c.dtype == CAD_BF16;
+  const int64_t es = bf ? 2 : 4;
+  const int64_t pr = max_parts_rows(c, T);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  const size_t o_x = take(T * d * 4), o_hn = take(T * d * 4), o_qkv = take(T * (hq + 2 * hkv) * hd * 4),
+               o_q = take(T * hq * hd * es * (bf ? 2 : 1)), o_attn = take(T * hq * hd * 4), o_act = take(T * F * 4),
+               o_cand = take((size_t)max_candidates((int)V) * T * 8), o_po = take(pr * hq * hd * 4),
+               o_pml = take(pr * hq * 2 * 4), o_sv = take(4);
+  // each sequence's span rows padded to 64 in the span K/V workspace
+  const int64_t span_cap = bf ? (T + 64 * seqs + 63) / 64 * 64 : 0;
+  const size_t o_spk = take((size_t)span_cap * hkv * hd * 2), o_spv = take((size_t)span_cap * hkv * hd * 2);
+  const size_t o_sws = take(bf ? (size_t)split_floats * 4 : 0);
+  const size_t o_nss = take(bf ? (size_t)16 * rms_slices((int)d) * 4 : 0);
+  if (base) {
+    *w = Workspace{};
+    w->rows = T;
+    w->x = (float*)(base + o_x);
+    w->hn = base + o_hn;
+    w->qkv = (float*)(base + o_qkv);
+    w->q = base + o_q;
+    w->attn = base + o_attn;
+    w->act = base + o_act;
+    w->cand = (uint32_t*)(base + o_cand);
+    w->part_o = (float*)(base + o_po);
+    w->part_ml = (float*)(base + o_pml);
+    w->part_cap = pr;
+    w->survivors = (int32_t*)(base + o_sv);
+    if (bf) {
+      w->span_k = (f16_t*)(base + o_spk);
+      w->span_v = (f16_t*)(base + o_spv);
+      w->span_cap = (int32_t)span_cap;
+      w->split_ws = (float*)(base + o_sws);
+      w->split_cap = split_floats;
+      w->norm_ss = (float*)(base + o_nss);
+    }
+  }
+  return off;
 }
 
 // RMSNorm (with gain `gain`) of the R rows of the residual stream, after
@@ -217,21 +280,21 @@ hipError_t launch_norm(cad_model* m, const void* gain, int R, GemmArgs& g, hipSt
   m->x_parts = 0;
   g.lda = c.d_model;
   if (c.dtype == CAD_BF16 && R <= NORM_IN_PROJ_MAX_ROWS && aligned16(gain)) {
-    g.A = m->x;
+    g.A = m->w->x;
     g.A_lo = nullptr;
     g.norm_g = gain;
-    g.norm_ss = m->norm_ss;
+    g.norm_ss = m->w->norm_ss;
     g.norm_slices = rms_slices(c.d_model);
     g.norm_eps = c.rms_eps;
-    return launch_rms_slices(m->x, m->split_ws, np, R, c.d_model, m->norm_ss, s);
+    return launch_rms_slices(m->w->x, m->w->split_ws, np, R, c.d_model, m->w->norm_ss, s);
   }
-  g.A = m->hn;
-  g.A_lo = lo_plane(m, m->hn, c.d_model);
-  return launch_rmsnorm(c.dtype, m->x, m->split_ws, np, gain, R, c.d_model, c.rms_eps, m->hn,
-                        lo_plane(m, m->hn, c.d_model), s);
+  g.A = m->w->hn;
+  g.A_lo = lo_plane(m, m->w->hn, c.d_model);
+  return launch_rmsnorm(c.dtype, m->w->x, m->w->split_ws, np, gain, R, c.d_model, c.rms_eps, m->w->hn,
+                        lo_plane(m, m->w->hn, c.d_model), s);
 }
 
-// Run cache indices [c0, c1) over the rows already embedded in m->x.
+// Run cache indices [c0, c1) over the rows already embedded in m->w->x.
 cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, int c1,
                       const int32_t* write_limit, int32_t* dev_status, hipStream_t s) {
   const cad_config& c = m->cfg;
@@ -246,9 +309,9 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
   }
   // partitions of each query tile's key axis (cached keys, then the span's own)
   const int n_parts = attention_parts(R, rm.n_seq, hq, hkv, max_L, max_rows);
-  if ((int64_t)n_parts * R > m->part_cap)
+  if ((int64_t)n_parts * R > m->w->part_cap)
     return fail(CAD_E_CAPACITY, "attention partitions %d x %d rows exceed the workspace", n_parts, R);
-  if (c.dtype == CAD_BF16 && rm.pstart[rm.n_seq] > m->span_cap)
+  if (c.dtype == CAD_BF16 && rm.pstart[rm.n_seq] > m->w->span_cap)
     return fail(CAD_E_CAPACITY, "span workspace too small for %d padded rows", rm.pstart[rm.n_seq]);
   for (int ci = c0; ci < c1; ++ci) {
     const int li = c.loop_depth > 1 ? 0 : ci;
@@ -256,22 +319,22 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
     GemmArgs g{};
     LAUNCH(PF_NORM, launch_norm(m, m->attn_norm[li], R, g, s));
     g.W = m->w_qkv[li]; g.ldw = d;
-    g.M = R; g.N = qkv_rows; g.K = d; g.out_f32 = m->qkv; g.ldo = qkv_rows;
-    g.split_ws = m->split_ws;
+    g.M = R; g.N = qkv_rows; g.K = d; g.out_f32 = m->w->qkv; g.ldo = qkv_rows;
+    g.split_ws = m->w->split_ws; g.split_cap = m->w->split_cap;
     int qkv_parts = 0;
     LAUNCH(PF_QKV, launch_gemm(c.dtype, GEMM_QKV, g, s, &qkv_parts));
-    LAUNCH(PF_ROPE, launch_rope_append(c.dtype, m->qkv, m->split_ws, qkv_parts, R, hq, hkv, hd, m->freq, rm, v,
-                                       write_limit, m->q, q_lo_plane(m), dev_status, s));
-    LAUNCH(PF_ATTN, launch_attention(c.dtype, m->q, q_lo_plane(m), R, hq, hkv, hd, rm, v, n_parts, m->part_o,
-                                     m->part_ml, m->attn, lo_plane(m, m->attn, (int64_t)hq * hd), dev_status, s));
+    LAUNCH(PF_ROPE, launch_rope_append(c.dtype, m->w->qkv, m->w->split_ws, qkv_parts, R, hq, hkv, hd, m->freq, rm, v,
+                                       write_limit, m->w->q, q_lo_plane(m), dev_status, s));
+    LAUNCH(PF_ATTN, launch_attention(c.dtype, m->w->q, q_lo_plane(m), R, hq, hkv, hd, rm, v, n_parts, m->w->part_o,
+                                     m->w->part_ml, m->w->attn, lo_plane(m, m->w->attn, (int64_t)hq * hd), dev_status, s));
     if (c.dtype == CAD_BF16 && n_parts > 1)
-      LAUNCH(PF_MERGE, launch_attention_merge(m->part_o, m->part_ml, n_parts, R, hq, hd, m->attn,
-                                              lo_plane(m, m->attn, (int64_t)hq * hd), s));
+      LAUNCH(PF_MERGE, launch_attention_merge(m->w->part_o, m->w->part_ml, n_parts, R, hq, hd, m->w->attn,
+                                              lo_plane(m, m->w->attn, (int64_t)hq * hd), s));
     g = GemmArgs{};
-    g.A = m->attn; g.A_lo = lo_plane(m, m->attn, (int64_t)hq * hd); g.lda = hq * hd;
+    g.A = m->w->attn; g.A_lo = lo_plane(m, m->w->attn, (int64_t)hq * hd); g.lda = hq * hd;
     g.W = m->w_o[li]; g.ldw = hq * hd;
-    g.M = R; g.N = d; g.K = hq * hd; g.out_f32 = m->x; g.ldo = d;
-    g.split_ws = m->split_ws;
+    g.M = R; g.N = d; g.K = hq * hd; g.out_f32 = m->w->x; g.ldo = d;
+    g.split_ws = m->w->split_ws; g.split_cap = m->w->split_cap;
     LAUNCH(PF_O, launch_gemm(c.dtype, GEMM_O, g, s, &m->x_parts));
     g = GemmArgs{};
     LAUNCH(PF_NORM, launch_norm(m, m->ffn_norm[li], R, g, s));
@@ -282,32 +345,42 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
     // against 2e-2), which halves that projection's matrix-core work and
     // activation reads; the weight-streaming path keeps the two bf16 planes
     const int act_f16 = c.dtype == CAD_BF16 && R > 16;
-    g.M = R; g.N = F; g.K = d; g.up_off = F; g.out_act = m->act;
-    g.out_act_lo = act_f16 ? nullptr : lo_plane(m, m->act, F);
+    g.M = R; g.N = F; g.K = d; g.up_off = F; g.out_act = m->w->act;
+    g.out_act_lo = act_f16 ? nullptr : lo_plane(m, m->w->act, F);
     g.act_f16 = act_f16;
-    g.split_ws = m->split_ws;
+    g.split_ws = m->w->split_ws; g.split_cap = m->w->split_cap;
     LAUNCH(PF_GATEUP, launch_gemm(c.dtype, GEMM_GATE_UP, g, s));
     g = GemmArgs{};
-    g.A = m->act; g.A_lo = act_f16 ? nullptr : lo_plane(m, m->act, F); g.lda = F; g.W = m->w_down[li]; g.ldw = F;
+    g.A = m->w->act; g.A_lo = act_f16 ? nullptr : lo_plane(m, m->w->act, F); g.lda = F; g.W = m->w_down[li]; g.ldw = F;
     g.act_f16 = act_f16;
-    g.M = R; g.N = d; g.K = F; g.out_f32 = m->x; g.ldo = d;
-    g.split_ws = m->split_ws;
+    g.M = R; g.N = d; g.K = F; g.out_f32 = m->w->x; g.ldo = d;
+    g.split_ws = m->w->split_ws; g.split_cap = m->w->split_cap;
     LAUNCH(PF_DOWN, launch_gemm(c.dtype, GEMM_DOWN, g, s, &m->x_parts));
   }
   return CAD_OK;
 }
 
-// final norm + LM head + masked argmax
-cad_status readout(cad_model* m, int R, float* logits, const uint32_t* mask, int32_t* argmax,
-                   int32_t* dev_status, hipStream_t s) {
+// final norm + LM head (masked-argmax candidates; fp32 logits only if
+// `logits` is set) + the decision step: every row's argmax and the
+// acceptance of every sequence (rows at or beyond *limit, when given, get
+// argmax -1 and are not examined)
+cad_status readout(cad_model* m, const RowMap& rm, float* logits, const uint32_t* mask, const int32_t* span,
+                   int mode, const int32_t* limit, int32_t* argmax, int32_t* accepted, int32_t* dev_status,
+                   hipStream_t s) {
   const cad_config& c = m->cfg;
+  const int R = rm.total;
   GemmArgs g{};
   LAUNCH(PF_NORM, launch_norm(m, m->final_norm, R, g, s));
   g.W = m->lm_head; g.ldw = c.d_model;
   g.M = R; g.N = c.vocab; g.K = c.d_model; g.out_f32 = logits; g.ldo = c.vocab;
-  g.split_ws = m->split_ws;
+  g.split_ws = m->w->split_ws; g.split_cap = m->w->split_cap;
+  g.mask = mask;
+  g.mask_words = (c.vocab + 31) / 32;
+  g.cand = m->w->cand;
+  int n_cand = 0;
+  g.n_cand = &n_cand;
   LAUNCH(PF_HEAD, launch_gemm(c.dtype, GEMM_LM_HEAD, g, s));
-  LAUNCH(PF_ARGMAX, launch_argmax(logits, R, c.vocab, mask, argmax, dev_status, s));
+  LAUNCH(PF_DECIDE, launch_decide(m->w->cand, n_cand, R, rm, span, mode, limit, argmax, accepted, dev_status, s));
   return CAD_OK;
 }
 
@@ -371,48 +444,18 @@ cad_status cad_model_create(const cad_config* cfg, const cad_weights* w, cad_mod
     m->w_gate_up.push_back(w->w_gate_up[i]);
     m->w_down.push_back(w->w_down[i]);
   }
-  const int64_t T = c.max_tokens, d = c.d_model, hq = c.n_q_heads, hkv = c.n_kv_heads,
-                hd = c.head_dim, F = c.ffn_dim, V = c.vocab;
-  const int64_t es = m->esize;
-  const int64_t pr = max_parts_rows(c);
-  size_t off = 0;
-  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
-  const size_t o_x = take(T * d * 4), o_hn = take(T * d * 4), o_qkv = take(T * (hq + 2 * hkv) * hd * 4),
-               o_q = take(T * hq * hd * es * (c.dtype == CAD_BF16 ? 2 : 1)), o_attn = take(T * hq * hd * 4), o_act = take(T * F * 4),
-               o_logits = take(T * V * 4), o_po = take(pr * hq * hd * 4), o_pml = take(pr * hq * 2 * 4),
-               o_freq = take(hd / 2 * 8), o_si = take(T * 4), o_sv = take(4);
-  const bool split = c.dtype == CAD_BF16;
-  const int64_t span_cap = split ? (T + 64 * CAD_MAX_SEQS + 63) / 64 * 64 : 0;
-  const size_t o_spk = take((size_t)span_cap * hkv * hd * 2), o_spv = take((size_t)span_cap * hkv * hd * 2);
-  const size_t o_sws = take(split ? (size_t)GEMM_SPLIT_FLOATS * 4 : 0);
-  const size_t o_nss = take(split ? (size_t)16 * rms_slices((int)d) * 4 : 0);
-  hipError_t e = hipMalloc(&m->ws, off);
+  const int64_t hd = c.head_dim;
+  const int64_t split_floats = c.dtype == CAD_BF16 ? GEMM_SPLIT_FLOATS : 0;
+  const size_t o_freq = layout_workspace(c, c.max_tokens, CAD_MAX_SEQS, split_floats, nullptr, nullptr);
+  const size_t bytes = o_freq + align_up(hd / 2 * 8);
+  hipError_t e = hipMalloc(&m->ws, bytes);
   if (e != hipSuccess) {
     delete m;
-    return fail(CAD_E_HIP, "hipMalloc(%zu): %s", off, hipGetErrorString(e));
+    return fail(CAD_E_HIP, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
   }
-  m->ws_bytes = off;
-  char* base = (char*)m->ws;
-  m->x = (float*)(base + o_x);
-  m->hn = base + o_hn;
-  m->qkv = (float*)(base + o_qkv);
-  m->q = base + o_q;
-  m->attn = base + o_attn;
-  m->act = base + o_act;
-  m->logits = (float*)(base + o_logits);
-  m->part_o = (float*)(base + o_po);
-  m->part_ml = (float*)(base + o_pml);
-  m->part_cap = pr;
-  m->freq = (double*)(base + o_freq);
-  m->scratch_i = (int32_t*)(base + o_si);
-  m->survivors = (int32_t*)(base + o_sv);
-  if (split) {
-    m->span_k = (f16_t*)(base + o_spk);
-    m->span_v = (f16_t*)(base + o_spv);
-    m->span_cap = (int32_t)span_cap;
-    m->split_ws = (float*)(base + o_sws);
-    m->norm_ss = (float*)(base + o_nss);
-  }
+  m->ws_bytes = bytes;
+  layout_workspace(c, c.max_tokens, CAD_MAX_SEQS, split_floats, (char*)m->ws, &m->main);
+  m->freq = (double*)((char*)m->ws + o_freq);
   std::vector<double> fr(hd / 2);
   for (int64_t i = 0; i < hd / 2; ++i) fr[i] = std::pow((double)c.rope_theta, -2.0 * (double)i / (double)hd);
   e = hipMemcpy(m->freq, fr.data(), fr.size() * 8, hipMemcpyHostToDevice);
@@ -435,7 +478,7 @@ void cad_model_destroy(cad_model* m) {
 }
 
 cad_status cad_splice_forward(cad_model* m, const cad_kv* kv, int64_t L, const int32_t* span,
-                              int32_t N, const uint32_t* mask, int32_t mode, int32_t* argmax,
+                              int32_t N, const uint32_t* mask, cad_mode mode, int32_t* argmax,
                               int32_t* accepted, float* logits, int32_t* dev_status,
                               cad_stream stream) {
   cad_status st = check_common(m, kv, span, argmax, accepted, logits, mode);
@@ -453,26 +496,23 @@ cad_status cad_splice_forward(cad_model* m, const cad_kv* kv, int64_t L, const i
   rowmap_pad(rm);
   const cad_config& c = m->cfg;
   m->x_parts = 0;
-  LAUNCH(PF_EMBED, launch_embed(c.dtype, m->tok_embed, c.vocab, c.d_model, span, N, m->x, dev_status, s));
+  LAUNCH(PF_EMBED, launch_embed(c.dtype, m->tok_embed, c.vocab, c.d_model, span, N, m->w->x, dev_status, s));
   st = run_blocks(m, kv, rm, 0, c.n_layers, nullptr, dev_status, s);
   if (st != CAD_OK) return st;
-  st = readout(m, N, logits ? logits : m->logits, mask, argmax, dev_status, s);
-  if (st != CAD_OK) return st;
-  LAUNCH(PF_ACCEPT, launch_accept(argmax, span, rm, mode, nullptr, accepted, s));
-  return CAD_OK;
+  return readout(m, rm, logits, mask, span, mode, nullptr, argmax, accepted, dev_status, s);
 }
 
 cad_status cad_decode_step(cad_model* m, const cad_kv* kv, int64_t L, const int32_t* token,
                            const uint32_t* mask_row, int32_t* argmax, float* logits,
                            int32_t* dev_status, cad_stream stream) {
   if (!m) return fail(CAD_E_ARG, "model is NULL");
-  return cad_splice_forward(m, kv, L, token, 1, mask_row, CAD_COMMIT, argmax, m->survivors, logits,
+  return cad_splice_forward(m, kv, L, token, 1, mask_row, CAD_COMMIT, argmax, m->w->survivors, logits,
                             dev_status, stream);
 }
 
 cad_status cad_splice_forward_batched(cad_model* m, const cad_kv* kv, int32_t n_seq,
                                       const int64_t* seq_L, const int32_t* offsets,
-                                      const int32_t* spans, const uint32_t* mask, int32_t mode,
+                                      const int32_t* spans, const uint32_t* mask, cad_mode mode,
                                       int32_t* argmax, int32_t* accepted, float* logits,
                                       int32_t* dev_status, cad_stream stream) {
   cad_status st = check_common(m, kv, spans, argmax, accepted, logits, mode);
@@ -499,13 +539,10 @@ cad_status cad_splice_forward_batched(cad_model* m, const cad_kv* kv, int32_t n_
   hipStream_t s = (hipStream_t)stream;
   const cad_config& c = m->cfg;
   m->x_parts = 0;
-  LAUNCH(PF_EMBED, launch_embed(c.dtype, m->tok_embed, c.vocab, c.d_model, spans, rm.total, m->x, dev_status, s));
+  LAUNCH(PF_EMBED, launch_embed(c.dtype, m->tok_embed, c.vocab, c.d_model, spans, rm.total, m->w->x, dev_status, s));
   st = run_blocks(m, kv, rm, 0, c.n_layers, nullptr, dev_status, s);
   if (st != CAD_OK) return st;
-  st = readout(m, rm.total, logits ? logits : m->logits, mask, argmax, dev_status, s);
-  if (st != CAD_OK) return st;
-  LAUNCH(PF_ACCEPT, launch_accept(argmax, spans, rm, mode, nullptr, accepted, s));
-  return CAD_OK;
+  return readout(m, rm, logits, mask, spans, mode, nullptr, argmax, accepted, dev_status, s);
 }
 
 cad_status cad_splice_forward_looped(cad_model* m, const cad_kv* kv, int64_t L,
@@ -530,19 +567,14 @@ cad_status cad_splice_forward_looped(cad_model* m, const cad_kv* kv, int64_t L,
   rm.L[0] = L;
   rowmap_pad(rm);
   m->x_parts = 0;
-  LAUNCH(PF_EMBED, launch_embed(c.dtype, m->tok_embed, c.vocab, c.d_model, span, N, m->x, dev_status, s));
+  LAUNCH(PF_EMBED, launch_embed(c.dtype, m->tok_embed, c.vocab, c.d_model, span, N, m->w->x, dev_status, s));
   st = run_blocks(m, kv, rm, 0, screen_depth, nullptr, dev_status, s);
   if (st != CAD_OK) return st;
-  st = readout(m, N, m->logits, mask, screen_argmax, dev_status, s);
+  st = readout(m, rm, nullptr, mask, span, CAD_VERIFY, nullptr, screen_argmax, survivors, dev_status, s);
   if (st != CAD_OK) return st;
-  LAUNCH(PF_ACCEPT, launch_accept(screen_argmax, span, rm, CAD_VERIFY, nullptr, survivors, s));
   st = run_blocks(m, kv, rm, screen_depth, c.loop_depth, survivors, dev_status, s);
   if (st != CAD_OK) return st;
-  st = readout(m, N, logits ? logits : m->logits, mask, argmax, dev_status, s);
-  if (st != CAD_OK) return st;
-  LAUNCH(PF_MASKROWS, launch_mask_rows(argmax, N, survivors, s));
-  LAUNCH(PF_ACCEPT, launch_accept(argmax, span, rm, CAD_VERIFY, survivors, accepted, s));
-  return CAD_OK;
+  return readout(m, rm, logits, mask, span, CAD_VERIFY, survivors, argmax, accepted, dev_status, s);
 }
 
 cad_status cad_profile_enable(cad_model* m, int32_t family_mask) {

@@ -112,9 +112,13 @@ struct KVView {
   int32_t span_cap;
 };
 
-enum Epi { EPI_STORE_F32 = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
-// projection roles; each fixes its epilogue (qkv, lm_head: store; o, down:
-// residual add; gate_up: SwiGLU) and names its kernels
+// EPI_ARGMAX (the LM head): the fp32 logits are stored only if out_f32 is
+// set; every row gets one masked-argmax candidate (value, lowest id) per
+// column tile in `cand`, which k_decide reduces
+enum Epi { EPI_STORE_F32 = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3 };
+// projection roles; each fixes its epilogue (qkv: store; lm_head: masked
+// argmax candidates; o, down: residual add; gate_up: SwiGLU) and names its
+// kernels
 enum GemmRole { GEMM_QKV = 0, GEMM_O = 1, GEMM_GATE_UP = 2, GEMM_DOWN = 3, GEMM_LM_HEAD = 4 };
 
 struct GemmArgs {
@@ -131,8 +135,10 @@ struct GemmArgs {
   int64_t ldo;
   void* out_act;     // SWIGLU destination [M][N]: fp32 (fp32 models) or the hi plane (bf16 models)
   void* out_act_lo;  // bf16 models: lo plane of the SWIGLU destination
-  // split-K scratch (library workspace): fp32 partial sums [split][M][cols]
+  // split-K scratch (library workspace): fp32 partial sums [split][M][cols],
+  // split_cap floats
   float* split_ws;
+  int64_t split_cap;
   // bf16 models, at most 16 rows: when norm_ss is set, A is the fp32
   // residual stream [M][lda] and the projection normalises it while staging
   // (RMSNorm with gain norm_g [K], bf16, and the slice sums of squares
@@ -145,9 +151,22 @@ struct GemmArgs {
   // plane (out_act as f16, no lo plane), and the down projection reads it
   // (A is then a single half plane and the weights are widened to half)
   int act_f16;
+  // EPI_ARGMAX: per-row vocabulary bitmask [M][mask_words] (bit v % 32 of
+  // word v / 32 = id v allowed) or nullptr (all allowed); candidates
+  // cand[c][M] as (fp32 value bits, id) pairs, id -1 when tile c allows
+  // nothing for that row; the launcher reports the candidate count per row
+  // in *n_cand (a host pointer, never read by a kernel)
+  const uint32_t* mask;
+  int mask_words;
+  uint32_t* cand;
+  int* n_cand;
 };
 
-// split-K workspace of the tiled GEMMs: GEMM_SPLIT_FLOATS floats (128 MB)
+// most masked-argmax candidates per row any LM-head path produces: one per
+// 64 vocabulary ids
+inline int max_candidates(int vocab) { return (vocab + 63) / 64; }
+
+// split-K workspace of a model's own workspace: GEMM_SPLIT_FLOATS floats (128 MB)
 constexpr int64_t GEMM_SPLIT_FLOATS = (int64_t)32 << 20;
 
 // ---- launchers (stream-ordered, no host sync) ----
@@ -181,13 +200,16 @@ hipError_t launch_attention(int dtype, const void* q, const void* q_lo, int rows
 // log-sum-exp merge of the key partitions (bf16 models, n_parts > 1), into bf16 planes
 hipError_t launch_attention_merge(const float* part_o, const float* part_ml, int n_parts, int rows,
                                   int hq, int hd, void* out, void* out_lo, hipStream_t s);
-hipError_t launch_argmax(const float* logits, int rows, int vocab, const uint32_t* mask,
-                         int32_t* out, int32_t* status, hipStream_t s);
-hipError_t launch_accept(const int32_t* argmax, const int32_t* span, const RowMap& rm, int mode,
-                         const int32_t* limit, int32_t* accepted, hipStream_t s);
-hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
-// argmax[r] = -1 for rows r >= *limit
-hipError_t launch_mask_rows(int32_t* argmax, int rows, const int32_t* limit, hipStream_t s);
+// Masked argmax of every row from the LM head's candidates (cand[c][rows],
+// n_cand per row: larger value wins, then the lower id), then the
+// acceptance scan of every sequence (COMMIT: its row count; VERIFY: 1 + the
+// leading j >= 1 with argmax[j-1] == span[j]).  `limit` (device, optional,
+// single-sequence calls) caps the rows: rows at or beyond max(1, *limit)
+// get argmax -1 and are not examined.  Rows that allow nothing get -1 and
+// set CAD_DEV_EMPTY_MASK.
+hipError_t launch_decide(const uint32_t* cand, int n_cand, int rows, const RowMap& rm, const int32_t* span,
+                         int mode, const int32_t* limit, int32_t* argmax, int32_t* accepted, int32_t* status,
+                         hipStream_t s);
 hipError_t launch_suffix_match(const int32_t* tokens, int64_t T, int max_n, int min_n, int K,
                                int32_t* out_tokens, int32_t* out_len, int64_t* out_pos,
                                hipStream_t s);

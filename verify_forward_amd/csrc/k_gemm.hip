@@ -47,7 +47,8 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 template <int EPI, bool SPLIT>
 __device__ __forceinline__ void epi4(const GemmArgs& a, int m, int n, f32x4 c, f32x4 cu) {
   if (m >= a.M) return;
-  if (EPI == EPI_STORE_F32 || EPI == EPI_RESID) {
+  if (EPI == EPI_ARGMAX && !a.out_f32) return;  // logits not requested
+  if (EPI == EPI_STORE_F32 || EPI == EPI_RESID || EPI == EPI_ARGMAX) {
     float* o = a.out_f32 + (int64_t)m * a.ldo + n;
     if (n + 3 < a.N && ((a.ldo & 3) == 0)) {
       f32x4* o4 = (f32x4*)o;
@@ -89,6 +90,48 @@ __device__ __forceinline__ void epi4(const GemmArgs& a, int m, int n, f32x4 c, f
     for (int r = 0; r < 4; ++r)
       if (n + r < a.N) o[r] = silu_mul(c[r], cu[r]);
   }
+}
+
+// ---- masked-argmax candidates (EPI_ARGMAX, the LM head) ----
+// Order: the larger value wins, equal values go to the lower id; id < 0 is
+// "no allowed id".  Every scan below visits one lane's columns in increasing
+// order with a strict comparison, so within a lane the lowest id of a tie
+// is kept, and lanes are merged with the explicit id tie-break.
+__device__ __forceinline__ bool cand_better(float v, int i, float bv, int bi) {
+  return i >= 0 && (bi < 0 || v > bv || (v == bv && i < bi));
+}
+
+// allowed columns among n .. n + 3 of row m (n a multiple of 4, m < M): bit
+// r set = column n + r is in the vocabulary and allowed by the mask
+__device__ __forceinline__ uint32_t allowed4(const GemmArgs& a, int m, int n) {
+  if (n >= a.N) return 0u;
+  uint32_t b = a.mask ? (a.mask[(int64_t)m * a.mask_words + (n >> 5)] >> (n & 31)) & 0xFu : 0xFu;
+  if (n + 4 > a.N) b &= (1u << (a.N - n)) - 1u;
+  return b;
+}
+
+// fold four consecutive columns n .. n + 3 (allowed bits `ok`) into (bv, bi)
+__device__ __forceinline__ void scan4(f32x4 c, int n, uint32_t ok, float& bv, int& bi) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (((ok >> r) & 1u) && (bi < 0 || c[r] > bv)) {
+      bv = c[r];
+      bi = n + r;
+    }
+}
+
+// merge (bv, bi) with the lane `lane ^ off` (a lane swap through LDS hardware)
+__device__ __forceinline__ void cand_xor(float& bv, int& bi, int off) {
+  const float ov = __shfl_xor(bv, off);
+  const int oi = __shfl_xor(bi, off);
+  if (cand_better(ov, oi, bv, bi)) {
+    bv = ov;
+    bi = oi;
+  }
+}
+
+__device__ __forceinline__ void put_cand(const GemmArgs& a, int c, int m, float bv, int bi) {
+  *(u32x2*)(a.cand + 2 * ((int64_t)c * a.M + m)) = u32x2{__float_as_uint(bv), (uint32_t)bi};
 }
 
 // ---------------------------------------------------------------------------
@@ -334,7 +377,32 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& a, int n_rg, in
   }
   // lane: activation row m = i16, weight rows 4g + r of the block
   const int m = i16;
-  if (EPI == EPI_SWIGLU) {
+  if constexpr (EPI == EPI_ARGMAX) {
+    // LM head (never split): logits if requested, then one candidate per
+    // row and work-group (its 64 vocabulary ids): the four lane groups of a
+    // wave are merged by lane swaps, the four waves through LDS
+    const int n = blk * 16 + 4 * g;
+    epi4<EPI, true>(a, m, n, acc, acc);
+    float bv = 0.f;
+    int bi = -1;
+    scan4(acc, n, m < a.M ? allowed4(a, m, n) : 0u, bv, bi);
+    cand_xor(bv, bi, 16);
+    cand_xor(bv, bi, 32);
+    __shared__ u32x2 scand[4][16];
+    if (g == 0) scand[wave][i16] = u32x2{__float_as_uint(bv), (uint32_t)bi};
+    __syncthreads();
+    if (tid < 16 && tid < a.M) {
+      float cv = __uint_as_float(scand[0][tid][0]);
+      int ci = (int)scand[0][tid][1];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        const float ov = __uint_as_float(scand[w][tid][0]);
+        const int oi = (int)scand[w][tid][1];
+        if (cand_better(ov, oi, cv, ci)) { cv = ov; ci = oi; }
+      }
+      put_cand(a, rg, tid, cv, ci);
+    }
+  } else if (EPI == EPI_SWIGLU) {
     // lanes g = 0, 1 hold gate rows 4g + r, lanes g + 2 the matching up rows
     f32x4 cu;
 #pragma unroll
@@ -561,6 +629,28 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& a, int n_tn, int
     }
     return;
   }
+  if constexpr (EPI == EPI_ARGMAX) {
+    // LM head: logits if requested, then one candidate per row and weight
+    // tile (TN vocabulary ids); a lane scans its 16 fragments in increasing
+    // column order, the four lane groups of a row are merged by lane swaps
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = wrow0 + 16 * mb + i16;
+      const int mc = min(m, a.M - 1);
+      float bv = 0.f;
+      int bi = -1;
+#pragma unroll
+      for (int x = 0; x < NB; ++x) {
+        const int n = tn * TN + x * 16 + 4 * g;
+        epi4<EPI, true>(a, m, n, acc[x][mb], acc[x][mb]);
+        scan4(acc[x][mb], n, allowed4(a, mc, n), bv, bi);
+      }
+      cand_xor(bv, bi, 16);
+      cand_xor(bv, bi, 32);
+      if (g == 0 && m < a.M) put_cand(a, tn, m, bv, bi);
+    }
+    return;
+  }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -620,6 +710,15 @@ __device__ __forceinline__ void gemm_f32_body(const GemmArgs& a) {
     f32x4 c = {acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
     f32x4 cu = {accu[i][0], accu[i][1], accu[i][2], accu[i][3]};
     epi4<EPI, false>(a, m, n0 + tx * 4, c, cu);
+    if constexpr (EPI == EPI_ARGMAX) {
+      // one candidate per row and 64-column tile: the 16 threads of a row
+      // (consecutive lanes tx = 0..15) merged by lane swaps
+      float bv = 0.f;
+      int bi = -1;
+      scan4(c, n0 + tx * 4, m < a.M ? allowed4(a, m, n0 + tx * 4) : 0u, bv, bi);
+      for (int off = 1; off < 16; off <<= 1) cand_xor(bv, bi, off);
+      if (tx == 0 && m < a.M) put_cand(a, blockIdx.x, m, bv, bi);
+    }
   }
 }
 
@@ -644,6 +743,44 @@ __device__ __forceinline__ void gemm_reduce_body(const GemmArgs& a, int splits) 
     if (EPI == EPI_SWIGLU) cu += *(const f32x4*)(p + s * plane + a.N);
   }
   epi4<EPI, true>(a, m, n, c, cu);
+}
+
+// The LM head after a k split: one work-group of 256 threads per (row m =
+// blockIdx.y, 1024-column chunk blockIdx.x); each thread adds the partials
+// of four consecutive columns in split order, stores the logits if
+// requested and scans them; the chunk's candidate is merged over the
+// work-group (lane swaps, then the four waves in order through LDS).
+constexpr int REDUCE_ARGMAX_COLS = 1024;
+__device__ __forceinline__ void gemm_reduce_argmax_body(const GemmArgs& a, int splits) {
+  const int m = blockIdx.y, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int n = blockIdx.x * REDUCE_ARGMAX_COLS + 4 * t;
+  float bv = 0.f;
+  int bi = -1;
+  if (n < a.N) {
+    const int64_t plane = (int64_t)a.M * a.N;
+    const float* p = a.split_ws + (int64_t)m * a.N + n;
+    f32x4 c = *(const f32x4*)p;
+    for (int sp = 1; sp < splits; ++sp) c += *(const f32x4*)(p + sp * plane);
+    epi4<EPI_ARGMAX, true>(a, m, n, c, c);
+    scan4(c, n, allowed4(a, m, n), bv, bi);
+  }
+  for (int off = 1; off < 64; off <<= 1) cand_xor(bv, bi, off);
+  __shared__ u32x2 sc[4];
+  if (lane == 0) sc[wave] = u32x2{__float_as_uint(bv), (uint32_t)bi};
+  __syncthreads();
+  if (t == 0) {
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      const float ov = __uint_as_float(sc[w][0]);
+      const int oi = (int)sc[w][1];
+      if (cand_better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    put_cand(a, blockIdx.x, m, bv, bi);
+  }
+}
+
+__global__ void __launch_bounds__(256) k_gemm_reduce_argmax_lm_head(GemmArgs a, int splits) {
+  gemm_reduce_argmax_body(a, splits);
 }
 
 // Tiled shapes: eight waves (two per SIMD) of 32 activation rows each (256
@@ -678,7 +815,7 @@ CAD_GEMM_KERNELS(qkv, EPI_STORE_F32, TN8_QKV)
 CAD_GEMM_KERNELS(o, EPI_RESID, TILE_N)
 CAD_GEMM_KERNELS(gate_up, EPI_SWIGLU, TN8_GATE_UP)
 CAD_GEMM_KERNELS(down, EPI_RESID, TILE_N)
-CAD_GEMM_KERNELS(lm_head, EPI_STORE_F32, TILE_N)
+CAD_GEMM_KERNELS(lm_head, EPI_ARGMAX, TILE_N)
 #undef CAD_GEMM_KERNELS
 // the down projection over a single half activation plane (act_f16)
 __global__ void __launch_bounds__(512) k_gemm_down_h(GemmArgs a, int n_tn, int n_tm, int splits) {
@@ -702,10 +839,13 @@ static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled8, int t
                              bool rows128 = false) {
   if (partials) *partials = 0;
   if (a.norm_ss && (dtype != CAD_BF16 || a.M > 16 || a.norm_slices > 32)) return hipErrorInvalidValue;
+  if (EPI == EPI_ARGMAX && (!a.cand || !a.n_cand || (a.mask && a.mask_words * 32 < a.N)))
+    return hipErrorInvalidValue;
   const bool leave = partials != nullptr && EPI != EPI_SWIGLU && a.split_ws != nullptr && a.N % 4 == 0;
   if (dtype == CAD_F32) {
     dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
     hipLaunchKernelGGL(f32, grid, dim3(256), 0, s, a);
+    if (EPI == EPI_ARGMAX) *a.n_cand = (int)grid.x;
   } else if (a.M <= 16) {
     const int nblk = (EPI == EPI_SWIGLU) ? (a.N + 7) / 8 : (a.N + 15) / 16;
     const int n_rg = (nblk + 3) / 4;
@@ -722,12 +862,13 @@ static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled8, int t
     const int max_splits = (a.K + 511) / 512;
     if (leave)
       for (int c = min(nch, max_splits); c > 1; --c)
-        if (nch % c == 0 && (int64_t)c * a.M * a.N <= GEMM_SPLIT_FLOATS) {
+        if (nch % c == 0 && (int64_t)c * a.M * a.N <= a.split_cap) {
           splits = c;
           break;
         }
     hipLaunchKernelGGL(a.norm_ss ? skinny_norm : skinny, dim3(n_rg * splits), dim3(256), 0, s, a, n_rg, splits);
     if (splits > 1) *partials = splits;
+    if (EPI == EPI_ARGMAX) *a.n_cand = n_rg;  // one candidate per 64 vocabulary ids (never split)
   } else {
     // rows128: 128-row activation tiles at any row count (the O projection:
     // as fast as 256-row tiles at N = 512, and half the k splits, so half
@@ -744,13 +885,18 @@ static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled8, int t
     const int64_t split_floats = (int64_t)a.M * a.N * (EPI == EPI_SWIGLU ? 2 : 1);
     int splits = 1;
     if (a.split_ws && a.N % 64 == 0)
-      while (tiles * (splits + 1) <= 256 && nk / (splits + 1) >= 16 && split_floats * (splits + 1) <= GEMM_SPLIT_FLOATS)
+      while (tiles * (splits + 1) <= 256 && nk / (splits + 1) >= 16 && split_floats * (splits + 1) <= a.split_cap)
         ++splits;
     hipLaunchKernelGGL(small ? tiled_s : tiled8, dim3(tiles * splits), dim3(512), 0, s, a, n_tn, n_tm,
                        splits);
+    if (EPI == EPI_ARGMAX) *a.n_cand = n_tn;  // one candidate per weight tile
     if (splits > 1) {
       if (leave) {
         *partials = splits;
+      } else if (EPI == EPI_ARGMAX) {
+        const dim3 grid((unsigned)((a.N + REDUCE_ARGMAX_COLS - 1) / REDUCE_ARGMAX_COLS), (unsigned)a.M);
+        hipLaunchKernelGGL(k_gemm_reduce_argmax_lm_head, grid, dim3(256), 0, s, a, splits);
+        *a.n_cand = (int)grid.x;
       } else {
         const int64_t groups = (int64_t)a.M * (a.N / 4);
         hipLaunchKernelGGL(reduce, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, a, splits);
@@ -777,7 +923,7 @@ hipError_t launch_gemm(int dtype, int role, const GemmArgs& a, hipStream_t s, in
                                      k_gemv_down, k_gemvn_down, k_gemm_f32_down, partials, s);
       }
       return CAD_LAUNCH(EPI_RESID, down, TILE_N);
-    default: return CAD_LAUNCH(EPI_STORE_F32, lm_head, TILE_N);
+    default: return CAD_LAUNCH(EPI_ARGMAX, lm_head, TILE_N);
 #undef CAD_LAUNCH
   }
 }

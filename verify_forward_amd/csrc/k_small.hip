@@ -1,6 +1,7 @@
 // Row-wise kernels of the splice path: embedding gather, RMSNorm, rotary
-// positions + KV append, masked argmax, acceptance scan and the suffix-match
-// proposal.  All are bandwidth- or latency-bound; one work-group per row.
+// positions + KV append, the decision step (masked argmax from the LM head's
+// candidates, acceptance scan) and the suffix-match proposal.  All are
+// bandwidth- or latency-bound.
 #include "cad_internal.h"
 
 namespace cad {
@@ -364,116 +365,112 @@ hipError_t launch_rope_append(int dtype, const float* qkv, const float* qkv_part
 }
 
 // ---------------------------------------------------------------------------
-// masked argmax per row over fp32 logits: lowest id among equal maxima,
-// -1 (and CAD_DEV_EMPTY_MASK) when the row allows nothing
+// Decision step after the LM head: the masked argmax of every row from the
+// candidates the LM head's epilogue left (one per column tile: the tile's
+// largest allowed logit and its lowest id), then the acceptance scan of every
+// sequence.  A work-group of DECIDE_THREADS threads takes DECIDE_ROWS rows
+// (each wave DECIDE_RB of them, every candidate load in flight at once, up
+// to DECIDE_CPL per lane and chunk) and merges each row over its wave by
+// lane swaps.  When one work-group covers every row it also runs the
+// acceptance scan after a barrier (one thread per sequence); otherwise
+// k_accept follows as a second launch.
 // ---------------------------------------------------------------------------
+constexpr int DECIDE_THREADS = 1024;
+constexpr int DECIDE_RB = 4;    // rows per wave
+constexpr int DECIDE_ROWS = DECIDE_RB * DECIDE_THREADS / 64;  // rows per work-group
+constexpr int DECIDE_CPL = 4;   // candidates per lane, row and chunk
+
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return bi < 0 || v > bv || (v == bv && i < bi);
+  return i >= 0 && (bi < 0 || v > bv || (v == bv && i < bi));
 }
 
-constexpr int ARGMAX_THREADS = 1024;
-
-// One work-group per row; each thread takes whole 32-token mask words: the
-// word and its 32 logits (eight 16-byte loads, all in flight together) are
-// read unconditionally (indices clamped to the row) and the allowed ids are
-// compared in registers, in increasing id order.
-__global__ void __launch_bounds__(ARGMAX_THREADS) k_argmax(const float* __restrict__ logits, int vocab,
-                                                           const uint32_t* __restrict__ mask,
-                                                           int32_t* __restrict__ out, int32_t* status) {
-  __shared__ float sv[ARGMAX_THREADS / 64];
-  __shared__ int si[ARGMAX_THREADS / 64];
-  const int r = blockIdx.x;
-  const float* lg = logits + (int64_t)r * vocab;
-  const int words = (vocab + 31) / 32;
-  const bool vec = (vocab & 3) == 0;  // rows 16-byte aligned: vector loads
-  float bv = 0.f;
-  int bi = -1;
-  for (int w = threadIdx.x; w < words; w += blockDim.x) {
-    const uint32_t bits = mask ? mask[(int64_t)r * words + w] : 0xFFFFFFFFu;
-    float x[32];
-    if (vec) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int v4 = min(w * 8 + j, vocab / 4 - 1);
-        const f32x4 t = *(const f32x4*)(lg + 4 * v4);
-        x[4 * j] = t[0], x[4 * j + 1] = t[1], x[4 * j + 2] = t[2], x[4 * j + 3] = t[3];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 32; ++j) x[j] = lg[min(w * 32 + j, vocab - 1)];
-    }
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const int v = w * 32 + j;
-      if (((bits >> j) & 1u) && v < vocab && better(x[j], v, bv, bi)) { bv = x[j]; bi = v; }
-    }
-  }
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(bv, o);
-    const int oi = __shfl_xor(bi, o);
-    if (oi >= 0 && better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-  }
-  const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
-  if (l == 0) { sv[wv] = bv; si[wv] = bi; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int i = 1; i < (int)(blockDim.x >> 6); ++i)
-      if (si[i] >= 0 && better(sv[i], si[i], bv, bi)) { bv = sv[i]; bi = si[i]; }
-    out[r] = bi;
-    if (bi < 0 && status) atomicOr(status, (int32_t)CAD_DEV_EMPTY_MASK);
-  }
-}
-
-hipError_t launch_argmax(const float* logits, int rows, int vocab, const uint32_t* mask,
-                         int32_t* out, int32_t* status, hipStream_t s) {
-  if (vocab <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_argmax, dim3(rows), dim3(ARGMAX_THREADS), 0, s, logits, vocab, mask, out, status);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// acceptance: COMMIT -> N; VERIFY -> 1 + leading j >= 1 with a[j-1] == s[j].
-// `limit` (device, optional) caps the rows examined (the screening survivors).
-// ---------------------------------------------------------------------------
-__global__ void k_accept(const int32_t* __restrict__ a, const int32_t* __restrict__ span, RowMap rm,
-                         int mode, const int32_t* limit, int32_t* __restrict__ accepted) {
-  const int b = threadIdx.x;
-  if (b >= rm.n_seq) return;
+// acceptance of sequence b: COMMIT -> its rows (capped by the limit);
+// VERIFY -> 1 + the leading j >= 1 with argmax[j - 1] == span[j]
+__device__ __forceinline__ void accept_seq(const RowMap& rm, int b, const int32_t* span, int mode, const int32_t* limit,
+                                           int lim, const int32_t* argmax, int32_t* accepted) {
   const int s0 = rm.start[b];
   int n = rm.start[b + 1] - s0;
-  if (limit) n = min(n, max(1, *limit));
+  if (limit) n = min(n, lim);
   int acc = n;
   if (mode == CAD_VERIFY) {
     acc = 1;
-    while (acc < n && a[s0 + acc - 1] == span[s0 + acc]) ++acc;
+    while (acc < n && argmax[s0 + acc - 1] == span[s0 + acc]) ++acc;
   }
   accepted[b] = acc;
 }
 
-hipError_t launch_accept(const int32_t* argmax, const int32_t* span, const RowMap& rm, int mode,
-                         const int32_t* limit, int32_t* accepted, hipStream_t s) {
-  hipLaunchKernelGGL(k_accept, dim3(1), dim3(64), 0, s, argmax, span, rm, mode, limit, accepted);
-  return hipGetLastError();
+template <bool ACCEPT>
+__global__ void __launch_bounds__(DECIDE_THREADS) k_decide(const u32x2* __restrict__ cand, int n_cand, int rows,
+                                                           RowMap rm, const int32_t* __restrict__ span, int mode,
+                                                           const int32_t* limit, int32_t* __restrict__ argmax,
+                                                           int32_t* __restrict__ accepted, int32_t* status) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lim = limit ? max(1, *limit) : rows;
+  const int r0 = blockIdx.x * DECIDE_ROWS + wave * DECIDE_RB;
+  float bv[DECIDE_RB];
+  int bi[DECIDE_RB];
+#pragma unroll
+  for (int j = 0; j < DECIDE_RB; ++j) bv[j] = 0.f, bi[j] = -1;
+  // candidate chunks in increasing column order (one chunk for up to
+  // 64 * DECIDE_CPL candidates per row)
+  for (int c0 = 0; c0 < n_cand && r0 < rows; c0 += 64 * DECIDE_CPL) {
+    u32x2 e[DECIDE_RB][DECIDE_CPL];
+#pragma unroll
+    for (int j = 0; j < DECIDE_RB; ++j)
+#pragma unroll
+      for (int u = 0; u < DECIDE_CPL; ++u) {
+        // clamped indices: every load reads a valid candidate
+        const int c = min(c0 + lane + 64 * u, n_cand - 1), r = min(r0 + j, rows - 1);
+        e[j][u] = cand[(int64_t)c * rows + r];
+      }
+#pragma unroll
+    for (int j = 0; j < DECIDE_RB; ++j)
+#pragma unroll
+      for (int u = 0; u < DECIDE_CPL; ++u) {
+        const float v = __uint_as_float(e[j][u][0]);
+        const int i = (int)e[j][u][1];
+        if (c0 + lane + 64 * u < n_cand && better(v, i, bv[j], bi[j])) { bv[j] = v; bi[j] = i; }
+      }
+  }
+#pragma unroll
+  for (int j = 0; j < DECIDE_RB; ++j) {
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv[j], o);
+      const int oi = __shfl_xor(bi[j], o);
+      if (better(ov, oi, bv[j], bi[j])) { bv[j] = ov; bi[j] = oi; }
+    }
+    const int r = r0 + j;
+    if (lane == 0 && r < rows) {
+      argmax[r] = r < lim ? bi[j] : -1;
+      if (r < lim && bi[j] < 0 && status) atomicOr(status, (int32_t)CAD_DEV_EMPTY_MASK);
+    }
+  }
+  if constexpr (ACCEPT) {
+    // the barrier makes this work-group's argmax stores visible to all of it
+    __syncthreads();
+    if ((int)threadIdx.x < rm.n_seq) accept_seq(rm, threadIdx.x, span, mode, limit, lim, argmax, accepted);
+  }
 }
 
-__global__ void k_fill_i32(int32_t* p, int n, int32_t v) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = v;
+__global__ void k_accept(RowMap rm, const int32_t* __restrict__ span, int mode, const int32_t* limit,
+                         const int32_t* __restrict__ argmax, int32_t* __restrict__ accepted) {
+  const int b = threadIdx.x;
+  if (b < rm.n_seq) accept_seq(rm, b, span, mode, limit, limit ? max(1, *limit) : 0, argmax, accepted);
 }
 
-hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_fill_i32, dim3((n + 255) / 256), dim3(256), 0, s, p, n, v);
-  return hipGetLastError();
-}
-
-__global__ void k_mask_rows(int32_t* a, int rows, const int32_t* limit) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < rows && i >= *limit) a[i] = -1;
-}
-
-hipError_t launch_mask_rows(int32_t* argmax, int rows, const int32_t* limit, hipStream_t s) {
-  hipLaunchKernelGGL(k_mask_rows, dim3((rows + 255) / 256), dim3(256), 0, s, argmax, rows, limit);
+hipError_t launch_decide(const uint32_t* cand, int n_cand, int rows, const RowMap& rm, const int32_t* span,
+                         int mode, const int32_t* limit, int32_t* argmax, int32_t* accepted, int32_t* status,
+                         hipStream_t s) {
+  if (n_cand < 1 || rows < 1 || rm.n_seq > 64) return hipErrorInvalidValue;
+  const int wgs = (rows + DECIDE_ROWS - 1) / DECIDE_ROWS;
+  if (wgs == 1) {
+    hipLaunchKernelGGL(k_decide<true>, dim3(1), dim3(DECIDE_THREADS), 0, s, (const u32x2*)cand, n_cand, rows, rm, span,
+                       mode, limit, argmax, accepted, status);
+  } else {
+    hipLaunchKernelGGL(k_decide<false>, dim3(wgs), dim3(DECIDE_THREADS), 0, s, (const u32x2*)cand, n_cand, rows, rm,
+                       span, mode, limit, argmax, accepted, status);
+    hipLaunchKernelGGL(k_accept, dim3(1), dim3(64), 0, s, rm, span, mode, limit, argmax, accepted);
+  }
   return hipGetLastError();
 }
 
