@@ -167,6 +167,24 @@ cad_status cad_decode_step(cad_model* m, const cad_kv* kv, int64_t L, const int3
                            const uint32_t* mask_row, int32_t* argmax, float* logits,
                            int32_t* dev_status, cad_stream stream);
 
+/* The decode step for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, semantics and errors as cad_decode_step; the
+ * step's per-call buffers (activations, split-K partial sums, attention
+ * partials, argmax candidates) live in a static device array of
+ * CAD_NOALLOC_SCRATCH_BYTES bytes that the library holds on each GPU until
+ * the process ends (its address is resolved once per device, at
+ * cad_model_create or this call's first use on a device), instead of the
+ * model's workspace.  The call allocates nothing.  A model whose one-row
+ * workspace exceeds the scratch returns CAD_E_CAPACITY.  Every call on one
+ * GPU shares that GPU's array, which keeps the last call's contents (nothing
+ * in it needs to start at zero): calls that overlap in time on one GPU (two
+ * streams, two host threads) race and must be serialised by the caller. */
+#define CAD_NOALLOC_SCRATCH_BYTES (4 << 20)
+cad_status cad_decode_step_noalloc(cad_model* m, const cad_kv* kv, int64_t L, const int32_t* token,
+                                   const uint32_t* mask_row, int32_t* argmax, float* logits,
+                                   int32_t* dev_status, cad_stream stream);
+
 /* Context-copy proposal (CopyLoop §2 "Block Construction").  tokens: dev
  * int32 [T], the whole history whose last element is the new head.  For n =
  * min(max_ngram, T-1) down to min_ngram, find the largest p with p + n <= T-1

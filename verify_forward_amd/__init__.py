@@ -25,8 +25,9 @@ CAD_KV_BLOCK = 16
 CAD_MAX_SEQS = 64
 
 EXPORTS = ("cad_model_create", "cad_model_destroy", "cad_last_error", "cad_splice_forward",
-           "cad_decode_step", "cad_propose_suffix_match",
+           "cad_decode_step", "cad_decode_step_noalloc", "cad_propose_suffix_match",
            "cad_splice_forward_batched", "cad_splice_forward_looped", "cad_profile_enable", "cad_profile_read")
+CAD_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 PROFILE_FAMILIES = ("embed", "rmsnorm", "gemm_qkv", "rope_append", "attention", "attn_merge", "gemm_o",
                     "gemm_gate_up", "gemm_down", "gemm_lm_head", "decide")
@@ -81,6 +82,7 @@ def lib() -> ctypes.CDLL:
         L.cad_splice_forward.argtypes = [_VP, ctypes.POINTER(cad_kv), i64, _VP, i32, _VP, i32, _VP, _VP,
                                          _VP, _VP, _VP]
         L.cad_decode_step.argtypes = [_VP, ctypes.POINTER(cad_kv), i64, _VP, _VP, _VP, _VP, _VP, _VP]
+        L.cad_decode_step_noalloc.argtypes = [_VP, ctypes.POINTER(cad_kv), i64, _VP, _VP, _VP, _VP, _VP, _VP]
         L.cad_propose_suffix_match.argtypes = [_VP, i64, i32, i32, i32, _VP, _VP, _VP, _VP]
         L.cad_splice_forward_batched.argtypes = [_VP, ctypes.POINTER(cad_kv), i32, _VP, _VP, _VP, _VP, i32,
                                                  _VP, _VP, _VP, _VP, _VP]
@@ -88,7 +90,7 @@ def lib() -> ctypes.CDLL:
                                                 _VP, _VP, _VP, _VP, _VP, _VP]
         L.cad_profile_enable.argtypes = [_VP, i32]
         L.cad_profile_read.argtypes = [_VP, ctypes.c_char_p, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)]
-        for name in ("cad_model_create", "cad_splice_forward", "cad_decode_step",
+        for name in ("cad_model_create", "cad_splice_forward", "cad_decode_step", "cad_decode_step_noalloc",
                      "cad_propose_suffix_match",
                      "cad_splice_forward_batched", "cad_splice_forward_looped", "cad_profile_enable",
                      "cad_profile_read"):
@@ -211,6 +213,15 @@ def cad_decode_step(model: Model, kv: KVCache, L: int, token: torch.Tensor, mask
     s = kv.struct()
     _check(lib().cad_decode_step(model.handle, ctypes.byref(s), int(L), _p(token), _p(mask_row), _p(argmax),
                                  _p(logits), _p(dev_status), _stream(stream)))
+
+
+def cad_decode_step_noalloc(model: Model, kv: KVCache, L: int, token: torch.Tensor,
+                            mask_row: Optional[torch.Tensor], argmax: torch.Tensor,
+                            logits: Optional[torch.Tensor] = None, dev_status: Optional[torch.Tensor] = None,
+                            stream=None):
+    s = kv.struct()
+    _check(lib().cad_decode_step_noalloc(model.handle, ctypes.byref(s), int(L), _p(token), _p(mask_row),
+                                         _p(argmax), _p(logits), _p(dev_status), _stream(stream)))
 
 
 def cad_propose_suffix_match(tokens: torch.Tensor, max_ngram: int, min_ngram: int, K: int,

@@ -15,6 +15,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -64,7 +65,8 @@ struct ProfRec {
 // Per-call device buffers of the splice path (activations, partial sums,
 // attention partials, candidates), carved from one block of device memory:
 // the model's workspace (allocated at create, sized for max_tokens rows and
-// CAD_MAX_SEQS sequences).
+// CAD_MAX_SEQS sequences) or, for cad_decode_step_noalloc, the library's
+// static scratch array (one row, one sequence).
 struct Workspace {
   int64_t rows = 0;          // row capacity T (plane stride of the two-plane buffers)
   float* x = nullptr;        // [T][d] residual stream
@@ -406,6 +408,51 @@ cad_status check_seq(const cad_kv* kv, int64_t L, int64_t N, int max_tokens) {
   return CAD_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Static scratch for cad_decode_step_noalloc: the one-row workspace of a
+// decode step lives here, so that call allocates nothing.  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory: its device
+// address is resolved per device with hipGetSymbolAddress and only that
+// address is passed to kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[CAD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device (nullptr until resolved)
+
+// The device address of `scratch` on the current device, resolved once per
+// device (with that device current) and kept.
+cad_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(CAD_E_UNSUPPORTED, "device %d beyond the scratch table", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(CAD_E_HIP, "hipGetSymbolAddress returned no address for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CAD_OK;
+}
+
+// Split-K partial floats a one-row call needs: the weight-streaming
+// projections that leave partial sums (QKV, O, down) split K into at most one
+// piece per 512 k.  With this capacity a one-row call takes the same splits
+// as on the model's own workspace.
+int64_t one_row_split_floats(const cad_config& c) {
+  if (c.dtype != CAD_BF16) return 0;
+  auto f = [](int64_t K, int64_t N) { return (K + 511) / 512 * N; };
+  const int64_t qkv = (int64_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  int64_t best = f(c.d_model, qkv);
+  best = std::max(best, f((int64_t)c.n_q_heads * c.head_dim, c.d_model));
+  best = std::max(best, f(c.ffn_dim, c.d_model));
+  return best;
+}
+
 }  // namespace
 
 extern "C" {
@@ -455,6 +502,14 @@ cad_status cad_model_create(const cad_config* cfg, const cad_weights* w, cad_mod
   }
   m->ws_bytes = bytes;
   layout_workspace(c, c.max_tokens, CAD_MAX_SEQS, split_floats, (char*)m->ws, &m->main);
+  // set-up of the allocation-free decode step: the scratch address of this device
+  void* scratch_dev = nullptr;
+  st = scratch_of_current_device(&scratch_dev);
+  if (st != CAD_OK) {
+    (void)hipFree(m->ws);
+    delete m;
+    return st;
+  }
   m->freq = (double*)((char*)m->ws + o_freq);
   std::vector<double> fr(hd / 2);
   for (int64_t i = 0; i < hd / 2; ++i) fr[i] = std::pow((double)c.rope_theta, -2.0 * (double)i / (double)hd);
@@ -508,6 +563,32 @@ cad_status cad_decode_step(cad_model* m, const cad_kv* kv, int64_t L, const int3
   if (!m) return fail(CAD_E_ARG, "model is NULL");
   return cad_splice_forward(m, kv, L, token, 1, mask_row, CAD_COMMIT, argmax, m->w->survivors, logits,
                             dev_status, stream);
+}
+
+cad_status cad_decode_step_noalloc(cad_model* m, const cad_kv* kv, int64_t L, const int32_t* token,
+                                   const uint32_t* mask_row, int32_t* argmax, float* logits, int32_t* dev_status,
+                                   cad_stream stream) {
+  if (!m) return fail(CAD_E_ARG, "model is NULL");
+  void* base = nullptr;
+  cad_status st = scratch_of_current_device(&base);
+  if (st != CAD_OK) return st;
+  const int64_t split_floats = one_row_split_floats(m->cfg);
+  const size_t need = layout_workspace(m->cfg, 1, 1, split_floats, nullptr, nullptr);
+  if (need > (size_t)CAD_NOALLOC_SCRATCH_BYTES)
+    return fail(CAD_E_CAPACITY, "a decode step of this model needs %zu bytes of scratch; the maximum is %d", need,
+                CAD_NOALLOC_SCRATCH_BYTES);
+  Workspace ws;
+  layout_workspace(m->cfg, 1, 1, split_floats, (char*)base, &ws);
+  // run on the scratch workspace, with no instrumentation (recording would
+  // create events)
+  const uint32_t prof = m->prof_mask;
+  m->prof_mask = 0;
+  m->w = &ws;
+  st = cad_splice_forward(m, kv, L, token, 1, mask_row, CAD_COMMIT, argmax, ws.survivors, logits, dev_status,
+                          stream);
+  m->w = &m->main;
+  m->prof_mask = prof;
+  return st;
 }
 
 cad_status cad_splice_forward_batched(cad_model* m, const cad_kv* kv, int32_t n_seq,
