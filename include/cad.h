@@ -226,13 +226,100 @@ cad_status cad_splice_forward_looped(cad_model* m, const cad_kv* kv, int64_t L,
                                      int32_t* survivors, int32_t* argmax, int32_t* accepted,
                                      float* logits, int32_t* dev_status, cad_stream stream);
 
+/* ---- CopyLoop's concurrent pipeline on a looped model (loop_depth D > 1) ----
+ * CopyLoop §2 "Concurrent Pipeline": positions at different recurrence
+ * depths advance together, each on its own depth's KV states; §2 "Shallow
+ * Screening" and "Full-Depth Verification" read them out at depths ds and D.
+ *
+ * cad_loop_step: one tick.  Every group -- a run of `rows` consecutive
+ * positions starting at absolute position `pos`, that has had `depth`
+ * applications of the shared block so far -- gets one more application, on
+ * cache index `depth` (its rows attend to keys 0 .. pos + j of that depth's
+ * cache, and write their own K/V there).  A group's residual streams live in
+ * the caller's `state` (dev fp32 [state_rows][d_model], rows state ..
+ * state + rows - 1): read at the start of the tick for depth > 0 (depth 0
+ * starts from the embedding of the group's tokens), written back at its end.
+ * Groups must not share state rows; older (lower-position) groups must be
+ * deeper, so that every key a row reads has been written at its depth.
+ * tokens: dev int32 [total rows], the groups' tokens in group order.  If any
+ * group has readout = 1, the final norm and LM head run after the tick and
+ * argmax (dev int32 [total rows]; masked by `mask`, dev uint32 [total
+ * rows][ceil(V/32)] or NULL) and accepted (dev int32 [n_groups]; the VERIFY
+ * rule applied to each group's tokens) are written for every row and group
+ * (the caller uses those of its readout groups), and the fp32 logits of
+ * every row to `logits` (dev float [total rows][V]) if it is not NULL;
+ * otherwise none of them is touched.  All groups read block-table row 0 (one
+ * request).
+ * 1 <= n_groups <= CAD_MAX_SEQS; total rows <= max_tokens. */
+typedef struct {
+  int64_t pos;      /* absolute position of the group's first row */
+  int32_t rows;     /* >= 1 consecutive positions */
+  int32_t depth;    /* applications done before this tick, 0 .. loop_depth - 1 */
+  int32_t state;    /* first row of the group in `state` */
+  int32_t readout;  /* 1: masked argmax + acceptance after the tick; 0: none */
+} cad_loop_group;
+cad_status cad_loop_step(cad_model* m, const cad_kv* kv, int32_t n_groups, const cad_loop_group* groups,
+                         const int32_t* tokens, float* state, int32_t state_rows, const uint32_t* mask,
+                         int32_t* argmax, int32_t* accepted, float* logits, int32_t* dev_status,
+                         cad_stream stream);
+
+/* cad_loop_decode: CopyLoop decoding of one request on a looped model, the
+ * native scheduler over cad_loop_step (CopyLoop §2; §A.1 "Decoding
+ * algorithm").  The prompt (host int32 [L0]) is prefilled at every depth and
+ * its last full-depth prediction is the first token.  Then every tick
+ * advances every block in flight by one depth: a block is a head followed by
+ * up to max_copy tokens copied after the longest earlier match of the
+ * history's suffix (lengths max_ngram down to min_ngram, the suffix-match
+ * kernel); at screen_depth its tail is cut to the prefix agreeing with the
+ * predictions one position earlier, the cut rows are released and the last
+ * survivor's prediction heads the next block; at the full depth the tail is
+ * verified the same way -- the first mismatch commits the full-depth token as
+ * a correction and discards the block's rest and every younger block, a full
+ * match commits the last prediction as the next token (which the next
+ * block's head must equal, or that block and its descendants are discarded
+ * the same way).  At most max_rows rows are in flight: a block admitted with
+ * r free rows keeps at most r - 1 copied tokens, a head with no free row
+ * waits.  The committed tokens (out, host int32 [n_new]) are greedy
+ * full-depth decoding's.  The host reads decisions back after every tick
+ * that reads a block out (and after each proposal): this call synchronises
+ * its stream.  cad_loop_create allocates the pipeline's device buffers (the
+ * residual streams of loop_depth x (max_copy + 1) rows, a device history of
+ * max_len tokens) and pinned host staging; the model's max_tokens bounds the
+ * rows per tick and the prefill chunk.  max_len and the block table must
+ * hold L0 + n_new + loop_depth x (max_copy + 1) positions.  The KV cache is
+ * overwritten from position 0. */
+typedef struct cad_loop cad_loop;
+typedef struct {
+  int32_t screen_depth;  /* ds, 1 <= ds < loop_depth */
+  int32_t max_copy;      /* K, 0 .. 64 */
+  int32_t max_ngram, min_ngram;  /* suffix lengths, 1 <= min <= max <= 64 */
+  int32_t max_rows;      /* admission limit: rows in flight, >= 1, <= max_tokens */
+} cad_loop_params;
+typedef struct {
+  int64_t ticks;         /* cad_loop_step calls */
+  int64_t rows_run;      /* rows advanced by one depth, summed over ticks */
+  int64_t blocks;        /* blocks admitted */
+  int64_t proposed;      /* copied tokens proposed */
+  int64_t screened_out;  /* copied rows released at the screening depth */
+  int64_t rejected;      /* copied rows refused at the full depth */
+  int64_t discarded;     /* rows of younger blocks dropped with a refusal */
+  int64_t committed;     /* tokens committed (may pass n_new by a block) */
+  int64_t host_syncs;    /* host synchronisations */
+  int32_t dev_status;    /* CAD_DEV_* bits seen by the device */
+} cad_loop_stats;
+cad_status cad_loop_create(cad_model* m, int64_t max_len, const cad_loop_params* p, cad_loop** out);
+void cad_loop_destroy(cad_loop* lp);
+cad_status cad_loop_decode(cad_loop* lp, const cad_kv* kv, const int32_t* prompt, int64_t L0, int32_t n_new,
+                           int32_t* out, cad_loop_stats* stats, cad_stream stream);
+
 /* ---- instrumentation (measurement only, not part of the method) ----
  * Kernel families, in bit order: 0 "embed", 1 "rmsnorm", 2 "gemm_qkv",
  * 3 "rope_append", 4 "attention" (the partial-attention kernel), 5
  * "attn_merge" (the log-sum-exp merge of key partitions), 6 "gemm_o",
  * 7 "gemm_gate_up", 8 "gemm_down", 9 "gemm_lm_head" (with the mask and the
  * per-tile argmax in its epilogue), 10 "decide" (the argmax over the LM
- * head's tiles and the acceptance scan).  Each family is one kernel (one
+ * head's tiles and the acceptance scan), 11 "loop_state" (loading and saving
+ * the residual streams of a pipeline tick).  Each family is one kernel (one
  * named kernel per path; the LM head after a k split adds its reduce).
  * cad_profile_enable(m, family_mask) starts a fresh collection in which
  * every launch of a family whose bit is set is bracketed by a pair of

@@ -38,7 +38,9 @@ from .decision import masked_argmax, acceptance, top2_margin
 from .suffix import suffix_match
 from .looped import looped_splice
 from .batched import batched_splice
+from .copyloop import loop_step, copyloop_decode, greedy_decode
 
 __all__ = ["Config", "KVCache", "rms_norm", "rope_rotate", "decode_step", "splice",
            "sequential", "prefill", "final_logits", "masked_argmax", "acceptance",
-           "top2_margin", "suffix_match", "looped_splice", "batched_splice"]
+           "top2_margin", "suffix_match", "looped_splice", "batched_splice",
+           "loop_step", "copyloop_decode", "greedy_decode"]

@@ -26,11 +26,12 @@ CAD_MAX_SEQS = 64
 
 EXPORTS = ("cad_model_create", "cad_model_destroy", "cad_last_error", "cad_splice_forward",
            "cad_decode_step", "cad_decode_step_noalloc", "cad_propose_suffix_match",
-           "cad_splice_forward_batched", "cad_splice_forward_looped", "cad_profile_enable", "cad_profile_read")
+           "cad_splice_forward_batched", "cad_splice_forward_looped", "cad_loop_step", "cad_loop_create",
+           "cad_loop_destroy", "cad_loop_decode", "cad_profile_enable", "cad_profile_read")
 CAD_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 PROFILE_FAMILIES = ("embed", "rmsnorm", "gemm_qkv", "rope_append", "attention", "attn_merge", "gemm_o",
-                    "gemm_gate_up", "gemm_down", "gemm_lm_head", "decide")
+                    "gemm_gate_up", "gemm_down", "gemm_lm_head", "decide", "loop_state")
 CAD_PROFILE_ALL = -1
 
 
@@ -64,6 +65,22 @@ class cad_kv(ctypes.Structure):
                 ("block_table", _VP), ("max_blocks_per_seq", ctypes.c_int32)]
 
 
+class cad_loop_group(ctypes.Structure):
+    _fields_ = [("pos", ctypes.c_int64), ("rows", ctypes.c_int32), ("depth", ctypes.c_int32),
+                ("state", ctypes.c_int32), ("readout", ctypes.c_int32)]
+
+
+class cad_loop_params(ctypes.Structure):
+    _fields_ = [("screen_depth", ctypes.c_int32), ("max_copy", ctypes.c_int32), ("max_ngram", ctypes.c_int32),
+                ("min_ngram", ctypes.c_int32), ("max_rows", ctypes.c_int32)]
+
+
+class cad_loop_stats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("ticks", "rows_run", "blocks", "proposed", "screened_out", "rejected",
+                                              "discarded", "committed", "host_syncs")] + \
+               [("dev_status", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -88,11 +105,18 @@ def lib() -> ctypes.CDLL:
                                                  _VP, _VP, _VP, _VP, _VP]
         L.cad_splice_forward_looped.argtypes = [_VP, ctypes.POINTER(cad_kv), i64, _VP, i32, i32, _VP, _VP,
                                                 _VP, _VP, _VP, _VP, _VP, _VP]
+        L.cad_loop_step.argtypes = [_VP, ctypes.POINTER(cad_kv), i32, ctypes.POINTER(cad_loop_group), _VP, _VP, i32,
+                                    _VP, _VP, _VP, _VP, _VP, _VP]
+        L.cad_loop_create.argtypes = [_VP, i64, ctypes.POINTER(cad_loop_params), ctypes.POINTER(_VP)]
+        L.cad_loop_destroy.argtypes = [_VP]
+        L.cad_loop_destroy.restype = None
+        L.cad_loop_decode.argtypes = [_VP, ctypes.POINTER(cad_kv), _VP, i64, i32, _VP, ctypes.POINTER(cad_loop_stats),
+                                      _VP]
         L.cad_profile_enable.argtypes = [_VP, i32]
         L.cad_profile_read.argtypes = [_VP, ctypes.c_char_p, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)]
         for name in ("cad_model_create", "cad_splice_forward", "cad_decode_step", "cad_decode_step_noalloc",
-                     "cad_propose_suffix_match",
-                     "cad_splice_forward_batched", "cad_splice_forward_looped", "cad_profile_enable",
+                     "cad_propose_suffix_match", "cad_splice_forward_batched", "cad_splice_forward_looped",
+                     "cad_loop_step", "cad_loop_create", "cad_loop_decode", "cad_profile_enable",
                      "cad_profile_read"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -256,6 +280,59 @@ def cad_splice_forward_looped(model: Model, kv: KVCache, L: int, span: torch.Ten
                                            int(screen_depth), _p(mask), _p(screen_argmax), _p(survivors),
                                            _p(argmax), _p(accepted), _p(logits), _p(dev_status),
                                            _stream(stream)))
+
+
+def cad_loop_step(model: Model, kv: KVCache, groups: Sequence, tokens: torch.Tensor, state: torch.Tensor,
+                  mask: Optional[torch.Tensor], argmax: Optional[torch.Tensor], accepted: Optional[torch.Tensor],
+                  logits: Optional[torch.Tensor] = None, dev_status: Optional[torch.Tensor] = None, stream=None):
+    """``groups``: sequence of (pos, rows, depth, state_row, readout) tuples;
+    ``state``: float32 device tensor [state_rows][d_model]."""
+    arr = (cad_loop_group * len(groups))(*[cad_loop_group(int(p), int(r), int(d), int(st), int(ro))
+                                           for p, r, d, st, ro in groups])
+    s = kv.struct()
+    _check(lib().cad_loop_step(model.handle, ctypes.byref(s), len(groups), arr, _p(tokens), _p(state),
+                               int(state.shape[0]), _p(mask), _p(argmax), _p(accepted), _p(logits),
+                               _p(dev_status), _stream(stream)))
+
+
+class Loop:
+    """Owns a ``cad_loop*`` (the pipeline's buffers) and keeps its model alive."""
+
+    def __init__(self, handle, model: Model):
+        self.handle, self.model = handle, model
+
+    def __del__(self):
+        try:
+            if self.handle:
+                cad_loop_destroy(self)
+        except Exception:
+            pass
+
+
+def cad_loop_create(model: Model, max_len: int, screen_depth: int, max_copy: int, max_rows: int,
+                    max_ngram: int = 4, min_ngram: int = 1) -> Loop:
+    p = cad_loop_params(int(screen_depth), int(max_copy), int(max_ngram), int(min_ngram), int(max_rows))
+    h = _VP()
+    _check(lib().cad_loop_create(model.handle, int(max_len), ctypes.byref(p), ctypes.byref(h)))
+    return Loop(h, model)
+
+
+def cad_loop_destroy(loop: Loop):
+    if loop.handle:
+        lib().cad_loop_destroy(loop.handle)
+        loop.handle = None
+
+
+def cad_loop_decode(loop: Loop, kv: KVCache, prompt: Sequence[int], n_new: int, stream=None):
+    """Returns ``(tokens, stats)``: the ``n_new`` committed tokens and the
+    pipeline counters as a dict."""
+    pr = (ctypes.c_int32 * len(prompt))(*[int(t) for t in prompt])
+    out = (ctypes.c_int32 * int(n_new))()
+    st = cad_loop_stats()
+    s = kv.struct()
+    _check(lib().cad_loop_decode(loop.handle, ctypes.byref(s), ctypes.cast(pr, _VP), len(prompt), int(n_new),
+                                 ctypes.cast(out, _VP), ctypes.byref(st), _stream(stream)))
+    return list(out), {n: int(getattr(st, n)) for n, _ in cad_loop_stats._fields_}
 
 
 def cad_profile_enable(model: Model, families=CAD_PROFILE_ALL):

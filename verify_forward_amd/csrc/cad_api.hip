@@ -51,11 +51,11 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 enum ProfFamily {
   PF_EMBED, PF_NORM, PF_QKV, PF_ROPE, PF_ATTN, PF_MERGE, PF_O, PF_GATEUP, PF_DOWN, PF_HEAD,
-  PF_DECIDE, PF_COUNT
+  PF_DECIDE, PF_LOOP_STATE, PF_COUNT
 };
 static const char* const kProfNames[PF_COUNT] = {
     "embed", "rmsnorm", "gemm_qkv", "rope_append", "attention", "attn_merge", "gemm_o",
-    "gemm_gate_up", "gemm_down", "gemm_lm_head", "decide"};
+    "gemm_gate_up", "gemm_down", "gemm_lm_head", "decide", "loop_state"};
 
 struct ProfRec {
   int family;
@@ -201,6 +201,7 @@ KVView view_of(const cad_model* m, const cad_kv* kv, int ci) {
   v.table = kv->block_table;
   v.num_blocks = kv->num_blocks;
   v.max_blocks = kv->max_blocks_per_seq;
+  v.cache_stride = kv->num_blocks * c.n_kv_heads * CAD_KV_BLOCK * c.head_dim;
   v.span_k = m->w->span_k;
   v.span_v = m->w->span_v;
   v.span_cap = m->w->span_cap;
@@ -455,6 +456,15 @@ int64_t one_row_split_floats(const cad_config& c) {
 
 }  // namespace
 
+namespace cad {
+cad_status set_error(cad_status s, const char* msg) {
+  g_err = msg;
+  return s;
+}
+}  // namespace cad
+
+const cad_config* cad_model_config(const cad_model* m) { return &m->cfg; }
+
 extern "C" {
 
 const char* cad_last_error(void) { return g_err.c_str(); }
@@ -656,6 +666,62 @@ cad_status cad_splice_forward_looped(cad_model* m, const cad_kv* kv, int64_t L,
   st = run_blocks(m, kv, rm, screen_depth, c.loop_depth, survivors, dev_status, s);
   if (st != CAD_OK) return st;
   return readout(m, rm, logits, mask, span, CAD_VERIFY, survivors, argmax, accepted, dev_status, s);
+}
+
+cad_status cad_loop_step(cad_model* m, const cad_kv* kv, int32_t n_groups, const cad_loop_group* groups,
+                         const int32_t* tokens, float* state, int32_t state_rows, const uint32_t* mask,
+                         int32_t* argmax, int32_t* accepted, float* logits, int32_t* dev_status,
+                         cad_stream stream) {
+  if (!m) return fail(CAD_E_ARG, "model is NULL");
+  const cad_config& c = m->cfg;
+  if (c.loop_depth < 2) return fail(CAD_E_ARG, "model is not looped (loop_depth < 2)");
+  cad_status st = check_kv(m, kv);
+  if (st != CAD_OK) return st;
+  if (n_groups < 1 || n_groups > CAD_MAX_SEQS) return fail(CAD_E_ARG, "n_groups %d outside [1, %d]", n_groups, CAD_MAX_SEQS);
+  if (!groups || !tokens || !state) return fail(CAD_E_ARG, "groups/tokens/state is NULL");
+  if (state_rows < 1) return fail(CAD_E_ARG, "state_rows %d < 1", state_rows);
+  RowMap rm{};
+  StateMap sm{};
+  rm.n_seq = n_groups;
+  bool any_readout = false;
+  for (int b = 0; b < n_groups; ++b) {
+    const cad_loop_group& g = groups[b];
+    if (g.rows < 1) return fail(CAD_E_ARG, "group %d has no rows", b);
+    if (g.depth < 0 || g.depth >= c.loop_depth)
+      return fail(CAD_E_ARG, "group %d depth %d outside [0, %d)", b, g.depth, c.loop_depth);
+    if (g.readout != 0 && g.readout != 1) return fail(CAD_E_ARG, "group %d readout %d is neither 0 nor 1", b, g.readout);
+    if (g.state < 0 || (int64_t)g.state + g.rows > state_rows)
+      return fail(CAD_E_ARG, "group %d state rows [%d, %d) outside [0, %d)", b, g.state, g.state + g.rows, state_rows);
+    for (int o = 0; o < b; ++o)
+      if (g.state < groups[o].state + groups[o].rows && groups[o].state < g.state + g.rows)
+        return fail(CAD_E_ARG, "groups %d and %d share state rows", o, b);
+    st = check_seq(kv, g.pos, g.rows, c.max_tokens);
+    if (st != CAD_OK) return st;
+    rm.start[b + 1] = rm.start[b] + g.rows;
+    if (rm.start[b + 1] > c.max_tokens)
+      return fail(CAD_E_CAPACITY, "%d rows in the tick exceed max_tokens %d", rm.start[b + 1], c.max_tokens);
+    rm.L[b] = g.pos;
+    sm.base[b] = g.state;
+    any_readout |= g.readout != 0;
+  }
+  if ((any_readout && (!argmax || !accepted))) return fail(CAD_E_ARG, "argmax/accepted is NULL with a readout");
+  if (logits && !aligned16(logits)) return fail(CAD_E_ARG, "logits must be 16-byte aligned");
+  rm.total = rm.start[n_groups];
+  rowmap_pad(rm);
+  for (int b = 0; b < n_groups; ++b) {
+    rm.trow[b] = 0;                // one request: block-table row 0
+    rm.cidx[b] = groups[b].depth;  // its depth's cache
+  }
+  hipStream_t s = (hipStream_t)stream;
+  LAUNCH(PF_LOOP_STATE, launch_loop_load(c.dtype, m->tok_embed, c.vocab, c.d_model, tokens, state, rm, sm, m->w->x,
+                                         dev_status, s));
+  m->x_parts = 0;
+  st = run_blocks(m, kv, rm, 0, 1, nullptr, dev_status, s);
+  if (st != CAD_OK) return st;
+  LAUNCH(PF_LOOP_STATE, launch_loop_store(m->w->x, m->w->split_ws, m->x_parts, c.d_model, state, rm, sm, s));
+  m->x_parts = 0;
+  if (!any_readout) return CAD_OK;
+  return readout(m, rm, logits, mask, tokens, CAD_VERIFY, nullptr, argmax, accepted, dev_status, s);
 }
 
 cad_status cad_profile_enable(cad_model* m, int32_t family_mask) {

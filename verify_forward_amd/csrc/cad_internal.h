@@ -77,18 +77,30 @@ template <> __device__ __forceinline__ f16_t from_f<f16_t>(float v) { return f2h
 
 // Which sequence each span row belongs to and at which absolute position it
 // sits.  Passed by value to the kernels (fits the kernel-argument segment).
+// A "sequence" here is a run of consecutive positions that share a cache: a
+// request of a batched call, or a group of positions of a looped decoder at
+// one recurrence depth (CopyLoop's concurrent pipeline runs groups at
+// several depths in one launch, each on its own depth's cache).
 struct RowMap {
   int32_t n_seq;
   int32_t total;
   int32_t start[CAD_MAX_SEQS + 1];   // CSR row offsets
   int32_t pstart[CAD_MAX_SEQS + 1];  // row offsets in the span K/V workspace (each sequence padded to 64 rows)
-  int64_t L[CAD_MAX_SEQS];           // cache length before the call
+  int64_t L[CAD_MAX_SEQS];           // cache length before the call (absolute position of the first row)
+  int32_t trow[CAD_MAX_SEQS];        // block-table row of the sequence
+  int32_t cidx[CAD_MAX_SEQS];        // cache index of the sequence, relative to the KVView's base
 };
 
-// fill pstart from start
+// fill pstart from start; every sequence reads its own block-table row and
+// the KVView's cache (callers with other tables or caches set trow / cidx
+// afterwards)
 inline void rowmap_pad(RowMap& rm) {
   rm.pstart[0] = 0;
-  for (int b = 0; b < rm.n_seq; ++b) rm.pstart[b + 1] = rm.pstart[b] + (rm.start[b + 1] - rm.start[b] + 63) / 64 * 64;
+  for (int b = 0; b < rm.n_seq; ++b) {
+    rm.pstart[b + 1] = rm.pstart[b] + (rm.start[b + 1] - rm.start[b] + 63) / 64 * 64;
+    rm.trow[b] = b;
+    rm.cidx[b] = 0;
+  }
 }
 
 __device__ __forceinline__ int row_seq(const RowMap& rm, int r) {
@@ -101,9 +113,10 @@ __device__ __forceinline__ int row_seq(const RowMap& rm, int r) {
 struct KVView {
   void* k;               // [num_blocks][Hkv][16][hd]
   void* v;               // [num_blocks][Hkv][hd][16]
-  const int32_t* table;  // [n_seq][max_blocks]
+  const int32_t* table;  // [rows][max_blocks]
   int64_t num_blocks;
   int32_t max_blocks;
+  int64_t cache_stride;  // elements from one cache index to the next (RowMap.cidx)
   // bf16 models: this call's span K (after rotation) and V at half precision,
   // read by attention for keys >= L instead of their bf16 cache copies.
   // span_k [span_cap][Hkv][hd]; span_v [Hkv][hd][span_cap]; rows at RowMap.pstart
@@ -169,6 +182,16 @@ inline int max_candidates(int vocab) { return (vocab + 63) / 64; }
 // split-K workspace of a model's own workspace: GEMM_SPLIT_FLOATS floats (128 MB)
 constexpr int64_t GEMM_SPLIT_FLOATS = (int64_t)32 << 20;
 
+// First row of each sequence's hidden states in a caller's state buffer
+// (the looped decoder's pipeline tick carries every row's residual stream
+// from one tick to the next).
+struct StateMap {
+  int32_t base[CAD_MAX_SEQS];
+};
+
+// the calling thread's error message (cad_last_error) and the given status
+cad_status set_error(cad_status s, const char* msg);
+
 // ---- launchers (stream-ordered, no host sync) ----
 hipError_t launch_embed(int dtype, const void* table, int vocab, int d, const int32_t* tokens,
                         int rows, float* x, int32_t* status, hipStream_t s);
@@ -181,6 +204,15 @@ hipError_t launch_rmsnorm(int dtype, float* x, const float* x_part, int n_part, 
 // squares of 256-element slices to ss [rows][rms_slices(d)]; the
 // weight-streaming projection that follows applies the norm (GemmArgs.norm_*)
 hipError_t launch_rms_slices(float* x, const float* x_part, int n_part, int rows, int d, float* ss, hipStream_t s);
+// pipeline tick of a looped model: x[r] = the embedding of tokens[r] for rows
+// of sequences at cache index 0 (their first application of the block), else
+// the row's saved state state[sm.base[b] + j] (fp32 [.][d])
+hipError_t launch_loop_load(int dtype, const void* table, int vocab, int d, const int32_t* tokens, const float* state,
+                            const RowMap& rm, const StateMap& sm, float* x, int32_t* status, hipStream_t s);
+// x += the n_part pending partial planes (written back) and every row saved
+// to state[sm.base[b] + j]
+hipError_t launch_loop_store(float* x, const float* x_part, int n_part, int d, float* state, const RowMap& rm,
+                             const StateMap& sm, hipStream_t s);
 int rms_slices(int d);
 // partials: see launch_epi; nullptr makes every launch apply its epilogue
 hipError_t launch_gemm(int dtype, int role, const GemmArgs& a, hipStream_t s, int* partials = nullptr);
@@ -220,3 +252,6 @@ hipError_t launch_suffix_match(const int32_t* tokens, int64_t T, int max_n, int 
 int attention_parts(int rows, int n_seq, int hq, int hkv, int64_t max_cache_keys, int max_seq_rows);
 
 }  // namespace cad
+
+// shape of a model handle (library-internal accessor)
+const cad_config* cad_model_config(const cad_model* m);

@@ -200,14 +200,15 @@ k_attn_bf16(AttnArgs p) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) m_run[qb] = -1e30f, l_run[qb] = 0.f;
 
-  const int32_t* table = p.kv.table + (int64_t)b * p.kv.max_blocks;
+  const int32_t* table = p.kv.table + (int64_t)p.rm.trow[b] * p.kv.max_blocks;
   // Staging: the threads of wave w copy cache block jb = w / (TPB / 64) of
   // each tile, so the block id is uniform over the wave (a scalar load).
   const int jb = __builtin_amdgcn_readfirstlane(tid / TPB);
   const int ct = tid % TPB;
   const int64_t kv_blk_stride = (int64_t)p.hkv * CAD_KV_BLOCK * HD;  // elements per cache block
-  const bf16_t* kbase = (const bf16_t*)p.kv.k + (int64_t)kvh * CAD_KV_BLOCK * HD;
-  const bf16_t* vbase = (const bf16_t*)p.kv.v + (int64_t)kvh * CAD_KV_BLOCK * HD;
+  const int64_t coff = (int64_t)p.rm.cidx[b] * p.kv.cache_stride + (int64_t)kvh * CAD_KV_BLOCK * HD;
+  const bf16_t* kbase = (const bf16_t*)p.kv.k + coff;
+  const bf16_t* vbase = (const bf16_t*)p.kv.v + coff;
   // cache block of tile t for this wave (lane 0 of the result), or -1 when
   // the tile's part of the key range does not reach it (then nothing is
   // read); unused by span tiles.  Lanes 32..63 read the next block's id
@@ -509,10 +510,11 @@ __global__ void __launch_bounds__(256, 2) k_attn_dec(AttnArgs p) {
   const int64_t t0 = TT * part / p.n_parts, t1 = TT * (part + 1) / p.n_parts;
   const int nw = t1 - t0 > wave ? (int)((t1 - t0 - wave + 3) / 4) : 0;
   const int64_t nblk = (L + CAD_KV_BLOCK - 1) / CAD_KV_BLOCK;  // cached blocks of the sequence
-  const int32_t* table = p.kv.table + (int64_t)b * p.kv.max_blocks;
+  const int32_t* table = p.kv.table + (int64_t)p.rm.trow[b] * p.kv.max_blocks;
   const int64_t kv_blk_stride = (int64_t)p.hkv * CAD_KV_BLOCK * HD;
-  const bf16_t* kbase = (const bf16_t*)p.kv.k + (int64_t)kvh * CAD_KV_BLOCK * HD;
-  const bf16_t* vbase = (const bf16_t*)p.kv.v + (int64_t)kvh * CAD_KV_BLOCK * HD;
+  const int64_t coff = (int64_t)p.rm.cidx[b] * p.kv.cache_stride + (int64_t)kvh * CAD_KV_BLOCK * HD;
+  const bf16_t* kbase = (const bf16_t*)p.kv.k + coff;
+  const bf16_t* vbase = (const bf16_t*)p.kv.v + coff;
   const int64_t srow0 = p.rm.pstart[b];  // span workspace row of key L (64-row padded region)
 
   f32x4 o[DB];
@@ -855,9 +857,9 @@ k_attn_f32(AttnArgs p, int hd) {
   const float* q = (const float*)p.q + ((int64_t)r * p.hq + head) * hd;
   for (int d = lane; d < hd; d += 64) sq[d] = q[d];
   __syncthreads();
-  const float* kc = (const float*)p.kv.k;
-  const float* vc = (const float*)p.kv.v;
-  const int32_t* table = p.kv.table + (int64_t)b * p.kv.max_blocks;
+  const float* kc = (const float*)p.kv.k + (int64_t)p.rm.cidx[b] * p.kv.cache_stride;
+  const float* vc = (const float*)p.kv.v + (int64_t)p.rm.cidx[b] * p.kv.cache_stride;
+  const int32_t* table = p.kv.table + (int64_t)p.rm.trow[b] * p.kv.max_blocks;
   const float scale = 1.0f / sqrtf((float)hd);
   float m = -INFINITY, l = 0.f;
   float o[F32_MAX_HD];

@@ -47,6 +47,64 @@ hipError_t launch_embed(int dtype, const void* table, int vocab, int d, const in
 }
 
 // ---------------------------------------------------------------------------
+// pipeline tick of a looped decoder: each row's residual stream is the
+// embedding of its token on its group's first application of the shared
+// block, and the state saved by the previous tick afterwards; after the tick
+// every row's stream (with the pending k-split partials of the last
+// projection added in split order) is saved again
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void k_loop_load(const T* __restrict__ table, int vocab, int d, const int32_t* __restrict__ tok,
+                            const float* __restrict__ state, RowMap rm, StateMap sm, float* __restrict__ x,
+                            int32_t* status) {
+  const int r = blockIdx.x;
+  const int b = row_seq(rm, r);
+  float* dst = x + (int64_t)r * d;
+  if (rm.cidx[b] > 0) {
+    const float* src = state + (int64_t)(sm.base[b] + r - rm.start[b]) * d;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) dst[i] = src[i];
+    return;
+  }
+  const int t = tok[r];
+  const bool ok = t >= 0 && t < vocab;
+  if (!ok && threadIdx.x == 0 && status) atomicOr(status, (int32_t)CAD_DEV_BAD_TOKEN);
+  const T* src = table + (int64_t)(ok ? t : 0) * d;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) dst[i] = ok ? to_f<T>(src[i]) : 0.f;
+}
+
+hipError_t launch_loop_load(int dtype, const void* table, int vocab, int d, const int32_t* tokens, const float* state,
+                            const RowMap& rm, const StateMap& sm, float* x, int32_t* status, hipStream_t s) {
+  if (dtype == CAD_BF16)
+    hipLaunchKernelGGL(k_loop_load<bf16_t>, dim3(rm.total), dim3(ROW_THREADS), 0, s, (const bf16_t*)table, vocab, d,
+                       tokens, state, rm, sm, x, status);
+  else
+    hipLaunchKernelGGL(k_loop_load<float>, dim3(rm.total), dim3(ROW_THREADS), 0, s, (const float*)table, vocab, d,
+                       tokens, state, rm, sm, x, status);
+  return hipGetLastError();
+}
+
+__global__ void k_loop_store(float* __restrict__ x, const float* __restrict__ x_part, int n_part, int d,
+                             float* __restrict__ state, RowMap rm, StateMap sm) {
+  const int r = blockIdx.x;
+  const int b = row_seq(rm, r);
+  float* xr = x + (int64_t)r * d;
+  float* st = state + (int64_t)(sm.base[b] + r - rm.start[b]) * d;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    float v = xr[i];
+    for (int sp = 0; sp < n_part; ++sp) v += x_part[((int64_t)sp * rm.total + r) * d + i];
+    if (n_part > 0) xr[i] = v;
+    st[i] = v;
+  }
+}
+
+hipError_t launch_loop_store(float* x, const float* x_part, int n_part, int d, float* state, const RowMap& rm,
+                             const StateMap& sm, hipStream_t s) {
+  if (n_part > 0 && !x_part) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_loop_store, dim3(rm.total), dim3(ROW_THREADS), 0, s, x, x_part, n_part, d, state, rm, sm);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // RMSNorm: out[r] = x[r] / sqrt(mean(x[r]^2) + eps) * g: fp32 for fp32
 // models, split into bf16 hi / lo planes (the next projection's operands)
 // for bf16 models
@@ -229,7 +287,7 @@ __global__ void __launch_bounds__(ROPE_THREADS) k_rope_append(const float* __res
   // independent loads first: this row's cache block and its rotation
   // frequency (one pair per thread)
   bool write_kv = write_limit == nullptr || local < *write_limit;
-  const int64_t blk = write_kv ? kv.table[(int64_t)b * kv.max_blocks + pos / CAD_KV_BLOCK] : 0;
+  const int64_t blk = write_kv ? kv.table[(int64_t)rm.trow[b] * kv.max_blocks + pos / CAD_KV_BLOCK] : 0;
   const double fr = (int)threadIdx.x < half ? freq[threadIdx.x] : 0.0;
   // the row's projection output for these heads, staged in LDS as
   // [q heads][k heads][v heads] x hd: the stored values, or the sum of the
@@ -284,8 +342,8 @@ __global__ void __launch_bounds__(ROPE_THREADS) k_rope_append(const float* __res
     write_kv = false;
   }
   const int slot = (int)(pos % CAD_KV_BLOCK);
-  T* kc = (T*)kv.k;
-  T* vc = (T*)kv.v;
+  T* kc = (T*)kv.k + (int64_t)rm.cidx[b] * kv.cache_stride;
+  T* vc = (T*)kv.v + (int64_t)rm.cidx[b] * kv.cache_stride;
   const int64_t wrow = rm.pstart[b] + local;  // span workspace row
   f16_t* sk = kv.span_k ? kv.span_k + wrow * hkv * hd : nullptr;
   // the row's rotation, one (cos, sin) per pair, in LDS
