@@ -312,6 +312,86 @@ def looped_bench(reps=10):
                         "L=4096, head + suffix-match proposal (K=8)", **res}
 
 
+def copyloop_bench(n_new=64, L0=4096, K=8, ds=2):
+    """CopyLoop decoding on the looped shape (d 2048, 16 x 128 heads, FFN
+    5632, vocab 32000, depth 8): prefill of a 4096-token prompt, then n_new
+    tokens by the pipeline (context-copy blocks of up to K = 8 tokens,
+    screening at depth 2, verification at depth 8, admission limit 64 rows)
+    and by device-resident full-depth autoregressive decoding (one looped
+    splice of one token through all 8 depths per token, each step's argmax
+    fed to the next on the device).  Cases: the random-init model of the
+    configuration on the repeated-line prompt (its depth-2 readouts rarely
+    agree with depth 8, so screening prunes nearly every copy); the same with
+    the block's weights scaled by 0.1 (depths agree: a stand-in for a looped
+    model whose shallow predictions are usable); and that model on a prompt
+    whose last 256 tokens are its own greedy continuation (the repeated-span
+    regime context copying targets).  Reports tokens/s of both decoders, the
+    speedup, whether they committed the same tokens, and the pipeline
+    counters."""
+    import torch
+    import synth
+    import verify_forward_amd as cad
+    shape = synth.LOOPED
+    D = shape.loop_depth
+    out = {"workload": f"looped shared block (d 2048, 16 x 128 heads, FFN 5632, vocab 32000, depth 8), "
+                       f"prompt of {L0} tokens, {n_new} new tokens, K={K}, ds={ds}, max_rows=64"}
+    lines = [int(t) for t in synth.make_line_prompt(L0, shape.vocab).tokens]
+    cap = L0 + 256 + n_new + D * (K + 1) + 16
+    nb = (cap + 15) // 16
+
+    def ar_decode(model, kv, prompt, n):
+        """device-resident greedy decoding: tokens stay on the device"""
+        pr = torch.tensor(prompt, dtype=torch.int32, device="cuda")
+        gen = torch.empty(n, dtype=torch.int32, device="cuda")
+        sa = torch.empty(len(prompt), dtype=torch.int32, device="cuda")
+        am = torch.empty(len(prompt), dtype=torch.int32, device="cuda")
+        one = torch.empty(1, dtype=torch.int32, device="cuda")
+        sv = torch.empty(1, dtype=torch.int32, device="cuda")
+        acc = torch.empty(1, dtype=torch.int32, device="cuda")
+        L = len(prompt)
+        cad.cad_splice_forward_looped(model, kv, 0, pr, D, None, sa, sv, am, acc)
+        gen[0:1].copy_(sa[L - 1:L])
+        for i in range(1, n):
+            cad.cad_splice_forward_looped(model, kv, L + i - 1, gen[i - 1:i], D, None, gen[i:i + 1], sv, one, acc)
+        return gen
+
+    for name, scale, self_cont in (("random_init", 1.0, False), ("block_scaled_0.1", 0.1, False),
+                                   ("block_scaled_0.1_self_continuation", 0.1, True)):
+        W = synth.make_weights(shape, device="cuda")
+        if scale != 1.0:
+            for k in ("w_qkv", "w_o", "w_gate_up", "w_down"):
+                W["layers"][0][k].mul_(scale)
+        kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device="cuda")
+        model = cad.cad_model_create(shape, W, max_tokens=L0)
+        prompt = lines
+        if self_cont:
+            cont = ar_decode(model, kv, lines[:L0 - 256], 256)
+            prompt = lines[:L0 - 256] + [int(t) for t in cont.cpu()]
+        loop = cad.cad_loop_create(model, cap, ds, K, 64)
+        cad.cad_loop_decode(loop, kv, prompt, 8)          # warm up
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        toks, st = cad.cad_loop_decode(loop, kv, prompt, n_new)
+        torch.cuda.synchronize()
+        t_loop = time.perf_counter() - t0
+        ar_decode(model, kv, prompt, n_new)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        gen = ar_decode(model, kv, prompt, n_new)
+        torch.cuda.synchronize()
+        t_ar = time.perf_counter() - t0
+        out[name] = {"pipeline_tok_s": round(n_new / t_loop, 1), "full_depth_ar_tok_s": round(n_new / t_ar, 1),
+                     "tokens_equal_to_ar": [int(t) for t in gen.cpu()] == [int(t) for t in toks],
+                     "speedup": round(t_ar / t_loop, 3), "pipeline_s": round(t_loop, 4), "ar_s": round(t_ar, 4),
+                     "stats": st}
+        log(f"[bench] copyloop {name}: {out[name]['pipeline_tok_s']} tok/s vs AR {out[name]['full_depth_ar_tok_s']}")
+        cad.cad_loop_destroy(loop)
+        cad.cad_model_destroy(model)
+        del kv, W
+        torch.cuda.empty_cache()
+    return out
+
+
 def s_of_n(wl, Ns=(1, 2, 4, 8, 16, 32, 64, 128, 256, 512), L=1024):
     """The pages' s(N) = T(N one-token decode steps) / T(one splice of N) at the
     7B shape and L = 1024 (Copy-as-Decode §3 "Kernel microbenchmark", Table 1's
@@ -497,7 +577,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the serve, looped, s(N) and copy-bandwidth reports")
-    ap.add_argument("--only", choices=["serve", "looped"],
+    ap.add_argument("--only", choices=["serve", "looped", "copyloop"],
                     help="run only the batched serve or the looped-block report (one JSON line; for kernel profiles)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain device copy of 1 GiB first (a known-size reference for HBM counters)")
@@ -522,6 +602,9 @@ def main():
     N, L = args.span, args.L
     if args.only == "looped":
         print(json.dumps({"looped": looped_bench()}), flush=True)
+        return
+    if args.only == "copyloop":
+        print(json.dumps({"copyloop_pipeline": copyloop_bench()}), flush=True)
         return
     wl = Workload(shape, L, max_tokens=max(N, 512))
     if args.only == "serve":
@@ -635,6 +718,7 @@ def main():
     if not args.no_extras:
         out["looped"] = looped_bench()
         log("[bench] looped done")
+        out["copyloop_pipeline"] = copyloop_bench()
         out["llama_1b"] = sweep_1b()
 
     if not args.no_cpu_baseline:

@@ -246,6 +246,13 @@ hipError_t launch_suffix_match(const int32_t* tokens, int64_t T, int max_n, int 
                                int32_t* out_tokens, int32_t* out_len, int64_t* out_pos,
                                hipStream_t s);
 
+// the next block's context-copy proposal straight after a readout: head =
+// argmax[*kept - 1] is written to hist[pos + *kept] (and out_head), then the
+// suffix match runs over hist[0 .. pos + *kept]
+hipError_t launch_propose_next(int32_t* hist, int64_t pos, const int32_t* kept, const int32_t* argmax, int max_n,
+                               int min_n, int K, int32_t* out_tokens, int32_t* out_len, int64_t* out_pos,
+                               int32_t* out_head, hipStream_t s);
+
 // attention split: partitions of each query tile's key axis (cached keys up
 // to max L, then the span's own) so that small spans still fill the chip
 // (max_seq_rows: the most span rows any sequence of the call has)

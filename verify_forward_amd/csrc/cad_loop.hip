@@ -8,9 +8,11 @@
 // Every tick advances every block in flight by one depth in one call of
 // cad_loop_step (each block on its own depth's cache); the blocks that reach
 // the screening depth or the full depth are read out in the same call, and
-// the host reads the decisions back (one synchronisation per tick with a
-// readout, plus one per admitted block for its context-copy proposal, which
-// the suffix-match kernel makes on the device).
+// right after it the device makes the context-copy proposal for the block
+// that would follow each readout (the screened block's successor, and the
+// correction after a full-depth readout), so the host reads decisions and
+// proposals back with one synchronisation per tick with a readout.  (A head
+// that waits for room gets its proposal when it is admitted, with one more.)
 //
 // Rules (the plainest reading of the pages where they leave a step open):
 //   * the prompt is prefilled at every depth; its last full-depth prediction
@@ -47,7 +49,10 @@ struct Block {
   int32_t depth = 0;
   int32_t slot = -1;
   bool in_flight = false;
+  int32_t ready = -1;  // waiting head: proposal slot already computed on the device this tick (-1: none)
 };
+
+constexpr int kPropSlots = 2;  // proposals made after a tick: 0 after screening, 1 after full depth
 
 cad_status loop_fail(cad_status s, const std::string& msg) { return cad::set_error(s, msg.c_str()); }
 
@@ -65,9 +70,9 @@ struct cad_loop {
   int32_t* d_argmax = nullptr;
   int32_t* d_accepted = nullptr;
   int32_t* d_hist = nullptr;
-  int32_t* d_prop = nullptr;
-  int32_t* d_prop_len = nullptr;
-  int64_t* d_prop_pos = nullptr;
+  int32_t* d_prop = nullptr;      // [1 + kPropSlots][65]: tokens[64], then the length
+  int64_t* d_prop_pos = nullptr;  // [1 + kPropSlots]
+  int32_t* d_prop_head = nullptr; // [kPropSlots]
   int32_t* d_status = nullptr;
   int32_t* d_pf_sargmax = nullptr;
   int32_t* d_pf_argmax = nullptr;
@@ -78,7 +83,7 @@ struct cad_loop {
   int32_t* h_argmax = nullptr;
   int32_t* h_accepted = nullptr;
   int32_t* h_hist = nullptr;
-  int32_t* h_prop = nullptr;
+  int32_t* h_prop = nullptr;      // [1 + kPropSlots][65]
 };
 
 namespace {
@@ -138,34 +143,52 @@ struct Run {
 
   // the youngest entry, if it waits: admit it with a context-copy tail when
   // a row is free (proposal on the device, one synchronisation)
+  // upload the host history's changes to the device copy
+  cad_status sync_hist() {
+    const size_t n = hist.size() - dev_valid;
+    if (n > 0) {
+      std::memcpy(lp->h_hist, hist.data() + dev_valid, n * 4);
+      LOOP_HIP(hipMemcpyAsync(lp->d_hist + dev_valid, lp->h_hist, n * 4, hipMemcpyHostToDevice, s));
+      dev_valid = hist.size();
+    }
+    return CAD_OK;
+  }
+
   cad_status admit_waiting() {
     if (blocks.empty() || blocks.back().in_flight) return CAD_OK;
     Block& b = blocks.back();
     const int32_t room = lp->p.max_rows - rows_in_flight();
-    if (room < 1) return CAD_OK;
+    if (room < 1) {
+      b.ready = -1;  // a later admission proposes again
+      return CAD_OK;
+    }
     truncate_hist((size_t)b.pos);
     hist.push_back(b.toks[0]);
     int32_t n_tail = 0;
+    const int32_t* tail = nullptr;
     if (lp->p.max_copy > 0 && room > 1) {
-      const size_t n = hist.size() - dev_valid;
-      if (n > 0) {
-        std::memcpy(lp->h_hist, hist.data() + dev_valid, n * 4);
-        LOOP_HIP(hipMemcpyAsync(lp->d_hist + dev_valid, lp->h_hist, n * 4, hipMemcpyHostToDevice, s));
-        dev_valid = hist.size();
+      int slot = b.ready;
+      if (slot < 0) {
+        // no proposal made on the device after the last tick: make one now
+        slot = kPropSlots;
+        cad_status r = sync_hist();
+        if (r != CAD_OK) return r;
+        int32_t* dp = lp->d_prop + slot * 65;
+        LOOP_CALL(cad_propose_suffix_match(lp->d_hist, (int64_t)hist.size(), lp->p.max_ngram, lp->p.min_ngram,
+                                           lp->p.max_copy, dp, dp + 64, lp->d_prop_pos + slot, s));
+        LOOP_HIP(hipMemcpyAsync(lp->h_prop + slot * 65, dp, 65 * 4, hipMemcpyDeviceToHost, s));
+        LOOP_HIP(hipStreamSynchronize(s));
+        ++st.host_syncs;
       }
-      LOOP_CALL(cad_propose_suffix_match(lp->d_hist, (int64_t)hist.size(), lp->p.max_ngram, lp->p.min_ngram,
-                                         lp->p.max_copy, lp->d_prop, lp->d_prop_len, lp->d_prop_pos, s));
-      LOOP_HIP(hipMemcpyAsync(lp->h_prop, lp->d_prop, (size_t)lp->p.max_copy * 4, hipMemcpyDeviceToHost, s));
-      LOOP_HIP(hipMemcpyAsync(lp->h_prop + lp->p.max_copy, lp->d_prop_len, 4, hipMemcpyDeviceToHost, s));
-      LOOP_HIP(hipStreamSynchronize(s));
-      ++st.host_syncs;
-      n_tail = lp->h_prop[lp->p.max_copy];
+      tail = lp->h_prop + slot * 65;
+      n_tail = tail[64];
       if (n_tail > room - 1) n_tail = room - 1;
       if (n_tail < 0) n_tail = 0;
     }
+    b.ready = -1;
     b.toks.resize(1);
-    for (int32_t j = 0; j < n_tail; ++j) b.toks.push_back(lp->h_prop[j]);
-    for (int32_t j = 0; j < n_tail; ++j) hist.push_back(lp->h_prop[j]);
+    for (int32_t j = 0; j < n_tail; ++j) b.toks.push_back(tail[j]);
+    for (int32_t j = 0; j < n_tail; ++j) hist.push_back(tail[j]);
     // blocks in flight sit at distinct depths, so the loop_depth slots never run out
     if (free_slots.empty()) return loop_fail(CAD_E_ARG, "no free pipeline slot (more blocks in flight than depths)");
     b.slot = free_slots.back();
@@ -237,6 +260,12 @@ struct Run {
         live.push_back(i);
       }
       if (groups.empty()) return loop_fail(CAD_E_ARG, "pipeline empty before the decode finished");
+      const bool propose = any_read && lp->p.max_copy > 0;
+      if (propose) {
+        // the device history must hold every token in flight for the proposals below
+        cad_status r2 = sync_hist();
+        if (r2 != CAD_OK) return r2;
+      }
       LOOP_HIP(hipMemcpyAsync(lp->d_tokens, h_tok, (size_t)total * 4, hipMemcpyHostToDevice, s));
       LOOP_HIP(hipEventRecord(lp->tok_copied[st.ticks & 1], s));
       LOOP_CALL(cad_loop_step(lp->m, kv, (int32_t)groups.size(), groups.data(), lp->d_tokens, lp->state,
@@ -245,10 +274,39 @@ struct Run {
       ++st.ticks;
       st.rows_run += total;
       if (any_read) {
+        if (propose) {
+          // proposals for the successor of the screened block (slot 0) and for
+          // the token after the full-depth block (slot 1), screening first: the
+          // full-depth one may write a correction into the history
+          int32_t o = 0;
+          for (int pass = 0; pass < kPropSlots; ++pass) {
+            o = 0;
+            for (size_t k = 0; k < groups.size(); ++k) {
+              const int32_t after = groups[k].depth + 1;
+              if (groups[k].readout && ((pass == 0 && after == ds) || (pass == 1 && after == D))) {
+                int32_t* dp = lp->d_prop + pass * 65;
+                LOOP_HIP(cad::launch_propose_next(lp->d_hist, groups[k].pos, lp->d_accepted + k, lp->d_argmax + o,
+                                             lp->p.max_ngram, lp->p.min_ngram, lp->p.max_copy, dp, dp + 64,
+                                             lp->d_prop_pos + pass, lp->d_prop_head + pass, s));
+              }
+              o += groups[k].rows;
+            }
+          }
+          LOOP_HIP(hipMemcpyAsync(lp->h_prop, lp->d_prop, kPropSlots * 65 * 4, hipMemcpyDeviceToHost, s));
+        }
         LOOP_HIP(hipMemcpyAsync(lp->h_argmax, lp->d_argmax, (size_t)total * 4, hipMemcpyDeviceToHost, s));
         LOOP_HIP(hipMemcpyAsync(lp->h_accepted, lp->d_accepted, groups.size() * 4, hipMemcpyDeviceToHost, s));
         LOOP_HIP(hipStreamSynchronize(s));
         ++st.host_syncs;
+        if (propose) {
+          // the device wrote each proposal's head into its history copy; the
+          // host history takes those positions over when it admits or corrects
+          for (size_t k = 0; k < groups.size(); ++k)
+            if (groups[k].readout) {
+              const size_t at = (size_t)(groups[k].pos + lp->h_accepted[k]);
+              if (dev_valid > at) dev_valid = at;
+            }
+        }
       }
       // per block of this tick: its readout (row offset in the tick, accepted)
       std::vector<int32_t> row0(blocks.size(), -1), accd(blocks.size(), 0);
@@ -294,6 +352,7 @@ struct Run {
             Block c;
             c.pos = pos_next;
             c.toks.push_back(nxt);
+            c.ready = 1;  // proposed on the device after this tick
             blocks.push_back(c);
             row0.push_back(-1);
             accd.push_back(0);
@@ -310,6 +369,7 @@ struct Run {
             Block nb;
             nb.pos = b.pos + keep;
             nb.toks.push_back(a[keep - 1]);
+            nb.ready = 0;  // proposed on the device after this tick
             blocks.push_back(nb);
             row0.push_back(-1);
             accd.push_back(0);
@@ -365,9 +425,9 @@ cad_status cad_loop_create(cad_model* m, int64_t max_len, const cad_loop_params*
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = up256(off + bytes); return o; };
   const size_t o_state = take(srows * d * 4), o_tok = take(srows * 4), o_am = take(srows * 4),
-               o_acc = take(CAD_MAX_SEQS * 4), o_hist = take(max_len * 4), o_prop = take(64 * 4),
-               o_plen = take(4), o_ppos = take(8), o_st = take(4), o_pfs = take(T * 4), o_pfa = take(T * 4),
-               o_pfm = take(2 * 4);
+               o_acc = take(CAD_MAX_SEQS * 4), o_hist = take(max_len * 4), o_prop = take((1 + kPropSlots) * 65 * 4),
+               o_phead = take(kPropSlots * 4), o_ppos = take((1 + kPropSlots) * 8), o_st = take(4),
+               o_pfs = take(T * 4), o_pfa = take(T * 4), o_pfm = take(2 * 4);
   hipError_t e = hipMalloc(&lp->dev, off);
   if (e != hipSuccess) {
     delete lp;
@@ -380,7 +440,7 @@ cad_status cad_loop_create(cad_model* m, int64_t max_len, const cad_loop_params*
   lp->d_accepted = (int32_t*)(b + o_acc);
   lp->d_hist = (int32_t*)(b + o_hist);
   lp->d_prop = (int32_t*)(b + o_prop);
-  lp->d_prop_len = (int32_t*)(b + o_plen);
+  lp->d_prop_head = (int32_t*)(b + o_phead);
   lp->d_prop_pos = (int64_t*)(b + o_ppos);
   lp->d_status = (int32_t*)(b + o_st);
   lp->d_pf_sargmax = (int32_t*)(b + o_pfs);
@@ -389,7 +449,7 @@ cad_status cad_loop_create(cad_model* m, int64_t max_len, const cad_loop_params*
   size_t hoff = 0;
   auto htake = [&](size_t bytes) { size_t o = hoff; hoff = up256(hoff + bytes); return o; };
   const size_t h_tok0 = htake(srows * 4), h_tok1 = htake(srows * 4), h_am = htake(std::max<int64_t>(srows, 1) * 4), h_acc = htake(CAD_MAX_SEQS * 4),
-               h_hist = htake(max_len * 4), h_prop = htake(65 * 4);
+               h_hist = htake(max_len * 4), h_prop = htake((1 + kPropSlots) * 65 * 4);
   e = hipHostMalloc(&lp->host, hoff, hipHostMallocDefault);
   if (e != hipSuccess) {
     (void)hipFree(lp->dev);

@@ -538,10 +538,13 @@ hipError_t launch_decide(const uint32_t* cand, int n_cand, int rows, const RowMa
 // ---------------------------------------------------------------------------
 constexpr int SUFFIX_THREADS = 1024;
 
-__global__ void __launch_bounds__(SUFFIX_THREADS)
-k_suffix_match(const int32_t* __restrict__ x, int64_t T, int max_n, int min_n, int K,
-               int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_len,
-               int64_t* __restrict__ out_pos) {
+// The search itself, over x[0 .. T-1] (T may come from device memory): the
+// largest start p of each suffix length n (max_n down to min_n) with
+// x[p .. p+n-1] == x[T-n .. T-1] and p + n <= T - 1; the first n that
+// matches gives the proposal x[p+n .. min(p+n+K, T) - 1].
+__device__ void suffix_match_body(const int32_t* __restrict__ x, int64_t T, int max_n, int min_n, int K,
+                                  int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_len,
+                                  int64_t* __restrict__ out_pos) {
   __shared__ int32_t suf[64];
   __shared__ long long red[SUFFIX_THREADS / 64];
   __shared__ long long found;
@@ -583,11 +586,46 @@ k_suffix_match(const int32_t* __restrict__ x, int64_t T, int max_n, int min_n, i
   if (threadIdx.x == 0) { *out_len = len; *out_pos = start; }
 }
 
+__global__ void __launch_bounds__(SUFFIX_THREADS)
+k_suffix_match(const int32_t* __restrict__ x, int64_t T, int max_n, int min_n, int K,
+               int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_len,
+               int64_t* __restrict__ out_pos) {
+  suffix_match_body(x, T, max_n, min_n, K, out_tokens, out_len, out_pos);
+}
+
 hipError_t launch_suffix_match(const int32_t* tokens, int64_t T, int max_n, int min_n, int K,
                                int32_t* out_tokens, int32_t* out_len, int64_t* out_pos,
                                hipStream_t s) {
   hipLaunchKernelGGL(k_suffix_match, dim3(1), dim3(SUFFIX_THREADS), 0, s, tokens, T, max_n, min_n, K,
                      out_tokens, out_len, out_pos);
+  return hipGetLastError();
+}
+
+// The next block's proposal straight after a readout, with no host round
+// trip: the block at `pos` keeps keep = *kept rows, its prediction at the
+// last kept row is the next head, written to hist[pos + keep], and the
+// suffix match runs over hist[0 .. pos + keep].  out_head receives the head.
+__global__ void __launch_bounds__(SUFFIX_THREADS)
+k_propose_next(int32_t* __restrict__ hist, int64_t pos, const int32_t* __restrict__ kept,
+               const int32_t* __restrict__ argmax, int max_n, int min_n, int K, int32_t* __restrict__ out_tokens,
+               int32_t* __restrict__ out_len, int64_t* __restrict__ out_pos, int32_t* __restrict__ out_head) {
+  __shared__ int32_t head;
+  const int keep = *kept;
+  if (threadIdx.x == 0) {
+    head = argmax[keep - 1];
+    hist[pos + keep] = head;
+    *out_head = head;
+  }
+  // the barrier publishes the head (LDS) and its history store to the work-group
+  __syncthreads();
+  suffix_match_body(hist, pos + keep + 1, max_n, min_n, K, out_tokens, out_len, out_pos);
+}
+
+hipError_t launch_propose_next(int32_t* hist, int64_t pos, const int32_t* kept, const int32_t* argmax, int max_n,
+                               int min_n, int K, int32_t* out_tokens, int32_t* out_len, int64_t* out_pos,
+                               int32_t* out_head, hipStream_t s) {
+  hipLaunchKernelGGL(k_propose_next, dim3(1), dim3(SUFFIX_THREADS), 0, s, hist, pos, kept, argmax, max_n, min_n, K,
+                     out_tokens, out_len, out_pos, out_head);
   return hipGetLastError();
 }
 
