@@ -39,8 +39,9 @@ from .suffix import suffix_match
 from .looped import looped_splice
 from .batched import batched_splice
 from .copyloop import loop_step, copyloop_decode, greedy_decode
+from .cad_program import program_decode
 
 __all__ = ["Config", "KVCache", "rms_norm", "rope_rotate", "decode_step", "splice",
            "sequential", "prefill", "final_logits", "masked_argmax", "acceptance",
            "top2_margin", "suffix_match", "looped_splice", "batched_splice",
-           "loop_step", "copyloop_decode", "greedy_decode"]
+           "loop_step", "copyloop_decode", "greedy_decode", "program_decode"]
