@@ -312,6 +312,88 @@ void cad_loop_destroy(cad_loop* lp);
 cad_status cad_loop_decode(cad_loop* lp, const cad_kv* kv, const int32_t* prompt, int64_t L0, int32_t n_new,
                            int32_t* out, cad_loop_stats* stats, cad_stream stream);
 
+/* ---- Copy-as-Decode program decoding (Copy-as-Decode §2) ----
+ * cad_program_decode: the model writes a program over a document, one
+ * request, with the grammar automaton on the device (§2.1 grammar, §2.3
+ * masked steps and forced-template prefills, appendix "States.", "Forced
+ * prefills." and "Token-sequence end-of-gen detector."):
+ *   program := <program> op* </program>;  op := <copy lines="a-b"/> | <gen> text </gen>
+ * The prompt (host int32 [L0], ending with the ids of "<program>") is
+ * prefilled; then every decision is the masked argmax of the last fed row:
+ * at an op boundary {"<"} (first op) or {"<", "</"} ({"</"} once max_ops
+ * ops are done); after "<" {copy, gen}; inside a copy range the digits that
+ * keep the number reachable (no leading zero, the first number in [1, U],
+ * the second in [first, U]; U = the document's lines, or tokens when
+ * unit_tokens = 1, §5 "Token-level extension."), then "-" or the closing
+ * quote; inside a gen body every id (free generation) until the rolling
+ * window over the last three ids holds the ids of "</gen>", or max_gen ids.
+ * What follows a decision is fed in one forward: the chosen id alone; a
+ * forced template ("copy" kw '="' after copy, "gen" ">" after gen, "</"
+ * "program" ">" for the end, "</gen>" after a length-capped body); after the
+ * closing quote, the quote, "/>" and the document's units a..b (the copy
+ * splice, §2.4).  Inside a gen body with draft_k > 0, the pending id and up
+ * to draft_k ids continuing the most recent earlier match of the suffix of
+ * document + stream (lengths 4 down to 1) are verified in one forward (§5
+ * "Composition with speculative decoding."; lossless: the stream is the
+ * same as without drafts).  Decoding stops after the terminator, or at the
+ * first decision once max_stream program ids have been fed.
+ * The host synchronises when the next forward's length depends on a
+ * decision (a template, a copy, a verify) and otherwise launches up to
+ * `chain` single steps ahead; a chained step whose chain has ended (the
+ * decision before it asked for a longer feed) writes its K/V past the end of
+ * the stream, where the next forward overwrites it, and takes no decision.
+ * Results: stream_out (host int32 [stream_cap]) the program ids fed after
+ * the prompt; ops_out (host int32 [max_ops][5]) one record per op: kind (0
+ * copy, 1 gen), a, b (copy), body start in the stream, body length (gen; an
+ * unfinished body at a stop counts its ids so far); out (host int32
+ * [out_cap]) the resolved output (§2.2: copies expanded to the document,
+ * gen bodies as generated).  A result longer than its buffer is truncated
+ * and the call returns CAD_E_CAPACITY (stats are filled either way).
+ * doc: host int32 [doc_n], 1 <= doc_n <= max_doc; line_start: host int32
+ * [n_lines + 1], line_start[0] = 0, non-decreasing, line_start[n_lines] =
+ * doc_n (NULL allowed when unit_tokens = 1).  Needs loop_depth 1,
+ * max_tokens >= draft_k + 1 and a block table and max_len holding L0 +
+ * max_stream + 2 x max_doc + 2 x draft_k + chain + 16 positions.  The KV
+ * cache is overwritten from position 0.  The call synchronises its stream. */
+typedef struct cad_program cad_program;
+typedef struct {
+  int32_t lt, lt_slash, gt;        /* "<", "</", ">" */
+  int32_t copy, gen, program;      /* tag names */
+  int32_t kw;                      /* " lines" (or " tokens") */
+  int32_t eq_quote, quote, slash_gt, hyphen;  /* '="', '"', "/>", "-" */
+  int32_t digits[10];              /* "0" .. "9" */
+} cad_program_table;
+typedef struct {
+  int32_t max_doc;     /* most document tokens, >= 1 */
+  int32_t max_stream;  /* no decision once this many program ids are fed, >= 1 */
+  int32_t max_ops;     /* ops per program, >= 1 */
+  int32_t max_gen;     /* ids per gen body, >= 1 */
+  int32_t draft_k;     /* drafted ids per verify inside gen bodies, 0 (no drafts) .. 64 */
+  int32_t chain;       /* most single steps launched between host synchronisations, 1 .. 64 */
+} cad_program_params;
+typedef struct {
+  int64_t forwards;         /* forwards that fed program ids, plus one for the prompt */
+  int64_t idle_steps;       /* chained steps launched after their chain had ended */
+  int64_t host_syncs;       /* host synchronisations */
+  int32_t decisions;        /* decisions taken */
+  int32_t masked_steps;     /* of them under a mask (every decision outside gen bodies) */
+  int32_t forced_prefills;  /* template feeds */
+  int32_t copies, copied_tokens;
+  int32_t drafts, draft_tokens, draft_accepted;  /* verify forwards, drafted ids, accepted ids */
+  int32_t stream_n;         /* program ids fed */
+  int32_t n_ops;            /* op records (an unfinished gen op included) */
+  int32_t out_n;            /* resolved output length */
+  int32_t fsm_error;        /* 0; 1: a decision outside its mask (a mask that allowed nothing) */
+  int32_t dev_status;       /* CAD_DEV_* bits seen by the device */
+} cad_program_stats;
+cad_status cad_program_create(cad_model* m, int64_t max_len, const cad_program_table* t,
+                              const cad_program_params* p, cad_program** out);
+void cad_program_destroy(cad_program* pr);
+cad_status cad_program_decode(cad_program* pr, const cad_kv* kv, const int32_t* prompt, int64_t L0,
+                              const int32_t* doc, int32_t doc_n, const int32_t* line_start, int32_t n_lines,
+                              int32_t unit_tokens, int32_t* stream_out, int32_t stream_cap, int32_t* ops_out,
+                              int32_t* out, int32_t out_cap, cad_program_stats* stats, cad_stream stream);
+
 /* ---- instrumentation (measurement only, not part of the method) ----
  * Kernel families, in bit order: 0 "embed", 1 "rmsnorm", 2 "gemm_qkv",
  * 3 "rope_append", 4 "attention" (the partial-attention kernel), 5

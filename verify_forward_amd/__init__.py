@@ -27,7 +27,8 @@ CAD_MAX_SEQS = 64
 EXPORTS = ("cad_model_create", "cad_model_destroy", "cad_last_error", "cad_splice_forward",
            "cad_decode_step", "cad_decode_step_noalloc", "cad_propose_suffix_match",
            "cad_splice_forward_batched", "cad_splice_forward_looped", "cad_loop_step", "cad_loop_create",
-           "cad_loop_destroy", "cad_loop_decode", "cad_profile_enable", "cad_profile_read")
+           "cad_loop_destroy", "cad_loop_decode", "cad_program_create", "cad_program_destroy",
+           "cad_program_decode", "cad_profile_enable", "cad_profile_read")
 CAD_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 PROFILE_FAMILIES = ("embed", "rmsnorm", "gemm_qkv", "rope_append", "attention", "attn_merge", "gemm_o",
@@ -81,6 +82,24 @@ class cad_loop_stats(ctypes.Structure):
                [("dev_status", ctypes.c_int32)]
 
 
+class cad_program_table(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("lt", "lt_slash", "gt", "copy", "gen", "program", "kw", "eq_quote",
+                                              "quote", "slash_gt", "hyphen")] + [("digits", ctypes.c_int32 * 10)]
+
+
+class cad_program_params(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("max_doc", "max_stream", "max_ops", "max_gen", "draft_k", "chain")]
+
+
+class cad_program_stats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("forwards", "idle_steps", "host_syncs")] + \
+               [(n, ctypes.c_int32) for n in ("decisions", "masked_steps", "forced_prefills", "copies", "copied_tokens",
+                                              "drafts", "draft_tokens", "draft_accepted", "stream_n", "n_ops",
+                                              "out_n", "fsm_error", "dev_status")]
+
+
+PROGRAM_OP_INTS = 5  # op record: kind (0 copy, 1 gen), a, b, body start, body length
+
 _lib = None
 
 
@@ -112,12 +131,18 @@ def lib() -> ctypes.CDLL:
         L.cad_loop_destroy.restype = None
         L.cad_loop_decode.argtypes = [_VP, ctypes.POINTER(cad_kv), _VP, i64, i32, _VP, ctypes.POINTER(cad_loop_stats),
                                       _VP]
+        L.cad_program_create.argtypes = [_VP, i64, ctypes.POINTER(cad_program_table),
+                                         ctypes.POINTER(cad_program_params), ctypes.POINTER(_VP)]
+        L.cad_program_destroy.argtypes = [_VP]
+        L.cad_program_destroy.restype = None
+        L.cad_program_decode.argtypes = [_VP, ctypes.POINTER(cad_kv), _VP, i64, _VP, i32, _VP, i32, i32, _VP, i32,
+                                         _VP, _VP, i32, ctypes.POINTER(cad_program_stats), _VP]
         L.cad_profile_enable.argtypes = [_VP, i32]
         L.cad_profile_read.argtypes = [_VP, ctypes.c_char_p, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)]
         for name in ("cad_model_create", "cad_splice_forward", "cad_decode_step", "cad_decode_step_noalloc",
                      "cad_propose_suffix_match", "cad_splice_forward_batched", "cad_splice_forward_looped",
-                     "cad_loop_step", "cad_loop_create", "cad_loop_decode", "cad_profile_enable",
-                     "cad_profile_read"):
+                     "cad_loop_step", "cad_loop_create", "cad_loop_decode", "cad_program_create",
+                     "cad_program_decode", "cad_profile_enable", "cad_profile_read"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -333,6 +358,78 @@ def cad_loop_decode(loop: Loop, kv: KVCache, prompt: Sequence[int], n_new: int, 
     _check(lib().cad_loop_decode(loop.handle, ctypes.byref(s), ctypes.cast(pr, _VP), len(prompt), int(n_new),
                                  ctypes.cast(out, _VP), ctypes.byref(st), _stream(stream)))
     return list(out), {n: int(getattr(st, n)) for n, _ in cad_loop_stats._fields_}
+
+
+class Program:
+    """Owns a ``cad_program*`` (the decoder's device buffers) and keeps its
+    model alive."""
+
+    def __init__(self, handle, model: Model, params: cad_program_params):
+        self.handle, self.model, self.params = handle, model, params
+
+    def __del__(self):
+        try:
+            if self.handle:
+                cad_program_destroy(self)
+        except Exception:
+            pass
+
+
+def cad_program_create(model: Model, max_len: int, table, max_doc: int, max_stream: int, max_ops: int,
+                       max_gen: int, draft_k: int = 0, chain: int = 4) -> Program:
+    """``table``: an object with the structural ids as attributes (lt,
+    lt_slash, gt, copy, gen, program, kw, eq_quote, quote, slash_gt, hyphen,
+    digits)."""
+    t = cad_program_table(*[int(getattr(table, n)) for n, _ in cad_program_table._fields_[:-1]],
+                          (ctypes.c_int32 * 10)(*[int(d) for d in table.digits]))
+    p = cad_program_params(int(max_doc), int(max_stream), int(max_ops), int(max_gen), int(draft_k), int(chain))
+    h = _VP()
+    _check(lib().cad_program_create(model.handle, int(max_len), ctypes.byref(t), ctypes.byref(p), ctypes.byref(h)))
+    return Program(h, model, p)
+
+
+def cad_program_destroy(prog: Program):
+    if prog.handle:
+        lib().cad_program_destroy(prog.handle)
+        prog.handle = None
+
+
+def cad_program_decode(prog: Program, kv: KVCache, prompt: Sequence[int], doc_lines: Sequence[Sequence[int]],
+                       unit: str = "lines", stream=None):
+    """Decode a program after ``prompt`` over the document ``doc_lines``
+    (its lines, each a list of ids).  Returns ``(stream, ops, output,
+    stats)``: the program ids fed after the prompt, the ops (``{"op":
+    "copy", "a", "b"}`` or ``{"op": "gen", "body"}``, the body read from the
+    stream), the resolved output and the counters as a dict."""
+    if unit not in ("lines", "tokens"):
+        raise ValueError("unit must be 'lines' or 'tokens'")
+    flat = [int(x) for line in doc_lines for x in line]
+    starts = [0]
+    for line in doc_lines:
+        starts.append(starts[-1] + len(line))
+    p = prog.params
+    pr = (ctypes.c_int32 * len(prompt))(*[int(t) for t in prompt])
+    doc = (ctypes.c_int32 * len(flat))(*flat)
+    ls = (ctypes.c_int32 * len(starts))(*starts)
+    stream_cap = int(p.max_stream) + len(flat) + 2 * int(p.draft_k) + 16
+    out_cap = int(p.max_ops) * len(flat) + stream_cap
+    s_out = (ctypes.c_int32 * stream_cap)()
+    o_out = (ctypes.c_int32 * (int(p.max_ops) * PROGRAM_OP_INTS))()
+    out = (ctypes.c_int32 * out_cap)()
+    st = cad_program_stats()
+    s = kv.struct()
+    _check(lib().cad_program_decode(prog.handle, ctypes.byref(s), ctypes.cast(pr, _VP), len(prompt),
+                                    ctypes.cast(doc, _VP), len(flat), ctypes.cast(ls, _VP), len(doc_lines),
+                                    int(unit == "tokens"), ctypes.cast(s_out, _VP), stream_cap,
+                                    ctypes.cast(o_out, _VP), ctypes.cast(out, _VP), out_cap, ctypes.byref(st),
+                                    _stream(stream)))
+    stats = {n: int(getattr(st, n)) for n, _ in cad_program_stats._fields_}
+    toks = list(s_out[:stats["stream_n"]])
+    ops = []
+    for i in range(stats["n_ops"]):
+        kind, a, b, start, n = o_out[i * PROGRAM_OP_INTS:(i + 1) * PROGRAM_OP_INTS]
+        ops.append({"op": "copy", "a": a, "b": b} if kind == 0 else {"op": "gen", "body": toks[start:start + n]})
+    return toks, ops, list(out[:stats["out_n"]]), stats
 
 
 def cad_profile_enable(model: Model, families=CAD_PROFILE_ALL):

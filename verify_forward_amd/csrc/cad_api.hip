@@ -461,6 +461,29 @@ cad_status set_error(cad_status s, const char* msg) {
   g_err = msg;
   return s;
 }
+
+cad_status splice_rows(cad_model* m, const cad_kv* kv, int64_t L, const int32_t* span, int N, const uint32_t* mask,
+                       int mode, const int32_t* limit, int32_t* argmax, int32_t* accepted, float* logits,
+                       int32_t* dev_status, hipStream_t s) {
+  cad_status st = check_common(m, kv, span, argmax, accepted, logits, mode);
+  if (st != CAD_OK) return st;
+  if (m->cfg.loop_depth > 1) return fail(CAD_E_ARG, "looped model: use cad_splice_forward_looped");
+  st = check_seq(kv, L, N, m->cfg.max_tokens);
+  if (st != CAD_OK) return st;
+  RowMap rm{};
+  rm.n_seq = 1;
+  rm.total = N;
+  rm.start[0] = 0;
+  rm.start[1] = N;
+  rm.L[0] = L;
+  rowmap_pad(rm);
+  const cad_config& c = m->cfg;
+  m->x_parts = 0;
+  LAUNCH(PF_EMBED, launch_embed(c.dtype, m->tok_embed, c.vocab, c.d_model, span, N, m->w->x, dev_status, s));
+  st = run_blocks(m, kv, rm, 0, c.n_layers, limit, dev_status, s);
+  if (st != CAD_OK) return st;
+  return readout(m, rm, logits, mask, span, mode, limit, argmax, accepted, dev_status, s);
+}
 }  // namespace cad
 
 const cad_config* cad_model_config(const cad_model* m) { return &m->cfg; }
@@ -546,25 +569,8 @@ cad_status cad_splice_forward(cad_model* m, const cad_kv* kv, int64_t L, const i
                               int32_t N, const uint32_t* mask, cad_mode mode, int32_t* argmax,
                               int32_t* accepted, float* logits, int32_t* dev_status,
                               cad_stream stream) {
-  cad_status st = check_common(m, kv, span, argmax, accepted, logits, mode);
-  if (st != CAD_OK) return st;
-  if (m->cfg.loop_depth > 1) return fail(CAD_E_ARG, "looped model: use cad_splice_forward_looped");
-  st = check_seq(kv, L, N, m->cfg.max_tokens);
-  if (st != CAD_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
-  RowMap rm{};
-  rm.n_seq = 1;
-  rm.total = N;
-  rm.start[0] = 0;
-  rm.start[1] = N;
-  rm.L[0] = L;
-  rowmap_pad(rm);
-  const cad_config& c = m->cfg;
-  m->x_parts = 0;
-  LAUNCH(PF_EMBED, launch_embed(c.dtype, m->tok_embed, c.vocab, c.d_model, span, N, m->w->x, dev_status, s));
-  st = run_blocks(m, kv, rm, 0, c.n_layers, nullptr, dev_status, s);
-  if (st != CAD_OK) return st;
-  return readout(m, rm, logits, mask, span, mode, nullptr, argmax, accepted, dev_status, s);
+  return cad::splice_rows(m, kv, L, span, N, mask, mode, nullptr, argmax, accepted, logits, dev_status,
+                          (hipStream_t)stream);
 }
 
 cad_status cad_decode_step(cad_model* m, const cad_kv* kv, int64_t L, const int32_t* token,

@@ -253,6 +253,69 @@ hipError_t launch_propose_next(int32_t* hist, int64_t pos, const int32_t* kept, 
                                int min_n, int K, int32_t* out_tokens, int32_t* out_len, int64_t* out_pos,
                                int32_t* out_head, hipStream_t s);
 
+// ---- Copy-as-Decode program automaton (device-resident state) ----
+enum FsmStateId { FSM_AWAIT_OP = 0, FSM_AFTER_LT = 1, FSM_NUM_A = 2, FSM_NUM_B = 3, FSM_GEN_BODY = 4, FSM_DONE = 5 };
+// what the next forward is: none yet; one chained single step (the feed is
+// one token); a splice of feed_n tokens whose last row takes a decision; the
+// terminator's splice (no decision follows); nothing more (stream limit,
+// error)
+enum FsmAction { FSM_ACT_NONE = 0, FSM_ACT_STEP = 1, FSM_ACT_FEED = 2, FSM_ACT_LAST = 3, FSM_ACT_STOP = 4 };
+// token ids of the program's structural literals (kw: " lines" or " tokens")
+struct FsmTable {
+  int32_t lt, lt_slash, gt, copy, gen, program, kw, eq_quote, quote, slash_gt, hyphen;
+  int32_t digits[10];
+};
+struct FsmLimits {
+  int32_t units;        // copy ranges lie in [1, units] (lines or tokens of the document)
+  int32_t unit_tokens;  // 1: a range counts document tokens, 0: lines (through the line table)
+  int32_t max_ops, max_gen, max_stream;
+  int32_t vocab_words;  // ceil(vocab / 32)
+  int32_t doc_n;        // document tokens at the front of the history
+  int32_t hist_cap;     // history capacity (document + stream + one feed + a draft)
+  int32_t draft_k;      // draft length inside gen bodies (0: none)
+};
+// one int32 per field so the host reads it back as a plain array
+struct FsmState {
+  int32_t state, n_ops, v, nd, a, gen_len, win[3];
+  int32_t action, feed_n, chain_ok, stream_n, error;
+  int32_t decisions, chained, masked, forced, copies, copied, drafts, draft_tokens, draft_accepted, out_n;
+};
+// op records [max_ops][5]: kind (0 copy, 1 gen), a, b (copy range), body
+// start in the stream and body length (gen)
+constexpr int FSM_OP_INTS = 5;
+
+hipError_t launch_fsm_init(FsmState* st, hipStream_t s);
+// the current decision's vocabulary mask, replicated to `rows` rows
+hipError_t launch_fsm_mask(const FsmState* st, const FsmTable& t, const FsmLimits& lim, uint32_t* mask, int rows,
+                           hipStream_t s);
+// take the decision argmax[decide_row] (force = 1: after a host-launched
+// splice; 0: a chained step, which acts only while chain_ok is set) and build
+// the next feed, appended to the stream (hist[doc_n + stream_n ..])
+hipError_t launch_fsm_advance(FsmState* st, const FsmTable& t, const FsmLimits& lim, const int32_t* argmax,
+                              int decide_row, int force, const int32_t* line_start, int32_t* hist, int32_t* feed,
+                              int32_t* ops, hipStream_t s);
+// inside a gen body with a pending single-token feed: append up to draft_k
+// drafted tokens (suffix match over the history) to the feed, set feed_n to
+// the rows that count and write the verify forward's draft_k + 1 mask rows
+hipError_t launch_fsm_draft(FsmState* st, const FsmTable& t, const FsmLimits& lim, int32_t* hist, int32_t* feed,
+                            uint32_t* mask, int32_t* tmp_len, int64_t* tmp_pos, hipStream_t s);
+// after the verify forward: pass the accepted drafts through the automaton,
+// then take the decision that follows them
+hipError_t launch_fsm_verified(FsmState* st, const FsmTable& t, const FsmLimits& lim, const int32_t* argmax,
+                               const int32_t* accepted, const int32_t* line_start, int32_t* hist, int32_t* feed,
+                               int32_t* ops, hipStream_t s);
+// the program's output: copies expanded from the document, gen bodies from
+// the stream, into out[0 .. out_cap) (out_n = the full length)
+hipError_t launch_fsm_resolve(FsmState* st, const FsmLimits& lim, const int32_t* line_start, const int32_t* hist,
+                              const int32_t* ops, int32_t* out, int out_cap, hipStream_t s);
+
+// cad_splice_forward (models with loop_depth 1, its checks included) with
+// an optional device row limit: rows at or beyond *limit write no K/V and
+// rows at or beyond max(1, *limit) are not decided
+cad_status splice_rows(cad_model* m, const cad_kv* kv, int64_t L, const int32_t* span, int N, const uint32_t* mask,
+                       int mode, const int32_t* limit, int32_t* argmax, int32_t* accepted, float* logits,
+                       int32_t* dev_status, hipStream_t s);
+
 // attention split: partitions of each query tile's key axis (cached keys up
 // to max L, then the span's own) so that small spans still fill the chip
 // (max_seq_rows: the most span rows any sequence of the call has)
