@@ -392,6 +392,128 @@ def copyloop_bench(n_new=64, L0=4096, K=8, ds=2):
     return out
 
 
+class ProgramTable:
+    """Structural-literal ids of the program grammar: the pages' Qwen2.5 ids
+    for "<", "</", ">", "copy", "gen", "program", " lines", '="' and "/>";
+    single characters ('"', "-", digits) at their byte-level ids."""
+    lt, lt_slash, gt, copy, gen, program, kw, eq_quote, slash_gt = 27, 522, 29, 8560, 4370, 14906, 5128, 428, 2577
+    quote, hyphen, digits = 1, 12, tuple(range(15, 25))
+
+
+class ProgramTableSwapped(ProgramTable):
+    """The same table with the ids of "<" and "</" exchanged: the random-init
+    7B model's argmax prefers the id that ends the program at every op
+    boundary with the pages' ids, and the other one with these, so its
+    programs run to max_ops (a stand-in for long multi-op programs)."""
+    lt, lt_slash = 522, 27
+
+
+def host_round_trip_ms(reps=50):
+    """One host round trip as the program decoder makes it: a small
+    device-to-host copy of the automaton's state and a stream
+    synchronisation (median over reps)."""
+    import numpy as np
+    import torch
+    x = torch.zeros(32, dtype=torch.int32, device="cuda")
+    h = torch.empty(32, dtype=torch.int32, pin_memory=True)
+    ts = []
+    for _ in range(reps + 5):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        h.copy_(x, non_blocking=True)
+        torch.cuda.current_stream().synchronize()
+        ts.append((time.perf_counter() - t0) * 1e3)
+    return round(float(np.median(ts[5:])), 4)
+
+
+def program_bench(wl, s_curve, L0=4096, max_ops=16, max_gen=32, max_stream=1024, doc_seeds=(0, 1)):
+    """Copy-as-Decode program decoding (cad_program_decode: the grammar
+    automaton, masks, feeds and stream on the device) at the 7B shape: each
+    document is a 4096-token repeated-line prompt (80-token lines, one per
+    seed), the prompt is the document followed by "<program>", and the
+    random-init model writes whatever program its argmax gives (ops, ranges
+    and gen bodies are its own decisions; bodies end by the 32-id cap).
+    Reported per document and configuration (no drafts with chains of 1 and
+    4; drafts of 8): the program's ops, the decode time after the prompt's
+    prefill, output tokens/s, the time the same output would take as
+    one-token decode steps (tau measured at the same cache length), the
+    realized speedup, forwards, host round trips and idle chained steps.
+    The span policy (Table 17) is read off the s(N) curve at L = 1024 with a
+    fixed cost per copy op c = one forced prefill (T_PP(4)) plus the
+    decoder's host round trips per op at the measured round-trip time."""
+    import torch
+    import synth
+    from verify_forward_amd import policy
+    cad = wl.cad
+    shape = wl.shape
+    cap = L0 + 3 + max_stream + 2 * L0 + 2 * 8 + 64 + 64
+    nb = (cap + 15) // 16
+    kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device="cuda")
+    am = torch.empty(512, dtype=torch.int32, device="cuda")
+    acc = torch.empty(1, dtype=torch.int32, device="cuda")
+    one = torch.empty(1, dtype=torch.int32, device="cuda")
+    rt = host_round_trip_ms()
+    out = {"workload": f"program decoding at the 7B shape over {len(doc_seeds)} {L0}-token repeated-line documents "
+                       f"(lines of 80 ids), max_ops {max_ops}, max_gen {max_gen}, random-init weights",
+           "host_round_trip_ms": rt, "documents": []}
+    configs = (("steps_chain1", 0, 1), ("steps_chain4", 0, 4), ("drafts8_chain4", 8, 4))
+    totals = {name: [0, 0.0, 0.0, 0, 0] for name, _, _ in configs}   # out tokens, decode ms, as-steps ms, syncs, ops
+    for tname, t, seed in [(tn, tb, sd) for tn, tb in (("pages_ids", ProgramTable), ("lt_ids_swapped",
+                                                                                   ProgramTableSwapped))
+                           for sd in doc_seeds]:
+        progs = {name: cad.cad_program_create(wl.model, nb * 16, t, max_doc=L0, max_stream=max_stream,
+                                              max_ops=max_ops, max_gen=max_gen, draft_k=k, chain=c)
+                 for name, k, c in configs}
+        toks = [int(x) for x in synth.make_line_prompt(L0, shape.vocab, seed=seed).tokens]
+        doc = [toks[i:i + 80] for i in range(0, len(toks), 80)]
+        prompt = toks + [t.lt, t.program, t.gt]
+        pr = torch.tensor(prompt, dtype=torch.int32, device="cuda")
+
+        def prefill():
+            for off in range(0, len(prompt), 512):
+                cad.cad_splice_forward(wl.model, kv, off, pr[off:off + 512], None, cad.CAD_COMMIT, am, acc)
+        t_prefill = pct(call_times_ms(prefill, 3, warmup=1))["median_ms"]
+        tau = pct(call_times_ms(lambda: cad.cad_decode_step(wl.model, kv, len(prompt), pr[:1], None, one),
+                                10))["median_ms"]
+        rec = {"table": tname, "seed": seed, "prefill_ms": t_prefill, "tau_ms": tau}
+        for name, _, _ in configs:
+            prog = progs[name]
+            cad.cad_program_decode(prog, kv, prompt, doc)        # warm up
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            stream, ops, output, st = cad.cad_program_decode(prog, kv, prompt, doc)
+            torch.cuda.synchronize()
+            dec = (time.perf_counter() - t0) * 1e3 - t_prefill
+            rec[name] = {"decode_ms": round(dec, 2), "out_tokens": st["out_n"], "program_ids": st["stream_n"],
+                         "out_tok_s": round(st["out_n"] / (dec * 1e-3), 1),
+                         "as_decode_steps_ms": round(st["out_n"] * tau, 2),
+                         "realized_speedup": round(st["out_n"] * tau / dec, 3),
+                         "ops": " ".join(f"c{o['b'] - o['a'] + 1}" if o["op"] == "copy" else f"g{len(o['body'])}"
+                                         for o in ops),
+                         "stats": st}
+            tt = totals[name]
+            tt[0] += st["out_n"]; tt[1] += dec; tt[2] += st["out_n"] * tau; tt[3] += st["host_syncs"]
+            tt[4] += max(st["n_ops"], 1)
+            log(f"[bench] program {tname} seed {seed} {name}: {rec[name]['ops']}: {rec[name]['out_tok_s']} out "
+                f"tok/s, speedup {rec[name]['realized_speedup']}")
+        out["documents"].append(rec)
+        for name, _, _ in configs:
+            cad.cad_program_destroy(progs[name])
+    for name, _, _ in configs:
+        n_out, dec, steps, syncs, n_ops = totals[name]
+        out[name] = {"out_tok_s": round(n_out / (dec * 1e-3), 1), "realized_speedup": round(steps / dec, 3),
+                     "host_syncs_per_op": round(syncs / n_ops, 2)}
+    curve = {r["N"]: r["s"] for r in s_curve}
+    t_forced = next(r["splice_ms"] for r in s_curve if r["N"] == 4)
+    tau_1024 = next(r["decode_steps_ms"] for r in s_curve if r["N"] == 1)
+    c_ms = t_forced + out["steps_chain4"]["host_syncs_per_op"] * rt
+    out["span_policy"] = {**policy.policy_report(curve, c_ms=c_ms, tau_ms=tau_1024), "c_ms": round(c_ms, 4),
+                          "tau_ms": tau_1024, "curve": "s(N) at L = 1024, grid N >= 2"}
+    del kv
+    torch.cuda.empty_cache()
+    return out
+
+
 def s_of_n(wl, Ns=(1, 2, 4, 8, 16, 32, 64, 128, 256, 512), L=1024):
     """The pages' s(N) = T(N one-token decode steps) / T(one splice of N) at the
     7B shape and L = 1024 (Copy-as-Decode §3 "Kernel microbenchmark", Table 1's
@@ -577,7 +699,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the serve, looped, s(N) and copy-bandwidth reports")
-    ap.add_argument("--only", choices=["serve", "looped", "copyloop"],
+    ap.add_argument("--only", choices=["serve", "looped", "copyloop", "program"],
                     help="run only the batched serve or the looped-block report (one JSON line; for kernel profiles)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain device copy of 1 GiB first (a known-size reference for HBM counters)")
@@ -609,6 +731,10 @@ def main():
     wl = Workload(shape, L, max_tokens=max(N, 512))
     if args.only == "serve":
         print(json.dumps({"serve": serve_bench(wl)}), flush=True)
+        return
+    if args.only == "program":
+        curve = s_of_n(wl, Ns=(1, 2, 4, 8, 16, 32, 64))
+        print(json.dumps({"program": program_bench(wl, curve)}), flush=True)
         return
     io = wl.inputs(N)
 
@@ -706,6 +832,7 @@ def main():
 
     if not args.no_extras:
         out["s_of_N_L1024"] = s_of_n(wl)
+        out["program_decoding"] = program_bench(wl, out["s_of_N_L1024"])
         out["serve"] = serve_bench(wl)
         log(f"[bench] serve: {out['serve']['value']} tok/s")
         out["achievable_copy_GBs"] = copy_bandwidth()
