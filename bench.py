@@ -662,30 +662,44 @@ def cpu_baseline(shape, L, N):
 
 # ----------------------------------------------------------------------------
 
-def source_digest():
-    """sha256 over the HIP sources: stored counter readings apply only to the kernels they were taken on."""
+# the source file that holds each kernel family (with the header every kernel
+# includes): a stored counter reading applies while these files are unchanged
+FAMILY_SOURCE = {"attention": "k_attn.hip", "attn_merge": "k_attn.hip", "gemm_qkv": "k_gemm.hip",
+                 "gemm_o": "k_gemm.hip", "gemm_gate_up": "k_gemm.hip", "gemm_down": "k_gemm.hip",
+                 "gemm_lm_head": "k_gemm.hip"}
+
+
+def source_digest(fam=None):
+    """sha256 over the HIP sources a kernel family is built from (its file
+    and cad_internal.h; the small kernels' file for the other families), or
+    over every HIP source when ``fam`` is None."""
     import glob
     import hashlib
     h = hashlib.sha256()
     here = os.path.dirname(os.path.abspath(__file__))
-    for p in sorted(glob.glob(os.path.join(here, "verify_forward_amd", "csrc", "*"))):
+    csrc = os.path.join(here, "verify_forward_amd", "csrc")
+    if fam is None:
+        files = sorted(glob.glob(os.path.join(csrc, "*")))
+    else:
+        files = [os.path.join(csrc, FAMILY_SOURCE.get(fam, "k_small.hip")), os.path.join(csrc, "cad_internal.h")]
+    for p in files:
         h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
 
 def stored_traffic(fam, N, L):
     """HBM bytes per launch of ``fam`` from the committed rocprofv3 counter
-    summary of this workload, or None when there is none or the kernels have
-    changed since it was taken."""
+    summary of this workload, or None when there is none or the kernel's
+    sources have changed since it was taken."""
     here = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(here, "profiles", f"traffic_7b_L{L}_N{N}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_digest") != source_digest():
-        return None
     k = rec.get("kernels", {}).get(fam)
-    return None if k is None else k.get("hbm_bytes_per_launch")
+    if k is None or k.get("source_digest") != source_digest(fam):
+        return None
+    return k.get("hbm_bytes_per_launch")
 
 
 def main():
