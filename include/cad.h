@@ -248,15 +248,18 @@ cad_status cad_splice_forward_looped(cad_model* m, const cad_kv* kv, int64_t L,
  * rule applied to each group's tokens) are written for every row and group
  * (the caller uses those of its readout groups), and the fp32 logits of
  * every row to `logits` (dev float [total rows][V]) if it is not NULL;
- * otherwise none of them is touched.  All groups read block-table row 0 (one
- * request).
+ * otherwise none of them is touched.  Each group reads and writes its
+ * positions through block-table row `table_row` (one request: row 0; two
+ * lines of blocks over the same positions, as branching makes, map their
+ * own positions to different blocks).
  * 1 <= n_groups <= CAD_MAX_SEQS; total rows <= max_tokens. */
 typedef struct {
-  int64_t pos;      /* absolute position of the group's first row */
-  int32_t rows;     /* >= 1 consecutive positions */
-  int32_t depth;    /* applications done before this tick, 0 .. loop_depth - 1 */
-  int32_t state;    /* first row of the group in `state` */
-  int32_t readout;  /* 1: masked argmax + acceptance after the tick; 0: none */
+  int64_t pos;        /* absolute position of the group's first row */
+  int32_t rows;       /* >= 1 consecutive positions */
+  int32_t depth;      /* applications done before this tick, 0 .. loop_depth - 1 */
+  int32_t state;      /* first row of the group in `state` */
+  int32_t readout;    /* 1: masked argmax + acceptance after the tick; 0: none */
+  int32_t table_row;  /* block-table row its positions map through (>= 0; the caller's table holds it) */
 } cad_loop_group;
 cad_status cad_loop_step(cad_model* m, const cad_kv* kv, int32_t n_groups, const cad_loop_group* groups,
                          const int32_t* tokens, float* state, int32_t state_rows, const uint32_t* mask,
@@ -280,7 +283,19 @@ cad_status cad_loop_step(cad_model* m, const cad_kv* kv, int32_t n_groups, const
  * the same way).  At most max_rows rows are in flight: a block admitted with
  * r free rows keeps at most r - 1 copied tokens, a head with no free row
  * waits.  The committed tokens (out, host int32 [n_new]) are greedy
- * full-depth decoding's.  The host reads decisions back after every tick
+ * full-depth decoding's.  With branch_depth = d2 > 0 (CopyLoop §A.2) a
+ * block is also read out at depth d2: if the prediction at its last
+ * surviving row differs there from the depth-ds one that headed its child,
+ * a second child headed by the d2 prediction is admitted (at most one such
+ * fork is live; it needs a free row and the first child in flight); the
+ * two children's lines keep their own KV states -- the second line maps its
+ * positions through block-table row 1, whose first spare entries (at least
+ * ceil((loop_depth x (max_copy + 1) + 16) / 16) + 1 blocks not used by row
+ * 0) the caller provides, the slots of older positions in the block where
+ * the fork starts being copied there as they are written -- until the
+ * parent's full-depth readout keeps the line whose head is the verified
+ * token (the second line's K/V are then copied into row 0's blocks) or
+ * neither (a correction block follows).  The host reads decisions back after every tick
  * that reads a block out (and after each proposal): this call synchronises
  * its stream.  cad_loop_create allocates the pipeline's device buffers (the
  * residual streams of loop_depth x (max_copy + 1) rows, a device history of
@@ -294,6 +309,7 @@ typedef struct {
   int32_t max_copy;      /* K, 0 .. 64 */
   int32_t max_ngram, min_ngram;  /* suffix lengths, 1 <= min <= max <= 64 */
   int32_t max_rows;      /* admission limit: rows in flight, >= 1, <= max_tokens */
+  int32_t branch_depth;  /* d2 of second-readout branching, ds < d2 < loop_depth; 0: none */
 } cad_loop_params;
 typedef struct {
   int64_t ticks;         /* cad_loop_step calls */
@@ -305,6 +321,10 @@ typedef struct {
   int64_t discarded;     /* rows of younger blocks dropped with a refusal */
   int64_t committed;     /* tokens committed (may pass n_new by a block) */
   int64_t host_syncs;    /* host synchronisations */
+  int64_t forks;         /* second children admitted (branching) */
+  int64_t forks_kept;    /* resolutions that kept the second child's line */
+  int64_t forks_lost;    /* resolutions that kept the first child's line */
+  int64_t fork_rows_dropped;  /* rows in flight of the line removed there (also in discarded) */
   int32_t dev_status;    /* CAD_DEV_* bits seen by the device */
 } cad_loop_stats;
 cad_status cad_loop_create(cad_model* m, int64_t max_len, const cad_loop_params* p, cad_loop** out);

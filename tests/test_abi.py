@@ -97,3 +97,35 @@ def test_calls_reject_null_model_and_bad_sizes():
     assert L.cad_propose_suffix_match(p, -1, 4, 1, 4, p, p, p, None) == cad.CAD_E_ARG
     assert L.cad_propose_suffix_match(None, 4, 4, 1, 4, p, p, p, None) == cad.CAD_E_ARG
     assert L.cad_propose_suffix_match(p, 4, 4, 1, 4, None, p, p, None) == cad.CAD_E_ARG
+
+
+STRUCTS = ("cad_config", "cad_weights", "cad_kv", "cad_loop_group", "cad_loop_params", "cad_loop_stats",
+           "cad_program_table", "cad_program_params", "cad_program_stats")
+
+
+def test_binding_structs_match_the_header(tmp_path):
+    """The binding's ctypes structures have the header's size and field
+    offsets (a C program built with the host compiler prints them)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no host C compiler")
+    lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "cad.h"', "int main(void) {"]
+    for name in STRUCTS:
+        lines.append(f'  printf("{name} size %zu\\n", sizeof({name}));')
+        for f, _ in getattr(cad, name)._fields_:
+            lines.append(f'  printf("{name} {f} %zu\\n", offsetof({name}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = {}
+    for ln in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines():
+        s, f, v = ln.split()
+        got[(s, f)] = int(v)
+    for name in STRUCTS:
+        T = getattr(cad, name)
+        assert got[(name, "size")] == ctypes.sizeof(T), name
+        for f, _ in T._fields_:
+            assert got[(name, f)] == getattr(T, f).offset, (name, f)

@@ -24,6 +24,16 @@
   prompt of 256 tokens): the committed tokens equal the oracle's greedy
   full-depth decoding, every one of whose decisions has a margin above 0.1
   (asserted).
+* ``cad_loop_decode`` with second-readout branching (CopyLoop §A.2): on the
+  fp32 tiny block applied 4 or 6 times, weights scaled by 0.3, 0.5 and 1.0,
+  seeded uniform prompts of 40 ids chosen so that forks are made, kept and
+  lost (one case) and every decision the oracle takes has a margin above
+  1e-3: the committed tokens and every counter, fork counters included,
+  equal ``oracle.copyloop_branch_decode``'s, and the cache the decoder
+  leaves holds a clean forward's K/V for every fed committed position at
+  every depth (1e-4), the second line's states copied back where it was
+  kept.  The bf16 looped shape with branching commits greedy full-depth
+  decoding's tokens.  Bad branching arguments are refused on the host.
 """
 import numpy as np
 import pytest
@@ -206,7 +216,11 @@ def test_loop_decode_matches_oracle_pipeline_fp32(seed_id, ds, monkeypatch):
     cad.cad_model_destroy(model)
 
 
-def test_loop_decode_looped_bf16_equals_greedy_full_depth():
+_bf16_ref = {}
+
+
+@pytest.mark.parametrize("d2", [0, 5])
+def test_loop_decode_looped_bf16_equals_greedy_full_depth(d2):
     dev = _dev()
     shape = synth.LOOPED
     cfg = Config.of(shape)
@@ -215,22 +229,130 @@ def test_loop_decode_looped_bf16_equals_greedy_full_depth():
     prompt = [int(t) for t in synth.make_line_prompt(256, shape.vocab, seed=5, line_len_range=(8, 16)).tokens]
     n, K, ds = 16, 8, 2
     cap = len(prompt) + n + shape.loop_depth * (K + 1) + 1
-    okv = KVCache.empty(shape.loop_depth, shape.n_kv_heads, cap, shape.head_dim)
-    x = oracle.decoder.splice_hidden(cfg, W64, okv, 0, prompt)
-    lg = oracle.final_logits(cfg, W64, x[-1:])
-    want, margins = [int(np.argmax(lg[0]))], [float(oracle.top2_margin(lg, None)[0])]
-    while len(want) < n:
-        lg = oracle.decoder.decode_step(cfg, W64, okv, len(prompt) + len(want) - 1, want[-1])[None]
-        margins.append(float(oracle.top2_margin(lg, None)[0]))
-        want.append(int(np.argmax(lg[0])))
-    assert min(margins) > 0.1
-    nb = (cap + BLK - 1) // BLK
-    kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device=dev)
+    if "want" not in _bf16_ref:
+        okv = KVCache.empty(shape.loop_depth, shape.n_kv_heads, cap, shape.head_dim)
+        x = oracle.decoder.splice_hidden(cfg, W64, okv, 0, prompt)
+        lg = oracle.final_logits(cfg, W64, x[-1:])
+        want, margins = [int(np.argmax(lg[0]))], [float(oracle.top2_margin(lg, None)[0])]
+        while len(want) < n:
+            lg = oracle.decoder.decode_step(cfg, W64, okv, len(prompt) + len(want) - 1, want[-1])[None]
+            margins.append(float(oracle.top2_margin(lg, None)[0]))
+            want.append(int(np.argmax(lg[0])))
+        _bf16_ref.update(want=want, margin=min(margins))
+    want = _bf16_ref["want"]
+    assert _bf16_ref["margin"] > 0.1
+    if d2:
+        kv, nb = _branch_kv(shape, cap, K, dev)
+    else:
+        nb = (cap + BLK - 1) // BLK
+        kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device=dev)
     model = cad.cad_model_create(shape, _to(Wt, dev), max_tokens=512)
-    loop = cad.cad_loop_create(model, cap, ds, K, 64)
+    loop = cad.cad_loop_create(model, cap, ds, K, 64, branch_depth=d2)
     got, st = cad.cad_loop_decode(loop, kv, prompt, n)
-    print(f"looped bf16: {st}; tokens {got}", flush=True)
+    print(f"looped bf16 d2={d2}: {st}; tokens {got}", flush=True)
     assert got == want
     assert st["dev_status"] == 0 and st["committed"] >= n
+    cad.cad_loop_destroy(loop)
+    cad.cad_model_destroy(model)
+
+
+# ---------------------------------------------------------------------------
+# second-readout branching
+# ---------------------------------------------------------------------------
+
+def _branch_kv(shape, cap, K, dev):
+    """A pool holding the request's blocks (block-table row 0, in order)
+    and the spare blocks the second line maps its positions to (row 1)."""
+    nb = (cap + BLK - 1) // BLK
+    spare = -(-(shape.loop_depth * (K + 1) + 16) // 16) + 1
+    table = torch.zeros((2, max(nb, spare)), dtype=torch.int32)
+    table[0, :nb] = torch.arange(nb, dtype=torch.int32)
+    table[1, :spare] = torch.arange(nb, nb + spare, dtype=torch.int32)
+    return cad.KVCache.alloc(shape, nb + spare, table, device=dev), nb
+
+
+# name: (block scale, depth D, ds, d2, K, max_rows, prompt seed); the oracle's forks (kept, lost) noted
+BRANCH_CASES = {
+    "scale0.3": (0.3, 4, 1, 3, 8, 24, 11),    # 5 forks, 5 kept
+    "rows6": (0.5, 4, 2, 3, 4, 6, 5),         # 20 forks, 20 kept, at most 6 rows in flight
+    "scale1": (1.0, 4, 1, 3, 8, 24, 1),       # 14 forks, 8 kept
+    "lost": (1.0, 4, 2, 3, 8, 24, 1),         # 10 forks, 7 kept, 1 lost
+    "depth6": (0.3, 6, 2, 4, 8, 24, 11),      # 4 forks, 2 kept
+}
+COUNTERS = ("ticks", "rows_run", "blocks", "proposed", "screened_out", "rejected", "discarded", "committed",
+            "forks", "forks_kept", "forks_lost", "fork_rows_dropped")
+
+
+@pytest.mark.parametrize("name", list(BRANCH_CASES))
+def test_loop_decode_branching_matches_oracle(name, monkeypatch):
+    dev = _dev()
+    scale, D, ds, d2, K, max_rows, pseed = BRANCH_CASES[name]
+    shape, Wt, Wn = _tiny_loop(scale, D)
+    cfg = Config.of(shape)
+    W64 = _f64(Wn)
+    prompt = [int(t) for t in np.random.default_rng(pseed).integers(0, shape.vocab, size=40)]
+    n = 24
+    margins = []
+    real = CL.masked_argmax
+
+    def recording(lg, mask):
+        margins.extend(oracle.top2_margin(lg, mask))
+        return real(lg, mask)
+    monkeypatch.setattr(CL, "masked_argmax", recording)
+    cap = len(prompt) + n + D * (K + 1) + 1
+    ocap = cap + 2 * D * (K + 1)
+    want, st_ref = CL.copyloop_branch_decode(cfg, W64, KVCache.empty(D, 4, ocap, 64), prompt, n, ds, d2, K, max_rows)
+    monkeypatch.undo()
+    assert min(margins) > 1e-3, min(margins)
+    assert st_ref["forks"] > 0
+    if name == "lost":
+        assert st_ref["forks_lost"] > 0 and st_ref["forks_kept"] > 0
+    full = oracle.greedy_decode(cfg, W64, KVCache.empty(D, 4, ocap, 64), prompt, st_ref["committed"])
+    assert want == full[:n]
+    kv, nb = _branch_kv(shape, cap, K, dev)
+    model = cad.cad_model_create(shape, _to(Wt, dev), max_tokens=64)
+    loop = cad.cad_loop_create(model, cap, ds, K, max_rows, branch_depth=d2)
+    print(f"branching {name}: D {D} ds {ds} d2 {d2} K {K} max_rows {max_rows}", flush=True)
+    got, st = cad.cad_loop_decode(loop, kv, prompt, n)
+    print(f"  {st}", flush=True)
+    assert got == want
+    assert st["dev_status"] == 0
+    for k in COUNTERS:
+        assert st[k] == st_ref[k], (k, st[k], st_ref[k])
+    # every fed committed position's K/V at every depth, through row 0
+    P = len(prompt) + st["committed"] - 1
+    ref = KVCache.empty(D, 4, ocap, 64)
+    oracle.decoder.splice_hidden(cfg, W64, ref, 0, (prompt + full)[:P])
+    gk, gv = H.read_span(kv, 0, P)
+    for c in range(D):
+        ek = float(np.max(np.abs(gk[c] - ref.k[c][:, :P])))
+        ev = float(np.max(np.abs(gv[c] - ref.v[c][:, :P])))
+        assert ek <= 1e-4 and ev <= 1e-4, (c, ek, ev)
+    cad.cad_loop_destroy(loop)
+    cad.cad_model_destroy(model)
+
+
+def test_loop_branching_arguments_checked():
+    dev = _dev()
+    shape, Wt, Wn = _tiny_loop(0.3)
+    model = cad.cad_model_create(shape, _to(Wt, dev), max_tokens=64)
+    for ds, d2 in ((2, 2), (2, 1), (1, 4)):
+        with pytest.raises(cad.CadError) as e:
+            cad.cad_loop_create(model, 256, ds, 8, 24, branch_depth=d2)
+        assert e.value.status == cad.CAD_E_ARG
+    loop = cad.cad_loop_create(model, 256, 1, 8, 24, branch_depth=3)
+    prompt = list(range(40))
+    # a one-row table
+    nb = 16
+    kv1 = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device=dev)
+    with pytest.raises(cad.CadError):
+        cad.cad_loop_decode(loop, kv1, prompt, 8)
+    # spare blocks that are also the request's, or outside the pool
+    kv, _ = _branch_kv(shape, 256, 8, dev)
+    for bad in (3, kv.num_blocks):
+        kv.block_table[1, 0] = bad
+        with pytest.raises(cad.CadError) as e:
+            cad.cad_loop_decode(loop, kv, prompt, 8)
+        assert e.value.status == cad.CAD_E_ARG
     cad.cad_loop_destroy(loop)
     cad.cad_model_destroy(model)

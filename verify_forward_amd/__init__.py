@@ -68,17 +68,18 @@ class cad_kv(ctypes.Structure):
 
 class cad_loop_group(ctypes.Structure):
     _fields_ = [("pos", ctypes.c_int64), ("rows", ctypes.c_int32), ("depth", ctypes.c_int32),
-                ("state", ctypes.c_int32), ("readout", ctypes.c_int32)]
+                ("state", ctypes.c_int32), ("readout", ctypes.c_int32), ("table_row", ctypes.c_int32)]
 
 
 class cad_loop_params(ctypes.Structure):
     _fields_ = [("screen_depth", ctypes.c_int32), ("max_copy", ctypes.c_int32), ("max_ngram", ctypes.c_int32),
-                ("min_ngram", ctypes.c_int32), ("max_rows", ctypes.c_int32)]
+                ("min_ngram", ctypes.c_int32), ("max_rows", ctypes.c_int32), ("branch_depth", ctypes.c_int32)]
 
 
 class cad_loop_stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("ticks", "rows_run", "blocks", "proposed", "screened_out", "rejected",
-                                              "discarded", "committed", "host_syncs")] + \
+                                              "discarded", "committed", "host_syncs", "forks", "forks_kept",
+                                              "forks_lost", "fork_rows_dropped")] + \
                [("dev_status", ctypes.c_int32)]
 
 
@@ -310,10 +311,11 @@ def cad_splice_forward_looped(model: Model, kv: KVCache, L: int, span: torch.Ten
 def cad_loop_step(model: Model, kv: KVCache, groups: Sequence, tokens: torch.Tensor, state: torch.Tensor,
                   mask: Optional[torch.Tensor], argmax: Optional[torch.Tensor], accepted: Optional[torch.Tensor],
                   logits: Optional[torch.Tensor] = None, dev_status: Optional[torch.Tensor] = None, stream=None):
-    """``groups``: sequence of (pos, rows, depth, state_row, readout) tuples;
-    ``state``: float32 device tensor [state_rows][d_model]."""
-    arr = (cad_loop_group * len(groups))(*[cad_loop_group(int(p), int(r), int(d), int(st), int(ro))
-                                           for p, r, d, st, ro in groups])
+    """``groups``: sequence of (pos, rows, depth, state_row, readout[,
+    table_row]) tuples (table_row 0 when left out); ``state``: float32
+    device tensor [state_rows][d_model]."""
+    arr = (cad_loop_group * len(groups))(*[cad_loop_group(int(g[0]), int(g[1]), int(g[2]), int(g[3]), int(g[4]),
+                                                          int(g[5]) if len(g) > 5 else 0) for g in groups])
     s = kv.struct()
     _check(lib().cad_loop_step(model.handle, ctypes.byref(s), len(groups), arr, _p(tokens), _p(state),
                                int(state.shape[0]), _p(mask), _p(argmax), _p(accepted), _p(logits),
@@ -323,8 +325,8 @@ def cad_loop_step(model: Model, kv: KVCache, groups: Sequence, tokens: torch.Ten
 class Loop:
     """Owns a ``cad_loop*`` (the pipeline's buffers) and keeps its model alive."""
 
-    def __init__(self, handle, model: Model):
-        self.handle, self.model = handle, model
+    def __init__(self, handle, model: Model, params: cad_loop_params):
+        self.handle, self.model, self.params = handle, model, params
 
     def __del__(self):
         try:
@@ -335,11 +337,12 @@ class Loop:
 
 
 def cad_loop_create(model: Model, max_len: int, screen_depth: int, max_copy: int, max_rows: int,
-                    max_ngram: int = 4, min_ngram: int = 1) -> Loop:
-    p = cad_loop_params(int(screen_depth), int(max_copy), int(max_ngram), int(min_ngram), int(max_rows))
+                    max_ngram: int = 4, min_ngram: int = 1, branch_depth: int = 0) -> Loop:
+    p = cad_loop_params(int(screen_depth), int(max_copy), int(max_ngram), int(min_ngram), int(max_rows),
+                        int(branch_depth))
     h = _VP()
     _check(lib().cad_loop_create(model.handle, int(max_len), ctypes.byref(p), ctypes.byref(h)))
-    return Loop(h, model)
+    return Loop(h, model, p)
 
 
 def cad_loop_destroy(loop: Loop):
@@ -350,7 +353,10 @@ def cad_loop_destroy(loop: Loop):
 
 def cad_loop_decode(loop: Loop, kv: KVCache, prompt: Sequence[int], n_new: int, stream=None):
     """Returns ``(tokens, stats)``: the ``n_new`` committed tokens and the
-    pipeline counters as a dict."""
+    pipeline counters as a dict.  With branching the block table needs two
+    rows (row 1 leads with the spare blocks of the second line)."""
+    if loop.params.branch_depth > 0 and kv.block_table.numel() < 2 * kv.max_blocks_per_seq:
+        raise CadError(CAD_E_ARG, "branching needs a block table of two rows")
     pr = (ctypes.c_int32 * len(prompt))(*[int(t) for t in prompt])
     out = (ctypes.c_int32 * int(n_new))()
     st = cad_loop_stats()

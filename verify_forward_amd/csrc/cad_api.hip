@@ -696,6 +696,7 @@ cad_status cad_loop_step(cad_model* m, const cad_kv* kv, int32_t n_groups, const
     if (g.depth < 0 || g.depth >= c.loop_depth)
       return fail(CAD_E_ARG, "group %d depth %d outside [0, %d)", b, g.depth, c.loop_depth);
     if (g.readout != 0 && g.readout != 1) return fail(CAD_E_ARG, "group %d readout %d is neither 0 nor 1", b, g.readout);
+    if (g.table_row < 0) return fail(CAD_E_ARG, "group %d table row %d < 0", b, g.table_row);
     if (g.state < 0 || (int64_t)g.state + g.rows > state_rows)
       return fail(CAD_E_ARG, "group %d state rows [%d, %d) outside [0, %d)", b, g.state, g.state + g.rows, state_rows);
     for (int o = 0; o < b; ++o)
@@ -715,7 +716,7 @@ cad_status cad_loop_step(cad_model* m, const cad_kv* kv, int32_t n_groups, const
   rm.total = rm.start[n_groups];
   rowmap_pad(rm);
   for (int b = 0; b < n_groups; ++b) {
-    rm.trow[b] = 0;                // one request: block-table row 0
+    rm.trow[b] = groups[b].table_row;
     rm.cidx[b] = groups[b].depth;  // its depth's cache
   }
   hipStream_t s = (hipStream_t)stream;

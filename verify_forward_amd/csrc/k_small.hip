@@ -401,6 +401,45 @@ __global__ void __launch_bounds__(ROPE_THREADS) k_rope_append(const float* __res
   }
 }
 
+// Copy cache slots [lo, hi) of block `src` into block `dst` at every cache
+// index of a paged pool (a looped model's depths): one work-group per (pair,
+// cache index).  pairs: [n_pairs][4] = src, dst, lo, hi (checked by the host:
+// blocks in [0, num_blocks), 0 <= lo < hi <= 16).
+template <typename T>
+__global__ void __launch_bounds__(256) k_kv_copy(T* __restrict__ k, T* __restrict__ v, int64_t cache_stride, int hkv,
+                                                 int hd, const int32_t* __restrict__ pairs) {
+  const int pr = blockIdx.x;
+  const int64_t ci = blockIdx.y;
+  const int64_t src = pairs[4 * pr], dst = pairs[4 * pr + 1];
+  const int lo = pairs[4 * pr + 2], n = pairs[4 * pr + 3] - lo;
+  const int64_t blk = (int64_t)hkv * CAD_KV_BLOCK * hd;
+  T* kc = k + ci * cache_stride;
+  T* vc = v + ci * cache_stride;
+  const int64_t per_head = (int64_t)n * hd;
+  for (int64_t i = threadIdx.x; i < hkv * per_head; i += blockDim.x) {
+    // K [head][slot][hd]: slots lo .. lo + n - 1 of each head are contiguous
+    const int64_t h = i / per_head, r = i % per_head;
+    const int64_t o = (h * CAD_KV_BLOCK + lo) * hd + r;
+    kc[dst * blk + o] = kc[src * blk + o];
+    // V [head][hd][slot]: n slots of each (head, dim)
+    const int64_t d = r / n, sl = lo + r % n;
+    const int64_t ov = (h * hd + d) * CAD_KV_BLOCK + sl;
+    vc[dst * blk + ov] = vc[src * blk + ov];
+  }
+}
+
+hipError_t launch_kv_copy(int dtype, void* k, void* v, int64_t cache_stride, int n_cache, int hkv, int hd,
+                          const int32_t* pairs, int n_pairs, hipStream_t s) {
+  if (n_pairs < 1) return hipSuccess;
+  const dim3 grid((unsigned)n_pairs, (unsigned)n_cache);
+  if (dtype == CAD_BF16)
+    hipLaunchKernelGGL((k_kv_copy<bf16_t>), grid, dim3(256), 0, s, (bf16_t*)k, (bf16_t*)v, cache_stride, hkv, hd,
+                       pairs);
+  else
+    hipLaunchKernelGGL((k_kv_copy<float>), grid, dim3(256), 0, s, (float*)k, (float*)v, cache_stride, hkv, hd, pairs);
+  return hipGetLastError();
+}
+
 // rows at most this many: one work-group per (row, KV group)
 constexpr int ROPE_GROUPED_MAX_ROWS = 64;
 
