@@ -312,7 +312,7 @@ def looped_bench(reps=10):
                         "L=4096, head + suffix-match proposal (K=8)", **res}
 
 
-def copyloop_bench(n_new=64, L0=4096, K=8, ds=2):
+def copyloop_bench(n_new=64, L0=4096, K=8, ds=2, d2=5):
     """CopyLoop decoding on the looped shape (d 2048, 16 x 128 heads, FFN
     5632, vocab 32000, depth 8): prefill of a 4096-token prompt, then n_new
     tokens by the pipeline (context-copy blocks of up to K = 8 tokens,
@@ -325,19 +325,25 @@ def copyloop_bench(n_new=64, L0=4096, K=8, ds=2):
     the block's weights scaled by 0.1 (depths agree: a stand-in for a looped
     model whose shallow predictions are usable); and that model on a prompt
     whose last 256 tokens are its own greedy continuation (the repeated-span
-    regime context copying targets).  Reports tokens/s of both decoders, the
-    speedup, whether they committed the same tokens, and the pipeline
-    counters."""
+    regime context copying targets).  Each case runs the pipeline without
+    and with second-readout branching at depth d2 = 5 (CopyLoop §A.2).
+    Reports tokens/s of the decoders, the speedups, whether they committed
+    the same tokens, and the pipeline counters."""
     import torch
     import synth
     import verify_forward_amd as cad
     shape = synth.LOOPED
     D = shape.loop_depth
     out = {"workload": f"looped shared block (d 2048, 16 x 128 heads, FFN 5632, vocab 32000, depth 8), "
-                       f"prompt of {L0} tokens, {n_new} new tokens, K={K}, ds={ds}, max_rows=64"}
+                       f"prompt of {L0} tokens, {n_new} new tokens, K={K}, ds={ds}, max_rows=64, "
+                       f"branching at d2={d2}"}
     lines = [int(t) for t in synth.make_line_prompt(L0, shape.vocab).tokens]
     cap = L0 + 256 + n_new + D * (K + 1) + 16
     nb = (cap + 15) // 16
+    spare = -(-(D * (K + 1) + 16) // 16) + 1     # the second line's blocks (block-table row 1)
+    table = torch.zeros((2, nb), dtype=torch.int32)
+    table[0] = torch.arange(nb, dtype=torch.int32)
+    table[1, :spare] = torch.arange(nb, nb + spare, dtype=torch.int32)
 
     def ar_decode(model, kv, prompt, n):
         """device-resident greedy decoding: tokens stay on the device"""
@@ -361,31 +367,40 @@ def copyloop_bench(n_new=64, L0=4096, K=8, ds=2):
         if scale != 1.0:
             for k in ("w_qkv", "w_o", "w_gate_up", "w_down"):
                 W["layers"][0][k].mul_(scale)
-        kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device="cuda")
+        kv = cad.KVCache.alloc(shape, nb + spare, table, device="cuda")
         model = cad.cad_model_create(shape, W, max_tokens=L0)
         prompt = lines
         if self_cont:
             cont = ar_decode(model, kv, lines[:L0 - 256], 256)
             prompt = lines[:L0 - 256] + [int(t) for t in cont.cpu()]
-        loop = cad.cad_loop_create(model, cap, ds, K, 64)
-        cad.cad_loop_decode(loop, kv, prompt, 8)          # warm up
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        toks, st = cad.cad_loop_decode(loop, kv, prompt, n_new)
-        torch.cuda.synchronize()
-        t_loop = time.perf_counter() - t0
+        runs = {}
+        for bd in (0, d2):
+            loop = cad.cad_loop_create(model, cap, ds, K, 64, branch_depth=bd)
+            cad.cad_loop_decode(loop, kv, prompt, 8)          # warm up
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            toks, st = cad.cad_loop_decode(loop, kv, prompt, n_new)
+            torch.cuda.synchronize()
+            runs[bd] = (time.perf_counter() - t0, toks, st)
+            cad.cad_loop_destroy(loop)
         ar_decode(model, kv, prompt, n_new)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         gen = ar_decode(model, kv, prompt, n_new)
         torch.cuda.synchronize()
         t_ar = time.perf_counter() - t0
+        gen = [int(t) for t in gen.cpu()]
+        t_loop, toks, st = runs[0]
+        t_br, toks_br, st_br = runs[d2]
         out[name] = {"pipeline_tok_s": round(n_new / t_loop, 1), "full_depth_ar_tok_s": round(n_new / t_ar, 1),
-                     "tokens_equal_to_ar": [int(t) for t in gen.cpu()] == [int(t) for t in toks],
+                     "tokens_equal_to_ar": gen == [int(t) for t in toks],
                      "speedup": round(t_ar / t_loop, 3), "pipeline_s": round(t_loop, 4), "ar_s": round(t_ar, 4),
-                     "stats": st}
-        log(f"[bench] copyloop {name}: {out[name]['pipeline_tok_s']} tok/s vs AR {out[name]['full_depth_ar_tok_s']}")
-        cad.cad_loop_destroy(loop)
+                     "stats": st,
+                     "branching": {"tok_s": round(n_new / t_br, 1), "speedup": round(t_ar / t_br, 3),
+                                   "tokens_equal_to_ar": gen == [int(t) for t in toks_br], "s": round(t_br, 4),
+                                   "stats": st_br}}
+        log(f"[bench] copyloop {name}: {out[name]['pipeline_tok_s']} tok/s (branching "
+            f"{out[name]['branching']['tok_s']}) vs AR {out[name]['full_depth_ar_tok_s']}")
         cad.cad_model_destroy(model)
         del kv, W
         torch.cuda.empty_cache()

@@ -74,7 +74,52 @@ struct Block {
   uint64_t id = 0;
 };
 
-constexpr int kPropSlots = 2;  // proposals made after a tick: 0 after screening, 1 after full depth
+// proposals made on the device after a tick: the successor of the block
+// screened on the first line's history (0), the token after the full-depth
+// block (1), the successor of the block screened on the second line's (2),
+// and the second child's head of a block read out at the branch depth on
+// the first or the second line's history (3, 4); then the slot of a
+// proposal made when a head is admitted
+constexpr int kPropScreen0 = 0, kPropFull = 1, kPropScreen1 = 2, kPropFork = 3, kPropSlots = 5;
+// What the host reads back after a tick, contiguous on the device and in
+// pinned memory so that one copy brings it: the groups' acceptance, the
+// proposals ([1 + kPropSlots][65]: tokens[64], then the length; padded to
+// 16 bytes), then the argmax of every row.
+constexpr int kRbProp = CAD_MAX_SEQS, kRbArgmax = kRbProp + ((1 + kPropSlots) * 65 + 3) / 4 * 4;
+
+// Copy cache slots [lo, hi) of block `src` into block `dst` at every cache
+// index of a paged pool (a looped model's depths): one work-group per (pair,
+// cache index, KV head).  pairs: [n_pairs][4] = src, dst, lo, hi (checked
+// by the host: blocks in [0, num_blocks), 0 <= lo < hi <= 16).
+template <typename T>
+__global__ void __launch_bounds__(256) k_kv_copy(T* __restrict__ k, T* __restrict__ v, int64_t cache_stride, int hd,
+                                                 const int32_t* __restrict__ pairs) {
+  const int pr = blockIdx.x, h = blockIdx.z, hkv = gridDim.z;
+  const int lo = pairs[4 * pr + 2], n = pairs[4 * pr + 3] - lo;
+  const int64_t blk = (int64_t)hkv * CAD_KV_BLOCK * hd;
+  const int64_t head = (int64_t)blockIdx.y * cache_stride + (int64_t)h * CAD_KV_BLOCK * hd;
+  T* ks = k + pairs[4 * pr] * blk + head;
+  T* kd = k + pairs[4 * pr + 1] * blk + head;
+  T* vs = v + pairs[4 * pr] * blk + head;
+  T* vd = v + pairs[4 * pr + 1] * blk + head;
+  // K [slot][hd]: slots lo .. lo + n - 1 are contiguous
+  for (int i = threadIdx.x; i < n * hd; i += blockDim.x) kd[lo * hd + i] = ks[lo * hd + i];
+  // V [hd][slot]: n slots of each dimension
+  for (int dd = threadIdx.x; dd < hd; dd += blockDim.x)
+    for (int sl = lo; sl < lo + n; ++sl) vd[dd * CAD_KV_BLOCK + sl] = vs[dd * CAD_KV_BLOCK + sl];
+}
+
+hipError_t launch_kv_copy(int dtype, void* k, void* v, int64_t cache_stride, int n_cache, int hkv, int hd,
+                          const int32_t* pairs, int n_pairs, hipStream_t s) {
+  if (n_pairs < 1) return hipSuccess;
+  const dim3 grid((unsigned)n_pairs, (unsigned)n_cache, (unsigned)hkv);
+  if (dtype == CAD_BF16)
+    hipLaunchKernelGGL((k_kv_copy<cad::bf16_t>), grid, dim3(256), 0, s, (cad::bf16_t*)k, (cad::bf16_t*)v, cache_stride,
+                       hd, pairs);
+  else
+    hipLaunchKernelGGL((k_kv_copy<float>), grid, dim3(256), 0, s, (float*)k, (float*)v, cache_stride, hd, pairs);
+  return hipGetLastError();
+}
 
 cad_status loop_fail(cad_status s, const std::string& msg) { return cad::set_error(s, msg.c_str()); }
 
@@ -93,6 +138,7 @@ struct cad_loop {
   int32_t* d_accepted = nullptr;
   int32_t* d_hist = nullptr;      // history of the first line (device)
   int32_t* d_hist2 = nullptr;     // history of the second line (branching)
+  int32_t* d_spec[2] = {nullptr, nullptr};  // a possible second child's history, per line (branching)
   int32_t* d_table = nullptr;     // [2][tbl_stride] block-table rows the pipeline runs on
   int32_t* d_pairs = nullptr;     // [max_pairs][4] KV block copies
   int32_t tbl_stride = 0, max_pairs = 0;
@@ -145,6 +191,7 @@ struct Run {
   std::vector<int32_t> hist[2];
   size_t dev_valid[2] = {0, 0};
   int32_t* d_hist[2] = {nullptr, nullptr};
+  int32_t* d_spec[2] = {nullptr, nullptr};  // branching: histories made for a possible second child
   std::vector<int32_t> out;
   std::deque<Block> blocks;      // oldest first; waiting heads are admitted in this order
   std::vector<int32_t> free_slots;
@@ -229,7 +276,7 @@ struct Run {
     int32_t n_tail = 0;
     const int32_t* tail = nullptr;
     if (lp->p.max_copy > 0 && room > 1) {
-      int slot = line == 0 ? b.ready : -1;
+      int slot = b.ready;
       if (slot < 0) {
         slot = kPropSlots;
         cad_status r = sync_hist(line);
@@ -286,7 +333,7 @@ struct Run {
   cad_status kv_copy(int first, int n) {
     if (n <= 0) return CAD_OK;
     LOOP_HIP(hipMemcpyAsync(lp->d_pairs + 4 * first, lp->h_pairs + 4 * first, (size_t)n * 16, hipMemcpyHostToDevice, s));
-    LOOP_HIP(cad::launch_kv_copy(lp->cfg.dtype, user_kv->k, user_kv->v, cache_stride, n_caches(),
+    LOOP_HIP(launch_kv_copy(lp->cfg.dtype, user_kv->k, user_kv->v, cache_stride, n_caches(),
                                  lp->cfg.n_kv_heads, lp->cfg.head_dim, lp->d_pairs + 4 * first, n, s));
     return CAD_OK;
   }
@@ -295,14 +342,19 @@ struct Run {
   // row 0's block to the second line's (pair 0, staged at the fork)
   cad_status sync_fork_block() {
     if (!fork_live || fork_pos % CAD_KV_BLOCK == 0) return CAD_OK;
-    LOOP_HIP(cad::launch_kv_copy(lp->cfg.dtype, user_kv->k, user_kv->v, cache_stride, n_caches(),
+    LOOP_HIP(launch_kv_copy(lp->cfg.dtype, user_kv->k, user_kv->v, cache_stride, n_caches(),
                                  lp->cfg.n_kv_heads, lp->cfg.head_dim, lp->d_pairs, 1, s));
     return CAD_OK;
   }
 
-  // make the fork at block i (read out at d2): the second child, headed by h1
-  cad_status make_fork(size_t i, int32_t h1, int32_t room, std::vector<int32_t>& row0r, std::vector<int32_t>& accd) {
+  // make the fork at block i (read out at d2): the second child, headed by
+  // h1; with `proposed`, its history and proposal were made on the device
+  // after the tick (in d_spec of the block's table row, proposal slot
+  // kPropFork + that row)
+  cad_status make_fork(size_t i, int32_t h1, int32_t room, bool proposed, std::vector<int32_t>& row0r,
+                       std::vector<int32_t>& accd) {
     const Block& b = blocks[i];
+    const int trow = b.tick_row;
     fork_live = true;
     fork_parent = b.id;
     fork_pos = b.pos + (int64_t)b.toks.size();
@@ -323,15 +375,20 @@ struct Run {
       if (r != CAD_OK) return r;
     }
     // the second line's history: the first line's up to the fork
-    cad_status r = sync_hist(0);
-    if (r != CAD_OK) return r;
-    LOOP_HIP(hipMemcpyAsync(d_hist[1], d_hist[0], (size_t)fork_pos * 4, hipMemcpyDeviceToDevice, s));
+    if (proposed) {
+      std::swap(d_hist[1], d_spec[trow]);
+    } else {
+      cad_status r = sync_hist(0);
+      if (r != CAD_OK) return r;
+      LOOP_HIP(hipMemcpyAsync(d_hist[1], d_hist[0], (size_t)fork_pos * 4, hipMemcpyDeviceToDevice, s));
+    }
     hist[1].assign(hist[0].begin(), hist[0].begin() + fork_pos);
     dev_valid[1] = (size_t)fork_pos;
     Block nb;
     nb.pos = fork_pos;
     nb.toks.push_back(h1);
     nb.line = 1;
+    nb.ready = proposed ? kPropFork + trow : -1;
     nb.id = next_id++;
     blocks.push_back(nb);
     row0r.push_back(-1);
@@ -430,6 +487,8 @@ struct Run {
     const int32_t D = lp->cfg.loop_depth, ds = lp->p.screen_depth, d2 = lp->p.branch_depth;
     d_hist[0] = lp->d_hist;
     d_hist[1] = lp->d_hist2;
+    d_spec[0] = lp->d_spec[0];
+    d_spec[1] = lp->d_spec[1];
     for (int32_t i = lp->n_slots - 1; i >= 0; --i) free_slots.push_back(i);
     kv = user_kv;
     cad_status r = CAD_OK;
@@ -486,11 +545,17 @@ struct Run {
       if (groups.empty()) return loop_fail(CAD_E_ARG, "pipeline empty before the decode finished");
       const bool propose = any_read && lp->p.max_copy > 0;
       if (propose) {
-        // the device history must hold every token in flight for the proposals below
+        // the device histories must hold every token in flight for the proposals below
         cad_status r2 = sync_hist(0);
+        if (r2 == CAD_OK && fork_live) r2 = sync_hist(1);
         if (r2 != CAD_OK) return r2;
       }
-      LOOP_HIP(hipMemcpyAsync(lp->d_tokens, h_tok, (size_t)total * 4, hipMemcpyHostToDevice, s));
+      // with branching, each group's row count follows the tokens (the kept
+      // rows of a possible second child's proposal)
+      int32_t n_up = total;
+      if (d2 > 0)
+        for (const cad_loop_group& g : groups) h_tok[n_up++] = g.rows;
+      LOOP_HIP(hipMemcpyAsync(lp->d_tokens, h_tok, (size_t)n_up * 4, hipMemcpyHostToDevice, s));
       LOOP_HIP(hipEventRecord(lp->tok_copied[st.ticks & 1], s));
       LOOP_CALL(cad_loop_step(lp->m, kv, (int32_t)groups.size(), groups.data(), lp->d_tokens, lp->state,
                               lp->n_slots * lp->slot_rows, nullptr, lp->d_argmax, lp->d_accepted, nullptr,
@@ -499,40 +564,58 @@ struct Run {
       st.rows_run += total;
       if (any_read) {
         if (propose) {
-          // proposals (first line's history) for the successor of the
-          // screened block (slot 0) and for the token after the full-depth
-          // block (slot 1), screening first: the full-depth one may write a
-          // correction into the history
+          // For a block read out at the branch depth, the history of a
+          // possible second child (its line's up to the child, then the
+          // depth-d2 prediction at its last row as the head) and that
+          // child's proposal.
           int32_t o = 0;
-          for (int pass = 0; pass < kPropSlots; ++pass) {
+          for (size_t k = 0; k < groups.size(); ++k) {
+            const cad_loop_group& g = groups[k];
+            if (g.readout && d2 > 0 && g.depth + 1 == d2) {
+              const int r = g.table_row, slot = kPropFork + r;
+              LOOP_HIP(hipMemcpyAsync(d_spec[r], d_hist[r], (size_t)(g.pos + g.rows) * 4, hipMemcpyDeviceToDevice, s));
+              int32_t* dp = lp->d_prop + slot * 65;
+              LOOP_HIP(cad::launch_propose_next(d_spec[r], g.pos, lp->d_tokens + total + k, lp->d_argmax + o,
+                                                lp->p.max_ngram, lp->p.min_ngram, lp->p.max_copy, dp, dp + 64,
+                                                lp->d_prop_pos + slot, lp->d_prop_head + slot, s));
+            }
+            o += g.rows;
+          }
+          // Then the successor of the block screened on each line's history
+          // and the token after the full-depth block, screening first: the
+          // full-depth one may write a correction into the history.
+          const int passes[3][3] = {{kPropScreen0, 0, ds}, {kPropScreen1, 1, ds}, {kPropFull, 0, D}};
+          for (const auto& ps : passes) {
             o = 0;
             for (size_t k = 0; k < groups.size(); ++k) {
-              const int32_t after = groups[k].depth + 1;
-              if (groups[k].readout && groups[k].table_row == 0 &&
-                  ((pass == 0 && after == ds) || (pass == 1 && after == D))) {
-                int32_t* dp = lp->d_prop + pass * 65;
-                LOOP_HIP(cad::launch_propose_next(d_hist[0], groups[k].pos, lp->d_accepted + k, lp->d_argmax + o,
+              const cad_loop_group& g = groups[k];
+              if (g.readout && g.table_row == ps[1] && g.depth + 1 == ps[2]) {
+                int32_t* dp = lp->d_prop + ps[0] * 65;
+                LOOP_HIP(cad::launch_propose_next(d_hist[ps[1]], g.pos, lp->d_accepted + k, lp->d_argmax + o,
                                                   lp->p.max_ngram, lp->p.min_ngram, lp->p.max_copy, dp, dp + 64,
-                                                  lp->d_prop_pos + pass, lp->d_prop_head + pass, s));
+                                                  lp->d_prop_pos + ps[0], lp->d_prop_head + ps[0], s));
               }
-              o += groups[k].rows;
+              o += g.rows;
             }
           }
-          LOOP_HIP(hipMemcpyAsync(lp->h_prop, lp->d_prop, kPropSlots * 65 * 4, hipMemcpyDeviceToHost, s));
         }
-        LOOP_HIP(hipMemcpyAsync(lp->h_argmax, lp->d_argmax, (size_t)total * 4, hipMemcpyDeviceToHost, s));
-        LOOP_HIP(hipMemcpyAsync(lp->h_accepted, lp->d_accepted, groups.size() * 4, hipMemcpyDeviceToHost, s));
+        // acceptance, proposals and argmax in one copy
+        LOOP_HIP(hipMemcpyAsync(lp->h_accepted, lp->d_accepted, (size_t)(kRbArgmax + total) * 4,
+                                hipMemcpyDeviceToHost, s));
         LOOP_HIP(hipStreamSynchronize(s));
         ++st.host_syncs;
         if (propose) {
-          // the device wrote each proposal's head into the first line's
-          // history copy; the host history takes those positions over when it
-          // admits or corrects
-          for (size_t k = 0; k < groups.size(); ++k)
-            if (groups[k].readout && groups[k].table_row == 0) {
+          // the device wrote the head of each screening or full-depth
+          // proposal into its line's history copy; the host history takes
+          // those positions over when it admits or corrects
+          for (size_t k = 0; k < groups.size(); ++k) {
+            const int32_t after = groups[k].depth + 1;
+            if (groups[k].readout && (after == ds || after == D)) {
+              const int r = groups[k].table_row;
               const size_t at = (size_t)(groups[k].pos + lp->h_accepted[k]);
-              if (dev_valid[0] > at) dev_valid[0] = at;
+              if (dev_valid[r] > at) dev_valid[r] = at;
             }
+          }
         }
       }
       // per block of this tick: its readout (row offset in the tick, accepted)
@@ -609,7 +692,7 @@ struct Run {
             Block c;
             c.pos = pos_next;
             c.toks.push_back(nxt);
-            c.ready = 1;  // proposed on the device after this tick
+            c.ready = kPropFull;  // proposed on the device after this tick
             c.id = next_id++;
             blocks.push_back(c);
             row0r.push_back(-1);
@@ -626,7 +709,7 @@ struct Run {
               const int32_t h1 = a[m - 1];
               const int32_t room = lp->p.max_rows - rows_in_flight();
               if (h1 != child.toks[0] && room >= 1 && !free_slots.empty()) {
-                r = make_fork(i, h1, room, row0r, accd);
+                r = make_fork(i, h1, room, propose, row0r, accd);
                 if (r != CAD_OK) return r;
               }
             }
@@ -644,8 +727,8 @@ struct Run {
             nb.pos = b.pos + keep;
             nb.toks.push_back(a[keep - 1]);
             nb.line = b.line;
-            // proposed on the device after this tick if the block ran on the first line's history
-            nb.ready = b.tick_row == 0 ? 0 : -1;
+            // proposed on the device after this tick, on the history the block ran on
+            nb.ready = b.tick_row == 0 ? kPropScreen0 : kPropScreen1;
             nb.id = next_id++;
             // a first-line block goes before the second line's blocks
             size_t at = blocks.size();
@@ -723,10 +806,12 @@ cad_status cad_loop_create(cad_model* m, int64_t max_len, const cad_loop_params*
   const int64_t d = c->d_model, srows = (int64_t)lp->n_slots * lp->slot_rows, T = c->max_tokens;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = up256(off + bytes); return o; };
-  const size_t o_state = take(srows * d * 4), o_tok = take(srows * 4), o_am = take(srows * 4),
-               o_acc = take(CAD_MAX_SEQS * 4), o_hist = take(max_len * 4),
-               o_hist2 = take(branch ? max_len * 4 : 0), o_tbl = take((size_t)lp->tbl_stride * 2 * 4),
-               o_pairs = take((size_t)lp->max_pairs * 16), o_prop = take((1 + kPropSlots) * 65 * 4),
+  const size_t rb_bytes = (size_t)(kRbArgmax + std::max<int64_t>(srows, 1)) * 4;
+  const size_t o_state = take(srows * d * 4), o_tok = take((srows + CAD_MAX_SEQS) * 4), o_rb = take(rb_bytes),
+               o_hist = take(max_len * 4),
+               o_hist2 = take(branch ? max_len * 4 : 0), o_spec0 = take(branch ? max_len * 4 : 0),
+               o_spec1 = take(branch ? max_len * 4 : 0), o_tbl = take((size_t)lp->tbl_stride * 2 * 4),
+               o_pairs = take((size_t)lp->max_pairs * 16),
                o_phead = take(kPropSlots * 4), o_ppos = take((1 + kPropSlots) * 8), o_st = take(4),
                o_pfs = take(T * 4), o_pfa = take(T * 4), o_pfm = take(2 * 4);
   hipError_t e = hipMalloc(&lp->dev, off);
@@ -737,13 +822,15 @@ cad_status cad_loop_create(cad_model* m, int64_t max_len, const cad_loop_params*
   char* b = (char*)lp->dev;
   lp->state = (float*)(b + o_state);
   lp->d_tokens = (int32_t*)(b + o_tok);
-  lp->d_argmax = (int32_t*)(b + o_am);
-  lp->d_accepted = (int32_t*)(b + o_acc);
+  lp->d_accepted = (int32_t*)(b + o_rb);
+  lp->d_prop = lp->d_accepted + kRbProp;
+  lp->d_argmax = lp->d_accepted + kRbArgmax;
   lp->d_hist = (int32_t*)(b + o_hist);
   lp->d_hist2 = branch ? (int32_t*)(b + o_hist2) : nullptr;
+  lp->d_spec[0] = branch ? (int32_t*)(b + o_spec0) : nullptr;
+  lp->d_spec[1] = branch ? (int32_t*)(b + o_spec1) : nullptr;
   lp->d_table = branch ? (int32_t*)(b + o_tbl) : nullptr;
   lp->d_pairs = branch ? (int32_t*)(b + o_pairs) : nullptr;
-  lp->d_prop = (int32_t*)(b + o_prop);
   lp->d_prop_head = (int32_t*)(b + o_phead);
   lp->d_prop_pos = (int64_t*)(b + o_ppos);
   lp->d_status = (int32_t*)(b + o_st);
@@ -752,8 +839,8 @@ cad_status cad_loop_create(cad_model* m, int64_t max_len, const cad_loop_params*
   lp->d_pf_misc = (int32_t*)(b + o_pfm);
   size_t hoff = 0;
   auto htake = [&](size_t bytes) { size_t o = hoff; hoff = up256(hoff + bytes); return o; };
-  const size_t h_tok0 = htake(srows * 4), h_tok1 = htake(srows * 4), h_am = htake(std::max<int64_t>(srows, 1) * 4), h_acc = htake(CAD_MAX_SEQS * 4),
-               h_hist = htake(max_len * 4), h_prop = htake((1 + kPropSlots) * 65 * 4),
+  const size_t h_tok0 = htake((srows + CAD_MAX_SEQS) * 4), h_tok1 = htake((srows + CAD_MAX_SEQS) * 4), h_rb = htake(rb_bytes),
+               h_hist = htake(max_len * 4),
                h_tbl = htake((size_t)lp->tbl_stride * 2 * 4), h_pairs = htake((size_t)lp->max_pairs * 16);
   e = hipHostMalloc(&lp->host, hoff, hipHostMallocDefault);
   if (e != hipSuccess) {
@@ -771,10 +858,10 @@ cad_status cad_loop_create(cad_model* m, int64_t max_len, const cad_loop_params*
       return loop_fail(CAD_E_HIP, std::string("hipEventCreate: ") + hipGetErrorString(e));
     }
   }
-  lp->h_argmax = (int32_t*)(h + h_am);
-  lp->h_accepted = (int32_t*)(h + h_acc);
+  lp->h_accepted = (int32_t*)(h + h_rb);
+  lp->h_prop = lp->h_accepted + kRbProp;
+  lp->h_argmax = lp->h_accepted + kRbArgmax;
   lp->h_hist = (int32_t*)(h + h_hist);
-  lp->h_prop = (int32_t*)(h + h_prop);
   lp->h_table = branch ? (int32_t*)(h + h_tbl) : nullptr;
   lp->h_pairs = branch ? (int32_t*)(h + h_pairs) : nullptr;
   *out = lp;

@@ -84,24 +84,41 @@ hipError_t launch_loop_load(int dtype, const void* table, int vocab, int d, cons
   return hipGetLastError();
 }
 
-__global__ void k_loop_store(float* __restrict__ x, const float* __restrict__ x_part, int n_part, int d,
-                             float* __restrict__ state, RowMap rm, StateMap sm) {
-  const int r = blockIdx.x;
+// One thread per four elements of a row: the pending k-split partial sums
+// are added to x in split order (their loads issued in batches of eight, so
+// the row does not wait for them one by one), and the row is saved to its
+// state slot.
+__global__ void __launch_bounds__(ROW_THREADS) k_loop_store(float* __restrict__ x, const float* __restrict__ x_part,
+                                                         int n_part, int d, float* __restrict__ state, RowMap rm,
+                                                         StateMap sm) {
+  const int r = blockIdx.y;
+  const int i = 4 * (blockIdx.x * ROW_THREADS + threadIdx.x);
+  if (i >= d) return;
   const int b = row_seq(rm, r);
-  float* xr = x + (int64_t)r * d;
-  float* st = state + (int64_t)(sm.base[b] + r - rm.start[b]) * d;
-  for (int i = threadIdx.x; i < d; i += blockDim.x) {
-    float v = xr[i];
-    for (int sp = 0; sp < n_part; ++sp) v += x_part[((int64_t)sp * rm.total + r) * d + i];
-    if (n_part > 0) xr[i] = v;
-    st[i] = v;
+  float* xr = x + (int64_t)r * d + i;
+  f32x4 v = *(const f32x4*)xr;
+  constexpr int PB = 8;
+  for (int sp = 0; sp < n_part; sp += PB) {
+    f32x4 t[PB];
+#pragma unroll
+    for (int j = 0; j < PB; ++j)
+      t[j] = *(const f32x4*)(x_part + ((int64_t)min(sp + j, n_part - 1) * rm.total + r) * d + i);
+#pragma unroll
+    for (int j = 0; j < PB; ++j)
+      if (sp + j < n_part) v += t[j];
   }
+  if (n_part > 0) *(f32x4*)xr = v;
+  // the state buffer is the caller's: plain element stores, no alignment assumed
+  float* st = state + (int64_t)(sm.base[b] + r - rm.start[b]) * d + i;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) st[e] = v[e];
 }
 
 hipError_t launch_loop_store(float* x, const float* x_part, int n_part, int d, float* state, const RowMap& rm,
                              const StateMap& sm, hipStream_t s) {
   if (n_part > 0 && !x_part) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_loop_store, dim3(rm.total), dim3(ROW_THREADS), 0, s, x, x_part, n_part, d, state, rm, sm);
+  const dim3 grid((unsigned)((d / 4 + ROW_THREADS - 1) / ROW_THREADS), (unsigned)rm.total);
+  hipLaunchKernelGGL(k_loop_store, grid, dim3(ROW_THREADS), 0, s, x, x_part, n_part, d, state, rm, sm);
   return hipGetLastError();
 }
 
@@ -399,45 +416,6 @@ __global__ void __launch_bounds__(ROPE_THREADS) k_rope_append(const float* __res
     if (write_kv) vc[((blk * hkv + g) * hd + dd) * CAD_KV_BLOCK + slot] = from_f<T>(vv);
     if (kv.span_v) kv.span_v[((int64_t)g * hd + dd) * kv.span_cap + wrow] = f2h(vv);
   }
-}
-
-// Copy cache slots [lo, hi) of block `src` into block `dst` at every cache
-// index of a paged pool (a looped model's depths): one work-group per (pair,
-// cache index).  pairs: [n_pairs][4] = src, dst, lo, hi (checked by the host:
-// blocks in [0, num_blocks), 0 <= lo < hi <= 16).
-template <typename T>
-__global__ void __launch_bounds__(256) k_kv_copy(T* __restrict__ k, T* __restrict__ v, int64_t cache_stride, int hkv,
-                                                 int hd, const int32_t* __restrict__ pairs) {
-  const int pr = blockIdx.x;
-  const int64_t ci = blockIdx.y;
-  const int64_t src = pairs[4 * pr], dst = pairs[4 * pr + 1];
-  const int lo = pairs[4 * pr + 2], n = pairs[4 * pr + 3] - lo;
-  const int64_t blk = (int64_t)hkv * CAD_KV_BLOCK * hd;
-  T* kc = k + ci * cache_stride;
-  T* vc = v + ci * cache_stride;
-  const int64_t per_head = (int64_t)n * hd;
-  for (int64_t i = threadIdx.x; i < hkv * per_head; i += blockDim.x) {
-    // K [head][slot][hd]: slots lo .. lo + n - 1 of each head are contiguous
-    const int64_t h = i / per_head, r = i % per_head;
-    const int64_t o = (h * CAD_KV_BLOCK + lo) * hd + r;
-    kc[dst * blk + o] = kc[src * blk + o];
-    // V [head][hd][slot]: n slots of each (head, dim)
-    const int64_t d = r / n, sl = lo + r % n;
-    const int64_t ov = (h * hd + d) * CAD_KV_BLOCK + sl;
-    vc[dst * blk + ov] = vc[src * blk + ov];
-  }
-}
-
-hipError_t launch_kv_copy(int dtype, void* k, void* v, int64_t cache_stride, int n_cache, int hkv, int hd,
-                          const int32_t* pairs, int n_pairs, hipStream_t s) {
-  if (n_pairs < 1) return hipSuccess;
-  const dim3 grid((unsigned)n_pairs, (unsigned)n_cache);
-  if (dtype == CAD_BF16)
-    hipLaunchKernelGGL((k_kv_copy<bf16_t>), grid, dim3(256), 0, s, (bf16_t*)k, (bf16_t*)v, cache_stride, hkv, hd,
-                       pairs);
-  else
-    hipLaunchKernelGGL((k_kv_copy<float>), grid, dim3(256), 0, s, (float*)k, (float*)v, cache_stride, hkv, hd, pairs);
-  return hipGetLastError();
 }
 
 // rows at most this many: one work-group per (row, KV group)
