@@ -316,11 +316,6 @@ cad_status splice_rows(cad_model* m, const cad_kv* kv, int64_t L, const int32_t*
                        int mode, const int32_t* limit, int32_t* argmax, int32_t* accepted, float* logits,
                        int32_t* dev_status, hipStream_t s);
 
-// copy cache slots between blocks of a paged pool at every cache index:
-// pairs (device) [n_pairs][4] = src block, dst block, first slot, end slot
-hipError_t launch_kv_copy(int dtype, void* k, void* v, int64_t cache_stride, int n_cache, int hkv, int hd,
-                          const int32_t* pairs, int n_pairs, hipStream_t s);
-
 // attention split: partitions of each query tile's key axis (cached keys up
 // to max L, then the span's own) so that small spans still fill the chip
 // (max_seq_rows: the most span rows any sequence of the call has)
