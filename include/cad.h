@@ -298,11 +298,16 @@ cad_status cad_loop_step(cad_model* m, const cad_kv* kv, int32_t n_groups, const
  * neither (a correction block follows).  The host reads decisions back after every tick
  * that reads a block out (and after each proposal): this call synchronises
  * its stream.  cad_loop_create allocates the pipeline's device buffers (the
- * residual streams of loop_depth x (max_copy + 1) rows, a device history of
- * max_len tokens) and pinned host staging; the model's max_tokens bounds the
- * rows per tick and the prefill chunk.  max_len and the block table must
- * hold L0 + n_new + loop_depth x (max_copy + 1) positions.  The KV cache is
- * overwritten from position 0. */
+ * residual streams of loop_depth x (max_copy + 1) rows -- twice that with
+ * branching --, a device history of max_len tokens -- four with branching:
+ * the two lines' and a possible second child's per line -- and with
+ * branching a two-row block table of ceil(max_len / 16) entries per row)
+ * and pinned host staging; the model's max_tokens bounds the rows per tick
+ * and the prefill chunk.  max_len and block-table row 0 must hold L0 + n_new
+ * + loop_depth x (max_copy + 1) positions; with branching the caller's
+ * table has two rows (the first spare entries of row 1 as above, in the
+ * pool, distinct and not in row 0's first blocks; checked on the host).  The
+ * KV cache is overwritten from position 0 (the spare blocks too). */
 typedef struct cad_loop cad_loop;
 typedef struct {
   int32_t screen_depth;  /* ds, 1 <= ds < loop_depth */
