@@ -27,8 +27,8 @@
 * ``cad_loop_decode`` with second-readout branching (CopyLoop §A.2): on the
   fp32 tiny block applied 4 or 6 times, weights scaled by 0.3, 0.5 and 1.0,
   seeded uniform prompts of 40 ids chosen so that forks are made, kept and
-  lost (one case) and every decision the oracle takes has a margin above
-  1e-3: the committed tokens and every counter, fork counters included,
+  lost (one case), one of them without context copies (K = 0), and every
+  decision the oracle takes has a margin above 1e-3: the committed tokens and every counter, fork counters included,
   equal ``oracle.copyloop_branch_decode``'s, and the cache the decoder
   leaves holds a clean forward's K/V for every fed committed position at
   every depth (1e-4), the second line's states copied back where it was
@@ -278,6 +278,7 @@ BRANCH_CASES = {
     "scale1": (1.0, 4, 1, 3, 8, 24, 1),       # 14 forks, 8 kept
     "lost": (1.0, 4, 2, 3, 8, 24, 1),         # 10 forks, 7 kept, 1 lost
     "depth6": (0.3, 6, 2, 4, 8, 24, 11),      # 4 forks, 2 kept
+    "no-copies": (0.5, 4, 1, 3, 0, 24, 2),    # K = 0: 19 forks, 12 kept (no proposals anywhere)
 }
 COUNTERS = ("ticks", "rows_run", "blocks", "proposed", "screened_out", "rejected", "discarded", "committed",
             "forks", "forks_kept", "forks_lost", "fork_rows_dropped")
