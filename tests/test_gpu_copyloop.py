@@ -7,7 +7,9 @@
   buffer): a block taken through three ticks, then joined by a younger block
   at depth 0 and a third at depth 0 a tick later, with readouts along the
   way; the states, the readout logits and decisions and the K/V written at
-  every depth are compared with ``oracle.loop_step``.  The fp32 tiny block
+  every depth are compared with ``oracle.loop_step``.  Two groups at the
+  same positions through block-table rows 0 and 1 each match the oracle on
+  a cache of their own, and each row's blocks hold only their group's K/V.  The fp32 tiny block
   (1e-4 bar) and the bf16 looped shape (d 2048, 16 x 128 heads, FFN 5632, depth
   8; logits 2e-2, K/V 2e-2 plus half a bfloat16 spacing, argmax where the
   oracle's top-2 margin exceeds 0.1).
@@ -169,6 +171,53 @@ def test_loop_step_mixed_depths_looped_bf16():
     L = 1000
     kl, vl = synth.random_kv_logical(shape, L, seed=72, device=dev)
     _run_ticks(shape, W, W64, kl, vl, L, 2e-2, 0.1, dev)
+
+
+def test_loop_step_table_rows_keep_lines_apart():
+    """Two groups at the same positions and depth in one tick, the first
+    through block-table row 0, the second through row 1 (disjoint blocks
+    holding the same prefix): each group's readout equals the oracle's tick
+    on a cache of its own, and each row's blocks end up with exactly its own
+    group's K/V (a group written through the wrong row would mix them)."""
+    dev = _dev()
+    shape, Wt, Wn = _tiny_loop(0.3)
+    cfg = Config.of(shape)
+    W64 = _f64(Wn)
+    L = 40
+    nb = (L + 16 + BLK - 1) // BLK
+    table = torch.zeros((2, nb), dtype=torch.int32)
+    table[0] = torch.arange(nb, dtype=torch.int32)
+    table[1] = torch.arange(nb, 2 * nb, dtype=torch.int32).flip(0)   # other blocks, in another order
+    kv = cad.KVCache.alloc(shape, 2 * nb, table, device=dev)
+    kl, vl = synth.random_kv_logical(shape, L, seed=71, device=dev)
+    H.write_prefix(kv, kl, vl, seq=0)
+    H.write_prefix(kv, kl, vl, seq=1)
+    model = cad.cad_model_create(shape, _to(Wt, dev), max_tokens=16)
+    toks = [[7, 900, 31], [15, 15]]
+    groups = [(L, 3, 0, 0, 1, 0), (L, 2, 0, 4, 1, 1)]
+    flat = toks[0] + toks[1]
+    state = torch.zeros((8, shape.d_model), dtype=torch.float32, device=dev)
+    am = torch.full((5,), -9, dtype=torch.int32, device=dev)
+    acc = torch.full((2,), -9, dtype=torch.int32, device=dev)
+    lg = torch.zeros((5, shape.vocab), dtype=torch.float32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    cad.cad_loop_step(model, kv, groups, H.tensors_i32(flat), state, None, am, acc, lg, status)
+    torch.cuda.synchronize()
+    assert int(status[0]) == 0
+    lg = lg.cpu().numpy()
+    kl64, vl64 = kl.double().cpu().numpy(), vl.double().cpu().numpy()
+    r0 = 0
+    for gi, (t, g) in enumerate(zip(toks, groups)):
+        okv = KVCache.from_prefix(kl64, vl64, L + 16)
+        ref = oracle.loop_step(cfg, W64, okv, [dict(pos=g[0], rows=g[1], depth=0, state=0, readout=1)], t,
+                               np.zeros((4, shape.d_model)))[0]
+        n = g[1]
+        assert float(np.max(np.abs(lg[r0:r0 + n] - ref))) <= 1e-4, gi
+        gk, gv = H.read_span(kv, L, n, seq=gi)
+        assert float(np.max(np.abs(gk[0] - okv.k[0][:, L:L + n]))) <= 1e-4, gi
+        assert float(np.max(np.abs(gv[0] - okv.v[0][:, L:L + n]))) <= 1e-4, gi
+        r0 += n
+    cad.cad_model_destroy(model)
 
 
 # ---------------------------------------------------------------------------
