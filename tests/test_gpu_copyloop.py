@@ -333,7 +333,9 @@ BRANCH_CASES = {
     "lost": (1.0, 4, 2, 3, 8, 24, 1),         # 10 forks, 7 kept, 1 lost
     "depth6": (0.3, 6, 2, 4, 8, 24, 11),      # 4 forks, 2 kept
     "no-copies": (0.5, 4, 1, 3, 0, 24, 2),    # K = 0: 19 forks, 12 kept (no proposals anywhere)
+    "rows1": (1.0, 4, 1, 3, 8, 1, 3),         # one row in flight: no tails, never room for a second child
 }
+NO_ROOM = {"rows1"}
 COUNTERS = ("ticks", "rows_run", "blocks", "proposed", "screened_out", "rejected", "discarded", "committed",
             "forks", "forks_kept", "forks_lost", "fork_rows_dropped")
 
@@ -359,7 +361,7 @@ def test_loop_decode_branching_matches_oracle(name, monkeypatch):
     want, st_ref = CL.copyloop_branch_decode(cfg, W64, KVCache.empty(D, 4, ocap, 64), prompt, n, ds, d2, K, max_rows)
     monkeypatch.undo()
     assert min(margins) > 1e-3, min(margins)
-    assert st_ref["forks"] > 0
+    assert (st_ref["forks"] == 0) == (name in NO_ROOM)
     if name == "lost":
         assert st_ref["forks_lost"] > 0 and st_ref["forks_kept"] > 0
     full = oracle.greedy_decode(cfg, W64, KVCache.empty(D, 4, ocap, 64), prompt, st_ref["committed"])

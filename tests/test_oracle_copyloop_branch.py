@@ -48,6 +48,7 @@ CASES = [  # scale, D, ds, d2, K, max_rows
     (0.3, 4, 1, 3, 8, 24), (0.3, 4, 2, 3, 8, 24), (0.3, 6, 2, 4, 8, 24),
     (0.5, 4, 1, 3, 8, 24), (0.5, 4, 2, 3, 4, 6), (1.0, 4, 1, 3, 8, 24), (1.0, 4, 1, 2, 8, 24),
     (1.0, 6, 2, 4, 3, 2),
+    (1.0, 4, 1, 3, 8, 1), (0.5, 4, 2, 3, 8, 1),   # one row in flight: no tails, no room for a second child
 ]
 
 
