@@ -25,7 +25,10 @@ Workloads (seeded, synthetic; the tiny fp32 model):
   later one: gen bodies end by the end-of-gen window after 20 ids, repeat
   (drafts are accepted, the window closes inside accepted drafts), and also
   end by the cap; the same model with "<" elsewhere on the cycle gives six
-  copies in a row.
+  copies in a row;
+* degenerate programs on the same models: at most one op (a copy; a gen
+  body that reaches the length cap), gen bodies capped at one id (mixed with
+  a copy; six in a row), and a stream limit of three ids.
 """
 import numpy as np
 import pytest
@@ -101,6 +104,12 @@ CASES = {
     "stream-limit": (1.0, {}, "lines", 6, 12, 40, 58),       # c8 c8 c8 g1 (stopped inside the body)
     "eog-window": (0.1, dict(CYCLE, lt=646), "lines", 6, 30, 512, 58),  # g20 g20 g30 g30 g30 g30
     "copies": (0.1, dict(CYCLE, lt=334), "lines", 6, 30, 512, 6),       # c7 x 6
+    # degenerate programs: one op allowed, one-id gen bodies, a stream limit inside the first template
+    "one-op": (1.0, {}, "lines", 1, 12, 512, 18),                       # c8
+    "one-op-gen": (0.1, dict(CYCLE, lt=646), "lines", 1, 30, 512, 18),  # g30 (the length cap)
+    "gen1-mixed": (1.0, {}, "lines", 6, 1, 512, 19),                    # g1 g1 g1 g1 c9 g1
+    "gen1-cycle": (0.1, dict(CYCLE, lt=646), "lines", 6, 1, 512, 67),   # g1 x 6
+    "stream3": (1.0, {}, "lines", 6, 12, 3, 19),                        # three ids: stopped inside a template
 }
 MARGIN = 2e-4   # twice the fp32 tiny model's logit bar (1e-4 absolute)
 
