@@ -24,7 +24,9 @@
  *     Nothing synchronises the host except create and destroy.
  *   - Argument errors are detected on the host, return a non-zero
  *     cad_status and enqueue nothing; cad_last_error() then describes the
- *     failure (thread-local string).  HIP launch failures return CAD_E_HIP.
+ *     failure (thread-local string).  HIP launch failures return CAD_E_HIP,
+ *     and so does a failed host allocation ("host allocation failed"): no
+ *     C++ exception leaves the library.
  *   - Data-dependent faults found on the device (token id outside the
  *     vocabulary, a mask row that allows nothing, a block-table entry outside
  *     the pool) are OR-ed into the optional `dev_status` word; the kernels

@@ -35,7 +35,10 @@ cad_status fail(cad_status s, const char* fmt, ...) {
   va_start(ap, fmt);
   vsnprintf(buf, sizeof buf, fmt, ap);
   va_end(ap);
-  g_err = buf;
+  try {
+    g_err = buf;
+  } catch (...) {  // no room for the message: the status still reports the failure
+  }
   return s;
 }
 
@@ -458,7 +461,10 @@ int64_t one_row_split_floats(const cad_config& c) {
 
 namespace cad {
 cad_status set_error(cad_status s, const char* msg) {
-  g_err = msg;
+  try {
+    g_err = msg;
+  } catch (...) {  // no room for the message: the status still reports the failure
+  }
   return s;
 }
 
@@ -492,7 +498,7 @@ extern "C" {
 
 const char* cad_last_error(void) { return g_err.c_str(); }
 
-cad_status cad_model_create(const cad_config* cfg, const cad_weights* w, cad_model** out) {
+cad_status cad_model_create(const cad_config* cfg, const cad_weights* w, cad_model** out) try {
   if (!out) return fail(CAD_E_ARG, "out is NULL");
   *out = nullptr;
   cad_status st = check_config(cfg);
@@ -509,6 +515,11 @@ cad_status cad_model_create(const cad_config* cfg, const cad_weights* w, cad_mod
         !ok_ptr(w->w_gate_up[i]) || !ok_ptr(w->w_down[i]))
       return fail(CAD_E_ARG, "layer %d weight pointer NULL or misaligned", i);
 
+  // rotary frequencies theta^(-2i / hd), uploaded with the workspace
+  const int64_t hd = c.head_dim;
+  std::vector<double> fr(hd / 2);
+  for (int64_t i = 0; i < hd / 2; ++i) fr[i] = std::pow((double)c.rope_theta, -2.0 * (double)i / (double)hd);
+
   cad_model* m = new (std::nothrow) cad_model();
   if (!m) return fail(CAD_E_HIP, "host allocation failed");
   m->cfg = c;
@@ -516,15 +527,17 @@ cad_status cad_model_create(const cad_config* cfg, const cad_weights* w, cad_mod
   m->tok_embed = w->tok_embed;
   m->final_norm = w->final_norm;
   m->lm_head = w->lm_head;
-  for (int i = 0; i < c.n_layers; ++i) {
-    m->attn_norm.push_back(w->attn_norm[i]);
-    m->w_qkv.push_back(w->w_qkv[i]);
-    m->w_o.push_back(w->w_o[i]);
-    m->ffn_norm.push_back(w->ffn_norm[i]);
-    m->w_gate_up.push_back(w->w_gate_up[i]);
-    m->w_down.push_back(w->w_down[i]);
+  try {
+    m->attn_norm.assign(w->attn_norm, w->attn_norm + c.n_layers);
+    m->w_qkv.assign(w->w_qkv, w->w_qkv + c.n_layers);
+    m->w_o.assign(w->w_o, w->w_o + c.n_layers);
+    m->ffn_norm.assign(w->ffn_norm, w->ffn_norm + c.n_layers);
+    m->w_gate_up.assign(w->w_gate_up, w->w_gate_up + c.n_layers);
+    m->w_down.assign(w->w_down, w->w_down + c.n_layers);
+  } catch (...) {
+    delete m;
+    throw;
   }
-  const int64_t hd = c.head_dim;
   const int64_t split_floats = c.dtype == CAD_BF16 ? GEMM_SPLIT_FLOATS : 0;
   const size_t o_freq = layout_workspace(c, c.max_tokens, CAD_MAX_SEQS, split_floats, nullptr, nullptr);
   const size_t bytes = o_freq + align_up(hd / 2 * 8);
@@ -544,8 +557,6 @@ cad_status cad_model_create(const cad_config* cfg, const cad_weights* w, cad_mod
     return st;
   }
   m->freq = (double*)((char*)m->ws + o_freq);
-  std::vector<double> fr(hd / 2);
-  for (int64_t i = 0; i < hd / 2; ++i) fr[i] = std::pow((double)c.rope_theta, -2.0 * (double)i / (double)hd);
   e = hipMemcpy(m->freq, fr.data(), fr.size() * 8, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
@@ -555,6 +566,9 @@ cad_status cad_model_create(const cad_config* cfg, const cad_weights* w, cad_mod
   }
   *out = m;
   return CAD_OK;
+} catch (...) {
+  // host containers and messages are C++: nothing they throw crosses the C ABI
+  return cad::set_error(CAD_E_HIP, "host allocation failed");
 }
 
 void cad_model_destroy(cad_model* m) {
@@ -568,22 +582,28 @@ void cad_model_destroy(cad_model* m) {
 cad_status cad_splice_forward(cad_model* m, const cad_kv* kv, int64_t L, const int32_t* span,
                               int32_t N, const uint32_t* mask, cad_mode mode, int32_t* argmax,
                               int32_t* accepted, float* logits, int32_t* dev_status,
-                              cad_stream stream) {
+                              cad_stream stream) try {
   return cad::splice_rows(m, kv, L, span, N, mask, mode, nullptr, argmax, accepted, logits, dev_status,
                           (hipStream_t)stream);
+} catch (...) {
+  // host containers and messages are C++: nothing they throw crosses the C ABI
+  return cad::set_error(CAD_E_HIP, "host allocation failed");
 }
 
 cad_status cad_decode_step(cad_model* m, const cad_kv* kv, int64_t L, const int32_t* token,
                            const uint32_t* mask_row, int32_t* argmax, float* logits,
-                           int32_t* dev_status, cad_stream stream) {
+                           int32_t* dev_status, cad_stream stream) try {
   if (!m) return fail(CAD_E_ARG, "model is NULL");
   return cad_splice_forward(m, kv, L, token, 1, mask_row, CAD_COMMIT, argmax, m->w->survivors, logits,
                             dev_status, stream);
+} catch (...) {
+  // host containers and messages are C++: nothing they throw crosses the C ABI
+  return cad::set_error(CAD_E_HIP, "host allocation failed");
 }
 
 cad_status cad_decode_step_noalloc(cad_model* m, const cad_kv* kv, int64_t L, const int32_t* token,
                                    const uint32_t* mask_row, int32_t* argmax, float* logits, int32_t* dev_status,
-                                   cad_stream stream) {
+                                   cad_stream stream) try {
   if (!m) return fail(CAD_E_ARG, "model is NULL");
   void* base = nullptr;
   cad_status st = scratch_of_current_device(&base);
@@ -605,13 +625,16 @@ cad_status cad_decode_step_noalloc(cad_model* m, const cad_kv* kv, int64_t L, co
   m->w = &m->main;
   m->prof_mask = prof;
   return st;
+} catch (...) {
+  // host containers and messages are C++: nothing they throw crosses the C ABI
+  return cad::set_error(CAD_E_HIP, "host allocation failed");
 }
 
 cad_status cad_splice_forward_batched(cad_model* m, const cad_kv* kv, int32_t n_seq,
                                       const int64_t* seq_L, const int32_t* offsets,
                                       const int32_t* spans, const uint32_t* mask, cad_mode mode,
                                       int32_t* argmax, int32_t* accepted, float* logits,
-                                      int32_t* dev_status, cad_stream stream) {
+                                      int32_t* dev_status, cad_stream stream) try {
   cad_status st = check_common(m, kv, spans, argmax, accepted, logits, mode);
   if (st != CAD_OK) return st;
   if (m->cfg.loop_depth > 1) return fail(CAD_E_ARG, "looped model: use cad_splice_forward_looped");
@@ -640,13 +663,16 @@ cad_status cad_splice_forward_batched(cad_model* m, const cad_kv* kv, int32_t n_
   st = run_blocks(m, kv, rm, 0, c.n_layers, nullptr, dev_status, s);
   if (st != CAD_OK) return st;
   return readout(m, rm, logits, mask, spans, mode, nullptr, argmax, accepted, dev_status, s);
+} catch (...) {
+  // host containers and messages are C++: nothing they throw crosses the C ABI
+  return cad::set_error(CAD_E_HIP, "host allocation failed");
 }
 
 cad_status cad_splice_forward_looped(cad_model* m, const cad_kv* kv, int64_t L,
                                      const int32_t* span, int32_t N, int32_t screen_depth,
                                      const uint32_t* mask, int32_t* screen_argmax,
                                      int32_t* survivors, int32_t* argmax, int32_t* accepted,
-                                     float* logits, int32_t* dev_status, cad_stream stream) {
+                                     float* logits, int32_t* dev_status, cad_stream stream) try {
   cad_status st = check_common(m, kv, span, argmax, accepted, logits, CAD_VERIFY);
   if (st != CAD_OK) return st;
   const cad_config& c = m->cfg;
@@ -672,12 +698,15 @@ cad_status cad_splice_forward_looped(cad_model* m, const cad_kv* kv, int64_t L,
   st = run_blocks(m, kv, rm, screen_depth, c.loop_depth, survivors, dev_status, s);
   if (st != CAD_OK) return st;
   return readout(m, rm, logits, mask, span, CAD_VERIFY, survivors, argmax, accepted, dev_status, s);
+} catch (...) {
+  // host containers and messages are C++: nothing they throw crosses the C ABI
+  return cad::set_error(CAD_E_HIP, "host allocation failed");
 }
 
 cad_status cad_loop_step(cad_model* m, const cad_kv* kv, int32_t n_groups, const cad_loop_group* groups,
                          const int32_t* tokens, float* state, int32_t state_rows, const uint32_t* mask,
                          int32_t* argmax, int32_t* accepted, float* logits, int32_t* dev_status,
-                         cad_stream stream) {
+                         cad_stream stream) try {
   if (!m) return fail(CAD_E_ARG, "model is NULL");
   const cad_config& c = m->cfg;
   if (c.loop_depth < 2) return fail(CAD_E_ARG, "model is not looped (loop_depth < 2)");
@@ -729,9 +758,12 @@ cad_status cad_loop_step(cad_model* m, const cad_kv* kv, int32_t n_groups, const
   m->x_parts = 0;
   if (!any_readout) return CAD_OK;
   return readout(m, rm, logits, mask, tokens, CAD_VERIFY, nullptr, argmax, accepted, dev_status, s);
+} catch (...) {
+  // host containers and messages are C++: nothing they throw crosses the C ABI
+  return cad::set_error(CAD_E_HIP, "host allocation failed");
 }
 
-cad_status cad_profile_enable(cad_model* m, int32_t family_mask) {
+cad_status cad_profile_enable(cad_model* m, int32_t family_mask) try {
   if (!m) return fail(CAD_E_ARG, "model is NULL");
   if (family_mask) {
     HIP_TRY(hipDeviceSynchronize());
@@ -740,9 +772,12 @@ cad_status cad_profile_enable(cad_model* m, int32_t family_mask) {
   }
   m->prof_mask = (uint32_t)family_mask & ((1u << PF_COUNT) - 1u);
   return CAD_OK;
+} catch (...) {
+  // host containers and messages are C++: nothing they throw crosses the C ABI
+  return cad::set_error(CAD_E_HIP, "host allocation failed");
 }
 
-cad_status cad_profile_read(cad_model* m, const char* family, int64_t* launches, double* total_ms) {
+cad_status cad_profile_read(cad_model* m, const char* family, int64_t* launches, double* total_ms) try {
   if (!m || !family || !launches || !total_ms) return fail(CAD_E_ARG, "NULL argument");
   int f = -1;
   for (int i = 0; i < PF_COUNT; ++i)
@@ -761,11 +796,14 @@ cad_status cad_profile_read(cad_model* m, const char* family, int64_t* launches,
   *launches = n;
   *total_ms = ms;
   return CAD_OK;
+} catch (...) {
+  // host containers and messages are C++: nothing they throw crosses the C ABI
+  return cad::set_error(CAD_E_HIP, "host allocation failed");
 }
 
 cad_status cad_propose_suffix_match(const int32_t* tokens, int64_t T, int32_t max_ngram,
                                     int32_t min_ngram, int32_t K, int32_t* out_tokens,
-                                    int32_t* out_len, int64_t* out_pos, cad_stream stream) {
+                                    int32_t* out_len, int64_t* out_pos, cad_stream stream) try {
   if (T < 0) return fail(CAD_E_ARG, "negative history length");
   if (T > 0 && !tokens) return fail(CAD_E_ARG, "tokens is NULL");
   if (!out_tokens || !out_len || !out_pos) return fail(CAD_E_ARG, "output pointer is NULL");
@@ -775,6 +813,9 @@ cad_status cad_propose_suffix_match(const int32_t* tokens, int64_t T, int32_t ma
   HIP_TRY(launch_suffix_match(tokens, T, max_ngram, min_ngram, K, out_tokens, out_len, out_pos,
                               (hipStream_t)stream));
   return CAD_OK;
+} catch (...) {
+  // host containers and messages are C++: nothing they throw crosses the C ABI
+  return cad::set_error(CAD_E_HIP, "host allocation failed");
 }
 
 }  // extern "C"

@@ -764,7 +764,7 @@ struct Run {
 
 extern "C" {
 
-cad_status cad_loop_create(cad_model* m, int64_t max_len, const cad_loop_params* p, cad_loop** out) {
+cad_status cad_loop_create(cad_model* m, int64_t max_len, const cad_loop_params* p, cad_loop** out) try {
   if (!out) return loop_fail(CAD_E_ARG, "out is NULL");
   *out = nullptr;
   if (!m || !p) return loop_fail(CAD_E_ARG, "model/params is NULL");
@@ -866,6 +866,9 @@ cad_status cad_loop_create(cad_model* m, int64_t max_len, const cad_loop_params*
   lp->h_pairs = branch ? (int32_t*)(h + h_pairs) : nullptr;
   *out = lp;
   return CAD_OK;
+} catch (...) {
+  // host containers and messages are C++: nothing they throw crosses the C ABI
+  return cad::set_error(CAD_E_HIP, "host allocation failed");
 }
 
 void cad_loop_destroy(cad_loop* lp) {
@@ -880,7 +883,7 @@ void cad_loop_destroy(cad_loop* lp) {
 }
 
 cad_status cad_loop_decode(cad_loop* lp, const cad_kv* kv, const int32_t* prompt, int64_t L0, int32_t n_new,
-                           int32_t* out_tokens, cad_loop_stats* stats, cad_stream stream) {
+                           int32_t* out_tokens, cad_loop_stats* stats, cad_stream stream) try {
   if (!lp || !kv || !prompt || !out_tokens) return loop_fail(CAD_E_ARG, "NULL argument");
   if (L0 < 1 || n_new < 1) return loop_fail(CAD_E_ARG, "need a prompt and at least one new token");
   const int64_t need = L0 + n_new + (int64_t)lp->cfg.loop_depth * lp->slot_rows;
@@ -897,6 +900,9 @@ cad_status cad_loop_decode(cad_loop* lp, const cad_kv* kv, const int32_t* prompt
   const cad_status r = run.decode(prompt, L0, n_new, out_tokens, need);
   if (stats) *stats = run.st;
   return r;
+} catch (...) {
+  // host containers and messages are C++: nothing they throw crosses the C ABI
+  return cad::set_error(CAD_E_HIP, "host allocation failed");
 }
 
 }  // extern "C"

@@ -170,7 +170,7 @@ void cad_program_destroy(cad_program* pr) {
 }
 
 cad_status cad_program_create(cad_model* m, int64_t max_len, const cad_program_table* t,
-                              const cad_program_params* p, cad_program** out) {
+                              const cad_program_params* p, cad_program** out) try {
   if (!out) return prog_fail(CAD_E_ARG, "out is NULL");
   *out = nullptr;
   if (!m || !t || !p) return prog_fail(CAD_E_ARG, "model/table/params is NULL");
@@ -247,12 +247,15 @@ cad_status cad_program_create(cad_model* m, int64_t max_len, const cad_program_t
   }
   *out = pr;
   return CAD_OK;
+} catch (...) {
+  // host containers and messages are C++: nothing they throw crosses the C ABI
+  return cad::set_error(CAD_E_HIP, "host allocation failed");
 }
 
 cad_status cad_program_decode(cad_program* pr, const cad_kv* kv, const int32_t* prompt, int64_t L0,
                               const int32_t* doc, int32_t doc_n, const int32_t* line_start, int32_t n_lines,
                               int32_t unit_tokens, int32_t* stream_out, int32_t stream_cap, int32_t* ops_out,
-                              int32_t* out, int32_t out_cap, cad_program_stats* stats, cad_stream stream) {
+                              int32_t* out, int32_t out_cap, cad_program_stats* stats, cad_stream stream) try {
   if (!pr || !kv || !prompt || !doc || !stats || !stream_out || !ops_out || !out)
     return prog_fail(CAD_E_ARG, "NULL argument");
   const cad_program_params& p = pr->p;
@@ -378,6 +381,9 @@ cad_status cad_program_decode(cad_program* pr, const cad_kv* kv, const int32_t* 
     return prog_fail(CAD_E_CAPACITY, fmt("results longer than their buffers (stream %lld, output %lld)", h.stream_n,
                                          h.out_n));
   return CAD_OK;
+} catch (...) {
+  // host containers and messages are C++: nothing they throw crosses the C ABI
+  return cad::set_error(CAD_E_HIP, "host allocation failed");
 }
 
 }  // extern "C"
