@@ -49,8 +49,10 @@
 // the second line's K/V are then copied into row 0's blocks and its history
 // becomes the history -- or neither (a correction block follows).  At most
 // one fork is live; it needs its parent's first child in flight, a free row
-// and a free slot.  The second line's waiting heads are proposed when they
-// are admitted (one synchronisation each).
+// and a free slot.  The second line's screened successors and the second
+// child itself are proposed on the device after the tick like the first
+// line's (the child's history is copied from its line's, with the depth-d2
+// head written after it).
 #include <algorithm>
 #include <cstring>
 #include <deque>
