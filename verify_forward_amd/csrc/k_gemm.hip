@@ -21,11 +21,10 @@
 //   * tiled (M > 16): a work-group of eight waves owns 256 weight rows and
 //     256 (or 128) activation rows; each wave computes all 256 weight rows
 //     against its own 32 (or 16) activation rows.  The weight tile is the
-//     only operand that goes through LDS (three buffers, k steps of 32, or
+//     only operand that goes through LDS (four stages, k steps of 32, or
 //     64 for the 128-row tiles, loaded three steps ahead into registers);
-//     each wave loads its
-//     activation fragments (both planes) straight into registers two steps
-//     ahead.  LDS traffic per
+//     each wave loads its activation fragments (both planes) straight into
+//     registers two steps ahead.  LDS traffic per
 //     multiply-add is then set by the weights alone, which keeps the LDS
 //     port (128 B/clk/CU) below the matrix-core rate.  When the output has
 //     too few tiles to occupy the 256 compute units, K is split over several
@@ -457,7 +456,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& a, int n_tn, int
   constexpr int WLDK = TKK + 8;                 // LDS row stride of a weight stage (80 or 144 bytes: the 16 rows of a fragment read hit distinct banks)
   constexpr int WCH = (TN * CPR + NT - 1) / NT;  // 16-byte weight chunks per thread per k step
   static_assert(TN % 32 == 0, "whole gate/up block pairs");
-  __shared__ __attribute__((aligned(16))) bf16_t sw[3][TN * WLDK];
+  __shared__ __attribute__((aligned(16))) bf16_t sw[4][TN * WLDK];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, i16 = lane & 15;
@@ -554,17 +553,35 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& a, int n_tn, int
         }
       }
     }
+    // issue order: each weight fragment is read from LDS two fragments
+    // ahead of the products that use it, so one wave's LDS latency hides
+    // behind its own products (left to itself the compiler reads a pair
+    // and waits on it at once; gate/up at N = 512 -5 %)
+    constexpr int PF = MB * (F16A ? 1 : 2), NF = NB * KH, LA = 2;
+    __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);  // LDS reads
+#pragma unroll
+    for (int i = 0; i < NF - LA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);  // matrix-core products
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, PF * LA, 0);
   };
 
   const int nk = a.K / TKK;
   const int kt0 = (int)((int64_t)nk * sp / splits), kt1 = (int)((int64_t)nk * (sp + 1) / splits);
   auto cl = [&](int kt) { return min(kt, kt1 - 1); };  // past the end: load the last step again (never used)
-  // Pipeline over three LDS buffers and three register buffers per operand:
+  // Pipeline over four LDS stages and three register buffers per operand:
   // the weights of step j are loaded at the start of step j - 3 into rw[j%3]
-  // and written to LDS buffer j%3 at the end of step j - 2; the activations
-  // of step j are loaded at the start of step j - 2 into ra[j%3].  The
-  // prologue issues its loads in the order the loop does, so the loop is
-  // entered with the same loads in flight as it is re-entered.
+  // and written to LDS stage j%4 at the end of step j - 2; the activations
+  // of step j are loaded at the start of step j - 2 into ra[j%3].  Stage
+  // (r + 2) % 4, written at the end of step r (counted from the split's
+  // first step), was last read at step r - 2, so one barrier after every
+  // odd step keeps both orders: every wave has left step r - 2 before any
+  // wave writes at the end of step r, and a stage written at the end of
+  // step r is read at step r + 2 after a barrier (half the barriers of
+  // three stages: gate/up at N = 512 -2 %).  The prologue issues its loads
+  // in the order the loop does, so the loop is entered with the same loads
+  // in flight as it is re-entered.
   u32x4 rw0[WCH], rw1[WCH], rw2[WCH], ra0[MB][2 * KH], ra1[MB][2 * KH], ra2[MB][2 * KH];
   wload(rw0, kt0);
   wload(rw1, cl(kt0 + 1));
@@ -574,27 +591,27 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& a, int n_tn, int
   wstore(rw0, 0);
   wstore(rw1, 1);
   __syncthreads();
-#define CAD_GEMM_STEP(KT, U, RW_NEW, RA_NEW, RA_CUR, RW_OUT)   \
+#define CAD_GEMM_STEP(KT, RW_NEW, RA_NEW, RA_CUR, RW_OUT)     \
   wload(RW_NEW, cl((KT) + 3));                                  \
   aload(RA_NEW, cl((KT) + 2));                                  \
   __builtin_amdgcn_sched_barrier(0);                            \
-  compute(U, RA_CUR);                                           \
+  compute(((KT) - kt0) & 3, RA_CUR);                            \
   __builtin_amdgcn_sched_barrier(0);                            \
-  wstore(RW_OUT, ((U) + 2) % 3);                                \
-  __syncthreads();
+  wstore(RW_OUT, ((KT) - kt0 + 2) & 3);                         \
+  if (((KT) - kt0) & 1) __syncthreads();
   // three steps per iteration, no exit in between (every path back to the
   // loop head has the same loads in flight); up to two more steps after it
   int kt = kt0;
   for (; kt + 2 < kt1; kt += 3) {
-    CAD_GEMM_STEP(kt, 0, rw0, ra2, ra0, rw2)
-    CAD_GEMM_STEP(kt + 1, 1, rw1, ra0, ra1, rw0)
-    CAD_GEMM_STEP(kt + 2, 2, rw2, ra1, ra2, rw1)
+    CAD_GEMM_STEP(kt, rw0, ra2, ra0, rw2)
+    CAD_GEMM_STEP(kt + 1, rw1, ra0, ra1, rw0)
+    CAD_GEMM_STEP(kt + 2, rw2, ra1, ra2, rw1)
   }
   if (kt < kt1) {
-    CAD_GEMM_STEP(kt, 0, rw0, ra2, ra0, rw2)
+    CAD_GEMM_STEP(kt, rw0, ra2, ra0, rw2)
   }
   if (kt + 1 < kt1) {
-    CAD_GEMM_STEP(kt + 1, 1, rw1, ra0, ra1, rw0)
+    CAD_GEMM_STEP(kt + 1, rw1, ra0, ra1, rw0)
   }
 #undef CAD_GEMM_STEP
   // epilogue: acc[x][mb] lane -> weight rows 16x + 4g + r, activation row wrow0 + 16mb + i16
