@@ -179,8 +179,12 @@ __global__ void __launch_bounds__(NT) k_rmsnorm(float* __restrict__ x, const flo
       if (i4 < n4) *(f32x4*)(xr + 4 * i4) = v[j];
     }
   }
+  // groups past the row end hold clamped partial sums: they are neither
+  // stored nor counted
 #pragma unroll
-  for (int j = 0; j < V4; ++j) ss += v[j][0] * v[j][0] + v[j][1] * v[j][1] + v[j][2] * v[j][2] + v[j][3] * v[j][3];
+  for (int j = 0; j < V4; ++j)
+    if ((int)threadIdx.x + j * NT < n4)
+      ss += v[j][0] * v[j][0] + v[j][1] * v[j][1] + v[j][2] * v[j][2] + v[j][3] * v[j][3];
   ss = block_sum(ss, red);
   const float rs = 1.0f / sqrtf(ss / (float)d + eps);
 #pragma unroll
