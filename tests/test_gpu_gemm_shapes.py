@@ -11,7 +11,8 @@ the weight tiles end part-way through a tile (1216 QKV rows over 192-row
 tiles, 1088 over 256), and the gate/up projection splits K and leaves its
 sums to the reduce kernel.  The spans cover the weight-streaming path
 (5 rows), the 128-row tiles (40 rows) and the 256-row tiles (300 rows,
-two activation tiles, the second partial).
+two activation tiles, the second partial; and 200 rows on an empty cache,
+where attention sees only the span's own keys).
 
 "ragged-vocab": 2 layers, d_model 1152, 9 query heads of 128 over 3 KV
 heads, FFN 2240, vocab 1001: the LM head's last weight tile holds 9 ids
@@ -58,7 +59,7 @@ def edge_model(request):
     return shape, W, synth.weights_to_numpy(Wc)
 
 
-@pytest.mark.parametrize("L,N", [(300, 5), (300, 40), (211, 300)])
+@pytest.mark.parametrize("L,N", [(300, 5), (300, 40), (211, 300), (0, 200)])
 def test_edge_shapes(edge_model, L, N):
     SHAPE, W, Wn = edge_model
     cfg = Config.of(SHAPE)
