@@ -1,5 +1,6 @@
 """Test-side helpers for the GPU parity tests: moving caches between the
-oracle's logical layout and the library's paged layout, and building models.
+oracle's logical layout and the library's paged layout, building models, and
+masks under which the looped block's decisions have clear margins.
 
 The paged layout (include/cad.h): ``k [cache][block][Hkv][16][hd]`` and
 ``v [cache][block][Hkv][hd][16]``; token t of sequence b sits in block
@@ -8,6 +9,7 @@ The paged layout (include/cad.h): ``k [cache][block][Hkv][16][hd]`` and
 import numpy as np
 import torch
 
+import synth
 import verify_forward_amd as cad
 
 BLK = cad.CAD_KV_BLOCK
@@ -91,3 +93,29 @@ def kv_close_stored(a, b, tol):
     a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
     lim = np.maximum(tol, bf16_ulp(np.maximum(np.abs(a), np.abs(b))))
     return bool(np.all(np.abs(a - b) <= lim)), float(np.max(np.abs(a - b)))
+
+
+def clear_margin_mask(screen_logits, full_logits, gap):
+    """A per-position mask under which every masked decision of both
+    readouts has a top-2 margin of at least ``gap``, built from the oracle's
+    unmasked logits.  Row k allows its screening argmax a_s; its full-depth
+    argmax a_f too when the two readouts separate them by ``gap`` each way
+    (rows past ``full_logits`` have no full-depth readout); and every id at
+    least ``gap`` below the allowed leaders in both readouts.  The screening
+    argmax is unchanged by the mask, so the survivors are too."""
+    N, V = screen_logits.shape
+    allowed = np.zeros((N, V), dtype=bool)
+    for k in range(N):
+        s = screen_logits[k]
+        a_s = int(np.argmax(s))
+        lead = [a_s]
+        ok = s <= s[a_s] - gap
+        if k < len(full_logits):
+            f = full_logits[k]
+            a_f = int(np.argmax(f))
+            if a_f != a_s and s[a_s] - s[a_f] >= gap and f[a_f] - f[a_s] >= gap:
+                lead.append(a_f)
+            ok &= f <= max(f[i] for i in lead) - gap
+        allowed[k] = ok
+        allowed[k, lead] = True
+    return synth.pack_mask(allowed)

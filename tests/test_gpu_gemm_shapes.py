@@ -19,7 +19,10 @@ heads, FFN 2240, vocab 1001: the LM head's last weight tile holds 9 ids
 (the masked argmax candidates of a partial tile, at every path).
 
 In both, the mask of row 0 allows only the vocabulary's last six ids, so
-its argmax must come from the last weight tile.
+its argmax must come from the last weight tile.  The same shapes also run a
+batched call (five sequences of 1 to 130 rows over a shuffled pool), and
+the odd-steps widths a looped block (applied 3 times, screened at depth 1
+or 2).
 
 Bars: logits max|diff| <= 2e-2 (bf16 models); appended K/V within the same
 bound; argmax bit-exact where the oracle's masked top-2 margin exceeds 0.1.
@@ -95,3 +98,123 @@ def test_edge_shapes(edge_model, L, N):
     ok_v, ev = H.kv_close(gv[:, :, L:], np.stack([okv.v[c][:, L:] for c in range(cfg.n_layers)]), TOL)
     print(f"  kv max|diff| = {ek:.3e} / {ev:.3e}", flush=True)
     assert ok_k and ok_v
+
+
+def test_edge_shapes_batched(edge_model):
+    """A batched call at the edge shapes: five sequences over one shuffled
+    pool, a one-token step on a one-key cache, copies of 40 and 130 rows, a
+    7-row copy and a one-token step on a 300-key cache; every sequence
+    against its own oracle splice."""
+    SHAPE, W, Wn = edge_model
+    cfg = Config.of(SHAPE)
+    Ls = [1, 17, 211, 64, 300]
+    Ns = [1, 40, 7, 130, 1]
+    prompt = synth.make_line_prompt(512, SHAPE.vocab, seed=13)
+    spans = [synth.pick_span(prompt, n) for n in Ns]
+    offsets = np.concatenate([[0], np.cumsum(Ns)]).astype(np.int32)
+    total = int(offsets[-1])
+    mask = synth.banned_ids_mask(total, SHAPE.vocab, 64, seed=3)
+    need = [(L + n + BLK - 1) // BLK for L, n in zip(Ls, Ns)]
+    pool = int(sum(need)) + 3
+    perm = synth.shuffled_block_table(pool, pool, seed=21).numpy()
+    table = np.full((len(Ls), max(need)), -1, dtype=np.int32)
+    used = 0
+    for b, nb in enumerate(need):
+        table[b, :nb] = perm[used:used + nb]
+        used += nb
+    kv = cad.KVCache.alloc(SHAPE, pool, torch.from_numpy(table), device="cuda")
+    pre = []
+    for b, L in enumerate(Ls):
+        kl, vl = synth.random_kv_logical(SHAPE, L, seed=60 + b, device="cpu")
+        H.write_prefix(kv, kl.cuda(), vl.cuda(), seq=b)
+        pre.append((kl, vl))
+    model = cad.cad_model_create(SHAPE, W, max_tokens=total)
+    o = H.outputs(total, SHAPE.vocab, n_seq=len(Ls))
+    cad.cad_splice_forward_batched(model, kv, Ls, offsets, H.tensors_i32(np.concatenate(spans)),
+                                   torch.from_numpy(mask.view(np.int32)).cuda(), cad.CAD_VERIFY,
+                                   o["argmax"], o["accepted"], o["logits"], o["status"])
+    torch.cuda.synchronize()
+    cad.cad_model_destroy(model)
+    assert int(o["status"][0]) == 0
+    lg, am = o["logits"].cpu().numpy(), o["argmax"].cpu().numpy()
+    graded = 0
+    for b, (L, n) in enumerate(zip(Ls, Ns)):
+        s0, s1 = int(offsets[b]), int(offsets[b + 1])
+        kl, vl = pre[b]
+        okv = KVCache.from_prefix(kl.double().numpy(), vl.double().numpy(), L + n)
+        ref = oracle.splice(cfg, Wn, okv, L, spans[b])
+        err = float(np.max(np.abs(lg[s0:s1] - ref)))
+        print(f"{SHAPE.name} seq {b}: L={L} N={n} logits max|diff| {err:.3e}", flush=True)
+        assert err <= TOL
+        sure = oracle.top2_margin(ref, mask[s0:s1]) > MARGIN
+        graded += int(sure.sum())
+        assert np.array_equal(am[s0:s1][sure], oracle.masked_argmax(ref, mask[s0:s1])[sure])
+        gk, gv = H.read_seq(kv, L + n, seq=b)
+        ok_k, _ = H.kv_close(gk[:, :, L:], np.stack([okv.k[c][:, L:] for c in range(cfg.n_layers)]), TOL)
+        ok_v, _ = H.kv_close(gv[:, :, L:], np.stack([okv.v[c][:, L:] for c in range(cfg.n_layers)]), TOL)
+        assert ok_k and ok_v
+    assert graded > 0
+
+
+def _depth_chain(cfg, Wn, kl, vl, L, head, n, depth):
+    """The oracle's greedy chain at readout depth ``depth`` from ``head``."""
+    chain = KVCache.from_prefix(kl.double().numpy(), vl.double().numpy(), L + n)
+    span = [head]
+    for j in range(n - 1):
+        lg = oracle.decode_step(cfg, Wn, chain, L + j, span[j], depth=depth)[None]
+        span.append(int(oracle.masked_argmax(lg, None)[0]))
+    return np.asarray(span, dtype=np.int32)
+
+
+@pytest.mark.parametrize("N,ds,planted", [(9, 1, False), (40, 2, False), (40, 2, True)])
+def test_edge_shape_looped(N, ds, planted):
+    """The looped path at the odd-steps widths (one block applied 3 times):
+    screening at depth ds, then the survivors at full depth, under a mask
+    built from the oracle's own logits so that every decision has a 0.5
+    margin; screening argmax, survivors, full-depth logits, argmax and
+    acceptance against the oracle.  40 rows put the block on the 128-row
+    tiles; the planted span is the oracle's own depth-ds greedy chain, so
+    every row survives screening and all 40 go to full depth."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    shape = SHAPES["odd-steps"].replace(name="odd-steps-loop3", n_layers=1, loop_depth=3)
+    cfg = Config.of(shape)
+    Wc = synth.make_weights(shape, seed=synth.SEED_WEIGHTS, device="cpu")
+    W = {k: (v.cuda() if torch.is_tensor(v) else [{n: t.cuda() for n, t in lw.items()} for lw in v])
+         for k, v in Wc.items()}
+    Wn = synth.weights_to_numpy(Wc)
+    L = 300
+    kl, vl = synth.random_kv_logical(shape, L, seed=77, device="cpu")
+    if planted:
+        span = _depth_chain(cfg, Wn, kl, vl, L, 29, N, ds)
+    else:
+        span = synth.pick_span(synth.make_line_prompt(512, shape.vocab, seed=17), N)
+    kl64, vl64 = kl.double().numpy(), vl.double().numpy()
+    res0 = oracle.looped_splice(cfg, Wn, KVCache.from_prefix(kl64, vl64, L + N), L, span, ds)
+    mask = H.clear_margin_mask(res0["screen_logits"], res0["logits"], 0.5)
+    res = oracle.looped_splice(cfg, Wn, KVCache.from_prefix(kl64, vl64, L + N), L, span, ds, mask)
+    m = res["survivors"]
+    assert m == res0["survivors"]
+    if planted:
+        assert m == N
+    nb = (L + N + BLK - 1) // BLK
+    kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device="cuda")
+    H.write_prefix(kv, kl.cuda(), vl.cuda())
+    model = cad.cad_model_create(shape, W, max_tokens=N)
+    sa = torch.full((N,), -9, dtype=torch.int32, device="cuda")
+    sv = torch.full((1,), -9, dtype=torch.int32, device="cuda")
+    o = H.outputs(N, shape.vocab)
+    cad.cad_splice_forward_looped(model, kv, L, H.tensors_i32(span), ds,
+                                  torch.from_numpy(mask.view(np.int32).copy()).cuda(), sa, sv, o["argmax"],
+                                  o["accepted"], o["logits"], o["status"])
+    torch.cuda.synchronize()
+    cad.cad_model_destroy(model)
+    assert int(o["status"][0]) == 0
+    err = float(np.max(np.abs(o["logits"].cpu().numpy()[:m] - res["logits"])))
+    print(f"looped N={N} ds={ds}: survivors {int(sv[0])} (oracle {m}), full-depth logits of {m} rows "
+          f"max|diff| {err:.3e}", flush=True)
+    assert np.array_equal(sa.cpu().numpy(), res["screen_argmax"])
+    assert int(sv[0]) == m
+    assert err <= TOL
+    assert np.array_equal(o["argmax"].cpu().numpy(), res["argmax"])
+    assert int(o["accepted"][0]) == res["accepted"]

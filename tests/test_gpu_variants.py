@@ -164,32 +164,6 @@ def _looped_cache(shape, L, kl, vl, N, dev):
     return kv
 
 
-def _clear_margin_mask(screen_logits, full_logits, gap):
-    """A per-position mask under which every masked decision of both
-    readouts has a top-2 margin of at least ``gap``, built from the oracle's
-    unmasked logits.  Row k allows its screening argmax a_s; its full-depth
-    argmax a_f too when the two readouts separate them by ``gap`` each way
-    (rows past ``full_logits`` have no full-depth readout); and every id at
-    least ``gap`` below the allowed leaders in both readouts.  The screening
-    argmax is unchanged by the mask, so the survivors are too."""
-    N, V = screen_logits.shape
-    allowed = np.zeros((N, V), dtype=bool)
-    for k in range(N):
-        s = screen_logits[k]
-        a_s = int(np.argmax(s))
-        lead = [a_s]
-        ok = s <= s[a_s] - gap
-        if k < len(full_logits):
-            f = full_logits[k]
-            a_f = int(np.argmax(f))
-            if a_f != a_s and s[a_s] - s[a_f] >= gap and f[a_f] - f[a_s] >= gap:
-                lead.append(a_f)
-            ok &= f <= max(f[i] for i in lead) - gap
-        allowed[k] = ok
-        allowed[k, lead] = True
-    return synth.pack_mask(allowed)
-
-
 def _run_looped(model, shape, L, kl, vl, span, ds, mask, dev):
     N = len(span)
     kv = _looped_cache(shape, L, kl, vl, N, dev)
@@ -213,7 +187,7 @@ def _looped_case(looped_args, span, ds, label, tol=TOL, gap=0.5):
     N = len(span)
     kl64, vl64 = kl.double().cpu().numpy(), vl.double().cpu().numpy()
     res0 = oracle.looped_splice(cfg, W64, KVCache.from_prefix(kl64, vl64, L + N), L, span, ds)
-    mask = _clear_margin_mask(res0["screen_logits"], res0["logits"], gap)
+    mask = H.clear_margin_mask(res0["screen_logits"], res0["logits"], gap)
     res = oracle.looped_splice(cfg, W64, KVCache.from_prefix(kl64, vl64, L + N), L, span, ds, mask)
     m = res["survivors"]
     assert m == res0["survivors"]
