@@ -173,6 +173,21 @@ def test_loop_step_mixed_depths_looped_bf16():
     _run_ticks(shape, W, W64, kl, vl, L, 2e-2, 0.1, dev)
 
 
+def test_loop_step_mixed_depths_edge_width_bf16():
+    """The same ticks at widths that leave partial tiles and odd k-step
+    counts in every projection (d_model 1088, 17 query heads of 64 over one
+    KV head, FFN 2112), one block applied 4 times."""
+    dev = _dev()
+    shape = synth.Shape("edge-loop4", 1, 1088, 17, 1, 64, 2112, 4096, loop_depth=4)
+    Wc = synth.make_weights(shape, device="cpu")
+    L = 300
+    kl, vl = synth.random_kv_logical(shape, L, seed=73, device="cpu")
+    _run_ticks(shape, _to(Wc, dev), _f64({k: (v.double().numpy() if torch.is_tensor(v) else
+                                                [{n: t.double().numpy() for n, t in lw.items()} for lw in v])
+                                            for k, v in Wc.items()}),
+               kl.to(dev), vl.to(dev), L, 2e-2, 0.1, dev)
+
+
 def test_loop_step_table_rows_keep_lines_apart():
     """Two groups at the same positions and depth in one tick, the first
     through block-table row 0, the second through row 1 (disjoint blocks
