@@ -24,7 +24,8 @@ ignored once the kernel sources change).  ``cpu_baseline`` times the float64
 CPU oracle on a bounded sample of the same workload.  ``sweep`` reports the
 other span lengths of the same shape; the extras add the pages' s(N) sweep at
 L = 1024, the batched serve, the looped block, the 1B shape (flushed and
-unflushed) and achievable HBM and matrix-core references.  A device status
+unflushed), one GPU's share of the 7B shape at 8-way tensor parallelism, and
+achievable HBM and matrix-core references.  A device status
 other than 0 (a data fault in the timed calls) prints the line with an
 ``error`` and exits with status 3.
 """
@@ -614,6 +615,48 @@ def sweep_1b(reps=20, Ns=(1, 4, 8, 16, 64, 256), L=4096):
             "L": L, "rows": rows}
 
 
+def tp8_share_bench(reps=20, Ns=(1, 16, 128, 512), L=16384):
+    """One GPU's share of the 7B shape under 8-way tensor parallelism (one KV
+    head and its four query heads, FFN 1792, vocab 4000; 32 layers, the
+    residual stream full width), random-init bf16, L = 16384, span of N
+    tokens from a duplicated line, COMMIT, no mask: per-call HIP-event times.
+    The two all-reduces per layer that tensor parallelism adds (N x d_model
+    bf16 each) are not part of it: they are counted, not run."""
+    import torch
+    import synth
+    import verify_forward_amd as cad
+    shape = synth.LLAMA_7B_TP8
+    W = synth.make_weights(shape, device="cuda")
+    nb = (L + max(Ns) + 15) // 16
+    kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(synth.SEED_KV + 4)
+    for t in (kv.k, kv.v):
+        t.copy_(torch.randn(t.shape, generator=g, device="cuda", dtype=torch.float32).mul_(synth.kv_std(shape)))
+    model = cad.cad_model_create(shape, W, max_tokens=max(Ns))
+    prompt = synth.make_line_prompt(L, shape.vocab)
+    rows = []
+    for N in Ns:
+        span = torch.from_numpy(synth.pick_span(prompt, N).astype("int32")).cuda()
+        am = torch.empty(N, dtype=torch.int32, device="cuda")
+        acc = torch.empty(1, dtype=torch.int32, device="cuda")
+        fn = lambda: cad.cad_splice_forward(model, kv, L, span, None, cad.CAD_COMMIT, am, acc)
+        st = pct(call_times_ms(fn, reps))
+        ms = st["median_ms"]
+        b, f = forward_work(shape, N, L)
+        rows.append({"N": N, **st, "hbm_frac": round(b / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                     "mfma_frac": round(f / (ms * 1e-3) / (MFMA_PEAK_TFLOPS * 1e12), 4),
+                     "share_bytes": b, "allreduce_bytes_per_layer": 2 * N * shape.d_model * 2})
+        log(f"[bench] 7B TP-8 share N={N}: {ms} ms")
+    cad.cad_model_destroy(model)
+    del kv, W
+    torch.cuda.empty_cache()
+    return {"workload": "one GPU's share of the 7B shape at 8-way tensor parallelism (32 layers, d_model 4096, "
+                        "4 q / 1 kv heads x 128, SwiGLU 1792, vocab 4000), random-init bf16, L=16384, span N from a "
+                        "duplicated line, COMMIT, no mask; the all-reduces are not run",
+            "L": L, "rows": rows}
+
+
 def matrix_core_reference():
     """Achievable matrix-core rate on this GPU: torch's (hipBLASLt) bf16 GEMM
     8192 x 8192 x 8192, TFLOP/s (a practical reference; the roofline peak
@@ -881,6 +924,7 @@ def main():
         log("[bench] looped done")
         out["copyloop_pipeline"] = copyloop_bench()
         out["llama_1b"] = sweep_1b()
+        out["tp8_share_7b"] = tp8_share_bench()
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, L, N)

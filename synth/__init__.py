@@ -69,7 +69,12 @@ TINY = Shape("tiny", 1, 256, 4, 4, 64, 1024, 1024, dtype="f32")
 LLAMA_1B = Shape("llama-1b", 16, 2048, 32, 8, 64, 8192, 32000)
 LLAMA_7B = Shape("llama-7b", 32, 4096, 32, 8, 128, 14336, 32000)
 LOOPED = Shape("looped-2b", 1, 2048, 16, 16, 128, 5632, 32000, loop_depth=8)
-SHAPES = {s.name: s for s in (TINY, LLAMA_1B, LLAMA_7B, LOOPED)}
+# one GPU's share of the 7B shape under 8-way tensor parallelism: one KV head
+# with its four query heads, an eighth of the FFN columns and of the
+# vocabulary (a vocabulary-split LM head); the residual stream stays d_model
+# wide on every GPU
+LLAMA_7B_TP8 = Shape("llama-7b-tp8-share", 32, 4096, 4, 1, 128, 1792, 4000)
+SHAPES = {s.name: s for s in (TINY, LLAMA_1B, LLAMA_7B, LOOPED, LLAMA_7B_TP8)}
 
 
 # ----------------------------------------------------------------------------

@@ -18,8 +18,13 @@ where attention sees only the span's own keys).
 heads, FFN 2240, vocab 1001: the LM head's last weight tile holds 9 ids
 (the masked argmax candidates of a partial tile, at every path).
 
-In both, the mask of row 0 allows only the vocabulary's last six ids, so
-its argmax must come from the last weight tile.  The same shapes also run a
+"tp8-share": two layers of one GPU's share of the 7B shape at 8-way tensor
+parallelism (d_model 4096, one KV head and its 4 query heads of 128, FFN
+1792, vocab 4000): attention and O projection 512 wide against a 4096-wide
+residual stream.
+
+In all three, the mask of row 0 allows only the vocabulary's last six ids,
+so its argmax must come from the last weight tile.  The same shapes also run a
 batched call (five sequences of 1 to 130 rows over a shuffled pool), and
 the odd-steps widths a looped block (applied 3 times, screened at depth 1
 or 2).
@@ -46,6 +51,7 @@ BLK = cad.CAD_KV_BLOCK
 SHAPES = {
     "odd-steps": synth.Shape("odd-steps", 2, 1088, 17, 1, 64, 2112, 4096),
     "ragged-vocab": synth.Shape("ragged-vocab", 2, 1152, 9, 3, 128, 2240, 1001),
+    "tp8-share": synth.LLAMA_7B_TP8.replace(name="tp8-share-2layer", n_layers=2),
 }
 
 
