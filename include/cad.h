@@ -64,6 +64,9 @@ typedef enum {
 #define CAD_DEV_BAD_TOKEN 1u  /* a span token is outside [0, vocab): its embedding row reads as zeros */
 #define CAD_DEV_EMPTY_MASK 2u /* a mask row allows no id: that argmax is -1 */
 #define CAD_DEV_BAD_BLOCK 4u  /* a block-table entry is outside [0, num_blocks): that K/V is skipped */
+#define CAD_DEV_F16_RANGE 8u  /* a value written at half precision for the matrix cores (q, the span's own
+                                 K/V, the down projection's input above 16 rows) exceeded 65504 and was
+                                 saturated: the results of that call are not reliable */
 
 #define CAD_KV_BLOCK 16       /* tokens per KV block */
 #define CAD_MAX_SEQS 64       /* sequences per batched call */

@@ -277,6 +277,36 @@ def test_short_bad_block_sets_status(model_w):
     assert int(o["status"][0]) & cad.CAD_DEV_BAD_BLOCK
 
 
+@pytest.mark.parametrize("which,scale,N", [("w_qkv", 1e6, 3), ("w_gate_up", 1e3, 40)])
+def test_half_range_sets_status(which, scale, N):
+    """Activations beyond half precision's range are saturated where they are
+    written at half precision and flag the call: q and the span's own K/V
+    (the QKV weights scaled by 1e6, any span length), and the SwiGLU output
+    that feeds the down projection as one half plane above 16 rows (the
+    gate/up weights scaled by 1e3, 40 rows).  The unscaled model leaves the
+    bit clear (every parity test asserts a zero status)."""
+    dev = _dev()
+    shape = SHAPES["gqa128"]
+    W = synth.make_weights(shape, seed=synth.SEED_WEIGHTS, device=dev)
+    for lw in W["layers"]:
+        lw[which].mul_(scale)
+    L = 100
+    kl, vl = _prefix(shape, L, seed=9, dev=dev)
+    nb = (L + N + BLK - 1) // BLK
+    kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device=dev)
+    H.write_prefix(kv, kl, vl)
+    model = cad.cad_model_create(shape, W, max_tokens=N)
+    o = H.outputs(N, shape.vocab)
+    span = synth.pick_span(synth.make_line_prompt(256, shape.vocab, seed=3), N)
+    cad.cad_splice_forward(model, kv, L, H.tensors_i32(span), None, cad.CAD_COMMIT, o["argmax"], o["accepted"],
+                           o["logits"], o["status"])
+    torch.cuda.synchronize()
+    cad.cad_model_destroy(model)
+    st = int(o["status"][0])
+    print(f"{which} x {scale:g}, N={N}: status {st}", flush=True)
+    assert st & cad.CAD_DEV_F16_RANGE
+
+
 def test_bad_token_sets_status(model_w):
     """A token id outside the vocabulary sets a status bit; its row is
     embedded as zeros (no table access out of range) and every output stays

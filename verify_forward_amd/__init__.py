@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libcad.so")
 CAD_F32, CAD_BF16 = 0, 1
 CAD_COMMIT, CAD_VERIFY = 0, 1
 CAD_OK, CAD_E_ARG, CAD_E_CAPACITY, CAD_E_UNSUPPORTED, CAD_E_HIP = 0, 1, 2, 3, 4
-CAD_DEV_BAD_TOKEN, CAD_DEV_EMPTY_MASK, CAD_DEV_BAD_BLOCK = 1, 2, 4
+CAD_DEV_BAD_TOKEN, CAD_DEV_EMPTY_MASK, CAD_DEV_BAD_BLOCK, CAD_DEV_F16_RANGE = 1, 2, 4, 8
 CAD_KV_BLOCK = 16
 CAD_MAX_SEQS = 64
 

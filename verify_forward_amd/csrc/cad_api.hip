@@ -354,6 +354,7 @@ cad_status run_blocks(cad_model* m, const cad_kv* kv, const RowMap& rm, int c0, 
     g.M = R; g.N = F; g.K = d; g.up_off = F; g.out_act = m->w->act;
     g.out_act_lo = act_f16 ? nullptr : lo_plane(m, m->w->act, F);
     g.act_f16 = act_f16;
+    g.status = dev_status;
     g.split_ws = m->w->split_ws; g.split_cap = m->w->split_cap;
     LAUNCH(PF_GATEUP, launch_gemm(c.dtype, GEMM_GATE_UP, g, s));
     g = GemmArgs{};

@@ -162,8 +162,11 @@ struct GemmArgs {
   float norm_eps;
   // bf16 models, more than 16 rows: the SWIGLU epilogue writes one half
   // plane (out_act as f16, no lo plane), and the down projection reads it
-  // (A is then a single half plane and the weights are widened to half)
+  // (A is then a single half plane and the weights are widened to half);
+  // a value beyond half's range is saturated and sets CAD_DEV_F16_RANGE in
+  // *status (when status is set)
   int act_f16;
+  int32_t* status;
   // EPI_ARGMAX: per-row vocabulary bitmask [M][mask_words] (bit v % 32 of
   // word v / 32 = id v allowed) or nullptr (all allowed); candidates
   // cand[c][M] as (fp32 value bits, id) pairs, id -1 when tile c allows

@@ -64,13 +64,21 @@ __device__ __forceinline__ void epi4(const GemmArgs& a, int m, int n, f32x4 c, f
   } else if (SPLIT && a.act_f16) {
     // one half plane (the down projection's operand on the tiled path)
     f16_t* o = (f16_t*)a.out_act + (int64_t)m * a.N + n;
+    float y[4];
+    bool big = false;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      y[r] = silu_mul(c[r], cu[r]);
+      big |= n + r < a.N && !(fabsf(y[r]) <= 65504.f);
+    }
+    if (big && a.status) atomicOr(a.status, (int32_t)CAD_DEV_F16_RANGE);
     if (n + 3 < a.N && ((a.N & 3) == 0)) {
-      const f16x2 h01 = {f2h(silu_mul(c[0], cu[0])), f2h(silu_mul(c[1], cu[1]))};
-      const f16x2 h23 = {f2h(silu_mul(c[2], cu[2])), f2h(silu_mul(c[3], cu[3]))};
+      const f16x2 h01 = {f2h(y[0]), f2h(y[1])};
+      const f16x2 h23 = {f2h(y[2]), f2h(y[3])};
       *(u32x2*)o = u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
     } else {
       for (int r = 0; r < 4; ++r)
-        if (n + r < a.N) o[r] = f2h(silu_mul(c[r], cu[r]));
+        if (n + r < a.N) o[r] = f2h(y[r]);
     }
   } else if (SPLIT) {
     bf16_t* o = (bf16_t*)a.out_act + (int64_t)m * a.N + n;

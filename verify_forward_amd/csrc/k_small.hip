@@ -384,13 +384,18 @@ __global__ void __launch_bounds__(ROPE_THREADS) k_rope_append(const float* __res
     rot[i] = float2{cs, sn};
   }
   __syncthreads();
-  // rotations: q heads then k heads (staged order), one (head, pair) per item
+  // rotations: q heads then k heads (staged order), one (head, pair) per item.
+  // Values past half's range (q always, k and v in the span workspace of a
+  // bf16 model) are saturated there and flagged.
+  constexpr bool HALF = sizeof(TQ) == 2;
+  bool big = false;
   const int n_rot = (nq + nk) * half;
   for (int it = threadIdx.x; it < n_rot; it += blockDim.x) {
     const int hs = it / half, i = it % half;
     const float c = rot[i].x, s = rot[i].y;
     const float a = ld(hs * hd + i), bb = ld(hs * hd + i + half);
     const float ra = a * c - bb * s, rb = a * s + bb * c;
+    if (HALF) big |= !(fabsf(ra) <= 65504.f) || !(fabsf(rb) <= 65504.f);
     if (hs < nq) {
       const int h = qh0 + hs;
       TQ* qo = q_out + ((int64_t)r * hq + h) * hd;
@@ -417,9 +422,11 @@ __global__ void __launch_bounds__(ROPE_THREADS) k_rope_append(const float* __res
   for (int it = threadIdx.x; it < nk * hd; it += blockDim.x) {
     const int g = kh0 + it / hd, dd = it % hd;
     const float vv = ld((nq + nk) * hd + it);
+    if (HALF) big |= !(fabsf(vv) <= 65504.f);
     if (write_kv) vc[((blk * hkv + g) * hd + dd) * CAD_KV_BLOCK + slot] = from_f<T>(vv);
     if (kv.span_v) kv.span_v[((int64_t)g * hd + dd) * kv.span_cap + wrow] = f2h(vv);
   }
+  if (big && status) atomicOr(status, (int32_t)CAD_DEV_F16_RANGE);
 }
 
 // rows at most this many: one work-group per (row, KV group)
