@@ -842,6 +842,12 @@ CAD_GEMM_KERNELS(gate_up, EPI_SWIGLU, TN8_GATE_UP)
 CAD_GEMM_KERNELS(down, EPI_RESID, TILE_N)
 CAD_GEMM_KERNELS(lm_head, EPI_ARGMAX, TILE_N)
 #undef CAD_GEMM_KERNELS
+// the O projection at 17-128 rows: 128-row weight tiles, so that its 4096
+// columns make 32 tiles and eight k splits fill the 256 CUs (256-row tiles
+// left half of them idle at that many rows)
+__global__ void __launch_bounds__(512) k_gemm_s_o_n128(GemmArgs a, int n_tn, int n_tm, int splits) {
+  gemm_tiled_body<EPI_RESID, 128, 8, 1>(a, n_tn, n_tm, splits);
+}
 // the down projection over a single half activation plane (act_f16)
 __global__ void __launch_bounds__(512) k_gemm_down_h(GemmArgs a, int n_tn, int n_tm, int splits) {
   gemm_tiled_body<EPI_RESID, TILE_N, 8, 2, true>(a, n_tn, n_tm, splits);
@@ -938,6 +944,9 @@ hipError_t launch_gemm(int dtype, int role, const GemmArgs& a, hipStream_t s, in
                   k_gemm_f32_##NAME, partials, s)
     case GEMM_QKV: return CAD_LAUNCH(EPI_STORE_F32, qkv, TN8_QKV);
     case GEMM_O:
+      if (a.M > 16 && a.M <= 128)
+        return launch_epi<EPI_RESID>(dtype, a, k_gemm_o, 128, k_gemm_s_o_n128, k_gemm_reduce_o, k_gemv_o,
+                                     k_gemvn_o, k_gemm_f32_o, partials, s, true);
       return launch_epi<EPI_RESID>(dtype, a, k_gemm_o, TILE_N, k_gemm_s_o, k_gemm_reduce_o, k_gemv_o, k_gemvn_o,
                                    k_gemm_f32_o, partials, s, true);
     case GEMM_GATE_UP: return CAD_LAUNCH(EPI_SWIGLU, gate_up, TN8_GATE_UP);
