@@ -66,3 +66,45 @@ def test_decode_step_noalloc_matches_decode_step():
         assert torch.equal(kv_na.k[:, : L // BLK], kv_ref.k[:, : L // BLK])
         del kv_ref, kv_na
     cad.cad_model_destroy(model)
+
+
+@pytest.mark.parametrize("shape", [synth.Shape("odd-steps", 2, 1088, 17, 1, 64, 2112, 4096),
+                                   synth.Shape("ragged-vocab", 2, 1152, 9, 3, 128, 2240, 1001)],
+                         ids=["odd-steps", "ragged-vocab"])
+def test_decode_step_noalloc_edge_shapes(shape):
+    """The same comparison at widths that leave partial tiles in every
+    projection and a ragged vocabulary (after the 7B test in the same
+    process, the shared scratch starts with another model's leftovers)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dev = "cuda"
+    W = synth.make_weights(shape, device=dev)
+    model = cad.cad_model_create(shape, W, max_tokens=16)
+    for i, L in enumerate((900, 37)):
+        nb = (L + 1 + BLK - 1) // BLK
+        kl, vl = synth.random_kv_logical(shape, L, seed=600 + i, device=dev)
+        kv_ref = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device=dev)
+        H.write_prefix(kv_ref, kl, vl)
+        kv_na = cad.KVCache(kv_ref.k.clone(), kv_ref.v.clone(), kv_ref.block_table.clone())
+        token = H.tensors_i32([(311 + 97 * i) % shape.vocab])
+        mask = synth.banned_ids_mask(1, shape.vocab, 64, seed=i)
+        mask_t = torch.from_numpy(mask.view(np.int32)).to(dev)
+        o_ref, o_na = H.outputs(1, shape.vocab), H.outputs(1, shape.vocab)
+        cad.cad_decode_step(model, kv_ref, L, token, mask_t, o_ref["argmax"], o_ref["logits"], o_ref["status"])
+        cad.cad_decode_step_noalloc(model, kv_na, L, token, mask_t, o_na["argmax"], o_na["logits"], o_na["status"])
+        torch.cuda.synchronize()
+        assert int(o_ref["status"][0]) == 0 and int(o_na["status"][0]) == 0
+        lr, ln = o_ref["logits"].cpu().numpy(), o_na["logits"].cpu().numpy()
+        err = float(np.max(np.abs(lr - ln)))
+        kr, vr = H.read_span(kv_ref, L, 1)
+        kn, vn = H.read_span(kv_na, L, 1)
+        ok_k, _ = H.kv_close(kn, kr, TOL)
+        ok_v, _ = H.kv_close(vn, vr, TOL)
+        print(f"{shape.name} call {i}: L={L} logits max|diff| {err:.3e} (bit-equal: {np.array_equal(lr, ln)})",
+              flush=True)
+        assert err <= TOL
+        assert ok_k and ok_v
+        if oracle.top2_margin(lr.astype(np.float64), mask)[0] > 0.1:
+            assert int(o_na["argmax"][0]) == int(o_ref["argmax"][0])
+        del kv_ref, kv_na
+    cad.cad_model_destroy(model)
