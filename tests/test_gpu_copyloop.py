@@ -325,6 +325,51 @@ def test_loop_decode_looped_bf16_equals_greedy_full_depth(d2):
     cad.cad_model_destroy(model)
 
 
+_edge_ref = {}
+
+
+@pytest.mark.parametrize("d2", [0, 3])
+def test_loop_decode_edge_width_bf16_equals_greedy_full_depth(d2):
+    """CopyLoop decoding (and branching at d2 = 3) of a block at the edge
+    widths (d_model 1088, 17 query heads of 64 over one KV head, FFN 2112,
+    vocab 4096) applied 4 times, screened at depth 2: the committed tokens
+    equal the oracle's full-depth greedy decode, whose every decision has a
+    top-2 margin above 0.1 for this prompt (asserted)."""
+    dev = _dev()
+    shape = synth.Shape("edge-loop4", 1, 1088, 17, 1, 64, 2112, 4096, loop_depth=4)
+    cfg = Config.of(shape)
+    Wt = synth.make_weights(shape, seed=0)
+    W64 = _f64(synth.weights_to_numpy(Wt))
+    prompt = [int(t) for t in synth.make_line_prompt(256, shape.vocab, seed=8, line_len_range=(8, 16)).tokens]
+    n, K, ds = 16, 8, 2
+    cap = len(prompt) + n + shape.loop_depth * (K + 1) + 1
+    if "want" not in _edge_ref:
+        okv = KVCache.empty(shape.loop_depth, shape.n_kv_heads, cap, shape.head_dim)
+        x = oracle.decoder.splice_hidden(cfg, W64, okv, 0, prompt)
+        lg = oracle.final_logits(cfg, W64, x[-1:])
+        want, margins = [int(np.argmax(lg[0]))], [float(oracle.top2_margin(lg, None)[0])]
+        while len(want) < n:
+            lg = oracle.decoder.decode_step(cfg, W64, okv, len(prompt) + len(want) - 1, want[-1])[None]
+            margins.append(float(oracle.top2_margin(lg, None)[0]))
+            want.append(int(np.argmax(lg[0])))
+        _edge_ref.update(want=want, margin=min(margins))
+    want = _edge_ref["want"]
+    assert _edge_ref["margin"] > 0.1
+    if d2:
+        kv, nb = _branch_kv(shape, cap, K, dev)
+    else:
+        nb = (cap + BLK - 1) // BLK
+        kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device=dev)
+    model = cad.cad_model_create(shape, _to(Wt, dev), max_tokens=512)
+    loop = cad.cad_loop_create(model, cap, ds, K, 64, branch_depth=d2)
+    got, st = cad.cad_loop_decode(loop, kv, prompt, n)
+    print(f"edge-width bf16 d2={d2}: {st}; tokens {got}", flush=True)
+    assert got == want
+    assert st["dev_status"] == 0 and st["committed"] >= n
+    cad.cad_loop_destroy(loop)
+    cad.cad_model_destroy(model)
+
+
 # ---------------------------------------------------------------------------
 # second-readout branching
 # ---------------------------------------------------------------------------
