@@ -23,7 +23,11 @@ parallelism (d_model 4096, one KV head and its 4 query heads of 128, FFN
 1792, vocab 4000): attention and O projection 512 wide against a 4096-wide
 residual stream.
 
-In all three, the mask of row 0 allows only the vocabulary's last six ids,
+"big-vocab": a vocabulary of 128256 ids over a 256-wide model: the masked
+argmax reduces 501 candidates per row from the tiled LM head (2004 from the
+weight-streaming one), and the LM head dominates the call.
+
+In all four, the mask of row 0 allows only the vocabulary's last six ids,
 so its argmax must come from the last weight tile.  The same shapes also run a
 batched call (five sequences of 1 to 130 rows over a shuffled pool), and
 the odd-steps widths a looped block (applied 3 times, screened at depth 1
@@ -52,6 +56,7 @@ SHAPES = {
     "odd-steps": synth.Shape("odd-steps", 2, 1088, 17, 1, 64, 2112, 4096),
     "ragged-vocab": synth.Shape("ragged-vocab", 2, 1152, 9, 3, 128, 2240, 1001),
     "tp8-share": synth.LLAMA_7B_TP8.replace(name="tp8-share-2layer", n_layers=2),
+    "big-vocab": synth.Shape("big-vocab", 2, 256, 4, 2, 64, 512, 128256),
 }
 
 
