@@ -27,8 +27,12 @@ residual stream.
 argmax reduces 501 candidates per row from the tiled LM head (2004 from the
 weight-streaming one), and the LM head dominates the call.
 
-In all four, the mask of row 0 allows only the vocabulary's last six ids,
-so its argmax must come from the last weight tile.  The same shapes also run a
+"mha64" and "g8-128": the attention group sizes the production shapes do
+not use, one query head per KV head at head_dim 64 (the register-fragment
+kernel up to 16 rows) and eight at head_dim 128 (that kernel up to 2 rows).
+
+In all of them, the mask of row 0 allows only the vocabulary's last six
+ids, so its argmax must come from the last weight tile.  The same shapes also run a
 batched call (five sequences of 1 to 130 rows over a shuffled pool), and
 the odd-steps widths a looped block (applied 3 times, screened at depth 1
 or 2).
@@ -57,6 +61,8 @@ SHAPES = {
     "ragged-vocab": synth.Shape("ragged-vocab", 2, 1152, 9, 3, 128, 2240, 1001),
     "tp8-share": synth.LLAMA_7B_TP8.replace(name="tp8-share-2layer", n_layers=2),
     "big-vocab": synth.Shape("big-vocab", 2, 256, 4, 2, 64, 512, 128256),
+    "mha64": synth.Shape("mha64", 2, 1024, 16, 16, 64, 2048, 4096),
+    "g8-128": synth.Shape("g8-128", 2, 1024, 8, 1, 128, 2048, 4096),
 }
 
 
