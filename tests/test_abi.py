@@ -129,3 +129,17 @@ def test_binding_structs_match_the_header(tmp_path):
         assert got[(name, "size")] == ctypes.sizeof(T), name
         for f, _ in T._fields_:
             assert got[(name, f)] == getattr(T, f).offset, (name, f)
+
+
+def test_binding_constants_match_the_header():
+    """Every ``#define CAD_*`` number and every ``cad_status`` / ``cad_mode``
+    enumerator of include/cad.h has the same value in the binding."""
+    text = open(os.path.join(ROOT, "include", "cad.h")).read()
+    defines = {}
+    for name, expr in re.findall(r"^#define\s+(CAD_[A-Z0-9_]+)\s+(\(?-?[0-9][0-9xu <()-]*)", text, re.M):
+        defines[name] = eval(expr.replace("u", ""))
+    enums = {name: int(v) for name, v in re.findall(r"\b(CAD_[A-Z0-9_]+)\s*=\s*(-?\d+)", text)}
+    both = {**defines, **enums}
+    assert {"CAD_DEV_F16_RANGE", "CAD_KV_BLOCK", "CAD_OK", "CAD_COMMIT"} <= set(both)
+    for name, value in both.items():
+        assert getattr(cad, name) == value, name
