@@ -29,6 +29,15 @@ Workloads (seeded, synthetic; the tiny fp32 model):
 * degenerate programs on the same models: at most one op (a copy; a gen
   body that reaches the length cap), gen bodies capped at one id (mixed with
   a copy; six in a row), and a stream limit of three ids.
+
+The bf16 cases run the same shape in bfloat16 (the weights rounded from the
+same draws) with the LM head scaled by 32, a power of two and so exact in
+bf16: the argmax of every step is unchanged by the scale, and the masked
+top-2 margins of the decisions grow with it past 0.1, the decision bar of
+the bf16 parity tests (five times their 2e-2 logit bar).  A splice over the
+prompt checks that bar on the scaled model first.  The eog-window case
+stays fp32-only: in bf16 its id cycle closes the end-of-gen window only
+once and some of its decision margins stay below the bar.
 """
 import numpy as np
 import pytest
@@ -55,12 +64,14 @@ def _dev():
     return "cuda"
 
 
-def _model(scale):
-    shape = synth.TINY
+def _model(scale, dtype="f32"):
+    shape = synth.TINY if dtype == "f32" else synth.TINY.replace(name="tiny-bf16", dtype="bf16")
     Wt = synth.make_weights(shape, seed=5)
     if scale != 1.0:
         for k in ("w_qkv", "w_o", "w_gate_up", "w_down"):
             Wt["layers"][0][k].mul_(scale)
+    if dtype == "bf16":
+        Wt["lm_head"].mul_(BF16_HEAD_SCALE)
     return shape, Wt, synth.weights_to_numpy(Wt)
 
 
@@ -112,14 +123,18 @@ CASES = {
     "stream3": (1.0, {}, "lines", 6, 12, 3, 19),                        # three ids: stopped inside a template
 }
 MARGIN = 2e-4   # twice the fp32 tiny model's logit bar (1e-4 absolute)
+BF16_CASES = ["mixed-lines", "mixed-tokens", "long-gen", "copies", "one-op-gen", "gen1-mixed", "stream-limit"]
+BF16_HEAD_SCALE = 32.0
+BF16_MARGIN = 0.1    # five times the bf16 logit bar (2e-2)
+BF16_TOL = 2e-2
 
 _ref_cache = {}
 
 
-def _reference(name):
-    if name not in _ref_cache:
+def _reference(name, dtype="f32"):
+    if (name, dtype) not in _ref_cache:
         scale, over, unit, max_ops, max_gen, max_stream, seed = CASES[name]
-        shape, Wt, W = _model(scale)
+        shape, Wt, W = _model(scale, dtype)
         cfg = Config.of(shape)
         table = CP.Table(**{**BASE, **over})
         doc, prompt = _doc_prompt(table, seed)
@@ -127,18 +142,52 @@ def _reference(name):
         ref = CP.program_decode(cfg, W, kv, prompt, doc, table, unit=unit, max_ops=max_ops, max_gen=max_gen,
                                 max_stream=max_stream)
         margin = _replay_min_margin(cfg, W, prompt, ref[0], doc, table, unit, max_ops, max_gen)
-        _ref_cache[name] = (shape, Wt, W, cfg, table, doc, prompt, ref, margin)
-    return _ref_cache[name]
+        _ref_cache[name, dtype] = (shape, Wt, W, cfg, table, doc, prompt, ref, margin)
+    return _ref_cache[name, dtype]
+
+
+def _to_dev(Wt, dev):
+    return {k: (v.to(dev) if torch.is_tensor(v) else [{kk: vv.to(dev) for kk, vv in lw.items()} for lw in v])
+            for k, v in Wt.items()}
 
 
 @pytest.mark.parametrize("name", list(CASES))
 @pytest.mark.parametrize("draft_k,chain", [(0, 1), (0, 4), (0, 64), (3, 4), (8, 2)])
 def test_program_decode_matches_oracle(name, draft_k, chain):
+    _check_program(name, "f32", MARGIN, draft_k, chain)
+
+
+@pytest.mark.parametrize("name", BF16_CASES)
+@pytest.mark.parametrize("draft_k,chain", [(0, 1), (0, 64), (8, 2)])
+def test_program_decode_bf16_matches_oracle(name, draft_k, chain):
+    """The same comparison on the bfloat16 model (the product's dtype)."""
     dev = _dev()
-    shape, Wt, W, cfg, table, doc, prompt, ref, margin = _reference(name)
+    shape, Wt, W, cfg, table, doc, prompt, ref, margin = _reference(name, "bf16")
+    # the logit bar on this model: a splice over the prompt against the oracle
+    nb = (len(prompt) + BLK - 1) // BLK
+    kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device=dev)
+    model = cad.cad_model_create(shape, _to_dev(Wt, dev), max_tokens=len(prompt))
+    o = {"argmax": torch.empty(len(prompt), dtype=torch.int32, device=dev),
+         "accepted": torch.empty(1, dtype=torch.int32, device=dev),
+         "logits": torch.empty(len(prompt), shape.vocab, dtype=torch.float32, device=dev),
+         "status": torch.zeros(1, dtype=torch.int32, device=dev)}
+    cad.cad_splice_forward(model, kv, 0, torch.tensor(prompt, dtype=torch.int32, device=dev), None, cad.CAD_COMMIT,
+                           o["argmax"], o["accepted"], o["logits"], o["status"])
+    lref = oracle.splice(cfg, W, KVCache.empty(1, cfg.n_kv_heads, len(prompt), cfg.head_dim), 0, prompt)
+    torch.cuda.synchronize()
+    cad.cad_model_destroy(model)
+    err = float(np.max(np.abs(o["logits"].cpu().numpy() - lref)))
+    print(f"{name} bf16 prompt logits max|diff| {err:.3e} (logit std {lref.std():.2f})", flush=True)
+    assert int(o["status"][0]) == 0 and err <= BF16_TOL
+    _check_program(name, "bf16", BF16_MARGIN, draft_k, chain)
+
+
+def _check_program(name, dtype, bar, draft_k, chain):
+    dev = _dev()
+    shape, Wt, W, cfg, table, doc, prompt, ref, margin = _reference(name, dtype)
     scale, over, unit, max_ops, max_gen, max_stream, seed = CASES[name]
     stream_ref, ops_ref, out_ref, st_ref = ref
-    assert margin > MARGIN, margin
+    assert margin > bar, margin
     if draft_k:   # the oracle's drafts are lossless too
         kv_o = KVCache.empty(1, cfg.n_kv_heads, 2048, cfg.head_dim)
         alt = CP.program_decode(cfg, W, kv_o, prompt, doc, table, unit=unit, max_ops=max_ops, max_gen=max_gen,
@@ -148,12 +197,10 @@ def test_program_decode_matches_oracle(name, draft_k, chain):
     cap = len(prompt) + max_stream + 2 * max_doc + 2 * draft_k + chain + 64
     nb = (cap + BLK - 1) // BLK
     kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device=dev)
-    model = cad.cad_model_create(shape, {k: (v.to(dev) if torch.is_tensor(v) else
-                                             [{kk: vv.to(dev) for kk, vv in lw.items()} for lw in v])
-                                         for k, v in Wt.items()}, max_tokens=64)
+    model = cad.cad_model_create(shape, _to_dev(Wt, dev), max_tokens=64)
     prog = cad.cad_program_create(model, nb * BLK, table, max_doc=max_doc, max_stream=max_stream, max_ops=max_ops,
                                   max_gen=max_gen, draft_k=draft_k, chain=chain)
-    print(f"{name} draft_k={draft_k} chain={chain}", flush=True)
+    print(f"{name} {dtype} draft_k={draft_k} chain={chain} (oracle margin {margin:.3g})", flush=True)
     got, ops, out, st = cad.cad_program_decode(prog, kv, prompt, doc, unit=unit)
     print(f"  stats {st}", flush=True)
     assert st["fsm_error"] == 0 and st["dev_status"] == 0
@@ -184,9 +231,7 @@ def test_program_decode_repeated_bodies_use_drafts():
     assert sum(1 for o in ops_ref if o["op"] == "gen" and len(o["body"]) < 30) >= 2
     nb = 64
     kv = cad.KVCache.alloc(shape, nb, synth.identity_block_table(nb), device=dev)
-    model = cad.cad_model_create(shape, {k: (v.to(dev) if torch.is_tensor(v) else
-                                             [{kk: vv.to(dev) for kk, vv in lw.items()} for lw in v])
-                                         for k, v in Wt.items()}, max_tokens=64)
+    model = cad.cad_model_create(shape, _to_dev(Wt, dev), max_tokens=64)
     prog = cad.cad_program_create(model, nb * BLK, table, max_doc=128, max_stream=512, max_ops=6, max_gen=30,
                                   draft_k=8, chain=4)
     got, ops, out, st = cad.cad_program_decode(prog, kv, prompt, doc, unit="lines")
