@@ -10,9 +10,11 @@ on the 128-row tiles; 34 steps of 32 split into two odd halves on the
 the weight tiles end part-way through a tile (1216 QKV rows over 192-row
 tiles, 1088 over 256), and the gate/up projection splits K and leaves its
 sums to the reduce kernel.  The spans cover the weight-streaming path
-(5 rows), the 128-row tiles (40 rows) and the 256-row tiles (300 rows,
-two activation tiles, the second partial; and 200 rows on an empty cache,
-where attention sees only the span's own keys).
+(5 and 16 rows), the 128-row activation tiles (17, 40 and 128 rows; QKV,
+O and down there on 128-row weight tiles, 1216 and 1088 rows ending
+part-way through one) and the 256-row tiles (129 rows, one full activation
+tile and one row of the next; 300 rows, the second partial; and 200 rows
+on an empty cache, where attention sees only the span's own keys).
 
 "ragged-vocab": 2 layers, d_model 1152, 9 query heads of 128 over 3 KV
 heads, FFN 2240, vocab 1001: the LM head's last weight tile holds 9 ids
@@ -93,7 +95,10 @@ def edge_model(request):
     return shape, W, synth.weights_to_numpy(Wc)
 
 
-@pytest.mark.parametrize("L,N", [(300, 5), (300, 40), (211, 300), (0, 200)])
+# 16 / 17 and 128 / 129 rows are where the projections change kernels
+# (weight streaming -> 128-row tiles -> 256-row tiles)
+@pytest.mark.parametrize("L,N", [(300, 5), (300, 16), (300, 17), (300, 40), (123, 128), (123, 129), (211, 300),
+                                 (0, 200)])
 def test_edge_shapes(edge_model, L, N):
     SHAPE, W, Wn = edge_model
     cfg = Config.of(SHAPE)
