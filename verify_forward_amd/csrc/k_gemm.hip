@@ -842,9 +842,9 @@ CAD_GEMM_KERNELS(gate_up, EPI_SWIGLU, TN8_GATE_UP)
 CAD_GEMM_KERNELS(down, EPI_RESID, TILE_N)
 CAD_GEMM_KERNELS(lm_head, EPI_ARGMAX, TILE_N)
 #undef CAD_GEMM_KERNELS
-// the O projection at 17-128 rows: 128-row weight tiles, so that its 4096
-// columns make 32 tiles and eight k splits fill the 256 CUs (256-row tiles
-// left half of them idle at that many rows)
+// the O projection on 128-row weight tiles (where use_n128 picks them): at
+// 17-128 rows its 4096 columns then make 32 tiles and eight k splits fill
+// the 256 CUs (256-row tiles left half of them idle at that many rows)
 __global__ void __launch_bounds__(512) k_gemm_s_o_n128(GemmArgs a, int n_tn, int n_tm, int splits) {
   gemm_tiled_body<EPI_RESID, 128, 8, 1>(a, n_tn, n_tm, splits);
 }
@@ -866,6 +866,40 @@ __global__ void __launch_bounds__(512) k_gemm_s_down_h(GemmArgs a, int n_tn, int
 // that adds them (N = 128: step 8.81 -> 8.59 ms; N = 64: 6.94 -> 6.77 ms)
 __global__ void __launch_bounds__(512) k_gemm_s_down_h_n128(GemmArgs a, int n_tn, int n_tm, int splits) {
   gemm_tiled_body<EPI_RESID, 128, 8, 1, true>(a, n_tn, n_tm, splits);
+}
+
+// Tiles and k splits of a tiled launch: one work-group per CU at a time,
+// so K is split while the split tiles still fit the 256 compute units at
+// once, keeping at least 16 k steps of 32 per split and the partials within
+// the workspace.
+struct TiledPlan {
+  int n_tn, n_tm, splits;
+  int wgs() const { return n_tn * n_tm * splits; }
+};
+static TiledPlan tiled_plan(const GemmArgs& a, int cols_per_tile, int tm_rows, bool swiglu) {
+  TiledPlan p;
+  p.n_tn = (a.N + cols_per_tile - 1) / cols_per_tile;
+  p.n_tm = (a.M + tm_rows - 1) / tm_rows;
+  p.splits = 1;
+  const int tiles = p.n_tn * p.n_tm, nk = a.K / TK;
+  const int64_t split_floats = (int64_t)a.M * a.N * (swiglu ? 2 : 1);
+  if (a.split_ws && a.N % 64 == 0)
+    while (tiles * (p.splits + 1) <= 256 && nk / (p.splits + 1) >= 16 &&
+           split_floats * (p.splits + 1) <= a.split_cap)
+      ++p.splits;
+  return p;
+}
+
+// QKV, O and down (bf16, more than 16 rows) on 128 x 128 tiles (128 weight
+// rows, 128 activation rows): always at 17-128 rows (fewer k splits, so
+// fewer partial planes for the consumer; measured faster), and above that
+// wherever the default tiles leave more compute units idle (the 1B shape at
+// N = 256: its 2048-wide K allows at most four splits, so QKV and O made 64
+// work-groups and down 128).
+static bool use_n128(const GemmArgs& a, int default_cols, bool default_rows128) {
+  if (a.M <= 16) return false;
+  if (a.M <= 128) return true;
+  return tiled_plan(a, 128, 128, false).wgs() > tiled_plan(a, default_cols, default_rows128 ? 128 : 256, false).wgs();
 }
 
 typedef void (*TiledFn)(GemmArgs, int, int, int);
@@ -918,18 +952,8 @@ static hipError_t launch_epi(int dtype, const GemmArgs& a, TiledFn tiled8, int t
     // the partial planes for the RMSNorm that adds them: 15.1 -> 12.9 us)
     const bool small = a.M <= 128 || rows128;
     const int tm_rows = small ? 128 : 256;
-    const int tn = tn8;
-    const int cols_per_tile = (EPI == EPI_SWIGLU) ? tn / 2 : tn;
-    const int n_tn = (a.N + cols_per_tile - 1) / cols_per_tile, n_tm = (a.M + tm_rows - 1) / tm_rows;
-    const int tiles = n_tn * n_tm, nk = a.K / TK;
-    // one work-group per CU at a time: split K while the split tiles still
-    // fit the 256 compute units at once, keeping at least 16 k steps of 32
-    // per split and the partials within the workspace
-    const int64_t split_floats = (int64_t)a.M * a.N * (EPI == EPI_SWIGLU ? 2 : 1);
-    int splits = 1;
-    if (a.split_ws && a.N % 64 == 0)
-      while (tiles * (splits + 1) <= 256 && nk / (splits + 1) >= 16 && split_floats * (splits + 1) <= a.split_cap)
-        ++splits;
+    const TiledPlan pl = tiled_plan(a, (EPI == EPI_SWIGLU) ? tn8 / 2 : tn8, tm_rows, EPI == EPI_SWIGLU);
+    const int n_tn = pl.n_tn, n_tm = pl.n_tm, tiles = n_tn * n_tm, splits = pl.splits;
     hipLaunchKernelGGL(small ? tiled_s : tiled8, dim3(tiles * splits), dim3(512), 0, s, a, n_tn, n_tm,
                        splits);
     if (EPI == EPI_ARGMAX) *a.n_cand = n_tn;  // one candidate per weight tile
@@ -955,12 +979,12 @@ hipError_t launch_gemm(int dtype, int role, const GemmArgs& a, hipStream_t s, in
   launch_epi<EPI>(dtype, a, k_gemm_##NAME, TN8, k_gemm_s_##NAME, k_gemm_reduce_##NAME, k_gemv_##NAME, k_gemvn_##NAME, \
                   k_gemm_f32_##NAME, partials, s)
     case GEMM_QKV:
-      if (dtype == CAD_BF16 && a.M > 16 && a.M <= 128)
+      if (dtype == CAD_BF16 && use_n128(a, TN8_QKV, false))
         return launch_epi<EPI_STORE_F32>(dtype, a, k_gemm_qkv, 128, k_gemm_s_qkv_n128, k_gemm_reduce_qkv, k_gemv_qkv,
-                                         k_gemvn_qkv, k_gemm_f32_qkv, partials, s);
+                                         k_gemvn_qkv, k_gemm_f32_qkv, partials, s, true);
       return CAD_LAUNCH(EPI_STORE_F32, qkv, TN8_QKV);
     case GEMM_O:
-      if (a.M > 16 && a.M <= 128)
+      if (dtype == CAD_BF16 && use_n128(a, TILE_N, true))
         return launch_epi<EPI_RESID>(dtype, a, k_gemm_o, 128, k_gemm_s_o_n128, k_gemm_reduce_o, k_gemv_o,
                                      k_gemvn_o, k_gemm_f32_o, partials, s, true);
       return launch_epi<EPI_RESID>(dtype, a, k_gemm_o, TILE_N, k_gemm_s_o, k_gemm_reduce_o, k_gemv_o, k_gemvn_o,
@@ -969,9 +993,9 @@ hipError_t launch_gemm(int dtype, int role, const GemmArgs& a, hipStream_t s, in
     case GEMM_DOWN:
       if (a.act_f16) {
         if (dtype != CAD_BF16 || a.M <= 16) return hipErrorInvalidValue;
-        if (a.M <= 128)
+        if (use_n128(a, TILE_N, false))
           return launch_epi<EPI_RESID>(dtype, a, k_gemm_down_h, 128, k_gemm_s_down_h_n128, k_gemm_reduce_down,
-                                       k_gemv_down, k_gemvn_down, k_gemm_f32_down, partials, s);
+                                       k_gemv_down, k_gemvn_down, k_gemm_f32_down, partials, s, true);
         return launch_epi<EPI_RESID>(dtype, a, k_gemm_down_h, TILE_N, k_gemm_s_down_h, k_gemm_reduce_down,
                                      k_gemv_down, k_gemvn_down, k_gemm_f32_down, partials, s);
       }
