@@ -854,6 +854,11 @@ __global__ void __launch_bounds__(512) k_gemm_s_o_n128(GemmArgs a, int n_tn, int
 __global__ void __launch_bounds__(512) k_gemm_s_qkv_n128(GemmArgs a, int n_tn, int n_tm, int splits) {
   gemm_tiled_body<EPI_STORE_F32, 128, 8, 1>(a, n_tn, n_tm, splits);
 }
+// gate/up on 128-row weight tiles (64 SwiGLU columns; where fuller_n128
+// picks them)
+__global__ void __launch_bounds__(512) k_gemm_s_gate_up_n128(GemmArgs a, int n_tn, int n_tm, int splits) {
+  gemm_tiled_body<EPI_SWIGLU, 128, 8, 1>(a, n_tn, n_tm, splits);
+}
 // the down projection over a single half activation plane (act_f16)
 __global__ void __launch_bounds__(512) k_gemm_down_h(GemmArgs a, int n_tn, int n_tm, int splits) {
   gemm_tiled_body<EPI_RESID, TILE_N, 8, 2, true>(a, n_tn, n_tm, splits);
@@ -898,10 +903,20 @@ static TiledPlan tiled_plan(const GemmArgs& a, int cols_per_tile, int tm_rows, b
 // wherever the default tiles leave more compute units idle (the 1B shape at
 // N = 256: its 2048-wide K allows at most four splits, so QKV and O made 64
 // work-groups and down 128).
+// Whether the 128 x 128 tiles make more work-groups than the default tiles
+// (both counted up to the 256 that run at once).  Gate/up takes them only
+// then (the 1B shape at N = 256: 222 work-groups with three k splits and a
+// reduce kernel, against 256 tiles with neither: 2.72 -> 2.51 ms; at 17-128
+// rows of the 7B shape they measured slower).
+static bool fuller_n128(const GemmArgs& a, int default_cols, bool default_rows128, bool swiglu) {
+  const int c = swiglu ? 64 : 128;
+  return min(tiled_plan(a, c, 128, swiglu).wgs(), 256) >
+         min(tiled_plan(a, default_cols, (a.M <= 128 || default_rows128) ? 128 : 256, swiglu).wgs(), 256);
+}
 static bool use_n128(const GemmArgs& a, int default_cols, bool default_rows128) {
   if (a.M <= 16) return false;
   if (a.M <= 128) return true;
-  return tiled_plan(a, 128, 128, false).wgs() > tiled_plan(a, default_cols, default_rows128 ? 128 : 256, false).wgs();
+  return fuller_n128(a, default_cols, default_rows128, false);
 }
 
 typedef void (*TiledFn)(GemmArgs, int, int, int);
@@ -991,7 +1006,11 @@ hipError_t launch_gemm(int dtype, int role, const GemmArgs& a, hipStream_t s, in
                                      k_gemvn_o, k_gemm_f32_o, partials, s, true);
       return launch_epi<EPI_RESID>(dtype, a, k_gemm_o, TILE_N, k_gemm_s_o, k_gemm_reduce_o, k_gemv_o, k_gemvn_o,
                                    k_gemm_f32_o, partials, s, true);
-    case GEMM_GATE_UP: return CAD_LAUNCH(EPI_SWIGLU, gate_up, TN8_GATE_UP);
+    case GEMM_GATE_UP:
+      if (dtype == CAD_BF16 && a.M > 16 && fuller_n128(a, TN8_GATE_UP / 2, false, true))
+        return launch_epi<EPI_SWIGLU>(dtype, a, k_gemm_gate_up, 128, k_gemm_s_gate_up_n128, k_gemm_reduce_gate_up,
+                                      k_gemv_gate_up, k_gemvn_gate_up, k_gemm_f32_gate_up, partials, s, true);
+      return CAD_LAUNCH(EPI_SWIGLU, gate_up, TN8_GATE_UP);
     case GEMM_DOWN:
       if (a.act_f16) {
         if (dtype != CAD_BF16 || a.M <= 16) return hipErrorInvalidValue;
